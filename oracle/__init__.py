@@ -1,0 +1,17 @@
+"""fp64 CPU oracle for the top-K KL distillation loss.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path (the HIP library and its
+Python binding) may import, call or execute anything in this package; only the
+tests, the smoke check and the bench's CPU-baseline leg use it.
+"""
+from .kd_oracle import (  # noqa: F401
+    teacher_scaled_grid,
+    oracle_from_logits,
+    oracle_loss_grads,
+    oracle_rows,
+    oracle_entropy,
+    oracle_entropy_rows,
+    oracle_select_top_fraction,
+    oracle_entropy_select_kl,
+    oracle_validate_topk,
+)

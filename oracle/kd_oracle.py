@@ -1,0 +1,277 @@
+"""Plain fp64 definition of the offline top-K KL distillation loss and its gradients.
+
+TEST INFRASTRUCTURE ONLY: the GPU library never imports this module, and this
+module imports nothing from the GPU library. Inputs arrive as host arrays
+(bf16 values already widened exactly to fp32); every step below runs in fp64.
+
+Sources (web pages; the citation names the page and the section):
+  [HF]    "Making Knowledge Distillation Cheap Enough to Run at Scale", as
+          written up in "Knowledge Distillation 비용 줄이기: offline top-K logits와
+          chunked KL 적용 기준" (aibase.it) - sections "offline top-K logits" and
+          "what chunked KL loss does" (dense KL expands the cached top-K logits
+          into a dense teacher probability grid and compares it with the dense
+          student log-probability grid; that dense form is the correctness
+          baseline; the chunked and fused forms compute the same loss without the
+          grids), and "operations" (cache validation items).
+  [REV]   "[논문리뷰] Efficient Knowledge Distillation for LLMs: Offline Top-K
+          Logits and a Fused Chunked KL Loss" - section 1 (key terms: the fused
+          loss folds the output projection into the loss, chunk by chunk).
+  [AIT]   AI Trends summary of the same work - glossary (KL loss, top-K cache,
+          chunked KL) and evidence list (all loss variants reach the same loss).
+  [PRIM]  "LLM Primer, Chapter 6 - Pruning and Distillation", section 6.2 (the
+          loss is the KL divergence between temperature-softened teacher and
+          student distributions; MiniLLM's reverse KL is named as the departure).
+  [SKD]   "Rethinking Selective Knowledge Distillation" summary (gist.science) -
+          Method, section 2 (SE-KD: supervise the top-k% positions ranked by
+          student entropy H(q_t)) and section 3 (selective LM head, chunked
+          entropy).
+
+Readings where the pages are silent (each is repeated in the design doc):
+  * forward KL(p_teacher || q_student) [HF dense KL compares a teacher probability
+    grid with a student log-probability grid; PRIM names reverse KL as another
+    method's departure];
+  * both sides softened by the same T: p = softmax(l/T), q = softmax(z/T) [PRIM 6.2];
+  * no T^2 factor on the loss;
+  * loss = sum over valid positions of KL_t, divided by the global count N of
+    valid positions; N = 0 gives loss 0 and zero gradients;
+  * teacher probabilities are renormalised over the K cached entries only;
+  * duplicate ids in a row: their probabilities add;
+  * a teacher logit of -inf gives p = 0; a row whose K logits are all -inf is a
+    missing position and is excluded like a masked row;
+  * entropy is in nats over the full vocabulary at T = 1; selection keeps
+    floor(num*S/den) positions, highest entropy first, lower index on ties.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "teacher_scaled_grid",
+    "oracle_from_logits",
+    "oracle_loss_grads",
+    "oracle_rows",
+    "oracle_entropy",
+    "oracle_entropy_rows",
+    "oracle_select_top_fraction",
+    "oracle_entropy_select_kl",
+    "oracle_validate_topk",
+]
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+def _logsumexp_rows(X: np.ndarray) -> np.ndarray:
+    """log sum_v exp(X[t, v]) per row, fp64; rows of all -inf give -inf."""
+    m = np.max(X, axis=1)
+    mf = np.where(np.isfinite(m), m, 0.0)
+    with np.errstate(divide="ignore"):
+        return np.log(np.sum(np.exp(X - mf[:, None]), axis=1)) + mf
+
+
+def _present_rows(tlogits, T):
+    """Rows whose teacher log-normaliser is finite (at least one finite logit, none +inf/NaN)."""
+    tl = _f64(tlogits)
+    if tl.shape[1] == 0:
+        return np.zeros(tl.shape[0], dtype=bool)
+    with np.errstate(invalid="ignore"):
+        return np.isfinite(_logsumexp_rows(tl / float(T)))
+
+
+def teacher_scaled_grid(ids: np.ndarray, tlogits: np.ndarray, V: int, T: float) -> np.ndarray:
+    """Dense teacher grid of l/T, -inf off the cached top-K ids [HF, "what chunked KL loss does"].
+
+    Entries that share an id in one row are combined with logaddexp of their
+    scaled logits, so that after the softmax their probabilities add.
+    """
+    ids = np.asarray(ids)
+    S, K = ids.shape
+    if S and K and (ids.min() < 0 or ids.max() >= V):
+        raise ValueError("teacher id out of range [0, V)")
+    L = np.full((S, V), -np.inf)
+    rows = np.arange(S)
+    scaled = _f64(tlogits) / float(T)
+    for k in range(K):
+        cur = L[rows, ids[:, k]]
+        with np.errstate(invalid="ignore"):
+            L[rows, ids[:, k]] = np.logaddexp(cur, scaled[:, k])
+    return L
+
+
+def _row_terms(Z, ids, tlogits, T):
+    """Per-row dense terms of the definition for a block of rows.
+
+    Returns (kl[t], lse[t] = logsumexp(z_t/T), soft[t, v] = softmax(z_t/T) - p_t,
+    present[t] = row has at least one finite teacher logit).
+    """
+    Z = _f64(Z)
+    S, V = Z.shape
+    Lt = teacher_scaled_grid(ids, tlogits, V, T)                 # dense teacher grid of l/T
+    lse_t = _logsumexp_rows(Lt)
+    present = np.isfinite(lse_t)
+    lse_t_safe = np.where(present, lse_t, 0.0)
+    with np.errstate(invalid="ignore"):
+        logP = Lt - lse_t_safe[:, None]                          # log of the renormalised top-K softmax
+    P = np.where(present[:, None], np.exp(logP), 0.0)
+    ZT = Z / float(T)
+    lse = _logsumexp_rows(ZT)                                    # log-normaliser of z/T over all V
+    with np.errstate(invalid="ignore"):
+        logQ = ZT - lse[:, None]
+    pos = P > 0.0
+    kl = np.zeros(S)
+    for t in range(S):                                           # sum over p > 0 only: 0*log 0 = 0
+        sel = pos[t]
+        kl[t] = np.sum(P[t, sel] * (logP[t, sel] - logQ[t, sel]))
+    soft = np.exp(logQ) - P                                      # d KL_t / d(z_t/T)
+    return kl, lse, soft, present
+
+
+def oracle_from_logits(Z, ids, tlogits, T=1.0, mask=None, grad_loss=1.0):
+    """Loss and logit gradient from given student logits Z[S, V] (dense definition).
+
+    Returns dict(loss, kl_rows, lse, dZ, N, valid); dZ = d loss / d Z.
+    """
+    Z = _f64(Z)
+    S = Z.shape[0]
+    kl, lse, soft, present = _row_terms(Z, ids, tlogits, T)
+    m = np.ones(S, dtype=bool) if mask is None else (np.asarray(mask) != 0)
+    valid = m & present
+    N = int(valid.sum())
+    if N == 0:
+        return dict(loss=0.0, kl_rows=kl, lse=lse, dZ=np.zeros_like(Z), N=0, valid=valid)
+    loss = math.fsum(kl[valid]) / N                              # mean over valid positions
+    coef = float(grad_loss) / (float(T) * N)
+    dZ = np.where(valid[:, None], soft, 0.0) * coef              # (softmax(z/T) - p) / (T N)
+    return dict(loss=loss, kl_rows=kl, lse=lse, dZ=dZ, N=N, valid=valid)
+
+
+def oracle_loss_grads(hidden, W, ids, tlogits, T=1.0, mask=None, grad_loss=1.0, chunk=None):
+    """Loss, dHidden, dW of the top-K KL loss through the output projection.
+
+    chunk=None: the dense definition (full [S, V] grids) [HF dense KL].
+    chunk=C: the same sum taken over row blocks of C, each projected, folded
+    into the loss and discarded, with the count N of valid rows taken over all
+    rows [REV section 1; HF "what chunked KL loss does"].
+    """
+    Hd, Wd = _f64(hidden), _f64(W)
+    S = Hd.shape[0]
+    ids = np.asarray(ids)
+    tl = _f64(tlogits)
+    if chunk is None:
+        Z = Hd @ Wd.T
+        r = oracle_from_logits(Z, ids, tl, T, mask, grad_loss)
+        dH = r["dZ"] @ Wd                                        # chain rule through z = h W^T
+        dW = r["dZ"].T @ Hd
+        return dict(loss=r["loss"], kl_rows=r["kl_rows"], lse=r["lse"], dH=dH, dW=dW,
+                    N=r["N"], valid=r["valid"])
+    C = int(chunk)
+    if C <= 0:
+        raise ValueError("chunk must be positive")
+    m = np.ones(S, dtype=bool) if mask is None else (np.asarray(mask) != 0)
+    present = _present_rows(tl, T)
+    valid = m & present
+    N = int(valid.sum())
+    kl_all = np.zeros(S)
+    lse_all = np.zeros(S)
+    dH = np.zeros_like(Hd)
+    dW = np.zeros_like(Wd)
+    coef = float(grad_loss) / (float(T) * N) if N else 0.0
+    for c0 in range(0, S, C):
+        c1 = min(S, c0 + C)
+        Zc = Hd[c0:c1] @ Wd.T
+        kl, lse, soft, _ = _row_terms(Zc, ids[c0:c1], tl[c0:c1], T)
+        kl_all[c0:c1] = kl
+        lse_all[c0:c1] = lse
+        if N:
+            Gc = np.where(valid[c0:c1, None], soft, 0.0) * coef
+            dH[c0:c1] = Gc @ Wd
+            dW += Gc.T @ Hd[c0:c1]
+    loss = math.fsum(kl_all[valid]) / N if N else 0.0
+    return dict(loss=loss, kl_rows=kl_all, lse=lse_all, dH=dH, dW=dW, N=N, valid=valid)
+
+
+def oracle_rows(hidden_rows, W, ids_rows, tl_rows, T, N, grad_loss=1.0):
+    """Per-row outputs for a sample of rows, given the global valid count N.
+
+    Every row of the loss depends only on its own hidden state and cache row,
+    so kl_t, lse_t and dHidden_t of sampled rows follow the definition exactly.
+    Returns dict(kl_rows, lse, dH) for the given rows (all treated as valid).
+    """
+    Hd, Wd = _f64(hidden_rows), _f64(W)
+    Z = Hd @ Wd.T
+    kl, lse, soft, present = _row_terms(Z, ids_rows, tl_rows, T)
+    coef = float(grad_loss) / (float(T) * N) if N else 0.0
+    G = np.where(present[:, None], soft, 0.0) * coef
+    return dict(kl_rows=kl, lse=lse, dH=G @ Wd)
+
+
+def oracle_entropy_rows(Z):
+    """Entropy in nats of softmax(z_t) over the full vocabulary, per row [SKD section 2]."""
+    Z = _f64(Z)
+    lse = _logsumexp_rows(Z)
+    logq = Z - lse[:, None]
+    q = np.exp(logq)
+    return -np.sum(np.where(q > 0.0, q * logq, 0.0), axis=1)
+
+
+def oracle_entropy(hidden, W, chunk=None):
+    """Student entropy H(q_t), q_t = softmax(hidden_t W^T), per position [SKD sections 2-3].
+
+    chunk bounds the rows projected at once (the chunked-entropy form); the
+    result does not depend on it.
+    """
+    Hd, Wd = _f64(hidden), _f64(W)
+    S = Hd.shape[0]
+    C = S if chunk is None else int(chunk)
+    out = np.zeros(S)
+    for c0 in range(0, S, max(C, 1)):
+        c1 = min(S, c0 + C)
+        out[c0:c1] = oracle_entropy_rows(Hd[c0:c1] @ Wd.T)
+    return out
+
+
+def oracle_select_top_fraction(entropy, num, den):
+    """Keep floor(num*S/den) positions, highest entropy first, lower index on ties [SKD section 2].
+
+    Returns (mask uint8 [S], idx int32 ascending, count).
+    """
+    e = _f64(entropy)
+    S = e.shape[0]
+    if den <= 0 or num < 0 or num > den:
+        raise ValueError("need 0 <= num <= den, den > 0")
+    k = (int(num) * S) // int(den)
+    order = np.argsort(-e, kind="stable")
+    keep = np.sort(order[:k])
+    mask = np.zeros(S, dtype=np.uint8)
+    mask[keep] = 1
+    return mask, keep.astype(np.int32), k
+
+
+def oracle_entropy_select_kl(hidden, W, ids, tlogits, num=20, den=100, T=1.0, grad_loss=1.0,
+                             chunk=None):
+    """Entropy-selective variant: entropy over all positions, top num/den kept,
+    then the top-K KL loss and gradients over the kept positions only
+    [SKD sections 2-3: SE-KD with a selective LM head]."""
+    ent = oracle_entropy(hidden, W, chunk=chunk)
+    mask, idx, k = oracle_select_top_fraction(ent, num, den)
+    r = oracle_loss_grads(hidden, W, ids, tlogits, T=T, mask=mask, grad_loss=grad_loss,
+                          chunk=chunk)
+    r.update(entropy=ent, mask=mask, idx=idx, count=k)
+    return r
+
+
+def oracle_validate_topk(ids, tlogits, V):
+    """Cache checks named in [HF "operations"]: token id range and missing positions.
+
+    Returns (n_bad_id, n_empty_row, n_bad_logit): ids outside [0, V); rows whose
+    K logits are all -inf; logits that are NaN or +inf.
+    """
+    ids = np.asarray(ids)
+    tl = _f64(tlogits)
+    n_bad_id = int(np.count_nonzero((ids < 0) | (ids >= V)))
+    n_empty = int(np.count_nonzero(np.all(np.isneginf(tl), axis=1))) if tl.size else 0
+    n_bad_logit = int(np.count_nonzero(np.isnan(tl) | np.isposinf(tl)))
+    return n_bad_id, n_empty, n_bad_logit
