@@ -1,0 +1,276 @@
+"""Python binding of the fused chunked top-K KL distillation loss (HIP, gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library ``libkdtopk.so`` built from ``csrc/`` (see ``build.py``); PyTorch
+supplies device memory and the stream. The entry points carry the C names of
+``include/kd_topk_kl.h``. There is no CPU fallback: importing this package
+without the built library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "KD_BF16", "KD_F32", "KdError", "kd_problem", "lib",
+    "kd_abi_version", "kd_status_str", "kd_workspace_bytes",
+    "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_student_entropy",
+    "kd_select_top_fraction", "kd_validate_topk",
+    "kd_profile_enable", "kd_profile_read", "kd_profile_reset",
+    "KDTopKKL", "kd_topk_kl", "LIB_PATH",
+]
+
+KD_BF16, KD_F32 = 0, 1
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkdtopk.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m chunked_top_kl_amd.build` "
+        "(hipcc for gfx950). There is no fallback implementation.")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+
+class kd_problem(ctypes.Structure):
+    _fields_ = [("S", ctypes.c_int64), ("H", ctypes.c_int64), ("V", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("chunk", ctypes.c_int64),
+                ("temperature", ctypes.c_float), ("hw_dtype", ctypes.c_int32),
+                ("tl_dtype", ctypes.c_int32)]
+
+
+class kd_kernel_stat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64),
+                ("total_ms", ctypes.c_double)]
+
+
+_P = ctypes.c_void_p
+_PP = ctypes.POINTER(kd_problem)
+_I64P = ctypes.POINTER(ctypes.c_int64)
+lib.kd_abi_version.restype = ctypes.c_int
+lib.kd_status_str.restype = ctypes.c_char_p
+lib.kd_status_str.argtypes = [ctypes.c_int]
+lib.kd_workspace_bytes.restype = ctypes.c_size_t
+lib.kd_workspace_bytes.argtypes = [_PP]
+lib.kd_topk_kl_fwd.restype = ctypes.c_int
+lib.kd_topk_kl_fwd.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+lib.kd_topk_kl_bwd.restype = ctypes.c_int
+lib.kd_topk_kl_bwd.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P,
+                               ctypes.c_size_t, _P]
+lib.kd_student_entropy.restype = ctypes.c_int
+lib.kd_student_entropy.argtypes = [_PP, _P, _P, _P, _P, ctypes.c_size_t, _P]
+lib.kd_select_top_fraction.restype = ctypes.c_int
+lib.kd_select_top_fraction.argtypes = [_PP, _P, _P, _P, ctypes.c_int64, ctypes.c_int64, _P, _P,
+                                       _I64P, _P, ctypes.c_size_t, _P]
+lib.kd_validate_topk.restype = ctypes.c_int
+lib.kd_validate_topk.argtypes = [_PP, _P, _P, _I64P, _I64P, _I64P, _P, ctypes.c_size_t, _P]
+lib.kd_profile_enable.restype = ctypes.c_int
+lib.kd_profile_enable.argtypes = [ctypes.c_int]
+lib.kd_profile_read.restype = ctypes.c_int
+lib.kd_profile_read.argtypes = [ctypes.POINTER(kd_kernel_stat), ctypes.c_int]
+lib.kd_profile_reset.restype = ctypes.c_int
+
+
+class KdError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {kd_status_str(code)}")
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise KdError(code, where)
+
+
+def kd_abi_version() -> int:
+    return lib.kd_abi_version()
+
+
+def kd_status_str(code: int) -> str:
+    return lib.kd_status_str(int(code)).decode()
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return KD_BF16
+    if t == torch.float32:
+        return KD_F32
+    raise TypeError(f"unsupported dtype {t}: bfloat16 or float32 expected")
+
+
+def make_problem(S, H, V, K, chunk, T, hw_dtype, tl_dtype) -> kd_problem:
+    return kd_problem(int(S), int(H), int(V), int(K), int(chunk), float(T), int(hw_dtype),
+                      int(tl_dtype))
+
+
+def kd_workspace_bytes(problem: kd_problem) -> int:
+    return int(lib.kd_workspace_bytes(ctypes.byref(problem)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _problem_of(hidden, W, topk_ids, topk_logits, T, chunk):
+    if hidden.dim() != 2 or W.dim() != 2 or topk_ids.dim() != 2 or topk_logits.dim() != 2:
+        raise ValueError("hidden [S,H], W [V,H], topk_ids [S,K], topk_logits [S,K] expected")
+    S, H = hidden.shape
+    V = W.shape[0]
+    K = topk_ids.shape[1]
+    if W.shape[1] != H or topk_ids.shape[0] != S or tuple(topk_logits.shape) != (S, K):
+        raise ValueError("inconsistent shapes")
+    if hidden.dtype != W.dtype:
+        raise TypeError("hidden and W must share a dtype")
+    if topk_ids.dtype != torch.int32:
+        raise TypeError("topk_ids must be int32")
+    for t in (hidden, W, topk_ids, topk_logits):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous device tensors")
+    return make_problem(S, H, V, K, chunk, T, _dtype_code(hidden.dtype),
+                        _dtype_code(topk_logits.dtype))
+
+
+def _mask_arg(mask, S):
+    if mask is None:
+        return None
+    if mask.dtype not in (torch.uint8, torch.bool) or mask.numel() != S or not mask.is_contiguous():
+        raise ValueError("mask must be a contiguous uint8/bool tensor of S elements")
+    return mask
+
+
+def _workspace(problem, device, workspace):
+    need = kd_workspace_bytes(problem)
+    if need == 0:
+        _check(2, "kd_workspace_bytes")
+    if workspace is not None and workspace.numel() >= need and workspace.data_ptr() % 256 == 0:
+        return workspace
+    return torch.empty(need, dtype=torch.uint8, device=device)
+
+
+def kd_topk_kl_fwd(hidden, W, topk_ids, topk_logits, T=1.0, chunk=1024, mask=None,
+                   want_kl_rows=False, want_z_topk=False, workspace=None):
+    """Forward pass. Returns dict(loss [1] f32, lse [S] f32, kl_rows, z_topk)."""
+    p = _problem_of(hidden, W, topk_ids, topk_logits, T, chunk)
+    mask = _mask_arg(mask, p.S)
+    dev = hidden.device
+    ws = _workspace(p, dev, workspace)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(p.S, dtype=torch.float32, device=dev)
+    kl = torch.empty(p.S, dtype=torch.float32, device=dev) if want_kl_rows else None
+    zt = torch.empty(p.S, p.K, dtype=torch.float32, device=dev) if want_z_topk else None
+    _check(lib.kd_topk_kl_fwd(ctypes.byref(p), _ptr(hidden), _ptr(W), _ptr(topk_ids),
+                              _ptr(topk_logits), _ptr(mask), _ptr(loss), _ptr(lse), _ptr(kl),
+                              _ptr(zt), _ptr(ws), ws.numel(), _stream(dev)), "kd_topk_kl_fwd")
+    return dict(loss=loss, lse=lse, kl_rows=kl, z_topk=zt)
+
+
+def kd_topk_kl_bwd(hidden, W, topk_ids, topk_logits, lse, grad_loss, T=1.0, chunk=1024,
+                   mask=None, dW=None, accumulate_dW=False, workspace=None):
+    """Backward pass. Returns (dhidden [S,H] f32, dW [V,H] f32)."""
+    p = _problem_of(hidden, W, topk_ids, topk_logits, T, chunk)
+    mask = _mask_arg(mask, p.S)
+    dev = hidden.device
+    ws = _workspace(p, dev, workspace)
+    if grad_loss.dtype != torch.float32 or grad_loss.numel() != 1:
+        raise ValueError("grad_loss must be a float32 tensor of one element")
+    grad_loss = grad_loss.contiguous()
+    dh = torch.empty(p.S, p.H, dtype=torch.float32, device=dev)
+    if dW is None:
+        dW = torch.empty(p.V, p.H, dtype=torch.float32, device=dev)
+        accumulate_dW = False
+    elif dW.dtype != torch.float32 or tuple(dW.shape) != (p.V, p.H) or not dW.is_contiguous():
+        raise ValueError("dW must be a contiguous float32 [V,H] tensor")
+    _check(lib.kd_topk_kl_bwd(ctypes.byref(p), _ptr(hidden), _ptr(W), _ptr(topk_ids),
+                              _ptr(topk_logits), _ptr(mask), _ptr(lse), _ptr(grad_loss),
+                              _ptr(dh), _ptr(dW), 1 if accumulate_dW else 0, _ptr(ws),
+                              ws.numel(), _stream(dev)), "kd_topk_kl_bwd")
+    return dh, dW
+
+
+def kd_student_entropy(hidden, W, chunk=1024, workspace=None):
+    """Per-position entropy (nats) of softmax(hidden W^T), float64 [S]."""
+    S, H = hidden.shape
+    p = make_problem(S, H, W.shape[0], 1, chunk, 1.0, _dtype_code(hidden.dtype), KD_BF16)
+    dev = hidden.device
+    ws = _workspace(p, dev, workspace)
+    ent = torch.empty(S, dtype=torch.float64, device=dev)
+    _check(lib.kd_student_entropy(ctypes.byref(p), _ptr(hidden), _ptr(W), _ptr(ent), _ptr(ws),
+                                  ws.numel(), _stream(dev)), "kd_student_entropy")
+    return ent
+
+
+def kd_select_top_fraction(entropy, hidden, W, num=20, den=100, chunk=1024, workspace=None):
+    """Keep floor(num*S/den) highest-entropy positions. Returns (mask u8 [S], idx i32 [count], count)."""
+    S, H = hidden.shape
+    p = make_problem(S, H, W.shape[0], 1, chunk, 1.0, _dtype_code(hidden.dtype), KD_BF16)
+    dev = hidden.device
+    ws = _workspace(p, dev, workspace)
+    mask = torch.empty(S, dtype=torch.uint8, device=dev)
+    idx = torch.empty(max(S, 1), dtype=torch.int32, device=dev)
+    cnt = ctypes.c_int64(0)
+    _check(lib.kd_select_top_fraction(ctypes.byref(p), _ptr(hidden), _ptr(W), _ptr(entropy),
+                                      int(num), int(den), _ptr(mask), _ptr(idx), ctypes.byref(cnt),
+                                      _ptr(ws), ws.numel(), _stream(dev)),
+           "kd_select_top_fraction")
+    return mask, idx[: cnt.value], cnt.value
+
+
+def kd_validate_topk(topk_ids, topk_logits, V, workspace=None):
+    """Counts of (ids outside [0,V), all -inf rows, NaN/+inf logits)."""
+    S, K = topk_ids.shape
+    p = make_problem(S, 8, V, K, 1, 1.0, KD_BF16, _dtype_code(topk_logits.dtype))
+    dev = topk_ids.device
+    ws = _workspace(p, dev, workspace)
+    a, b, c = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(lib.kd_validate_topk(ctypes.byref(p), _ptr(topk_ids), _ptr(topk_logits),
+                                ctypes.byref(a), ctypes.byref(b), ctypes.byref(c), _ptr(ws),
+                                ws.numel(), _stream(dev)), "kd_validate_topk")
+    return a.value, b.value, c.value
+
+
+def kd_profile_enable(on=True):
+    _check(lib.kd_profile_enable(1 if on else 0), "kd_profile_enable")
+
+
+def kd_profile_reset():
+    _check(lib.kd_profile_reset(), "kd_profile_reset")
+
+
+def kd_profile_read(max_entries=64):
+    """Per-kernel {name: (launches, total_ms)} recorded while profiling was on."""
+    arr = (kd_kernel_stat * max_entries)()
+    n = lib.kd_profile_read(arr, max_entries)
+    if n < 0:
+        _check(-n, "kd_profile_read")
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n)}
+
+
+class KDTopKKL(torch.autograd.Function):
+    """loss = mean over valid positions of KL(p_teacher || softmax(hidden W^T / T))."""
+
+    @staticmethod
+    def forward(ctx, hidden, W, topk_ids, topk_logits, T, chunk, mask):
+        out = kd_topk_kl_fwd(hidden, W, topk_ids, topk_logits, T, chunk, mask)
+        ctx.save_for_backward(hidden, W, topk_ids, topk_logits, out["lse"], mask)
+        ctx.T, ctx.chunk, ctx.has_mask = T, chunk, mask is not None
+        return out["loss"][0]
+
+    @staticmethod
+    def backward(ctx, grad):
+        hidden, W, topk_ids, topk_logits, lse, mask = ctx.saved_tensors
+        g = grad.detach().reshape(1).to(torch.float32).contiguous()
+        dh, dW = kd_topk_kl_bwd(hidden, W, topk_ids, topk_logits, lse, g, ctx.T, ctx.chunk,
+                                mask if ctx.has_mask else None)
+        dh = dh.to(hidden.dtype) if ctx.needs_input_grad[0] else None
+        dW = dW.to(W.dtype) if ctx.needs_input_grad[1] else None
+        return dh, dW, None, None, None, None, None
+
+
+def kd_topk_kl(hidden, W, topk_ids, topk_logits, T=1.0, chunk=1024, mask=None):
+    """Differentiable fused chunked top-K KL loss (scalar)."""
+    return KDTopKKL.apply(hidden, W, topk_ids, topk_logits, float(T), int(chunk), mask)

@@ -1,0 +1,579 @@
+// C ABI of the fused chunked top-K KL loss: argument checks, workspace plan,
+// and the launch sequences of the forward, backward, entropy, selection and
+// validation entry points. Declarations and contracts: include/kd_topk_kl.h.
+#include "kd_topk_kl.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kd_common.hpp"
+#include "kd_kernels.hpp"
+
+namespace {
+
+using kd::ceil_div;
+using kd::round_up;
+
+// Work-group scheduling (splits, split-K) is planned for the MI355X's 256
+// compute units whatever the device reports, so that workspace sizes are a
+// pure function of the problem.
+constexpr int kCostCUs = 256;
+constexpr int64_t kMaxK = 4096;
+constexpr int64_t kMaxRows = int64_t(1) << 30;
+constexpr double kSelectEps = 2e-5;   // bound on |fp32-path entropy - fp64 entropy| (nats)
+constexpr int kRefineBlocks = 512;
+
+// ------------------------------------------------------------------ profiling
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t pool_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct Prof {
+  hipStream_t st;
+  const char* name;
+  hipEvent_t a = nullptr, b = nullptr;
+  Prof(const char* n, hipStream_t s) : st(s), name(n) {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    if (!g_prof_on) return;
+    a = pool_event();
+    b = pool_event();
+    if (a && b) hipEventRecord(a, st);
+  }
+  ~Prof() {
+    if (!a || !b) return;
+    hipEventRecord(b, st);
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    g_prof_recs.push_back({name, a, b});
+  }
+};
+
+// ------------------------------------------------------------------ device check
+int check_device() {
+  static std::mutex mu;
+  static std::map<int, bool> ok_by_dev;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KD_ERR_HIP;
+  std::lock_guard<std::mutex> g(mu);
+  auto it = ok_by_dev.find(dev);
+  if (it == ok_by_dev.end()) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return KD_ERR_HIP;
+    bool ok = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    it = ok_by_dev.emplace(dev, ok).first;
+  }
+  return it->second ? KD_OK : KD_ERR_ARCH;
+}
+
+// ------------------------------------------------------------------ problem checks
+int check_problem(const kd_problem* p) {
+  if (!p) return KD_ERR_NULL;
+  if (p->hw_dtype != KD_BF16 && p->hw_dtype != KD_F32) return KD_ERR_DTYPE;
+  if (p->tl_dtype != KD_BF16 && p->tl_dtype != KD_F32) return KD_ERR_DTYPE;
+  if (p->S < 0 || p->S > kMaxRows) return KD_ERR_SHAPE;
+  if (p->H <= 0 || p->V <= 0 || p->K <= 0) return KD_ERR_SHAPE;
+  if (p->K > p->V || p->K > kMaxK) return KD_ERR_SHAPE;
+  if (p->H % 8 != 0 || p->H > (int64_t(1) << 20)) return KD_ERR_SHAPE;
+  if (p->V > (int64_t(1) << 30)) return KD_ERR_SHAPE;
+  if (!(p->temperature > 0.0f) || !std::isfinite(p->temperature)) return KD_ERR_TEMPERATURE;
+  if (p->chunk <= 0) return KD_ERR_CHUNK;
+  return KD_OK;
+}
+
+// ------------------------------------------------------------------ workspace plan
+struct Layout {
+  size_t count, present, pos, idx, ids_s, p_s, korig_s, negH;
+  size_t pm, ps, pd, bsum;
+  size_t G, Xc, dhp;
+  size_t em, es, eu;
+  size_t band, refined, scal, dscal, rpart, counters;
+  size_t total;
+  int64_t C;          // rows per backward chunk (<= S, >= 1)
+  int64_t Vp;         // padded row length of the gradient tile
+  int64_t esz;
+};
+
+Layout plan(const kd_problem* p) {
+  Layout L;
+  std::memset(&L, 0, sizeof(L));
+  const int64_t S = p->S, H = p->H, V = p->V, K = p->K;
+  L.esz = p->hw_dtype == KD_F32 ? 4 : 2;
+  L.C = p->chunk < S ? p->chunk : (S > 0 ? S : 1);
+  L.Vp = round_up(V, 8);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (size_t)round_up((int64_t)bytes, 256);
+    return o;
+  };
+  const int64_t Sx = S > 0 ? S : 1;
+  L.count = take(64 * 4);
+  L.present = take(Sx);
+  L.pos = take(Sx * 4);
+  L.idx = take(Sx * 4);
+  L.ids_s = take(Sx * K * 4);
+  L.p_s = take(Sx * K * 4);
+  L.korig_s = take(Sx * K * 4);
+  L.negH = take(Sx * 4);
+  const int64_t pe = (int64_t)kd::sweep_grid(Sx, (int)V, kCostCUs) * kd::kTile;
+  L.pm = take(pe * 4);
+  L.ps = take(pe * 4);
+  L.pd = take(pe * 4);
+  L.bsum = take((ceil_div(Sx, 256) + 1) * 8);
+  L.G = take(L.C * L.Vp * L.esz);
+  L.Xc = take(L.C * H * L.esz);
+  int ksmax = 1;
+  for (int64_t r = kd::kTile; r < L.C + kd::kTile; r += kd::kTile) {
+    const int rows = (int)(r < L.C ? r : L.C);
+    const int ks = kd::dh_splits(rows, (int)V, (int)H, kCostCUs, p->hw_dtype == KD_F32);
+    if (ks > ksmax) ksmax = ks;
+  }
+  L.dhp = take((size_t)ksmax * L.C * H * 4);
+  L.em = take(pe * 4);
+  L.es = take(pe * 8);
+  L.eu = take(pe * 8);
+  L.band = take(Sx * 4);
+  L.refined = take(Sx * 8);
+  L.scal = take(16 * 4);
+  L.dscal = take(16 * 8);
+  L.rpart = take((size_t)4096 * kRefineBlocks * 3 * 8);
+  L.counters = take(4 * 8);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+int check_ws(const Layout& L, void* ws, size_t ws_bytes) {
+  if (!ws || ((uintptr_t)ws & 255u) != 0 || ws_bytes < L.total) return KD_ERR_WORKSPACE;
+  return KD_OK;
+}
+
+#define KD_HIP(x)                              \
+  do {                                         \
+    if ((x) != hipSuccess) return KD_ERR_HIP;  \
+  } while (0)
+
+// teacher prepass + compaction, shared by fwd and bwd
+int teacher_tables(const kd_problem* p, const Layout& L, const int32_t* ids, const void* tl,
+                   const uint8_t* mask, float* z_topk, void* ws, hipStream_t st) {
+  {
+    Prof pr("prepass", st);
+    KD_HIP(kd::launch_prepass(ids, tl, p->tl_dtype == KD_F32, p->S, (int)p->K, (int)p->V,
+                              p->temperature, at<int32_t>(ws, L.ids_s), at<float>(ws, L.p_s),
+                              at<int32_t>(ws, L.korig_s), at<float>(ws, L.negH),
+                              at<uint8_t>(ws, L.present), z_topk, st));
+  }
+  {
+    Prof pr("compact", st);
+    KD_HIP(kd::launch_compact(at<uint8_t>(ws, L.present), mask, p->S, at<int32_t>(ws, L.idx),
+                              at<int32_t>(ws, L.pos), at<int32_t>(ws, L.count), st));
+  }
+  return KD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kd_abi_version(void) { return KD_ABI_VERSION; }
+
+const char* kd_status_str(int s) {
+  switch (s) {
+    case KD_OK: return "KD_OK: success";
+    case KD_ERR_NULL: return "KD_ERR_NULL: a required pointer is NULL";
+    case KD_ERR_SHAPE: return "KD_ERR_SHAPE: invalid problem sizes";
+    case KD_ERR_DTYPE: return "KD_ERR_DTYPE: unknown dtype code";
+    case KD_ERR_TEMPERATURE: return "KD_ERR_TEMPERATURE: temperature must be finite and > 0";
+    case KD_ERR_CHUNK: return "KD_ERR_CHUNK: chunk must be > 0";
+    case KD_ERR_WORKSPACE: return "KD_ERR_WORKSPACE: workspace NULL, misaligned or too small";
+    case KD_ERR_BAD_ID: return "KD_ERR_BAD_ID: teacher id outside [0, V)";
+    case KD_ERR_HIP: return "KD_ERR_HIP: HIP runtime or launch failure";
+    case KD_ERR_ARCH: return "KD_ERR_ARCH: current device is not gfx950";
+    case KD_ERR_ARG: return "KD_ERR_ARG: invalid argument";
+    default: return "unknown kd_status";
+  }
+}
+
+size_t kd_workspace_bytes(const kd_problem* p) {
+  if (check_problem(p) != KD_OK) return 0;
+  return plan(p).total;
+}
+
+int kd_topk_kl_fwd(const kd_problem* p, const void* hidden, const void* W, const int32_t* ids,
+                   const void* tl, const uint8_t* mask, float* loss, float* lse, float* kl_rows,
+                   float* z_topk, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!W || !loss || (p->S > 0 && (!hidden || !ids || !tl || !lse))) return KD_ERR_NULL;
+  const Layout L = plan(p);
+  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = teacher_tables(p, L, ids, tl, mask, z_topk, ws, st))) return rc;
+  const int S = (int)p->S, V = (int)p->V, H = (int)p->H, K = (int)p->K;
+  const int f32 = p->hw_dtype == KD_F32;
+  if (S > 0) {
+    kd::SweepArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.W = (const char*)W;
+    a.ldw = (int64_t)H * L.esz;
+    a.X = (const char*)hidden;
+    a.ldx = (int64_t)H * L.esz;
+    a.x_row0 = 0;
+    const bool map = mask != nullptr;
+    a.idx = map ? at<int32_t>(ws, L.idx) : nullptr;
+    a.nrows_dev = map ? at<int32_t>(ws, L.count) : nullptr;
+    a.row_begin = 0;
+    a.row_cap = S;
+    a.V = V;
+    a.H = H;
+    a.K = K;
+    a.ncu = kCostCUs;
+    a.T = p->temperature;
+    a.ids_s = at<int32_t>(ws, L.ids_s);
+    a.p_s = at<float>(ws, L.p_s);
+    a.korig_s = at<int32_t>(ws, L.korig_s);
+    a.pm = at<float>(ws, L.pm);
+    a.ps = at<float>(ws, L.ps);
+    a.pd = at<float>(ws, L.pd);
+    a.z_topk = z_topk;
+    Prof pr("fwd_lse_gather", st);
+    KD_HIP(kd::launch_sweep(kd::kSweepFwd, f32, map, a, kd::sweep_grid(S, V, kCostCUs), st));
+  }
+  kd::CombineArgs c;
+  std::memset(&c, 0, sizeof(c));
+  c.S = S;
+  c.V = V;
+  c.ncu = kCostCUs;
+  c.K = K;
+  c.identity = mask == nullptr;
+  c.T = p->temperature;
+  c.pos = at<int32_t>(ws, L.pos);
+  c.nrows_dev = at<int32_t>(ws, L.count);
+  c.pm = at<float>(ws, L.pm);
+  c.ps = at<float>(ws, L.ps);
+  c.pd = at<float>(ws, L.pd);
+  c.negH = at<float>(ws, L.negH);
+  c.lse = lse;
+  c.kl_rows = kl_rows;
+  c.z_topk = z_topk;
+  c.block_sums = at<double>(ws, L.bsum);
+  c.loss = loss;
+  {
+    Prof pr("fwd_combine", st);
+    KD_HIP(kd::launch_fwd_combine(c, st));
+  }
+  return KD_OK;
+}
+
+int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const int32_t* ids,
+                   const void* tl, const uint8_t* mask, const float* lse, const float* grad_loss,
+                   float* dhidden, float* dW, int accumulate_dW, void* ws, size_t ws_bytes,
+                   void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!W || !dW || !grad_loss || (p->S > 0 && (!hidden || !ids || !tl || !lse || !dhidden)))
+    return KD_ERR_NULL;
+  if (accumulate_dW != 0 && accumulate_dW != 1) return KD_ERR_ARG;
+  const Layout L = plan(p);
+  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = teacher_tables(p, L, ids, tl, mask, nullptr, ws, st))) return rc;
+  const int S = (int)p->S, V = (int)p->V, H = (int)p->H, K = (int)p->K;
+  const int f32 = p->hw_dtype == KD_F32;
+  const int C = (int)L.C;
+  if (S > 0) {
+    Prof pr("zero_rows", st);
+    KD_HIP(kd::launch_zero_invalid_rows(at<int32_t>(ws, L.pos), S, H, dhidden, st));
+  }
+  const int64_t row_bytes = (int64_t)H * L.esz;
+  const int nchunks = S > 0 ? (int)ceil_div(S, C) : 1;
+  const int dgrid = kd::dh_grid(C, V, H, kCostCUs, f32);
+  const int sgrid = kd::sweep_grid(C, V, kCostCUs);
+  for (int ci = 0; ci < nchunks; ++ci) {
+    const int row_begin = ci * C;
+    if (S > 0) {
+      Prof pr("gather_rows", st);
+      KD_HIP(kd::launch_gather_rows((const char*)hidden, row_bytes, at<int32_t>(ws, L.idx),
+                                    at<int32_t>(ws, L.count), row_begin, C, row_bytes,
+                                    at<char>(ws, L.Xc), st));
+    }
+    if (S > 0) {
+      kd::SweepArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.W = (const char*)W;
+      a.ldw = row_bytes;
+      a.X = at<char>(ws, L.Xc);
+      a.ldx = row_bytes;
+      a.x_row0 = 0;
+      a.idx = at<int32_t>(ws, L.idx);
+      a.nrows_dev = at<int32_t>(ws, L.count);
+      a.row_begin = row_begin;
+      a.row_cap = C;
+      a.V = V;
+      a.H = H;
+      a.K = K;
+      a.ncu = kCostCUs;
+      a.T = p->temperature;
+      a.ids_s = at<int32_t>(ws, L.ids_s);
+      a.p_s = at<float>(ws, L.p_s);
+      a.korig_s = at<int32_t>(ws, L.korig_s);
+      a.lse = lse;
+      a.grad_loss = grad_loss;
+      a.G = at<char>(ws, L.G);
+      a.ldg = L.Vp * L.esz;
+      Prof pr("bwd_grad_tile", st);
+      KD_HIP(kd::launch_sweep(kd::kSweepBwdG, f32, 0, a, sgrid, st));
+    }
+    if (S > 0) {
+      kd::DhArgs d;
+      d.G = at<char>(ws, L.G);
+      d.ldg = L.Vp * L.esz;
+      d.W = (const char*)W;
+      d.ldw = row_bytes;
+      d.nrows_dev = at<int32_t>(ws, L.count);
+      d.row_begin = row_begin;
+      d.row_cap = C;
+      d.V = V;
+      d.H = H;
+      d.ncu = kCostCUs;
+      d.part = at<float>(ws, L.dhp);
+      {
+        Prof pr("bwd_dhidden", st);
+        KD_HIP(kd::launch_dh(f32, d, dgrid, st));
+      }
+      kd::DhReduceArgs r;
+      r.part = at<float>(ws, L.dhp);
+      r.idx = at<int32_t>(ws, L.idx);
+      r.nrows_dev = at<int32_t>(ws, L.count);
+      r.row_begin = row_begin;
+      r.row_cap = C;
+      r.V = V;
+      r.H = H;
+      r.ncu = kCostCUs;
+      r.dH = dhidden;
+      Prof pr("bwd_dhidden_reduce", st);
+      KD_HIP(kd::launch_dh_reduce(r, f32, st));
+    }
+    kd::DwArgs w;
+    w.G = at<char>(ws, L.G);
+    w.ldg = L.Vp * L.esz;
+    w.g_mn_bytes = L.Vp * L.esz;
+    w.Xc = at<char>(ws, L.Xc);
+    w.ldx = row_bytes;
+    w.nrows_dev = at<int32_t>(ws, L.count);
+    w.row_begin = row_begin;
+    w.row_cap = C;
+    w.V = V;
+    w.H = H;
+    w.beta_first = accumulate_dW;
+    w.dW = dW;
+    Prof pr("bwd_dw", st);
+    KD_HIP(kd::launch_dw(f32, w, st));
+  }
+  return KD_OK;
+}
+
+int kd_student_entropy(const kd_problem* p, const void* hidden, const void* W, double* entropy,
+                       void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!W || (p->S > 0 && (!hidden || !entropy))) return KD_ERR_NULL;
+  const Layout L = plan(p);
+  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const int S = (int)p->S, V = (int)p->V, H = (int)p->H;
+  if (S == 0) return KD_OK;
+  kd::SweepArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.W = (const char*)W;
+  a.ldw = (int64_t)H * L.esz;
+  a.X = (const char*)hidden;
+  a.ldx = (int64_t)H * L.esz;
+  a.row_begin = 0;
+  a.row_cap = S;
+  a.V = V;
+  a.H = H;
+  a.K = (int)p->K;
+  a.ncu = kCostCUs;
+  a.T = 1.0f;
+  a.em = at<float>(ws, L.em);
+  a.es = at<double>(ws, L.es);
+  a.eu = at<double>(ws, L.eu);
+  {
+    Prof pr("entropy_sweep", st);
+    KD_HIP(kd::launch_sweep(kd::kSweepEnt, p->hw_dtype == KD_F32, 0, a,
+                            kd::sweep_grid(S, V, kCostCUs), st));
+  }
+  kd::EntCombineArgs c;
+  c.S = S;
+  c.V = V;
+  c.ncu = kCostCUs;
+  c.em = a.em;
+  c.es = a.es;
+  c.eu = a.eu;
+  c.entropy = entropy;
+  Prof pr("entropy_combine", st);
+  KD_HIP(kd::launch_ent_combine(c, st));
+  return KD_OK;
+}
+
+int kd_select_top_fraction(const kd_problem* p, const void* hidden, const void* W,
+                           const double* entropy, int64_t num, int64_t den, uint8_t* mask_out,
+                           int32_t* idx_out, int64_t* count_out, void* ws, size_t ws_bytes,
+                           void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!count_out || !W || (p->S > 0 && (!hidden || !entropy || !mask_out))) return KD_ERR_NULL;
+  if (den <= 0 || num < 0 || num > den) return KD_ERR_ARG;
+  const Layout L = plan(p);
+  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t S = p->S;
+  const int64_t k = (num * S) / den;
+  *count_out = 0;
+  if (S == 0) return KD_OK;
+  kd::SelectWs w;
+  w.keys = nullptr;
+  w.band = at<int32_t>(ws, L.band);
+  w.refined = at<double>(ws, L.refined);
+  w.scal = at<int32_t>(ws, L.scal);
+  w.dscal = at<double>(ws, L.dscal);
+  w.rpart = at<double>(ws, L.rpart);
+  w.hist = nullptr;
+  {
+    Prof pr("select_threshold", st);
+    KD_HIP(kd::launch_select_threshold(entropy, S, k, kSelectEps, w, st));
+  }
+  int32_t n_band = 0;
+  KD_HIP(hipMemcpyAsync(&n_band, w.scal, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  KD_HIP(hipStreamSynchronize(st));
+  const int f32 = p->hw_dtype == KD_F32;
+  const int64_t ld = p->H * L.esz;
+  if (n_band > 0 && n_band <= 4096) {
+    const int R = kd::refine_rows_per_pass((int)p->H, f32);
+    const int nblk = (int)std::min<int64_t>(kRefineBlocks, ceil_div(p->V, 64));
+    for (int off = 0; off < n_band; off += R) {
+      const int n = std::min(R, n_band - off);
+      Prof pr("select_refine_fp64", st);
+      KD_HIP(kd::launch_refine(f32, (const char*)hidden, ld, (const char*)W, ld, (int)p->V,
+                               (int)p->H, w, off, n, nblk, st));
+    }
+    {
+      Prof pr("select_final", st);
+      KD_HIP(kd::launch_select_final(entropy, S, k, w, n_band, nblk, mask_out, idx_out, st));
+    }
+  } else {
+    Prof pr("select_final", st);
+    KD_HIP(kd::launch_select_final(entropy, S, k, w, n_band, 1, mask_out, idx_out, st));
+  }
+  int32_t cnt = 0;
+  KD_HIP(hipMemcpyAsync(&cnt, w.scal + 2, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  KD_HIP(hipStreamSynchronize(st));
+  *count_out = cnt;
+  return KD_OK;
+}
+
+int kd_validate_topk(const kd_problem* p, const int32_t* ids, const void* tl, int64_t* n_bad_id,
+                     int64_t* n_empty_row, int64_t* n_bad_logit, void* ws, size_t ws_bytes,
+                     void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!n_bad_id || !n_empty_row || !n_bad_logit || (p->S > 0 && (!ids || !tl))) return KD_ERR_NULL;
+  const Layout L = plan(p);
+  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  unsigned long long* cnt = at<unsigned long long>(ws, L.counters);
+  {
+    Prof pr("validate", st);
+    KD_HIP(kd::launch_validate(ids, tl, p->tl_dtype == KD_F32, p->S, (int)p->K, (int)p->V, cnt,
+                               st));
+  }
+  unsigned long long h[3] = {0, 0, 0};
+  KD_HIP(hipMemcpyAsync(h, cnt, sizeof(h), hipMemcpyDeviceToHost, st));
+  KD_HIP(hipStreamSynchronize(st));
+  *n_bad_id = (int64_t)h[0];
+  *n_empty_row = (int64_t)h[1];
+  *n_bad_logit = (int64_t)h[2];
+  return KD_OK;
+}
+
+int kd_profile_enable(int on) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  g_prof_on = on != 0;
+  return KD_OK;
+}
+
+int kd_profile_reset(void) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  for (auto& r : g_prof_recs) {
+    g_event_pool.push_back(r.a);
+    g_event_pool.push_back(r.b);
+  }
+  g_prof_recs.clear();
+  return KD_OK;
+}
+
+int kd_profile_read(kd_kernel_stat* out, int max_entries) {
+  std::vector<ProfRec> recs;
+  {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    recs = g_prof_recs;
+  }
+  std::vector<std::string> names;
+  std::map<std::string, std::pair<int64_t, double>> agg;
+  for (auto& r : recs) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return -KD_ERR_HIP;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return -KD_ERR_HIP;
+    auto it = agg.find(r.name);
+    if (it == agg.end()) {
+      names.push_back(r.name);
+      it = agg.emplace(r.name, std::make_pair((int64_t)0, 0.0)).first;
+    }
+    it->second.first += 1;
+    it->second.second += ms;
+  }
+  int n = 0;
+  for (auto& nm : names) {
+    if (n >= max_entries || !out) break;
+    std::memset(&out[n], 0, sizeof(kd_kernel_stat));
+    std::strncpy(out[n].name, nm.c_str(), sizeof(out[n].name) - 1);
+    out[n].launches = agg[nm].first;
+    out[n].total_ms = agg[nm].second;
+    ++n;
+  }
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,233 @@
+// Backward contractions of one chunk ("backward recomputes the chunk"):
+//   dHidden rows = G W        (K = vocabulary, split-K with a fixed-order reduce)
+//   dW          (+)= G^T X_c  (K = chunk rows, fp32 read-modify-write of dW)
+// plus the small row kernels around them (gather of the chunk's hidden rows,
+// zero rows for positions that take no part).
+#include "kd_gemm_core.hpp"
+#include "kd_kernels.hpp"
+
+namespace kd {
+
+// rows of this chunk actually present (device count N)
+__device__ inline int chunk_rows(const int32_t* nrows_dev, int row_begin, int row_cap) {
+  int n = *nrows_dev - row_begin;
+  return n < row_cap ? n : row_cap;
+}
+
+// ---------------------------------------------------------------------------
+// dHidden partials: part[split][r][h] = sum_{v in split} G[r][v] W[v][h]
+//   M = chunk rows (A = G, [rows][Vp], K contiguous), N = h (B = W viewed as
+//   [K = V rows][N = H], MN contiguous -> transposing loader).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  const int rows = chunk_rows(a.nrows_dev, a.row_begin, a.row_cap);
+  if (rows <= 0) return;
+  constexpr int esz = Elem<T>::size, kper = Elem<T>::per_step;
+  const int mt = (int)ceil_div(rows, kTile), nt = (int)ceil_div(a.H, kTile);
+  const int nks_total = (int)ceil_div(a.V, kper);
+  const int ks = splitk_factor(mt * nt, nks_total, a.ncu);
+  const int total = mt * nt * ks;
+  if ((int)blockIdx.x >= total) return;
+  const int L = xcd_remap(blockIdx.x, total);
+  const int split = L / (mt * nt), rem = L % (mt * nt);
+  const int n = rem / mt, m = rem % mt;
+  const int per = (int)ceil_div(nks_total, ks);
+  const int kbeg = split * per;
+  const int kend = (kbeg + per < nks_total) ? kbeg + per : nks_total;
+  const int nk = kend - kbeg;
+
+  LoaderKC la;
+  la.init(a.G + (int64_t)m * kTile * a.ldg, a.ldg, rows - m * kTile, (int64_t)kbeg * kStepBytes,
+          (int64_t)a.V * esz);
+  LoaderKS<T> lb;
+  lb.init(a.W + (int64_t)n * kTile * esz, a.ldw, kbeg * kper, a.V,
+          (int64_t)(a.H - n * kTile) * esz);
+  floatx16 acc[4][4];
+  gemm_mainloop<T>(acc, la, lb, nk > 0 ? nk : 0, lds);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  float* part = a.part + (int64_t)split * a.row_cap * a.H;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int h = n * kTile + wn * 128 + j * 32 + (lane & 31);
+      if (h >= a.H) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m * kTile + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < rows) part[(int64_t)row * a.H + h] = acc[i][j][r];
+      }
+    }
+}
+
+__host__ __device__ int dh_splits(int rows, int V, int H, int ncu, int f32) {
+  const int kper = f32 ? Elem<float>::per_step : Elem<__bf16>::per_step;
+  const int mt = (int)ceil_div(rows, kTile), nt = (int)ceil_div(H, kTile);
+  return splitk_factor(mt * nt, (int)ceil_div(V, kper), ncu);
+}
+
+int dh_grid(int row_cap, int V, int H, int ncu, int f32) {
+  int best = 1;
+  for (int r = kTile; r < row_cap + kTile; r += kTile) {
+    const int rows = r < row_cap ? r : row_cap;
+    const int mt = (int)ceil_div(rows, kTile), nt = (int)ceil_div(H, kTile);
+    const int g = mt * nt * dh_splits(rows, V, H, ncu, f32);
+    if (g > best) best = g;
+  }
+  return best;
+}
+
+hipError_t launch_dh(int f32, const DhArgs& a, int grid, hipStream_t st) {
+  if (grid <= 0) return hipSuccess;
+  if (f32) hipLaunchKernelGGL(dh_kernel<float>, dim3(grid), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL(dh_kernel<__bf16>, dim3(grid), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+// dHidden[idx[row_begin + r]][h] = sum over splits (fixed order) of part[s][r][h]
+__global__ __launch_bounds__(256) void dh_reduce_kernel(DhReduceArgs a, int ks_f32) {
+  const int rows = chunk_rows(a.nrows_dev, a.row_begin, a.row_cap);
+  if (rows <= 0) return;
+  const int ks = dh_splits(rows, a.V, a.H, a.ncu, ks_f32);
+  const int h4 = a.H / 4;
+  const int64_t total = (int64_t)rows * h4;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * 256) {
+    const int r = (int)(q / h4), c = (int)(q % h4);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < ks; ++s) {
+      const float4 v = *(const float4*)(a.part + ((int64_t)s * a.row_cap + r) * a.H + 4 * c);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    const int orow = a.idx[a.row_begin + r];
+    *(float4*)(a.dH + (int64_t)orow * a.H + 4 * c) = acc;
+  }
+}
+
+hipError_t launch_dh_reduce(const DhReduceArgs& a, int f32, hipStream_t st) {
+  const int64_t work = (int64_t)a.row_cap * (a.H / 4);
+  int grid = (int)ceil_div(work, 256);
+  if (grid > 4096) grid = 4096;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(dh_reduce_kernel, dim3(grid), dim3(256), 0, st, a, f32);
+  return hipGetLastError();
+}
+
+// dH rows of positions that take no part are zero
+__global__ __launch_bounds__(256) void zero_rows_kernel(const int32_t* pos, int64_t S, int H,
+                                                        float* dH) {
+  const int h4 = H / 4;
+  const int64_t total = S * h4;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * 256) {
+    const int64_t t = q / h4;
+    if (pos[t] < 0) *(float4*)(dH + t * H + 4 * (q % h4)) = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+hipError_t launch_zero_invalid_rows(const int32_t* pos, int64_t S, int H, float* dH,
+                                    hipStream_t st) {
+  if (S <= 0) return hipSuccess;
+  int64_t grid = ceil_div(S * (H / 4), 256);
+  if (grid > 8192) grid = 8192;
+  hipLaunchKernelGGL(zero_rows_kernel, dim3((int)grid), dim3(256), 0, st, pos, S, H, dH);
+  return hipGetLastError();
+}
+
+// out[r] = X[idx[row_begin + r]] for the chunk's rows (16-byte copies)
+__global__ __launch_bounds__(256) void gather_rows_kernel(const char* X, int64_t ldx,
+                                                          const int32_t* idx,
+                                                          const int32_t* nrows_dev, int row_begin,
+                                                          int row_cap, int64_t row_bytes,
+                                                          char* out) {
+  const int rows = chunk_rows(nrows_dev, row_begin, row_cap);
+  if (rows <= 0) return;
+  const int64_t g = row_bytes / 16;
+  const int64_t total = (int64_t)rows * g;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * 256) {
+    const int64_t r = q / g, c = q % g;
+    const int orow = idx[row_begin + r];
+    *(uint4*)(out + r * row_bytes + c * 16) = *(const uint4*)(X + (int64_t)orow * ldx + c * 16);
+  }
+}
+
+hipError_t launch_gather_rows(const char* X, int64_t ldx, const int32_t* idx,
+                              const int32_t* nrows_dev, int row_begin, int row_cap,
+                              int64_t row_bytes, char* out, hipStream_t st) {
+  int64_t grid = ceil_div((int64_t)row_cap * (row_bytes / 16), 256);
+  if (grid > 8192) grid = 8192;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((int)grid), dim3(256), 0, st, X, ldx, idx,
+                     nrows_dev, row_begin, row_cap, row_bytes, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// dW[v][h] (+)= sum_r G[r][v] X_c[r][h]
+//   M = v (A = G^T: G is [K = rows][MN = Vp]), N = h (B = X_c: [K = rows][N = H]);
+//   both operands go through the transposing loader. Chunk 0 with
+//   beta_first = 0 overwrites dW (and writes zeros when the chunk is empty);
+//   later chunks add, and return at once when they hold no rows.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256, 1) void dw_kernel(DwArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  int rows = chunk_rows(a.nrows_dev, a.row_begin, a.row_cap);
+  if (rows <= 0) {
+    if (a.row_begin > 0) return;
+    rows = 0;
+  }
+  constexpr int esz = Elem<T>::size, kper = Elem<T>::per_step;
+  const int mt = (int)ceil_div(a.V, kTile), nt = (int)ceil_div(a.H, kTile);
+  const int total = mt * nt;
+  if ((int)blockIdx.x >= total) return;
+  // grouped raster: 4 vocabulary tiles x all h tiles per group
+  const int L = xcd_remap(blockIdx.x, total);
+  const int GM = 4;
+  const int group = L / (GM * nt);
+  const int first_m = group * GM;
+  const int gsz = (mt - first_m) < GM ? (mt - first_m) : GM;
+  const int in = L % (GM * nt);
+  const int m = first_m + in % gsz, n = in / gsz;
+
+  LoaderKS<T> la;
+  la.init(a.G + (int64_t)m * kTile * esz, a.ldg, 0, rows, a.g_mn_bytes - (int64_t)m * kTile * esz);
+  LoaderKS<T> lb;
+  lb.init(a.Xc + (int64_t)n * kTile * esz, a.ldx, 0, rows, (int64_t)(a.H - n * kTile) * esz);
+  floatx16 acc[4][4];
+  gemm_mainloop<T>(acc, la, lb, (int)ceil_div(rows, kper), lds);
+
+  const bool beta = (a.row_begin > 0) || a.beta_first;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int h = n * kTile + wn * 128 + j * 32 + (lane & 31);
+    if (h >= a.H) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = m * kTile + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (v < a.V) {
+          float* p = a.dW + (int64_t)v * a.H + h;
+          *p = beta ? *p + acc[i][j][r] : acc[i][j][r];
+        }
+      }
+  }
+}
+
+hipError_t launch_dw(int f32, const DwArgs& a, hipStream_t st) {
+  const int grid = (int)(ceil_div(a.V, kTile) * ceil_div(a.H, kTile));
+  if (f32) hipLaunchKernelGGL(dw_kernel<float>, dim3(grid), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL(dw_kernel<__bf16>, dim3(grid), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace kd

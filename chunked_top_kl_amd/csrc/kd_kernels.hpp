@@ -1,0 +1,120 @@
+// Kernel argument blocks and host launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kd {
+
+enum SweepKind { kSweepFwd = 0, kSweepBwdG = 1, kSweepEnt = 2 };
+
+// Vocabulary-sweep projection (forward LSE + gather, backward gradient tile,
+// entropy). Rows are "launch rows" r in [0, rows): compacted row
+// row_begin + r, original row idx[row_begin + r] (identity when idx is NULL).
+struct SweepArgs {
+  const char* W; int64_t ldw;         // [V,H] storage, row stride in bytes
+  const char* X; int64_t ldx;         // token rows: hidden [S,H] (row map) or a gathered chunk
+  int x_row0;                         // row of X holding launch row 0 (when X is read without a map)
+  const int32_t* idx;                 // compacted -> original row (teacher tables, lse), or NULL
+  const int32_t* nrows_dev;           // device row count N, or NULL (use row_cap)
+  int row_begin, row_cap;             // this launch covers compacted rows [row_begin, row_begin+row_cap) ∩ [0,N)
+  int V, H, K, ncu;
+  float T;
+  // teacher tables from the prepass, indexed by original row
+  const int32_t* ids_s; const float* p_s; const int32_t* korig_s;
+  // forward outputs: partials [split][r], split stride = (token tiles) * 256
+  float* pm; float* ps; float* pd;
+  float* z_topk;                      // [S,K] or NULL
+  // backward
+  const float* lse; const float* grad_loss;
+  char* G; int64_t ldg;               // gradient tile [row_cap, Vp], bytes per row
+  // entropy partials
+  float* em; double* es; double* eu;
+};
+
+struct CombineArgs {
+  int S, V, ncu, K;
+  int identity;                       // forward ran over all S rows in order (no row map)
+  float T;
+  const int32_t* pos; const int32_t* nrows_dev;
+  const float* pm; const float* ps; const float* pd;
+  const float* negH;
+  float* lse; float* kl_rows; float* z_topk;
+  double* block_sums;
+  float* loss;
+};
+
+struct EntCombineArgs {
+  int S, V, ncu;
+  const float* em; const double* es; const double* eu;
+  double* entropy;
+};
+
+struct DhArgs {
+  const char* G; int64_t ldg;         // [rows, Vp]
+  const char* W; int64_t ldw;         // [V, H]
+  const int32_t* nrows_dev;
+  int row_begin, row_cap, V, H, ncu;
+  float* part;                        // [split][row_cap][H] fp32
+};
+
+struct DhReduceArgs {
+  const float* part; const int32_t* idx; const int32_t* nrows_dev;
+  int row_begin, row_cap, V, H, ncu;
+  float* dH;
+};
+
+struct DwArgs {
+  const char* G; int64_t ldg; int64_t g_mn_bytes;   // G: [rows, Vp]
+  const char* Xc; int64_t ldx;                      // gathered hidden rows [rows, H]
+  const int32_t* nrows_dev;
+  int row_begin, row_cap, V, H, beta_first;
+  float* dW;
+};
+
+// ------------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error.
+hipError_t launch_prepass(const int32_t* ids, const void* tl, int tl_f32, int64_t S, int K, int V,
+                          float T, int32_t* ids_s, float* p_s, int32_t* korig_s, float* negH,
+                          uint8_t* present, float* z_topk, hipStream_t st);
+hipError_t launch_compact(const uint8_t* present, const uint8_t* mask, int64_t S, int32_t* idx,
+                          int32_t* pos, int32_t* count, hipStream_t st);
+hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid, hipStream_t st);
+int sweep_grid(int64_t rows_max, int V, int ncu);
+hipError_t launch_fwd_combine(const CombineArgs& a, hipStream_t st);
+hipError_t launch_ent_combine(const EntCombineArgs& a, hipStream_t st);
+hipError_t launch_gather_rows(const char* X, int64_t ldx, const int32_t* idx,
+                              const int32_t* nrows_dev, int row_begin, int row_cap,
+                              int64_t row_bytes, char* out, hipStream_t st);
+hipError_t launch_zero_invalid_rows(const int32_t* pos, int64_t S, int H, float* dH,
+                                    hipStream_t st);
+hipError_t launch_dh(int f32, const DhArgs& a, int grid, hipStream_t st);
+int dh_grid(int row_cap, int V, int H, int ncu, int f32);
+__host__ __device__ int dh_splits(int rows, int V, int H, int ncu, int f32);
+hipError_t launch_dh_reduce(const DhReduceArgs& a, int f32, hipStream_t st);
+hipError_t launch_dw(int f32, const DwArgs& a, hipStream_t st);
+hipError_t launch_validate(const int32_t* ids, const void* tl, int tl_f32, int64_t S, int K,
+                           int V, unsigned long long* counters, hipStream_t st);
+hipError_t launch_fill_u8(uint8_t* p, uint8_t v, int64_t n, hipStream_t st);
+
+// selection
+struct SelectWs {
+  unsigned long long* keys;   // [S]
+  int32_t* band;              // [S] band rows
+  double* refined;            // [S] fp64 entropies of band rows (band order)
+  int32_t* scal;              // small scalars: [0]=n_band [1]=n_above [2]=k
+  double* dscal;              // [0]=threshold value
+  double* rpart;              // refine partials [cap][nblk][3]
+  unsigned int* hist;         // scratch
+};
+hipError_t launch_select_threshold(const double* entropy, int64_t S, int64_t k, double eps,
+                                   const SelectWs& w, hipStream_t st);
+hipError_t launch_refine(int f32, const char* X, int64_t ldx, const char* W, int64_t ldw, int V,
+                         int H, const SelectWs& w, int band_off, int band_n, int nblk,
+                         hipStream_t st);
+int refine_rows_per_pass(int H, int f32);
+hipError_t launch_select_final(const double* entropy, int64_t S, int64_t k, const SelectWs& w,
+                               int n_band, int nblk, uint8_t* mask, int32_t* idx_out,
+                               hipStream_t st);
+
+}  // namespace kd

@@ -1,0 +1,226 @@
+// Teacher-side prepass, row compaction and cache validation.
+//
+// Prepass, one wave per position ("offline top-K logits": K cached ids and
+// logits per position, softened by the stored temperature):
+//   p_k   = softmax over the row's usable entries of l_k / T
+//   negH  = sum_k p_k log p_k  (0 log 0 = 0)
+//   (id, p, k) sorted by id ascending, ties by k, so that the projection
+//   epilogue can walk each row's ids in vocabulary order.
+// An entry is usable when its id lies in [0, V) and its logit is finite;
+// -inf entries get p = 0; an id outside [0, V) is never dereferenced later
+// (it is stored as 0x7FFFFFFF, past every vocabulary tile). A row takes part
+// ("present") when it has a usable entry and no NaN / +inf logit.
+#include "kd_common.hpp"
+#include "kd_kernels.hpp"
+
+namespace kd {
+
+__device__ inline float load_logit(const void* tl, int tl_f32, int64_t i) {
+  return tl_f32 ? ((const float*)tl)[i] : bf16_to_f32(((const uint16_t*)tl)[i]);
+}
+
+__global__ void prepass_kernel(const int32_t* ids, const void* tl, int tl_f32, int64_t S, int K,
+                               int V, float invT, int n2, int32_t* ids_s, float* p_s,
+                               int32_t* korig_s, float* negH_out, uint8_t* present,
+                               float* z_topk) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int rpb = blockDim.x >> 6;
+  unsigned long long* key = (unsigned long long*)smem + (int64_t)wv * n2;
+  float* pv = (float*)(smem + (int64_t)rpb * n2 * 8) + (int64_t)wv * n2;
+  const int64_t t = (int64_t)blockIdx.x * rpb + wv;
+  const bool live = t < S;
+  const int64_t base = (live ? t : 0) * K;
+
+  // 1. row max over usable entries, flags
+  float mx = -INFINITY;
+  int bad = 0;
+  for (int k = lane; k < K; k += 64) {
+    const int id = live ? ids[base + k] : 0;
+    const float l = live ? load_logit(tl, tl_f32, base + k) : -INFINITY;
+    if (isnan(l) || l == INFINITY) bad = 1;
+    if (id >= 0 && id < V && isfinite(l)) mx = fmaxf(mx, l * invT);
+  }
+  mx = wave_max(mx);
+  bad = (int)wave_sum((float)bad) > 0;
+  // 2. normaliser
+  float z = 0.0f;
+  if (mx != -INFINITY) {
+    for (int k = lane; k < K; k += 64) {
+      const int id = live ? ids[base + k] : 0;
+      const float l = live ? load_logit(tl, tl_f32, base + k) : -INFINITY;
+      if (id >= 0 && id < V && isfinite(l)) z += __expf(l * invT - mx);
+    }
+  }
+  z = wave_sum(z);
+  const float logz = __logf(z);
+  // 3. probabilities, entropy term, sort keys
+  float nh = 0.0f;
+  for (int k = lane; k < n2; k += 64) {
+    unsigned long long kk = ~0ull;
+    float p = 0.0f;
+    if (k < K && live) {
+      const int id = ids[base + k];
+      const float l = load_logit(tl, tl_f32, base + k);
+      const bool inr = id >= 0 && id < V;
+      if (inr && isfinite(l) && mx != -INFINITY) {
+        const float lp = (l * invT - mx) - logz;
+        p = __expf(lp);
+        if (p > 0.0f) nh += p * lp;
+      }
+      const uint32_t kid = inr ? (uint32_t)id : 0x7FFFFFFFu;
+      kk = ((unsigned long long)kid << 32) | (uint32_t)k;
+      if (z_topk) z_topk[base + k] = __int_as_float(0x7FC00000);  // NaN until gathered
+    }
+    key[k] = kk;
+    pv[k] = p;
+  }
+  nh = wave_sum(nh);
+  __syncthreads();
+  // 4. bitonic sort of (key, p) ascending by key (each wave its own row)
+  for (int kk = 2; kk <= n2; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int i = lane; i < n2; i += 64) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const bool up = (i & kk) == 0;
+          const unsigned long long a = key[i], b = key[ixj];
+          if ((a > b) == up) {
+            key[i] = b;
+            key[ixj] = a;
+            const float tp = pv[i];
+            pv[i] = pv[ixj];
+            pv[ixj] = tp;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (!live) return;
+  for (int k = lane; k < K; k += 64) {
+    const unsigned long long kk = key[k];
+    ids_s[base + k] = (int32_t)(kk >> 32);
+    p_s[base + k] = pv[k];
+    korig_s[base + k] = (int32_t)(kk & 0xFFFFFFFFu);
+  }
+  if (lane == 0) {
+    negH_out[t] = nh;
+    present[t] = (!bad && mx != -INFINITY) ? 1 : 0;
+  }
+}
+
+hipError_t launch_prepass(const int32_t* ids, const void* tl, int tl_f32, int64_t S, int K, int V,
+                          float T, int32_t* ids_s, float* p_s, int32_t* korig_s, float* negH,
+                          uint8_t* present, float* z_topk, hipStream_t st) {
+  if (S <= 0) return hipSuccess;
+  int n2 = 1;
+  while (n2 < K) n2 <<= 1;
+  const int rpb = n2 <= 1024 ? 4 : 1;
+  const size_t lds = (size_t)rpb * n2 * 12;
+  const int64_t grid = ceil_div(S, rpb);
+  hipLaunchKernelGGL(prepass_kernel, dim3((unsigned)grid), dim3(64 * rpb), lds, st, ids, tl, tl_f32,
+                     S, K, V, 1.0f / T, n2, ids_s, p_s, korig_s, negH, present, z_topk);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Compaction: valid_t = present_t && (mask_t != 0 or no mask). idx[r] lists
+// the valid positions in ascending order, pos[t] = r or -1, count = N.
+// One work-group of 1024 threads; each thread owns a contiguous segment.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* present, const uint8_t* mask,
+                                                       int64_t S, int32_t* idx, int32_t* pos,
+                                                       int32_t* count) {
+  __shared__ int32_t sc[1024];
+  const int tid = threadIdx.x;
+  const int64_t seg = ceil_div(S, 1024);
+  const int64_t t0 = tid * seg;
+  const int64_t t1 = (t0 + seg < S) ? t0 + seg : S;
+  int c = 0;
+  for (int64_t t = t0; t < t1; ++t) c += (present[t] && (!mask || mask[t])) ? 1 : 0;
+  sc[tid] = c;
+  __syncthreads();
+  // Hillis-Steele inclusive scan
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? sc[tid - o] : 0;
+    __syncthreads();
+    sc[tid] += v;
+    __syncthreads();
+  }
+  int off = sc[tid] - c;
+  for (int64_t t = t0; t < t1; ++t) {
+    if (present[t] && (!mask || mask[t])) {
+      idx[off] = (int32_t)t;
+      pos[t] = off++;
+    } else {
+      pos[t] = -1;
+    }
+  }
+  if (tid == 1023) count[0] = sc[1023];
+}
+
+hipError_t launch_compact(const uint8_t* present, const uint8_t* mask, int64_t S, int32_t* idx,
+                          int32_t* pos, int32_t* count, hipStream_t st) {
+  hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, st, present, mask, S, idx, pos, count);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Validation counters: [0] ids outside [0, V), [1] rows whose logits are all
+// -inf, [2] NaN / +inf logits. Integer atomics: the totals do not depend on
+// the order of the additions.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void validate_kernel(const int32_t* ids, const void* tl,
+                                                       int tl_f32, int64_t S, int K, int V,
+                                                       unsigned long long* counters) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= S) return;
+  int nbad = 0, nlog = 0, nfin = 0;
+  for (int k = lane; k < K; k += 64) {
+    const int id = ids[t * K + k];
+    const float l = load_logit(tl, tl_f32, t * K + k);
+    nbad += (id < 0 || id >= V) ? 1 : 0;
+    nlog += (isnan(l) || l == INFINITY) ? 1 : 0;
+    nfin += (l != -INFINITY) ? 1 : 0;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    nbad += __shfl_xor(nbad, o, 64);
+    nlog += __shfl_xor(nlog, o, 64);
+    nfin += __shfl_xor(nfin, o, 64);
+  }
+  if (lane == 0) {
+    if (nbad) atomicAdd(&counters[0], (unsigned long long)nbad);
+    if (nfin == 0) atomicAdd(&counters[1], 1ull);
+    if (nlog) atomicAdd(&counters[2], (unsigned long long)nlog);
+  }
+}
+
+__global__ void zero_u64_kernel(unsigned long long* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0ull;
+}
+
+hipError_t launch_validate(const int32_t* ids, const void* tl, int tl_f32, int64_t S, int K,
+                           int V, unsigned long long* counters, hipStream_t st) {
+  hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(64), 0, st, counters, 3);
+  if (S > 0)
+    hipLaunchKernelGGL(validate_kernel, dim3((unsigned)ceil_div(S, 4)), dim3(256), 0, st, ids, tl,
+                       tl_f32, S, K, V, counters);
+  return hipGetLastError();
+}
+
+__global__ void fill_u8_kernel(uint8_t* p, uint8_t v, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = v;
+}
+
+hipError_t launch_fill_u8(uint8_t* p, uint8_t v, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int64_t grid = ceil_div(n, 256);
+  if (grid > 4096) grid = 4096;
+  hipLaunchKernelGGL(fill_u8_kernel, dim3((unsigned)grid), dim3(256), 0, st, p, v, n);
+  return hipGetLastError();
+}
+
+}  // namespace kd

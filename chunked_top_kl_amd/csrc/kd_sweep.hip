@@ -1,0 +1,522 @@
+// Vocabulary-sweep projection kernels: the fused lm_head GEMM with
+//  - forward: online base-2 log-sum-exp of z/T and the gather of z at the
+//    teacher ids ("what chunked KL loss does": project, fold into the loss,
+//    discard - nothing of [rows, V] is stored);
+//  - backward: the logit gradient (softmax(z/T) - p)/T * g/N as a bf16 tile,
+//    with p scattered at the teacher ids ("backward recomputes the chunk");
+//  - entropy: online (max, sum, sum e*y) of softmax(z) for H(q_t)
+//    ("Rethinking Selective Knowledge Distillation", chunked entropy).
+//
+// Orientation: MFMA rows (M) are vocabulary entries (A = W tile), MFMA columns
+// (N) are tokens (B = hidden rows). Each lane therefore owns whole token
+// columns, so the per-token running state stays in registers for the entire
+// sweep and needs only one cross-lane merge at the end.
+#include "kd_gemm_core.hpp"
+#include "kd_kernels.hpp"
+
+#include <map>
+#include <type_traits>
+#include <mutex>
+#include <tuple>
+
+namespace kd {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// vocabulary index of accumulator element (i, r) for this lane, relative to vw0
+__device__ inline int acc_row(int i, int r, int half) { return i * 32 + 8 * (r >> 2) + 4 * half + (r & 3); }
+
+__device__ inline int lower_bound_ids(const int32_t* p, int K, int key) {
+  int lo = 0, hi = K;
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if (p[mid] < key) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Merge two partial entropy triples (max m in log2 units, S = sum 2^(y-m),
+// U = sum 2^(y-m) (y-m)) into the first.
+__device__ inline void ent_merge(float& m, double& S, double& U, float m2, double S2, double U2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) {
+    m = m2;
+    S = S2;
+    U = U2;
+    return;
+  }
+  const float mn = fmaxf(m, m2);
+  const double d1 = (double)(m - mn), d2 = (double)(m2 - mn);
+  const double f1 = exp2(d1), f2 = exp2(d2);
+  U = (U + S * d1) * f1 + (U2 + S2 * d2) * f2;
+  S = S * f1 + S2 * f2;
+  m = mn;
+}
+
+// Teacher cursor of one token column: position `cur` in the row's id-sorted
+// table (row offset `base` = original row * K) and the id found there.
+struct Cursor {
+  int64_t base;
+  int cur, nid;
+};
+
+__device__ inline void cursor_adv(Cursor& c, const int32_t* ids_s, int K) {
+  ++c.cur;
+  c.nid = c.cur < K ? ids_s[c.base + c.cur] : 0x7FFFFFFF;
+}
+
+// Walk the teacher ids of one token column that fall in [lo, lo+128) (this
+// wave's half tile). Accumulator values are addressed per lane through a
+// small per-lane LDS slot (16 floats): for each 32-row block i that holds a
+// hit of some lane, the block is dumped to the slot and on(i, slot) is
+// called; `me`/`rr` tell the lane whether its current hit sits in block i and
+// at which of its 16 registers. After each round every lane with a hit
+// advances its cursor.
+template <class F>
+__device__ __forceinline__ void walk_hits(Cursor& c, const int32_t* ids_s, int K, int lo, int half,
+                                          F&& on) {
+  while (c.nid < lo) cursor_adv(c, ids_s, K);
+  const int hi = lo + 128;
+  while (true) {
+    const bool h = c.nid < hi;
+    if (ballot(h) == 0) break;
+    const int local = c.nid - lo;
+    const bool mine = h && (((local >> 2) & 1) == half);
+    const int blk = local >> 5;
+    const int rr = ((local >> 3) & 3) * 4 + (local & 3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool me = mine && blk == i;
+      if (ballot(me)) on(i, me, rr, c.base + c.cur);
+    }
+    if (h) cursor_adv(c, ids_s, K);
+  }
+}
+
+template <typename T, int KIND, bool MAP>
+__global__ __launch_bounds__(256, 1) void sweep_kernel(SweepArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + 4 * 4096];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int half = lane >> 5;
+  float* slot = (float*)(lds + kLdsBytes + w * 4096 + lane * 64);
+
+  int rows = a.row_cap;
+  if (a.nrows_dev) {
+    int n = *a.nrows_dev - a.row_begin;
+    rows = n < rows ? n : rows;
+  }
+  if (rows <= 0) return;
+  const int ntt = (int)ceil_div(rows, kTile);
+  const int nvt = (int)ceil_div(a.V, kTile);
+  const int ns = sweep_splits(ntt, nvt, a.ncu);
+  const int total = ntt * ns;
+  if ((int)blockIdx.x >= total) return;
+  const int L = xcd_remap(blockIdx.x, total);
+  const int jt = L / ns, b = L % ns;
+  const int vt_begin = (int)((int64_t)b * nvt / ns);
+  const int vt_end = (int)((int64_t)(b + 1) * nvt / ns);
+
+  constexpr int esz = Elem<T>::size;
+  const int64_t kbytes = (int64_t)a.H * esz;
+  const int nk = (int)ceil_div(kbytes, kStepBytes);
+  const float c = kLog2e / a.T;
+  const float invT = 1.0f / a.T;
+
+  // B operand: token rows of this tile
+  typename std::conditional<MAP, LoaderKCMap, LoaderKC>::type lb;
+  if constexpr (MAP) {
+    lb.init(a.X, a.ldx, a.idx, a.row_begin + jt * kTile, a.row_begin + rows, 0, kbytes);
+  } else {
+    lb.init(a.X + (int64_t)(a.x_row0 + jt * kTile) * a.ldx, a.ldx, rows - jt * kTile, 0, kbytes);
+  }
+
+  // token columns owned by this lane: launch rows tl0 + 32*j
+  const int tl0 = jt * kTile + wn * 128 + (lane & 31);
+  int orow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int cr = a.row_begin + ((tl0 + 32 * j) < rows ? tl0 + 32 * j : 0);
+    orow[j] = a.idx ? a.idx[cr] : cr;
+  }
+
+  // per-kind running state
+  float m[4], s[4], d[4];
+  double S64[4], U64[4];
+  Cursor cu[4];
+  float lse2[4];
+  float coef = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    m[j] = -INFINITY;
+    s[j] = 0.0f;
+    d[j] = 0.0f;
+    S64[j] = 0.0;
+    U64[j] = 0.0;
+    lse2[j] = 0.0f;
+    if constexpr (KIND != kSweepEnt) {
+      cu[j].base = (int64_t)orow[j] * a.K;
+      if (tl0 + 32 * j < rows) {
+        cu[j].cur = lower_bound_ids(a.ids_s + cu[j].base, a.K, vt_begin * kTile);
+        cu[j].nid = cu[j].cur < a.K ? a.ids_s[cu[j].base + cu[j].cur] : 0x7FFFFFFF;
+      } else {
+        cu[j].cur = a.K;
+        cu[j].nid = 0x7FFFFFFF;
+      }
+    }
+    if constexpr (KIND == kSweepBwdG)
+      lse2[j] = (tl0 + 32 * j < rows) ? a.lse[orow[j]] * kLog2e : 0.0f;
+  }
+  if constexpr (KIND == kSweepBwdG) {
+    const int n = *a.nrows_dev;
+    coef = (n > 0) ? a.grad_loss[0] / ((float)n * a.T) : 0.0f;
+  }
+
+  for (int vt = vt_begin; vt < vt_end; ++vt) {
+    LoaderKC la;
+    la.init(a.W + (int64_t)vt * kTile * a.ldw, a.ldw, a.V - vt * kTile, 0, kbytes);
+    floatx16 acc[4][4];
+    gemm_mainloop<T>(acc, la, lb, nk, lds);
+
+    const int vw0 = vt * kTile + wm * 128;
+    if (vw0 >= a.V) continue;  // wave-uniform: this half tile is past the vocabulary
+    const bool tail = vw0 + 128 > a.V;
+    if (tail) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (vw0 + acc_row(i, r, half) >= a.V) acc[i][j][r] = -INFINITY;
+    }
+
+    if constexpr (KIND == kSweepFwd) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+        const float mn = fmaxf(m[j], mx * c);
+        if (mn != -INFINITY) {
+          const float sc = fast_exp2(m[j] - mn);
+          float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; r += 4) {
+              s0 += fast_exp2(fmaf(acc[i][j][r + 0], c, -mn));
+              s1 += fast_exp2(fmaf(acc[i][j][r + 1], c, -mn));
+              s2 += fast_exp2(fmaf(acc[i][j][r + 2], c, -mn));
+              s3 += fast_exp2(fmaf(acc[i][j][r + 3], c, -mn));
+            }
+          s[j] = s[j] * sc + ((s0 + s1) + (s2 + s3));
+          m[j] = mn;
+        }
+        float* zrow = a.z_topk ? a.z_topk + (int64_t)orow[j] * a.K : nullptr;
+        walk_hits(cu[j], a.ids_s, a.K, vw0, half, [&](int i, bool me, int rr, int64_t e) {
+          floatx4* sl = (floatx4*)slot;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            sl[q] = floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                            acc[i][j][4 * q + 3]};
+          if (me) {
+            const float val = slot[rr];
+            d[j] += a.p_s[e] * val;
+            if (zrow) zrow[a.korig_s[e]] = val * invT;
+          }
+        });
+      }
+    }
+
+    if constexpr (KIND == kSweepEnt) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+        const float mn = fmaxf(m[j], mx * c);
+        if (mn != -INFINITY) {
+          float st0 = 0.f, st1 = 0.f, ut0 = 0.f, ut1 = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+              const float y0 = fmaf(acc[i][j][r], c, -mn), y1 = fmaf(acc[i][j][r + 1], c, -mn);
+              const float e0 = fast_exp2(y0), e1 = fast_exp2(y1);
+              st0 += e0;
+              st1 += e1;
+              ut0 += (e0 > 0.f) ? e0 * y0 : 0.f;
+              ut1 += (e1 > 0.f) ? e1 * y1 : 0.f;
+            }
+          const float st = st0 + st1, ut = ut0 + ut1;
+          if (m[j] == -INFINITY) {
+            S64[j] = st;
+            U64[j] = ut;
+          } else {
+            const float dm = m[j] - mn;
+            const double f = (double)fast_exp2(dm);
+            U64[j] = (U64[j] + S64[j] * (double)dm) * f + (double)ut;
+            S64[j] = S64[j] * f + (double)st;
+          }
+          m[j] = mn;
+        }
+      }
+    }
+
+    if constexpr (KIND == kSweepBwdG) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = fast_exp2(fmaf(acc[i][j][r], c, -lse2[j]));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        walk_hits(cu[j], a.ids_s, a.K, vw0, half, [&](int i, bool me, int rr, int64_t e) {
+          floatx4* sl = (floatx4*)slot;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            sl[q] = floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                            acc[i][j][4 * q + 3]};
+          if (me) slot[rr] -= a.p_s[e];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const floatx4 v = sl[q];
+            acc[i][j][4 * q] = v[0];
+            acc[i][j][4 * q + 1] = v[1];
+            acc[i][j][4 * q + 2] = v[2];
+            acc[i][j][4 * q + 3] = v[3];
+          }
+        });
+      // columns in [V, round_up(V, 8)) are written as zeros so that 16-byte
+      // granules read by the dHidden product never hold stale data
+      const int Vp = (int)round_up(a.V, 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (tl0 + 32 * j >= rows) continue;
+        char* grow = a.G + (int64_t)(tl0 + 32 * j) * a.ldg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int v = vw0 + i * 32 + 8 * q + 4 * half;
+            if (v >= Vp) continue;
+            const float g0 = acc[i][j][4 * q + 0] * coef, g1 = acc[i][j][4 * q + 1] * coef;
+            const float g2 = acc[i][j][4 * q + 2] * coef, g3 = acc[i][j][4 * q + 3] * coef;
+            if constexpr (sizeof(T) == 2) {
+              uint2 pk;
+              pk.x = f32_to_bf16_bits(g0) | (f32_to_bf16_bits(g1) << 16);
+              pk.y = f32_to_bf16_bits(g2) | (f32_to_bf16_bits(g3) << 16);
+              *(uint2*)(grow + (int64_t)v * 2) = pk;
+            } else {
+              *(float4*)(grow + (int64_t)v * 4) = make_float4(g0, g1, g2, g3);
+            }
+          }
+      }
+    }
+  }
+
+  if constexpr (KIND == kSweepBwdG) return;
+
+  // ---- end of sweep: merge lane halves, then the two waves sharing tokens
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (KIND == kSweepFwd) {
+      const float m2 = __shfl_xor(m[j], 32, 64), s2 = __shfl_xor(s[j], 32, 64);
+      const float d2 = __shfl_xor(d[j], 32, 64);
+      lse2_merge(m[j], s[j], m2, s2);
+      d[j] += d2;
+    } else {
+      const float m2 = __shfl_xor(m[j], 32, 64);
+      const double S2 = __shfl_xor(S64[j], 32, 64), U2 = __shfl_xor(U64[j], 32, 64);
+      ent_merge(m[j], S64[j], U64[j], m2, S2, U2);
+    }
+  }
+  __syncthreads();
+  // exchange area: [wn][128] x {m, s|S, d|U}
+  float* xm = (float*)lds;
+  double* xa = (double*)(lds + 2 * 128 * 4);
+  double* xb = xa + 2 * 128;
+  if (wm == 1 && lane < 32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = wn * 128 + j * 32 + lane;
+      xm[t] = m[j];
+      if constexpr (KIND == kSweepFwd) {
+        xa[t] = s[j];
+        xb[t] = d[j];
+      } else {
+        xa[t] = S64[j];
+        xb[t] = U64[j];
+      }
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && lane < 32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = wn * 128 + j * 32 + lane;
+      if (tl0 + 32 * j >= rows) continue;
+      const int64_t o = (int64_t)b * ntt * kTile + tl0 + 32 * j;
+      if constexpr (KIND == kSweepFwd) {
+        lse2_merge(m[j], s[j], xm[t], (float)xa[t]);
+        d[j] += (float)xb[t];
+        a.pm[o] = m[j];
+        a.ps[o] = s[j];
+        a.pd[o] = d[j];
+      } else {
+        ent_merge(m[j], S64[j], U64[j], xm[t], xa[t], xb[t]);
+        a.em[o] = m[j];
+        a.es[o] = S64[j];
+        a.eu[o] = U64[j];
+      }
+    }
+  }
+}
+
+// grid size: the largest work-group count any row count up to rows_max can use
+int sweep_grid(int64_t rows_max, int V, int ncu) {
+  static std::mutex mu;
+  static std::map<std::tuple<int64_t, int, int>, int> memo;
+  std::lock_guard<std::mutex> g(mu);
+  auto key = std::make_tuple(rows_max, V, ncu);
+  auto it = memo.find(key);
+  if (it != memo.end()) return it->second;
+  const int nvt = (int)ceil_div(V, kTile);
+  const int ntt_max = (int)ceil_div(rows_max, kTile);
+  int best = 1;
+  for (int n = 1; n <= ntt_max; ++n) {
+    int g2 = n * sweep_splits(n, nvt, ncu);
+    if (g2 > best) best = g2;
+  }
+  memo[key] = best;
+  return best;
+}
+
+hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid, hipStream_t st) {
+  if (grid <= 0) return hipSuccess;
+  dim3 g(grid), blk(kThreads);
+#define KD_SWEEP(T, K, M) hipLaunchKernelGGL((sweep_kernel<T, K, M>), g, blk, 0, st, a)
+  if (!f32) {
+    if (kind == kSweepFwd && map) KD_SWEEP(__bf16, kSweepFwd, true);
+    else if (kind == kSweepFwd) KD_SWEEP(__bf16, kSweepFwd, false);
+    else if (kind == kSweepBwdG) KD_SWEEP(__bf16, kSweepBwdG, false);
+    else KD_SWEEP(__bf16, kSweepEnt, false);
+  } else {
+    if (kind == kSweepFwd && map) KD_SWEEP(float, kSweepFwd, true);
+    else if (kind == kSweepFwd) KD_SWEEP(float, kSweepFwd, false);
+    else if (kind == kSweepBwdG) KD_SWEEP(float, kSweepBwdG, false);
+    else KD_SWEEP(float, kSweepEnt, false);
+  }
+#undef KD_SWEEP
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Forward combine: merge the split partials of each row into lse and KL_t,
+// then fp64 block sums of KL over valid rows (fixed order, no atomics).
+//   KL_t = sum_k p log p - (sum_k p z_k)/T + log sum_v exp(z_v/T)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fwd_combine_kernel(CombineArgs a) {
+  __shared__ double red[256];
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  double contrib = 0.0;
+  if (t < a.S) {
+    const int pr = a.pos[t];
+    if (pr < 0) {
+      a.lse[t] = 0.0f;
+      if (a.kl_rows) a.kl_rows[t] = 0.0f;
+      if (a.z_topk)
+        for (int k = 0; k < a.K; ++k) a.z_topk[(int64_t)t * a.K + k] = __int_as_float(0x7FC00000);
+    } else {
+      // partial row: the original row when the forward ran over all rows
+      const int r = a.identity ? t : pr;
+      const int n = a.identity ? a.S : *a.nrows_dev;
+      const int ns = sweep_splits((int)ceil_div(n, kTile), (int)ceil_div(a.V, kTile), a.ncu);
+      float M = -INFINITY, sum = 0.0f, dot = 0.0f;
+      const int64_t stride = ceil_div(n, kTile) * kTile;
+      for (int b = 0; b < ns; ++b) {
+        const int64_t o = (int64_t)b * stride + r;
+        lse2_merge(M, sum, a.pm[o], a.ps[o]);
+        dot += a.pd[o];
+      }
+      const float lse = (M + __log2f(sum)) * kLn2;
+      const float kl = a.negH[t] - dot / a.T + lse;
+      a.lse[t] = lse;
+      if (a.kl_rows) a.kl_rows[t] = kl;
+      contrib = kl;
+    }
+  }
+  red[threadIdx.x] = contrib;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) a.block_sums[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(256) void loss_final_kernel(const double* block_sums, int nblk,
+                                                         const int32_t* nrows_dev, float* loss) {
+  __shared__ double red[256];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < nblk; i += 256) acc += block_sums[i];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int n = *nrows_dev;
+    loss[0] = n > 0 ? (float)(red[0] / (double)n) : 0.0f;
+  }
+}
+
+hipError_t launch_fwd_combine(const CombineArgs& a, hipStream_t st) {
+  const int nblk = (int)ceil_div(a.S, 256);
+  if (nblk > 0) hipLaunchKernelGGL(fwd_combine_kernel, dim3(nblk), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(256), 0, st, (const double*)a.block_sums,
+                     nblk, a.nrows_dev, a.loss);
+  return hipGetLastError();
+}
+
+// Entropy combine in fp64:  H = ln(sum) - ln2 * U / sum  (U in log2 units).
+__global__ __launch_bounds__(256) void ent_combine_kernel(EntCombineArgs a) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.S) return;
+  const int ns = sweep_splits((int)ceil_div(a.S, kTile), (int)ceil_div(a.V, kTile), a.ncu);
+  double M = -INFINITY, Ssum = 0.0, U = 0.0;
+  const int64_t stride = ceil_div(a.S, kTile) * kTile;
+  for (int b = 0; b < ns; ++b) {
+    const int64_t o = (int64_t)b * stride + t;
+    const double m2 = a.em[o], S2 = a.es[o], U2 = a.eu[o];
+    if (m2 == -INFINITY) continue;
+    if (M == -INFINITY) {
+      M = m2; Ssum = S2; U = U2;
+      continue;
+    }
+    const double mn = fmax(M, m2);
+    const double f1 = exp2(M - mn), f2 = exp2(m2 - mn);
+    U = (U + Ssum * (M - mn)) * f1 + (U2 + S2 * (m2 - mn)) * f2;
+    Ssum = Ssum * f1 + S2 * f2;
+    M = mn;
+  }
+  a.entropy[t] = log(Ssum) - 0.6931471805599453 * U / Ssum;
+}
+
+hipError_t launch_ent_combine(const EntCombineArgs& a, hipStream_t st) {
+  const int nblk = (int)ceil_div(a.S, 256);
+  if (nblk > 0) hipLaunchKernelGGL(ent_combine_kernel, dim3(nblk), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace kd

@@ -1,0 +1,196 @@
+/*
+ * kd_topk_kl.h - C ABI of the fused chunked top-K KL distillation loss for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (offline distillation against a cached teacher top-K):
+ *   for each position t with student hidden state h_t (row of hidden[S,H]) and
+ *   cached teacher entries (id_tk, l_tk), k = 0..K-1:
+ *     z_t    = h_t W^T                       student logits over the vocabulary V
+ *     p_tk   = softmax_k(l_tk / T)           teacher top-K softmax, renormalised
+ *                                            over the K cached entries
+ *     KL_t   = sum_k p_tk (log p_tk - log softmax(z_t/T)[id_tk])
+ *   loss = (sum over valid t of KL_t) / N,  N = number of valid positions.
+ * The [S,V] logit grid is never stored: rows are projected tile by tile, the
+ * log-normaliser of z/T is reduced online and the teacher ids are gathered as
+ * the tiles pass; the backward pass projects each chunk of rows again.
+ *
+ * Sources (web pages; cited by title and section):
+ *  - "Making Knowledge Distillation Cheap Enough to Run at Scale" (aibase.it
+ *    write-up "Knowledge Distillation 비용 줄이기"): section "offline top-K
+ *    logits" (per-position top-100 ids and logits, cached once with the
+ *    temperature), section "what chunked KL loss does" (dense KL as the
+ *    correctness baseline; fused chunked KL folds the output projection into
+ *    the loss, projects one sequence chunk at a time, discards it, and
+ *    recomputes it in the backward pass), section "operations" (cache
+ *    validation: id range, missing positions, sort order, logit dtype).
+ *  - "Efficient Knowledge Distillation for LLMs: Offline Top-K Logits and a
+ *    Fused Chunked KL Loss" (paper review), section 1 (fused chunked KL loss:
+ *    no full-vocabulary logit tensor) and section 3 (memory linear in S).
+ *  - "LLM Primer, Chapter 6 - Pruning and Distillation", section 6.2 (KL of
+ *    temperature-softened teacher and student distributions).
+ *  - "Rethinking Selective Knowledge Distillation" (summary), Method
+ *    section 2 (SE-KD: top-k% positions by student entropy H(q_t)) and
+ *    section 3 (selective LM head; chunked entropy computation).
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked [device] are device memory owned by the caller; the
+ *    library never allocates or frees device memory. Pointers marked [host]
+ *    are host memory. All arrays are dense row-major.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *    on it in order; no entry point synchronises the host unless it says so.
+ *  - `ws` / `ws_bytes`: caller-provided device workspace of at least
+ *    kd_workspace_bytes(problem) bytes, 256-byte aligned. Its contents on
+ *    entry are ignored and on exit are unspecified. Calls that overlap in time
+ *    must use distinct workspaces.
+ *  - Argument errors are detected on the host before anything is enqueued and
+ *    returned as a kd_status; a failed launch returns KD_ERR_HIP. Data errors
+ *    (ids outside [0,V), rows whose K logits are all -inf) are not errors of
+ *    fwd/bwd: out-of-range ids are skipped (never dereferenced) and treated as
+ *    absent entries, and all -inf rows are excluded like masked rows;
+ *    kd_validate_topk reports them.
+ */
+#ifndef KD_TOPK_KL_H
+#define KD_TOPK_KL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KD_ABI_VERSION 1
+
+typedef enum kd_status {
+  KD_OK = 0,
+  KD_ERR_NULL = 1,         /* a required pointer is NULL                          */
+  KD_ERR_SHAPE = 2,        /* S<0, H/V/K<=0, K>V, H not a multiple of 8, sizes too large */
+  KD_ERR_DTYPE = 3,        /* dtype code not one of kd_dtype                      */
+  KD_ERR_TEMPERATURE = 4,  /* T <= 0 or not finite                                */
+  KD_ERR_CHUNK = 5,        /* chunk <= 0                                          */
+  KD_ERR_WORKSPACE = 6,    /* ws NULL, misaligned, or smaller than kd_workspace_bytes */
+  KD_ERR_BAD_ID = 7,       /* reserved: reported counts come from kd_validate_topk */
+  KD_ERR_HIP = 8,          /* a HIP runtime call or kernel launch failed          */
+  KD_ERR_ARCH = 9,         /* current device is not gfx950                        */
+  KD_ERR_ARG = 10          /* other invalid argument (fraction, accumulate flag)  */
+} kd_status;
+
+typedef enum kd_dtype { KD_BF16 = 0, KD_F32 = 1 } kd_dtype;
+
+/* Problem description shared by all entry points.
+ *   S      positions (rows of hidden); S = 0 is allowed (empty problem)
+ *   H      hidden size; multiple of 8
+ *   V      vocabulary size (rows of W)
+ *   K      teacher entries per position, 1 <= K <= min(V, 4096)
+ *   chunk  rows per backward chunk: bounds the [chunk, V] bf16 gradient tile
+ *          held in the workspace (the only workspace term that grows with V)
+ *   temperature  T > 0, applied to teacher and student logits alike
+ *   hw_dtype     storage type of hidden and W (both the same)
+ *   tl_dtype     storage type of topk_logits                                */
+typedef struct kd_problem {
+  int64_t S, H, V, K, chunk;
+  float temperature;
+  int32_t hw_dtype;
+  int32_t tl_dtype;
+} kd_problem;
+
+/* ABI version of the loaded library (KD_ABI_VERSION). */
+int kd_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+const char* kd_status_str(int status);
+
+/* Workspace bytes needed by every entry point below for this problem (the
+ * maximum over them). Returns 0 if the problem itself is invalid. The size is
+ * linear in S (per-row teacher tables and partials) plus a constant part
+ * (the [chunk, V] bf16 gradient tile and split-K partials of dHidden). */
+size_t kd_workspace_bytes(const kd_problem* problem);
+
+/* Forward pass ("what chunked KL loss does": project, fold into the loss,
+ * discard; the online log-normaliser of z/T over V and the gather of z at the
+ * teacher ids run inside the projection's epilogue).
+ *   hidden      [device] [S,H] hw_dtype
+ *   W           [device] [V,H] hw_dtype (output projection, nn.Linear layout)
+ *   topk_ids    [device] [S,K] int32 teacher ids, any order, duplicates add
+ *   topk_logits [device] [S,K] tl_dtype teacher logits (-inf = absent entry)
+ *   mask        [device] [S] uint8, nonzero = position takes part; NULL = all
+ *   loss        [device] [1] float32: sum of KL_t over valid rows / N (0 if N=0)
+ *   lse         [device] [S] float32: log sum_v exp(z_tv / T) for valid rows,
+ *               0 for rows not taking part; needed by kd_topk_kl_bwd
+ *   kl_rows     [device] [S] float32 or NULL: KL_t for valid rows, 0 otherwise
+ *   z_topk      [device] [S,K] float32 or NULL: z_t[id_tk] / T for valid rows
+ *               and in-range ids (same order as topk_ids), NaN elsewhere      */
+int kd_topk_kl_fwd(const kd_problem* problem, const void* hidden, const void* W,
+                   const int32_t* topk_ids, const void* topk_logits, const uint8_t* mask,
+                   float* loss, float* lse, float* kl_rows, float* z_topk,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Backward pass: rows are projected again chunk by chunk ("backward
+ * recomputes the chunk"); the logit gradient
+ *   G_tv = g/N * (softmax(z_t/T)_v - p_t(v)) / T,   g = *grad_loss,
+ * with p_t(v) the teacher probability scattered to its id, is formed in the
+ * projection's epilogue as a bf16 [chunk,V] tile and contracted twice:
+ *   dhidden[t] = G_t W  (rows not taking part are set to 0),
+ *   dW        (+)= G^T hidden_chunk, accumulated over chunks in fp32.
+ *   lse         [device] [S] float32 from kd_topk_kl_fwd with the same inputs
+ *   grad_loss   [device] [1] float32 upstream gradient of loss
+ *   dhidden     [device] [S,H] float32 output
+ *   dW          [device] [V,H] float32 output; accumulate_dW = 1 adds to its
+ *               contents (tied weights), 0 overwrites                          */
+int kd_topk_kl_bwd(const kd_problem* problem, const void* hidden, const void* W,
+                   const int32_t* topk_ids, const void* topk_logits, const uint8_t* mask,
+                   const float* lse, const float* grad_loss,
+                   float* dhidden, float* dW, int accumulate_dW,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Per-position student entropy H(q_t) = -sum_v q_tv ln q_tv in nats, with
+ * q_t = softmax(z_t) over the full vocabulary at temperature 1 ("Rethinking
+ * Selective Knowledge Distillation", Method 2-3: student entropy as the
+ * position signal, computed chunk-wise without storing logits). The
+ * temperature field of the problem is not used.
+ *   entropy     [device] [S] float64 output                                   */
+int kd_student_entropy(const kd_problem* problem, const void* hidden, const void* W,
+                       double* entropy, void* ws, size_t ws_bytes, void* stream);
+
+/* Keep the floor(num*S/den) positions of highest entropy, lower index first
+ * on ties (SE-KD top-k% selection, Method section 2). Entropies within a band
+ * around the cut are recomputed in fp64 from hidden and W before the decision,
+ * so the kept set is the one an fp64 evaluation gives.
+ *   entropy     [device] [S] float64 from kd_student_entropy (not modified)
+ *   mask_out    [device] [S] uint8: 1 = kept
+ *   idx_out     [device] [S] int32 or NULL: kept positions in ascending order
+ *               in the first count entries
+ *   count_out   [host] number kept. Synchronises the host with the stream.  */
+int kd_select_top_fraction(const kd_problem* problem, const void* hidden, const void* W,
+                           const double* entropy, int64_t num, int64_t den,
+                           uint8_t* mask_out, int32_t* idx_out, int64_t* count_out,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Cache validation ("operations": id range and missing positions).
+ *   n_bad_id     [host] ids outside [0, V)
+ *   n_empty_row  [host] rows whose K logits are all -inf
+ *   n_bad_logit  [host] logits that are NaN or +inf
+ * Synchronises the host with the stream.                                     */
+int kd_validate_topk(const kd_problem* problem, const int32_t* topk_ids, const void* topk_logits,
+                     int64_t* n_bad_id, int64_t* n_empty_row, int64_t* n_bad_logit,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Kernel timing (off by default). When on, every kernel the library enqueues
+ * is bracketed by HIP events on the same stream. kd_profile_read synchronises
+ * those events and reports, per kernel name, the number of launches and the
+ * summed duration in milliseconds; it returns the number of names written (at
+ * most max_entries). kd_profile_reset discards the records.                 */
+typedef struct kd_kernel_stat {
+  char name[48];
+  int64_t launches;
+  double total_ms;
+} kd_kernel_stat;
+int kd_profile_enable(int on);
+int kd_profile_read(kd_kernel_stat* out, int max_entries);
+int kd_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KD_TOPK_KL_H */

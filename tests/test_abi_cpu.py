@@ -1,0 +1,97 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports every
+symbol the header declares, and rejects invalid arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kd_topk_kl.h")
+
+kd = pytest.importorskip("chunked_top_kl_amd", reason="HIP library not built")
+
+KD_OK, KD_ERR_NULL, KD_ERR_SHAPE, KD_ERR_DTYPE, KD_ERR_TEMPERATURE = 0, 1, 2, 3, 4
+KD_ERR_CHUNK, KD_ERR_WORKSPACE, KD_ERR_ARG = 5, 6, 10
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(kd_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert "kd_topk_kl_fwd" in names and "kd_topk_kl_bwd" in names
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(kd.lib, n), f"{n} not exported by {kd.LIB_PATH}"
+
+
+def test_version_and_status_strings():
+    assert kd.kd_abi_version() == 1
+    for c in range(11):
+        assert kd.kd_status_str(c).startswith("KD_")
+    assert "unknown" in kd.kd_status_str(99)
+
+
+def prob(**kw):
+    d = dict(S=128, H=64, V=1000, K=10, chunk=32, T=1.0, hw=kd.KD_BF16, tl=kd.KD_BF16)
+    d.update(kw)
+    return kd.make_problem(d["S"], d["H"], d["V"], d["K"], d["chunk"], d["T"], d["hw"], d["tl"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S=-1), KD_ERR_SHAPE), (dict(H=0), KD_ERR_SHAPE), (dict(H=60), KD_ERR_SHAPE),
+    (dict(V=0), KD_ERR_SHAPE), (dict(K=0), KD_ERR_SHAPE), (dict(K=1001), KD_ERR_SHAPE),
+    (dict(K=5000, V=10000), KD_ERR_SHAPE), (dict(hw=7), KD_ERR_DTYPE), (dict(tl=-1), KD_ERR_DTYPE),
+    (dict(T=0.0), KD_ERR_TEMPERATURE), (dict(T=-1.0), KD_ERR_TEMPERATURE),
+    (dict(T=float("nan")), KD_ERR_TEMPERATURE), (dict(T=float("inf")), KD_ERR_TEMPERATURE),
+    (dict(chunk=0), KD_ERR_CHUNK),
+])
+def test_invalid_problems_rejected(kw, code):
+    p = prob(**kw)
+    assert kd.kd_workspace_bytes(p) == 0
+    fake = ctypes.c_void_p(0x1000)
+    rc = kd.lib.kd_topk_kl_fwd(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, None,
+                               None, fake, 1 << 40, None)
+    assert rc == code
+
+
+def test_null_and_workspace_errors():
+    p = prob()
+    fake = ctypes.c_void_p(0x1000)
+    assert kd.lib.kd_topk_kl_fwd(None, fake, fake, fake, fake, None, fake, fake, None, None, fake,
+                                 1 << 40, None) == KD_ERR_NULL
+    assert kd.lib.kd_topk_kl_fwd(ctypes.byref(p), None, fake, fake, fake, None, fake, fake, None,
+                                 None, fake, 1 << 40, None) == KD_ERR_NULL
+    need = kd.kd_workspace_bytes(p)
+    assert need > 0
+    # too small, misaligned, NULL workspace
+    assert kd.lib.kd_topk_kl_fwd(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, None,
+                                 None, ctypes.c_void_p(0x10000), need - 1, None) == KD_ERR_WORKSPACE
+    assert kd.lib.kd_topk_kl_fwd(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, None,
+                                 None, ctypes.c_void_p(0x10010), need, None) == KD_ERR_WORKSPACE
+    assert kd.lib.kd_topk_kl_bwd(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, fake,
+                                 fake, 2, ctypes.c_void_p(0x10000), need, None) == KD_ERR_ARG
+    cnt = ctypes.c_int64(0)
+    assert kd.lib.kd_select_top_fraction(ctypes.byref(p), fake, fake, fake, 3, 2, fake, None,
+                                         ctypes.byref(cnt), ctypes.c_void_p(0x10000), need,
+                                         None) == KD_ERR_ARG
+
+
+def test_workspace_linear_in_S_and_bounded_in_V():
+    sizes = [kd.kd_workspace_bytes(prob(S=S, H=3072, V=128256, K=100, chunk=2048))
+             for S in (16384, 32768, 65536, 131072, 262144)]
+    d = [b - a for a, b in zip(sizes, sizes[1:])]
+    per_token = [x / dS for x, dS in zip(d, (16384, 32768, 65536, 131072))]
+    # per-token slope (teacher tables + split partials) stays a few KB per token; the
+    # split count of the sweep varies a little with the number of token tiles
+    assert max(per_token) < 1.3 * min(per_token)
+    assert 1000 < min(per_token) and max(per_token) < 6000
+    # the chunk-sized part grows with chunk, not with S
+    a = kd.kd_workspace_bytes(prob(S=32768, H=2880, V=201088, K=100, chunk=1024))
+    b = kd.kd_workspace_bytes(prob(S=32768, H=2880, V=201088, K=100, chunk=2048))
+    assert b - a >= 1024 * 201088 * 2
