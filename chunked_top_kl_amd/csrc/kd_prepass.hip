@@ -3,7 +3,8 @@
 // Prepass, one wave per position ("offline top-K logits": K cached ids and
 // logits per position, softened by the stored temperature):
 //   p_k   = softmax over the row's usable entries of l_k / T
-//   negH  = sum_k p_k log p_k  (0 log 0 = 0)
+//   negH  = sum over distinct ids of P log P, P = sum of p_k sharing the id
+//           (0 log 0 = 0)
 //   (id, p, k) sorted by id ascending, ties by k, so that the projection
 //   epilogue can walk each row's ids in vocabulary order.
 // An entry is usable when its id lies in [0, V) and its logit is finite;
@@ -63,11 +64,7 @@ __global__ void prepass_kernel(const int32_t* ids, const void* tl, int tl_f32, i
       const int id = ids[base + k];
       const float l = load_logit(tl, tl_f32, base + k);
       const bool inr = id >= 0 && id < V;
-      if (inr && isfinite(l) && mx != -INFINITY) {
-        const float lp = (l * invT - mx) - logz;
-        p = __expf(lp);
-        if (p > 0.0f) nh += p * lp;
-      }
+      if (inr && isfinite(l) && mx != -INFINITY) p = __expf((l * invT - mx) - logz);
       const uint32_t kid = inr ? (uint32_t)id : 0x7FFFFFFFu;
       kk = ((unsigned long long)kid << 32) | (uint32_t)k;
       if (z_topk) z_topk[base + k] = __int_as_float(0x7FC00000);  // NaN until gathered
@@ -75,7 +72,6 @@ __global__ void prepass_kernel(const int32_t* ids, const void* tl, int tl_f32, i
     key[k] = kk;
     pv[k] = p;
   }
-  nh = wave_sum(nh);
   __syncthreads();
   // 4. bitonic sort of (key, p) ascending by key (each wave its own row)
   for (int kk = 2; kk <= n2; kk <<= 1) {
@@ -97,6 +93,16 @@ __global__ void prepass_kernel(const int32_t* ids, const void* tl, int tl_f32, i
       __syncthreads();
     }
   }
+  // teacher entropy term over merged probabilities: entries sharing an id form
+  // one run after the sort and their probabilities add
+  for (int k = lane; k < K; k += 64) {
+    const uint32_t id = (uint32_t)(key[k] >> 32);
+    if (id == 0x7FFFFFFFu || (k > 0 && (uint32_t)(key[k - 1] >> 32) == id)) continue;
+    float P = 0.0f;
+    for (int q = k; q < K && (uint32_t)(key[q] >> 32) == id; ++q) P += pv[q];
+    if (P > 0.0f) nh += P * __logf(P);
+  }
+  nh = wave_sum(nh);
   if (!live) return;
   for (int k = lane; k < K; k += 64) {
     const unsigned long long kk = key[k];
