@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused chunked top-K KL loss (forward + backward) on one MI355X.
+
+One step = the whole hot path over one batch: teacher prepass, fused projection
+with online log-sum-exp and id gather, combine and loss, then per chunk the
+recomputed gradient tile, dHidden and dW contractions.
+
+Default workload (the 32K-context, large-vocabulary configuration):
+  S=32768, H=2880, V=201088, K=100, T=1.0, chunk=2048, bf16 hidden/W, bf16
+  teacher logits, int32 ids; synthetic inputs from kd_synth (seed 1003).
+
+Prints ONE JSON line. Besides tokens/s it reports the achieved MFMA fraction
+(counting 4 contractions of 2*S*H*V FLOP per step), per-kernel HIP-event
+timings over the timed region, the roofline of the dominant kernel, peak
+device memory against S for the 256K-context configuration shapes, and the
+fp64 CPU oracle timed on a bounded sample of rows.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+
+WORKLOADS = {
+    "c2": dict(S=8192, H=3072, V=128256, K=100, T=1.0, chunk=1024, seed=1002,
+               name="8K context: S=8192 H=3072 V=128256 K=100 T=1.0 chunk=1024 bf16"),
+    "c3": dict(S=32768, H=2880, V=201088, K=100, T=1.0, chunk=2048, seed=1003,
+               name="32K context, large vocab: S=32768 H=2880 V=201088 K=100 T=1.0 chunk=2048 bf16"),
+    "c4": dict(S=262144, H=3072, V=128256, K=100, T=2.0, chunk=2048, seed=1004,
+               name="256K context: S=262144 H=3072 V=128256 K=100 T=2.0 chunk=2048 bf16"),
+    "c5": dict(S=32768, H=2048, V=151936, K=100, T=1.0, chunk=1024, seed=1005,
+               name="entropy-selective: S=32768 H=2048 V=151936 K=100 top 20% by entropy, chunk=1024 bf16"),
+}
+
+METRIC = "fwd+bwd tokens/s at S=32K,V=201088 + MFMA % of peak + peak GiB vs S"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def to_dev(p, torch):
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    return bf(p.hidden_bits), bf(p.W_bits), torch.from_numpy(p.ids).cuda(), bf(p.tl_bits)
+
+
+def kernel_flops(name, wl, C_rows, S_rows):
+    """Algorithmic FLOPs of one launch of a projection kernel."""
+    H, V = wl["H"], wl["V"]
+    if name in ("fwd_lse_gather", "entropy_sweep"):
+        return 2.0 * S_rows * H * V
+    if name in ("bwd_grad_tile", "bwd_dhidden", "bwd_dw"):
+        return 2.0 * C_rows * H * V
+    return None
+
+
+def run_step(kd, torch, wl, t, ws, mask=None):
+    hidden, W, ids, tl = t
+    out = kd.kd_topk_kl_fwd(hidden, W, ids, tl, wl["T"], wl["chunk"], mask, workspace=ws)
+    g = torch.ones(1, dtype=torch.float32, device="cuda")
+    dh, dW = kd.kd_topk_kl_bwd(hidden, W, ids, tl, out["lse"], g, wl["T"], wl["chunk"], mask,
+                               workspace=ws)
+    return out, dh, dW
+
+
+def run_c5_step(kd, torch, wl, t, ws):
+    hidden, W, ids, tl = t
+    ent = kd.kd_student_entropy(hidden, W, workspace=ws)
+    mask, idx, cnt = kd.kd_select_top_fraction(ent, hidden, W, 20, 100, workspace=ws)
+    return run_step(kd, torch, wl, t, ws, mask=mask), cnt
+
+
+def cpu_baseline(p, wl, rows):
+    """fp64 oracle forward+backward on the first `rows` positions of the same workload."""
+    from oracle import oracle_loss_grads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    oracle_loss_grads(p.hidden[:rows], p.W, p.ids[:rows], p.tlogits[:rows], T=wl["T"], chunk=128)
+    dt = time.perf_counter() - t0
+    return dict(value=rows / dt, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"first {rows} positions of the workload (full H and V): fp64 loss, "
+                       f"dHidden and the dW contribution of those rows, row blocks of 128; {dt:.1f} s")
+
+
+def mem_sweep(kd, torch, sizes, seed=1004):
+    """Peak device memory of one fwd+bwd at the 256K-context shapes for several S."""
+    from kd_synth import make_problem
+    H, V, K, T, C = 3072, 128256, 100, 2.0, 2048
+    Smax = max(sizes)
+    log(f"[bench] generating memory-sweep inputs S<={Smax}")
+    p = make_problem(Smax, H, V, K, T=T, chunk=C, seed=seed)
+    out = {}
+    for S in sorted(sizes):
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        hidden = torch.from_numpy(p.hidden_bits[:S].view(np.int16)).view(torch.bfloat16).cuda()
+        W = torch.from_numpy(p.W_bits.view(np.int16)).view(torch.bfloat16).cuda()
+        ids = torch.from_numpy(p.ids[:S]).cuda()
+        tl = torch.from_numpy(p.tl_bits[:S].view(np.int16)).view(torch.bfloat16).cuda()
+        fo = kd.kd_topk_kl_fwd(hidden, W, ids, tl, T, C)
+        g = torch.ones(1, dtype=torch.float32, device="cuda")
+        dh, dW = kd.kd_topk_kl_bwd(hidden, W, ids, tl, fo["lse"], g, T, C)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        out[S] = peak / 2**30
+        log(f"[bench] mem S={S}: peak {out[S]:.3f} GiB (loss {float(fo['loss'][0]):.4f})")
+        del hidden, W, ids, tl, fo, dh, dW, g
+    xs = np.array(sorted(out), dtype=np.float64)
+    ys = np.array([out[s] for s in sorted(out)])
+    A = np.stack([np.ones_like(xs), xs], axis=1)
+    coef, *_ = np.linalg.lstsq(A, ys, rcond=None)
+    pred = A @ coef
+    r2 = 1.0 - float(np.sum((ys - pred) ** 2)) / max(float(np.sum((ys - ys.mean()) ** 2)), 1e-30)
+    return dict(shapes="H=3072 V=128256 K=100 T=2 chunk=2048 bf16",
+                peak_gib={str(int(k)): round(v, 4) for k, v in out.items()},
+                fit_intercept_gib=round(float(coef[0]), 4),
+                fit_kib_per_token=round(float(coef[1]) * 2**20, 3), r2=round(r2, 6))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--chunk", type=int, default=None)
+    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mem-sweep", action="store_true")
+    ap.add_argument("--mem-sizes", default="16384,32768,65536,131072,262144")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a device copy of this many MiB (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the loss shards by positions; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunked_top_kl_amd as kd
+    from kd_synth import make_problem
+
+    wl = dict(WORKLOADS[args.workload])
+    if args.chunk:
+        wl["chunk"] = args.chunk
+        wl["name"] = wl["name"].replace(f"chunk={WORKLOADS[args.workload]['chunk']}",
+                                        f"chunk={args.chunk}")
+    S, H, V, K, C = wl["S"], wl["H"], wl["V"], wl["K"], wl["chunk"]
+    log(f"[bench] generating inputs: {wl['name']}")
+    t0 = time.perf_counter()
+    p = make_problem(S, H, V, K, T=wl["T"], chunk=C, seed=wl["seed"])
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
+    t = to_dev(p, torch)
+    prob = kd.make_problem(S, H, V, K, C, wl["T"], kd.KD_BF16, kd.KD_BF16)
+    ws = torch.empty(kd.kd_workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * 2**20 // 4
+        a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
+        del a, b
+
+    step = (lambda: run_c5_step(kd, torch, wl, t, ws)) if args.workload == "c5" else \
+        (lambda: run_step(kd, torch, wl, t, ws))
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {i + 1}/{args.warmup} done")
+
+    torch.cuda.reset_peak_memory_stats()
+    kd.kd_profile_reset()
+    kd.kd_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        res = step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kd.kd_profile_enable(False)
+    prof = kd.kd_profile_read()
+    kd.kd_profile_reset()
+    peak_gib = torch.cuda.max_memory_allocated() / 2**30
+    ms = dt * 1000.0 / args.steps
+    log(f"[bench] {args.steps} steps in {dt:.3f} s: {ms:.2f} ms/step")
+
+    N_rows = S
+    if args.workload == "c5":
+        N_rows = int(res[1])
+    # counted MFMA work of one step
+    if args.workload == "c5":
+        flops = 2.0 * S * H * V + 8.0 * N_rows * H * V
+    else:
+        flops = 8.0 * S * H * V
+    mfma_frac = flops / (ms / 1000.0) / (PEAK_BF16_TFLOPS * 1e12)
+
+    kernels = {}
+    for name, (n, tot) in prof.items():
+        per = tot / max(n, 1)
+        rows = N_rows if name in ("fwd_lse_gather",) else S
+        f = kernel_flops(name, wl, C, rows if name != "entropy_sweep" else S)
+        if name in ("bwd_grad_tile", "bwd_dhidden", "bwd_dw"):
+            f = 8.0 * N_rows * H * V / 4.0 / max(n / args.steps, 1)   # per launch, averaged over chunks
+        kernels[name] = dict(launches_per_step=round(n / args.steps, 2), ms_per_step=round(tot / args.steps, 4),
+                             avg_ms=round(per, 5),
+                             tflops=(round(f / (per / 1000.0) / 1e12, 1) if f else None))
+    dom = max(kernels.items(), key=lambda kv: kv[1]["ms_per_step"])
+    dom_name, dom_v = dom
+    dom_flops = kernel_flops(dom_name, wl, C, N_rows)
+    if dom_name in ("bwd_grad_tile", "bwd_dhidden", "bwd_dw"):
+        dom_flops = 8.0 * N_rows * H * V / 4.0 / max(dom_v["launches_per_step"], 1)
+    achieved = dom_flops / (dom_v["avg_ms"] / 1000.0) / 1e12 if dom_flops else None
+    roofline = dict(kernel=dom_name, bound="mfma", achieved=round(achieved, 1) if achieved else None,
+                    peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 4) if achieved else None,
+                    traffic=None,
+                    flops_per_launch=dom_flops, avg_ms=dom_v["avg_ms"])
+
+    result = {
+        "metric": METRIC,
+        "value": round(S / (ms / 1000.0), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl["name"], "S": S, "H": H, "V": V, "K": K, "T": wl["T"],
+                   "chunk": C, "rows_in_loss": N_rows},
+        "mfma_frac": round(mfma_frac, 4),
+        "counted_tflop_per_step": round(flops / 1e12, 3),
+        "peak_gib": round(peak_gib, 3),
+        "loss": float(res[0][0]["loss"][0]) if args.workload == "c5" else float(res[0]["loss"][0]),
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_mem_sweep:
+        sizes = [int(x) for x in args.mem_sizes.split(",") if x]
+        del t, ws
+        torch.cuda.empty_cache()
+        result["peak_gib_vs_S"] = mem_sweep(kd, torch, sizes)
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows")
+        result["cpu_baseline"] = cpu_baseline(p, wl, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
