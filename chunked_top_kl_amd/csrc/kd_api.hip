@@ -106,12 +106,13 @@ int check_problem(const kd_problem* p) {
 struct Layout {
   size_t count, present, pos, idx, ids_s, p_s, korig_s, negH;
   size_t pm, ps, pd, bsum;
-  size_t G, Xc, dhp;
+  size_t G, GT, WT, XcT, dhp;
   size_t em, es, eu;
   size_t band, refined, scal, dscal, rpart, counters;
   size_t total;
   int64_t C;          // rows per backward chunk (<= S, >= 1)
   int64_t Vp;         // padded row length of the gradient tile
+  int64_t Cp;         // padded row length of the transposed chunk tiles
   int64_t esz;
 };
 
@@ -122,6 +123,7 @@ Layout plan(const kd_problem* p) {
   L.esz = p->hw_dtype == KD_F32 ? 4 : 2;
   L.C = p->chunk < S ? p->chunk : (S > 0 ? S : 1);
   L.Vp = round_up(V, 8);
+  L.Cp = round_up(L.C, 32);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -143,7 +145,9 @@ Layout plan(const kd_problem* p) {
   L.pd = take(pe * 4);
   L.bsum = take((ceil_div(Sx, 256) + 1) * 8);
   L.G = take(L.C * L.Vp * L.esz);
-  L.Xc = take(L.C * H * L.esz);
+  L.GT = take(L.Vp * L.Cp * L.esz);
+  L.WT = take(H * L.Vp * L.esz);
+  L.XcT = take(H * L.Cp * L.esz);
   int ksmax = 1;
   for (int64_t r = kd::kTile; r < L.C + kd::kTile; r += kd::kTile) {
     const int rows = (int)(r < L.C ? r : L.C);
@@ -317,22 +321,26 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
   const int nchunks = S > 0 ? (int)ceil_div(S, C) : 1;
   const int dgrid = kd::dh_grid(C, V, H, kCostCUs, f32);
   const int sgrid = kd::sweep_grid(C, V, kCostCUs);
+  const int Vp = (int)L.Vp, Cp = (int)L.Cp;
+  if (S > 0) {
+    Prof pr("transpose_w", st);
+    KD_HIP(kd::launch_transpose_w(f32, (const char*)W, V, H, at<char>(ws, L.WT), Vp, st));
+  }
   for (int ci = 0; ci < nchunks; ++ci) {
     const int row_begin = ci * C;
     if (S > 0) {
-      Prof pr("gather_rows", st);
-      KD_HIP(kd::launch_gather_rows((const char*)hidden, row_bytes, at<int32_t>(ws, L.idx),
-                                    at<int32_t>(ws, L.count), row_begin, C, row_bytes,
-                                    at<char>(ws, L.Xc), st));
+      Prof pr("gather_rows_t", st);
+      KD_HIP(kd::launch_gather_rows_t(f32, (const char*)hidden, row_bytes, at<int32_t>(ws, L.idx),
+                                      at<int32_t>(ws, L.count), row_begin, C, H,
+                                      at<char>(ws, L.XcT), (int64_t)Cp * L.esz, Cp, st));
     }
     if (S > 0) {
       kd::SweepArgs a;
       std::memset(&a, 0, sizeof(a));
       a.W = (const char*)W;
       a.ldw = row_bytes;
-      a.X = at<char>(ws, L.Xc);
+      a.X = (const char*)hidden;
       a.ldx = row_bytes;
-      a.x_row0 = 0;
       a.idx = at<int32_t>(ws, L.idx);
       a.nrows_dev = at<int32_t>(ws, L.count);
       a.row_begin = row_begin;
@@ -349,15 +357,17 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
       a.grad_loss = grad_loss;
       a.G = at<char>(ws, L.G);
       a.ldg = L.Vp * L.esz;
+      a.GT = at<char>(ws, L.GT);
+      a.ldgt = L.Cp * L.esz;
       Prof pr("bwd_grad_tile", st);
-      KD_HIP(kd::launch_sweep(kd::kSweepBwdG, f32, 0, a, sgrid, st));
+      KD_HIP(kd::launch_sweep(kd::kSweepBwdG, f32, 1, a, sgrid, st));
     }
     if (S > 0) {
       kd::DhArgs d;
       d.G = at<char>(ws, L.G);
       d.ldg = L.Vp * L.esz;
-      d.W = (const char*)W;
-      d.ldw = row_bytes;
+      d.WT = at<char>(ws, L.WT);
+      d.ldwt = L.Vp * L.esz;
       d.nrows_dev = at<int32_t>(ws, L.count);
       d.row_begin = row_begin;
       d.row_cap = C;
@@ -383,11 +393,11 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
       KD_HIP(kd::launch_dh_reduce(r, f32, st));
     }
     kd::DwArgs w;
-    w.G = at<char>(ws, L.G);
-    w.ldg = L.Vp * L.esz;
-    w.g_mn_bytes = L.Vp * L.esz;
-    w.Xc = at<char>(ws, L.Xc);
-    w.ldx = row_bytes;
+    w.GT = at<char>(ws, L.GT);
+    w.ldgt = L.Cp * L.esz;
+    w.Vp = Vp;
+    w.XcT = at<char>(ws, L.XcT);
+    w.ldxt = L.Cp * L.esz;
     w.nrows_dev = at<int32_t>(ws, L.count);
     w.row_begin = row_begin;
     w.row_cap = C;

@@ -11,29 +11,17 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
-// Tile geometry of every projection kernel.
-//   A work-group of 256 threads (4 wave64) computes a 256 x 256 output tile
-//   as 2 x 2 waves of 128 x 128, each wave 4 x 4 MFMA 32x32 blocks.
-//   One k-step stages 128 bytes of K per row (64 bf16 or 32 fp32) for both
-//   operands in LDS, double-buffered. LDS rows are padded to 144 bytes so that
-//   16 consecutive rows read at the same k-granule hit distinct banks.
+// Tile geometry of every projection kernel: a work-group of 256 threads
+// (4 wave64) computes a 256 x 256 output tile as 2 x 2 waves of 128 x 128,
+// each wave 4 x 4 MFMA 32x32 blocks. The staging pipeline is described in
+// kd_gemm_core.hpp.
 // ---------------------------------------------------------------------------
 constexpr int kThreads = 256;
 constexpr int kTile = 256;          // rows of each operand tile (M and N)
-constexpr int kStepBytes = 128;     // K bytes per row per k-step
-constexpr int kLdsRow = 144;        // padded LDS row stride in bytes
-constexpr int kLdsTile = kTile * kLdsRow;          // 36864 bytes
-constexpr int kLdsBytes = 4 * kLdsTile;            // A,B x double buffer = 147456
 
 template <typename T> struct Elem;
-template <> struct Elem<__bf16> {
-  static constexpr int size = 2;
-  static constexpr int per_step = 64;     // K elements per k-step
-};
-template <> struct Elem<float> {
-  static constexpr int size = 4;
-  static constexpr int per_step = 32;
-};
+template <> struct Elem<__bf16> { static constexpr int size = 2; };
+template <> struct Elem<float> { static constexpr int size = 4; };
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }

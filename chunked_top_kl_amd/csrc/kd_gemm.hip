@@ -1,8 +1,9 @@
 // Backward contractions of one chunk ("backward recomputes the chunk"):
 //   dHidden rows = G W        (K = vocabulary, split-K with a fixed-order reduce)
 //   dW          (+)= G^T X_c  (K = chunk rows, fp32 read-modify-write of dW)
-// plus the small row kernels around them (gather of the chunk's hidden rows,
-// zero rows for positions that take no part).
+// plus the small kernels around them (transposed gather of the chunk's hidden
+// rows, transpose of W, split-K reduce, zero rows for positions that take no
+// part). Every operand is read K-contiguous by the direct-to-LDS main loop.
 #include "kd_gemm_core.hpp"
 #include "kd_kernels.hpp"
 
@@ -16,17 +17,17 @@ __device__ inline int chunk_rows(const int32_t* nrows_dev, int row_begin, int ro
 
 // ---------------------------------------------------------------------------
 // dHidden partials: part[split][r][h] = sum_{v in split} G[r][v] W[v][h]
-//   M = chunk rows (A = G, [rows][Vp], K contiguous), N = h (B = W viewed as
-//   [K = V rows][N = H], MN contiguous -> transposing loader).
+//   M = chunk rows (A = G [rows][Vp]), N = h (B = W^T [H][Vp]); both operands
+//   K (= vocabulary) contiguous. The vocabulary is split into `ks` ranges.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
   const int rows = chunk_rows(a.nrows_dev, a.row_begin, a.row_cap);
   if (rows <= 0) return;
-  constexpr int esz = Elem<T>::size, kper = Elem<T>::per_step;
+  constexpr int esz = Elem<T>::size;
   const int mt = (int)ceil_div(rows, kTile), nt = (int)ceil_div(a.H, kTile);
-  const int nks_total = (int)ceil_div(a.V, kper);
+  const int nks_total = (int)ceil_div((int64_t)a.V * esz, kKB);
   const int ks = splitk_factor(mt * nt, nks_total, a.ncu);
   const int total = mt * nt * ks;
   if ((int)blockIdx.x >= total) return;
@@ -36,16 +37,15 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
   const int per = (int)ceil_div(nks_total, ks);
   const int kbeg = split * per;
   const int kend = (kbeg + per < nks_total) ? kbeg + per : nks_total;
-  const int nk = kend - kbeg;
+  const int nk = kend > kbeg ? kend - kbeg : 0;
 
-  LoaderKC la;
-  la.init(a.G + (int64_t)m * kTile * a.ldg, a.ldg, rows - m * kTile, (int64_t)kbeg * kStepBytes,
-          (int64_t)a.V * esz);
-  LoaderKS<T> lb;
-  lb.init(a.W + (int64_t)n * kTile * esz, a.ldw, kbeg * kper, a.V,
-          (int64_t)(a.H - n * kTile) * esz);
+  DmaOperand la, lb;
+  la.init(a.G + (int64_t)m * kTile * a.ldg, a.ldg, rows - m * kTile, (int64_t)kbeg * kKB,
+          (int64_t)a.V * esz, 0);
+  lb.init(a.WT + (int64_t)n * kTile * a.ldwt, a.ldwt, a.H - n * kTile, (int64_t)kbeg * kKB,
+          (int64_t)a.V * esz, 1);
   floatx16 acc[4][4];
-  gemm_mainloop<T>(acc, la, lb, nk > 0 ? nk : 0, lds);
+  gemm_mainloop<T>(acc, la, lb, nk, lds);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
   float* part = a.part + (int64_t)split * a.row_cap * a.H;
@@ -64,9 +64,9 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
 }
 
 __host__ __device__ int dh_splits(int rows, int V, int H, int ncu, int f32) {
-  const int kper = f32 ? Elem<float>::per_step : Elem<__bf16>::per_step;
+  const int esz = f32 ? 4 : 2;
   const int mt = (int)ceil_div(rows, kTile), nt = (int)ceil_div(H, kTile);
-  return splitk_factor(mt * nt, (int)ceil_div(V, kper), ncu);
+  return splitk_factor(mt * nt, (int)ceil_div((int64_t)V * esz, kKB), ncu);
 }
 
 int dh_grid(int row_cap, int V, int H, int ncu, int f32) {
@@ -140,51 +140,95 @@ hipError_t launch_zero_invalid_rows(const int32_t* pos, int64_t S, int H, float*
   return hipGetLastError();
 }
 
-// out[r] = X[idx[row_begin + r]] for the chunk's rows (16-byte copies)
-__global__ __launch_bounds__(256) void gather_rows_kernel(const char* X, int64_t ldx,
-                                                          const int32_t* idx,
-                                                          const int32_t* nrows_dev, int row_begin,
-                                                          int row_cap, int64_t row_bytes,
-                                                          char* out) {
+// out[h][r] = X[idx[row_begin + r]][h] for the chunk's rows r < rows and
+// out[h][r] = 0 for rows <= r < Cp (the gathered rows, transposed: the dW
+// product reads them with K = chunk rows contiguous). 64 x 64 tiles via LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void gather_rows_t_kernel(const char* X, int64_t ldx,
+                                                            const int32_t* idx,
+                                                            const int32_t* nrows_dev,
+                                                            int row_begin, int row_cap, int H,
+                                                            char* out, int64_t ldo, int Cp) {
+  __shared__ T tile[64][65];
   const int rows = chunk_rows(nrows_dev, row_begin, row_cap);
   if (rows <= 0) return;
-  const int64_t g = row_bytes / 16;
-  const int64_t total = (int64_t)rows * g;
-  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total;
-       q += (int64_t)gridDim.x * 256) {
-    const int64_t r = q / g, c = q % g;
-    const int orow = idx[row_begin + r];
-    *(uint4*)(out + r * row_bytes + c * 16) = *(const uint4*)(X + (int64_t)orow * ldx + c * 16);
+  const int r0 = blockIdx.x * 64, h0 = blockIdx.y * 64;
+  if (r0 >= Cp) return;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int rr = ty; rr < 64; rr += 4) {
+    const int r = r0 + rr, h = h0 + tx;
+    T v = (T)0.0f;
+    if (r < rows && h < H) v = ((const T*)(X + (int64_t)idx[row_begin + r] * ldx))[h];
+    tile[rr][tx] = v;
+  }
+  __syncthreads();
+  for (int hh = ty; hh < 64; hh += 4) {
+    const int h = h0 + hh, r = r0 + tx;
+    if (h < H && r < Cp) ((T*)(out + (int64_t)h * ldo))[r] = tile[tx][hh];
   }
 }
 
-hipError_t launch_gather_rows(const char* X, int64_t ldx, const int32_t* idx,
-                              const int32_t* nrows_dev, int row_begin, int row_cap,
-                              int64_t row_bytes, char* out, hipStream_t st) {
-  int64_t grid = ceil_div((int64_t)row_cap * (row_bytes / 16), 256);
-  if (grid > 8192) grid = 8192;
-  if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(gather_rows_kernel, dim3((int)grid), dim3(256), 0, st, X, ldx, idx,
-                     nrows_dev, row_begin, row_cap, row_bytes, out);
+hipError_t launch_gather_rows_t(int f32, const char* X, int64_t ldx, const int32_t* idx,
+                                const int32_t* nrows_dev, int row_begin, int row_cap, int H,
+                                char* out, int64_t ldo, int Cp, hipStream_t st) {
+  dim3 grid((unsigned)ceil_div(Cp, 64), (unsigned)ceil_div(H, 64));
+  if (f32)
+    hipLaunchKernelGGL(gather_rows_t_kernel<float>, grid, dim3(256), 0, st, X, ldx, idx, nrows_dev,
+                       row_begin, row_cap, H, out, ldo, Cp);
+  else
+    hipLaunchKernelGGL(gather_rows_t_kernel<__bf16>, grid, dim3(256), 0, st, X, ldx, idx,
+                       nrows_dev, row_begin, row_cap, H, out, ldo, Cp);
+  return hipGetLastError();
+}
+
+// WT[h][v] = W[v][h] for v < V, 0 for V <= v < Vp (64 x 64 tiles via LDS)
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_w_kernel(const T* W, int V, int H, T* WT,
+                                                          int Vp) {
+  __shared__ T tile[64][65];
+  const int v0 = blockIdx.x * 64, h0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int vv = ty; vv < 64; vv += 4) {
+    const int v = v0 + vv, h = h0 + tx;
+    T x = (T)0.0f;
+    if (v < V && h < H) x = W[(int64_t)v * H + h];
+    tile[vv][tx] = x;
+  }
+  __syncthreads();
+  for (int hh = ty; hh < 64; hh += 4) {
+    const int h = h0 + hh, v = v0 + tx;
+    if (h < H && v < Vp) WT[(int64_t)h * Vp + v] = tile[tx][hh];
+  }
+}
+
+hipError_t launch_transpose_w(int f32, const char* W, int V, int H, char* WT, int Vp,
+                              hipStream_t st) {
+  dim3 grid((unsigned)ceil_div(Vp, 64), (unsigned)ceil_div(H, 64));
+  if (f32)
+    hipLaunchKernelGGL(transpose_w_kernel<float>, grid, dim3(256), 0, st, (const float*)W, V, H,
+                       (float*)WT, Vp);
+  else
+    hipLaunchKernelGGL(transpose_w_kernel<__bf16>, grid, dim3(256), 0, st, (const __bf16*)W, V,
+                       H, (__bf16*)WT, Vp);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // dW[v][h] (+)= sum_r G[r][v] X_c[r][h]
-//   M = v (A = G^T: G is [K = rows][MN = Vp]), N = h (B = X_c: [K = rows][N = H]);
-//   both operands go through the transposing loader. Chunk 0 with
+//   M = v (A = G^T [Vp][Cp]), N = h (B = X_c^T [H][Cp]); K = chunk rows,
+//   contiguous in both. Chunk 0 with
 //   beta_first = 0 overwrites dW (and writes zeros when the chunk is empty);
 //   later chunks add, and return at once when they hold no rows.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256, 1) void dw_kernel(DwArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
   int rows = chunk_rows(a.nrows_dev, a.row_begin, a.row_cap);
   if (rows <= 0) {
     if (a.row_begin > 0) return;
     rows = 0;
   }
-  constexpr int esz = Elem<T>::size, kper = Elem<T>::per_step;
+  constexpr int esz = Elem<T>::size;
   const int mt = (int)ceil_div(a.V, kTile), nt = (int)ceil_div(a.H, kTile);
   const int total = mt * nt;
   if ((int)blockIdx.x >= total) return;
@@ -197,29 +241,36 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DwArgs a) {
   const int in = L % (GM * nt);
   const int m = first_m + in % gsz, n = in / gsz;
 
-  LoaderKS<T> la;
-  la.init(a.G + (int64_t)m * kTile * esz, a.ldg, 0, rows, a.g_mn_bytes - (int64_t)m * kTile * esz);
-  LoaderKS<T> lb;
-  lb.init(a.Xc + (int64_t)n * kTile * esz, a.ldx, 0, rows, (int64_t)(a.H - n * kTile) * esz);
+  DmaOperand la, lb;
+  la.init(a.GT + (int64_t)m * kTile * a.ldgt, a.ldgt, a.Vp - m * kTile, 0, (int64_t)rows * esz, 0);
+  lb.init(a.XcT + (int64_t)n * kTile * a.ldxt, a.ldxt, a.H - n * kTile, 0, (int64_t)rows * esz, 1);
   floatx16 acc[4][4];
-  gemm_mainloop<T>(acc, la, lb, (int)ceil_div(rows, kper), lds);
+  gemm_mainloop<T>(acc, la, lb, (int)ceil_div((int64_t)rows * esz, kKB), lds);
 
   const bool beta = (a.row_begin > 0) || a.beta_first;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  // 16 rows of one 32x32 block per step: all loads of the block are issued
+  // before any store, so the read-modify-write streams instead of serialising
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int h = n * kTile + wn * 128 + j * 32 + (lane & 31);
-    if (h >= a.H) continue;
+    const bool hok = h < a.H;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const int v0 = m * kTile + wm * 128 + i * 32 + 4 * (lane >> 5);
+      float* base = a.dW + (int64_t)v0 * a.H + h;
+      float old[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int v = m * kTile + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (v < a.V) {
-          float* p = a.dW + (int64_t)v * a.H + h;
-          *p = beta ? *p + acc[i][j][r] : acc[i][j][r];
-        }
+        const int v = v0 + 8 * (r >> 2) + (r & 3);
+        old[r] = (beta && hok && v < a.V) ? base[(int64_t)(8 * (r >> 2) + (r & 3)) * a.H] : 0.0f;
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = v0 + 8 * (r >> 2) + (r & 3);
+        if (hok && v < a.V) base[(int64_t)(8 * (r >> 2) + (r & 3)) * a.H] = old[r] + acc[i][j][r];
+      }
+    }
   }
 }
 

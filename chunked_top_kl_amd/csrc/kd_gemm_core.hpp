@@ -2,14 +2,21 @@
 //
 // Computes a 256 x 256 fp32 tile  acc[m][n] = sum_k A[m][k] * B[k][n]  with
 // v_mfma_f32_32x32x16_bf16 (bf16 operands) or v_mfma_f32_32x32x2_f32 (fp32
-// operands). Operands are staged through LDS in a K-contiguous layout
-// ([row][k], 144-byte padded rows), double-buffered, one k-step (128 bytes of
-// K per row) at a time. Two global layouts are supported per operand:
-//   LoaderKC - operand stored [MN rows][K] (K contiguous), optional row map;
-//   LoaderKS - operand stored [K rows][MN] (MN contiguous): each thread loads
-//              an 8 x 8 (bf16) or 8 x 4 (fp32) block and transposes it in
-//              registers before the LDS store, so the MFMA loop is the same.
-// Out-of-range rows and K columns are loaded as zeros.
+// operands). Both operands are stored row-major with K contiguous
+// ([rows][K]); the tile's rows are contiguous in memory (a row stride `ld`).
+//
+// Data path: global memory -> LDS by direct buffer loads (buffer_load_dwordx4
+// ... lds: each lane's 16 bytes land at M0 + 16*lane, no register staging),
+// through two LDS stages of 128 bytes of K per row (whole cache lines), then
+// LDS -> registers (ds_read_b128) -> MFMA. The loads of stage k+2 are issued
+// as soon as stage k has been read into registers. Rows and K bytes outside
+// the operand read as zero (buffer range checks). The loads are issued from inline assembly so that the compiler does
+// not order every LDS read behind them; their completion is awaited explicitly
+// with s_waitcnt vmcnt before the stage barrier.
+//
+// LDS layout of one operand stage: 256 rows x 128 bytes, the eight 16-byte
+// granules of row r permuted by g ^ ((r >> 1) & 7) so that the 16 rows read
+// together by an MFMA fragment load fall in distinct banks.
 //
 // Result layout (per wave w = 2*wm + wn, lane l, block (i, j), register r):
 //   m = wm*128 + i*32 + 8*(r/4) + 4*(l/32) + r%4,   n = wn*128 + j*32 + l%32.
@@ -19,243 +26,216 @@
 
 namespace kd {
 
-__device__ inline uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+constexpr int kStages = 2;
+constexpr int kKB = 128;                         // K bytes per row per stage (a cache line)
+constexpr int kStageOp = kTile * kKB;            // 32 KB: one operand of one stage
+constexpr int kStageBytes = 2 * kStageOp;        // 64 KB
+constexpr int kMainLds = kStages * kStageBytes;  // 128 KB
+constexpr uint32_t kOob = 0x80000000u;           // an offset at or past this reads zero
 
-// Raw buffer resource over [p, p + bytes): loads at offsets >= bytes return 0.
-// Callers keep bytes < 2^31 and mark a lane's load invalid by adding kOob.
-constexpr uint32_t kOob = 0x80000000u;
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+
+// Raw buffer resource over [p, p + bytes) (bytes clamped below 2^31).
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
   if (bytes < 0) bytes = 0;
   if (bytes > 0x7FFFFFFFll) bytes = 0x7FFFFFFFll;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
-__device__ inline uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+
+// 16 bytes per lane from rs at voff into LDS at m0 + 16 * lane.
+__device__ __forceinline__ void dma16(uint32_t m0, uint32_t voff, __amdgpu_buffer_rsrc_t rs) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(voff), "s"(rs) : "memory", "m0");
+}
+
+// Opaque copy: keeps the compiler from hoisting per-tile address arithmetic
+// out of the tile loop (which would keep it live, and spilled, across the
+// epilogues).
+template <typename X>
+__device__ __forceinline__ X opaque(X x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // ---------------------------------------------------------------------------
-// [MN][K] operand with contiguous rows (no map): one buffer resource per tile.
-// Thread t loads rows (t>>3) + 32*i (i < 8), 16-byte granule t&7 of a k-step.
+// One operand tile: 256 rows starting at `tile0`, row stride `ld` bytes,
+// `rows_valid` rows inside the operand, K bytes [kb0, kb_lim) of each row.
+// Wave w fills rows [64w, 64w + 64) of each stage with 8 loads of 8 rows.
 // ---------------------------------------------------------------------------
-struct LoaderKC {
+struct DmaOperand {
   __amdgpu_buffer_rsrc_t rs;
-  uint32_t voff, rstride;
+  uint32_t voff;      // lane's offset for load q = 0 (row and permuted granule)
+  uint32_t qstride;   // 8 rows
+  uint32_t gofs;      // lane's granule offset inside the 128-byte stage row
+  uint32_t ldsoff;    // operand and wave block inside a stage
   int64_t kb0, kb_lim;
 
-  // tile0: address of the tile's first row; ld: row stride (bytes);
-  // rows_valid: rows of the tile inside the operand; kb0: first K byte of
-  // k-step 0; kb_lim: valid K bytes per row.
   __device__ void init(const char* tile0, int64_t ld, int rows_valid, int64_t kb0_,
-                       int64_t kb_lim_) {
-    const int t = threadIdx.x;
+                       int64_t kb_lim_, int operand) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     if (rows_valid > kTile) rows_valid = kTile;
     rs = make_rsrc(tile0, rows_valid > 0 ? (int64_t)rows_valid * ld : 0);
-    voff = (uint32_t)((t >> 3) * ld + (t & 7) * 16);
-    rstride = (uint32_t)(32 * ld);
+    // lane -> row w*64 + 8q + lane/8, physical granule lane%8; the swizzle
+    // term ((8q + lane/8) >> 1) & 7 is (lane >> 4) for even q and (lane >> 4) ^ 4
+    // for odd q
+    const int row = lane >> 3;
+    const int g = (lane & 7) ^ (lane >> 4);
+    gofs = (uint32_t)(g * 16);
+    voff = opaque((uint32_t)((w * 64 + row) * ld) + gofs);
+    qstride = (uint32_t)(8 * ld);
+    ldsoff = (uint32_t)(operand * kStageOp + w * 64 * kKB);
     kb0 = kb0_;
     kb_lim = kb_lim_;
   }
-  __device__ void load(int kt, uint4 (&r)[8]) const {
-    const int64_t kb = kb0 + (int64_t)kt * kStepBytes;
-    uint32_t vo = voff + (uint32_t)kb;
-    if (kb + kStepBytes > kb_lim && kb + (threadIdx.x & 7) * 16 >= kb_lim) vo += kOob;
+  // enqueue the 8 loads of stage kt into the stage at LDS address `stage`
+  __device__ __forceinline__ void issue(int kt, uint32_t stage) const {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = bload(rs, vo + i * rstride);
+    for (int q = 0; q < 8; ++q) issue_one(kt, stage, q);
   }
-  __device__ void store(char* tile, const uint4 (&r)[8]) const {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *(uint4*)(tile + ((t >> 3) + 32 * i) * kLdsRow + (t & 7) * 16) = r[i];
+  // load q (rows 8q .. 8q+7 of this wave's 64-row block) of stage kt
+  __device__ __forceinline__ void issue_one(int kt, uint32_t stage, int q) const {
+    const int64_t kb = kb0 + (int64_t)kt * kKB;
+    // odd q: granule g ^ 4, i.e. 64 bytes further or back inside the row
+    const uint32_t gq = (q & 1) ? (gofs ^ 64u) : gofs;
+    uint32_t o = voff - gofs + gq + (uint32_t)kb + q * qstride;
+    if (kb + kKB > kb_lim && kb + gq >= kb_lim) o = kOob;
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(stage + ldsoff);
+    dma16(m0 + q * 1024, o, rs);
   }
 };
 
+// 16 bytes per lane from the 64-bit address `ga` into LDS at m0 + 16 * lane.
+__device__ __forceinline__ void dma16_global(uint32_t m0, const char* ga) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(m0), "v"(ga) : "memory", "m0");
+}
+
 // ---------------------------------------------------------------------------
-// [MN][K] operand whose rows are gathered through a row map (hidden rows of
-// the selected / compacted positions): 64-bit addressed global loads.
+// Operand tile whose rows are gathered through a row map (selected or
+// compacted positions): 64-bit per-lane addresses, no range checks. Rows past
+// mn_lim repeat the tile's first row and K granules past kb_lim re-read the
+// row's first granule: both only feed outputs that are discarded or products
+// with the other operand's exact zeros, so the data only has to be finite.
 // ---------------------------------------------------------------------------
-struct LoaderKCMap {
+struct DmaOperandMap {
   const char* base;
   int64_t ld;
-  int srow[8];
-  uint32_t rowmask;
+  int srow[8];           // lane's storage row for load q
+  uint32_t gofs, ldsoff;
   int64_t kb0, kb_lim;
 
-  // map: logical row -> storage row; mn0: first logical row of the tile;
-  // mn_lim: number of valid logical rows.
   __device__ void init(const char* base_, int64_t ld_, const int32_t* map, int mn0, int mn_lim,
-                       int64_t kb0_, int64_t kb_lim_) {
-    const int t = threadIdx.x;
+                       int64_t kb0_, int64_t kb_lim_, int operand) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int row = lane >> 3;
+    const int g = (lane & 7) ^ (lane >> 4);   // even q; odd q use g ^ 4
     base = base_;
     ld = ld_;
-    kb0 = kb0_ + (t & 7) * 16;
+    gofs = (uint32_t)(g * 16);
+    ldsoff = (uint32_t)(operand * kStageOp + w * 64 * kKB);
+    const int first = map[mn0];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int r = mn0 + w * 64 + q * 8 + row;
+      srow[q] = opaque(r < mn_lim ? map[r] : first);
+    }
+    kb0 = kb0_;
     kb_lim = kb_lim_;
-    rowmask = 0;
-    const int safe = map[mn0];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = mn0 + (t >> 3) + 32 * i;
-      const bool ok = row < mn_lim;
-      srow[i] = ok ? map[row] : safe;
-      rowmask |= (ok ? 1u : 0u) << i;
-    }
   }
-  __device__ void load(int kt, uint4 (&r)[8]) const {
-    const int64_t kb = kb0 + (int64_t)kt * kStepBytes;
-    const bool kok = kb < kb_lim;
-    const int64_t kbs = kok ? kb : (kb0 & (kStepBytes - 1));
+  __device__ __forceinline__ void issue(int kt, uint32_t stage) const {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint4 v = *(const uint4*)(base + (int64_t)srow[i] * ld + kbs);
-      const bool ok = kok && ((rowmask >> i) & 1u);
-      r[i] = ok ? v : zero4();
-    }
+    for (int q = 0; q < 8; ++q) issue_one(kt, stage, q);
   }
-  __device__ void store(char* tile, const uint4 (&r)[8]) const {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *(uint4*)(tile + ((t >> 3) + 32 * i) * kLdsRow + (t & 7) * 16) = r[i];
+  __device__ __forceinline__ void issue_one(int kt, uint32_t stage, int q) const {
+    const int64_t kb = kb0 + (int64_t)kt * kKB;
+    const uint32_t gq = (q & 1) ? (gofs ^ 64u) : gofs;
+    const int64_t o = (kb + gq < kb_lim) ? kb + gq : 0;
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(stage + ldsoff);
+    dma16_global(m0 + q * 1024, base + (int64_t)srow[q] * ld + o);
   }
 };
 
 // ---------------------------------------------------------------------------
-// [K][MN] operand (MN contiguous). A buffer resource is formed per k-step
-// over the k-step's K rows.
-//   bf16: thread t takes k-group kg = t&7 (8 rows) and MN granule mg = t>>3
-//         (8 elements); one k-step covers 64 K rows x 256 MN.
-//   fp32: kg = t&3, mg = t>>2 (4 elements); 32 K rows x 256 MN.
+// MFMAs of one sub-step (K = 16 bf16 / 8 fp32; a stage holds four).
 // ---------------------------------------------------------------------------
-template <typename T>
-struct LoaderKS {
-  static constexpr int kKRows = 128 / (int)sizeof(T);   // K rows per k-step: 64 | 32
-  static constexpr int kKG = kKRows / 8;                 // k-groups of 8 rows: 8 | 4
-  const char* base;
-  int64_t ld;
-  int k0, k_lim;
-  uint32_t voff;
-
-  // base: address of (K row 0, first MN column of the tile); ld: row stride
-  // (bytes); k0/k_lim: first K row of k-step 0 and the valid K rows;
-  // mn_valid_bytes: bytes of the tile's MN extent inside the operand.
-  __device__ void init(const char* base_, int64_t ld_, int k0_, int k_lim_,
-                       int64_t mn_valid_bytes) {
-    const int t = threadIdx.x;
-    base = base_;
-    ld = ld_;
-    k0 = k0_;
-    k_lim = k_lim_;
-    const int kg = t % kKG, mg = t / kKG;
-    voff = (uint32_t)(kg * 8 * ld + mg * 16);
-    if ((int64_t)mg * 16 >= mn_valid_bytes) voff += kOob;
-  }
-  __device__ void load(int kt, uint4 (&r)[8]) const {
-    const int kr = k0 + kt * kKRows;
-    const int nrows = k_lim - kr;
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(base + (int64_t)kr * ld, nrows > 0 ? (int64_t)(nrows < kKRows ? nrows : kKRows) * ld : 0);
+__device__ __forceinline__ void mfma16(floatx16 (&acc)[4][4], const bf16x8 (&a)[4],
+                                       const bf16x8 (&b)[4]) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = bload(rs, voff + (uint32_t)(e * ld));
-  }
-  __device__ void store(char* tile, const uint4 (&r)[8]) const;
-};
-
-template <>
-__device__ inline void LoaderKS<__bf16>::store(char* tile, const uint4 (&r)[8]) const {
-  const int t = threadIdx.x;
-  const int kg = t & 7, mg = t >> 3;
-  // element n of K row e sits in dword n/2, half n%2 of r[e]
-  const uint32_t* w = (const uint32_t*)r;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const int d = n >> 1;
-    uint4 o;
-    if (n & 1) {
-      o.x = (w[0 * 4 + d] >> 16) | (w[1 * 4 + d] & 0xFFFF0000u);
-      o.y = (w[2 * 4 + d] >> 16) | (w[3 * 4 + d] & 0xFFFF0000u);
-      o.z = (w[4 * 4 + d] >> 16) | (w[5 * 4 + d] & 0xFFFF0000u);
-      o.w = (w[6 * 4 + d] >> 16) | (w[7 * 4 + d] & 0xFFFF0000u);
-    } else {
-      o.x = (w[0 * 4 + d] & 0xFFFFu) | (w[1 * 4 + d] << 16);
-      o.y = (w[2 * 4 + d] & 0xFFFFu) | (w[3 * 4 + d] << 16);
-      o.z = (w[4 * 4 + d] & 0xFFFFu) | (w[5 * 4 + d] << 16);
-      o.w = (w[6 * 4 + d] & 0xFFFFu) | (w[7 * 4 + d] << 16);
-    }
-    *(uint4*)(tile + (mg * 8 + n) * kLdsRow + kg * 16) = o;
-  }
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
-template <>
-__device__ inline void LoaderKS<float>::store(char* tile, const uint4 (&r)[8]) const {
-  const int t = threadIdx.x;
-  const int kg = t & 3, mg = t >> 2;
-  const uint32_t* w = (const uint32_t*)r;   // w[e*4 + n]
+__device__ __forceinline__ void mfma16(floatx16 (&acc)[4][4], const floatx4 (&a)[4],
+                                       const floatx4 (&b)[4]) {
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    uint4 lo = make_uint4(w[0 * 4 + n], w[1 * 4 + n], w[2 * 4 + n], w[3 * 4 + n]);
-    uint4 hi = make_uint4(w[4 * 4 + n], w[5 * 4 + n], w[6 * 4 + n], w[7 * 4 + n]);
-    char* row = tile + (mg * 4 + n) * kLdsRow + kg * 32;
-    *(uint4*)(row) = lo;
-    *(uint4*)(row + 16) = hi;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// One k-step of MFMAs on the staged tiles (4 sub-steps).
-// ---------------------------------------------------------------------------
-template <typename T>
-__device__ inline void mfma_step(floatx16 (&acc)[4][4], const char* A, const char* B, int wm,
-                                 int wn, int lane);
-
-template <>
-__device__ inline void mfma_step<__bf16>(floatx16 (&acc)[4][4], const char* A, const char* B,
-                                         int wm, int wn, int lane) {
-  const char* pa = A + (wm * 128 + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
-  const char* pb = B + (wn * 128 + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    bf16x8 a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)(pa + i * 32 * kLdsRow + s * 32);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8*)(pb + j * 32 * kLdsRow + s * 32);
+  for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][q], b[j][q], acc[i][j], 0, 0, 0);
 }
 
-template <>
-__device__ inline void mfma_step<float>(floatx16 (&acc)[4][4], const char* A, const char* B,
-                                        int wm, int wn, int lane) {
-  const char* pa = A + (wm * 128 + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
-  const char* pb = B + (wn * 128 + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
+template <typename T> struct Frag;
+template <> struct Frag<__bf16> { using type = bf16x8; };
+template <> struct Frag<float> { using type = floatx4; };
+
+// Per-lane fragment addressing inside a stage: rows wm*128 + i*32 + (l & 31)
+// (A) and wn*128 + j*32 + (l & 31) (B), logical granule 2s + (l >> 5) for
+// sub-step s.
+struct FragAddr {
+  uint32_t a[4], b[4];
+  __device__ void init(int wm, int wn, int lane) {
+    const int r = lane & 31, swz = (r >> 1) & 7, half = lane >> 5;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    floatx4 a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *(const floatx4*)(pa + i * 32 * kLdsRow + s * 32);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *(const floatx4*)(pb + j * 32 * kLdsRow + s * 32);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][q], b[j][q], acc[i][j], 0, 0, 0);
+    for (int s = 0; s < 4; ++s) {
+      const int pg = (2 * s + half) ^ swz;
+      a[s] = (uint32_t)((wm * 128 + r) * kKB + pg * 16);
+      b[s] = (uint32_t)(kStageOp + (wn * 128 + r) * kKB + pg * 16);
+    }
   }
-}
+};
 
 // ---------------------------------------------------------------------------
-// Double-buffered main loop over nk k-steps. Every thread of the work-group
-// must call it with the same nk. LDS: A0 | B0 | A1 | B1 (kLdsBytes).
+// Main loop over nk stages (nk = ceil(K bytes / 128)). Every thread of the
+// work-group must call it with the same nk. `lds` points at kMainLds bytes.
+//
+// Stage kt has four sub-steps of 16 MFMAs; the fragments of sub-step s+1 are
+// read while sub-step s computes. Before the last sub-step: wait for this
+// wave's loads of stage kt+1, barrier (stage kt+1 visible to all waves, and
+// every wave holds its stage-kt fragments, so stage kt's buffer is free),
+// loads of stage kt+2 into that buffer, and the sub-step-0 fragments of
+// stage kt+1 - all while the last 16 MFMAs of stage kt run.
 // ---------------------------------------------------------------------------
-template <typename T, class LA, class LB>
-__device__ inline void gemm_mainloop(floatx16 (&acc)[4][4], const LA& la, const LB& lb, int nk,
+template <typename V>
+struct SubFrags {
+  V a[4], b[4];
+};
+
+template <class V>
+__device__ __forceinline__ void read_sub(SubFrags<V>& f, const char* stage, const FragAddr& fa,
+                                         int s) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.a[i] = *(const V*)(stage + fa.a[s] + i * 32 * kKB);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.b[j] = *(const V*)(stage + fa.b[s] + j * 32 * kKB);
+}
+
+template <typename T, class OA, class OB>
+__device__ inline void gemm_mainloop(floatx16 (&acc)[4][4], const OA& la, const OB& lb, int nk,
                                      char* lds) {
+  using V = typename Frag<T>::type;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -264,27 +244,52 @@ __device__ inline void gemm_mainloop(floatx16 (&acc)[4][4], const LA& la, const 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   if (nk <= 0) return;
-  uint4 ra[8], rb[8];
-  la.load(0, ra);
-  lb.load(0, rb);
-  la.store(lds, ra);
-  lb.store(lds + kLdsTile, rb);
+  FragAddr fa;
+  fa.init(wm, wn, lane);
+  const uint32_t base = lds_addr(lds);
+  // every wave has finished reading the stages of a previous call
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    char* cur = lds + (kt & 1) * 2 * kLdsTile;
-    char* nxt = lds + ((kt + 1) & 1) * 2 * kLdsTile;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      la.load(kt + 1, ra);
-      lb.load(kt + 1, rb);
-    }
-    mfma_step<T>(acc, cur, cur + kLdsTile, wm, wn, lane);
-    if (more) {
-      la.store(nxt, ra);
-      lb.store(nxt + kLdsTile, rb);
-    }
-    __syncthreads();
+  la.issue(0, base);
+  lb.issue(0, base);
+  if (nk > 1) {
+    la.issue(1, base + kStageBytes);
+    lb.issue(1, base + kStageBytes);
+    wait_vmcnt<16>();
+  } else {
+    wait_vmcnt<0>();
   }
+  __syncthreads();
+  SubFrags<V> f0, f1;
+  read_sub(f0, lds, fa, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* stage = lds + (kt & 1) * kStageBytes;
+    __builtin_amdgcn_sched_barrier(0);
+    read_sub(f1, stage, fa, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma16(acc, f0.a, f0.b);
+    __builtin_amdgcn_sched_barrier(0);
+    read_sub(f0, stage, fa, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma16(acc, f1.a, f1.b);
+    __builtin_amdgcn_sched_barrier(0);
+    read_sub(f1, stage, fa, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma16(acc, f0.a, f0.b);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) {
+      // the loads of stage kt+1 are this wave's oldest outstanding ones
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (kt + 2 < nk) {
+        la.issue(kt + 2, base + (kt & 1) * kStageBytes);
+        lb.issue(kt + 2, base + (kt & 1) * kStageBytes);
+      }
+      read_sub(f0, lds + ((kt + 1) & 1) * kStageBytes, fa, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mfma16(acc, f1.a, f1.b);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 }  // namespace kd

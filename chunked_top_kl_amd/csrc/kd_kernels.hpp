@@ -28,6 +28,7 @@ struct SweepArgs {
   // backward
   const float* lse; const float* grad_loss;
   char* G; int64_t ldg;               // gradient tile [row_cap, Vp], bytes per row
+  char* GT; int64_t ldgt;             // the same tile transposed [Vp, Cp]
   // entropy partials
   float* em; double* es; double* eu;
 };
@@ -52,7 +53,7 @@ struct EntCombineArgs {
 
 struct DhArgs {
   const char* G; int64_t ldg;         // [rows, Vp]
-  const char* W; int64_t ldw;         // [V, H]
+  const char* WT; int64_t ldwt;       // W transposed [H, Vp]
   const int32_t* nrows_dev;
   int row_begin, row_cap, V, H, ncu;
   float* part;                        // [split][row_cap][H] fp32
@@ -65,8 +66,8 @@ struct DhReduceArgs {
 };
 
 struct DwArgs {
-  const char* G; int64_t ldg; int64_t g_mn_bytes;   // G: [rows, Vp]
-  const char* Xc; int64_t ldx;                      // gathered hidden rows [rows, H]
+  const char* GT; int64_t ldgt; int Vp;             // gradient tile transposed [Vp, Cp]
+  const char* XcT; int64_t ldxt;                    // gathered hidden rows transposed [H, Cp]
   const int32_t* nrows_dev;
   int row_begin, row_cap, V, H, beta_first;
   float* dW;
@@ -83,9 +84,11 @@ hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid
 int sweep_grid(int64_t rows_max, int V, int ncu);
 hipError_t launch_fwd_combine(const CombineArgs& a, hipStream_t st);
 hipError_t launch_ent_combine(const EntCombineArgs& a, hipStream_t st);
-hipError_t launch_gather_rows(const char* X, int64_t ldx, const int32_t* idx,
-                              const int32_t* nrows_dev, int row_begin, int row_cap,
-                              int64_t row_bytes, char* out, hipStream_t st);
+hipError_t launch_gather_rows_t(int f32, const char* X, int64_t ldx, const int32_t* idx,
+                                const int32_t* nrows_dev, int row_begin, int row_cap, int H,
+                                char* out, int64_t ldo, int Cp, hipStream_t st);
+hipError_t launch_transpose_w(int f32, const char* W, int V, int H, char* WT, int Vp,
+                              hipStream_t st);
 hipError_t launch_zero_invalid_rows(const int32_t* pos, int64_t S, int H, float* dH,
                                     hipStream_t st);
 hipError_t launch_dh(int f32, const DhArgs& a, int grid, hipStream_t st);

@@ -99,10 +99,10 @@ __device__ __forceinline__ void walk_hits(Cursor& c, const int32_t* ids_s, int K
 
 template <typename T, int KIND, bool MAP>
 __global__ __launch_bounds__(256, 1) void sweep_kernel(SweepArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + 4 * 4096];
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds + 4 * 4096];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int half = lane >> 5;
-  float* slot = (float*)(lds + kLdsBytes + w * 4096 + lane * 64);
+  float* slot = (float*)(lds + kMainLds + w * 4096 + lane * 64);
 
   int rows = a.row_cap;
   if (a.nrows_dev) {
@@ -122,17 +122,9 @@ __global__ __launch_bounds__(256, 1) void sweep_kernel(SweepArgs a) {
 
   constexpr int esz = Elem<T>::size;
   const int64_t kbytes = (int64_t)a.H * esz;
-  const int nk = (int)ceil_div(kbytes, kStepBytes);
+  const int nk = (int)ceil_div(kbytes, kKB);
   const float c = kLog2e / a.T;
   const float invT = 1.0f / a.T;
-
-  // B operand: token rows of this tile
-  typename std::conditional<MAP, LoaderKCMap, LoaderKC>::type lb;
-  if constexpr (MAP) {
-    lb.init(a.X, a.ldx, a.idx, a.row_begin + jt * kTile, a.row_begin + rows, 0, kbytes);
-  } else {
-    lb.init(a.X + (int64_t)(a.x_row0 + jt * kTile) * a.ldx, a.ldx, rows - jt * kTile, 0, kbytes);
-  }
 
   // token columns owned by this lane: launch rows tl0 + 32*j
   const int tl0 = jt * kTile + wn * 128 + (lane & 31);
@@ -176,45 +168,58 @@ __global__ __launch_bounds__(256, 1) void sweep_kernel(SweepArgs a) {
   }
 
   for (int vt = vt_begin; vt < vt_end; ++vt) {
-    LoaderKC la;
-    la.init(a.W + (int64_t)vt * kTile * a.ldw, a.ldw, a.V - vt * kTile, 0, kbytes);
+    // operand state is rebuilt per tile so that nothing of the main loop stays
+    // live (and spillable) across the register-heavy epilogues
+    DmaOperand la;
+    la.init(a.W + (int64_t)vt * kTile * a.ldw, a.ldw, a.V - vt * kTile, 0, kbytes, 0);
+    typename std::conditional<MAP, DmaOperandMap, DmaOperand>::type lb;
+    if constexpr (MAP) {
+      lb.init(a.X, a.ldx, a.idx, a.row_begin + jt * kTile, a.row_begin + rows, 0, kbytes, 1);
+    } else {
+      lb.init(a.X + (int64_t)(a.x_row0 + jt * kTile) * a.ldx, a.ldx, rows - jt * kTile, 0,
+              kbytes, 1);
+    }
     floatx16 acc[4][4];
     gemm_mainloop<T>(acc, la, lb, nk, lds);
 
     const int vw0 = vt * kTile + wm * 128;
     if (vw0 >= a.V) continue;  // wave-uniform: this half tile is past the vocabulary
     const bool tail = vw0 + 128 > a.V;
-    if (tail) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (vw0 + acc_row(i, r, half) >= a.V) acc[i][j][r] = -INFINITY;
-    }
+    // columns in [V, round_up(V, 8)) of G are written as zeros (see the store)
+    const int Vp = (int)round_up(a.V, 8);
+    const int tpad = (int)round_up(rows, 8);
 
-    if constexpr (KIND == kSweepFwd) {
+    // One token column at a time: its 64 accumulators are copied to registers
+    // (z), processed, and the next column starts only after this one is done
+    // (sched_barrier), which bounds the live registers of the epilogue.
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_sched_barrier(0);
+      float z[64];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = acc[i][j][r];
+          if (tail && vw0 + acc_row(i, r, half) >= a.V) x = -INFINITY;
+          z[i * 16 + r] = x;
+        }
+
+      if constexpr (KIND == kSweepFwd) {
         float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+        for (int e = 0; e < 64; ++e) mx = fmaxf(mx, z[e]);
         const float mn = fmaxf(m[j], mx * c);
         if (mn != -INFINITY) {
           const float sc = fast_exp2(m[j] - mn);
           float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; r += 4) {
-              s0 += fast_exp2(fmaf(acc[i][j][r + 0], c, -mn));
-              s1 += fast_exp2(fmaf(acc[i][j][r + 1], c, -mn));
-              s2 += fast_exp2(fmaf(acc[i][j][r + 2], c, -mn));
-              s3 += fast_exp2(fmaf(acc[i][j][r + 3], c, -mn));
-            }
+          for (int e = 0; e < 64; e += 4) {
+            s0 += fast_exp2(fmaf(z[e + 0], c, -mn));
+            s1 += fast_exp2(fmaf(z[e + 1], c, -mn));
+            s2 += fast_exp2(fmaf(z[e + 2], c, -mn));
+            s3 += fast_exp2(fmaf(z[e + 3], c, -mn));
+          }
           s[j] = s[j] * sc + ((s0 + s1) + (s2 + s3));
           m[j] = mn;
         }
@@ -223,8 +228,8 @@ __global__ __launch_bounds__(256, 1) void sweep_kernel(SweepArgs a) {
           floatx4* sl = (floatx4*)slot;
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            sl[q] = floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                            acc[i][j][4 * q + 3]};
+            sl[q] = floatx4{z[i * 16 + 4 * q], z[i * 16 + 4 * q + 1], z[i * 16 + 4 * q + 2],
+                            z[i * 16 + 4 * q + 3]};
           if (me) {
             const float val = slot[rr];
             d[j] += a.p_s[e] * val;
@@ -232,30 +237,23 @@ __global__ __launch_bounds__(256, 1) void sweep_kernel(SweepArgs a) {
           }
         });
       }
-    }
 
-    if constexpr (KIND == kSweepEnt) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      if constexpr (KIND == kSweepEnt) {
         float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+        for (int e = 0; e < 64; ++e) mx = fmaxf(mx, z[e]);
         const float mn = fmaxf(m[j], mx * c);
         if (mn != -INFINITY) {
           float st0 = 0.f, st1 = 0.f, ut0 = 0.f, ut1 = 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-              const float y0 = fmaf(acc[i][j][r], c, -mn), y1 = fmaf(acc[i][j][r + 1], c, -mn);
-              const float e0 = fast_exp2(y0), e1 = fast_exp2(y1);
-              st0 += e0;
-              st1 += e1;
-              ut0 += (e0 > 0.f) ? e0 * y0 : 0.f;
-              ut1 += (e1 > 0.f) ? e1 * y1 : 0.f;
-            }
+          for (int e = 0; e < 64; e += 2) {
+            const float y0 = fmaf(z[e], c, -mn), y1 = fmaf(z[e + 1], c, -mn);
+            const float e0 = fast_exp2(y0), e1 = fast_exp2(y1);
+            st0 += e0;
+            st1 += e1;
+            ut0 += (e0 > 0.f) ? e0 * y0 : 0.f;
+            ut1 += (e1 > 0.f) ? e1 * y1 : 0.f;
+          }
           const float st = st0 + st1, ut = ut0 + ut1;
           if (m[j] == -INFINITY) {
             S64[j] = st;
@@ -269,58 +267,66 @@ __global__ __launch_bounds__(256, 1) void sweep_kernel(SweepArgs a) {
           m[j] = mn;
         }
       }
-    }
 
-    if constexpr (KIND == kSweepBwdG) {
+      if constexpr (KIND == kSweepBwdG) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = fast_exp2(fmaf(acc[i][j][r], c, -lse2[j]));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int e = 0; e < 64; ++e) z[e] = fast_exp2(fmaf(z[e], c, -lse2[j]));
         walk_hits(cu[j], a.ids_s, a.K, vw0, half, [&](int i, bool me, int rr, int64_t e) {
           floatx4* sl = (floatx4*)slot;
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            sl[q] = floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                            acc[i][j][4 * q + 3]};
+            sl[q] = floatx4{z[i * 16 + 4 * q], z[i * 16 + 4 * q + 1], z[i * 16 + 4 * q + 2],
+                            z[i * 16 + 4 * q + 3]};
           if (me) slot[rr] -= a.p_s[e];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const floatx4 v = sl[q];
-            acc[i][j][4 * q] = v[0];
-            acc[i][j][4 * q + 1] = v[1];
-            acc[i][j][4 * q + 2] = v[2];
-            acc[i][j][4 * q + 3] = v[3];
+            z[i * 16 + 4 * q] = v[0];
+            z[i * 16 + 4 * q + 1] = v[1];
+            z[i * 16 + 4 * q + 2] = v[2];
+            z[i * 16 + 4 * q + 3] = v[3];
           }
         });
-      // columns in [V, round_up(V, 8)) are written as zeros so that 16-byte
-      // granules read by the dHidden product never hold stale data
-      const int Vp = (int)round_up(a.V, 8);
+        // G [rows][Vp] feeds dHidden, G^T [Vp][Cp] feeds dW. Vocabulary
+        // columns in [V, Vp) and token columns in [rows, round_up(rows, 8))
+        // are written as zeros so that 16-byte granules read by the
+        // contractions never hold stale data.
+        const int t = tl0 + 32 * j;
+        if (t < tpad) {
+          const bool gv = t < rows;
+          char* grow = a.G + (int64_t)t * a.ldg;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (tl0 + 32 * j >= rows) continue;
-        char* grow = a.G + (int64_t)(tl0 + 32 * j) * a.ldg;
+          for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int v = vw0 + i * 32 + 8 * q + 4 * half;
-            if (v >= Vp) continue;
-            const float g0 = acc[i][j][4 * q + 0] * coef, g1 = acc[i][j][4 * q + 1] * coef;
-            const float g2 = acc[i][j][4 * q + 2] * coef, g3 = acc[i][j][4 * q + 3] * coef;
-            if constexpr (sizeof(T) == 2) {
-              uint2 pk;
-              pk.x = f32_to_bf16_bits(g0) | (f32_to_bf16_bits(g1) << 16);
-              pk.y = f32_to_bf16_bits(g2) | (f32_to_bf16_bits(g3) << 16);
-              *(uint2*)(grow + (int64_t)v * 2) = pk;
-            } else {
-              *(float4*)(grow + (int64_t)v * 4) = make_float4(g0, g1, g2, g3);
+            for (int q = 0; q < 4; ++q) {
+              const int v = vw0 + i * 32 + 8 * q + 4 * half;
+              if (v >= Vp) continue;
+              // token columns past `rows` hold a repeated row: exact zeros
+              const float g0 = gv ? z[i * 16 + 4 * q + 0] * coef : 0.0f;
+              const float g1 = gv ? z[i * 16 + 4 * q + 1] * coef : 0.0f;
+              const float g2 = gv ? z[i * 16 + 4 * q + 2] * coef : 0.0f;
+              const float g3 = gv ? z[i * 16 + 4 * q + 3] * coef : 0.0f;
+              char* gt = a.GT + (int64_t)v * a.ldgt + (int64_t)t * sizeof(T);
+              if constexpr (sizeof(T) == 2) {
+                const uint32_t b0 = f32_to_bf16_bits(g0), b1 = f32_to_bf16_bits(g1);
+                const uint32_t b2 = f32_to_bf16_bits(g2), b3 = f32_to_bf16_bits(g3);
+                if (gv)
+                  *(uint2*)(grow + (int64_t)v * 2) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+                *(uint16_t*)(gt) = (uint16_t)b0;
+                *(uint16_t*)(gt + a.ldgt) = (uint16_t)b1;
+                *(uint16_t*)(gt + 2 * a.ldgt) = (uint16_t)b2;
+                *(uint16_t*)(gt + 3 * a.ldgt) = (uint16_t)b3;
+              } else {
+                if (gv) *(float4*)(grow + (int64_t)v * 4) = make_float4(g0, g1, g2, g3);
+                *(float*)(gt) = g0;
+                *(float*)(gt + a.ldgt) = g1;
+                *(float*)(gt + 2 * a.ldgt) = g2;
+                *(float*)(gt + 3 * a.ldgt) = g3;
+              }
             }
-          }
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -408,12 +414,12 @@ hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid
   if (!f32) {
     if (kind == kSweepFwd && map) KD_SWEEP(__bf16, kSweepFwd, true);
     else if (kind == kSweepFwd) KD_SWEEP(__bf16, kSweepFwd, false);
-    else if (kind == kSweepBwdG) KD_SWEEP(__bf16, kSweepBwdG, false);
+    else if (kind == kSweepBwdG) KD_SWEEP(__bf16, kSweepBwdG, true);
     else KD_SWEEP(__bf16, kSweepEnt, false);
   } else {
     if (kind == kSweepFwd && map) KD_SWEEP(float, kSweepFwd, true);
     else if (kind == kSweepFwd) KD_SWEEP(float, kSweepFwd, false);
-    else if (kind == kSweepBwdG) KD_SWEEP(float, kSweepBwdG, false);
+    else if (kind == kSweepBwdG) KD_SWEEP(float, kSweepBwdG, true);
     else KD_SWEEP(float, kSweepEnt, false);
   }
 #undef KD_SWEEP
