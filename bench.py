@@ -33,13 +33,14 @@ PEAK_FP32_TFLOPS = 157.3       # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 
 WORKLOADS = {
-    "c2": dict(S=8192, H=3072, V=128256, K=100, T=1.0, chunk=1024, seed=1002,
+    "c2": dict(S=8192, H=3072, V=128256, K=100, T=1.0, chunk=1024, seed=1002, slug="8k_context",
                name="8K context: S=8192 H=3072 V=128256 K=100 T=1.0 chunk=1024 bf16"),
-    "c3": dict(S=32768, H=2880, V=201088, K=100, T=1.0, chunk=2048, seed=1003,
+    "c3": dict(S=32768, H=2880, V=201088, K=100, T=1.0, chunk=2048, seed=1003, slug="32k_context",
                name="32K context, large vocab: S=32768 H=2880 V=201088 K=100 T=1.0 chunk=2048 bf16"),
-    "c4": dict(S=262144, H=3072, V=128256, K=100, T=2.0, chunk=2048, seed=1004,
+    "c4": dict(S=262144, H=3072, V=128256, K=100, T=2.0, chunk=2048, seed=1004, slug="256k_context",
                name="256K context: S=262144 H=3072 V=128256 K=100 T=2.0 chunk=2048 bf16"),
     "c5": dict(S=32768, H=2048, V=151936, K=100, T=1.0, chunk=1024, seed=1005,
+               slug="entropy_selective_32k",
                name="entropy-selective: S=32768 H=2048 V=151936 K=100 top 20% by entropy, chunk=1024 bf16"),
 }
 
@@ -64,6 +65,24 @@ def kernel_flops(name, wl, C_rows, S_rows):
     if name in ("bwd_grad_tile", "bwd_dhidden", "bwd_dw"):
         return 2.0 * C_rows * H * V
     return None
+
+
+def measured_traffic(wl, step):
+    """HBM bytes per launch of `step` from the committed counter summary of this
+    workload, or None when there is none or the kernel sources changed since."""
+    from chunked_top_kl_amd.prof_summary import kernel_sources_hash, read_summary_json
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{wl['slug']}.md")
+    js = read_summary_json(path)
+    if not js or js.get("workload") != wl["name"]:
+        return None
+    if js.get("kernel_sources_sha256") != kernel_sources_hash():
+        log(f"[bench] {os.path.relpath(path, ROOT)} was measured on other kernel sources: traffic null")
+        return None
+    st = js.get("steps", {}).get(step)
+    if not st:
+        return None
+    return dict(bytes=st["traffic_bytes"], read_bytes=st["read_bytes"],
+                write_bytes=st["write_bytes"], source=os.path.relpath(path, ROOT))
 
 
 def run_step(kd, torch, wl, t, ws, mask=None):
@@ -142,7 +161,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--chunk", type=int, default=None)
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mem-sweep", action="store_true")
     ap.add_argument("--mem-sizes", default="16384,32768,65536,131072,262144")
@@ -232,10 +251,13 @@ def main():
     if dom_name in ("bwd_grad_tile", "bwd_dhidden", "bwd_dw"):
         dom_flops = 8.0 * N_rows * H * V / 4.0 / max(dom_v["launches_per_step"], 1)
     achieved = dom_flops / (dom_v["avg_ms"] / 1000.0) / 1e12 if dom_flops else None
+    tr = measured_traffic(wl, dom_name)
     roofline = dict(kernel=dom_name, bound="mfma", achieved=round(achieved, 1) if achieved else None,
                     peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / PEAK_BF16_TFLOPS, 4) if achieved else None,
-                    traffic=None,
+                    traffic=tr["bytes"] if tr else None,
+                    traffic_unit="HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
+                    traffic_detail=tr,
                     flops_per_launch=dom_flops, avg_ms=dom_v["avg_ms"])
 
     result = {

@@ -21,7 +21,7 @@ __device__ inline int chunk_rows(const int32_t* nrows_dev, int row_begin, int ro
 //   K (= vocabulary) contiguous. The vocabulary is split into `ks` ranges.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
+__device__ __forceinline__ void dh_body(DhArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kMainLds];
   const int rows = chunk_rows(a.nrows_dev, a.row_begin, a.row_cap);
   if (rows <= 0) return;
@@ -80,10 +80,13 @@ int dh_grid(int row_cap, int V, int H, int ncu, int f32) {
   return best;
 }
 
+extern "C" __global__ __launch_bounds__(256, 1) void kd_bwd_dhidden_bf16(DhArgs a) { dh_body<__bf16>(a); }
+extern "C" __global__ __launch_bounds__(256, 1) void kd_bwd_dhidden_f32(DhArgs a) { dh_body<float>(a); }
+
 hipError_t launch_dh(int f32, const DhArgs& a, int grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
-  if (f32) hipLaunchKernelGGL(dh_kernel<float>, dim3(grid), dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL(dh_kernel<__bf16>, dim3(grid), dim3(kThreads), 0, st, a);
+  if (f32) hipLaunchKernelGGL(kd_bwd_dhidden_f32, dim3(grid), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL(kd_bwd_dhidden_bf16, dim3(grid), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -221,7 +224,7 @@ hipError_t launch_transpose_w(int f32, const char* W, int V, int H, char* WT, in
 //   later chunks add, and return at once when they hold no rows.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256, 1) void dw_kernel(DwArgs a) {
+__device__ __forceinline__ void dw_body(DwArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kMainLds];
   int rows = chunk_rows(a.nrows_dev, a.row_begin, a.row_cap);
   if (rows <= 0) {
@@ -274,10 +277,13 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DwArgs a) {
   }
 }
 
+extern "C" __global__ __launch_bounds__(256, 1) void kd_bwd_dw_bf16(DwArgs a) { dw_body<__bf16>(a); }
+extern "C" __global__ __launch_bounds__(256, 1) void kd_bwd_dw_f32(DwArgs a) { dw_body<float>(a); }
+
 hipError_t launch_dw(int f32, const DwArgs& a, hipStream_t st) {
   const int grid = (int)(ceil_div(a.V, kTile) * ceil_div(a.H, kTile));
-  if (f32) hipLaunchKernelGGL(dw_kernel<float>, dim3(grid), dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL(dw_kernel<__bf16>, dim3(grid), dim3(kThreads), 0, st, a);
+  if (f32) hipLaunchKernelGGL(kd_bwd_dw_f32, dim3(grid), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL(kd_bwd_dw_bf16, dim3(grid), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

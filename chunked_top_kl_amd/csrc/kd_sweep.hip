@@ -98,7 +98,7 @@ __device__ __forceinline__ void walk_hits(Cursor& c, const int32_t* ids_s, int K
 }
 
 template <typename T, int KIND, bool MAP>
-__global__ __launch_bounds__(256, 1) void sweep_kernel(SweepArgs a) {
+__device__ __forceinline__ void sweep_body(SweepArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kMainLds + 4 * 4096];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int half = lane >> 5;
@@ -407,20 +407,36 @@ int sweep_grid(int64_t rows_max, int V, int ncu) {
   return best;
 }
 
+// One kernel symbol per variant, named after the step it performs (these are
+// the names that traces and counter dumps show).
+#define KD_SWEEP_KERNEL(NAME, T, KIND, MAP)                                  \
+  extern "C" __global__ __launch_bounds__(256, 1) void NAME(SweepArgs a) { \
+    sweep_body<T, KIND, MAP>(a);                                           \
+  }
+KD_SWEEP_KERNEL(kd_fwd_lse_gather_bf16, __bf16, kSweepFwd, false)
+KD_SWEEP_KERNEL(kd_fwd_lse_gather_rows_bf16, __bf16, kSweepFwd, true)
+KD_SWEEP_KERNEL(kd_bwd_grad_tile_bf16, __bf16, kSweepBwdG, true)
+KD_SWEEP_KERNEL(kd_entropy_sweep_bf16, __bf16, kSweepEnt, false)
+KD_SWEEP_KERNEL(kd_fwd_lse_gather_f32, float, kSweepFwd, false)
+KD_SWEEP_KERNEL(kd_fwd_lse_gather_rows_f32, float, kSweepFwd, true)
+KD_SWEEP_KERNEL(kd_bwd_grad_tile_f32, float, kSweepBwdG, true)
+KD_SWEEP_KERNEL(kd_entropy_sweep_f32, float, kSweepEnt, false)
+#undef KD_SWEEP_KERNEL
+
 hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   dim3 g(grid), blk(kThreads);
-#define KD_SWEEP(T, K, M) hipLaunchKernelGGL((sweep_kernel<T, K, M>), g, blk, 0, st, a)
+#define KD_SWEEP(NAME) hipLaunchKernelGGL(NAME, g, blk, 0, st, a)
   if (!f32) {
-    if (kind == kSweepFwd && map) KD_SWEEP(__bf16, kSweepFwd, true);
-    else if (kind == kSweepFwd) KD_SWEEP(__bf16, kSweepFwd, false);
-    else if (kind == kSweepBwdG) KD_SWEEP(__bf16, kSweepBwdG, true);
-    else KD_SWEEP(__bf16, kSweepEnt, false);
+    if (kind == kSweepFwd && map) KD_SWEEP(kd_fwd_lse_gather_rows_bf16);
+    else if (kind == kSweepFwd) KD_SWEEP(kd_fwd_lse_gather_bf16);
+    else if (kind == kSweepBwdG) KD_SWEEP(kd_bwd_grad_tile_bf16);
+    else KD_SWEEP(kd_entropy_sweep_bf16);
   } else {
-    if (kind == kSweepFwd && map) KD_SWEEP(float, kSweepFwd, true);
-    else if (kind == kSweepFwd) KD_SWEEP(float, kSweepFwd, false);
-    else if (kind == kSweepBwdG) KD_SWEEP(float, kSweepBwdG, true);
-    else KD_SWEEP(float, kSweepEnt, false);
+    if (kind == kSweepFwd && map) KD_SWEEP(kd_fwd_lse_gather_rows_f32);
+    else if (kind == kSweepFwd) KD_SWEEP(kd_fwd_lse_gather_f32);
+    else if (kind == kSweepBwdG) KD_SWEEP(kd_bwd_grad_tile_f32);
+    else KD_SWEEP(kd_entropy_sweep_f32);
   }
 #undef KD_SWEEP
   return hipGetLastError();

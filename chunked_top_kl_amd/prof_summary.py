@@ -1,0 +1,215 @@
+"""Short text summaries of rocprofv3 output for the top-K KL kernels.
+
+Two summaries are produced from rocprofv3's CSV output:
+
+* ``trace``: per-step kernel durations from ``--kernel-trace --stats``
+  (``*_kernel_stats.csv``), one row per path step.
+* ``traffic``: HBM bytes per launch from two ``--pmc`` runs (``FETCH_SIZE``,
+  then ``WRITE_SIZE``, each reported in KiB per dispatch). Each counter is
+  scaled by what it reads for a device-to-device copy of a known size (run in
+  the same process: ``bench.py --calib-copy-mib``), since these counters need
+  not count every byte once.
+
+Every summary records the SHA-256 of the kernel sources (``csrc/``) it was
+measured with; ``bench.py`` reports the traffic figure only while the sources
+still hash to that value.
+
+Usage::
+
+    python -m chunked_top_kl_amd.prof_summary trace --stats X_kernel_stats.csv \\
+        --out profiles/kernel_trace_<workload>.md --command "<command that made X>"
+    python -m chunked_top_kl_amd.prof_summary traffic --fetch F.csv --write W.csv \\
+        --calib-mib 1024 --out profiles/hbm_traffic_<workload>.md \\
+        --command "<FETCH command>" --command "<WRITE command>"
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import re
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+# kernel symbol (mangled or demangled) -> path step, as named by the library's
+# profiling scopes; the first matching pattern wins
+STEP_PATTERNS = [
+    ("kd_fwd_lse_gather", "fwd_lse_gather"),
+    ("kd_bwd_grad_tile", "bwd_grad_tile"),
+    ("kd_entropy_sweep", "entropy_sweep"),
+    ("kd_bwd_dhidden", "bwd_dhidden"),
+    ("kd_bwd_dw", "bwd_dw"),
+    ("dh_reduce_kernel", "bwd_dhidden_reduce"),
+    ("fwd_combine_kernel", "fwd_combine"),
+    ("loss_final_kernel", "fwd_combine"),
+    ("ent_combine_kernel", "entropy_combine"),
+    ("prepass_kernel", "prepass"),
+    ("compact_kernel", "compact"),
+    ("zero_rows_kernel", "zero_rows"),
+    ("gather_rows_t", "gather_rows_t"),
+    ("transpose_w", "transpose_w"),
+    ("select_threshold", "select_threshold"),
+    ("refine_kernel", "select_refine_fp64"),
+    ("select_final", "select_final"),
+    ("validate_kernel", "validate"),
+    ("zero_u64_kernel", "validate"),
+    ("copyBuffer", "device_copy"),
+]
+
+
+def kernel_sources_hash() -> str:
+    """SHA-256 over the kernel sources (file names and contents, sorted by name)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def step_of(kernel_name: str) -> str:
+    for pat, step in STEP_PATTERNS:
+        if pat in kernel_name:
+            return step
+    return "other"
+
+
+def _json_block(obj) -> str:
+    return "```json\n" + json.dumps(obj, indent=1, sort_keys=True) + "\n```\n"
+
+
+def read_summary_json(path: str):
+    """The JSON block of a summary written by this module, or None."""
+    try:
+        with open(path) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    return json.loads(m.group(1)) if m else None
+
+
+# ---------------------------------------------------------------------------
+# kernel trace
+# ---------------------------------------------------------------------------
+def summarize_trace(stats_csv: str, commands, workload: str, steps: int) -> str:
+    rows = list(csv.DictReader(open(stats_csv)))
+    agg = collections.OrderedDict()
+    for r in rows:
+        step = step_of(r["Name"])
+        calls = int(r["Calls"])
+        tot = float(r["TotalDurationNs"])
+        a = agg.setdefault(step, dict(calls=0, total_ns=0.0, kernels=set()))
+        a["calls"] += calls
+        a["total_ns"] += tot
+        a["kernels"].add(r["Name"] if len(r["Name"]) < 60 else r["Name"][:57] + "...")
+    total = sum(a["total_ns"] for a in agg.values())
+    out = [f"# Kernel trace: {workload}\n",
+           "rocprofv3 `--kernel-trace --stats`, durations per path step (all launches in the run,",
+           f"{steps} timed steps plus warm-up).\n",
+           "Commands (from the repository root):\n"]
+    out += [f"    {c}" for c in commands]
+    out += ["", "| step | launches | total ms | avg ms per launch | share |",
+            "|:--|--:|--:|--:|--:|"]
+    data = {}
+    for step, a in sorted(agg.items(), key=lambda kv: -kv[1]["total_ns"]):
+        avg = a["total_ns"] / max(a["calls"], 1) / 1e6
+        out.append(f"| {step} | {a['calls']} | {a['total_ns'] / 1e6:.3f} | {avg:.5f} | "
+                   f"{100.0 * a['total_ns'] / max(total, 1):.1f}% |")
+        data[step] = dict(launches=a["calls"], total_ms=round(a["total_ns"] / 1e6, 4),
+                          avg_ms=round(avg, 6), kernels=sorted(a["kernels"]))
+    out += ["", "Machine-readable copy:", "",
+            _json_block(dict(kind="kernel_trace", workload=workload,
+                             kernel_sources_sha256=kernel_sources_hash(), steps=data))]
+    return "\n".join(out)
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic
+# ---------------------------------------------------------------------------
+def _counter_rows(path, counter):
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        per[step_of(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return per
+
+
+def summarize_traffic(fetch_csv: str, write_csv: str, calib_mib: int, commands,
+                      workload: str) -> str:
+    fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
+    write = _counter_rows(write_csv, "WRITE_SIZE")
+    calib_kib = calib_mib * 1024.0
+    if not fetch.get("device_copy") or not write.get("device_copy"):
+        raise SystemExit("no device copy dispatch in the counter dumps: run bench.py with "
+                         "--calib-copy-mib")
+    # the calibration copy is the largest copy dispatch of the run
+    f_cal = max(fetch["device_copy"])
+    w_cal = max(write["device_copy"])
+    f_fac = calib_kib / f_cal
+    w_fac = calib_kib / w_cal
+    out = [f"# HBM traffic per launch: {workload}\n",
+           "rocprofv3 `--pmc FETCH_SIZE` and `--pmc WRITE_SIZE` (KiB per dispatch), each in a run",
+           "of its own, averaged over all launches of a step's kernels. Calibration: a",
+           f"device-to-device copy of {calib_mib} MiB in the same process read FETCH_SIZE =",
+           f"{f_cal:.0f} KiB and WRITE_SIZE = {w_cal:.0f} KiB, so the counters are scaled by",
+           f"{f_fac:.3f} (reads) and {w_fac:.3f} (writes).\n",
+           "Commands (from the repository root):\n"]
+    out += [f"    {c}" for c in commands]
+    out += ["", "| step | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | read GB | written GB | "
+            "total GB per launch |", "|:--|--:|--:|--:|--:|--:|--:|"]
+    data = {}
+    for step in sorted(set(fetch) | set(write)):
+        if step == "device_copy" or step not in fetch or step not in write:
+            continue
+        fv, wv = fetch[step], write[step]
+        fk = sum(fv) / len(fv)
+        wk = sum(wv) / len(wv)
+        rb = fk * 1024.0 * f_fac
+        wb = wk * 1024.0 * w_fac
+        out.append(f"| {step} | {len(fv)} | {fk:.0f} | {wk:.0f} | {rb / 1e9:.3f} | {wb / 1e9:.3f} | "
+                   f"{(rb + wb) / 1e9:.3f} |")
+        data[step] = dict(launches=len(fv), fetch_kib=round(fk, 1), write_kib=round(wk, 1),
+                          read_bytes=round(rb), write_bytes=round(wb),
+                          traffic_bytes=round(rb + wb))
+    out += ["", "Machine-readable copy:", "",
+            _json_block(dict(kind="hbm_traffic", workload=workload,
+                             kernel_sources_sha256=kernel_sources_hash(),
+                             calibration=dict(copy_mib=calib_mib, fetch_kib=f_cal,
+                                              write_kib=w_cal, fetch_factor=f_fac,
+                                              write_factor=w_fac),
+                             steps=data))]
+    return "\n".join(out)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description="summaries of rocprofv3 output")
+    sub = ap.add_subparsers(dest="what", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("--stats", required=True)
+    t.add_argument("--steps", type=int, default=0)
+    m = sub.add_parser("traffic")
+    m.add_argument("--fetch", required=True)
+    m.add_argument("--write", required=True)
+    m.add_argument("--calib-mib", type=int, required=True)
+    for p in (t, m):
+        p.add_argument("--out", required=True)
+        p.add_argument("--workload", required=True)
+        p.add_argument("--command", action="append", default=[])
+    a = ap.parse_args(argv)
+    if a.what == "trace":
+        text = summarize_trace(a.stats, a.command, a.workload, a.steps)
+    else:
+        text = summarize_traffic(a.fetch, a.write, a.calib_mib, a.command, a.workload)
+    with open(a.out, "w") as f:
+        f.write(text)
+    print(f"wrote {a.out}")
+
+
+if __name__ == "__main__":
+    main()

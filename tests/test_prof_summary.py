@@ -1,0 +1,66 @@
+"""Host logic of the rocprofv3 summaries (no GPU): symbol -> step mapping,
+copy-kernel calibration of the HBM counters, and the source-hash stamp."""
+import csv
+
+from chunked_top_kl_amd.prof_summary import (kernel_sources_hash, read_summary_json, step_of,
+                                             summarize_trace, summarize_traffic)
+
+PMC_FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _pmc_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=PMC_FIELDS)
+        w.writeheader()
+        for i, (name, val) in enumerate(rows):
+            w.writerow(dict(Dispatch_Id=i, Kernel_Name=name, Counter_Name=counter,
+                            Counter_Value=val))
+
+
+def test_step_names():
+    assert step_of("kd_bwd_dw_bf16") == "bwd_dw"
+    assert step_of("kd_fwd_lse_gather_rows_bf16") == "fwd_lse_gather"
+    assert step_of("kd_bwd_grad_tile_f32") == "bwd_grad_tile"
+    assert step_of("kd::dh_reduce_kernel(kd::DhReduceArgs, int)") == "bwd_dhidden_reduce"
+    assert step_of("kd_bwd_dhidden_bf16") == "bwd_dhidden"
+    assert step_of("__amd_rocclr_copyBuffer") == "device_copy"
+    assert step_of("something_else") == "other"
+
+
+def test_traffic_calibration(tmp_path):
+    # a 4 MiB copy that FETCH_SIZE counts at half and WRITE_SIZE at full size
+    f = tmp_path / "f.csv"
+    w = tmp_path / "w.csv"
+    _pmc_csv(f, "FETCH_SIZE", [("__amd_rocclr_copyBuffer", 2048.0), ("__amd_rocclr_copyBuffer", 1.0),
+                               ("kd_bwd_dw_bf16", 100.0), ("kd_bwd_dw_bf16", 300.0)])
+    _pmc_csv(w, "WRITE_SIZE", [("__amd_rocclr_copyBuffer", 4096.0),
+                               ("kd_bwd_dw_bf16", 50.0), ("kd_bwd_dw_bf16", 50.0)])
+    text = summarize_traffic(str(f), str(w), 4, ["cmd"], "wl")
+    out = tmp_path / "s.md"
+    out.write_text(text)
+    js = read_summary_json(str(out))
+    assert js["kernel_sources_sha256"] == kernel_sources_hash()
+    assert abs(js["calibration"]["fetch_factor"] - 2.0) < 1e-12
+    assert abs(js["calibration"]["write_factor"] - 1.0) < 1e-12
+    dw = js["steps"]["bwd_dw"]
+    assert dw["launches"] == 2
+    assert dw["read_bytes"] == 200 * 1024 * 2          # mean 200 KiB, x2
+    assert dw["write_bytes"] == 50 * 1024
+    assert dw["traffic_bytes"] == dw["read_bytes"] + dw["write_bytes"]
+
+
+def test_trace_summary(tmp_path):
+    p = tmp_path / "k.csv"
+    with open(p, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs"])
+        w.writeheader()
+        w.writerow(dict(Name="kd_bwd_dw_bf16", Calls=4, TotalDurationNs=4e6, AverageNs=1e6))
+        w.writerow(dict(Name="kd_fwd_lse_gather_bf16", Calls=1, TotalDurationNs=3e6, AverageNs=3e6))
+        w.writerow(dict(Name="kd_fwd_lse_gather_rows_bf16", Calls=1, TotalDurationNs=1e6,
+                        AverageNs=1e6))
+    out = tmp_path / "t.md"
+    out.write_text(summarize_trace(str(p), ["cmd"], "wl", 1))
+    js = read_summary_json(str(out))
+    assert js["steps"]["bwd_dw"]["avg_ms"] == 1.0
+    assert js["steps"]["fwd_lse_gather"]["launches"] == 2
+    assert js["steps"]["fwd_lse_gather"]["avg_ms"] == 2.0
