@@ -191,7 +191,7 @@ def main():
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
     t = to_dev(p, torch)
     prob = kd.make_problem(S, H, V, K, C, wl["T"], kd.KD_BF16, kd.KD_BF16)
-    ws = torch.empty(kd.kd_workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(kd.kd_topk_kl_workspace_bytes(prob), dtype=torch.uint8, device="cuda")
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * 2**20 // 4

@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "KD_BF16", "KD_F32", "KdError", "kd_problem", "lib",
-    "kd_abi_version", "kd_status_str", "kd_workspace_bytes",
+    "kd_abi_version", "kd_status_str", "kd_topk_kl_workspace_bytes",
     "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_student_entropy",
     "kd_select_top_fraction", "kd_validate_topk",
     "kd_profile_enable", "kd_profile_read", "kd_profile_reset",
@@ -51,8 +51,8 @@ _I64P = ctypes.POINTER(ctypes.c_int64)
 lib.kd_abi_version.restype = ctypes.c_int
 lib.kd_status_str.restype = ctypes.c_char_p
 lib.kd_status_str.argtypes = [ctypes.c_int]
-lib.kd_workspace_bytes.restype = ctypes.c_size_t
-lib.kd_workspace_bytes.argtypes = [_PP]
+lib.kd_topk_kl_workspace_bytes.restype = ctypes.c_size_t
+lib.kd_topk_kl_workspace_bytes.argtypes = [_PP]
 lib.kd_topk_kl_fwd.restype = ctypes.c_int
 lib.kd_topk_kl_fwd.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.kd_topk_kl_bwd.restype = ctypes.c_int
@@ -104,8 +104,8 @@ def make_problem(S, H, V, K, chunk, T, hw_dtype, tl_dtype) -> kd_problem:
                       int(tl_dtype))
 
 
-def kd_workspace_bytes(problem: kd_problem) -> int:
-    return int(lib.kd_workspace_bytes(ctypes.byref(problem)))
+def kd_topk_kl_workspace_bytes(problem: kd_problem) -> int:
+    return int(lib.kd_topk_kl_workspace_bytes(ctypes.byref(problem)))
 
 
 def _ptr(t):
@@ -144,9 +144,9 @@ def _mask_arg(mask, S):
 
 
 def _workspace(problem, device, workspace):
-    need = kd_workspace_bytes(problem)
+    need = kd_topk_kl_workspace_bytes(problem)
     if need == 0:
-        _check(2, "kd_workspace_bytes")
+        _check(2, "kd_topk_kl_workspace_bytes")
     if workspace is not None and workspace.numel() >= need and workspace.data_ptr() % 256 == 0:
         return workspace
     return torch.empty(need, dtype=torch.uint8, device=device)

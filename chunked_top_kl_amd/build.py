@@ -1,6 +1,8 @@
 """Build the HIP library libkdtopk.so in-tree for gfx950.
 
-Usage: python -m chunked_top_kl_amd.build   (or call build_library()).
+Usage: python chunked_top_kl_amd/build.py   (or call build_library()). Run it as
+a file, not as a module of the package: importing the package loads the
+library that this script rebuilds.
 """
 from __future__ import annotations
 

@@ -224,7 +224,7 @@ const char* kd_status_str(int s) {
   }
 }
 
-size_t kd_workspace_bytes(const kd_problem* p) {
+size_t kd_topk_kl_workspace_bytes(const kd_problem* p) {
   if (check_problem(p) != KD_OK) return 0;
   return plan(p).total;
 }

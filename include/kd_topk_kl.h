@@ -39,7 +39,7 @@
  *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *    on it in order; no entry point synchronises the host unless it says so.
  *  - `ws` / `ws_bytes`: caller-provided device workspace of at least
- *    kd_workspace_bytes(problem) bytes, 256-byte aligned. Its contents on
+ *    kd_topk_kl_workspace_bytes(problem) bytes, 256-byte aligned. Its contents on
  *    entry are ignored and on exit are unspecified. Calls that overlap in time
  *    must use distinct workspaces.
  *  - Argument errors are detected on the host before anything is enqueued and
@@ -68,7 +68,7 @@ typedef enum kd_status {
   KD_ERR_DTYPE = 3,        /* dtype code not one of kd_dtype                      */
   KD_ERR_TEMPERATURE = 4,  /* T <= 0 or not finite                                */
   KD_ERR_CHUNK = 5,        /* chunk <= 0                                          */
-  KD_ERR_WORKSPACE = 6,    /* ws NULL, misaligned, or smaller than kd_workspace_bytes */
+  KD_ERR_WORKSPACE = 6,    /* ws NULL, misaligned, or smaller than kd_topk_kl_workspace_bytes */
   KD_ERR_BAD_ID = 7,       /* reserved: reported counts come from kd_validate_topk */
   KD_ERR_HIP = 8,          /* a HIP runtime call or kernel launch failed          */
   KD_ERR_ARCH = 9,         /* current device is not gfx950                        */
@@ -104,7 +104,7 @@ const char* kd_status_str(int status);
  * maximum over them). Returns 0 if the problem itself is invalid. The size is
  * linear in S (per-row teacher tables and partials) plus a constant part
  * (the [chunk, V] bf16 gradient tile and split-K partials of dHidden). */
-size_t kd_workspace_bytes(const kd_problem* problem);
+size_t kd_topk_kl_workspace_bytes(const kd_problem* problem);
 
 /* Forward pass ("what chunked KL loss does": project, fold into the loss,
  * discard; the online log-normaliser of z/T over V and the gather of z at the

@@ -53,7 +53,7 @@ def prob(**kw):
 ])
 def test_invalid_problems_rejected(kw, code):
     p = prob(**kw)
-    assert kd.kd_workspace_bytes(p) == 0
+    assert kd.kd_topk_kl_workspace_bytes(p) == 0
     fake = ctypes.c_void_p(0x1000)
     rc = kd.lib.kd_topk_kl_fwd(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, None,
                                None, fake, 1 << 40, None)
@@ -67,7 +67,7 @@ def test_null_and_workspace_errors():
                                  1 << 40, None) == KD_ERR_NULL
     assert kd.lib.kd_topk_kl_fwd(ctypes.byref(p), None, fake, fake, fake, None, fake, fake, None,
                                  None, fake, 1 << 40, None) == KD_ERR_NULL
-    need = kd.kd_workspace_bytes(p)
+    need = kd.kd_topk_kl_workspace_bytes(p)
     assert need > 0
     # too small, misaligned, NULL workspace
     assert kd.lib.kd_topk_kl_fwd(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, None,
@@ -83,7 +83,7 @@ def test_null_and_workspace_errors():
 
 
 def test_workspace_linear_in_S_and_bounded_in_V():
-    sizes = [kd.kd_workspace_bytes(prob(S=S, H=3072, V=128256, K=100, chunk=2048))
+    sizes = [kd.kd_topk_kl_workspace_bytes(prob(S=S, H=3072, V=128256, K=100, chunk=2048))
              for S in (16384, 32768, 65536, 131072, 262144)]
     d = [b - a for a, b in zip(sizes, sizes[1:])]
     per_token = [x / dS for x, dS in zip(d, (16384, 32768, 65536, 131072))]
@@ -92,6 +92,6 @@ def test_workspace_linear_in_S_and_bounded_in_V():
     assert max(per_token) < 1.3 * min(per_token)
     assert 1000 < min(per_token) and max(per_token) < 6000
     # the chunk-sized part grows with chunk, not with S
-    a = kd.kd_workspace_bytes(prob(S=32768, H=2880, V=201088, K=100, chunk=1024))
-    b = kd.kd_workspace_bytes(prob(S=32768, H=2880, V=201088, K=100, chunk=2048))
+    a = kd.kd_topk_kl_workspace_bytes(prob(S=32768, H=2880, V=201088, K=100, chunk=1024))
+    b = kd.kd_topk_kl_workspace_bytes(prob(S=32768, H=2880, V=201088, K=100, chunk=2048))
     assert b - a >= 1024 * 201088 * 2
