@@ -213,10 +213,15 @@ struct FragAddr {
 //
 // Stage kt has four sub-steps of 16 MFMAs; the fragments of sub-step s+1 are
 // read while sub-step s computes. Before the last sub-step: wait for this
-// wave's loads of stage kt+1, barrier (stage kt+1 visible to all waves, and
-// every wave holds its stage-kt fragments, so stage kt's buffer is free),
-// loads of stage kt+2 into that buffer, and the sub-step-0 fragments of
-// stage kt+1 - all while the last 16 MFMAs of stage kt run.
+// wave's loads of stage kt+1 and barrier (stage kt+1 visible to all waves;
+// every wave holds its stage-kt fragments, so stage kt's buffer is free).
+// The last sub-step then issues, one per MFMA, the 16 loads of stage kt+2
+// into that buffer and the 8 sub-step-0 fragment reads of stage kt+1: issued
+// in one burst, the loads back up the vector memory queue and stall the
+// wave's in-order issue while the MFMA pipe has nothing queued. A stage at or
+// past the end of K reads zeros (or, for a row-mapped operand, a valid
+// granule) into the free buffer, so the issue needs no branch. The last stage
+// is peeled: it has no barrier, so it issues no loads.
 // ---------------------------------------------------------------------------
 template <typename V>
 struct SubFrags {
@@ -230,6 +235,35 @@ __device__ __forceinline__ void read_sub(SubFrags<V>& f, const char* stage, cons
   for (int i = 0; i < 4; ++i) f.a[i] = *(const V*)(stage + fa.a[s] + i * 32 * kKB);
 #pragma unroll
   for (int j = 0; j < 4; ++j) f.b[j] = *(const V*)(stage + fa.b[s] + j * 32 * kKB);
+}
+
+__device__ __forceinline__ void mfma_ij(floatx16& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mfma_ij(floatx16& acc, const floatx4& a, const floatx4& b) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[q], b[q], acc, 0, 0, 0);
+}
+
+// Last sub-step of stage kt with the loads of stage kn = kt + 2 (into the
+// buffer at `sbase`) and the sub-step-0 reads of the next stage interleaved.
+template <class V, class OA, class OB>
+__device__ __forceinline__ void mfma_sub_interleaved(floatx16 (&acc)[4][4], const SubFrags<V>& f,
+                                                     const OA& la, const OB& lb, int kn,
+                                                     uint32_t sbase, SubFrags<V>& fn,
+                                                     const char* nstage, const FragAddr& fa) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = i * 4 + j;
+      mfma_ij(acc[i][j], f.a[i], f.b[j]);
+      if (q < 8) la.issue_one(kn, sbase, q);
+      else lb.issue_one(kn, sbase, q - 8);
+      if (q < 4) fn.a[q] = *(const V*)(nstage + fa.a[0] + q * 32 * kKB);
+      else if (q < 8) fn.b[q - 4] = *(const V*)(nstage + fa.b[0] + (q - 4) * 32 * kKB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 template <typename T, class OA, class OB>
@@ -261,7 +295,7 @@ __device__ inline void gemm_mainloop(floatx16 (&acc)[4][4], const OA& la, const 
   __syncthreads();
   SubFrags<V> f0, f1;
   read_sub(f0, lds, fa, 0);
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int kt = 0; kt + 1 < nk; ++kt) {
     const char* stage = lds + (kt & 1) * kStageBytes;
     __builtin_amdgcn_sched_barrier(0);
     read_sub(f1, stage, fa, 1);
@@ -276,19 +310,33 @@ __device__ inline void gemm_mainloop(floatx16 (&acc)[4][4], const OA& la, const 
     __builtin_amdgcn_sched_barrier(0);
     mfma16(acc, f0.a, f0.b);
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) {
-      // the loads of stage kt+1 are this wave's oldest outstanding ones
-      wait_vmcnt<0>();
-      __syncthreads();
-      if (kt + 2 < nk) {
-        la.issue(kt + 2, base + (kt & 1) * kStageBytes);
-        lb.issue(kt + 2, base + (kt & 1) * kStageBytes);
-      }
-      read_sub(f0, lds + ((kt + 1) & 1) * kStageBytes, fa, 0);
-    }
+    // the loads of stage kt+1 are this wave's oldest outstanding ones
+    wait_vmcnt<0>();
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_sub_interleaved(acc, f1, la, lb, kt + 2, base + (kt & 1) * kStageBytes, f0,
+                         lds + ((kt + 1) & 1) * kStageBytes, fa);
+  }
+  {
+    const char* stage = lds + ((nk - 1) & 1) * kStageBytes;
+    __builtin_amdgcn_sched_barrier(0);
+    read_sub(f1, stage, fa, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma16(acc, f0.a, f0.b);
+    __builtin_amdgcn_sched_barrier(0);
+    read_sub(f0, stage, fa, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma16(acc, f1.a, f1.b);
+    __builtin_amdgcn_sched_barrier(0);
+    read_sub(f1, stage, fa, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma16(acc, f0.a, f0.b);
     __builtin_amdgcn_sched_barrier(0);
     mfma16(acc, f1.a, f1.b);
   }
+  // the loads of the stage past the end (zeros into a free buffer) have
+  // landed before the caller reuses the LDS
+  wait_vmcnt<0>();
   __builtin_amdgcn_sched_barrier(0);
 }
 
