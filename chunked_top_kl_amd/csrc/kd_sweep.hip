@@ -70,12 +70,14 @@ __device__ inline void cursor_adv(Cursor& c, const int32_t* ids_s, int K) {
 }
 
 // Walk the teacher ids of one token column that fall in [lo, lo+128) (this
-// wave's half tile). Accumulator values are addressed per lane through a
-// small per-lane LDS slot (16 floats): for each 32-row block i that holds a
-// hit of some lane, the block is dumped to the slot and on(i, slot) is
-// called; `me`/`rr` tell the lane whether its current hit sits in block i and
-// at which of its 16 registers. After each round every lane with a hit
-// advances its cursor.
+// wave's half tile). The two lanes of a token column (lane halves) walk the
+// same ids; a hit at local row r belongs to the lane whose half is bit 2 of r,
+// at its register (r >> 5) * 16 + ((r >> 3) & 3) * 4 + (r & 3). Each round
+// calls on(tgt, e) on every lane, with tgt that register or -1 when the lane
+// has no hit of its own this round, and e the hit's index in the sorted
+// table; then every lane with a hit advances. The callback reaches the
+// register with a compare-and-select over all 64 (static indices only), so
+// the column's values stay in registers across the walk.
 template <class F>
 __device__ __forceinline__ void walk_hits(Cursor& c, const int32_t* ids_s, int K, int lo, int half,
                                           F&& on) {
@@ -86,23 +88,142 @@ __device__ __forceinline__ void walk_hits(Cursor& c, const int32_t* ids_s, int K
     if (ballot(h) == 0) break;
     const int local = c.nid - lo;
     const bool mine = h && (((local >> 2) & 1) == half);
-    const int blk = local >> 5;
-    const int rr = ((local >> 3) & 3) * 4 + (local & 3);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool me = mine && blk == i;
-      if (ballot(me)) on(i, me, rr, c.base + c.cur);
-    }
+    const int tgt = mine ? (local >> 5) * 16 + ((local >> 3) & 3) * 4 + (local & 3) : -1;
+    on(tgt, c.base + c.cur);
     if (h) cursor_adv(c, ids_s, K);
+  }
+}
+
+// z[tgt] (tgt in [0, 64)); 0 for tgt < 0.
+__device__ __forceinline__ float pick64(const float (&z)[64], int tgt) {
+  float v = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 64; ++e) v = (e == tgt) ? z[e] : v;
+  return v;
+}
+
+// z[tgt] -= x (no change for tgt < 0).
+__device__ __forceinline__ void sub64(float (&z)[64], int tgt, float x) {
+#pragma unroll
+  for (int e = 0; e < 64; ++e) z[e] = (e == tgt) ? z[e] - x : z[e];
+}
+
+// ---------------------------------------------------------------------------
+// Gradient tile epilogue (bf16): G = coef * (2^(z*c - lse2) - p~) for the
+// 256 x 256 tile, written to G [rows][Vp] and G^T [Vp][Cp] through LDS so
+// that both are stored as whole 16-byte granules along their rows.
+//
+// Half of the token columns at a time (columns j = 2jp, 2jp+1 of every lane)
+// are staged in the idle main-loop stage area as
+//   G^T part: [256 v][128 t'] bf16, 256 B per row, 16-byte granule index
+//             xor 4 on rows with bit 2 set (the two lane halves write rows
+//             four apart);
+//   G part:   [128 t'][256 v] bf16, 512 B per row, granule index xor (t' & 31)
+//             (consecutive lanes write consecutive rows),
+// with staging column t' = wn*64 + (j&1)*32 + lane%32, i.e. tile token
+// (t' / 64) * 128 + 64 jp + t' % 64. Then all 256 threads store rows.
+// Every wave takes part in the barriers; a wave whose half tile lies past the
+// vocabulary computes nothing (its rows are at or past Vp and never stored).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int staged_token(int tp, int jp) {
+  return (tp >> 6) * 128 + 64 * jp + (tp & 63);
+}
+
+template <class CursorArr>
+__device__ __forceinline__ void grad_tile_staged(floatx16 (&acc)[4][4], const SweepArgs& a, int vt,
+                                                 int jt, int rows, int tl0, float c, float coef,
+                                                 const float (&lse2)[4], CursorArr& cu,
+                                                 char* lds) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int half = lane >> 5;
+  const int vw0 = vt * kTile + wm * 128;
+  const bool live = vw0 < a.V;
+  const bool tail = vw0 + 128 > a.V;
+  const int Vp = (int)round_up(a.V, 8);
+  const int tpad = (int)round_up(rows, 8);
+  char* sgt = lds;
+  char* sg = lds + 64 * 1024;
+  // every wave has read its last main-loop fragments before the area is reused
+  __syncthreads();
+#pragma unroll
+  for (int jp = 0; jp < 2; ++jp) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = 2 * jp + jj;
+      __builtin_amdgcn_sched_barrier(0);
+      if (live) {
+        float z[64];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float x = acc[i][j][r];
+            if (tail && vw0 + acc_row(i, r, half) >= a.V) x = -INFINITY;
+            z[i * 16 + r] = x;
+          }
+#pragma unroll
+        for (int e = 0; e < 64; ++e) z[e] = fast_exp2(fmaf(z[e], c, -lse2[j]));
+        walk_hits(cu[j], a.ids_s, a.K, vw0, half, [&](int tgt, int64_t e) {
+          sub64(z, tgt, tgt >= 0 ? a.p_s[e] : 0.0f);
+        });
+        // token columns past `rows` hold a repeated row: exact zeros
+        const float cf = (tl0 + 32 * j < rows) ? coef : 0.0f;
+        const int tp = wn * 64 + jj * 32 + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int vl = wm * 128 + i * 32 + 8 * q + 4 * half;
+            const uint32_t b0 = f32_to_bf16_bits(z[i * 16 + 4 * q + 0] * cf);
+            const uint32_t b1 = f32_to_bf16_bits(z[i * 16 + 4 * q + 1] * cf);
+            const uint32_t b2 = f32_to_bf16_bits(z[i * 16 + 4 * q + 2] * cf);
+            const uint32_t b3 = f32_to_bf16_bits(z[i * 16 + 4 * q + 3] * cf);
+            const int tcol = (((tp >> 3) ^ (((vl >> 2) & 1) << 2)) << 4) + (tp & 7) * 2;
+            *(uint16_t*)(sgt + (vl + 0) * 256 + tcol) = (uint16_t)b0;
+            *(uint16_t*)(sgt + (vl + 1) * 256 + tcol) = (uint16_t)b1;
+            *(uint16_t*)(sgt + (vl + 2) * 256 + tcol) = (uint16_t)b2;
+            *(uint16_t*)(sgt + (vl + 3) * 256 + tcol) = (uint16_t)b3;
+            const int vcol = (((vl >> 3) ^ (tp & 31)) << 4) + (vl & 7) * 2;
+            *(uint2*)(sg + tp * 512 + vcol) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+          }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    // G^T rows: 256 rows x 16 granules of 8 tokens
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+      const int g = it * 256 + tid;
+      const int vl = g >> 4, gr = g & 15;
+      const int v = vt * kTile + vl;
+      const int t = jt * kTile + staged_token(gr * 8, jp);
+      if (v < Vp && t < tpad) {
+        const u32x4 val = *(const u32x4*)(sgt + vl * 256 + ((gr ^ (((vl >> 2) & 1) << 2)) << 4));
+        __builtin_nontemporal_store(val, (u32x4*)(a.GT + (int64_t)v * a.ldgt + (int64_t)t * 2));
+      }
+    }
+    // G rows: 128 rows x 32 granules of 8 vocabulary entries
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+      const int g = it * 256 + tid;
+      const int tp = g >> 5, gr = g & 31;
+      const int t = jt * kTile + staged_token(tp, jp);
+      const int v = vt * kTile + gr * 8;
+      if (t < rows && v < Vp) {
+        const u32x4 val = *(const u32x4*)(sg + tp * 512 + ((gr ^ (tp & 31)) << 4));
+        __builtin_nontemporal_store(val, (u32x4*)(a.G + (int64_t)t * a.ldg + (int64_t)v * 2));
+      }
+    }
+    // the next half (or the next tile's loads) reuses the area
+    __syncthreads();
   }
 }
 
 template <typename T, int KIND, bool MAP>
 __device__ __forceinline__ void sweep_body(SweepArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kMainLds + 4 * 4096];
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int half = lane >> 5;
-  float* slot = (float*)(lds + kMainLds + w * 4096 + lane * 64);
 
   int rows = a.row_cap;
   if (a.nrows_dev) {
@@ -115,8 +236,15 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
   const int ns = sweep_splits(ntt, nvt, a.ncu);
   const int total = ntt * ns;
   if ((int)blockIdx.x >= total) return;
+  // Grouped raster: consecutive logical ids (one XCD, one round) walk up to 8
+  // token tiles fastest, then vocabulary ranges, so the 32 work-groups an XCD
+  // runs at once share each W panel up to 8 ways and each token panel 4 ways,
+  // and a vocabulary range of W is read by as few XCDs as the grid allows.
   const int L = xcd_remap(blockIdx.x, total);
-  const int jt = L / ns, b = L % ns;
+  const int GM = ntt < 8 ? ntt : 8;
+  const int grp = L / (GM * ns), in = L % (GM * ns);
+  const int gm = (ntt - grp * GM) < GM ? (ntt - grp * GM) : GM;
+  const int jt = grp * GM + in % gm, b = in / gm;
   const int vt_begin = (int)((int64_t)b * nvt / ns);
   const int vt_end = (int)((int64_t)(b + 1) * nvt / ns);
 
@@ -183,6 +311,10 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
     gemm_mainloop<T>(acc, la, lb, nk, lds);
 
     const int vw0 = vt * kTile + wm * 128;
+    if constexpr (KIND == kSweepBwdG && sizeof(T) == 2) {
+      grad_tile_staged(acc, a, vt, jt, rows, tl0, c, coef, lse2, cu, lds);
+      continue;
+    }
     if (vw0 >= a.V) continue;  // wave-uniform: this half tile is past the vocabulary
     const bool tail = vw0 + 128 > a.V;
     // columns in [V, round_up(V, 8)) of G are written as zeros (see the store)
@@ -224,14 +356,9 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
           m[j] = mn;
         }
         float* zrow = a.z_topk ? a.z_topk + (int64_t)orow[j] * a.K : nullptr;
-        walk_hits(cu[j], a.ids_s, a.K, vw0, half, [&](int i, bool me, int rr, int64_t e) {
-          floatx4* sl = (floatx4*)slot;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            sl[q] = floatx4{z[i * 16 + 4 * q], z[i * 16 + 4 * q + 1], z[i * 16 + 4 * q + 2],
-                            z[i * 16 + 4 * q + 3]};
-          if (me) {
-            const float val = slot[rr];
+        walk_hits(cu[j], a.ids_s, a.K, vw0, half, [&](int tgt, int64_t e) {
+          const float val = pick64(z, tgt);
+          if (tgt >= 0) {
             d[j] += a.p_s[e] * val;
             if (zrow) zrow[a.korig_s[e]] = val * invT;
           }
@@ -271,21 +398,8 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
       if constexpr (KIND == kSweepBwdG) {
 #pragma unroll
         for (int e = 0; e < 64; ++e) z[e] = fast_exp2(fmaf(z[e], c, -lse2[j]));
-        walk_hits(cu[j], a.ids_s, a.K, vw0, half, [&](int i, bool me, int rr, int64_t e) {
-          floatx4* sl = (floatx4*)slot;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            sl[q] = floatx4{z[i * 16 + 4 * q], z[i * 16 + 4 * q + 1], z[i * 16 + 4 * q + 2],
-                            z[i * 16 + 4 * q + 3]};
-          if (me) slot[rr] -= a.p_s[e];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const floatx4 v = sl[q];
-            z[i * 16 + 4 * q] = v[0];
-            z[i * 16 + 4 * q + 1] = v[1];
-            z[i * 16 + 4 * q + 2] = v[2];
-            z[i * 16 + 4 * q + 3] = v[3];
-          }
+        walk_hits(cu[j], a.ids_s, a.K, vw0, half, [&](int tgt, int64_t e) {
+          sub64(z, tgt, tgt >= 0 ? a.p_s[e] : 0.0f);
         });
         // G [rows][Vp] feeds dHidden, G^T [Vp][Cp] feeds dW. Vocabulary
         // columns in [V, Vp) and token columns in [rows, round_up(rows, 8))
