@@ -112,7 +112,10 @@ struct Layout {
   size_t total;
   int64_t C;          // rows per backward chunk (<= S, >= 1)
   int64_t Vp;         // padded row length of the gradient tile
-  int64_t Cp;         // padded row length of the transposed chunk tiles
+  int64_t Cp;         // token columns of the transposed chunk tiles (rows rounded to 32)
+  int64_t Cld;        // their row pitch in elements: Cp plus 128 bytes, so that the
+                      // 256 rows of a dW operand tile do not share one offset
+                      // modulo a large power of two (L2 channel conflicts)
   int64_t esz;
 };
 
@@ -124,6 +127,7 @@ Layout plan(const kd_problem* p) {
   L.C = p->chunk < S ? p->chunk : (S > 0 ? S : 1);
   L.Vp = round_up(V, 8);
   L.Cp = round_up(L.C, 32);
+  L.Cld = L.Cp + 128 / L.esz;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -145,9 +149,9 @@ Layout plan(const kd_problem* p) {
   L.pd = take(pe * 4);
   L.bsum = take((ceil_div(Sx, 256) + 1) * 8);
   L.G = take(L.C * L.Vp * L.esz);
-  L.GT = take(L.Vp * L.Cp * L.esz);
+  L.GT = take(L.Vp * L.Cld * L.esz);
   L.WT = take(H * L.Vp * L.esz);
-  L.XcT = take(H * L.Cp * L.esz);
+  L.XcT = take(H * L.Cld * L.esz);
   int ksmax = 1;
   for (int64_t r = kd::kTile; r < L.C + kd::kTile; r += kd::kTile) {
     const int rows = (int)(r < L.C ? r : L.C);
@@ -332,7 +336,7 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
       Prof pr("gather_rows_t", st);
       KD_HIP(kd::launch_gather_rows_t(f32, (const char*)hidden, row_bytes, at<int32_t>(ws, L.idx),
                                       at<int32_t>(ws, L.count), row_begin, C, H,
-                                      at<char>(ws, L.XcT), (int64_t)Cp * L.esz, Cp, st));
+                                      at<char>(ws, L.XcT), L.Cld * L.esz, Cp, st));
     }
     if (S > 0) {
       kd::SweepArgs a;
@@ -358,7 +362,7 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
       a.G = at<char>(ws, L.G);
       a.ldg = L.Vp * L.esz;
       a.GT = at<char>(ws, L.GT);
-      a.ldgt = L.Cp * L.esz;
+      a.ldgt = L.Cld * L.esz;
       Prof pr("bwd_grad_tile", st);
       KD_HIP(kd::launch_sweep(kd::kSweepBwdG, f32, 1, a, sgrid, st));
     }
@@ -394,10 +398,10 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
     }
     kd::DwArgs w;
     w.GT = at<char>(ws, L.GT);
-    w.ldgt = L.Cp * L.esz;
+    w.ldgt = L.Cld * L.esz;
     w.Vp = Vp;
     w.XcT = at<char>(ws, L.XcT);
-    w.ldxt = L.Cp * L.esz;
+    w.ldxt = L.Cld * L.esz;
     w.nrows_dev = at<int32_t>(ws, L.count);
     w.row_begin = row_begin;
     w.row_cap = C;

@@ -252,28 +252,64 @@ __device__ __forceinline__ void dw_body(DwArgs a) {
 
   const bool beta = (a.row_begin > 0) || a.beta_first;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
-  // 16 rows of one 32x32 block per step: all loads of the block are issued
-  // before any store, so the read-modify-write streams instead of serialising
+  // Read-modify-write of the tile's dW rows through a buffer resource over
+  // them: rows past V fall outside it and a column past H gets an offset past
+  // it, so loads read 0 and stores are dropped without a branch. Straight-line
+  // code lets the loads of one group (32 values) be in flight while the
+  // previous group is added and stored.
+  const int vrows = (a.V - m * kTile) < kTile ? (a.V - m * kTile) : kTile;
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(a.dW + (int64_t)m * kTile * a.H, (int64_t)vrows * a.H * 4);
+  uint32_t off[4][16];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int h = n * kTile + wn * 128 + j * 32 + (lane & 31);
-    const bool hok = h < a.H;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int v0 = m * kTile + wm * 128 + i * 32 + 4 * (lane >> 5);
-      float* base = a.dW + (int64_t)v0 * a.H + h;
-      float old[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int v = v0 + 8 * (r >> 2) + (r & 3);
-        old[r] = (beta && hok && v < a.V) ? base[(int64_t)(8 * (r >> 2) + (r & 3)) * a.H] : 0.0f;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int v = v0 + 8 * (r >> 2) + (r & 3);
-        if (hok && v < a.V) base[(int64_t)(8 * (r >> 2) + (r & 3)) * a.H] = old[r] + acc[i][j][r];
-      }
+    for (int r = 0; r < 16; ++r) {
+      // row within the tile of acc[i][j][r] for i = 0; block i adds 32 rows
+      const int row = wm * 128 + 4 * (lane >> 5) + 8 * (r >> 2) + (r & 3);
+      off[j][r] = h < a.H ? (uint32_t)((row * a.H + h) * 4) : kOob;
     }
+  }
+  const uint32_t istride = 32u * (uint32_t)a.H * 4u;
+  auto addr = [&](int j, int i, int r) -> int {
+    return (int)(off[j][r] == kOob ? kOob : off[j][r] + (uint32_t)i * istride);
+  };
+  // group g: block j = g / 2, blocks i = 2 (g % 2) and 2 (g % 2) + 1
+  auto ld = [&](int g, float (&o)[32]) {
+    const int j = g >> 1, i0 = (g & 1) * 2;
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        o[ii * 16 + r] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rs, addr(j, i0 + ii, r), 0, 0));
+  };
+  auto st = [&](int g, const float (&o)[32]) {
+    const int j = g >> 1, i0 = (g & 1) * 2;
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        __builtin_amdgcn_raw_buffer_store_b32(
+            __builtin_bit_cast(uint32_t, o[ii * 16 + r] + acc[i0 + ii][j][r]), rs,
+            addr(j, i0 + ii, r), 0, 0);
+  };
+  float b0[32], b1[32];
+  if (beta) {
+    ld(0, b0);
+#pragma unroll
+    for (int g = 0; g < 8; g += 2) {
+      ld(g + 1, b1);
+      st(g, b0);
+      if (g + 2 < 8) ld(g + 2, b0);
+      st(g + 1, b1);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) b0[e] = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) st(g, b0);
   }
 }
 
