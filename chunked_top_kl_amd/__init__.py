@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkdtopk.s
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m chunked_top_kl_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python chunked_top_kl_amd/build.py` (or `__graft_entry__.build()`) "
         "(hipcc for gfx950). There is no fallback implementation.")
 
 lib = ctypes.CDLL(LIB_PATH)

@@ -215,13 +215,14 @@ struct FragAddr {
 // read while sub-step s computes. Before the last sub-step: wait for this
 // wave's loads of stage kt+1 and barrier (stage kt+1 visible to all waves;
 // every wave holds its stage-kt fragments, so stage kt's buffer is free).
-// The last sub-step then issues, one per MFMA, the 16 loads of stage kt+2
-// into that buffer and the 8 sub-step-0 fragment reads of stage kt+1: issued
-// in one burst, the loads back up the vector memory queue and stall the
-// wave's in-order issue while the MFMA pipe has nothing queued. A stage at or
-// past the end of K reads zeros (or, for a row-mapped operand, a valid
-// granule) into the free buffer, so the issue needs no branch. The last stage
-// is peeled: it has no barrier, so it issues no loads.
+// The loads of stage kt+2 into that buffer are spread over the MFMAs: the 8
+// of operand A over the last sub-step of stage kt (with the 8 sub-step-0
+// fragment reads of stage kt+1), the 8 of operand B over the first sub-step
+// of stage kt+1. Issued in one burst, the loads back up the vector memory
+// queue and stall the wave's in-order issue while its MFMA pipe runs dry.
+// A stage at or past the end of K reads zeros (or, for a row-mapped operand,
+// a valid granule) into the free buffer, so the issue needs no branch. The
+// last stage is peeled: it issues no loads.
 // ---------------------------------------------------------------------------
 template <typename V>
 struct SubFrags {
@@ -245,21 +246,35 @@ __device__ __forceinline__ void mfma_ij(floatx16& acc, const floatx4& a, const f
   for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[q], b[q], acc, 0, 0, 0);
 }
 
-// Last sub-step of stage kt with the loads of stage kn = kt + 2 (into the
-// buffer at `sbase`) and the sub-step-0 reads of the next stage interleaved.
-template <class V, class OA, class OB>
-__device__ __forceinline__ void mfma_sub_interleaved(floatx16 (&acc)[4][4], const SubFrags<V>& f,
-                                                     const OA& la, const OB& lb, int kn,
-                                                     uint32_t sbase, SubFrags<V>& fn,
-                                                     const char* nstage, const FragAddr& fa) {
+// A sub-step whose MFMAs are interleaved with the 8 loads of one operand of
+// stage kn (into the buffer at `sbase`), one load per two MFMA blocks.
+template <class V, class OP>
+__device__ __forceinline__ void mfma_sub_loads(floatx16 (&acc)[4][4], const SubFrags<V>& f,
+                                               const OP& op, int kn, uint32_t sbase) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int q = i * 4 + j;
       mfma_ij(acc[i][j], f.a[i], f.b[j]);
-      if (q < 8) la.issue_one(kn, sbase, q);
-      else lb.issue_one(kn, sbase, q - 8);
+      if ((q & 1) == 0) op.issue_one(kn, sbase, q >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The same with the sub-step-0 fragment reads of the next stage as well.
+template <class V, class OP>
+__device__ __forceinline__ void mfma_sub_loads_reads(floatx16 (&acc)[4][4], const SubFrags<V>& f,
+                                                     const OP& op, int kn, uint32_t sbase,
+                                                     SubFrags<V>& fn, const char* nstage,
+                                                     const FragAddr& fa) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = i * 4 + j;
+      mfma_ij(acc[i][j], f.a[i], f.b[j]);
+      if ((q & 1) == 0) op.issue_one(kn, sbase, q >> 1);
       if (q < 4) fn.a[q] = *(const V*)(nstage + fa.a[0] + q * 32 * kKB);
       else if (q < 8) fn.b[q - 4] = *(const V*)(nstage + fa.b[0] + (q - 4) * 32 * kKB);
       __builtin_amdgcn_sched_barrier(0);
@@ -286,9 +301,9 @@ __device__ inline void gemm_mainloop(floatx16 (&acc)[4][4], const OA& la, const 
   la.issue(0, base);
   lb.issue(0, base);
   if (nk > 1) {
+    // operand B of stage 1 follows in the first sub-step, like every stage's
     la.issue(1, base + kStageBytes);
-    lb.issue(1, base + kStageBytes);
-    wait_vmcnt<16>();
+    wait_vmcnt<8>();
   } else {
     wait_vmcnt<0>();
   }
@@ -300,7 +315,8 @@ __device__ inline void gemm_mainloop(floatx16 (&acc)[4][4], const OA& la, const 
     __builtin_amdgcn_sched_barrier(0);
     read_sub(f1, stage, fa, 1);
     __builtin_amdgcn_sched_barrier(0);
-    mfma16(acc, f0.a, f0.b);
+    // operand B of stage kt+1
+    mfma_sub_loads(acc, f0, lb, kt + 1, base + ((kt + 1) & 1) * kStageBytes);
     __builtin_amdgcn_sched_barrier(0);
     read_sub(f0, stage, fa, 2);
     __builtin_amdgcn_sched_barrier(0);
@@ -310,11 +326,12 @@ __device__ inline void gemm_mainloop(floatx16 (&acc)[4][4], const OA& la, const 
     __builtin_amdgcn_sched_barrier(0);
     mfma16(acc, f0.a, f0.b);
     __builtin_amdgcn_sched_barrier(0);
-    // the loads of stage kt+1 are this wave's oldest outstanding ones
+    // this wave's loads of stage kt+1 (its A and B) are all it has outstanding
     wait_vmcnt<0>();
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    mfma_sub_interleaved(acc, f1, la, lb, kt + 2, base + (kt & 1) * kStageBytes, f0,
+    // operand A of stage kt+2 into stage kt's buffer, and stage kt+1's first reads
+    mfma_sub_loads_reads(acc, f1, la, kt + 2, base + (kt & 1) * kStageBytes, f0,
                          lds + ((kt + 1) & 1) * kStageBytes, fa);
   }
   {
