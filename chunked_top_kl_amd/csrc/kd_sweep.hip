@@ -118,13 +118,16 @@ __device__ __forceinline__ void sub64(float (&z)[64], int tgt, float x) {
 //   G^T part: [256 v][128 t'] bf16, 256 B per row, 16-byte granule index
 //             xor 4 on rows with bit 2 set (the two lane halves write rows
 //             four apart);
-//   G part:   [128 t'][256 v] bf16, 512 B per row, granule index xor (t' & 31)
-//             (consecutive lanes write consecutive rows),
+//   G part:   [128 t'][256 v] bf16, rows kGPitch = 528 B apart (padding
+//             puts the rows that consecutive lanes write in distinct banks),
 // with staging column t' = wn*64 + (j&1)*32 + lane%32, i.e. tile token
 // (t' / 64) * 128 + 64 jp + t' % 64. Then all 256 threads store rows.
 // Every wave takes part in the barriers; a wave whose half tile lies past the
 // vocabulary computes nothing (its rows are at or past Vp and never stored).
 // ---------------------------------------------------------------------------
+constexpr int kGPitch = 528;
+constexpr int kStagingLds = 64 * 1024 + 128 * kGPitch;   // fits in kMainLds + 2 KB
+
 __device__ __forceinline__ int staged_token(int tp, int jp) {
   return (tp >> 6) * 128 + 64 * jp + (tp & 63);
 }
@@ -163,29 +166,52 @@ __device__ __forceinline__ void grad_tile_staged(floatx16 (&acc)[4][4], const Sw
           }
 #pragma unroll
         for (int e = 0; e < 64; ++e) z[e] = fast_exp2(fmaf(z[e], c, -lse2[j]));
-        walk_hits(cu[j], a.ids_s, a.K, vw0, half, [&](int tgt, int64_t e) {
-          sub64(z, tgt, tgt >= 0 ? a.p_s[e] : 0.0f);
-        });
         // token columns past `rows` hold a repeated row: exact zeros
         const float cf = (tl0 + 32 * j < rows) ? coef : 0.0f;
         const int tp = wn * 64 + jj * 32 + (lane & 31);
+        // staging bases of this lane's first row (wm*128 + 4*half); row
+        // dv further on is at + dv*256 (G^T part) and + dv*2 (G part). The
+        // G^T granule swizzle bit ((row >> 2) & 1) is the lane half for all
+        // of this lane's rows.
+        char* gtb = sgt + (wm * 128 + 4 * half) * 256 +
+                    ((((tp >> 3) ^ (half << 2)) << 4) + (tp & 7) * 2);
+        char* gb = sg + tp * kGPitch + (wm * 128 + 4 * half) * 2;
+        // every value as if no teacher id hit it ...
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int vl = wm * 128 + i * 32 + 8 * q + 4 * half;
-            const uint32_t b0 = f32_to_bf16_bits(z[i * 16 + 4 * q + 0] * cf);
-            const uint32_t b1 = f32_to_bf16_bits(z[i * 16 + 4 * q + 1] * cf);
-            const uint32_t b2 = f32_to_bf16_bits(z[i * 16 + 4 * q + 2] * cf);
-            const uint32_t b3 = f32_to_bf16_bits(z[i * 16 + 4 * q + 3] * cf);
-            const int tcol = (((tp >> 3) ^ (((vl >> 2) & 1) << 2)) << 4) + (tp & 7) * 2;
-            *(uint16_t*)(sgt + (vl + 0) * 256 + tcol) = (uint16_t)b0;
-            *(uint16_t*)(sgt + (vl + 1) * 256 + tcol) = (uint16_t)b1;
-            *(uint16_t*)(sgt + (vl + 2) * 256 + tcol) = (uint16_t)b2;
-            *(uint16_t*)(sgt + (vl + 3) * 256 + tcol) = (uint16_t)b3;
-            const int vcol = (((vl >> 3) ^ (tp & 31)) << 4) + (vl & 7) * 2;
-            *(uint2*)(sg + tp * 512 + vcol) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+            const int dv = i * 32 + 8 * q;
+            const bf16x2 p01 = {(__bf16)(z[i * 16 + 4 * q + 0] * cf),
+                                (__bf16)(z[i * 16 + 4 * q + 1] * cf)};
+            const bf16x2 p23 = {(__bf16)(z[i * 16 + 4 * q + 2] * cf),
+                                (__bf16)(z[i * 16 + 4 * q + 3] * cf)};
+            const uint32_t u01 = __builtin_bit_cast(uint32_t, p01);
+            const uint32_t u23 = __builtin_bit_cast(uint32_t, p23);
+            *(uint16_t*)(gtb + (dv + 0) * 256) = (uint16_t)u01;
+            *(uint16_t*)(gtb + (dv + 1) * 256) = (uint16_t)(u01 >> 16);
+            *(uint16_t*)(gtb + (dv + 2) * 256) = (uint16_t)u23;
+            *(uint16_t*)(gtb + (dv + 3) * 256) = (uint16_t)(u23 >> 16);
+            *(uint2*)(gb + dv * 2) = make_uint2(u01, u23);
           }
+        // ... then each hit overwrites its two staged entries with
+        // coef * (q - P), computed in fp32 and rounded once. Duplicate ids
+        // of a row are adjacent in the sorted table and reach the same
+        // register in consecutive rounds of this lane: P sums their p.
+        int prev = -1;
+        float psum = 0.0f;
+        walk_hits(cu[j], a.ids_s, a.K, vw0, half, [&](int tgt, int64_t e) {
+          const float val = pick64(z, tgt);
+          if (tgt >= 0) {
+            psum = (tgt == prev ? psum : 0.0f) + a.p_s[e];
+            prev = tgt;
+            const int dv = (tgt >> 4) * 32 + 8 * ((tgt >> 2) & 3) + (tgt & 3);
+            const bf16x2 g = {(__bf16)((val - psum) * cf), (__bf16)0.0f};
+            const uint16_t gv = (uint16_t)__builtin_bit_cast(uint32_t, g);
+            *(uint16_t*)(gtb + dv * 256) = gv;
+            *(uint16_t*)(gb + dv * 2) = gv;
+          }
+        });
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -210,7 +236,7 @@ __device__ __forceinline__ void grad_tile_staged(floatx16 (&acc)[4][4], const Sw
       const int t = jt * kTile + staged_token(tp, jp);
       const int v = vt * kTile + gr * 8;
       if (t < rows && v < Vp) {
-        const u32x4 val = *(const u32x4*)(sg + tp * 512 + ((gr ^ (tp & 31)) << 4));
+        const u32x4 val = *(const u32x4*)(sg + tp * kGPitch + gr * 16);
         __builtin_nontemporal_store(val, (u32x4*)(a.G + (int64_t)t * a.ldg + (int64_t)v * 2));
       }
     }
@@ -221,7 +247,9 @@ __device__ __forceinline__ void grad_tile_staged(floatx16 (&acc)[4][4], const Sw
 
 template <typename T, int KIND, bool MAP>
 __device__ __forceinline__ void sweep_body(SweepArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
+  // main-loop stages; the gradient tile epilogue stages its output here too
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds + 2048];
+  static_assert(kStagingLds <= kMainLds + 2048, "staging area");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int half = lane >> 5;
 
