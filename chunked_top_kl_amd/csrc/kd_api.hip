@@ -27,7 +27,8 @@ using kd::round_up;
 constexpr int kCostCUs = 256;
 constexpr int64_t kMaxK = 4096;
 constexpr int64_t kMaxRows = int64_t(1) << 30;
-constexpr double kSelectEps = 2e-5;   // bound on |fp32-path entropy - fp64 entropy| (nats)
+constexpr double kSelectEps = 2e-5;
+constexpr int64_t kDwDepth = 8192;     // tokens per dW contraction (a multiple of chunks)   // bound on |fp32-path entropy - fp64 entropy| (nats)
 constexpr int kRefineBlocks = 512;
 
 // ------------------------------------------------------------------ profiling
@@ -112,7 +113,9 @@ struct Layout {
   size_t total;
   int64_t C;          // rows per backward chunk (<= S, >= 1)
   int64_t Vp;         // padded row length of the gradient tile
-  int64_t Cp;         // token columns of the transposed chunk tiles (rows rounded to 32)
+  int64_t slot;       // token columns of one chunk in the transposed tiles: round_up(C, 8)
+  int64_t nd;         // chunks per dW contraction (group)
+  int64_t Cp;         // token columns of the transposed tiles: nd slots rounded to 32
   int64_t Cld;        // their row pitch in elements: Cp plus 128 bytes, so that the
                       // 256 rows of a dW operand tile do not share one offset
                       // modulo a large power of two (L2 channel conflicts)
@@ -126,7 +129,17 @@ Layout plan(const kd_problem* p) {
   L.esz = p->hw_dtype == KD_F32 ? 4 : 2;
   L.C = p->chunk < S ? p->chunk : (S > 0 ? S : 1);
   L.Vp = round_up(V, 8);
-  L.Cp = round_up(L.C, 32);
+  L.slot = round_up(L.C, 8);
+  {
+    // dW contracts about kDwDepth tokens per launch: its fp32 read-modify-write
+    // of dW is paid once per group instead of once per chunk
+    const int64_t nch = S > 0 ? ceil_div(S, L.C) : 1;
+    int64_t nd = kDwDepth / L.slot;
+    if (nd < 1) nd = 1;
+    if (nd > nch) nd = nch;
+    L.nd = nd;
+  }
+  L.Cp = round_up(L.nd * L.slot, 32);
   L.Cld = L.Cp + 128 / L.esz;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -325,18 +338,20 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
   const int nchunks = S > 0 ? (int)ceil_div(S, C) : 1;
   const int dgrid = kd::dh_grid(C, V, H, kCostCUs, f32);
   const int sgrid = kd::sweep_grid(C, V, kCostCUs);
-  const int Vp = (int)L.Vp, Cp = (int)L.Cp;
+  const int Vp = (int)L.Vp;
   if (S > 0) {
     Prof pr("transpose_w", st);
     KD_HIP(kd::launch_transpose_w(f32, (const char*)W, V, H, at<char>(ws, L.WT), Vp, st));
   }
   for (int ci = 0; ci < nchunks; ++ci) {
     const int row_begin = ci * C;
+    const int slot = (int)(ci % L.nd);   // this chunk's columns in the dW group
     if (S > 0) {
       Prof pr("gather_rows_t", st);
       KD_HIP(kd::launch_gather_rows_t(f32, (const char*)hidden, row_bytes, at<int32_t>(ws, L.idx),
                                       at<int32_t>(ws, L.count), row_begin, C, H,
-                                      at<char>(ws, L.XcT), L.Cld * L.esz, Cp, st));
+                                      at<char>(ws, L.XcT) + slot * L.slot * L.esz, L.Cld * L.esz,
+                                      (int)L.slot, st));
     }
     if (S > 0) {
       kd::SweepArgs a;
@@ -361,7 +376,7 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
       a.grad_loss = grad_loss;
       a.G = at<char>(ws, L.G);
       a.ldg = L.Vp * L.esz;
-      a.GT = at<char>(ws, L.GT);
+      a.GT = at<char>(ws, L.GT) + slot * L.slot * L.esz;
       a.ldgt = L.Cld * L.esz;
       Prof pr("bwd_grad_tile", st);
       KD_HIP(kd::launch_sweep(kd::kSweepBwdG, f32, 1, a, sgrid, st));
@@ -396,21 +411,25 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
       Prof pr("bwd_dhidden_reduce", st);
       KD_HIP(kd::launch_dh_reduce(r, f32, st));
     }
-    kd::DwArgs w;
-    w.GT = at<char>(ws, L.GT);
-    w.ldgt = L.Cld * L.esz;
-    w.Vp = Vp;
-    w.XcT = at<char>(ws, L.XcT);
-    w.ldxt = L.Cld * L.esz;
-    w.nrows_dev = at<int32_t>(ws, L.count);
-    w.row_begin = row_begin;
-    w.row_cap = C;
-    w.V = V;
-    w.H = H;
-    w.beta_first = accumulate_dW;
-    w.dW = dW;
-    Prof pr("bwd_dw", st);
-    KD_HIP(kd::launch_dw(f32, w, st));
+    if (slot == L.nd - 1 || ci == nchunks - 1) {
+      kd::DwArgs w;
+      w.GT = at<char>(ws, L.GT);
+      w.ldgt = L.Cld * L.esz;
+      w.Vp = Vp;
+      w.XcT = at<char>(ws, L.XcT);
+      w.ldxt = L.Cld * L.esz;
+      w.nrows_dev = at<int32_t>(ws, L.count);
+      w.group_begin = (ci - slot) * C;
+      w.group_chunks = slot + 1;
+      w.chunk = C;
+      w.slot = (int)L.slot;
+      w.V = V;
+      w.H = H;
+      w.beta_first = accumulate_dW;
+      w.dW = dW;
+      Prof pr("bwd_dw", st);
+      KD_HIP(kd::launch_dw(f32, w, st));
+    }
   }
   return KD_OK;
 }

@@ -218,19 +218,22 @@ hipError_t launch_transpose_w(int f32, const char* W, int V, int H, char* WT, in
 
 // ---------------------------------------------------------------------------
 // dW[v][h] (+)= sum_r G[r][v] X_c[r][h]
-//   M = v (A = G^T [Vp][Cp]), N = h (B = X_c^T [H][Cp]); K = chunk rows,
-//   contiguous in both. Chunk 0 with
-//   beta_first = 0 overwrites dW (and writes zeros when the chunk is empty);
-//   later chunks add, and return at once when they hold no rows.
+//   M = v (A = G^T [Vp][slots]), N = h (B = X_c^T [H][slots]); K = the token
+//   columns of a group of chunks, contiguous in both. Group 0 with
+//   beta_first = 0 overwrites dW (and writes zeros when it is empty); later
+//   groups add, and return at once when they hold no rows.
 // ---------------------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ void dw_body(DwArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kMainLds];
-  int rows = chunk_rows(a.nrows_dev, a.row_begin, a.row_cap);
-  if (rows <= 0) {
-    if (a.row_begin > 0) return;
-    rows = 0;
+  // token columns of the group that hold data: whole slots of the full
+  // chunks, then the padded rows of a last partial one
+  int grows = chunk_rows(a.nrows_dev, a.group_begin, a.group_chunks * a.chunk);
+  if (grows <= 0) {
+    if (a.group_begin > 0) return;
+    grows = 0;
   }
+  const int rows = (grows / a.chunk) * a.slot + (int)round_up(grows % a.chunk, 8);
   constexpr int esz = Elem<T>::size;
   const int mt = (int)ceil_div(a.V, kTile), nt = (int)ceil_div(a.H, kTile);
   const int total = mt * nt;
@@ -250,7 +253,7 @@ __device__ __forceinline__ void dw_body(DwArgs a) {
   floatx16 acc[4][4];
   gemm_mainloop<T>(acc, la, lb, (int)ceil_div((int64_t)rows * esz, kKB), lds);
 
-  const bool beta = (a.row_begin > 0) || a.beta_first;
+  const bool beta = (a.group_begin > 0) || a.beta_first;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
   // Read-modify-write of the tile's dW rows through a buffer resource over
   // them: rows past V fall outside it and a column past H gets an offset past

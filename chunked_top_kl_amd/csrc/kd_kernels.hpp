@@ -65,11 +65,16 @@ struct DhReduceArgs {
   float* dH;
 };
 
+// dW contracts a group of consecutive chunks at once: chunk k of the group
+// occupies token columns [k*slot, k*slot + round_up(rows_k, 8)) of G^T and
+// X_c^T (zeros past rows_k), slot = round_up(C, 8).
 struct DwArgs {
-  const char* GT; int64_t ldgt; int Vp;             // gradient tile transposed [Vp, Cp]
-  const char* XcT; int64_t ldxt;                    // gathered hidden rows transposed [H, Cp]
+  const char* GT; int64_t ldgt; int Vp;             // gradient tiles transposed [Vp, slots]
+  const char* XcT; int64_t ldxt;                    // gathered hidden rows transposed [H, slots]
   const int32_t* nrows_dev;
-  int row_begin, row_cap, V, H, beta_first;
+  int group_begin;                                  // first compacted row of the group
+  int group_chunks, chunk, slot;                    // chunks in the group, C, round_up(C, 8)
+  int V, H, beta_first;
   float* dW;
 };
 

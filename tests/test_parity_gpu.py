@@ -154,6 +154,37 @@ def test_accumulate_dW(kd):
     assert torch.allclose(dW2 - 0.25, dW1, rtol=0, atol=1e-6)
 
 
+def test_dw_groups_of_chunks(kd):
+    # dW contracts up to 8192 tokens of consecutive chunks per launch: with a
+    # chunk of 2000 rows a group holds 4 chunks, so S = 9000 gives one full
+    # group and a second group of one partial chunk (1000 rows)
+    p = make_problem(9000, 64, 1000, 10, T=1.0, chunk=2000, seed=21)
+    got = run_fwd_bwd(kd, p, want=False)
+    check_against_oracle(p, got, chunk=1000)
+
+
+def test_dw_groups_with_mask_ending_inside_a_group(kd):
+    # the masked rows compact to N = 4500: chunks 0 and 1 are full, chunk 2
+    # holds 500 rows, chunk 3 and the second group hold none; dW accumulates
+    # into a non-zero buffer
+    p = make_problem(9000, 64, 1000, 10, T=2.0, chunk=2000, seed=22)
+    rng = np.random.default_rng(5)
+    keep = np.sort(rng.choice(9000, size=4500, replace=False))
+    mask = np.zeros(9000, dtype=bool)
+    mask[keep] = True
+    got = run_fwd_bwd(kd, p, mask=mask, want=False)
+    ref = check_against_oracle(p, got, mask=mask, chunk=1000)
+    hidden, W, ids, tl = to_device(p)
+    mk = torch.from_numpy(mask.astype(np.uint8)).cuda()
+    out = kd.kd_topk_kl_fwd(hidden, W, ids, tl, p.T, p.chunk, mk)
+    g = torch.ones(1, dtype=torch.float32, device="cuda")
+    base = torch.full((p.V, p.H), 0.5, dtype=torch.float32, device="cuda")
+    _, dW2 = kd.kd_topk_kl_bwd(hidden, W, ids, tl, out["lse"], g, p.T, p.chunk, mk,
+                               dW=base, accumulate_dW=True)
+    err = float(np.max(np.abs(dW2.cpu().numpy() - 0.5 - ref["dW"])))
+    assert err <= BF16_GRAD_FRAC * float(np.max(np.abs(ref["dW"])))
+
+
 def test_empty_problems(kd):
     # S = 0: loss 0, dW written as zeros
     W = torch.randn(300, 64, device="cuda").to(torch.bfloat16)
