@@ -112,7 +112,10 @@ struct Layout {
   size_t band, refined, scal, dscal, rpart, counters;
   size_t total;
   int64_t C;          // rows per backward chunk (<= S, >= 1)
-  int64_t Vp;         // padded row length of the gradient tile
+  int64_t Vp;         // vocabulary columns of the gradient tile: round_up(V, 8)
+  int64_t Vld;        // row pitch (elements) of G and W^T: an odd multiple of 128 bytes,
+                      // so that the 256 rows of an operand tile spread over all
+                      // 128-byte offsets modulo 4 KB (L2 channels)
   int64_t slot;       // token columns of one chunk in the transposed tiles: round_up(C, 8)
   int64_t nd;         // chunks per dW contraction (group)
   int64_t Cp;         // token columns of the transposed tiles: nd slots rounded to 32
@@ -129,6 +132,11 @@ Layout plan(const kd_problem* p) {
   L.esz = p->hw_dtype == KD_F32 ? 4 : 2;
   L.C = p->chunk < S ? p->chunk : (S > 0 ? S : 1);
   L.Vp = round_up(V, 8);
+  {
+    int64_t b = round_up(L.Vp * L.esz, 128);
+    if ((b / 128) % 2 == 0) b += 128;
+    L.Vld = b / L.esz;
+  }
   L.slot = round_up(L.C, 8);
   {
     // dW contracts about kDwDepth tokens per launch: its fp32 read-modify-write
@@ -161,9 +169,9 @@ Layout plan(const kd_problem* p) {
   L.ps = take(pe * 4);
   L.pd = take(pe * 4);
   L.bsum = take((ceil_div(Sx, 256) + 1) * 8);
-  L.G = take(L.C * L.Vp * L.esz);
+  L.G = take(L.C * L.Vld * L.esz);
   L.GT = take(L.Vp * L.Cld * L.esz);
-  L.WT = take(H * L.Vp * L.esz);
+  L.WT = take(H * L.Vld * L.esz);
   L.XcT = take(H * L.Cld * L.esz);
   int ksmax = 1;
   for (int64_t r = kd::kTile; r < L.C + kd::kTile; r += kd::kTile) {
@@ -341,7 +349,8 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
   const int Vp = (int)L.Vp;
   if (S > 0) {
     Prof pr("transpose_w", st);
-    KD_HIP(kd::launch_transpose_w(f32, (const char*)W, V, H, at<char>(ws, L.WT), Vp, st));
+    KD_HIP(kd::launch_transpose_w(f32, (const char*)W, V, H, at<char>(ws, L.WT), Vp, (int)L.Vld,
+                                  st));
   }
   for (int ci = 0; ci < nchunks; ++ci) {
     const int row_begin = ci * C;
@@ -375,7 +384,7 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
       a.lse = lse;
       a.grad_loss = grad_loss;
       a.G = at<char>(ws, L.G);
-      a.ldg = L.Vp * L.esz;
+      a.ldg = L.Vld * L.esz;
       a.GT = at<char>(ws, L.GT) + slot * L.slot * L.esz;
       a.ldgt = L.Cld * L.esz;
       Prof pr("bwd_grad_tile", st);
@@ -384,9 +393,9 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
     if (S > 0) {
       kd::DhArgs d;
       d.G = at<char>(ws, L.G);
-      d.ldg = L.Vp * L.esz;
+      d.ldg = L.Vld * L.esz;
       d.WT = at<char>(ws, L.WT);
-      d.ldwt = L.Vp * L.esz;
+      d.ldwt = L.Vld * L.esz;
       d.nrows_dev = at<int32_t>(ws, L.count);
       d.row_begin = row_begin;
       d.row_cap = C;

@@ -187,7 +187,7 @@ hipError_t launch_gather_rows_t(int f32, const char* X, int64_t ldx, const int32
 // WT[h][v] = W[v][h] for v < V, 0 for V <= v < Vp (64 x 64 tiles via LDS)
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_w_kernel(const T* W, int V, int H, T* WT,
-                                                          int Vp) {
+                                                          int Vp, int ldwt) {
   __shared__ T tile[64][65];
   const int v0 = blockIdx.x * 64, h0 = blockIdx.y * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -200,19 +200,19 @@ __global__ __launch_bounds__(256) void transpose_w_kernel(const T* W, int V, int
   __syncthreads();
   for (int hh = ty; hh < 64; hh += 4) {
     const int h = h0 + hh, v = v0 + tx;
-    if (h < H && v < Vp) WT[(int64_t)h * Vp + v] = tile[tx][hh];
+    if (h < H && v < Vp) WT[(int64_t)h * ldwt + v] = tile[tx][hh];
   }
 }
 
-hipError_t launch_transpose_w(int f32, const char* W, int V, int H, char* WT, int Vp,
+hipError_t launch_transpose_w(int f32, const char* W, int V, int H, char* WT, int Vp, int ldwt,
                               hipStream_t st) {
   dim3 grid((unsigned)ceil_div(Vp, 64), (unsigned)ceil_div(H, 64));
   if (f32)
     hipLaunchKernelGGL(transpose_w_kernel<float>, grid, dim3(256), 0, st, (const float*)W, V, H,
-                       (float*)WT, Vp);
+                       (float*)WT, Vp, ldwt);
   else
     hipLaunchKernelGGL(transpose_w_kernel<__bf16>, grid, dim3(256), 0, st, (const __bf16*)W, V,
-                       H, (__bf16*)WT, Vp);
+                       H, (__bf16*)WT, Vp, ldwt);
   return hipGetLastError();
 }
 
