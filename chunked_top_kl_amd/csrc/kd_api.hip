@@ -387,8 +387,26 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
       a.ldg = L.Vld * L.esz;
       a.GT = at<char>(ws, L.GT) + slot * L.slot * L.esz;
       a.ldgt = L.Cld * L.esz;
-      Prof pr("bwd_grad_tile", st);
-      KD_HIP(kd::launch_sweep(kd::kSweepBwdG, f32, 1, a, sgrid, st));
+      {
+        Prof pr("bwd_grad_tile", st);
+        KD_HIP(kd::launch_sweep(kd::kSweepBwdG, f32, 1, a, sgrid, st));
+      }
+      kd::GradTeacherArgs gt;
+      gt.G = a.G;
+      gt.ldg = a.ldg;
+      gt.GT = a.GT;
+      gt.ldgt = a.ldgt;
+      gt.idx = a.idx;
+      gt.nrows_dev = a.nrows_dev;
+      gt.row_begin = row_begin;
+      gt.row_cap = C;
+      gt.K = K;
+      gt.ids_s = a.ids_s;
+      gt.p_s = a.p_s;
+      gt.grad_loss = grad_loss;
+      gt.T = p->temperature;
+      Prof pr("bwd_grad_teacher", st);
+      KD_HIP(kd::launch_grad_teacher(f32, gt, st));
     }
     if (S > 0) {
       kd::DhArgs d;

@@ -78,6 +78,19 @@ struct DwArgs {
   float* dW;
 };
 
+// Teacher term of the gradient tile of one chunk (see kd_sweep.hip).
+struct GradTeacherArgs {
+  char* G; int64_t ldg;            // [rows][Vld]
+  char* GT; int64_t ldgt;          // [Vp][slots], this chunk's slot
+  const int32_t* idx;              // compacted row -> original row
+  const int32_t* nrows_dev;
+  int row_begin, row_cap, K;
+  const int32_t* ids_s;            // id-sorted teacher tables
+  const float* p_s;
+  const float* grad_loss;
+  float T;
+};
+
 // ------------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error.
 hipError_t launch_prepass(const int32_t* ids, const void* tl, int tl_f32, int64_t S, int K, int V,
@@ -86,6 +99,7 @@ hipError_t launch_prepass(const int32_t* ids, const void* tl, int tl_f32, int64_
 hipError_t launch_compact(const uint8_t* present, const uint8_t* mask, int64_t S, int32_t* idx,
                           int32_t* pos, int32_t* count, hipStream_t st);
 hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid, hipStream_t st);
+hipError_t launch_grad_teacher(int f32, const GradTeacherArgs& a, hipStream_t st);
 int sweep_grid(int64_t rows_max, int V, int ncu);
 hipError_t launch_fwd_combine(const CombineArgs& a, hipStream_t st);
 hipError_t launch_ent_combine(const EntCombineArgs& a, hipStream_t st);

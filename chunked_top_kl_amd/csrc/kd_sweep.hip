@@ -102,14 +102,9 @@ __device__ __forceinline__ float pick64(const float (&z)[64], int tgt) {
   return v;
 }
 
-// z[tgt] -= x (no change for tgt < 0).
-__device__ __forceinline__ void sub64(float (&z)[64], int tgt, float x) {
-#pragma unroll
-  for (int e = 0; e < 64; ++e) z[e] = (e == tgt) ? z[e] - x : z[e];
-}
-
 // ---------------------------------------------------------------------------
-// Gradient tile epilogue (bf16): G = coef * (2^(z*c - lse2) - p~) for the
+// Gradient tile epilogue (bf16): G = coef * 2^(z*c - lse2) (the teacher term
+// is applied afterwards by grad_teacher_kernel) for the
 // 256 x 256 tile, written to G [rows][Vp] and G^T [Vp][Cp] through LDS so
 // that both are stored as whole 16-byte granules along their rows.
 //
@@ -132,11 +127,9 @@ __device__ __forceinline__ int staged_token(int tp, int jp) {
   return (tp >> 6) * 128 + 64 * jp + (tp & 63);
 }
 
-template <class CursorArr>
 __device__ __forceinline__ void grad_tile_staged(floatx16 (&acc)[4][4], const SweepArgs& a, int vt,
                                                  int jt, int rows, int tl0, float c, float coef,
-                                                 const float (&lse2)[4], CursorArr& cu,
-                                                 char* lds) {
+                                                 const float (&lse2)[4], char* lds) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int half = lane >> 5;
   const int vw0 = vt * kTile + wm * 128;
@@ -176,7 +169,8 @@ __device__ __forceinline__ void grad_tile_staged(floatx16 (&acc)[4][4], const Sw
         char* gtb = sgt + (wm * 128 + 4 * half) * 256 +
                     ((((tp >> 3) ^ (half << 2)) << 4) + (tp & 7) * 2);
         char* gb = sg + tp * kGPitch + (wm * 128 + 4 * half) * 2;
-        // every value as if no teacher id hit it ...
+        // coef * q; the teacher term at the teacher ids is applied afterwards
+        // (grad_teacher_kernel)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -194,24 +188,6 @@ __device__ __forceinline__ void grad_tile_staged(floatx16 (&acc)[4][4], const Sw
             *(uint16_t*)(gtb + (dv + 3) * 256) = (uint16_t)(u23 >> 16);
             *(uint2*)(gb + dv * 2) = make_uint2(u01, u23);
           }
-        // ... then each hit overwrites its two staged entries with
-        // coef * (q - P), computed in fp32 and rounded once. Duplicate ids
-        // of a row are adjacent in the sorted table and reach the same
-        // register in consecutive rounds of this lane: P sums their p.
-        int prev = -1;
-        float psum = 0.0f;
-        walk_hits(cu[j], a.ids_s, a.K, vw0, half, [&](int tgt, int64_t e) {
-          const float val = pick64(z, tgt);
-          if (tgt >= 0) {
-            psum = (tgt == prev ? psum : 0.0f) + a.p_s[e];
-            prev = tgt;
-            const int dv = (tgt >> 4) * 32 + 8 * ((tgt >> 2) & 3) + (tgt & 3);
-            const bf16x2 g = {(__bf16)((val - psum) * cf), (__bf16)0.0f};
-            const uint16_t gv = (uint16_t)__builtin_bit_cast(uint32_t, g);
-            *(uint16_t*)(gtb + dv * 256) = gv;
-            *(uint16_t*)(gb + dv * 2) = gv;
-          }
-        });
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -264,12 +240,15 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
   const int ns = sweep_splits(ntt, nvt, a.ncu);
   const int total = ntt * ns;
   if ((int)blockIdx.x >= total) return;
-  // Grouped raster: consecutive logical ids (one XCD, one round) walk up to 8
-  // token tiles fastest, then vocabulary ranges, so the 32 work-groups an XCD
-  // runs at once share each W panel up to 8 ways and each token panel 4 ways,
-  // and a vocabulary range of W is read by as few XCDs as the grid allows.
+  // Raster. A launch of at most 8 token tiles (one chunk) walks its token
+  // tiles fastest, then vocabulary ranges: the 32 work-groups an XCD runs at
+  // once share each W panel up to 8 ways and each vocabulary range of W is
+  // read by as few XCDs as possible. A launch over many token tiles walks the
+  // vocabulary ranges fastest instead, so that an XCD holds few token panels
+  // at a time (8 of them, 11.8 MB at H = 2880, would not stay in its 4 MB L2
+  // and would be fetched again for every vocabulary tile).
   const int L = xcd_remap(blockIdx.x, total);
-  const int GM = ntt < 8 ? ntt : 8;
+  const int GM = ntt <= 8 ? ntt : 1;
   const int grp = L / (GM * ns), in = L % (GM * ns);
   const int gm = (ntt - grp * GM) < GM ? (ntt - grp * GM) : GM;
   const int jt = grp * GM + in % gm, b = in / gm;
@@ -305,7 +284,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
     S64[j] = 0.0;
     U64[j] = 0.0;
     lse2[j] = 0.0f;
-    if constexpr (KIND != kSweepEnt) {
+    if constexpr (KIND == kSweepFwd) {
       cu[j].base = (int64_t)orow[j] * a.K;
       if (tl0 + 32 * j < rows) {
         cu[j].cur = lower_bound_ids(a.ids_s + cu[j].base, a.K, vt_begin * kTile);
@@ -340,7 +319,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
 
     const int vw0 = vt * kTile + wm * 128;
     if constexpr (KIND == kSweepBwdG && sizeof(T) == 2) {
-      grad_tile_staged(acc, a, vt, jt, rows, tl0, c, coef, lse2, cu, lds);
+      grad_tile_staged(acc, a, vt, jt, rows, tl0, c, coef, lse2, lds);
       continue;
     }
     if (vw0 >= a.V) continue;  // wave-uniform: this half tile is past the vocabulary
@@ -424,11 +403,9 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
       }
 
       if constexpr (KIND == kSweepBwdG) {
+        // coef * q; the teacher term is applied by grad_teacher_kernel
 #pragma unroll
         for (int e = 0; e < 64; ++e) z[e] = fast_exp2(fmaf(z[e], c, -lse2[j]));
-        walk_hits(cu[j], a.ids_s, a.K, vw0, half, [&](int tgt, int64_t e) {
-          sub64(z, tgt, tgt >= 0 ? a.p_s[e] : 0.0f);
-        });
         // G [rows][Vp] feeds dHidden, G^T [Vp][Cp] feeds dW. Vocabulary
         // columns in [V, Vp) and token columns in [rows, round_up(rows, 8))
         // are written as zeros so that 16-byte granules read by the
@@ -581,6 +558,57 @@ hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid
     else KD_SWEEP(kd_entropy_sweep_f32);
   }
 #undef KD_SWEEP
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Teacher term of the gradient tile. The tile kernel stores coef * q for
+// every vocabulary entry; this kernel rewrites the entries at the teacher ids
+// of each chunk row as coef * q - coef * P, P the summed probability of a run
+// of equal ids in the sorted table (duplicates add), in both G and G^T. One
+// thread per (row, k); the first entry of a run does the update, so no two
+// threads touch one element. The stored value is read back, so the entry is
+// rounded to the storage type twice (once as coef * q); the second rounding
+// is of a value dominated by coef * P.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void grad_teacher_kernel(GradTeacherArgs a) {
+  int rows = a.row_cap;
+  {
+    const int n = *a.nrows_dev - a.row_begin;
+    rows = n < rows ? n : rows;
+  }
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int r = (int)(q / a.K), k = (int)(q % a.K);
+  if (rows <= 0 || r >= rows) return;
+  const int64_t base = (int64_t)a.idx[a.row_begin + r] * a.K;
+  const int id = a.ids_s[base + k];
+  if (id == 0x7FFFFFFF || (k > 0 && a.ids_s[base + k - 1] == id)) return;
+  float P = 0.0f;
+  for (int e = k; e < a.K && a.ids_s[base + e] == id; ++e) P += a.p_s[base + e];
+  const int n = *a.nrows_dev;
+  const float coef = (n > 0) ? a.grad_loss[0] / ((float)n * a.T) : 0.0f;
+  const float d = coef * P;
+  T* g = (T*)(a.G + (int64_t)r * a.ldg) + id;
+  T* gt = (T*)(a.GT + (int64_t)id * a.ldgt) + r;
+  if constexpr (sizeof(T) == 2) {
+    const float x = bf16_to_f32(*(const uint16_t*)g);
+    const bf16x2 y = {(__bf16)(x - d), (__bf16)0.0f};
+    const uint16_t b = (uint16_t)__builtin_bit_cast(uint32_t, y);
+    *(uint16_t*)g = b;
+    *(uint16_t*)gt = b;
+  } else {
+    const float y = *g - d;
+    *g = y;
+    *gt = y;
+  }
+}
+
+hipError_t launch_grad_teacher(int f32, const GradTeacherArgs& a, hipStream_t st) {
+  const int64_t grid = ceil_div((int64_t)a.row_cap * a.K, 256);
+  if (grid <= 0) return hipSuccess;
+  if (f32) hipLaunchKernelGGL(grad_teacher_kernel<float>, dim3((unsigned)grid), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(grad_teacher_kernel<__bf16>, dim3((unsigned)grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
