@@ -123,6 +123,7 @@ struct Layout {
                       // 256 rows of a dW operand tile do not share one offset
                       // modulo a large power of two (L2 channel conflicts)
   int64_t esz;
+  int ks;             // dHidden vocabulary splits
 };
 
 Layout plan(const kd_problem* p) {
@@ -173,13 +174,9 @@ Layout plan(const kd_problem* p) {
   L.GT = take(L.Vp * L.Cld * L.esz);
   L.WT = take(H * L.Vld * L.esz);
   L.XcT = take(H * L.Cld * L.esz);
-  int ksmax = 1;
-  for (int64_t r = kd::kTile; r < L.C + kd::kTile; r += kd::kTile) {
-    const int rows = (int)(r < L.C ? r : L.C);
-    const int ks = kd::dh_splits(rows, (int)V, (int)H, kCostCUs, p->hw_dtype == KD_F32);
-    if (ks > ksmax) ksmax = ks;
-  }
-  L.dhp = take((size_t)ksmax * L.C * H * 4);
+  // dHidden: vocabulary splits chosen for a full chunk, used for every chunk
+  L.ks = kd::dh_splits((int)L.C, (int)V, (int)H, kCostCUs, p->hw_dtype == KD_F32);
+  L.dhp = take((size_t)L.ks * kd::dh_split_stride((int)L.C, (int)H) * 4);
   L.em = take(pe * 4);
   L.es = take(pe * 8);
   L.eu = take(pe * 8);
@@ -420,12 +417,14 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
       d.V = V;
       d.H = H;
       d.ncu = kCostCUs;
+      d.ks = L.ks;
       d.part = at<float>(ws, L.dhp);
       {
         Prof pr("bwd_dhidden", st);
         KD_HIP(kd::launch_dh(f32, d, dgrid, st));
       }
       kd::DhReduceArgs r;
+      r.ks = L.ks;
       r.part = at<float>(ws, L.dhp);
       r.idx = at<int32_t>(ws, L.idx);
       r.nrows_dev = at<int32_t>(ws, L.count);
@@ -436,7 +435,7 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
       r.ncu = kCostCUs;
       r.dH = dhidden;
       Prof pr("bwd_dhidden_reduce", st);
-      KD_HIP(kd::launch_dh_reduce(r, f32, st));
+      KD_HIP(kd::launch_dh_reduce(r, st));
     }
     if (slot == L.nd - 1 || ci == nchunks - 1) {
       kd::DwArgs w;

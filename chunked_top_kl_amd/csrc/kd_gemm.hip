@@ -28,7 +28,7 @@ __device__ __forceinline__ void dh_body(DhArgs a) {
   constexpr int esz = Elem<T>::size;
   const int mt = (int)ceil_div(rows, kTile), nt = (int)ceil_div(a.H, kTile);
   const int nks_total = (int)ceil_div((int64_t)a.V * esz, kKB);
-  const int ks = splitk_factor(mt * nt, nks_total, a.ncu);
+  const int ks = a.ks;
   const int total = mt * nt * ks;
   if ((int)blockIdx.x >= total) return;
   const int L = xcd_remap(blockIdx.x, total);
@@ -48,7 +48,7 @@ __device__ __forceinline__ void dh_body(DhArgs a) {
   gemm_mainloop<T>(acc, la, lb, nk, lds);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
-  float* part = a.part + (int64_t)split * a.row_cap * a.H;
+  float* part = a.part + (int64_t)split * dh_split_stride(a.row_cap, a.H);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -70,14 +70,8 @@ __host__ __device__ int dh_splits(int rows, int V, int H, int ncu, int f32) {
 }
 
 int dh_grid(int row_cap, int V, int H, int ncu, int f32) {
-  int best = 1;
-  for (int r = kTile; r < row_cap + kTile; r += kTile) {
-    const int rows = r < row_cap ? r : row_cap;
-    const int mt = (int)ceil_div(rows, kTile), nt = (int)ceil_div(H, kTile);
-    const int g = mt * nt * dh_splits(rows, V, H, ncu, f32);
-    if (g > best) best = g;
-  }
-  return best;
+  const int mt = (int)ceil_div(row_cap, kTile), nt = (int)ceil_div(H, kTile);
+  return mt * nt * dh_splits(row_cap, V, H, ncu, f32);
 }
 
 extern "C" __global__ __launch_bounds__(256, 1) void kd_bwd_dhidden_bf16(DhArgs a) { dh_body<__bf16>(a); }
@@ -91,34 +85,48 @@ hipError_t launch_dh(int f32, const DhArgs& a, int grid, hipStream_t st) {
 }
 
 // dHidden[idx[row_begin + r]][h] = sum over splits (fixed order) of part[s][r][h]
-__global__ __launch_bounds__(256) void dh_reduce_kernel(DhReduceArgs a, int ks_f32) {
+__global__ __launch_bounds__(256) void dh_reduce_kernel(DhReduceArgs a) {
   const int rows = chunk_rows(a.nrows_dev, a.row_begin, a.row_cap);
-  if (rows <= 0) return;
-  const int ks = dh_splits(rows, a.V, a.H, a.ncu, ks_f32);
-  const int h4 = a.H / 4;
-  const int64_t total = (int64_t)rows * h4;
-  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total;
-       q += (int64_t)gridDim.x * 256) {
-    const int r = (int)(q / h4), c = (int)(q % h4);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < ks; ++s) {
-      const float4 v = *(const float4*)(a.part + ((int64_t)s * a.row_cap + r) * a.H + 4 * c);
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+  const int r = blockIdx.x;   // one work-group per compacted row of the chunk
+  if (r >= rows) return;
+  const int ks = a.ks;
+  const int64_t sstride = dh_split_stride(a.row_cap, a.H);
+  const float* src = a.part + (int64_t)r * a.H;
+  float* dst = a.dH + (int64_t)a.idx[a.row_begin + r] * a.H;
+  for (int c = threadIdx.x; c < a.H / 4; c += 256) {
+    // the first 8 partials are requested together (indices clamped, so the
+    // loads are unconditional) and added in split order: one memory round
+    // trip instead of one per split, and the same sum on every run
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = u < ks ? u : ks - 1;
+      v[u] = *(const float4*)(src + s * sstride + 4 * c);
     }
-    const int orow = a.idx[a.row_begin + r];
-    *(float4*)(a.dH + (int64_t)orow * a.H + 4 * c) = acc;
+    float4 acc = v[0];
+#pragma unroll
+    for (int u = 1; u < 8; ++u) {
+      if (u < ks) {
+        acc.x += v[u].x;
+        acc.y += v[u].y;
+        acc.z += v[u].z;
+        acc.w += v[u].w;
+      }
+    }
+    for (int s = 8; s < ks; ++s) {
+      const float4 w = *(const float4*)(src + s * sstride + 4 * c);
+      acc.x += w.x;
+      acc.y += w.y;
+      acc.z += w.z;
+      acc.w += w.w;
+    }
+    *(float4*)(dst + 4 * c) = acc;
   }
 }
 
-hipError_t launch_dh_reduce(const DhReduceArgs& a, int f32, hipStream_t st) {
-  const int64_t work = (int64_t)a.row_cap * (a.H / 4);
-  int grid = (int)ceil_div(work, 256);
-  if (grid > 4096) grid = 4096;
-  if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(dh_reduce_kernel, dim3(grid), dim3(256), 0, st, a, f32);
+hipError_t launch_dh_reduce(const DhReduceArgs& a, hipStream_t st) {
+  if (a.row_cap <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dh_reduce_kernel, dim3(a.row_cap), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

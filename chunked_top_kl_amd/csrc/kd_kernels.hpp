@@ -56,12 +56,21 @@ struct DhArgs {
   const char* WT; int64_t ldwt;       // W transposed [H, Vp]
   const int32_t* nrows_dev;
   int row_begin, row_cap, V, H, ncu;
+  int ks;                             // vocabulary splits (chosen for row_cap rows)
   float* part;                        // [split][row_cap][H] fp32
 };
 
+// Floats between the dHidden partials of consecutive splits: rows x H plus
+// 64 (256 bytes), so that the partials of one element, summed together by
+// the reduction, do not all sit at one offset modulo the HBM channel
+// interleave.
+__host__ __device__ inline int64_t dh_split_stride(int row_cap, int H) {
+  return (int64_t)row_cap * H + 64;
+}
+
 struct DhReduceArgs {
   const float* part; const int32_t* idx; const int32_t* nrows_dev;
-  int row_begin, row_cap, V, H, ncu;
+  int row_begin, row_cap, V, H, ncu, ks;
   float* dH;
 };
 
@@ -113,7 +122,7 @@ hipError_t launch_zero_invalid_rows(const int32_t* pos, int64_t S, int H, float*
 hipError_t launch_dh(int f32, const DhArgs& a, int grid, hipStream_t st);
 int dh_grid(int row_cap, int V, int H, int ncu, int f32);
 __host__ __device__ int dh_splits(int rows, int V, int H, int ncu, int f32);
-hipError_t launch_dh_reduce(const DhReduceArgs& a, int f32, hipStream_t st);
+hipError_t launch_dh_reduce(const DhReduceArgs& a, hipStream_t st);
 hipError_t launch_dw(int f32, const DwArgs& a, hipStream_t st);
 hipError_t launch_validate(const int32_t* ids, const void* tl, int tl_f32, int64_t S, int K,
                            int V, unsigned long long* counters, hipStream_t st);
