@@ -9,6 +9,7 @@ from .kd_oracle import (  # noqa: F401
     oracle_from_logits,
     oracle_loss_grads,
     oracle_rows,
+    oracle_dW_rows,
     oracle_entropy,
     oracle_entropy_rows,
     oracle_select_top_fraction,

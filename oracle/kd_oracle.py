@@ -52,6 +52,7 @@ __all__ = [
     "oracle_from_logits",
     "oracle_loss_grads",
     "oracle_rows",
+    "oracle_dW_rows",
     "oracle_entropy",
     "oracle_entropy_rows",
     "oracle_select_top_fraction",
@@ -193,19 +194,56 @@ def oracle_loss_grads(hidden, W, ids, tlogits, T=1.0, mask=None, grad_loss=1.0, 
     return dict(loss=loss, kl_rows=kl_all, lse=lse_all, dH=dH, dW=dW, N=N, valid=valid)
 
 
-def oracle_rows(hidden_rows, W, ids_rows, tl_rows, T, N, grad_loss=1.0):
+def oracle_rows(hidden_rows, W, ids_rows, tl_rows, T, N, grad_loss=1.0, grads=True):
     """Per-row outputs for a sample of rows, given the global valid count N.
 
     Every row of the loss depends only on its own hidden state and cache row,
     so kl_t, lse_t and dHidden_t of sampled rows follow the definition exactly.
-    Returns dict(kl_rows, lse, dH) for the given rows (all treated as valid).
+    Returns dict(kl_rows, lse, present, dH) for the given rows (all treated as
+    valid); grads=False skips dH.
     """
     Hd, Wd = _f64(hidden_rows), _f64(W)
     Z = Hd @ Wd.T
     kl, lse, soft, present = _row_terms(Z, ids_rows, tl_rows, T)
-    coef = float(grad_loss) / (float(T) * N) if N else 0.0
-    G = np.where(present[:, None], soft, 0.0) * coef
-    return dict(kl_rows=kl, lse=lse, dH=G @ Wd)
+    out = dict(kl_rows=kl, lse=lse, present=present)
+    if grads:
+        coef = float(grad_loss) / (float(T) * N) if N else 0.0
+        G = np.where(present[:, None], soft, 0.0) * coef
+        out["dH"] = G @ Wd
+    return out
+
+
+def oracle_dW_rows(hidden, W, ids, tlogits, T, lse, valid, vocab_rows, grad_loss=1.0):
+    """Rows `vocab_rows` of dW, given every row's student log-normaliser lse_t.
+
+    dW = dZ^T hidden with dZ[t, v] = g (softmax(z_t/T)_v - p_t,v) / (T N) on
+    valid rows [HF dense KL, differentiated]; column v of dZ needs only z[:, v]
+    (one projection per sampled vocabulary row) and lse. p_t,v is the
+    renormalised top-K teacher probability: the sum over the row's cached
+    entries with id v of exp(l_k/T - logsumexp_k(l_k/T)) (-inf entries give 0).
+    """
+    Hd = _f64(hidden)
+    vocab_rows = np.asarray(vocab_rows)
+    ids = np.asarray(ids)
+    valid = np.asarray(valid, dtype=bool)
+    N = int(valid.sum())
+    if N == 0:
+        return np.zeros((len(vocab_rows), Hd.shape[1]))
+    Zc = Hd @ _f64(W)[vocab_rows].T                              # z[:, v] for the sampled v
+    lse = _f64(lse)
+    with np.errstate(invalid="ignore", over="ignore"):
+        Q = np.exp(Zc / float(T) - np.where(valid, lse, 0.0)[:, None])
+    scaled = _f64(tlogits) / float(T)
+    lt = _logsumexp_rows(scaled)                                 # teacher log-normaliser per row
+    Pc = np.zeros_like(Q)
+    for k in range(ids.shape[1]):
+        with np.errstate(invalid="ignore"):
+            pk = np.where(np.isfinite(lt), np.exp(scaled[:, k] - np.where(np.isfinite(lt), lt, 0.0)), 0.0)
+        hit = ids[:, k][:, None] == vocab_rows[None, :]
+        Pc += np.where(hit, pk[:, None], 0.0)
+    coef = float(grad_loss) / (float(T) * N)
+    G = np.where(valid[:, None], Q - Pc, 0.0) * coef
+    return G.T @ Hd
 
 
 def oracle_entropy_rows(Z):

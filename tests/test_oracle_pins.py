@@ -10,7 +10,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle import (oracle_entropy, oracle_entropy_rows, oracle_from_logits,
+from oracle import (oracle_dW_rows, oracle_entropy, oracle_entropy_rows, oracle_from_logits,
                     oracle_loss_grads, oracle_rows, oracle_select_top_fraction,
                     oracle_validate_topk, oracle_entropy_select_kl)
 
@@ -355,3 +355,39 @@ def test_validate_counts():
     ids = np.array([[0, 5, 9], [10, -1, 3], [2, 2, 2]])
     tl = np.array([[1.0, 2.0, 3.0], [-np.inf, -np.inf, -np.inf], [np.nan, np.inf, 0.0]])
     assert oracle_validate_topk(ids, tl, 10) == (2, 1, 2)
+
+
+@pytest.mark.parametrize("T", [1.0, 2.0])
+def test_dW_rows_match_dense_definition(T):
+    # dW at sampled vocabulary rows, from every row's lse, equals the rows of
+    # the dense oracle's dW; with a mask, duplicate ids, -inf teacher entries
+    # and an all -inf (missing) row
+    rng = np.random.default_rng(31)
+    S, H, V, K = 9, 5, 13, 4
+    hidden = rng.standard_normal((S, H))
+    W = rng.standard_normal((V, H)) / np.sqrt(H)
+    ids = np.stack([rng.choice(V, K, replace=False) for _ in range(S)])
+    ids[2, 1] = ids[2, 0]                       # duplicate id
+    tl = np.sort(rng.standard_normal((S, K)), axis=1)[:, ::-1].copy()
+    tl[4, 3] = -np.inf                          # one -inf entry
+    tl[6, :] = -np.inf                          # a missing row
+    mask = np.ones(S, dtype=bool)
+    mask[1] = False
+    ref = oracle_loss_grads(hidden, W, ids, tl, T=T, mask=mask, grad_loss=0.7)
+    vocab_rows = np.array([0, 3, int(ids[2, 0]), 12])
+    got = oracle_dW_rows(hidden, W, ids, tl, T, ref["lse"], ref["valid"], vocab_rows, grad_loss=0.7)
+    assert np.allclose(got, ref["dW"][vocab_rows], rtol=1e-12, atol=1e-14)
+
+
+def test_rows_forward_only_matches():
+    rng = np.random.default_rng(32)
+    S, H, V, K = 6, 4, 11, 3
+    hidden = rng.standard_normal((S, H))
+    W = rng.standard_normal((V, H))
+    ids = np.stack([rng.choice(V, K, replace=False) for _ in range(S)])
+    tl = rng.standard_normal((S, K))
+    ref = oracle_loss_grads(hidden, W, ids, tl, T=1.5)
+    got = oracle_rows(hidden, W, ids, tl, 1.5, S, grads=False)
+    assert "dH" not in got
+    assert np.allclose(got["kl_rows"], ref["kl_rows"], rtol=1e-12, atol=1e-14)
+    assert np.allclose(got["lse"], ref["lse"], rtol=1e-12, atol=1e-14)
