@@ -27,9 +27,11 @@ using kd::round_up;
 constexpr int kCostCUs = 256;
 constexpr int64_t kMaxK = 4096;
 constexpr int64_t kMaxRows = int64_t(1) << 30;
-constexpr double kSelectEps = 2e-5;
-constexpr int64_t kDwDepth = 8192;     // tokens per dW contraction (a multiple of chunks)   // bound on |fp32-path entropy - fp64 entropy| (nats)
-constexpr int kRefineBlocks = 512;
+constexpr double kSelectEps = 2e-5;    // bound on |fp32-path entropy - fp64 entropy| (nats)
+constexpr int64_t kDwDepth = 8192;     // tokens per dW contraction (a multiple of chunks)
+constexpr int kRefineBatch = 256;      // band rows widened to fp64 per refinement launch
+// refinement work-groups: one vocabulary row per thread, 256 per group
+inline int64_t refine_blocks(int64_t V) { return ceil_div(V, 256); }
 
 // ------------------------------------------------------------------ profiling
 struct ProfRec {
@@ -109,7 +111,7 @@ struct Layout {
   size_t pm, ps, pd, bsum;
   size_t G, GT, WT, XcT, dhp;
   size_t em, es, eu;
-  size_t band, refined, scal, dscal, rpart, counters;
+  size_t band, refined, scal, dscal, rpart, xb, counters;
   size_t total;
   int64_t C;          // rows per backward chunk (<= S, >= 1)
   int64_t Vp;         // vocabulary columns of the gradient tile: round_up(V, 8)
@@ -184,7 +186,8 @@ Layout plan(const kd_problem* p) {
   L.refined = take(Sx * 8);
   L.scal = take(16 * 4);
   L.dscal = take(16 * 8);
-  L.rpart = take((size_t)4096 * kRefineBlocks * 3 * 8);
+  L.rpart = take((size_t)4096 * refine_blocks(V) * 3 * 8);
+  L.xb = take((size_t)kRefineBatch * H * 8);
   L.counters = take(4 * 8);
   L.total = off;
   return L;
@@ -539,13 +542,12 @@ int kd_select_top_fraction(const kd_problem* p, const void* hidden, const void* 
   const int f32 = p->hw_dtype == KD_F32;
   const int64_t ld = p->H * L.esz;
   if (n_band > 0 && n_band <= 4096) {
-    const int R = kd::refine_rows_per_pass((int)p->H, f32);
-    const int nblk = (int)std::min<int64_t>(kRefineBlocks, ceil_div(p->V, 64));
-    for (int off = 0; off < n_band; off += R) {
-      const int n = std::min(R, n_band - off);
+    const int nblk = refine_blocks(p->V);
+    for (int off = 0; off < n_band; off += kRefineBatch) {
+      const int n = std::min(kRefineBatch, n_band - off);
       Prof pr("select_refine_fp64", st);
       KD_HIP(kd::launch_refine(f32, (const char*)hidden, ld, (const char*)W, ld, (int)p->V,
-                               (int)p->H, w, off, n, nblk, st));
+                               (int)p->H, w, at<double>(ws, L.xb), off, n, nblk, st));
     }
     {
       Prof pr("select_final", st);

@@ -141,9 +141,8 @@ struct SelectWs {
 hipError_t launch_select_threshold(const double* entropy, int64_t S, int64_t k, double eps,
                                    const SelectWs& w, hipStream_t st);
 hipError_t launch_refine(int f32, const char* X, int64_t ldx, const char* W, int64_t ldw, int V,
-                         int H, const SelectWs& w, int band_off, int band_n, int nblk,
+                         int H, const SelectWs& w, double* xb, int band_off, int band_n, int nblk,
                          hipStream_t st);
-int refine_rows_per_pass(int H, int f32);
 hipError_t launch_select_final(const double* entropy, int64_t S, int64_t k, const SelectWs& w,
                                int n_band, int nblk, uint8_t* mask, int32_t* idx_out,
                                hipStream_t st);

@@ -8,6 +8,8 @@
 // the band in between is recomputed in fp64 from hidden and W and ranked by
 // (entropy descending, position ascending). The kept set is then the one an
 // fp64 evaluation of the entropies decides.
+#include <algorithm>
+
 #include "kd_common.hpp"
 #include "kd_kernels.hpp"
 
@@ -109,130 +111,217 @@ hipError_t launch_select_threshold(const double* entropy, int64_t S, int64_t k, 
 // (m, s = sum e^(z-m), u = sum e^(z-m)(z-m)) over a vocabulary block.
 // Partials rpart[row][blk] = (m, s, u).
 // ---------------------------------------------------------------------------
-constexpr int kRefineRows = 16;
-constexpr int kRefineLdsBytes = 96 * 1024;
 
-int refine_rows_per_pass(int H, int /*f32*/) {
-  int r = kRefineLdsBytes / (H * 4);
-  if (r > kRefineRows) r = kRefineRows;
-  if (r < 1) r = 1;
-  return r;
+// The band rows' hidden states widened to fp64 once: xb[r][h], r < n.
+template <typename T>
+__global__ __launch_bounds__(256) void band_rows_f64_kernel(const char* X, int64_t ldx, int H,
+                                                            const int32_t* band, int off, int n,
+                                                            double* xb) {
+  const int64_t total = (int64_t)n * H;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * 256) {
+    const int r = (int)(q / H), h = (int)(q % H);
+    const char* src = X + (int64_t)band[off + r] * ldx;
+    xb[q] = (sizeof(T) == 2) ? (double)bf16_to_f32(((const uint16_t*)src)[h])
+                             : (double)((const float*)src)[h];
+  }
 }
 
-template <typename T, int R>
-__global__ __launch_bounds__(256) void refine_kernel(const char* X, int64_t ldx, const char* Wm,
+// fp64 entropy partials of the band rows: z = x . w in fp64 from the exactly
+// widened inputs, then the online (m, s, u) of each band row over the
+// vocabulary rows of one tile. A work-group takes 8 band rows and a tile of
+// 256 vocabulary rows; each lane holds 8 vocabulary rows x 8 band rows of
+// sums. The 8 lanes that share a vocabulary row each take one 16-byte granule
+// of h per step, so a load instruction reads 8 whole 128-byte lines. The band
+// rows' values pass through LDS in pieces of kRefHc h, laid out [h][8 rows]
+// with 16 bytes of padding after every 8 h so the 8 granules of a step fall
+// in different banks; h past the end of a piece is zero there. Band rows past
+// the end repeat the last one so every FMA is unconditional; their results
+// are not written.
+constexpr int kRefTR = 8;        // band rows per work-group
+constexpr int kRefTV = 8;        // vocabulary rows per lane
+constexpr int kRefTile = 256;    // vocabulary rows per work-group
+constexpr int kRefHc = 1024;     // h per LDS piece
+constexpr int kRefLdsDoubles = kRefHc * kRefTR + (kRefHc / 8) * 2;
+
+__device__ __forceinline__ int ref_xs(int h, int r) { return h * kRefTR + (h >> 3) * 2 + r; }
+
+// (m, s, u) of a set of logits: m the max, s = sum e^(z-m), u = sum e^(z-m)(z-m)
+__device__ __forceinline__ void msu_merge(double& m1, double& s1, double& u1, double m2, double s2,
+                                          double u2) {
+  if (m2 == -INFINITY) return;
+  if (m1 == -INFINITY) {
+    m1 = m2;
+    s1 = s2;
+    u1 = u2;
+    return;
+  }
+  const double mn = fmax(m1, m2), f1 = exp(m1 - mn), f2 = exp(m2 - mn);
+  u1 = (u1 + s1 * (m1 - mn)) * f1 + (u2 + s2 * (m2 - mn)) * f2;
+  s1 = s1 * f1 + s2 * f2;
+  m1 = mn;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void refine_kernel(const double* __restrict__ xb, const char* Wm,
                                                      int64_t ldw, int V, int H, SelectWs w,
-                                                     int band_off, int band_n, int nblk) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  float* xs = (float*)smem;                       // [R][H]
-  __shared__ double red[3][256];
-  const int tid = threadIdx.x;
-  const int nr = band_n < R ? band_n : R;
-  for (int q = tid; q < nr * H; q += 256) {
-    const int r = q / H, h = q % H;
-    const int64_t row = w.band[band_off + r];
-    const char* src = X + row * ldx;
-    xs[q] = (sizeof(T) == 2) ? bf16_to_f32(((const uint16_t*)src)[h]) : ((const float*)src)[h];
-  }
-  __syncthreads();
-  const int vper = (int)ceil_div(V, nblk);
-  const int v0 = blockIdx.x * vper;
-  const int v1 = (v0 + vper < V) ? v0 + vper : V;
-  double m[R], s[R], u[R];
+                                                     int band_off, int n, int nblk) {
+  __shared__ __attribute__((aligned(16))) double xs[kRefLdsDoubles];
+  __shared__ double red[3][4][kRefTR];
+  // work-group order: the band groups of one vocabulary tile are consecutive
+  // on one XCD (work-groups are dealt to the 8 XCDs in turn), so the tile's
+  // W rows are fetched from HBM about once
+  const int ng = (n + kRefTR - 1) / kRefTR;
+  const int total = ng * nblk;
+  const int per_xcd = (total + 7) / 8;
+  const int logical = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (logical >= total) return;
+  const int grp = logical % ng, vt = logical / ng;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = lane & 7, a = lane >> 3;
+  const int r0 = grp * kRefTR;
+  const int nr = (n - r0) < kRefTR ? (n - r0) : kRefTR;
+  const int vbase = vt * kRefTile + wave * 64 + a * kRefTV;
+  int64_t roff[kRefTV];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    m[r] = -INFINITY;
-    s[r] = 0.0;
-    u[r] = 0.0;
-  }
-  for (int v = v0 + tid; v < v1; v += 256) {
-    double acc[R];
+  for (int j = 0; j < kRefTV; ++j) roff[j] = (int64_t)((vbase + j) < V ? vbase + j : V - 1) * ldw;
+  constexpr int per = 16 / (int)sizeof(T);
+  constexpr int step = 8 * per;
+  double acc[kRefTV][kRefTR];
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.0;
-    const char* wr = Wm + (int64_t)v * ldw;
-    constexpr int per = 16 / (int)sizeof(T);
-    for (int h = 0; h < H; h += per) {
-      const uint4 raw = *(const uint4*)(wr + (int64_t)h * sizeof(T));
-      const uint32_t* wd = (const uint32_t*)&raw;
+  for (int j = 0; j < kRefTV; ++j)
+#pragma unroll
+    for (int r = 0; r < kRefTR; ++r) acc[j][r] = 0.0;
+  for (int hc = 0; hc < H; hc += kRefHc) {
+    const int hn = (H - hc) < kRefHc ? (H - hc) : kRefHc;
+    const int hp = (hn + step - 1) / step * step;
+    __syncthreads();
+    for (int q = tid; q < kRefTR * hp; q += 256) {
+      const int r = q / hp, h = q % hp;
+      const int rr = r < nr ? r : nr - 1;
+      xs[ref_xs(h, r)] = h < hn ? xb[(int64_t)(r0 + rr) * H + hc + h] : 0.0;
+    }
+    __syncthreads();
+    // W granules are loaded one step ahead; a granule past the end of the
+    // row reads the row's first granule, and the band values it meets in LDS
+    // are zero
+    uint4 raw[kRefTV], nxt[kRefTV];
+    {
+      const int64_t ho = (int64_t)(b * per < hn ? hc + b * per : 0) * (int64_t)sizeof(T);
+#pragma unroll
+      for (int j = 0; j < kRefTV; ++j) raw[j] = *(const uint4*)(Wm + roff[j] + ho);
+    }
+    for (int hs = 0; hs < hp; hs += step) {
+      const int h0 = hs + b * per;
+      {
+        const int hq = h0 + step;
+        const int64_t ho = (int64_t)(hq < hn ? hc + hq : 0) * (int64_t)sizeof(T);
+#pragma unroll
+        for (int j = 0; j < kRefTV; ++j) nxt[j] = *(const uint4*)(Wm + roff[j] + ho);
+        __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of this step's FMAs
+      }
 #pragma unroll
       for (int e = 0; e < per; ++e) {
-        double wv;
-        if constexpr (sizeof(T) == 2) wv = (double)bf16_to_f32((uint16_t)(wd[e >> 1] >> ((e & 1) * 16)));
-        else wv = (double)__uint_as_float(wd[e]);
+        const double2* xp = (const double2*)(xs + ref_xs(h0 + e, 0));
+        double xv[kRefTR];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-          if (r < nr) acc[r] = fma((double)xs[r * H + h + e], wv, acc[r]);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (r >= nr) continue;
-      const double z = acc[r];
-      if (z > m[r]) {
-        if (m[r] == -INFINITY) {
-          s[r] = 0.0;
-          u[r] = 0.0;
-        } else {
-          const double f = exp(m[r] - z);
-          u[r] = (u[r] + s[r] * (m[r] - z)) * f;
-          s[r] = s[r] * f;
+        for (int r = 0; r < kRefTR / 2; ++r) {
+          const double2 t = xp[r];
+          xv[2 * r] = t.x;
+          xv[2 * r + 1] = t.y;
         }
-        m[r] = z;
+#pragma unroll
+        for (int j = 0; j < kRefTV; ++j) {
+          const uint32_t* wd = (const uint32_t*)&raw[j];
+          double wv;
+          if constexpr (sizeof(T) == 2) wv = (double)bf16_to_f32((uint16_t)(wd[e >> 1] >> ((e & 1) * 16)));
+          else wv = (double)__uint_as_float(wd[e]);
+#pragma unroll
+          for (int r = 0; r < kRefTR; ++r) acc[j][r] = fma(xv[r], wv, acc[j][r]);
+        }
       }
-      const double d = z - m[r];
-      const double e = exp(d);
-      s[r] += e;
-      u[r] += e * d;
+#pragma unroll
+      for (int j = 0; j < kRefTV; ++j) raw[j] = nxt[j];
     }
   }
-  // block merge per row (fixed tree order)
+  // sum over the 8 granule lanes, leaving band row b's sums on lane b:
+  // halve the band rows held at each of the three exchange steps
+  double t4[kRefTV][4], t2[kRefTV][2], z[kRefTV];
+  const bool u4 = (b & 4) != 0, u2 = (b & 2) != 0, u1 = (b & 1) != 0;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (r >= nr) continue;  // uniform
-    red[0][tid] = m[r];
-    red[1][tid] = s[r];
-    red[2][tid] = u[r];
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-      if (tid < o) {
-        double m1 = red[0][tid], s1 = red[1][tid], u1 = red[2][tid];
-        const double m2 = red[0][tid + o], s2 = red[1][tid + o], u2 = red[2][tid + o];
-        if (m2 != -INFINITY) {
-          if (m1 == -INFINITY) {
-            m1 = m2; s1 = s2; u1 = u2;
-          } else {
-            const double mn = fmax(m1, m2), f1 = exp(m1 - mn), f2 = exp(m2 - mn);
-            u1 = (u1 + s1 * (m1 - mn)) * f1 + (u2 + s2 * (m2 - mn)) * f2;
-            s1 = s1 * f1 + s2 * f2;
-            m1 = mn;
-          }
-        }
-        red[0][tid] = m1;
-        red[1][tid] = s1;
-        red[2][tid] = u1;
+  for (int j = 0; j < kRefTV; ++j) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const double keep = u4 ? acc[j][r + 4] : acc[j][r];
+      const double send = u4 ? acc[j][r] : acc[j][r + 4];
+      t4[j][r] = keep + __shfl_xor(send, 4);
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const double keep = u2 ? t4[j][r + 2] : t4[j][r];
+      const double send = u2 ? t4[j][r] : t4[j][r + 2];
+      t2[j][r] = keep + __shfl_xor(send, 2);
+    }
+    const double keep = u1 ? t2[j][1] : t2[j][0];
+    const double send = u1 ? t2[j][0] : t2[j][1];
+    z[j] = keep + __shfl_xor(send, 1);
+  }
+  // (m, s, u) of band row b over this lane's 8 vocabulary rows
+  double m = -INFINITY, sum = 0.0, uu = 0.0;
+#pragma unroll
+  for (int j = 0; j < kRefTV; ++j)
+    if (vbase + j < V) m = fmax(m, z[j]);
+  if (m != -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < kRefTV; ++j) {
+      if (vbase + j < V) {
+        const double d = z[j] - m, e = exp(d);
+        sum += e;
+        uu += e * d;
       }
-      __syncthreads();
     }
-    if (tid == 0) {
-      double* o = w.rpart + ((int64_t)(band_off + r) * nblk + blockIdx.x) * 3;
-      o[0] = red[0][0];
-      o[1] = red[1][0];
-      o[2] = red[2][0];
-    }
-    __syncthreads();
+  }
+  // over the 8 lanes of the wave that hold the same band row, then the waves
+#pragma unroll
+  for (int o = 8; o < 64; o <<= 1) {
+    const double m2 = __shfl_xor(m, o), s2 = __shfl_xor(sum, o), v2 = __shfl_xor(uu, o);
+    msu_merge(m, sum, uu, m2, s2, v2);
+  }
+  if (a == 0) {
+    red[0][wave][b] = m;
+    red[1][wave][b] = sum;
+    red[2][wave][b] = uu;
+  }
+  __syncthreads();
+  if (tid < kRefTR && tid < nr) {
+    double M = red[0][0][tid], Ssum = red[1][0][tid], U = red[2][0][tid];
+    for (int q = 1; q < 4; ++q) msu_merge(M, Ssum, U, red[0][q][tid], red[1][q][tid], red[2][q][tid]);
+    double* o = w.rpart + ((int64_t)(band_off + r0 + tid) * nblk + vt) * 3;
+    o[0] = M;
+    o[1] = Ssum;
+    o[2] = U;
   }
 }
 
 hipError_t launch_refine(int f32, const char* X, int64_t ldx, const char* W, int64_t ldw, int V,
-                         int H, const SelectWs& w, int band_off, int band_n, int nblk,
+                         int H, const SelectWs& w, double* xb, int band_off, int band_n, int nblk,
                          hipStream_t st) {
-  const size_t lds = (size_t)refine_rows_per_pass(H, f32) * H * 4;
-  if (f32)
-    hipLaunchKernelGGL((refine_kernel<float, kRefineRows>), dim3(nblk), dim3(256), lds, st, X, ldx,
-                       W, ldw, V, H, w, band_off, band_n, nblk);
-  else
-    hipLaunchKernelGGL((refine_kernel<__bf16, kRefineRows>), dim3(nblk), dim3(256), lds, st, X,
-                       ldx, W, ldw, V, H, w, band_off, band_n, nblk);
+  if (band_n <= 0) return hipSuccess;
+  const int64_t widen = ceil_div((int64_t)band_n * H, 256);
+  const int64_t nwg = ceil_div((int64_t)ceil_div(band_n, kRefTR) * nblk, 8) * 8;
+  if (nwg > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)nwg);
+  if (f32) {
+    hipLaunchKernelGGL(band_rows_f64_kernel<float>, dim3((unsigned)std::min<int64_t>(widen, 4096)),
+                       dim3(256), 0, st, X, ldx, H, w.band, band_off, band_n, xb);
+    hipLaunchKernelGGL(refine_kernel<float>, grid, dim3(256), 0, st, xb, W, ldw, V, H, w,
+                       band_off, band_n, nblk);
+  } else {
+    hipLaunchKernelGGL(band_rows_f64_kernel<__bf16>, dim3((unsigned)std::min<int64_t>(widen, 4096)),
+                       dim3(256), 0, st, X, ldx, H, w.band, band_off, band_n, xb);
+    hipLaunchKernelGGL(refine_kernel<__bf16>, grid, dim3(256), 0, st, xb, W, ldw, V, H, w,
+                       band_off, band_n, nblk);
+  }
   return hipGetLastError();
 }
 

@@ -287,6 +287,23 @@ def test_selection_index_set_bit_exact(kd, case):
     assert np.array_equal(mask.cpu().numpy(), rmask)
 
 
+@pytest.mark.parametrize("H,hw", [(200, "bf16"), (1096, "bf16"), (200, "f32")])
+def test_selection_ragged_hidden(kd, H, hw):
+    # hidden widths that leave a partial step (not a multiple of 64) and a
+    # second, ragged piece of the band rows (above 1024), and fp32 inputs;
+    # a crowded entropy distribution so that the fp64 refinement decides
+    S, V = 1200, 2999
+    p = make_problem(S, H, V, 4, seed=17, hidden_std=0.05, hw_dtype=hw, tl_dtype="f32")
+    hidden, W, _, _ = to_device(p)
+    ent = kd.kd_student_entropy(hidden, W)
+    mask, idx, cnt = kd.kd_select_top_fraction(ent, hidden, W, 20, 100)
+    ref_e = oracle_entropy(p.hidden, p.W, chunk=400)
+    rmask, ridx, rk = oracle_select_top_fraction(ref_e, 20, 100)
+    assert cnt == rk
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.array_equal(mask.cpu().numpy(), rmask)
+
+
 def test_entropy_selective_variant_reduced(kd):
     # entropy-selective config shapes (H=2048, V=151936) at S=2048: entropy over all
     # positions, top 20% kept, then the KL forward and backward on the kept rows only
