@@ -117,6 +117,34 @@ def cpu_baseline(p, wl, rows):
                        f"dHidden and the dW contribution of those rows, row blocks of 128; {dt:.1f} s")
 
 
+def chunk_sweep(kd, torch, wl, t, chunks, steps=3, warmup=1):
+    """fwd+bwd time and peak device memory of the workload at several chunk sizes."""
+    S, H, V, K = wl["S"], wl["H"], wl["V"], wl["K"]
+    hidden, W, ids, tl = t
+    out = {}
+    for C in chunks:
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        prob = kd.make_problem(S, H, V, K, C, wl["T"], kd.KD_BF16, kd.KD_BF16)
+        ws = torch.empty(kd.kd_topk_kl_workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+        wlc = dict(wl, chunk=C)
+        for _ in range(warmup):
+            run_step(kd, torch, wlc, t, ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            run_step(kd, torch, wlc, t, ws)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1000.0 / steps
+        out[str(C)] = dict(ms_per_step=round(ms, 3), tokens_per_s=round(S / (ms / 1000.0), 1),
+                           peak_gib=round(torch.cuda.max_memory_allocated() / 2**30, 3),
+                           workspace_gib=round(ws.numel() / 2**30, 3))
+        log(f"[bench] chunk {C}: {ms:.2f} ms/step, peak {out[str(C)]['peak_gib']} GiB")
+        del ws
+    return out
+
+
 def mem_sweep(kd, torch, sizes, seed=1004):
     """Peak device memory of one fwd+bwd at the 256K-context shapes for several S."""
     from kd_synth import make_problem
@@ -165,6 +193,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mem-sweep", action="store_true")
     ap.add_argument("--mem-sizes", default="16384,32768,65536,131072,262144")
+    ap.add_argument("--no-chunk-sweep", action="store_true",
+                    help="skip the fwd+bwd timing and peak memory at chunks 512/1024/2048")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -282,9 +312,13 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    del ws
+    torch.cuda.empty_cache()
+    if not args.no_chunk_sweep and args.workload == "c3":
+        result["chunk_sweep"] = chunk_sweep(kd, torch, wl, t, [512, 1024, 2048])
     if not args.no_mem_sweep:
         sizes = [int(x) for x in args.mem_sizes.split(",") if x]
-        del t, ws
+        del t
         torch.cuda.empty_cache()
         result["peak_gib_vs_S"] = mem_sweep(kd, torch, sizes)
     if not args.no_cpu_baseline:
