@@ -108,7 +108,7 @@ int check_problem(const kd_problem* p) {
 // ------------------------------------------------------------------ workspace plan
 struct Layout {
   size_t count, present, pos, idx, ids_s, p_s, korig_s, negH;
-  size_t pm, ps, pd, bsum;
+  size_t pm, ps, zs, bsum;
   size_t G, GT, WT, XcT, dhp;
   size_t em, es, eu;
   size_t band, refined, scal, dscal, rpart, xb, counters;
@@ -170,7 +170,7 @@ Layout plan(const kd_problem* p) {
   const int64_t pe = (int64_t)kd::sweep_grid(Sx, (int)V, kCostCUs) * kd::kTile;
   L.pm = take(pe * 4);
   L.ps = take(pe * 4);
-  L.pd = take(pe * 4);
+  L.zs = take(Sx * K * 4);
   L.bsum = take((ceil_div(Sx, 256) + 1) * 8);
   L.G = take(L.C * L.Vld * L.esz);
   L.GT = take(L.Vp * L.Cld * L.esz);
@@ -290,8 +290,7 @@ int kd_topk_kl_fwd(const kd_problem* p, const void* hidden, const void* W, const
     a.korig_s = at<int32_t>(ws, L.korig_s);
     a.pm = at<float>(ws, L.pm);
     a.ps = at<float>(ws, L.ps);
-    a.pd = at<float>(ws, L.pd);
-    a.z_topk = z_topk;
+    a.zs = at<float>(ws, L.zs);
     Prof pr("fwd_lse_gather", st);
     KD_HIP(kd::launch_sweep(kd::kSweepFwd, f32, map, a, kd::sweep_grid(S, V, kCostCUs), st));
   }
@@ -307,7 +306,10 @@ int kd_topk_kl_fwd(const kd_problem* p, const void* hidden, const void* W, const
   c.nrows_dev = at<int32_t>(ws, L.count);
   c.pm = at<float>(ws, L.pm);
   c.ps = at<float>(ws, L.ps);
-  c.pd = at<float>(ws, L.pd);
+  c.ids_s = at<int32_t>(ws, L.ids_s);
+  c.p_s = at<float>(ws, L.p_s);
+  c.korig_s = at<int32_t>(ws, L.korig_s);
+  c.zs = at<float>(ws, L.zs);
   c.negH = at<float>(ws, L.negH);
   c.lse = lse;
   c.kl_rows = kl_rows;

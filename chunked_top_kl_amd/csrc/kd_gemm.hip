@@ -9,6 +9,16 @@
 
 namespace kd {
 
+// operand with the third stage buffer (longer load lead): A (true) or B
+#ifndef KD_DH_A_EARLY
+#define KD_DH_A_EARLY 1
+#endif
+#ifndef KD_DW_A_EARLY
+#define KD_DW_A_EARLY 1
+#endif
+constexpr bool kDhAEarly = KD_DH_A_EARLY;
+constexpr bool kDwAEarly = KD_DW_A_EARLY;
+
 // rows of this chunk actually present (device count N)
 __device__ inline int chunk_rows(const int32_t* nrows_dev, int row_begin, int row_cap) {
   int n = *nrows_dev - row_begin;
@@ -41,11 +51,11 @@ __device__ __forceinline__ void dh_body(DhArgs a) {
 
   DmaOperand la, lb;
   la.init(a.G + (int64_t)m * kTile * a.ldg, a.ldg, rows - m * kTile, (int64_t)kbeg * kKB,
-          (int64_t)a.V * esz, 0);
+          (int64_t)a.V * esz);
   lb.init(a.WT + (int64_t)n * kTile * a.ldwt, a.ldwt, a.H - n * kTile, (int64_t)kbeg * kKB,
-          (int64_t)a.V * esz, 1);
+          (int64_t)a.V * esz);
   floatx16 acc[4][4];
-  gemm_mainloop<T>(acc, la, lb, nk, lds);
+  gemm_mainloop<T, kDhAEarly>(acc, la, lb, nk, lds);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
   float* part = a.part + (int64_t)split * dh_split_stride(a.row_cap, a.H);
@@ -256,10 +266,10 @@ __device__ __forceinline__ void dw_body(DwArgs a) {
   const int m = first_m + in % gsz, n = in / gsz;
 
   DmaOperand la, lb;
-  la.init(a.GT + (int64_t)m * kTile * a.ldgt, a.ldgt, a.Vp - m * kTile, 0, (int64_t)rows * esz, 0);
-  lb.init(a.XcT + (int64_t)n * kTile * a.ldxt, a.ldxt, a.H - n * kTile, 0, (int64_t)rows * esz, 1);
+  la.init(a.GT + (int64_t)m * kTile * a.ldgt, a.ldgt, a.Vp - m * kTile, 0, (int64_t)rows * esz);
+  lb.init(a.XcT + (int64_t)n * kTile * a.ldxt, a.ldxt, a.H - n * kTile, 0, (int64_t)rows * esz);
   floatx16 acc[4][4];
-  gemm_mainloop<T>(acc, la, lb, (int)ceil_div((int64_t)rows * esz, kKB), lds);
+  gemm_mainloop<T, kDwAEarly>(acc, la, lb, (int)ceil_div((int64_t)rows * esz, kKB), lds);
 
   const bool beta = (a.group_begin > 0) || a.beta_first;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;

@@ -7,16 +7,19 @@
 //
 // Data path: global memory -> LDS by direct buffer loads (buffer_load_dwordx4
 // ... lds: each lane's 16 bytes land at M0 + 16*lane, no register staging),
-// through two LDS stages of 128 bytes of K per row (whole cache lines), then
-// LDS -> registers (ds_read_b128) -> MFMA. The loads of stage k+2 are issued
-// as soon as stage k has been read into registers. Rows and K bytes outside
-// the operand read as zero (buffer range checks). The loads are issued from inline assembly so that the compiler does
-// not order every LDS read behind them; their completion is awaited explicitly
-// with s_waitcnt vmcnt before the stage barrier.
+// in stages of 128 bytes of K per row (whole cache lines), then LDS ->
+// registers (ds_read_b128) -> MFMA. One operand (the "early" one, chosen per
+// kernel) has three stage buffers and the other two (160 KB, the whole LDS of
+// a CU): the early operand's loads for stage k+2 start at the beginning of
+// stage k, the other's once stage k has been read into registers, so both
+// have more than a stage of memory latency to land in. Rows and K bytes outside the operand read as zero (buffer range
+// checks). The loads are issued from inline assembly so that the compiler
+// does not order every LDS read behind them; their completion is awaited
+// explicitly with s_waitcnt vmcnt before the stage barrier.
 //
-// LDS layout of one operand stage: 256 rows x 128 bytes, the eight 16-byte
-// granules of row r permuted by g ^ ((r >> 1) & 7) so that the 16 rows read
-// together by an MFMA fragment load fall in distinct banks.
+// LDS layout of one operand stage buffer: 256 rows x 128 bytes, the eight
+// 16-byte granules of row r permuted by g ^ ((r >> 1) & 7) so that the 16
+// rows read together by an MFMA fragment load fall in distinct banks.
 //
 // Result layout (per wave w = 2*wm + wn, lane l, block (i, j), register r):
 //   m = wm*128 + i*32 + 8*(r/4) + 4*(l/32) + r%4,   n = wn*128 + j*32 + l%32.
@@ -26,11 +29,11 @@
 
 namespace kd {
 
-constexpr int kStages = 2;
 constexpr int kKB = 128;                         // K bytes per row per stage (a cache line)
-constexpr int kStageOp = kTile * kKB;            // 32 KB: one operand of one stage
-constexpr int kStageBytes = 2 * kStageOp;        // 64 KB
-constexpr int kMainLds = kStages * kStageBytes;  // 128 KB
+constexpr int kOpBuf = kTile * kKB;              // 32 KB: one operand of one stage
+constexpr int kEBufs = 3;                        // stage buffers of the early operand
+constexpr int kLBase = kEBufs * kOpBuf;          // the other operand's two buffers follow
+constexpr int kMainLds = (kEBufs + 2) * kOpBuf;  // 160 KB
 constexpr uint32_t kOob = 0x80000000u;           // an offset at or past this reads zero
 
 __device__ inline uint32_t lds_addr(const void* p) {
@@ -76,11 +79,11 @@ struct DmaOperand {
   uint32_t voff;      // lane's offset for load q = 0 (row and permuted granule)
   uint32_t qstride;   // 8 rows
   uint32_t gofs;      // lane's granule offset inside the 128-byte stage row
-  uint32_t ldsoff;    // operand and wave block inside a stage
+  uint32_t ldsoff;    // wave block inside a stage buffer
   int64_t kb0, kb_lim;
 
   __device__ void init(const char* tile0, int64_t ld, int rows_valid, int64_t kb0_,
-                       int64_t kb_lim_, int operand) {
+                       int64_t kb_lim_) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     if (rows_valid > kTile) rows_valid = kTile;
     rs = make_rsrc(tile0, rows_valid > 0 ? (int64_t)rows_valid * ld : 0);
@@ -92,11 +95,11 @@ struct DmaOperand {
     gofs = (uint32_t)(g * 16);
     voff = opaque((uint32_t)((w * 64 + row) * ld) + gofs);
     qstride = (uint32_t)(8 * ld);
-    ldsoff = (uint32_t)(operand * kStageOp + w * 64 * kKB);
+    ldsoff = (uint32_t)(w * 64 * kKB);
     kb0 = kb0_;
     kb_lim = kb_lim_;
   }
-  // enqueue the 8 loads of stage kt into the stage at LDS address `stage`
+  // enqueue the 8 loads of stage kt into the stage buffer at LDS address `stage`
   __device__ __forceinline__ void issue(int kt, uint32_t stage) const {
 #pragma unroll
     for (int q = 0; q < 8; ++q) issue_one(kt, stage, q);
@@ -134,14 +137,14 @@ struct DmaOperandMap {
   int64_t kb0, kb_lim;
 
   __device__ void init(const char* base_, int64_t ld_, const int32_t* map, int mn0, int mn_lim,
-                       int64_t kb0_, int64_t kb_lim_, int operand) {
+                       int64_t kb0_, int64_t kb_lim_) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int row = lane >> 3;
     const int g = (lane & 7) ^ (lane >> 4);   // even q; odd q use g ^ 4
     base = base_;
     ld = ld_;
     gofs = (uint32_t)(g * 16);
-    ldsoff = (uint32_t)(operand * kStageOp + w * 64 * kKB);
+    ldsoff = (uint32_t)(w * 64 * kKB);
     const int first = map[mn0];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -191,9 +194,9 @@ template <typename T> struct Frag;
 template <> struct Frag<__bf16> { using type = bf16x8; };
 template <> struct Frag<float> { using type = floatx4; };
 
-// Per-lane fragment addressing inside a stage: rows wm*128 + i*32 + (l & 31)
-// (A) and wn*128 + j*32 + (l & 31) (B), logical granule 2s + (l >> 5) for
-// sub-step s.
+// Per-lane fragment addressing inside a stage buffer: rows wm*128 + i*32 +
+// (l & 31) (A) and wn*128 + j*32 + (l & 31) (B), logical granule 2s + (l >> 5)
+// for sub-step s.
 struct FragAddr {
   uint32_t a[4], b[4];
   __device__ void init(int wm, int wn, int lane) {
@@ -202,7 +205,7 @@ struct FragAddr {
     for (int s = 0; s < 4; ++s) {
       const int pg = (2 * s + half) ^ swz;
       a[s] = (uint32_t)((wm * 128 + r) * kKB + pg * 16);
-      b[s] = (uint32_t)(kStageOp + (wn * 128 + r) * kKB + pg * 16);
+      b[s] = (uint32_t)((wn * 128 + r) * kKB + pg * 16);
     }
   }
 };
@@ -210,19 +213,22 @@ struct FragAddr {
 // ---------------------------------------------------------------------------
 // Main loop over nk stages (nk = ceil(K bytes / 128)). Every thread of the
 // work-group must call it with the same nk. `lds` points at kMainLds bytes.
+// A_EARLY selects the operand with three buffers (A if true, else B).
 //
-// Stage kt has four sub-steps of 16 MFMAs; the fragments of sub-step s+1 are
-// read while sub-step s computes. Before the last sub-step: wait for this
-// wave's loads of stage kt+1 and barrier (stage kt+1 visible to all waves;
-// every wave holds its stage-kt fragments, so stage kt's buffer is free).
-// The loads of stage kt+2 into that buffer are spread over the MFMAs: the 8
-// of operand A over the last sub-step of stage kt (with the 8 sub-step-0
-// fragment reads of stage kt+1), the 8 of operand B over the first sub-step
-// of stage kt+1. Issued in one burst, the loads back up the vector memory
-// queue and stall the wave's in-order issue while its MFMA pipe runs dry.
-// A stage at or past the end of K reads zeros (or, for a row-mapped operand,
-// a valid granule) into the free buffer, so the issue needs no branch. The
-// last stage is peeled: it issues no loads.
+// Stage kt (early buffer kt % 3, late buffer kt % 2) has four sub-steps of 16
+// MFMAs; the fragments of sub-step s+1 are read while sub-step s computes.
+// The 8 loads of the early operand for stage kt+2 go out one per two MFMAs
+// over the first sub-step (their buffer held stage kt-1, released by the
+// previous barrier). Before the last sub-step: wait for this wave's loads of
+// stage kt+1 (the early operand's for kt+2 may still be in flight) and
+// barrier (stage kt+1 visible to all waves; every wave holds its stage-kt
+// fragments, so stage kt's late buffer is free). The 8 loads of the late
+// operand for stage kt+2 into that buffer are spread over the last sub-step,
+// with the 8 sub-step-0 fragment reads of stage kt+1. Issued in one burst,
+// the loads back up the vector memory queue and stall the wave's in-order
+// issue while its MFMA pipe runs dry. A stage at or past the end of K reads
+// zeros (or, for a row-mapped operand, a valid granule) into a free buffer,
+// so the issue needs no branch. The last stage is peeled: it issues no loads.
 // ---------------------------------------------------------------------------
 template <typename V>
 struct SubFrags {
@@ -230,12 +236,12 @@ struct SubFrags {
 };
 
 template <class V>
-__device__ __forceinline__ void read_sub(SubFrags<V>& f, const char* stage, const FragAddr& fa,
-                                         int s) {
+__device__ __forceinline__ void read_sub(SubFrags<V>& f, const char* sa, const char* sb,
+                                         const FragAddr& fa, int s) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = *(const V*)(stage + fa.a[s] + i * 32 * kKB);
+  for (int i = 0; i < 4; ++i) f.a[i] = *(const V*)(sa + fa.a[s] + i * 32 * kKB);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.b[j] = *(const V*)(stage + fa.b[s] + j * 32 * kKB);
+  for (int j = 0; j < 4; ++j) f.b[j] = *(const V*)(sb + fa.b[s] + j * 32 * kKB);
 }
 
 __device__ __forceinline__ void mfma_ij(floatx16& acc, const bf16x8& a, const bf16x8& b) {
@@ -266,8 +272,8 @@ __device__ __forceinline__ void mfma_sub_loads(floatx16 (&acc)[4][4], const SubF
 template <class V, class OP>
 __device__ __forceinline__ void mfma_sub_loads_reads(floatx16 (&acc)[4][4], const SubFrags<V>& f,
                                                      const OP& op, int kn, uint32_t sbase,
-                                                     SubFrags<V>& fn, const char* nstage,
-                                                     const FragAddr& fa) {
+                                                     SubFrags<V>& fn, const char* na,
+                                                     const char* nb, const FragAddr& fa) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -275,13 +281,13 @@ __device__ __forceinline__ void mfma_sub_loads_reads(floatx16 (&acc)[4][4], cons
       const int q = i * 4 + j;
       mfma_ij(acc[i][j], f.a[i], f.b[j]);
       if ((q & 1) == 0) op.issue_one(kn, sbase, q >> 1);
-      if (q < 4) fn.a[q] = *(const V*)(nstage + fa.a[0] + q * 32 * kKB);
-      else if (q < 8) fn.b[q - 4] = *(const V*)(nstage + fa.b[0] + (q - 4) * 32 * kKB);
+      if (q < 4) fn.a[q] = *(const V*)(na + fa.a[0] + q * 32 * kKB);
+      else if (q < 8) fn.b[q - 4] = *(const V*)(nb + fa.b[0] + (q - 4) * 32 * kKB);
       __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-template <typename T, class OA, class OB>
+template <typename T, bool A_EARLY, class OA, class OB>
 __device__ inline void gemm_mainloop(floatx16 (&acc)[4][4], const OA& la, const OB& lb, int nk,
                                      char* lds) {
   using V = typename Frag<T>::type;
@@ -296,62 +302,85 @@ __device__ inline void gemm_mainloop(floatx16 (&acc)[4][4], const OA& la, const 
   FragAddr fa;
   fa.init(wm, wn, lane);
   const uint32_t base = lds_addr(lds);
+  // buffer i of the early / late operand
+  auto ebuf = [&](int i) { return lds + i * kOpBuf; };
+  auto lbuf = [&](int i) { return lds + kLBase + i * kOpBuf; };
+  auto issue_e = [&](int kt, int i) {
+    if constexpr (A_EARLY) la.issue(kt, base + i * kOpBuf);
+    else lb.issue(kt, base + i * kOpBuf);
+  };
+  auto issue_l = [&](int kt, int i) {
+    if constexpr (A_EARLY) lb.issue(kt, base + kLBase + i * kOpBuf);
+    else la.issue(kt, base + kLBase + i * kOpBuf);
+  };
   // every wave has finished reading the stages of a previous call
   __syncthreads();
-  la.issue(0, base);
-  lb.issue(0, base);
+  issue_e(0, 0);
+  issue_l(0, 0);
   if (nk > 1) {
-    // operand B of stage 1 follows in the first sub-step, like every stage's
-    la.issue(1, base + kStageBytes);
-    wait_vmcnt<8>();
+    issue_e(1, 1);
+    issue_l(1, 1);
+    wait_vmcnt<16>();
   } else {
     wait_vmcnt<0>();
   }
   __syncthreads();
   SubFrags<V> f0, f1;
-  read_sub(f0, lds, fa, 0);
+  read_sub(f0, A_EARLY ? ebuf(0) : lbuf(0), A_EARLY ? lbuf(0) : ebuf(0), fa, 0);
+  int ie = 0;  // early buffer of stage kt
   for (int kt = 0; kt + 1 < nk; ++kt) {
-    const char* stage = lds + (kt & 1) * kStageBytes;
+    const int ie1 = ie == kEBufs - 1 ? 0 : ie + 1;    // stage kt+1
+    const int ie2 = ie1 == kEBufs - 1 ? 0 : ie1 + 1;  // stage kt+2 (stage kt-1's, free)
+    const char* sa = A_EARLY ? ebuf(ie) : lbuf(kt & 1);
+    const char* sb = A_EARLY ? lbuf(kt & 1) : ebuf(ie);
     __builtin_amdgcn_sched_barrier(0);
-    read_sub(f1, stage, fa, 1);
+    read_sub(f1, sa, sb, fa, 1);
     __builtin_amdgcn_sched_barrier(0);
-    // operand B of stage kt+1
-    mfma_sub_loads(acc, f0, lb, kt + 1, base + ((kt + 1) & 1) * kStageBytes);
+    // the early operand of stage kt+2
+    if constexpr (A_EARLY) mfma_sub_loads(acc, f0, la, kt + 2, base + ie2 * kOpBuf);
+    else mfma_sub_loads(acc, f0, lb, kt + 2, base + ie2 * kOpBuf);
     __builtin_amdgcn_sched_barrier(0);
-    read_sub(f0, stage, fa, 2);
+    read_sub(f0, sa, sb, fa, 2);
     __builtin_amdgcn_sched_barrier(0);
     mfma16(acc, f1.a, f1.b);
     __builtin_amdgcn_sched_barrier(0);
-    read_sub(f1, stage, fa, 3);
+    read_sub(f1, sa, sb, fa, 3);
     __builtin_amdgcn_sched_barrier(0);
     mfma16(acc, f0.a, f0.b);
     __builtin_amdgcn_sched_barrier(0);
-    // this wave's loads of stage kt+1 (its A and B) are all it has outstanding
-    wait_vmcnt<0>();
+    // this wave's loads of stage kt+1 (issued before the 8 of the early
+    // operand for kt+2, and loads complete in order) have landed
+    wait_vmcnt<8>();
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    // operand A of stage kt+2 into stage kt's buffer, and stage kt+1's first reads
-    mfma_sub_loads_reads(acc, f1, la, kt + 2, base + (kt & 1) * kStageBytes, f0,
-                         lds + ((kt + 1) & 1) * kStageBytes, fa);
+    // the late operand of stage kt+2 into stage kt's late buffer, and stage
+    // kt+1's first reads
+    const uint32_t lnext = base + kLBase + (kt & 1) * kOpBuf;
+    const char* na = A_EARLY ? ebuf(ie1) : lbuf((kt + 1) & 1);
+    const char* nb = A_EARLY ? lbuf((kt + 1) & 1) : ebuf(ie1);
+    if constexpr (A_EARLY) mfma_sub_loads_reads(acc, f1, lb, kt + 2, lnext, f0, na, nb, fa);
+    else mfma_sub_loads_reads(acc, f1, la, kt + 2, lnext, f0, na, nb, fa);
+    ie = ie1;
   }
   {
-    const char* stage = lds + ((nk - 1) & 1) * kStageBytes;
+    const char* sa = A_EARLY ? ebuf(ie) : lbuf((nk - 1) & 1);
+    const char* sb = A_EARLY ? lbuf((nk - 1) & 1) : ebuf(ie);
     __builtin_amdgcn_sched_barrier(0);
-    read_sub(f1, stage, fa, 1);
+    read_sub(f1, sa, sb, fa, 1);
     __builtin_amdgcn_sched_barrier(0);
     mfma16(acc, f0.a, f0.b);
     __builtin_amdgcn_sched_barrier(0);
-    read_sub(f0, stage, fa, 2);
+    read_sub(f0, sa, sb, fa, 2);
     __builtin_amdgcn_sched_barrier(0);
     mfma16(acc, f1.a, f1.b);
     __builtin_amdgcn_sched_barrier(0);
-    read_sub(f1, stage, fa, 3);
+    read_sub(f1, sa, sb, fa, 3);
     __builtin_amdgcn_sched_barrier(0);
     mfma16(acc, f0.a, f0.b);
     __builtin_amdgcn_sched_barrier(0);
     mfma16(acc, f1.a, f1.b);
   }
-  // the loads of the stage past the end (zeros into a free buffer) have
+  // the loads of the stages past the end (zeros into free buffers) have
   // landed before the caller reuses the LDS
   wait_vmcnt<0>();
   __builtin_amdgcn_sched_barrier(0);

@@ -22,9 +22,10 @@ struct SweepArgs {
   float T;
   // teacher tables from the prepass, indexed by original row
   const int32_t* ids_s; const float* p_s; const int32_t* korig_s;
-  // forward outputs: partials [split][r], split stride = (token tiles) * 256
-  float* pm; float* ps; float* pd;
-  float* z_topk;                      // [S,K] or NULL
+  // forward outputs: partials [split][r], split stride = (token tiles) * 256,
+  // and z at every teacher id, at its position in the sorted table
+  float* pm; float* ps;
+  float* zs;                          // [S,K], indexed like ids_s
   // backward
   const float* lse; const float* grad_loss;
   char* G; int64_t ldg;               // gradient tile [row_cap, Vp], bytes per row
@@ -38,7 +39,8 @@ struct CombineArgs {
   int identity;                       // forward ran over all S rows in order (no row map)
   float T;
   const int32_t* pos; const int32_t* nrows_dev;
-  const float* pm; const float* ps; const float* pd;
+  const float* pm; const float* ps;
+  const int32_t* ids_s; const float* p_s; const int32_t* korig_s; const float* zs;
   const float* negH;
   float* lse; float* kl_rows; float* z_topk;
   double* block_sums;

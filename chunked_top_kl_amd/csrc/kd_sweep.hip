@@ -21,6 +21,13 @@
 
 namespace kd {
 
+// operand with the third stage buffer (longer load lead): A = W (true) or the
+// token rows
+#ifndef KD_SWEEP_A_EARLY
+#define KD_SWEEP_A_EARLY 0
+#endif
+constexpr bool kSweepAEarly = KD_SWEEP_A_EARLY;
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -69,15 +76,20 @@ __device__ inline void cursor_adv(Cursor& c, const int32_t* ids_s, int K) {
   c.nid = c.cur < K ? ids_s[c.base + c.cur] : 0x7FFFFFFF;
 }
 
+// Register of this lane's half tile that holds local row `local` of the
+// half tile [lo, lo+128), or -1 when the row belongs to the other lane half.
+// The two lanes of a token column (lane halves) see the same ids; a local row
+// r belongs to the lane whose half is bit 2 of r, at register
+// (r >> 5) * 16 + ((r >> 3) & 3) * 4 + (r & 3).
+__device__ __forceinline__ int hit_reg(bool h, int local, int half) {
+  const bool mine = h && (((local >> 2) & 1) == half);
+  return mine ? (local >> 5) * 16 + ((local >> 3) & 3) * 4 + (local & 3) : -1;
+}
+
 // Walk the teacher ids of one token column that fall in [lo, lo+128) (this
-// wave's half tile). The two lanes of a token column (lane halves) walk the
-// same ids; a hit at local row r belongs to the lane whose half is bit 2 of r,
-// at its register (r >> 5) * 16 + ((r >> 3) & 3) * 4 + (r & 3). Each round
-// calls on(tgt, e) on every lane, with tgt that register or -1 when the lane
-// has no hit of its own this round, and e the hit's index in the sorted
-// table; then every lane with a hit advances. The callback reaches the
-// register with a compare-and-select over all 64 (static indices only), so
-// the column's values stay in registers across the walk.
+// wave's half tile) one id at a time. Each round calls on(tgt, e) on every
+// lane, with tgt the register of the lane's own hit or -1, and e the hit's
+// index in the sorted table; then every lane with a hit advances.
 template <class F>
 __device__ __forceinline__ void walk_hits(Cursor& c, const int32_t* ids_s, int K, int lo, int half,
                                           F&& on) {
@@ -86,11 +98,48 @@ __device__ __forceinline__ void walk_hits(Cursor& c, const int32_t* ids_s, int K
   while (true) {
     const bool h = c.nid < hi;
     if (ballot(h) == 0) break;
-    const int local = c.nid - lo;
-    const bool mine = h && (((local >> 2) & 1) == half);
-    const int tgt = mine ? (local >> 5) * 16 + ((local >> 3) & 3) * 4 + (local & 3) : -1;
-    on(tgt, c.base + c.cur);
+    on(hit_reg(h, c.nid - lo, half), c.base + c.cur);
     if (h) cursor_adv(c, ids_s, K);
+  }
+}
+
+// The same walk over a window of the next kWin ids of the column, loaded
+// before the tile's log-sum-exp so that their latency is hidden: ids below lo
+// (the other wave's half of the previous tile) are passed over, ids in
+// [lo, hi) are hits, and the cursor moves past every id below hi. Only when a
+// lane's whole window lies below hi does the one-id-at-a-time walk continue.
+constexpr int kWin = 4;
+
+__device__ __forceinline__ void window_load(int64_t base, int cur, const int32_t* ids_s, int K,
+                                            int (&n)[kWin]) {
+#pragma unroll
+  for (int q = 0; q < kWin; ++q) {
+    const int p = cur + q;
+    const int v = ids_s[base + (p < K ? p : K - 1)];
+    n[q] = p < K ? v : 0x7FFFFFFF;
+  }
+}
+
+template <class F>
+__device__ __forceinline__ void walk_window(int64_t base, int& cur, const int (&n)[kWin],
+                                            const int32_t* ids_s, int K, int lo, int half,
+                                            F&& on) {
+  const int hi = lo + 128;
+  int used = 0;
+#pragma unroll
+  for (int q = 0; q < kWin; ++q) {
+    const bool h = n[q] >= lo && n[q] < hi;
+    used += n[q] < hi ? 1 : 0;
+    if (ballot(h) == 0) continue;
+    on(hit_reg(h, n[q] - lo, half), base + cur + q);
+  }
+  cur += used;
+  const bool more = used == kWin;
+  if (ballot(more) != 0) {
+    Cursor c{base, cur, 0x7FFFFFFF};
+    if (more && cur < K) c.nid = ids_s[base + cur];
+    walk_hits(c, ids_s, K, lo, half, on);
+    cur = c.cur;
   }
 }
 
@@ -121,7 +170,7 @@ __device__ __forceinline__ float pick64(const float (&z)[64], int tgt) {
 // vocabulary computes nothing (its rows are at or past Vp and never stored).
 // ---------------------------------------------------------------------------
 constexpr int kGPitch = 528;
-constexpr int kStagingLds = 64 * 1024 + 128 * kGPitch;   // fits in kMainLds + 2 KB
+constexpr int kStagingLds = 64 * 1024 + 128 * kGPitch;   // inside the main-loop stage area
 
 __device__ __forceinline__ int staged_token(int tp, int jp) {
   return (tp >> 6) * 128 + 64 * jp + (tp & 63);
@@ -224,8 +273,8 @@ __device__ __forceinline__ void grad_tile_staged(floatx16 (&acc)[4][4], const Sw
 template <typename T, int KIND, bool MAP>
 __device__ __forceinline__ void sweep_body(SweepArgs a) {
   // main-loop stages; the gradient tile epilogue stages its output here too
-  __shared__ __attribute__((aligned(16))) char lds[kMainLds + 2048];
-  static_assert(kStagingLds <= kMainLds + 2048, "staging area");
+  __shared__ __attribute__((aligned(16))) char lds[kMainLds];
+  static_assert(kStagingLds <= kMainLds, "staging area");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int half = lane >> 5;
 
@@ -259,7 +308,6 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
   const int64_t kbytes = (int64_t)a.H * esz;
   const int nk = (int)ceil_div(kbytes, kKB);
   const float c = kLog2e / a.T;
-  const float invT = 1.0f / a.T;
 
   // token columns owned by this lane: launch rows tl0 + 32*j
   const int tl0 = jt * kTile + wn * 128 + (lane & 31);
@@ -271,28 +319,25 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
   }
 
   // per-kind running state
-  float m[4], s[4], d[4];
+  float m[4], s[4];
   double S64[4], U64[4];
-  Cursor cu[4];
+  int64_t cbase[4];
+  int ccur[4];
   float lse2[4];
   float coef = 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     m[j] = -INFINITY;
     s[j] = 0.0f;
-    d[j] = 0.0f;
     S64[j] = 0.0;
     U64[j] = 0.0;
     lse2[j] = 0.0f;
+    cbase[j] = 0;
+    ccur[j] = 0;
     if constexpr (KIND == kSweepFwd) {
-      cu[j].base = (int64_t)orow[j] * a.K;
-      if (tl0 + 32 * j < rows) {
-        cu[j].cur = lower_bound_ids(a.ids_s + cu[j].base, a.K, vt_begin * kTile);
-        cu[j].nid = cu[j].cur < a.K ? a.ids_s[cu[j].base + cu[j].cur] : 0x7FFFFFFF;
-      } else {
-        cu[j].cur = a.K;
-        cu[j].nid = 0x7FFFFFFF;
-      }
+      cbase[j] = (int64_t)orow[j] * a.K;
+      ccur[j] = (tl0 + 32 * j < rows) ? lower_bound_ids(a.ids_s + cbase[j], a.K, vt_begin * kTile)
+                                      : a.K;
     }
     if constexpr (KIND == kSweepBwdG)
       lse2[j] = (tl0 + 32 * j < rows) ? a.lse[orow[j]] * kLog2e : 0.0f;
@@ -306,16 +351,16 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
     // operand state is rebuilt per tile so that nothing of the main loop stays
     // live (and spillable) across the register-heavy epilogues
     DmaOperand la;
-    la.init(a.W + (int64_t)vt * kTile * a.ldw, a.ldw, a.V - vt * kTile, 0, kbytes, 0);
+    la.init(a.W + (int64_t)vt * kTile * a.ldw, a.ldw, a.V - vt * kTile, 0, kbytes);
     typename std::conditional<MAP, DmaOperandMap, DmaOperand>::type lb;
     if constexpr (MAP) {
-      lb.init(a.X, a.ldx, a.idx, a.row_begin + jt * kTile, a.row_begin + rows, 0, kbytes, 1);
+      lb.init(a.X, a.ldx, a.idx, a.row_begin + jt * kTile, a.row_begin + rows, 0, kbytes);
     } else {
       lb.init(a.X + (int64_t)(a.x_row0 + jt * kTile) * a.ldx, a.ldx, rows - jt * kTile, 0,
-              kbytes, 1);
+              kbytes);
     }
     floatx16 acc[4][4];
-    gemm_mainloop<T>(acc, la, lb, nk, lds);
+    gemm_mainloop<T, kSweepAEarly>(acc, la, lb, nk, lds);
 
     const int vw0 = vt * kTile + wm * 128;
     if constexpr (KIND == kSweepBwdG && sizeof(T) == 2) {
@@ -327,6 +372,13 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
     // columns in [V, round_up(V, 8)) of G are written as zeros (see the store)
     const int Vp = (int)round_up(a.V, 8);
     const int tpad = (int)round_up(rows, 8);
+
+    // the next teacher ids of every token column, for the walks below
+    int win[4][kWin];
+    if constexpr (KIND == kSweepFwd) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) window_load(cbase[j], ccur[j], a.ids_s, a.K, win[j]);
+    }
 
     // One token column at a time: its 64 accumulators are copied to registers
     // (z), processed, and the next column starts only after this one is done
@@ -362,14 +414,13 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
           s[j] = s[j] * sc + ((s0 + s1) + (s2 + s3));
           m[j] = mn;
         }
-        float* zrow = a.z_topk ? a.z_topk + (int64_t)orow[j] * a.K : nullptr;
-        walk_hits(cu[j], a.ids_s, a.K, vw0, half, [&](int tgt, int64_t e) {
-          const float val = pick64(z, tgt);
-          if (tgt >= 0) {
-            d[j] += a.p_s[e] * val;
-            if (zrow) zrow[a.korig_s[e]] = val * invT;
-          }
-        });
+        // z at the teacher ids, stored at their sorted positions; the
+        // combine forms sum_k p_k z_k from them
+        walk_window(cbase[j], ccur[j], win[j], a.ids_s, a.K, vw0, half,
+                    [&](int tgt, int64_t e) {
+                      const float val = pick64(z, tgt);
+                      if (tgt >= 0) a.zs[e] = val;
+                    });
       }
 
       if constexpr (KIND == kSweepEnt) {
@@ -456,9 +507,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
   for (int j = 0; j < 4; ++j) {
     if constexpr (KIND == kSweepFwd) {
       const float m2 = __shfl_xor(m[j], 32, 64), s2 = __shfl_xor(s[j], 32, 64);
-      const float d2 = __shfl_xor(d[j], 32, 64);
       lse2_merge(m[j], s[j], m2, s2);
-      d[j] += d2;
     } else {
       const float m2 = __shfl_xor(m[j], 32, 64);
       const double S2 = __shfl_xor(S64[j], 32, 64), U2 = __shfl_xor(U64[j], 32, 64);
@@ -477,7 +526,6 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
       xm[t] = m[j];
       if constexpr (KIND == kSweepFwd) {
         xa[t] = s[j];
-        xb[t] = d[j];
       } else {
         xa[t] = S64[j];
         xb[t] = U64[j];
@@ -493,10 +541,8 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
       const int64_t o = (int64_t)b * ntt * kTile + tl0 + 32 * j;
       if constexpr (KIND == kSweepFwd) {
         lse2_merge(m[j], s[j], xm[t], (float)xa[t]);
-        d[j] += (float)xb[t];
         a.pm[o] = m[j];
         a.ps[o] = s[j];
-        a.pd[o] = d[j];
       } else {
         ent_merge(m[j], S64[j], U64[j], xm[t], xa[t], xb[t]);
         a.em[o] = m[j];
@@ -633,15 +679,25 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(CombineArgs a) {
       const int r = a.identity ? t : pr;
       const int n = a.identity ? a.S : *a.nrows_dev;
       const int ns = sweep_splits((int)ceil_div(n, kTile), (int)ceil_div(a.V, kTile), a.ncu);
-      float M = -INFINITY, sum = 0.0f, dot = 0.0f;
+      float M = -INFINITY, sum = 0.0f;
       const int64_t stride = ceil_div(n, kTile) * kTile;
       for (int b = 0; b < ns; ++b) {
         const int64_t o = (int64_t)b * stride + r;
         lse2_merge(M, sum, a.pm[o], a.ps[o]);
-        dot += a.pd[o];
+      }
+      // sum_k p_k z_k over the row's usable ids, in sorted order; z_topk in
+      // the caller's order
+      const int64_t base = (int64_t)t * a.K;
+      const float invT = 1.0f / a.T;
+      double dot = 0.0;
+      for (int k = 0; k < a.K; ++k) {
+        if (a.ids_s[base + k] == 0x7FFFFFFF) break;   // out-of-range ids sort last
+        const float zv = a.zs[base + k];
+        dot += (double)a.p_s[base + k] * (double)zv;
+        if (a.z_topk) a.z_topk[base + a.korig_s[base + k]] = zv * invT;
       }
       const float lse = (M + __log2f(sum)) * kLn2;
-      const float kl = a.negH[t] - dot / a.T + lse;
+      const float kl = (float)((double)a.negH[t] - dot / (double)a.T + (double)lse);
       a.lse[t] = lse;
       if (a.kl_rows) a.kl_rows[t] = kl;
       contrib = kl;
