@@ -281,20 +281,20 @@ __device__ __forceinline__ void dw_body(DwArgs a) {
   const int vrows = (a.V - m * kTile) < kTile ? (a.V - m * kTile) : kTile;
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc(a.dW + (int64_t)m * kTile * a.H, (int64_t)vrows * a.H * 4);
-  uint32_t off[4][16];
+  // lane offset of column block j at the tile's first row of this lane; the
+  // element of accumulator (i, j, r) is a wave-uniform number of rows further.
+  // A column past H starts at kOob; adding at most 256 rows (< 2^30 bytes for
+  // H <= 2^20) keeps it at or past 2^31, outside the resource, with no wrap.
+  uint32_t vb[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int h = n * kTile + wn * 128 + j * 32 + (lane & 31);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      // row within the tile of acc[i][j][r] for i = 0; block i adds 32 rows
-      const int row = wm * 128 + 4 * (lane >> 5) + 8 * (r >> 2) + (r & 3);
-      off[j][r] = h < a.H ? (uint32_t)((row * a.H + h) * 4) : kOob;
-    }
+    const int row0 = wm * 128 + 4 * (lane >> 5);
+    vb[j] = h < a.H ? (uint32_t)((row0 * a.H + h) * 4) : kOob;
   }
-  const uint32_t istride = 32u * (uint32_t)a.H * 4u;
   auto addr = [&](int j, int i, int r) -> int {
-    return (int)(off[j][r] == kOob ? kOob : off[j][r] + (uint32_t)i * istride);
+    const uint32_t d = (uint32_t)((32 * i + 8 * (r >> 2) + (r & 3)) * a.H) * 4u;
+    return (int)(vb[j] + d);
   };
   // group g: block j = g / 2, blocks i = 2 (g % 2) and 2 (g % 2) + 1
   auto ld = [&](int g, float (&o)[32]) {
