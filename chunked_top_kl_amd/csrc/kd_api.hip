@@ -109,7 +109,7 @@ int check_problem(const kd_problem* p) {
 struct Layout {
   size_t count, present, pos, idx, ids_s, p_s, korig_s, negH;
   size_t pm, ps, zs, bsum;
-  size_t G, GT, WT, XcT, dhp;
+  size_t G, GT, WT, XcT, Xc, dhp;
   size_t em, es, eu;
   size_t band, refined, scal, dscal, rpart, xb, counters;
   size_t total;
@@ -176,6 +176,7 @@ Layout plan(const kd_problem* p) {
   L.GT = take(L.Vp * L.Cld * L.esz);
   L.WT = take(H * L.Vld * L.esz);
   L.XcT = take(H * L.Cld * L.esz);
+  L.Xc = take(L.C * H * L.esz);
   // dHidden: vocabulary splits chosen for a full chunk, used for every chunk
   L.ks = kd::dh_splits((int)L.C, (int)V, (int)H, kCostCUs, p->hw_dtype == KD_F32);
   L.dhp = take((size_t)L.ks * kd::dh_split_stride((int)L.C, (int)H) * 4);
@@ -362,15 +363,17 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
       KD_HIP(kd::launch_gather_rows_t(f32, (const char*)hidden, row_bytes, at<int32_t>(ws, L.idx),
                                       at<int32_t>(ws, L.count), row_begin, C, H,
                                       at<char>(ws, L.XcT) + slot * L.slot * L.esz, L.Cld * L.esz,
-                                      (int)L.slot, st));
+                                      (int)L.slot, at<char>(ws, L.Xc), st));
     }
     if (S > 0) {
       kd::SweepArgs a;
       std::memset(&a, 0, sizeof(a));
       a.W = (const char*)W;
       a.ldw = row_bytes;
-      a.X = (const char*)hidden;
+      // the chunk's rows, gathered in order by the pass above
+      a.X = at<char>(ws, L.Xc);
       a.ldx = row_bytes;
+      a.x_row0 = 0;
       a.idx = at<int32_t>(ws, L.idx);
       a.nrows_dev = at<int32_t>(ws, L.count);
       a.row_begin = row_begin;
@@ -391,7 +394,7 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
       a.ldgt = L.Cld * L.esz;
       {
         Prof pr("bwd_grad_tile", st);
-        KD_HIP(kd::launch_sweep(kd::kSweepBwdG, f32, 1, a, sgrid, st));
+        KD_HIP(kd::launch_sweep(kd::kSweepBwdG, f32, 0, a, sgrid, st));
       }
       kd::GradTeacherArgs gt;
       gt.G = a.G;

@@ -164,12 +164,15 @@ hipError_t launch_zero_invalid_rows(const int32_t* pos, int64_t S, int H, float*
 // out[h][r] = X[idx[row_begin + r]][h] for the chunk's rows r < rows and
 // out[h][r] = 0 for rows <= r < Cp (the gathered rows, transposed: the dW
 // product reads them with K = chunk rows contiguous). 64 x 64 tiles via LDS.
+// The same rows are also written in order, xc[r][h] (row pitch ldx), for the
+// gradient tile, which then reads its token operand as one contiguous block.
 template <typename T>
 __global__ __launch_bounds__(256) void gather_rows_t_kernel(const char* X, int64_t ldx,
                                                             const int32_t* idx,
                                                             const int32_t* nrows_dev,
                                                             int row_begin, int row_cap, int H,
-                                                            char* out, int64_t ldo, int Cp) {
+                                                            char* out, int64_t ldo, int Cp,
+                                                            char* xc) {
   __shared__ T tile[64][65];
   const int rows = chunk_rows(nrows_dev, row_begin, row_cap);
   if (rows <= 0) return;
@@ -179,7 +182,10 @@ __global__ __launch_bounds__(256) void gather_rows_t_kernel(const char* X, int64
   for (int rr = ty; rr < 64; rr += 4) {
     const int r = r0 + rr, h = h0 + tx;
     T v = (T)0.0f;
-    if (r < rows && h < H) v = ((const T*)(X + (int64_t)idx[row_begin + r] * ldx))[h];
+    if (r < rows && h < H) {
+      v = ((const T*)(X + (int64_t)idx[row_begin + r] * ldx))[h];
+      ((T*)(xc + (int64_t)r * ldx))[h] = v;
+    }
     tile[rr][tx] = v;
   }
   __syncthreads();
@@ -191,14 +197,14 @@ __global__ __launch_bounds__(256) void gather_rows_t_kernel(const char* X, int64
 
 hipError_t launch_gather_rows_t(int f32, const char* X, int64_t ldx, const int32_t* idx,
                                 const int32_t* nrows_dev, int row_begin, int row_cap, int H,
-                                char* out, int64_t ldo, int Cp, hipStream_t st) {
+                                char* out, int64_t ldo, int Cp, char* xc, hipStream_t st) {
   dim3 grid((unsigned)ceil_div(Cp, 64), (unsigned)ceil_div(H, 64));
   if (f32)
     hipLaunchKernelGGL(gather_rows_t_kernel<float>, grid, dim3(256), 0, st, X, ldx, idx, nrows_dev,
-                       row_begin, row_cap, H, out, ldo, Cp);
+                       row_begin, row_cap, H, out, ldo, Cp, xc);
   else
     hipLaunchKernelGGL(gather_rows_t_kernel<__bf16>, grid, dim3(256), 0, st, X, ldx, idx,
-                       nrows_dev, row_begin, row_cap, H, out, ldo, Cp);
+                       nrows_dev, row_begin, row_cap, H, out, ldo, Cp, xc);
   return hipGetLastError();
 }
 

@@ -116,7 +116,7 @@ hipError_t launch_fwd_combine(const CombineArgs& a, hipStream_t st);
 hipError_t launch_ent_combine(const EntCombineArgs& a, hipStream_t st);
 hipError_t launch_gather_rows_t(int f32, const char* X, int64_t ldx, const int32_t* idx,
                                 const int32_t* nrows_dev, int row_begin, int row_cap, int H,
-                                char* out, int64_t ldo, int Cp, hipStream_t st);
+                                char* out, int64_t ldo, int Cp, char* xc, hipStream_t st);
 hipError_t launch_transpose_w(int f32, const char* W, int V, int H, char* WT, int Vp, int ldwt,
                               hipStream_t st);
 hipError_t launch_zero_invalid_rows(const int32_t* pos, int64_t S, int H, float* dH,

@@ -580,11 +580,11 @@ int sweep_grid(int64_t rows_max, int V, int ncu) {
   }
 KD_SWEEP_KERNEL(kd_fwd_lse_gather_bf16, __bf16, kSweepFwd, false)
 KD_SWEEP_KERNEL(kd_fwd_lse_gather_rows_bf16, __bf16, kSweepFwd, true)
-KD_SWEEP_KERNEL(kd_bwd_grad_tile_bf16, __bf16, kSweepBwdG, true)
+KD_SWEEP_KERNEL(kd_bwd_grad_tile_bf16, __bf16, kSweepBwdG, false)
 KD_SWEEP_KERNEL(kd_entropy_sweep_bf16, __bf16, kSweepEnt, false)
 KD_SWEEP_KERNEL(kd_fwd_lse_gather_f32, float, kSweepFwd, false)
 KD_SWEEP_KERNEL(kd_fwd_lse_gather_rows_f32, float, kSweepFwd, true)
-KD_SWEEP_KERNEL(kd_bwd_grad_tile_f32, float, kSweepBwdG, true)
+KD_SWEEP_KERNEL(kd_bwd_grad_tile_f32, float, kSweepBwdG, false)
 KD_SWEEP_KERNEL(kd_entropy_sweep_f32, float, kSweepEnt, false)
 #undef KD_SWEEP_KERNEL
 
