@@ -15,4 +15,5 @@ from .kd_oracle import (  # noqa: F401
     oracle_select_top_fraction,
     oracle_entropy_select_kl,
     oracle_validate_topk,
+    oracle_teacher_topk,
 )

@@ -39,7 +39,11 @@ Readings where the pages are silent (each is repeated in the design doc):
   * a teacher logit of -inf gives p = 0; a row whose K logits are all -inf is a
     missing position and is excluded like a masked row;
   * entropy is in nats over the full vocabulary at T = 1; selection keeps
-    floor(num*S/den) positions, highest entropy first, lower index on ties.
+    floor(num*S/den) positions, highest entropy first, lower index on ties;
+  * the teacher cache holds, per position, the K entries of largest teacher
+    logit z = h . w_v (before any temperature), ordered by z descending with the
+    lower id first among equal logits; the stored logit is z rounded to fp32,
+    and then to bf16 when a bf16 cache is asked for.
 """
 from __future__ import annotations
 
@@ -58,6 +62,7 @@ __all__ = [
     "oracle_select_top_fraction",
     "oracle_entropy_select_kl",
     "oracle_validate_topk",
+    "oracle_teacher_topk",
 ]
 
 
@@ -313,3 +318,44 @@ def oracle_validate_topk(ids, tlogits, V):
     n_empty = int(np.count_nonzero(np.all(np.isneginf(tl), axis=1))) if tl.size else 0
     n_bad_logit = int(np.count_nonzero(np.isnan(tl) | np.isposinf(tl)))
     return n_bad_id, n_empty, n_bad_logit
+
+
+def _round_bf16_values(x32: np.ndarray) -> np.ndarray:
+    """fp32 values rounded to the nearest bf16 value (ties to even), as fp32."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
+    return r.astype(np.uint32).view(np.float32)
+
+
+def oracle_teacher_topk(hidden, W, K, out_dtype="f32"):
+    """Teacher top-K cache entries for every position.
+
+    [HF "offline top-K logits"]: the teacher's output is computed once and only
+    the logits of each position's K most likely tokens are kept; [HF
+    "operations"]: the cache holds per-position token ids and logits, and its
+    validation checks their top-K order. Softmax is monotone, so the K most
+    likely tokens are the K largest logits.
+
+    z = hidden @ W^T in fp64 from the exact inputs. Per row: the K entries of
+    largest z, ordered by z descending, the lower id first among equal z.
+    Returns (ids int32 [S, K], logits float32 [S, K]): z rounded to fp32, then
+    to bf16 (kept as fp32 values) when out_dtype is "bf16".
+    """
+    Z = _f64(hidden) @ _f64(W).T
+    S, V = Z.shape
+    if not 1 <= K <= V:
+        raise ValueError("need 1 <= K <= V")
+    ids = np.empty((S, K), dtype=np.int32)
+    vals = np.empty((S, K), dtype=np.float64)
+    col = np.arange(V)
+    for t in range(S):
+        order = np.lexsort((col, -Z[t]))[:K]     # primary: z descending; then id ascending
+        ids[t] = order
+        vals[t] = Z[t, order]
+    logits = vals.astype(np.float32)
+    if out_dtype == "bf16":
+        logits = _round_bf16_values(logits)
+    elif out_dtype != "f32":
+        raise ValueError("out_dtype must be 'f32' or 'bf16'")
+    return ids, logits
