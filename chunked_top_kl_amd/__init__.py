@@ -18,6 +18,7 @@ __all__ = [
     "kd_abi_version", "kd_status_str", "kd_topk_kl_workspace_bytes",
     "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_student_entropy",
     "kd_select_top_fraction", "kd_validate_topk",
+    "kd_teacher_topk_workspace_bytes", "kd_teacher_topk",
     "kd_profile_enable", "kd_profile_read", "kd_profile_reset",
     "KDTopKKL", "kd_topk_kl", "LIB_PATH",
 ]
@@ -65,6 +66,10 @@ lib.kd_select_top_fraction.argtypes = [_PP, _P, _P, _P, ctypes.c_int64, ctypes.c
                                        _I64P, _P, ctypes.c_size_t, _P]
 lib.kd_validate_topk.restype = ctypes.c_int
 lib.kd_validate_topk.argtypes = [_PP, _P, _P, _I64P, _I64P, _I64P, _P, ctypes.c_size_t, _P]
+lib.kd_teacher_topk_workspace_bytes.restype = ctypes.c_size_t
+lib.kd_teacher_topk_workspace_bytes.argtypes = [_PP]
+lib.kd_teacher_topk.restype = ctypes.c_int
+lib.kd_teacher_topk.argtypes = [_PP, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.kd_profile_enable.restype = ctypes.c_int
 lib.kd_profile_enable.argtypes = [ctypes.c_int]
 lib.kd_profile_read.restype = ctypes.c_int
@@ -218,6 +223,35 @@ def kd_select_top_fraction(entropy, hidden, W, num=20, den=100, chunk=1024, work
                                       _ptr(ws), ws.numel(), _stream(dev)),
            "kd_select_top_fraction")
     return mask, idx[: cnt.value], cnt.value
+
+
+def kd_teacher_topk_workspace_bytes(problem: kd_problem) -> int:
+    return int(lib.kd_teacher_topk_workspace_bytes(ctypes.byref(problem)))
+
+
+def kd_teacher_topk(hidden, W, K, chunk=2048, out_dtype=torch.bfloat16, workspace=None):
+    """Teacher top-K cache of every position: (ids int32 [S,K], logits [S,K] out_dtype),
+    the K largest teacher logits of each row of hidden W^T, largest first, lower id first
+    on ties (chosen in fp64; logits are the fp64 values rounded)."""
+    if hidden.dim() != 2 or W.dim() != 2 or hidden.shape[1] != W.shape[1]:
+        raise ValueError("hidden [S,H] and W [V,H] expected")
+    if hidden.dtype != W.dtype or not hidden.is_contiguous() or not W.is_contiguous():
+        raise ValueError("hidden and W must be contiguous and of one dtype")
+    S, H = hidden.shape
+    p = make_problem(S, H, W.shape[0], K, chunk, 1.0, _dtype_code(hidden.dtype),
+                     _dtype_code(out_dtype))
+    dev = hidden.device
+    need = kd_teacher_topk_workspace_bytes(p)
+    if need == 0:
+        raise KdError(2, "kd_teacher_topk")
+    if workspace is None or workspace.numel() < need or workspace.data_ptr() % 256 != 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ids = torch.empty(S, K, dtype=torch.int32, device=dev)
+    logits = torch.empty(S, K, dtype=out_dtype, device=dev)
+    _check(lib.kd_teacher_topk(ctypes.byref(p), _ptr(hidden), _ptr(W), _ptr(ids), _ptr(logits),
+                               _ptr(workspace), workspace.numel(), _stream(dev)),
+           "kd_teacher_topk")
+    return ids, logits
 
 
 def kd_validate_topk(topk_ids, topk_logits, V, workspace=None):

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkdtopk.so")
 
-SOURCES = ["kd_api.hip", "kd_sweep.hip", "kd_gemm.hip", "kd_prepass.hip", "kd_select.hip"]
+SOURCES = ["kd_api.hip", "kd_sweep.hip", "kd_gemm.hip", "kd_prepass.hip", "kd_select.hip",
+           "kd_teacher.hip"]
 
 ARCH = "gfx950"
 HIP_FLAGS = [

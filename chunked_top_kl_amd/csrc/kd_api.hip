@@ -569,6 +569,144 @@ int kd_select_top_fraction(const kd_problem* p, const void* hidden, const void* 
   return KD_OK;
 }
 
+// ------------------------------------------------------------------ teacher cache writer
+constexpr int64_t kPilotRows = 16384;      // vocabulary rows of the pilot pass
+constexpr int kTeacherFinalGroups = 512;   // work-groups of the final ranking
+constexpr int kTeacherBigGroups = 16;      // work-groups (and scratch areas) for large bands
+
+struct TeacherLayout {
+  int64_t C, P, ldp, cap;
+  size_t zp, cid, cz, cnt, te, bnd, tau2, big, nbig, wpart, wmax, scratch, total;
+};
+
+TeacherLayout plan_teacher(const kd_problem* p) {
+  TeacherLayout L{};
+  const int64_t S = p->S, V = p->V;
+  L.C = std::min<int64_t>(p->chunk, std::max<int64_t>(S, 1));
+  L.P = std::min<int64_t>(V, kPilotRows);
+  L.ldp = kd::round_up(L.C, 64);
+  L.cap = V;   // a row's candidates are distinct vocabulary entries
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (size_t)kd::round_up((int64_t)bytes, 256);
+    return o;
+  };
+  L.zp = take((size_t)L.P * L.ldp * 4);
+  L.cid = take((size_t)L.C * L.cap * 4);
+  L.cz = take((size_t)L.C * L.cap * 4);
+  L.cnt = take((size_t)L.C * 4);
+  L.te = take((size_t)L.C * 4);
+  L.bnd = take((size_t)L.C * 8);
+  L.tau2 = take((size_t)L.C * 4);
+  L.big = take((size_t)L.C * 4);
+  L.nbig = take(8);
+  L.wpart = take((size_t)kd::kTeacherWnormGroups * 8);
+  L.wmax = take(8);
+  L.scratch = take((size_t)kTeacherBigGroups * kd::teacher_scratch_entries(L.cap) * 12);
+  L.total = off;
+  return L;
+}
+
+size_t kd_teacher_topk_workspace_bytes(const kd_problem* p) {
+  if (check_problem(p)) return 0;
+  return plan_teacher(p).total;
+}
+
+int kd_teacher_topk(const kd_problem* p, const void* hidden, const void* W, int32_t* topk_ids,
+                    void* topk_logits, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!W || (p->S > 0 && (!hidden || !topk_ids || !topk_logits))) return KD_ERR_NULL;
+  const TeacherLayout L = plan_teacher(p);
+  if (!ws || ((uintptr_t)ws & 255u) != 0 || ws_bytes < L.total) return KD_ERR_WORKSPACE;
+  if ((rc = check_device())) return rc;
+  if (p->S == 0) return KD_OK;
+  hipStream_t st = (hipStream_t)stream;
+  const int f32 = p->hw_dtype == KD_F32;
+  const int64_t esz = f32 ? 4 : 2;
+  const int64_t oesz = p->tl_dtype == KD_F32 ? 4 : 2;
+  const int S = (int)p->S, H = (int)p->H, V = (int)p->V, K = (int)p->K;
+  const int P = (int)L.P;
+  const int64_t ld = (int64_t)H * esz;
+  {
+    Prof pr("teacher_wnorm", st);
+    KD_HIP(kd::launch_teacher_wnorm(f32, (const char*)W, ld, V, H, at<double>(ws, L.wpart),
+                                    at<double>(ws, L.wmax), st));
+  }
+  for (int64_t c0 = 0; c0 < S; c0 += L.C) {
+    const int rows = (int)std::min<int64_t>(L.C, S - c0);
+    const char* X = (const char*)hidden + c0 * ld;
+    kd::SweepArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.W = (const char*)W;
+    a.ldw = ld;
+    a.X = X;
+    a.ldx = ld;
+    a.row_cap = rows;
+    a.V = P;
+    a.H = H;
+    a.K = K;
+    a.ncu = kCostCUs;
+    a.T = 1.0f;
+    a.zp = at<float>(ws, L.zp);
+    a.ldp = L.ldp;
+    {
+      Prof pr("teacher_pilot", st);
+      KD_HIP(kd::launch_sweep(kd::kSweepPilot, f32, 0, a, kd::sweep_grid(rows, P, kCostCUs), st));
+    }
+    kd::TeacherArgs t;
+    std::memset(&t, 0, sizeof(t));
+    t.X = X;
+    t.ldx = ld;
+    t.W = (const char*)W;
+    t.ldw = ld;
+    t.rows = rows;
+    t.H = H;
+    t.V = V;
+    t.K = K;
+    t.P = P;
+    t.zp = at<float>(ws, L.zp);
+    t.ldp = L.ldp;
+    t.wmax = at<double>(ws, L.wmax);
+    t.te = at<float>(ws, L.te);
+    t.bnd = at<double>(ws, L.bnd);
+    t.cnt = at<int32_t>(ws, L.cnt);
+    t.cid = at<int32_t>(ws, L.cid);
+    t.cz = at<float>(ws, L.cz);
+    t.cap = L.cap;
+    t.scratch = at<char>(ws, L.scratch);
+    t.ids_out = topk_ids + c0 * K;
+    t.logits_out = (char*)topk_logits + c0 * K * oesz;
+    t.out_bf16 = p->tl_dtype == KD_BF16;
+    int32_t* nbig = at<int32_t>(ws, L.nbig);
+    {
+      Prof pr("teacher_threshold", st);
+      KD_HIP(kd::launch_teacher_threshold(f32, t, nbig, st));
+    }
+    if (V > P) {
+      kd::SweepArgs e = a;
+      e.W = (const char*)W + (int64_t)P * ld;
+      e.V = V - P;
+      e.te = t.te;
+      e.cnt = t.cnt;
+      e.cid = t.cid;
+      e.cz = t.cz;
+      e.cap = t.cap;
+      e.id_offset = P;
+      Prof pr("teacher_emit", st);
+      KD_HIP(kd::launch_sweep(kd::kSweepEmit, f32, 0, e, kd::sweep_grid(rows, V - P, kCostCUs),
+                              st));
+    }
+    {
+      Prof pr("teacher_final", st);
+      KD_HIP(kd::launch_teacher_final(f32, t, at<int32_t>(ws, L.big), nbig, at<float>(ws, L.tau2),
+                                      std::min(rows, kTeacherFinalGroups), kTeacherBigGroups, st));
+    }
+  }
+  return KD_OK;
+}
+
 int kd_validate_topk(const kd_problem* p, const int32_t* ids, const void* tl, int64_t* n_bad_id,
                      int64_t* n_empty_row, int64_t* n_bad_logit, void* ws, size_t ws_bytes,
                      void* stream) {

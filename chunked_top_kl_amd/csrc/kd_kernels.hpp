@@ -6,7 +6,7 @@
 
 namespace kd {
 
-enum SweepKind { kSweepFwd = 0, kSweepBwdG = 1, kSweepEnt = 2 };
+enum SweepKind { kSweepFwd = 0, kSweepBwdG = 1, kSweepEnt = 2, kSweepPilot = 3, kSweepEmit = 4 };
 
 // Vocabulary-sweep projection (forward LSE + gather, backward gradient tile,
 // entropy). Rows are "launch rows" r in [0, rows): compacted row
@@ -32,6 +32,28 @@ struct SweepArgs {
   char* GT; int64_t ldgt;             // the same tile transposed [Vp, Cp]
   // entropy partials
   float* em; double* es; double* eu;
+  // teacher cache writer: pilot logits zp[v][r] (pitch ldp floats); per-row
+  // emission threshold te, append counter cnt and candidate lists cid / cz
+  // (row r at r * cap); ids are stored + id_offset
+  float* zp; int64_t ldp;
+  const float* te; int32_t* cnt; int32_t* cid; float* cz; int64_t cap; int id_offset;
+};
+
+constexpr int kTeacherWnormGroups = 1024;   // work-groups of the max ||w_v|| pass
+
+// entries per work-group of the teacher writer's large-band scratch (12 bytes each)
+__host__ __device__ inline int64_t teacher_scratch_entries(int64_t cap) { return (cap + 1) & ~int64_t(1); }
+
+struct TeacherArgs {
+  const char* X; int64_t ldx;         // the chunk's hidden rows (row 0 of the chunk)
+  const char* W; int64_t ldw;
+  int rows, H, V, K, P;               // P: pilot vocabulary rows [0, P)
+  const float* zp; int64_t ldp;       // pilot logits [P][ldp]
+  const double* wmax;                 // max over v of ||w_v||_2
+  float* te; double* bnd;             // per row: emission threshold, error bound
+  int32_t* cnt; int32_t* cid; float* cz; int64_t cap;
+  char* scratch;                      // per work-group: cap x (id, fp64) for large bands
+  int32_t* ids_out; char* logits_out; int out_bf16;  // the chunk's rows of the cache
 };
 
 struct CombineArgs {
@@ -110,6 +132,11 @@ hipError_t launch_prepass(const int32_t* ids, const void* tl, int tl_f32, int64_
 hipError_t launch_compact(const uint8_t* present, const uint8_t* mask, int64_t S, int32_t* idx,
                           int32_t* pos, int32_t* count, hipStream_t st);
 hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid, hipStream_t st);
+hipError_t launch_teacher_wnorm(int f32, const char* W, int64_t ldw, int V, int H, double* part,
+                                double* wmax, hipStream_t st);
+hipError_t launch_teacher_threshold(int f32, const TeacherArgs& a, int32_t* nbig, hipStream_t st);
+hipError_t launch_teacher_final(int f32, const TeacherArgs& a, int32_t* big, int32_t* nbig,
+                                float* tau2, int grid, int grid_big, hipStream_t st);
 hipError_t launch_grad_teacher(int f32, const GradTeacherArgs& a, hipStream_t st);
 int sweep_grid(int64_t rows_max, int V, int ncu);
 hipError_t launch_fwd_combine(const CombineArgs& a, hipStream_t st);

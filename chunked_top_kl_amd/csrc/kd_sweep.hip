@@ -5,7 +5,12 @@
 //  - backward: the logit gradient (softmax(z/T) - p)/T * g/N as a bf16 tile,
 //    with p scattered at the teacher ids ("backward recomputes the chunk");
 //  - entropy: online (max, sum, sum e*y) of softmax(z) for H(q_t)
-//    ("Rethinking Selective Knowledge Distillation", chunked entropy).
+//    ("Rethinking Selective Knowledge Distillation", chunked entropy);
+//  - teacher cache writer ("offline top-K logits": the teacher's logits are
+//    computed once and only each position's K largest kept): a pilot pass
+//    that stores the fp32 logits of the first vocabulary rows, and an emit
+//    pass that appends every logit at or above a per-row threshold to the
+//    row's candidate list (kd_teacher.hip picks the K from those).
 //
 // Orientation: MFMA rows (M) are vocabulary entries (A = W tile), MFMA columns
 // (N) are tokens (B = hidden rows). Each lane therefore owns whole token
@@ -324,6 +329,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
   int64_t cbase[4];
   int ccur[4];
   float lse2[4];
+  float tej[4];   // emission threshold of each token column (teacher cache writer)
   float coef = 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -341,6 +347,9 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
     }
     if constexpr (KIND == kSweepBwdG)
       lse2[j] = (tl0 + 32 * j < rows) ? a.lse[orow[j]] * kLog2e : 0.0f;
+    tej[j] = INFINITY;
+    if constexpr (KIND == kSweepEmit)
+      if (tl0 + 32 * j < rows) tej[j] = a.te[tl0 + 32 * j];
   }
   if constexpr (KIND == kSweepBwdG) {
     const int n = *a.nrows_dev;
@@ -395,6 +404,37 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
           if (tail && vw0 + acc_row(i, r, half) >= a.V) x = -INFINITY;
           z[i * 16 + r] = x;
         }
+
+      if constexpr (KIND == kSweepPilot) {
+        // pilot logits of this token column, stored transposed: the 32 lanes
+        // of a vocabulary row write 32 consecutive tokens
+        const int t = tl0 + 32 * j;
+        if (t < rows) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int v = vw0 + acc_row(i, r, half);
+              if (!tail || v < a.V) a.zp[(int64_t)v * a.ldp + t] = z[i * 16 + r];
+            }
+        }
+      }
+
+      if constexpr (KIND == kSweepEmit) {
+        // every logit at or above the row's threshold joins the row's
+        // candidate list (entries past V hold -inf; columns past the rows
+        // have an infinite threshold)
+        const int t = tl0 + 32 * j;
+#pragma unroll
+        for (int e = 0; e < 64; ++e) {
+          if (z[e] >= tej[j]) {
+            const int v = vw0 + acc_row(e >> 4, e & 15, half);
+            const int pos = atomicAdd(a.cnt + t, 1);
+            a.cid[(int64_t)t * a.cap + pos] = v + a.id_offset;
+            a.cz[(int64_t)t * a.cap + pos] = z[e];
+          }
+        }
+      }
 
       if constexpr (KIND == kSweepFwd) {
         float mx = -INFINITY;
@@ -500,7 +540,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
     }
   }
 
-  if constexpr (KIND == kSweepBwdG) return;
+  if constexpr (KIND == kSweepBwdG || KIND == kSweepPilot || KIND == kSweepEmit) return;
 
   // ---- end of sweep: merge lane halves, then the two waves sharing tokens
 #pragma unroll
@@ -586,6 +626,10 @@ KD_SWEEP_KERNEL(kd_fwd_lse_gather_f32, float, kSweepFwd, false)
 KD_SWEEP_KERNEL(kd_fwd_lse_gather_rows_f32, float, kSweepFwd, true)
 KD_SWEEP_KERNEL(kd_bwd_grad_tile_f32, float, kSweepBwdG, false)
 KD_SWEEP_KERNEL(kd_entropy_sweep_f32, float, kSweepEnt, false)
+KD_SWEEP_KERNEL(kd_teacher_pilot_bf16, __bf16, kSweepPilot, false)
+KD_SWEEP_KERNEL(kd_teacher_emit_bf16, __bf16, kSweepEmit, false)
+KD_SWEEP_KERNEL(kd_teacher_pilot_f32, float, kSweepPilot, false)
+KD_SWEEP_KERNEL(kd_teacher_emit_f32, float, kSweepEmit, false)
 #undef KD_SWEEP_KERNEL
 
 hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid, hipStream_t st) {
@@ -596,11 +640,15 @@ hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid
     if (kind == kSweepFwd && map) KD_SWEEP(kd_fwd_lse_gather_rows_bf16);
     else if (kind == kSweepFwd) KD_SWEEP(kd_fwd_lse_gather_bf16);
     else if (kind == kSweepBwdG) KD_SWEEP(kd_bwd_grad_tile_bf16);
+    else if (kind == kSweepPilot) KD_SWEEP(kd_teacher_pilot_bf16);
+    else if (kind == kSweepEmit) KD_SWEEP(kd_teacher_emit_bf16);
     else KD_SWEEP(kd_entropy_sweep_bf16);
   } else {
     if (kind == kSweepFwd && map) KD_SWEEP(kd_fwd_lse_gather_rows_f32);
     else if (kind == kSweepFwd) KD_SWEEP(kd_fwd_lse_gather_f32);
     else if (kind == kSweepBwdG) KD_SWEEP(kd_bwd_grad_tile_f32);
+    else if (kind == kSweepPilot) KD_SWEEP(kd_teacher_pilot_f32);
+    else if (kind == kSweepEmit) KD_SWEEP(kd_teacher_emit_f32);
     else KD_SWEEP(kd_entropy_sweep_f32);
   }
 #undef KD_SWEEP

@@ -1,0 +1,431 @@
+// Teacher top-K cache writer: the steps around the pilot and emit sweeps.
+//
+// "Making Knowledge Distillation Cheap Enough to Run at Scale" (as written up
+// by aibase.it), section "offline top-K logits": the teacher's output is
+// computed once and only the logits of each position's K most likely tokens
+// are cached; section "operations": the cache holds token ids and logits per
+// position, and its validation checks the top-K order. Softmax is monotone, so
+// the K most likely tokens are the K largest logits; the cache lists them by
+// logit descending, the lower id first among equal logits.
+//
+// For a chunk of rows:
+//  1. pilot sweep (kd_sweep.hip): fp32 logits of vocabulary rows [0, P) into
+//     zp[v][r];
+//  2. teacher_threshold_kernel: per row, tau = the K-th largest pilot logit
+//     (exact: radix select on order-preserving keys) and a bound B on
+//     |fp32 logit - exact logit|; the emission threshold te = tau - 2B, rounded
+//     down; the pilot logits >= te start the row's candidate list;
+//  3. emit sweep over [P, V): every logit >= te is appended;
+//  4. teacher_final_kernel: tau2 = the K-th largest candidate (fp32); the
+//     candidates with logit >= tau2 - 2B (the band) are recomputed in fp64 from
+//     the inputs and ranked by (logit desc, id asc); the first K are written,
+//     with their logits rounded from fp64 to fp32 (then to bf16 for a bf16
+//     cache). A row whose band exceeds the LDS list goes to
+//     teacher_final_big_kernel, which ranks it in global scratch.
+//
+// Why the result is the exact top K: with |z32 - z| <= B for every entry, the
+// pilot holds K entries with z >= tau - B, so the K-th largest exact logit
+// y_K >= tau - B and every top-K entry has z32 >= y_K - B >= te, i.e. it is a
+// candidate. The candidates hold K entries with z32 >= tau2, so y_K >= tau2 - B
+// and an entry with z32 < tau2 - 2B has z < y_K: it cannot be in the top K.
+// B = 1.01 (H + 16) 2^-23 ||h||_2 max_v ||w_v||_2 + H 2^-90: an fp32 sum of H
+// products with at most one rounding per term, each at most 2^-23 relative
+// (round to nearest gives 2^-24), |sum of |h_i w_i|| <= ||h|| ||w||
+// (Cauchy-Schwarz), and the last term covers products flushed to zero.
+#include "kd_common.hpp"
+#include "kd_kernels.hpp"
+
+namespace kd {
+
+constexpr int kBandLds = 4096;   // band entries ranked in LDS
+
+// order-preserving key of an fp32 value (larger value, larger key)
+__device__ inline uint32_t fkey(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline float funkey(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+template <typename T>
+__device__ inline double elem_f64(const char* row, int h) {
+  if constexpr (sizeof(T) == 2) return (double)bf16_to_f32(((const uint16_t*)row)[h]);
+  else return (double)((const float*)row)[h];
+}
+
+// exact fp64 dot product of two rows of H elements (16-byte loads)
+template <typename T>
+__device__ inline double dot_f64(const char* x, const char* w, int H) {
+  constexpr int per = 16 / (int)sizeof(T);
+  double acc = 0.0;
+  int h = 0;
+  for (; h + per <= H; h += per) {
+    const uint4 xr = *(const uint4*)(x + (int64_t)h * sizeof(T));
+    const uint4 wr = *(const uint4*)(w + (int64_t)h * sizeof(T));
+    const uint32_t* xd = (const uint32_t*)&xr;
+    const uint32_t* wd = (const uint32_t*)&wr;
+#pragma unroll
+    for (int e = 0; e < per; ++e) {
+      double xv, wv;
+      if constexpr (sizeof(T) == 2) {
+        xv = (double)bf16_to_f32((uint16_t)(xd[e >> 1] >> ((e & 1) * 16)));
+        wv = (double)bf16_to_f32((uint16_t)(wd[e >> 1] >> ((e & 1) * 16)));
+      } else {
+        xv = (double)__uint_as_float(xd[e]);
+        wv = (double)__uint_as_float(wd[e]);
+      }
+      acc = fma(xv, wv, acc);
+    }
+  }
+  for (; h < H; ++h) acc = fma(elem_f64<T>(x, h), elem_f64<T>(w, h), acc);
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
+// max over v of ||w_v||_2: one wave per row, per-work-group maxima, then one
+// work-group over those.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void teacher_wnorm_kernel(const char* W, int64_t ldw, int V, int H,
+                                                            double* part) {
+  __shared__ double best[4];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  double m = 0.0;
+  for (int v = blockIdx.x * 4 + wv; v < V; v += gridDim.x * 4) {
+    const char* row = W + (int64_t)v * ldw;
+    double ss = 0.0;
+    for (int h = lane; h < H; h += 64) {
+      const double x = elem_f64<T>(row, h);
+      ss = fma(x, x, ss);
+    }
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    m = fmax(m, ss);
+  }
+  if (lane == 0) best[wv] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    part[blockIdx.x] = fmax(fmax(best[0], best[1]), fmax(best[2], best[3]));
+}
+
+__global__ __launch_bounds__(256) void teacher_wnorm_final_kernel(const double* part, int n,
+                                                                  double* wmax) {
+  __shared__ double red[256];
+  double m = 0.0;
+  for (int i = threadIdx.x; i < n; i += 256) m = fmax(m, part[i]);
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + o]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) wmax[0] = sqrt(red[0]);
+}
+
+hipError_t launch_teacher_wnorm(int f32, const char* W, int64_t ldw, int V, int H, double* part,
+                                double* wmax, hipStream_t st) {
+  if (f32)
+    hipLaunchKernelGGL(teacher_wnorm_kernel<float>, dim3(kTeacherWnormGroups), dim3(256), 0, st, W, ldw,
+                       V, H, part);
+  else
+    hipLaunchKernelGGL(teacher_wnorm_kernel<__bf16>, dim3(kTeacherWnormGroups), dim3(256), 0, st, W, ldw,
+                       V, H, part);
+  hipLaunchKernelGGL(teacher_wnorm_final_kernel, dim3(1), dim3(256), 0, st, (const double*)part,
+                     kTeacherWnormGroups, wmax);
+  return hipGetLastError();
+}
+
+// the bound B on |fp32 logit - exact logit| of a row with ||h|| = hn
+__device__ inline double logit_bound(int H, double hn, double wmax) {
+  return 1.01 * (double)(H + 16) * 0x1p-23 * hn * wmax + (double)H * 0x1p-90;
+}
+
+// ---------------------------------------------------------------------------
+// Per-row threshold from the pilot logits; 64 rows per work-group. Thread
+// (row = tid & 63, part = tid >> 6) reads every fourth pilot entry of its row,
+// so the 64 threads of a part read 64 consecutive rows of one zp line. The
+// K-th largest key is found digit by digit (4 passes of 8 bits, MSB first)
+// from per-row LDS histograms.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void teacher_threshold_kernel(TeacherArgs a, int32_t* nbig) {
+  __shared__ uint32_t hist[64][256];
+  __shared__ uint32_t prefix[64];
+  __shared__ int krem[64], lcnt[64];
+  __shared__ double nrm[4][64];
+  __shared__ float tes[64];
+  const int tid = threadIdx.x, row = tid & 63, part = tid >> 6;
+  const int r0 = blockIdx.x * 64, r = r0 + row;
+  const bool live = r < a.rows;
+  if (blockIdx.x == 0 && tid == 0) *nbig = 0;
+  {
+    double ss = 0.0;
+    if (live) {
+      const char* x = a.X + (int64_t)r * a.ldx;
+      for (int h = part; h < a.H; h += 4) {
+        const double v = elem_f64<T>(x, h);
+        ss = fma(v, v, ss);
+      }
+    }
+    nrm[part][row] = ss;
+  }
+  if (tid < 64) {
+    prefix[tid] = 0u;
+    krem[tid] = a.K;
+    lcnt[tid] = 0;
+  }
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t hmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    __syncthreads();
+    for (int q = tid; q < 64 * 256; q += 256) (&hist[0][0])[q] = 0u;
+    __syncthreads();
+    if (live) {
+      const uint32_t pre = prefix[row];
+      for (int v = part; v < a.P; v += 4) {
+        const uint32_t key = fkey(a.zp[(int64_t)v * a.ldp + r]);
+        if ((key & hmask) == pre) atomicAdd(&hist[row][(key >> shift) & 255u], 1u);
+      }
+    }
+    __syncthreads();
+    if (tid < 64 && r0 + tid < a.rows) {
+      int k = krem[tid];
+      int d = 255;
+      for (; d > 0; --d) {
+        const int c = (int)hist[tid][d];
+        if (c >= k) break;
+        k -= c;
+      }
+      prefix[tid] |= (uint32_t)d << shift;
+      krem[tid] = k;
+    }
+  }
+  __syncthreads();
+  if (tid < 64 && r0 + tid < a.rows) {
+    const float tau = funkey(prefix[tid]);
+    const double hn = sqrt(nrm[0][tid] + nrm[1][tid] + nrm[2][tid] + nrm[3][tid]);
+    const double b = logit_bound(a.H, hn, a.wmax[0]);
+    // rounded down: the margins exceed the rounding of the fp32 result
+    const double t = (double)tau - 2.0 * b * (1.0 + 0x1p-20) - fabs((double)tau) * 0x1p-22;
+    tes[tid] = (float)t;
+    a.te[r0 + tid] = (float)t;
+    a.bnd[r0 + tid] = b;
+  }
+  __syncthreads();
+  // the pilot entries at or above the threshold start the candidate list
+  if (live) {
+    const float te = tes[row];
+    int32_t* cid = a.cid + (int64_t)r * a.cap;
+    float* cz = a.cz + (int64_t)r * a.cap;
+    for (int v = part; v < a.P; v += 4) {
+      const float z = a.zp[(int64_t)v * a.ldp + r];
+      if (z >= te) {
+        const int pos = atomicAdd(&lcnt[row], 1);
+        cid[pos] = v;
+        cz[pos] = z;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 64 && r0 + tid < a.rows) a.cnt[r0 + tid] = lcnt[tid];
+}
+
+// K-th largest key among n fp32 values (one work-group; every thread returns it)
+__device__ inline uint32_t kth_largest_key(const float* z, int n, int K, uint32_t* hist,
+                                           uint32_t* s_prefix, int* s_krem) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    *s_prefix = 0u;
+    *s_krem = K;
+  }
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t hmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    __syncthreads();
+    hist[tid] = 0u;
+    __syncthreads();
+    const uint32_t pre = *s_prefix;
+    for (int i = tid; i < n; i += 256) {
+      const uint32_t key = fkey(z[i]);
+      if ((key & hmask) == pre) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int k = *s_krem;
+      int d = 255;
+      for (; d > 0; --d) {
+        const int c = (int)hist[d];
+        if (c >= k) break;
+        k -= c;
+      }
+      *s_prefix = pre | ((uint32_t)d << shift);
+      *s_krem = k;
+    }
+  }
+  __syncthreads();
+  return *s_prefix;
+}
+
+__device__ inline void write_entry(const TeacherArgs& a, int r, int rank, int id, double z) {
+  const int64_t o = (int64_t)r * a.K + rank;
+  a.ids_out[o] = id;
+  const float f = (float)z;   // round to nearest even
+  if (a.out_bf16) ((uint16_t*)a.logits_out)[o] = (uint16_t)f32_to_bf16_bits(f);
+  else ((float*)a.logits_out)[o] = f;
+}
+
+// ---------------------------------------------------------------------------
+// Final ranking: one work-group per row (persistent over rows).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void teacher_final_kernel(TeacherArgs a, int32_t* big,
+                                                            int32_t* nbig, float* tau2_out) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_krem, s_m;
+  __shared__ int lid[kBandLds];
+  __shared__ double lz[kBandLds];
+  const int tid = threadIdx.x;
+  for (int r = blockIdx.x; r < a.rows; r += gridDim.x) {
+    const int n = a.cnt[r];
+    const int32_t* cid = a.cid + (int64_t)r * a.cap;
+    const float* cz = a.cz + (int64_t)r * a.cap;
+    const float tau2 = funkey(kth_largest_key(cz, n, a.K, hist, &s_prefix, &s_krem));
+    const double thr = (double)tau2 - 2.0 * a.bnd[r];
+    if (tid == 0) s_m = 0;
+    __syncthreads();
+    // the band; a row with more than kBandLds entries is ranked by the
+    // second kernel (its list here is abandoned once full)
+    for (int i = tid; i < n; i += 256) {
+      if ((double)cz[i] >= thr) {
+        const int pos = atomicAdd(&s_m, 1);
+        if (pos < kBandLds) lid[pos] = cid[i];
+      }
+    }
+    __syncthreads();
+    const int m = s_m;
+    if (m > kBandLds) {
+      if (tid == 0) {
+        big[atomicAdd(nbig, 1)] = r;
+        tau2_out[r] = tau2;
+      }
+      __syncthreads();
+      continue;
+    }
+    const char* x = a.X + (int64_t)r * a.ldx;
+    for (int e = tid; e < m; e += 256) lz[e] = dot_f64<T>(x, a.W + (int64_t)lid[e] * a.ldw, a.H);
+    __syncthreads();
+    // rank by (logit desc, id asc); ids are distinct, so ranks are
+    for (int e = tid; e < m; e += 256) {
+      const double ze = lz[e];
+      const int ie = lid[e];
+      int rank = 0;
+      for (int f = 0; f < m; ++f) {
+        const double zf = lz[f];
+        rank += (zf > ze || (zf == ze && lid[f] < ie)) ? 1 : 0;
+      }
+      if (rank < a.K) write_entry(a, r, rank, ie, ze);
+    }
+    __syncthreads();
+  }
+}
+
+// Rows whose band exceeds the LDS list (many logits equal to within the
+// bound): the band goes to this work-group's scratch and the K entries are
+// taken by K rounds of arg-max over it.
+template <typename T>
+__global__ __launch_bounds__(256) void teacher_final_big_kernel(TeacherArgs a, const int32_t* big,
+                                                                const int32_t* nbig,
+                                                                const float* tau2_in) {
+  __shared__ int s_m;
+  __shared__ double rz[256];
+  __shared__ int ri[256], rp[256];
+  const int tid = threadIdx.x;
+  // this work-group's scratch: capE ids, then capE fp64 logits (capE even, so
+  // the fp64 array stays 8-byte aligned)
+  const int64_t capE = teacher_scratch_entries(a.cap);
+  int32_t* sid = (int32_t*)(a.scratch + (int64_t)blockIdx.x * capE * 12);
+  double* sz = (double*)(a.scratch + (int64_t)blockIdx.x * capE * 12 + capE * 4);
+  const int nb = *nbig;
+  for (int q = blockIdx.x; q < nb; q += gridDim.x) {
+    const int r = big[q];
+    const int n = a.cnt[r];
+    const int32_t* cid = a.cid + (int64_t)r * a.cap;
+    const float* cz = a.cz + (int64_t)r * a.cap;
+    const double thr = (double)tau2_in[r] - 2.0 * a.bnd[r];
+    if (tid == 0) s_m = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) {
+      if ((double)cz[i] >= thr) sid[atomicAdd(&s_m, 1)] = cid[i];
+    }
+    __syncthreads();
+    const int m = s_m;
+    const char* x = a.X + (int64_t)r * a.ldx;
+    for (int e = tid; e < m; e += 256) sz[e] = dot_f64<T>(x, a.W + (int64_t)sid[e] * a.ldw, a.H);
+    __syncthreads();
+    for (int k = 0; k < a.K; ++k) {
+      double bz = -INFINITY;
+      int bi = 0x7FFFFFFF, bp = -1;
+      for (int e = tid; e < m; e += 256) {
+        const int ie = sid[e];
+        if (ie < 0) continue;   // taken
+        const double ze = sz[e];
+        if (bp < 0 || ze > bz || (ze == bz && ie < bi)) {
+          bz = ze;
+          bi = ie;
+          bp = e;
+        }
+      }
+      rz[tid] = bz;
+      ri[tid] = bi;
+      rp[tid] = bp;
+      __syncthreads();
+      for (int o = 128; o > 0; o >>= 1) {
+        if (tid < o) {
+          const int p2 = rp[tid + o];
+          if (p2 >= 0 && (rp[tid] < 0 || rz[tid + o] > rz[tid] ||
+                          (rz[tid + o] == rz[tid] && ri[tid + o] < ri[tid]))) {
+            rz[tid] = rz[tid + o];
+            ri[tid] = ri[tid + o];
+            rp[tid] = p2;
+          }
+        }
+        __syncthreads();
+      }
+      if (tid == 0) {
+        write_entry(a, r, k, ri[0], rz[0]);
+        sid[rp[0]] = -1;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+hipError_t launch_teacher_threshold(int f32, const TeacherArgs& a, int32_t* nbig, hipStream_t st) {
+  const int grid = (int)ceil_div(a.rows, 64);
+  if (grid <= 0) return hipSuccess;
+  if (f32)
+    hipLaunchKernelGGL(teacher_threshold_kernel<float>, dim3(grid), dim3(256), 0, st, a, nbig);
+  else
+    hipLaunchKernelGGL(teacher_threshold_kernel<__bf16>, dim3(grid), dim3(256), 0, st, a, nbig);
+  return hipGetLastError();
+}
+
+hipError_t launch_teacher_final(int f32, const TeacherArgs& a, int32_t* big, int32_t* nbig,
+                                float* tau2, int grid, int grid_big, hipStream_t st) {
+  if (a.rows <= 0) return hipSuccess;
+  if (f32) {
+    hipLaunchKernelGGL(teacher_final_kernel<float>, dim3(grid), dim3(256), 0, st, a, big, nbig,
+                       tau2);
+    hipLaunchKernelGGL(teacher_final_big_kernel<float>, dim3(grid_big), dim3(256), 0, st, a,
+                       (const int32_t*)big, (const int32_t*)nbig, (const float*)tau2);
+  } else {
+    hipLaunchKernelGGL(teacher_final_kernel<__bf16>, dim3(grid), dim3(256), 0, st, a, big, nbig,
+                       tau2);
+    hipLaunchKernelGGL(teacher_final_big_kernel<__bf16>, dim3(grid_big), dim3(256), 0, st, a,
+                       (const int32_t*)big, (const int32_t*)nbig, (const float*)tau2);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kd

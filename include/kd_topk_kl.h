@@ -175,6 +175,30 @@ int kd_validate_topk(const kd_problem* problem, const int32_t* topk_ids, const v
                      int64_t* n_bad_id, int64_t* n_empty_row, int64_t* n_bad_logit,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* Teacher top-K cache writer ("offline top-K logits": the teacher's output
+ * is computed once and only each position's K most likely tokens are kept;
+ * "operations": the cache stores token ids and logits per position, in top-K
+ * order). For every position t: the K entries of largest teacher logit
+ * z_tv = h_t . w_v, ordered by logit descending, the lower id first among
+ * equal logits. The choice is exact: logits near the K-th largest are
+ * recomputed in fp64 from the inputs before the decision, so the entries are
+ * the ones an fp64 evaluation selects, and every logit written is that fp64
+ * value rounded to fp32 (then to bf16 for a bf16 cache). The [S,V] logit grid
+ * is never stored: problem->chunk positions are processed at a time.
+ *   hidden      [device] [S,H] hw_dtype: the teacher's final hidden states
+ *   W           [device] [V,H] hw_dtype: the teacher's output projection
+ *   topk_ids    [device] [S,K] int32 output
+ *   topk_logits [device] [S,K] tl_dtype output (raw logits: the temperature
+ *               is stored with the cache by the caller and not used here)
+ *   ws          at least kd_teacher_topk_workspace_bytes(problem) bytes (this
+ *               entry point does not use kd_topk_kl_workspace_bytes).
+ * Inputs must be finite. Logits that are equal to within the fp32 rounding
+ * bound take longer (a slower ranking path), not a different result.       */
+size_t kd_teacher_topk_workspace_bytes(const kd_problem* problem);
+int kd_teacher_topk(const kd_problem* problem, const void* hidden, const void* W,
+                    int32_t* topk_ids, void* topk_logits, void* ws, size_t ws_bytes,
+                    void* stream);
+
 /* Kernel timing (off by default). When on, every kernel the library enqueues
  * is bracketed by HIP events on the same stream. kd_profile_read synchronises
  * those events and reports, per kernel name, the number of launches and the
