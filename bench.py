@@ -101,14 +101,18 @@ def run_c5_step(kd, torch, wl, t, ws):
     return run_step(kd, torch, wl, t, ws, mask=mask), cnt
 
 
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(p, wl, rows):
     """fp64 oracle forward+backward on the first `rows` positions of the same workload."""
     from oracle import oracle_loss_grads
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    threads = blas_threads()
     t0 = time.perf_counter()
     oracle_loss_grads(p.hidden[:rows], p.W, p.ids[:rows], p.tlogits[:rows], T=wl["T"], chunk=128)
     dt = time.perf_counter() - t0
@@ -142,6 +146,68 @@ def chunk_sweep(kd, torch, wl, t, chunks, steps=3, warmup=1):
                            workspace_gib=round(ws.numel() / 2**30, 3))
         log(f"[bench] chunk {C}: {ms:.2f} ms/step, peak {out[str(C)]['peak_gib']} GiB")
         del ws
+    return out
+
+
+def teacher_leg(kd, torch, wl, t, p, steps=3, warmup=1, cpu_rows=64, cpu=True):
+    """Teacher top-K cache writer at the workload's shapes: the workload's
+    hidden rows and W stand in for the teacher's. Counted work: 2*S*H*V FLOP
+    (a pilot pass over the first vocabulary rows and an emit pass over the rest
+    cover the vocabulary once)."""
+    S, H, V, K, C = wl["S"], wl["H"], wl["V"], wl["K"], wl["chunk"]
+    hidden, W = t[0], t[1]
+    prob = kd.make_problem(S, H, V, K, C, 1.0, kd.KD_BF16, kd.KD_BF16)
+    ws = torch.empty(kd.kd_teacher_topk_workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        kd.kd_teacher_topk(hidden, W, K, chunk=C, workspace=ws)
+    torch.cuda.synchronize()
+    kd.kd_profile_reset()
+    kd.kd_profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ids, logits = kd.kd_teacher_topk(hidden, W, K, chunk=C, workspace=ws)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kd.kd_profile_enable(False)
+    prof = kd.kd_profile_read()
+    kd.kd_profile_reset()
+    ms = dt * 1000.0 / steps
+    P = min(V, 16384)
+    kernels = {}
+    for name, (n, tot) in prof.items():
+        per = tot / max(n, 1)
+        f = None
+        if name == "teacher_pilot":
+            f = 2.0 * S * H * P / (n / steps)
+        elif name == "teacher_emit":
+            f = 2.0 * S * H * (V - P) / (n / steps)
+        kernels[name] = dict(launches_per_step=round(n / steps, 2), ms_per_step=round(tot / steps, 4),
+                             avg_ms=round(per, 5),
+                             tflops=(round(f / (per / 1000.0) / 1e12, 1) if f else None))
+    em = kernels.get("teacher_emit")
+    roofline = None
+    if em:
+        f = 2.0 * S * H * (V - P) / em["launches_per_step"]
+        a = f / (em["avg_ms"] / 1000.0) / 1e12
+        roofline = dict(kernel="teacher_emit", bound="mfma", achieved=round(a, 1),
+                        peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=round(a / PEAK_BF16_TFLOPS, 4),
+                        flops_per_launch=f, avg_ms=em["avg_ms"])
+    out = dict(workload=f"teacher cache writer at {wl['name']} (synthetic teacher = the workload's hidden and W)",
+               ms=round(ms, 3), tokens_per_s=round(S / (ms / 1000.0), 1),
+               mfma_frac=round(2.0 * S * H * V / (ms / 1000.0) / (PEAK_BF16_TFLOPS * 1e12), 4),
+               workspace_gib=round(ws.numel() / 2**30, 3), roofline=roofline, kernels=kernels)
+    log(f"[bench] teacher cache writer: {ms:.2f} ms, {out['tokens_per_s']:.0f} tokens/s")
+    del ws, ids, logits
+    torch.cuda.empty_cache()
+    if cpu:
+        from oracle import oracle_teacher_topk
+        t0 = time.perf_counter()
+        oracle_teacher_topk(p.hidden[:cpu_rows], p.W, K, out_dtype="bf16")
+        d = time.perf_counter() - t0
+        out["cpu_baseline"] = dict(value=cpu_rows / d, unit="tokens/s", cores=blas_threads(),
+                                   kind="oracle",
+                                   sample=f"first {cpu_rows} positions (full H and V): fp64 logits and "
+                                          f"the sorted top-{K}; {d:.1f} s")
     return out
 
 
@@ -195,6 +261,8 @@ def main():
     ap.add_argument("--mem-sizes", default="16384,32768,65536,131072,262144")
     ap.add_argument("--no-chunk-sweep", action="store_true",
                     help="skip the fwd+bwd timing and peak memory at chunks 512/1024/2048")
+    ap.add_argument("--no-teacher", action="store_true",
+                    help="skip the teacher top-K cache writer leg")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -316,6 +384,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_chunk_sweep and args.workload == "c3":
         result["chunk_sweep"] = chunk_sweep(kd, torch, wl, t, [512, 1024, 2048])
+    if not args.no_teacher and args.workload == "c3":
+        result["teacher_topk"] = teacher_leg(kd, torch, wl, t, p, cpu=not args.no_cpu_baseline)
     if not args.no_mem_sweep:
         sizes = [int(x) for x in args.mem_sizes.split(",") if x]
         del t

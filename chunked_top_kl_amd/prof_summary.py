@@ -53,7 +53,14 @@ STEP_PATTERNS = [
     ("transpose_w", "transpose_w"),
     ("select_threshold", "select_threshold"),
     ("refine_kernel", "select_refine_fp64"),
+    ("band_rows_f64", "select_refine_fp64"),
     ("select_final", "select_final"),
+    ("kd_teacher_pilot", "teacher_pilot"),
+    ("kd_teacher_emit", "teacher_emit"),
+    ("teacher_threshold_kernel", "teacher_threshold"),
+    ("teacher_final_kernel", "teacher_final"),
+    ("teacher_final_big_kernel", "teacher_final"),
+    ("teacher_wnorm", "teacher_wnorm"),
     ("validate_kernel", "validate"),
     ("zero_u64_kernel", "validate"),
     ("copyBuffer", "device_copy"),
