@@ -571,11 +571,11 @@ int kd_select_top_fraction(const kd_problem* p, const void* hidden, const void* 
 
 // ------------------------------------------------------------------ teacher cache writer
 constexpr int64_t kPilotRows = 16384;      // vocabulary rows of the pilot pass
-constexpr int kTeacherFinalGroups = 512;   // work-groups of the final ranking
+constexpr int kTeacherFinalGroups = 4096;  // work-groups of the final ranking (one per row of a chunk up to this)
 constexpr int kTeacherBigGroups = 16;      // work-groups (and scratch areas) for large bands
 
 struct TeacherLayout {
-  int64_t C, P, ldp, cap;
+  int64_t C, P, NG, ldp, cap;   // P pilot vocabulary rows, NG groups of 16 of them
   size_t zp, cid, cz, cnt, te, bnd, tau2, big, nbig, wpart, wmax, scratch, total;
 };
 
@@ -584,6 +584,7 @@ TeacherLayout plan_teacher(const kd_problem* p) {
   const int64_t S = p->S, V = p->V;
   L.C = std::min<int64_t>(p->chunk, std::max<int64_t>(S, 1));
   L.P = std::min<int64_t>(V, kPilotRows);
+  L.NG = kd::ceil_div(L.P, kd::kTile) * 16;
   L.ldp = kd::round_up(L.C, 64);
   L.cap = V;   // a row's candidates are distinct vocabulary entries
   size_t off = 0;
@@ -592,7 +593,7 @@ TeacherLayout plan_teacher(const kd_problem* p) {
     off += (size_t)kd::round_up((int64_t)bytes, 256);
     return o;
   };
-  L.zp = take((size_t)L.P * L.ldp * 4);
+  L.zp = take((size_t)L.NG * L.ldp * 4);
   L.cid = take((size_t)L.C * L.cap * 4);
   L.cz = take((size_t)L.C * L.cap * 4);
   L.cnt = take((size_t)L.C * 4);
@@ -665,7 +666,7 @@ int kd_teacher_topk(const kd_problem* p, const void* hidden, const void* W, int3
     t.H = H;
     t.V = V;
     t.K = K;
-    t.P = P;
+    t.P = (int)L.NG;
     t.zp = at<float>(ws, L.zp);
     t.ldp = L.ldp;
     t.wmax = at<double>(ws, L.wmax);
@@ -684,19 +685,17 @@ int kd_teacher_topk(const kd_problem* p, const void* hidden, const void* W, int3
       Prof pr("teacher_threshold", st);
       KD_HIP(kd::launch_teacher_threshold(f32, t, nbig, st));
     }
-    if (V > P) {
+    {
       kd::SweepArgs e = a;
-      e.W = (const char*)W + (int64_t)P * ld;
-      e.V = V - P;
+      e.V = V;
       e.te = t.te;
       e.cnt = t.cnt;
       e.cid = t.cid;
       e.cz = t.cz;
       e.cap = t.cap;
-      e.id_offset = P;
+      e.id_offset = 0;
       Prof pr("teacher_emit", st);
-      KD_HIP(kd::launch_sweep(kd::kSweepEmit, f32, 0, e, kd::sweep_grid(rows, V - P, kCostCUs),
-                              st));
+      KD_HIP(kd::launch_sweep(kd::kSweepEmit, f32, 0, e, kd::sweep_grid(rows, V, kCostCUs), st));
     }
     {
       Prof pr("teacher_final", st);

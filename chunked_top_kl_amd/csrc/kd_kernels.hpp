@@ -32,7 +32,7 @@ struct SweepArgs {
   char* GT; int64_t ldgt;             // the same tile transposed [Vp, Cp]
   // entropy partials
   float* em; double* es; double* eu;
-  // teacher cache writer: pilot logits zp[v][r] (pitch ldp floats); per-row
+  // teacher cache writer: pilot group maxima zp[g][r] (pitch ldp floats); per-row
   // emission threshold te, append counter cnt and candidate lists cid / cz
   // (row r at r * cap); ids are stored + id_offset
   float* zp; int64_t ldp;
@@ -47,8 +47,8 @@ __host__ __device__ inline int64_t teacher_scratch_entries(int64_t cap) { return
 struct TeacherArgs {
   const char* X; int64_t ldx;         // the chunk's hidden rows (row 0 of the chunk)
   const char* W; int64_t ldw;
-  int rows, H, V, K, P;               // P: pilot vocabulary rows [0, P)
-  const float* zp; int64_t ldp;       // pilot logits [P][ldp]
+  int rows, H, V, K, P;               // P: groups of the pilot (rows of zp)
+  const float* zp; int64_t ldp;       // pilot group maxima [P][ldp]
   const double* wmax;                 // max over v of ||w_v||_2
   float* te; double* bnd;             // per row: emission threshold, error bound
   int32_t* cnt; int32_t* cid; float* cz; int64_t cap;

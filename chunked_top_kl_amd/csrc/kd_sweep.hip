@@ -8,9 +8,9 @@
 //    ("Rethinking Selective Knowledge Distillation", chunked entropy);
 //  - teacher cache writer ("offline top-K logits": the teacher's logits are
 //    computed once and only each position's K largest kept): a pilot pass
-//    that stores the fp32 logits of the first vocabulary rows, and an emit
-//    pass that appends every logit at or above a per-row threshold to the
-//    row's candidate list (kd_teacher.hip picks the K from those).
+//    that stores the maxima of groups of 16 logits of the first vocabulary
+//    rows, and an emit pass that appends every logit at or above a per-row
+//    threshold to the row's candidate list (kd_teacher.hip picks the K).
 //
 // Orientation: MFMA rows (M) are vocabulary entries (A = W tile), MFMA columns
 // (N) are tokens (B = hidden rows). Each lane therefore owns whole token
@@ -406,32 +406,51 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
         }
 
       if constexpr (KIND == kSweepPilot) {
-        // pilot logits of this token column, stored transposed: the 32 lanes
-        // of a vocabulary row write 32 consecutive tokens
+        // the maximum of each group of 16 logits this lane holds (block i of
+        // the lane's half tile), stored transposed: group
+        // vt*16 + wm*8 + 2i + half, the 32 lanes of a group row writing 32
+        // consecutive tokens. Entries past V hold -inf.
         const int t = tl0 + 32 * j;
         if (t < rows) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i) {
+            float gmx = z[i * 16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int v = vw0 + acc_row(i, r, half);
-              if (!tail || v < a.V) a.zp[(int64_t)v * a.ldp + t] = z[i * 16 + r];
-            }
+            for (int r = 1; r < 16; ++r) gmx = fmaxf(gmx, z[i * 16 + r]);
+            const int g = vt * 16 + wm * 8 + 2 * i + half;
+            a.zp[(int64_t)g * a.ldp + t] = gmx;
+          }
         }
       }
 
       if constexpr (KIND == kSweepEmit) {
         // every logit at or above the row's threshold joins the row's
-        // candidate list (entries past V hold -inf; columns past the rows
-        // have an infinite threshold)
+        // candidate list (columns past the rows have an infinite threshold).
+        // Entries past V are tested explicitly: they hold -inf, which a
+        // threshold of -inf (a row with fewer pilot groups than K) admits.
+        // The lane's hits are counted first and their slots reserved with one
+        // atomic, so the hits of a column do not each wait for a round trip.
         const int t = tl0 + 32 * j;
+        int nh = 0;
 #pragma unroll
         for (int e = 0; e < 64; ++e) {
-          if (z[e] >= tej[j]) {
+          const int v = vw0 + acc_row(e >> 4, e & 15, half);
+          nh += (z[e] >= tej[j] && (!tail || v < a.V)) ? 1 : 0;
+        }
+        if (nh > 0) {
+          int pos = atomicAdd(a.cnt + t, nh);
+          int32_t* cid = a.cid + (int64_t)t * a.cap;
+          float* cz = a.cz + (int64_t)t * a.cap;
+#pragma unroll
+          for (int e = 0; e < 64; ++e) {
             const int v = vw0 + acc_row(e >> 4, e & 15, half);
-            const int pos = atomicAdd(a.cnt + t, 1);
-            a.cid[(int64_t)t * a.cap + pos] = v + a.id_offset;
-            a.cz[(int64_t)t * a.cap + pos] = z[e];
+            if (z[e] >= tej[j] && (!tail || v < a.V)) {
+              if (pos < a.cap) {   // always: a row emits each vocabulary entry once
+                cid[pos] = v + a.id_offset;
+                cz[pos] = z[e];
+              }
+              ++pos;
+            }
           }
         }
       }

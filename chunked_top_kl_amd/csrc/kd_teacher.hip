@@ -9,13 +9,13 @@
 // logit descending, the lower id first among equal logits.
 //
 // For a chunk of rows:
-//  1. pilot sweep (kd_sweep.hip): fp32 logits of vocabulary rows [0, P) into
-//     zp[v][r];
-//  2. teacher_threshold_kernel: per row, tau = the K-th largest pilot logit
-//     (exact: radix select on order-preserving keys) and a bound B on
-//     |fp32 logit - exact logit|; the emission threshold te = tau - 2B, rounded
-//     down; the pilot logits >= te start the row's candidate list;
-//  3. emit sweep over [P, V): every logit >= te is appended;
+//  1. pilot sweep (kd_sweep.hip) over vocabulary rows [0, P): the maximum of
+//     each group of 16 fp32 logits, gm[g][r];
+//  2. teacher_threshold_kernel: per row, tau = the K-th largest group maximum
+//     (exact: radix select on order-preserving keys; -inf when the row has
+//     fewer than K groups) and a bound B on |fp32 logit - exact logit|; the
+//     emission threshold te = tau - 2B, rounded down;
+//  3. emit sweep over [0, V): every logit >= te joins the row's candidates;
 //  4. teacher_final_kernel: tau2 = the K-th largest candidate (fp32); the
 //     candidates with logit >= tau2 - 2B (the band) are recomputed in fp64 from
 //     the inputs and ranked by (logit desc, id asc); the first K are written,
@@ -23,10 +23,10 @@
 //     cache). A row whose band exceeds the LDS list goes to
 //     teacher_final_big_kernel, which ranks it in global scratch.
 //
-// Why the result is the exact top K: with |z32 - z| <= B for every entry, the
-// pilot holds K entries with z >= tau - B, so the K-th largest exact logit
-// y_K >= tau - B and every top-K entry has z32 >= y_K - B >= te, i.e. it is a
-// candidate. The candidates hold K entries with z32 >= tau2, so y_K >= tau2 - B
+// Why the result is the exact top K: with |z32 - z| <= B for every entry (in
+// either pass), K groups have a maximum >= tau, so K entries have z >= tau - B:
+// the K-th largest exact logit y_K >= tau - B and every top-K entry has
+// z32 >= y_K - B >= te, i.e. it is a candidate (and so are those K entries). The candidates hold K entries with z32 >= tau2, so y_K >= tau2 - B
 // and an entry with z32 < tau2 - 2B has z < y_K: it cannot be in the top K.
 // B = 1.01 (H + 16) 2^-23 ||h||_2 max_v ||w_v||_2 + H 2^-90: an fp32 sum of H
 // products with at most one rounding per term, each at most 2^-23 relative
@@ -37,7 +37,7 @@
 
 namespace kd {
 
-constexpr int kBandLds = 4096;   // band entries ranked in LDS
+constexpr int kBandLds = 1024;   // band entries ranked in LDS (a larger band goes to the second kernel)
 
 // order-preserving key of an fp32 value (larger value, larger key)
 __device__ inline uint32_t fkey(float f) {
@@ -54,32 +54,62 @@ __device__ inline double elem_f64(const char* row, int h) {
   else return (double)((const float*)row)[h];
 }
 
-// exact fp64 dot product of two rows of H elements (16-byte loads)
+// the part of an fp64 dot product that lane `sub` of `nsub` takes (16-byte
+// granules sub, sub + nsub, ...; H is a multiple of the granule). The loads
+// of 8 granules are issued before their FMAs, so the loop waits for memory
+// once per 8 granules rather than once per granule.
 template <typename T>
-__device__ inline double dot_f64(const char* x, const char* w, int H) {
+__device__ inline double dot_f64_part(const char* x, const char* w, int H, int sub, int nsub) {
   constexpr int per = 16 / (int)sizeof(T);
+  constexpr int U = 8;
+  const int ng = H / per;              // granules in a row
   double acc = 0.0;
-  int h = 0;
-  for (; h + per <= H; h += per) {
-    const uint4 xr = *(const uint4*)(x + (int64_t)h * sizeof(T));
-    const uint4 wr = *(const uint4*)(w + (int64_t)h * sizeof(T));
-    const uint32_t* xd = (const uint32_t*)&xr;
-    const uint32_t* wd = (const uint32_t*)&wr;
+  for (int g0 = sub; g0 < ng; g0 += U * nsub) {
+    uint4 xr[U], wr[U];
 #pragma unroll
-    for (int e = 0; e < per; ++e) {
-      double xv, wv;
-      if constexpr (sizeof(T) == 2) {
-        xv = (double)bf16_to_f32((uint16_t)(xd[e >> 1] >> ((e & 1) * 16)));
-        wv = (double)bf16_to_f32((uint16_t)(wd[e >> 1] >> ((e & 1) * 16)));
-      } else {
-        xv = (double)__uint_as_float(xd[e]);
-        wv = (double)__uint_as_float(wd[e]);
+    for (int u = 0; u < U; ++u) {
+      const int g = g0 + u * nsub;
+      const int gg = g < ng ? g : 0;   // past the row: a valid granule, not used
+      xr[u] = *(const uint4*)(x + (int64_t)gg * 16);
+      wr[u] = *(const uint4*)(w + (int64_t)gg * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (g0 + u * nsub >= ng) break;
+      const uint32_t* xd = (const uint32_t*)&xr[u];
+      const uint32_t* wd = (const uint32_t*)&wr[u];
+#pragma unroll
+      for (int e = 0; e < per; ++e) {
+        double xv, wv;
+        if constexpr (sizeof(T) == 2) {
+          xv = (double)bf16_to_f32((uint16_t)(xd[e >> 1] >> ((e & 1) * 16)));
+          wv = (double)bf16_to_f32((uint16_t)(wd[e >> 1] >> ((e & 1) * 16)));
+        } else {
+          xv = (double)__uint_as_float(xd[e]);
+          wv = (double)__uint_as_float(wd[e]);
+        }
+        acc = fma(xv, wv, acc);
       }
-      acc = fma(xv, wv, acc);
     }
   }
-  for (; h < H; ++h) acc = fma(elem_f64<T>(x, h), elem_f64<T>(w, h), acc);
   return acc;
+}
+
+// fp64 logits of n listed vocabulary entries of one row: 8 lanes per entry,
+// their parts added in a fixed order
+template <typename T>
+__device__ inline void band_logits(const char* x, const TeacherArgs& a, const int32_t* ids,
+                                   double* out, int n) {
+  const int tid = threadIdx.x, grp = tid >> 3, sub = tid & 7;
+  for (int e0 = 0; e0 < n; e0 += 32) {
+    const int e = e0 + grp;
+    double d = 0.0;
+    if (e < n) d = dot_f64_part<T>(x, a.W + (int64_t)ids[e] * a.ldw, a.H, sub, 8);
+    d += __shfl_xor(d, 1);
+    d += __shfl_xor(d, 2);
+    d += __shfl_xor(d, 4);
+    if (e < n && sub == 0) out[e] = d;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -141,54 +171,54 @@ __device__ inline double logit_bound(int H, double hn, double wmax) {
 }
 
 // ---------------------------------------------------------------------------
-// Per-row threshold from the pilot logits; 64 rows per work-group. Thread
-// (row = tid & 63, part = tid >> 6) reads every fourth pilot entry of its row,
-// so the 64 threads of a part read 64 consecutive rows of one zp line. The
+// Per-row threshold from the pilot's group maxima (a.P groups); 16 rows per
+// work-group, thread (row = tid & 15, sub = tid >> 4) reads every 16th group of
+// its row, so 16 consecutive threads read 16 consecutive rows of a gm line. The
 // K-th largest key is found digit by digit (4 passes of 8 bits, MSB first)
 // from per-row LDS histograms.
 // ---------------------------------------------------------------------------
+constexpr int kThrRows = 16;
+
 template <typename T>
 __global__ __launch_bounds__(256) void teacher_threshold_kernel(TeacherArgs a, int32_t* nbig) {
-  __shared__ uint32_t hist[64][256];
-  __shared__ uint32_t prefix[64];
-  __shared__ int krem[64], lcnt[64];
-  __shared__ double nrm[4][64];
-  __shared__ float tes[64];
-  const int tid = threadIdx.x, row = tid & 63, part = tid >> 6;
-  const int r0 = blockIdx.x * 64, r = r0 + row;
+  __shared__ uint32_t hist[kThrRows][256];
+  __shared__ uint32_t prefix[kThrRows];
+  __shared__ int krem[kThrRows];
+  __shared__ double nrm[16][kThrRows];
+  const int tid = threadIdx.x, row = tid & (kThrRows - 1), sub = tid >> 4;
+  const int r0 = blockIdx.x * kThrRows, r = r0 + row;
   const bool live = r < a.rows;
   if (blockIdx.x == 0 && tid == 0) *nbig = 0;
   {
     double ss = 0.0;
     if (live) {
       const char* x = a.X + (int64_t)r * a.ldx;
-      for (int h = part; h < a.H; h += 4) {
+      for (int h = sub; h < a.H; h += 16) {
         const double v = elem_f64<T>(x, h);
         ss = fma(v, v, ss);
       }
     }
-    nrm[part][row] = ss;
+    nrm[sub][row] = ss;
   }
-  if (tid < 64) {
+  if (tid < kThrRows) {
     prefix[tid] = 0u;
     krem[tid] = a.K;
-    lcnt[tid] = 0;
   }
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     const uint32_t hmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
     __syncthreads();
-    for (int q = tid; q < 64 * 256; q += 256) (&hist[0][0])[q] = 0u;
+    for (int q = tid; q < kThrRows * 256; q += 256) (&hist[0][0])[q] = 0u;
     __syncthreads();
     if (live) {
       const uint32_t pre = prefix[row];
-      for (int v = part; v < a.P; v += 4) {
-        const uint32_t key = fkey(a.zp[(int64_t)v * a.ldp + r]);
+      for (int g = sub; g < a.P; g += 16) {
+        const uint32_t key = fkey(a.zp[(int64_t)g * a.ldp + r]);
         if ((key & hmask) == pre) atomicAdd(&hist[row][(key >> shift) & 255u], 1u);
       }
     }
     __syncthreads();
-    if (tid < 64 && r0 + tid < a.rows) {
+    if (tid < kThrRows && r0 + tid < a.rows) {
       int k = krem[tid];
       int d = 255;
       for (; d > 0; --d) {
@@ -201,69 +231,18 @@ __global__ __launch_bounds__(256) void teacher_threshold_kernel(TeacherArgs a, i
     }
   }
   __syncthreads();
-  if (tid < 64 && r0 + tid < a.rows) {
-    const float tau = funkey(prefix[tid]);
-    const double hn = sqrt(nrm[0][tid] + nrm[1][tid] + nrm[2][tid] + nrm[3][tid]);
-    const double b = logit_bound(a.H, hn, a.wmax[0]);
+  if (tid < kThrRows && r0 + tid < a.rows) {
+    // fewer groups than K: no bound from the pilot, every logit is a candidate
+    const float tau = a.K <= a.P ? funkey(prefix[tid]) : -INFINITY;
+    double ssum = 0.0;
+    for (int q = 0; q < 16; ++q) ssum += nrm[q][tid];
+    const double b = logit_bound(a.H, sqrt(ssum), a.wmax[0]);
     // rounded down: the margins exceed the rounding of the fp32 result
     const double t = (double)tau - 2.0 * b * (1.0 + 0x1p-20) - fabs((double)tau) * 0x1p-22;
-    tes[tid] = (float)t;
     a.te[r0 + tid] = (float)t;
     a.bnd[r0 + tid] = b;
+    a.cnt[r0 + tid] = 0;
   }
-  __syncthreads();
-  // the pilot entries at or above the threshold start the candidate list
-  if (live) {
-    const float te = tes[row];
-    int32_t* cid = a.cid + (int64_t)r * a.cap;
-    float* cz = a.cz + (int64_t)r * a.cap;
-    for (int v = part; v < a.P; v += 4) {
-      const float z = a.zp[(int64_t)v * a.ldp + r];
-      if (z >= te) {
-        const int pos = atomicAdd(&lcnt[row], 1);
-        cid[pos] = v;
-        cz[pos] = z;
-      }
-    }
-  }
-  __syncthreads();
-  if (tid < 64 && r0 + tid < a.rows) a.cnt[r0 + tid] = lcnt[tid];
-}
-
-// K-th largest key among n fp32 values (one work-group; every thread returns it)
-__device__ inline uint32_t kth_largest_key(const float* z, int n, int K, uint32_t* hist,
-                                           uint32_t* s_prefix, int* s_krem) {
-  const int tid = threadIdx.x;
-  if (tid == 0) {
-    *s_prefix = 0u;
-    *s_krem = K;
-  }
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    const uint32_t hmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    __syncthreads();
-    hist[tid] = 0u;
-    __syncthreads();
-    const uint32_t pre = *s_prefix;
-    for (int i = tid; i < n; i += 256) {
-      const uint32_t key = fkey(z[i]);
-      if ((key & hmask) == pre) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int k = *s_krem;
-      int d = 255;
-      for (; d > 0; --d) {
-        const int c = (int)hist[d];
-        if (c >= k) break;
-        k -= c;
-      }
-      *s_prefix = pre | ((uint32_t)d << shift);
-      *s_krem = k;
-    }
-  }
-  __syncthreads();
-  return *s_prefix;
 }
 
 __device__ inline void write_entry(const TeacherArgs& a, int r, int rank, int id, double z) {
@@ -275,8 +254,27 @@ __device__ inline void write_entry(const TeacherArgs& a, int r, int rank, int id
 }
 
 // ---------------------------------------------------------------------------
-// Final ranking: one work-group per row (persistent over rows).
+// Final ranking: one work-group per row (persistent over rows). A row's
+// candidate logits stay in registers (kRegCand per thread) across the radix
+// passes and the band test when they fit; otherwise they are read again from
+// the list each time.
 // ---------------------------------------------------------------------------
+constexpr int kRegCand = 16;
+
+__device__ inline void radix_step(uint32_t* hist, uint32_t* s_prefix, int* s_krem, int shift) {
+  if (threadIdx.x == 0) {
+    int k = *s_krem;
+    int d = 255;
+    for (; d > 0; --d) {
+      const int c = (int)hist[d];
+      if (c >= k) break;
+      k -= c;
+    }
+    *s_prefix |= (uint32_t)d << shift;
+    *s_krem = k;
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void teacher_final_kernel(TeacherArgs a, int32_t* big,
                                                             int32_t* nbig, float* tau2_out) {
@@ -287,19 +285,65 @@ __global__ __launch_bounds__(256) void teacher_final_kernel(TeacherArgs a, int32
   __shared__ double lz[kBandLds];
   const int tid = threadIdx.x;
   for (int r = blockIdx.x; r < a.rows; r += gridDim.x) {
-    const int n = a.cnt[r];
+    const int n = (int)min((int64_t)a.cnt[r], a.cap);
     const int32_t* cid = a.cid + (int64_t)r * a.cap;
     const float* cz = a.cz + (int64_t)r * a.cap;
-    const float tau2 = funkey(kth_largest_key(cz, n, a.K, hist, &s_prefix, &s_krem));
+    const bool in_regs = n <= kRegCand * 256;
+    float zc[kRegCand];
+#pragma unroll
+    for (int u = 0; u < kRegCand; ++u) {
+      const int i = tid + 256 * u;
+      zc[u] = (in_regs && i < n) ? cz[i] : -INFINITY;
+    }
+    // tau2: the K-th largest candidate key, digit by digit
+    if (tid == 0) {
+      s_prefix = 0u;
+      s_krem = a.K;
+    }
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      const uint32_t hmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+      __syncthreads();
+      hist[tid] = 0u;
+      __syncthreads();
+      const uint32_t pre = s_prefix;
+      if (in_regs) {
+#pragma unroll
+        for (int u = 0; u < kRegCand; ++u) {
+          const uint32_t key = fkey(zc[u]);
+          if (tid + 256 * u < n && (key & hmask) == pre) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        }
+      } else {
+        for (int i = tid; i < n; i += 256) {
+          const uint32_t key = fkey(cz[i]);
+          if ((key & hmask) == pre) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        }
+      }
+      __syncthreads();
+      radix_step(hist, &s_prefix, &s_krem, shift);
+    }
+    __syncthreads();
+    const float tau2 = funkey(s_prefix);
     const double thr = (double)tau2 - 2.0 * a.bnd[r];
     if (tid == 0) s_m = 0;
     __syncthreads();
     // the band; a row with more than kBandLds entries is ranked by the
     // second kernel (its list here is abandoned once full)
-    for (int i = tid; i < n; i += 256) {
-      if ((double)cz[i] >= thr) {
-        const int pos = atomicAdd(&s_m, 1);
-        if (pos < kBandLds) lid[pos] = cid[i];
+    if (in_regs) {
+#pragma unroll
+      for (int u = 0; u < kRegCand; ++u) {
+        const int i = tid + 256 * u;
+        if (i < n && (double)zc[u] >= thr) {
+          const int pos = atomicAdd(&s_m, 1);
+          if (pos < kBandLds) lid[pos] = cid[i];
+        }
+      }
+    } else {
+      for (int i = tid; i < n; i += 256) {
+        if ((double)cz[i] >= thr) {
+          const int pos = atomicAdd(&s_m, 1);
+          if (pos < kBandLds) lid[pos] = cid[i];
+        }
       }
     }
     __syncthreads();
@@ -312,8 +356,7 @@ __global__ __launch_bounds__(256) void teacher_final_kernel(TeacherArgs a, int32
       __syncthreads();
       continue;
     }
-    const char* x = a.X + (int64_t)r * a.ldx;
-    for (int e = tid; e < m; e += 256) lz[e] = dot_f64<T>(x, a.W + (int64_t)lid[e] * a.ldw, a.H);
+    band_logits<T>(a.X + (int64_t)r * a.ldx, a, lid, lz, m);
     __syncthreads();
     // rank by (logit desc, id asc); ids are distinct, so ranks are
     for (int e = tid; e < m; e += 256) {
@@ -349,7 +392,7 @@ __global__ __launch_bounds__(256) void teacher_final_big_kernel(TeacherArgs a, c
   const int nb = *nbig;
   for (int q = blockIdx.x; q < nb; q += gridDim.x) {
     const int r = big[q];
-    const int n = a.cnt[r];
+    const int n = (int)min((int64_t)a.cnt[r], a.cap);
     const int32_t* cid = a.cid + (int64_t)r * a.cap;
     const float* cz = a.cz + (int64_t)r * a.cap;
     const double thr = (double)tau2_in[r] - 2.0 * a.bnd[r];
@@ -360,8 +403,7 @@ __global__ __launch_bounds__(256) void teacher_final_big_kernel(TeacherArgs a, c
     }
     __syncthreads();
     const int m = s_m;
-    const char* x = a.X + (int64_t)r * a.ldx;
-    for (int e = tid; e < m; e += 256) sz[e] = dot_f64<T>(x, a.W + (int64_t)sid[e] * a.ldw, a.H);
+    band_logits<T>(a.X + (int64_t)r * a.ldx, a, sid, sz, m);
     __syncthreads();
     for (int k = 0; k < a.K; ++k) {
       double bz = -INFINITY;
@@ -402,7 +444,7 @@ __global__ __launch_bounds__(256) void teacher_final_big_kernel(TeacherArgs a, c
 }
 
 hipError_t launch_teacher_threshold(int f32, const TeacherArgs& a, int32_t* nbig, hipStream_t st) {
-  const int grid = (int)ceil_div(a.rows, 64);
+  const int grid = (int)ceil_div(a.rows, kThrRows);
   if (grid <= 0) return hipSuccess;
   if (f32)
     hipLaunchKernelGGL(teacher_threshold_kernel<float>, dim3(grid), dim3(256), 0, st, a, nbig);
