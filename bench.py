@@ -67,11 +67,11 @@ def kernel_flops(name, wl, C_rows, S_rows):
     return None
 
 
-def measured_traffic(wl, step):
+def measured_traffic(wl, step, slug=None):
     """HBM bytes per launch of `step` from the committed counter summary of this
     workload, or None when there is none or the kernel sources changed since."""
     from chunked_top_kl_amd.prof_summary import kernel_sources_hash, read_summary_json
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{wl['slug']}.md")
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{slug or wl['slug']}.md")
     js = read_summary_json(path)
     if not js or js.get("workload") != wl["name"]:
         return None
@@ -151,9 +151,9 @@ def chunk_sweep(kd, torch, wl, t, chunks, steps=3, warmup=1):
 
 def teacher_leg(kd, torch, wl, t, p, steps=3, warmup=1, cpu_rows=64, cpu=True):
     """Teacher top-K cache writer at the workload's shapes: the workload's
-    hidden rows and W stand in for the teacher's. Counted work: 2*S*H*V FLOP
-    (a pilot pass over the first vocabulary rows and an emit pass over the rest
-    cover the vocabulary once)."""
+    hidden rows and W stand in for the teacher's. Counted work: 2*S*H*V FLOP,
+    the emit pass over the whole vocabulary (the pilot pass over its first
+    16384 rows is extra work and not counted)."""
     S, H, V, K, C = wl["S"], wl["H"], wl["V"], wl["K"], wl["chunk"]
     hidden, W = t[0], t[1]
     prob = kd.make_problem(S, H, V, K, C, 1.0, kd.KD_BF16, kd.KD_BF16)
@@ -180,17 +180,19 @@ def teacher_leg(kd, torch, wl, t, p, steps=3, warmup=1, cpu_rows=64, cpu=True):
         if name == "teacher_pilot":
             f = 2.0 * S * H * P / (n / steps)
         elif name == "teacher_emit":
-            f = 2.0 * S * H * (V - P) / (n / steps)
+            f = 2.0 * S * H * V / (n / steps)
         kernels[name] = dict(launches_per_step=round(n / steps, 2), ms_per_step=round(tot / steps, 4),
                              avg_ms=round(per, 5),
                              tflops=(round(f / (per / 1000.0) / 1e12, 1) if f else None))
     em = kernels.get("teacher_emit")
     roofline = None
     if em:
-        f = 2.0 * S * H * (V - P) / em["launches_per_step"]
+        f = 2.0 * S * H * V / em["launches_per_step"]
         a = f / (em["avg_ms"] / 1000.0) / 1e12
+        tr = measured_traffic(wl, "teacher_emit", slug="teacher_topk_" + wl["slug"])
         roofline = dict(kernel="teacher_emit", bound="mfma", achieved=round(a, 1),
                         peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=round(a / PEAK_BF16_TFLOPS, 4),
+                        traffic=tr["bytes"] if tr else None, traffic_detail=tr,
                         flops_per_launch=f, avg_ms=em["avg_ms"])
     out = dict(workload=f"teacher cache writer at {wl['name']} (synthetic teacher = the workload's hidden and W)",
                ms=round(ms, 3), tokens_per_s=round(S / (ms / 1000.0), 1),
@@ -263,6 +265,9 @@ def main():
                     help="skip the fwd+bwd timing and peak memory at chunks 512/1024/2048")
     ap.add_argument("--no-teacher", action="store_true",
                     help="skip the teacher top-K cache writer leg")
+    ap.add_argument("--teacher-only", action="store_true",
+                    help="time only the teacher top-K cache writer (steps / warmup calls) and "
+                         "print its line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -300,6 +305,16 @@ def main():
         log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
         del a, b
 
+    if args.teacher_only:
+        del ws
+        torch.cuda.empty_cache()
+        r = teacher_leg(kd, torch, wl, t, p, steps=args.steps, warmup=args.warmup,
+                        cpu=not args.no_cpu_baseline)
+        r.update(metric="teacher top-K cache writer tokens/s", value=r["tokens_per_s"],
+                 unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+                 higher_is_better=True, dtype="bf16", data="synthetic")
+        print(json.dumps(r), flush=True)
+        return
     step = (lambda: run_c5_step(kd, torch, wl, t, ws)) if args.workload == "c5" else \
         (lambda: run_step(kd, torch, wl, t, ws))
     for i in range(args.warmup):
