@@ -6,6 +6,7 @@ tests, the smoke check and the bench's CPU-baseline leg use it.
 """
 from .kd_oracle import (  # noqa: F401
     teacher_scaled_grid,
+    teacher_distribution,
     oracle_from_logits,
     oracle_loss_grads,
     oracle_rows,

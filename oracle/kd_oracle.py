@@ -40,6 +40,11 @@ Readings where the pages are silent (each is repeated in the design doc):
     missing position and is excluded like a masked row;
   * entropy is in nats over the full vocabulary at T = 1; selection keeps
     floor(num*S/den) positions, highest entropy first, lower index on ties;
+  * teacher targets may also be given as probabilities at K ids (sampled
+    sparse targets, [SKD] SE-KD3X class axis): they are used as given,
+    renormalised over the row (entries sharing an id add), and the temperature
+    then softens the student side only; a row with a negative, NaN or infinite
+    value, or with no positive mass, is missing;
   * the teacher cache holds, per position, the K entries of largest teacher
     logit z = h . w_v (before any temperature), ordered by z descending with the
     lower id first among equal logits; the stored logit is z rounded to fp32,
@@ -53,6 +58,7 @@ import numpy as np
 
 __all__ = [
     "teacher_scaled_grid",
+    "teacher_distribution",
     "oracle_from_logits",
     "oracle_loss_grads",
     "oracle_rows",
@@ -78,11 +84,16 @@ def _logsumexp_rows(X: np.ndarray) -> np.ndarray:
         return np.log(np.sum(np.exp(X - mf[:, None]), axis=1)) + mf
 
 
-def _present_rows(tlogits, T):
-    """Rows whose teacher log-normaliser is finite (at least one finite logit, none +inf/NaN)."""
+def _present_rows(tlogits, T, probs=False):
+    """Rows that take part: for logits, a finite teacher log-normaliser (at
+    least one finite logit, none +inf/NaN); for probabilities, every value
+    finite and >= 0 and a positive sum."""
     tl = _f64(tlogits)
     if tl.shape[1] == 0:
         return np.zeros(tl.shape[0], dtype=bool)
+    if probs:
+        ok = np.all(np.isfinite(tl) & (tl >= 0.0), axis=1)
+        return ok & (np.sum(np.where(np.isfinite(tl) & (tl > 0.0), tl, 0.0), axis=1) > 0.0)
     with np.errstate(invalid="ignore"):
         return np.isfinite(_logsumexp_rows(tl / float(T)))
 
@@ -107,7 +118,43 @@ def teacher_scaled_grid(ids: np.ndarray, tlogits: np.ndarray, V: int, T: float) 
     return L
 
 
-def _row_terms(Z, ids, tlogits, T):
+def teacher_distribution(ids, tvals, V, T, probs=False):
+    """Dense teacher distribution P[t, v] per row, log P, and the rows present.
+
+    probs=False: the cached logits softened by T and renormalised over the
+    row's K entries (softmax of the scaled grid; entries sharing an id add)
+    [HF "what chunked KL loss does"]. probs=True: the given probabilities
+    (sampled sparse targets, [SKD] SE-KD3X) scattered to their ids, entries
+    sharing an id adding, renormalised over the row.
+    """
+    ids = np.asarray(ids)
+    if not probs:
+        Lt = teacher_scaled_grid(ids, tvals, V, T)
+        lse_t = _logsumexp_rows(Lt)
+        present = np.isfinite(lse_t)
+        lse_t_safe = np.where(present, lse_t, 0.0)
+        with np.errstate(invalid="ignore"):
+            logP = Lt - lse_t_safe[:, None]
+        P = np.where(present[:, None], np.exp(logP), 0.0)
+        return P, logP, present
+    S, K = ids.shape
+    if S and K and (ids.min() < 0 or ids.max() >= V):
+        raise ValueError("teacher id out of range [0, V)")
+    pv = _f64(tvals)
+    present = _present_rows(pv, T, probs=True)
+    P = np.zeros((S, V))
+    rows = np.arange(S)
+    for k in range(K):
+        add = np.where(np.isfinite(pv[:, k]) & (pv[:, k] > 0.0), pv[:, k], 0.0)
+        P[rows, ids[:, k]] += add
+    mass = P.sum(axis=1)
+    P = np.where(present[:, None], P / np.where(mass > 0.0, mass, 1.0)[:, None], 0.0)
+    with np.errstate(divide="ignore"):
+        logP = np.log(P)
+    return P, logP, present
+
+
+def _row_terms(Z, ids, tlogits, T, probs=False):
     """Per-row dense terms of the definition for a block of rows.
 
     Returns (kl[t], lse[t] = logsumexp(z_t/T), soft[t, v] = softmax(z_t/T) - p_t,
@@ -115,13 +162,7 @@ def _row_terms(Z, ids, tlogits, T):
     """
     Z = _f64(Z)
     S, V = Z.shape
-    Lt = teacher_scaled_grid(ids, tlogits, V, T)                 # dense teacher grid of l/T
-    lse_t = _logsumexp_rows(Lt)
-    present = np.isfinite(lse_t)
-    lse_t_safe = np.where(present, lse_t, 0.0)
-    with np.errstate(invalid="ignore"):
-        logP = Lt - lse_t_safe[:, None]                          # log of the renormalised top-K softmax
-    P = np.where(present[:, None], np.exp(logP), 0.0)
+    P, logP, present = teacher_distribution(ids, tlogits, V, T, probs)   # dense teacher grid
     ZT = Z / float(T)
     lse = _logsumexp_rows(ZT)                                    # log-normaliser of z/T over all V
     with np.errstate(invalid="ignore"):
@@ -135,14 +176,14 @@ def _row_terms(Z, ids, tlogits, T):
     return kl, lse, soft, present
 
 
-def oracle_from_logits(Z, ids, tlogits, T=1.0, mask=None, grad_loss=1.0):
+def oracle_from_logits(Z, ids, tlogits, T=1.0, mask=None, grad_loss=1.0, probs=False):
     """Loss and logit gradient from given student logits Z[S, V] (dense definition).
 
     Returns dict(loss, kl_rows, lse, dZ, N, valid); dZ = d loss / d Z.
     """
     Z = _f64(Z)
     S = Z.shape[0]
-    kl, lse, soft, present = _row_terms(Z, ids, tlogits, T)
+    kl, lse, soft, present = _row_terms(Z, ids, tlogits, T, probs)
     m = np.ones(S, dtype=bool) if mask is None else (np.asarray(mask) != 0)
     valid = m & present
     N = int(valid.sum())
@@ -154,7 +195,8 @@ def oracle_from_logits(Z, ids, tlogits, T=1.0, mask=None, grad_loss=1.0):
     return dict(loss=loss, kl_rows=kl, lse=lse, dZ=dZ, N=N, valid=valid)
 
 
-def oracle_loss_grads(hidden, W, ids, tlogits, T=1.0, mask=None, grad_loss=1.0, chunk=None):
+def oracle_loss_grads(hidden, W, ids, tlogits, T=1.0, mask=None, grad_loss=1.0, chunk=None,
+                      probs=False):
     """Loss, dHidden, dW of the top-K KL loss through the output projection.
 
     chunk=None: the dense definition (full [S, V] grids) [HF dense KL].
@@ -168,7 +210,7 @@ def oracle_loss_grads(hidden, W, ids, tlogits, T=1.0, mask=None, grad_loss=1.0, 
     tl = _f64(tlogits)
     if chunk is None:
         Z = Hd @ Wd.T
-        r = oracle_from_logits(Z, ids, tl, T, mask, grad_loss)
+        r = oracle_from_logits(Z, ids, tl, T, mask, grad_loss, probs)
         dH = r["dZ"] @ Wd                                        # chain rule through z = h W^T
         dW = r["dZ"].T @ Hd
         return dict(loss=r["loss"], kl_rows=r["kl_rows"], lse=r["lse"], dH=dH, dW=dW,
@@ -177,7 +219,7 @@ def oracle_loss_grads(hidden, W, ids, tlogits, T=1.0, mask=None, grad_loss=1.0, 
     if C <= 0:
         raise ValueError("chunk must be positive")
     m = np.ones(S, dtype=bool) if mask is None else (np.asarray(mask) != 0)
-    present = _present_rows(tl, T)
+    present = _present_rows(tl, T, probs)
     valid = m & present
     N = int(valid.sum())
     kl_all = np.zeros(S)
@@ -188,7 +230,7 @@ def oracle_loss_grads(hidden, W, ids, tlogits, T=1.0, mask=None, grad_loss=1.0, 
     for c0 in range(0, S, C):
         c1 = min(S, c0 + C)
         Zc = Hd[c0:c1] @ Wd.T
-        kl, lse, soft, _ = _row_terms(Zc, ids[c0:c1], tl[c0:c1], T)
+        kl, lse, soft, _ = _row_terms(Zc, ids[c0:c1], tl[c0:c1], T, probs)
         kl_all[c0:c1] = kl
         lse_all[c0:c1] = lse
         if N:
@@ -199,7 +241,7 @@ def oracle_loss_grads(hidden, W, ids, tlogits, T=1.0, mask=None, grad_loss=1.0, 
     return dict(loss=loss, kl_rows=kl_all, lse=lse_all, dH=dH, dW=dW, N=N, valid=valid)
 
 
-def oracle_rows(hidden_rows, W, ids_rows, tl_rows, T, N, grad_loss=1.0, grads=True):
+def oracle_rows(hidden_rows, W, ids_rows, tl_rows, T, N, grad_loss=1.0, grads=True, probs=False):
     """Per-row outputs for a sample of rows, given the global valid count N.
 
     Every row of the loss depends only on its own hidden state and cache row,
@@ -209,7 +251,7 @@ def oracle_rows(hidden_rows, W, ids_rows, tl_rows, T, N, grad_loss=1.0, grads=Tr
     """
     Hd, Wd = _f64(hidden_rows), _f64(W)
     Z = Hd @ Wd.T
-    kl, lse, soft, present = _row_terms(Z, ids_rows, tl_rows, T)
+    kl, lse, soft, present = _row_terms(Z, ids_rows, tl_rows, T, probs)
     out = dict(kl_rows=kl, lse=lse, present=present)
     if grads:
         coef = float(grad_loss) / (float(T) * N) if N else 0.0
@@ -218,7 +260,7 @@ def oracle_rows(hidden_rows, W, ids_rows, tl_rows, T, N, grad_loss=1.0, grads=Tr
     return out
 
 
-def oracle_dW_rows(hidden, W, ids, tlogits, T, lse, valid, vocab_rows, grad_loss=1.0):
+def oracle_dW_rows(hidden, W, ids, tlogits, T, lse, valid, vocab_rows, grad_loss=1.0, probs=False):
     """Rows `vocab_rows` of dW, given every row's student log-normaliser lse_t.
 
     dW = dZ^T hidden with dZ[t, v] = g (softmax(z_t/T)_v - p_t,v) / (T N) on
@@ -238,14 +280,24 @@ def oracle_dW_rows(hidden, W, ids, tlogits, T, lse, valid, vocab_rows, grad_loss
     lse = _f64(lse)
     with np.errstate(invalid="ignore", over="ignore"):
         Q = np.exp(Zc / float(T) - np.where(valid, lse, 0.0)[:, None])
-    scaled = _f64(tlogits) / float(T)
-    lt = _logsumexp_rows(scaled)                                 # teacher log-normaliser per row
     Pc = np.zeros_like(Q)
-    for k in range(ids.shape[1]):
-        with np.errstate(invalid="ignore"):
-            pk = np.where(np.isfinite(lt), np.exp(scaled[:, k] - np.where(np.isfinite(lt), lt, 0.0)), 0.0)
-        hit = ids[:, k][:, None] == vocab_rows[None, :]
-        Pc += np.where(hit, pk[:, None], 0.0)
+    if probs:
+        pv = _f64(tlogits)
+        use = np.isfinite(pv) & (pv > 0.0)
+        mass = np.sum(np.where(use, pv, 0.0), axis=1)
+        ok = _present_rows(pv, T, probs=True)
+        for k in range(ids.shape[1]):
+            pk = np.where(ok & use[:, k], pv[:, k] / np.where(mass > 0.0, mass, 1.0), 0.0)
+            hit = ids[:, k][:, None] == vocab_rows[None, :]
+            Pc += np.where(hit, pk[:, None], 0.0)
+    else:
+        scaled = _f64(tlogits) / float(T)
+        lt = _logsumexp_rows(scaled)                             # teacher log-normaliser per row
+        for k in range(ids.shape[1]):
+            with np.errstate(invalid="ignore"):
+                pk = np.where(np.isfinite(lt), np.exp(scaled[:, k] - np.where(np.isfinite(lt), lt, 0.0)), 0.0)
+            hit = ids[:, k][:, None] == vocab_rows[None, :]
+            Pc += np.where(hit, pk[:, None], 0.0)
     coef = float(grad_loss) / (float(T) * N)
     G = np.where(valid[:, None], Q - Pc, 0.0) * coef
     return G.T @ Hd
