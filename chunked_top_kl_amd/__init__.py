@@ -14,7 +14,7 @@ import os
 import torch
 
 __all__ = [
-    "KD_BF16", "KD_F32", "KdError", "kd_problem", "lib",
+    "KD_BF16", "KD_F32", "KD_TEACHER_LOGITS", "KD_TEACHER_PROBS", "KdError", "kd_problem", "lib",
     "kd_abi_version", "kd_status_str", "kd_topk_kl_workspace_bytes",
     "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_student_entropy",
     "kd_select_top_fraction", "kd_validate_topk",
@@ -24,6 +24,7 @@ __all__ = [
 ]
 
 KD_BF16, KD_F32 = 0, 1
+KD_TEACHER_LOGITS, KD_TEACHER_PROBS = 0, 1
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkdtopk.so")
 
 if not os.path.exists(LIB_PATH):
@@ -38,7 +39,7 @@ class kd_problem(ctypes.Structure):
     _fields_ = [("S", ctypes.c_int64), ("H", ctypes.c_int64), ("V", ctypes.c_int64),
                 ("K", ctypes.c_int64), ("chunk", ctypes.c_int64),
                 ("temperature", ctypes.c_float), ("hw_dtype", ctypes.c_int32),
-                ("tl_dtype", ctypes.c_int32)]
+                ("tl_dtype", ctypes.c_int32), ("tl_kind", ctypes.c_int32)]
 
 
 class kd_kernel_stat(ctypes.Structure):
@@ -104,9 +105,9 @@ def _dtype_code(t: torch.dtype) -> int:
     raise TypeError(f"unsupported dtype {t}: bfloat16 or float32 expected")
 
 
-def make_problem(S, H, V, K, chunk, T, hw_dtype, tl_dtype) -> kd_problem:
+def make_problem(S, H, V, K, chunk, T, hw_dtype, tl_dtype, tl_kind=0) -> kd_problem:
     return kd_problem(int(S), int(H), int(V), int(K), int(chunk), float(T), int(hw_dtype),
-                      int(tl_dtype))
+                      int(tl_dtype), int(tl_kind))
 
 
 def kd_topk_kl_workspace_bytes(problem: kd_problem) -> int:
@@ -121,7 +122,7 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _problem_of(hidden, W, topk_ids, topk_logits, T, chunk):
+def _problem_of(hidden, W, topk_ids, topk_logits, T, chunk, teacher_probs=False):
     if hidden.dim() != 2 or W.dim() != 2 or topk_ids.dim() != 2 or topk_logits.dim() != 2:
         raise ValueError("hidden [S,H], W [V,H], topk_ids [S,K], topk_logits [S,K] expected")
     S, H = hidden.shape
@@ -137,7 +138,8 @@ def _problem_of(hidden, W, topk_ids, topk_logits, T, chunk):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("tensors must be contiguous device tensors")
     return make_problem(S, H, V, K, chunk, T, _dtype_code(hidden.dtype),
-                        _dtype_code(topk_logits.dtype))
+                        _dtype_code(topk_logits.dtype),
+                        KD_TEACHER_PROBS if teacher_probs else KD_TEACHER_LOGITS)
 
 
 def _mask_arg(mask, S):
@@ -158,9 +160,10 @@ def _workspace(problem, device, workspace):
 
 
 def kd_topk_kl_fwd(hidden, W, topk_ids, topk_logits, T=1.0, chunk=1024, mask=None,
-                   want_kl_rows=False, want_z_topk=False, workspace=None):
-    """Forward pass. Returns dict(loss [1] f32, lse [S] f32, kl_rows, z_topk)."""
-    p = _problem_of(hidden, W, topk_ids, topk_logits, T, chunk)
+                   want_kl_rows=False, want_z_topk=False, workspace=None, teacher_probs=False):
+    """Forward pass. Returns dict(loss [1] f32, lse [S] f32, kl_rows, z_topk).
+    teacher_probs: topk_logits hold probabilities (sampled targets), not logits."""
+    p = _problem_of(hidden, W, topk_ids, topk_logits, T, chunk, teacher_probs)
     mask = _mask_arg(mask, p.S)
     dev = hidden.device
     ws = _workspace(p, dev, workspace)
@@ -175,9 +178,9 @@ def kd_topk_kl_fwd(hidden, W, topk_ids, topk_logits, T=1.0, chunk=1024, mask=Non
 
 
 def kd_topk_kl_bwd(hidden, W, topk_ids, topk_logits, lse, grad_loss, T=1.0, chunk=1024,
-                   mask=None, dW=None, accumulate_dW=False, workspace=None):
+                   mask=None, dW=None, accumulate_dW=False, workspace=None, teacher_probs=False):
     """Backward pass. Returns (dhidden [S,H] f32, dW [V,H] f32)."""
-    p = _problem_of(hidden, W, topk_ids, topk_logits, T, chunk)
+    p = _problem_of(hidden, W, topk_ids, topk_logits, T, chunk, teacher_probs)
     mask = _mask_arg(mask, p.S)
     dev = hidden.device
     ws = _workspace(p, dev, workspace)
@@ -254,10 +257,12 @@ def kd_teacher_topk(hidden, W, K, chunk=2048, out_dtype=torch.bfloat16, workspac
     return ids, logits
 
 
-def kd_validate_topk(topk_ids, topk_logits, V, workspace=None):
-    """Counts of (ids outside [0,V), all -inf rows, NaN/+inf logits)."""
+def kd_validate_topk(topk_ids, topk_logits, V, workspace=None, teacher_probs=False):
+    """Counts of (ids outside [0,V), all -inf rows, NaN/+inf logits); for probabilities,
+    (ids outside [0,V), rows without a positive value, negative or non-finite values)."""
     S, K = topk_ids.shape
-    p = make_problem(S, 8, V, K, 1, 1.0, KD_BF16, _dtype_code(topk_logits.dtype))
+    p = make_problem(S, 8, V, K, 1, 1.0, KD_BF16, _dtype_code(topk_logits.dtype),
+                     KD_TEACHER_PROBS if teacher_probs else KD_TEACHER_LOGITS)
     dev = topk_ids.device
     ws = _workspace(p, dev, workspace)
     a, b, c = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int64(0)
@@ -288,10 +293,12 @@ class KDTopKKL(torch.autograd.Function):
     """loss = mean over valid positions of KL(p_teacher || softmax(hidden W^T / T))."""
 
     @staticmethod
-    def forward(ctx, hidden, W, topk_ids, topk_logits, T, chunk, mask):
-        out = kd_topk_kl_fwd(hidden, W, topk_ids, topk_logits, T, chunk, mask)
+    def forward(ctx, hidden, W, topk_ids, topk_logits, T, chunk, mask, teacher_probs=False):
+        out = kd_topk_kl_fwd(hidden, W, topk_ids, topk_logits, T, chunk, mask,
+                             teacher_probs=teacher_probs)
         ctx.save_for_backward(hidden, W, topk_ids, topk_logits, out["lse"], mask)
         ctx.T, ctx.chunk, ctx.has_mask = T, chunk, mask is not None
+        ctx.teacher_probs = teacher_probs
         return out["loss"][0]
 
     @staticmethod
@@ -299,12 +306,15 @@ class KDTopKKL(torch.autograd.Function):
         hidden, W, topk_ids, topk_logits, lse, mask = ctx.saved_tensors
         g = grad.detach().reshape(1).to(torch.float32).contiguous()
         dh, dW = kd_topk_kl_bwd(hidden, W, topk_ids, topk_logits, lse, g, ctx.T, ctx.chunk,
-                                mask if ctx.has_mask else None)
+                                mask if ctx.has_mask else None, teacher_probs=ctx.teacher_probs)
         dh = dh.to(hidden.dtype) if ctx.needs_input_grad[0] else None
         dW = dW.to(W.dtype) if ctx.needs_input_grad[1] else None
-        return dh, dW, None, None, None, None, None
+        return dh, dW, None, None, None, None, None, None
 
 
-def kd_topk_kl(hidden, W, topk_ids, topk_logits, T=1.0, chunk=1024, mask=None):
-    """Differentiable fused chunked top-K KL loss (scalar)."""
-    return KDTopKKL.apply(hidden, W, topk_ids, topk_logits, float(T), int(chunk), mask)
+def kd_topk_kl(hidden, W, topk_ids, topk_logits, T=1.0, chunk=1024, mask=None,
+               teacher_probs=False):
+    """Differentiable fused chunked top-K KL loss (scalar). teacher_probs: topk_logits
+    hold teacher probabilities (sampled sparse targets) instead of logits."""
+    return KDTopKKL.apply(hidden, W, topk_ids, topk_logits, float(T), int(chunk), mask,
+                          bool(teacher_probs))

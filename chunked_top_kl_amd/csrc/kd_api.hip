@@ -95,6 +95,7 @@ int check_problem(const kd_problem* p) {
   if (!p) return KD_ERR_NULL;
   if (p->hw_dtype != KD_BF16 && p->hw_dtype != KD_F32) return KD_ERR_DTYPE;
   if (p->tl_dtype != KD_BF16 && p->tl_dtype != KD_F32) return KD_ERR_DTYPE;
+  if (p->tl_kind != KD_TEACHER_LOGITS && p->tl_kind != KD_TEACHER_PROBS) return KD_ERR_ARG;
   if (p->S < 0 || p->S > kMaxRows) return KD_ERR_SHAPE;
   if (p->H <= 0 || p->V <= 0 || p->K <= 0) return KD_ERR_SHAPE;
   if (p->K > p->V || p->K > kMaxK) return KD_ERR_SHAPE;
@@ -214,7 +215,8 @@ int teacher_tables(const kd_problem* p, const Layout& L, const int32_t* ids, con
                    const uint8_t* mask, float* z_topk, void* ws, hipStream_t st) {
   {
     Prof pr("prepass", st);
-    KD_HIP(kd::launch_prepass(ids, tl, p->tl_dtype == KD_F32, p->S, (int)p->K, (int)p->V,
+    KD_HIP(kd::launch_prepass(ids, tl, p->tl_dtype == KD_F32, p->tl_kind == KD_TEACHER_PROBS,
+                              p->S, (int)p->K, (int)p->V,
                               p->temperature, at<int32_t>(ws, L.ids_s), at<float>(ws, L.p_s),
                               at<int32_t>(ws, L.korig_s), at<float>(ws, L.negH),
                               at<uint8_t>(ws, L.present), z_topk, st));
@@ -719,7 +721,8 @@ int kd_validate_topk(const kd_problem* p, const int32_t* ids, const void* tl, in
   unsigned long long* cnt = at<unsigned long long>(ws, L.counters);
   {
     Prof pr("validate", st);
-    KD_HIP(kd::launch_validate(ids, tl, p->tl_dtype == KD_F32, p->S, (int)p->K, (int)p->V, cnt,
+    KD_HIP(kd::launch_validate(ids, tl, p->tl_dtype == KD_F32, p->tl_kind == KD_TEACHER_PROBS,
+                               p->S, (int)p->K, (int)p->V, cnt,
                                st));
   }
   unsigned long long h[3] = {0, 0, 0};

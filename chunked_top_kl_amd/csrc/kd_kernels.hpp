@@ -126,9 +126,9 @@ struct GradTeacherArgs {
 
 // ------------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error.
-hipError_t launch_prepass(const int32_t* ids, const void* tl, int tl_f32, int64_t S, int K, int V,
-                          float T, int32_t* ids_s, float* p_s, int32_t* korig_s, float* negH,
-                          uint8_t* present, float* z_topk, hipStream_t st);
+hipError_t launch_prepass(const int32_t* ids, const void* tl, int tl_f32, int probs, int64_t S,
+                          int K, int V, float T, int32_t* ids_s, float* p_s, int32_t* korig_s,
+                          float* negH, uint8_t* present, float* z_topk, hipStream_t st);
 hipError_t launch_compact(const uint8_t* present, const uint8_t* mask, int64_t S, int32_t* idx,
                           int32_t* pos, int32_t* count, hipStream_t st);
 hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid, hipStream_t st);
@@ -153,8 +153,8 @@ int dh_grid(int row_cap, int V, int H, int ncu, int f32);
 __host__ __device__ int dh_splits(int rows, int V, int H, int ncu, int f32);
 hipError_t launch_dh_reduce(const DhReduceArgs& a, hipStream_t st);
 hipError_t launch_dw(int f32, const DwArgs& a, hipStream_t st);
-hipError_t launch_validate(const int32_t* ids, const void* tl, int tl_f32, int64_t S, int K,
-                           int V, unsigned long long* counters, hipStream_t st);
+hipError_t launch_validate(const int32_t* ids, const void* tl, int tl_f32, int probs, int64_t S,
+                           int K, int V, unsigned long long* counters, hipStream_t st);
 hipError_t launch_fill_u8(uint8_t* p, uint8_t v, int64_t n, hipStream_t st);
 
 // selection

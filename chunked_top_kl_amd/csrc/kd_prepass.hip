@@ -11,6 +11,11 @@
 // -inf entries get p = 0; an id outside [0, V) is never dereferenced later
 // (it is stored as 0x7FFFFFFF, past every vocabulary tile). A row takes part
 // ("present") when it has a usable entry and no NaN / +inf logit.
+// Targets given as probabilities (sampled sparse targets, "Rethinking
+// Selective Knowledge Distillation" SE-KD3X class axis): p_k = v_k / sum of
+// the row's usable v (id in [0, V), v > 0), the temperature left to the
+// student side; the row takes part when no value is negative or non-finite
+// and the usable values have a positive sum.
 #include "kd_common.hpp"
 #include "kd_kernels.hpp"
 
@@ -20,8 +25,8 @@ __device__ inline float load_logit(const void* tl, int tl_f32, int64_t i) {
   return tl_f32 ? ((const float*)tl)[i] : bf16_to_f32(((const uint16_t*)tl)[i]);
 }
 
-__global__ void prepass_kernel(const int32_t* ids, const void* tl, int tl_f32, int64_t S, int K,
-                               int V, float invT, int n2, int32_t* ids_s, float* p_s,
+__global__ void prepass_kernel(const int32_t* ids, const void* tl, int tl_f32, int probs, int64_t S,
+                               int K, int V, float invT, int n2, int32_t* ids_s, float* p_s,
                                int32_t* korig_s, float* negH_out, uint8_t* present,
                                float* z_topk) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -33,28 +38,36 @@ __global__ void prepass_kernel(const int32_t* ids, const void* tl, int tl_f32, i
   const bool live = t < S;
   const int64_t base = (live ? t : 0) * K;
 
-  // 1. row max over usable entries, flags
+  // 1. row max over usable entries (logits), flags
   float mx = -INFINITY;
   int bad = 0;
   for (int k = lane; k < K; k += 64) {
     const int id = live ? ids[base + k] : 0;
     const float l = live ? load_logit(tl, tl_f32, base + k) : -INFINITY;
-    if (isnan(l) || l == INFINITY) bad = 1;
-    if (id >= 0 && id < V && isfinite(l)) mx = fmaxf(mx, l * invT);
+    if (probs) {
+      if (live && !(isfinite(l) && l >= 0.0f)) bad = 1;
+    } else {
+      if (isnan(l) || l == INFINITY) bad = 1;
+      if (id >= 0 && id < V && isfinite(l)) mx = fmaxf(mx, l * invT);
+    }
   }
   mx = wave_max(mx);
   bad = (int)wave_sum((float)bad) > 0;
-  // 2. normaliser
+  // 2. normaliser: sum of exp(l/T - max) (logits) or of the usable values
   float z = 0.0f;
-  if (mx != -INFINITY) {
+  if (probs || mx != -INFINITY) {
     for (int k = lane; k < K; k += 64) {
       const int id = live ? ids[base + k] : 0;
       const float l = live ? load_logit(tl, tl_f32, base + k) : -INFINITY;
-      if (id >= 0 && id < V && isfinite(l)) z += __expf(l * invT - mx);
+      if (id >= 0 && id < V && isfinite(l)) {
+        if (probs) z += l > 0.0f ? l : 0.0f;
+        else z += __expf(l * invT - mx);
+      }
     }
   }
   z = wave_sum(z);
   const float logz = __logf(z);
+  const bool has_mass = probs ? (z > 0.0f) : (mx != -INFINITY);
   // 3. probabilities, entropy term, sort keys
   float nh = 0.0f;
   for (int k = lane; k < n2; k += 64) {
@@ -64,7 +77,10 @@ __global__ void prepass_kernel(const int32_t* ids, const void* tl, int tl_f32, i
       const int id = ids[base + k];
       const float l = load_logit(tl, tl_f32, base + k);
       const bool inr = id >= 0 && id < V;
-      if (inr && isfinite(l) && mx != -INFINITY) p = __expf((l * invT - mx) - logz);
+      if (inr && isfinite(l) && has_mass) {
+        if (probs) p = l > 0.0f ? l / z : 0.0f;
+        else p = __expf((l * invT - mx) - logz);
+      }
       const uint32_t kid = inr ? (uint32_t)id : 0x7FFFFFFFu;
       kk = ((unsigned long long)kid << 32) | (uint32_t)k;
       if (z_topk) z_topk[base + k] = __int_as_float(0x7FC00000);  // NaN until gathered
@@ -112,13 +128,13 @@ __global__ void prepass_kernel(const int32_t* ids, const void* tl, int tl_f32, i
   }
   if (lane == 0) {
     negH_out[t] = nh;
-    present[t] = (!bad && mx != -INFINITY) ? 1 : 0;
+    present[t] = (!bad && has_mass) ? 1 : 0;
   }
 }
 
-hipError_t launch_prepass(const int32_t* ids, const void* tl, int tl_f32, int64_t S, int K, int V,
-                          float T, int32_t* ids_s, float* p_s, int32_t* korig_s, float* negH,
-                          uint8_t* present, float* z_topk, hipStream_t st) {
+hipError_t launch_prepass(const int32_t* ids, const void* tl, int tl_f32, int probs, int64_t S,
+                          int K, int V, float T, int32_t* ids_s, float* p_s, int32_t* korig_s,
+                          float* negH, uint8_t* present, float* z_topk, hipStream_t st) {
   if (S <= 0) return hipSuccess;
   int n2 = 1;
   while (n2 < K) n2 <<= 1;
@@ -126,7 +142,7 @@ hipError_t launch_prepass(const int32_t* ids, const void* tl, int tl_f32, int64_
   const size_t lds = (size_t)rpb * n2 * 12;
   const int64_t grid = ceil_div(S, rpb);
   hipLaunchKernelGGL(prepass_kernel, dim3((unsigned)grid), dim3(64 * rpb), lds, st, ids, tl, tl_f32,
-                     S, K, V, 1.0f / T, n2, ids_s, p_s, korig_s, negH, present, z_topk);
+                     probs, S, K, V, 1.0f / T, n2, ids_s, p_s, korig_s, negH, present, z_topk);
   return hipGetLastError();
 }
 
@@ -174,12 +190,13 @@ hipError_t launch_compact(const uint8_t* present, const uint8_t* mask, int64_t S
 
 // ---------------------------------------------------------------------------
 // Validation counters: [0] ids outside [0, V), [1] rows whose logits are all
-// -inf, [2] NaN / +inf logits. Integer atomics: the totals do not depend on
-// the order of the additions.
+// -inf (probabilities: no positive value), [2] NaN / +inf logits
+// (probabilities: negative or non-finite values). Integer atomics: the totals
+// do not depend on the order of the additions.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void validate_kernel(const int32_t* ids, const void* tl,
-                                                       int tl_f32, int64_t S, int K, int V,
-                                                       unsigned long long* counters) {
+                                                       int tl_f32, int probs, int64_t S, int K,
+                                                       int V, unsigned long long* counters) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= S) return;
@@ -188,8 +205,13 @@ __global__ __launch_bounds__(256) void validate_kernel(const int32_t* ids, const
     const int id = ids[t * K + k];
     const float l = load_logit(tl, tl_f32, t * K + k);
     nbad += (id < 0 || id >= V) ? 1 : 0;
-    nlog += (isnan(l) || l == INFINITY) ? 1 : 0;
-    nfin += (l != -INFINITY) ? 1 : 0;
+    if (probs) {
+      nlog += (isfinite(l) && l >= 0.0f) ? 0 : 1;
+      nfin += (isfinite(l) && l > 0.0f) ? 1 : 0;
+    } else {
+      nlog += (isnan(l) || l == INFINITY) ? 1 : 0;
+      nfin += (l != -INFINITY) ? 1 : 0;
+    }
   }
   for (int o = 32; o > 0; o >>= 1) {
     nbad += __shfl_xor(nbad, o, 64);
@@ -207,12 +229,12 @@ __global__ void zero_u64_kernel(unsigned long long* p, int n) {
   if ((int)threadIdx.x < n) p[threadIdx.x] = 0ull;
 }
 
-hipError_t launch_validate(const int32_t* ids, const void* tl, int tl_f32, int64_t S, int K,
-                           int V, unsigned long long* counters, hipStream_t st) {
+hipError_t launch_validate(const int32_t* ids, const void* tl, int tl_f32, int probs, int64_t S,
+                           int K, int V, unsigned long long* counters, hipStream_t st) {
   hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(64), 0, st, counters, 3);
   if (S > 0)
     hipLaunchKernelGGL(validate_kernel, dim3((unsigned)ceil_div(S, 4)), dim3(256), 0, st, ids, tl,
-                       tl_f32, S, K, V, counters);
+                       tl_f32, probs, S, K, V, counters);
   return hipGetLastError();
 }
 

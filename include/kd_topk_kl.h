@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define KD_ABI_VERSION 1
+#define KD_ABI_VERSION 2
 
 typedef enum kd_status {
   KD_OK = 0,
@@ -72,10 +72,23 @@ typedef enum kd_status {
   KD_ERR_BAD_ID = 7,       /* reserved: reported counts come from kd_validate_topk */
   KD_ERR_HIP = 8,          /* a HIP runtime call or kernel launch failed          */
   KD_ERR_ARCH = 9,         /* current device is not gfx950                        */
-  KD_ERR_ARG = 10          /* other invalid argument (fraction, accumulate flag)  */
+  KD_ERR_ARG = 10          /* other invalid argument (fraction, accumulate flag, tl_kind) */
 } kd_status;
 
 typedef enum kd_dtype { KD_BF16 = 0, KD_F32 = 1 } kd_dtype;
+
+/* What topk_logits holds.
+ *   KD_TEACHER_LOGITS  cached teacher logits: p_tk = softmax_k(l_tk / T), the
+ *                      softmax taken over the row's K entries ("offline top-K
+ *                      logits").
+ *   KD_TEACHER_PROBS   teacher probabilities at the K ids, e.g. sampled sparse
+ *                      targets ("Rethinking Selective Knowledge Distillation",
+ *                      Method section 2, SE-KD3X class axis): p_tk = v_tk over
+ *                      the sum of the row's usable values (id in [0, V),
+ *                      value > 0); T then softens the student side only. A row
+ *                      with a negative or non-finite value, or no positive
+ *                      value, takes no part (like a masked row).              */
+typedef enum kd_teacher_kind { KD_TEACHER_LOGITS = 0, KD_TEACHER_PROBS = 1 } kd_teacher_kind;
 
 /* Problem description shared by all entry points.
  *   S      positions (rows of hidden); S = 0 is allowed (empty problem)
@@ -84,14 +97,17 @@ typedef enum kd_dtype { KD_BF16 = 0, KD_F32 = 1 } kd_dtype;
  *   K      teacher entries per position, 1 <= K <= min(V, 4096)
  *   chunk  rows per backward chunk: bounds the [chunk, V] bf16 gradient tile
  *          held in the workspace (the only workspace term that grows with V)
- *   temperature  T > 0, applied to teacher and student logits alike
+ *   temperature  T > 0, applied to teacher and student logits alike (to the
+ *                student only when tl_kind is KD_TEACHER_PROBS)
  *   hw_dtype     storage type of hidden and W (both the same)
- *   tl_dtype     storage type of topk_logits                                */
+ *   tl_dtype     storage type of topk_logits
+ *   tl_kind      kd_teacher_kind: what topk_logits holds                     */
 typedef struct kd_problem {
   int64_t S, H, V, K, chunk;
   float temperature;
   int32_t hw_dtype;
   int32_t tl_dtype;
+  int32_t tl_kind;
 } kd_problem;
 
 /* ABI version of the loaded library (KD_ABI_VERSION). */

@@ -31,16 +31,17 @@ def test_header_symbols_exported():
 
 
 def test_version_and_status_strings():
-    assert kd.kd_abi_version() == 1
+    assert kd.kd_abi_version() == 2
     for c in range(11):
         assert kd.kd_status_str(c).startswith("KD_")
     assert "unknown" in kd.kd_status_str(99)
 
 
 def prob(**kw):
-    d = dict(S=128, H=64, V=1000, K=10, chunk=32, T=1.0, hw=kd.KD_BF16, tl=kd.KD_BF16)
+    d = dict(S=128, H=64, V=1000, K=10, chunk=32, T=1.0, hw=kd.KD_BF16, tl=kd.KD_BF16, kind=0)
     d.update(kw)
-    return kd.make_problem(d["S"], d["H"], d["V"], d["K"], d["chunk"], d["T"], d["hw"], d["tl"])
+    return kd.make_problem(d["S"], d["H"], d["V"], d["K"], d["chunk"], d["T"], d["hw"], d["tl"],
+                           d["kind"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -49,7 +50,7 @@ def prob(**kw):
     (dict(K=5000, V=10000), KD_ERR_SHAPE), (dict(hw=7), KD_ERR_DTYPE), (dict(tl=-1), KD_ERR_DTYPE),
     (dict(T=0.0), KD_ERR_TEMPERATURE), (dict(T=-1.0), KD_ERR_TEMPERATURE),
     (dict(T=float("nan")), KD_ERR_TEMPERATURE), (dict(T=float("inf")), KD_ERR_TEMPERATURE),
-    (dict(chunk=0), KD_ERR_CHUNK),
+    (dict(chunk=0), KD_ERR_CHUNK), (dict(kind=2), 10), (dict(kind=-1), 10),
 ])
 def test_invalid_problems_rejected(kw, code):
     p = prob(**kw)
