@@ -17,4 +17,5 @@ from .kd_oracle import (  # noqa: F401
     oracle_entropy_select_kl,
     oracle_validate_topk,
     oracle_teacher_topk,
+    oracle_select_samples,
 )

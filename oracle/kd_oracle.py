@@ -40,6 +40,10 @@ Readings where the pages are silent (each is repeated in the design doc):
     missing position and is excluded like a masked row;
   * entropy is in nats over the full vocabulary at T = 1; selection keeps
     floor(num*S/den) positions, highest entropy first, lower index on ties;
+  * samples (segments of positions) are ranked by the mean entropy of their
+    positions ([SKD] SE-KD3X sample axis); floor(num*B/den) samples are kept,
+    highest mean first, lower sample index on ties; a sample without positions
+    has mean -inf;
   * teacher targets may also be given as probabilities at K ids (sampled
     sparse targets, [SKD] SE-KD3X class axis): they are used as given,
     renormalised over the row (entries sharing an id add), and the temperature
@@ -69,6 +73,7 @@ __all__ = [
     "oracle_entropy_select_kl",
     "oracle_validate_topk",
     "oracle_teacher_topk",
+    "oracle_select_samples",
 ]
 
 
@@ -411,3 +416,29 @@ def oracle_teacher_topk(hidden, W, K, out_dtype="f32"):
     elif out_dtype != "f32":
         raise ValueError("out_dtype must be 'f32' or 'bf16'")
     return ids, logits
+
+
+def oracle_select_samples(entropy, offsets, num, den):
+    """Keep floor(num*B/den) of B samples by mean student entropy, highest first,
+    lower sample index on ties ([SKD] Method section 2, SE-KD3X: the top l% of
+    training samples by the mean student entropy of a frozen student's single
+    forward pass). Sample b is positions [offsets[b], offsets[b+1]); one with no
+    positions has mean -inf.
+
+    Returns (sample mask uint8 [B], kept sample ids int32 ascending, count, means).
+    """
+    e = _f64(entropy)
+    off = np.asarray(offsets, dtype=np.int64)
+    B = off.shape[0] - 1
+    if B < 0 or np.any(np.diff(off) < 0) or (B > 0 and (off[0] < 0 or off[-1] > e.shape[0])):
+        raise ValueError("offsets must be non-decreasing within [0, S]")
+    if den <= 0 or num < 0 or num > den:
+        raise ValueError("need 0 <= num <= den, den > 0")
+    means = np.array([np.mean(e[off[b]:off[b + 1]]) if off[b + 1] > off[b] else -np.inf
+                      for b in range(B)])
+    k = (int(num) * B) // int(den)
+    order = np.argsort(-means, kind="stable")
+    keep = np.sort(order[:k])
+    mask = np.zeros(B, dtype=np.uint8)
+    mask[keep] = 1
+    return mask, keep.astype(np.int32), k, means
