@@ -17,7 +17,7 @@ __all__ = [
     "KD_BF16", "KD_F32", "KD_TEACHER_LOGITS", "KD_TEACHER_PROBS", "KdError", "kd_problem", "lib",
     "kd_abi_version", "kd_status_str", "kd_topk_kl_workspace_bytes",
     "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_student_entropy",
-    "kd_select_top_fraction", "kd_validate_topk",
+    "kd_select_top_fraction", "kd_select_samples", "kd_validate_topk",
     "kd_teacher_topk_workspace_bytes", "kd_teacher_topk",
     "kd_profile_enable", "kd_profile_read", "kd_profile_reset",
     "KDTopKKL", "kd_topk_kl", "LIB_PATH",
@@ -65,6 +65,9 @@ lib.kd_student_entropy.argtypes = [_PP, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.kd_select_top_fraction.restype = ctypes.c_int
 lib.kd_select_top_fraction.argtypes = [_PP, _P, _P, _P, ctypes.c_int64, ctypes.c_int64, _P, _P,
                                        _I64P, _P, ctypes.c_size_t, _P]
+lib.kd_select_samples.restype = ctypes.c_int
+lib.kd_select_samples.argtypes = [_PP, _P, _P, _P, _P, ctypes.c_int64, ctypes.c_int64,
+                                  ctypes.c_int64, _P, _P, _I64P, _P, ctypes.c_size_t, _P]
 lib.kd_validate_topk.restype = ctypes.c_int
 lib.kd_validate_topk.argtypes = [_PP, _P, _P, _I64P, _I64P, _I64P, _P, ctypes.c_size_t, _P]
 lib.kd_teacher_topk_workspace_bytes.restype = ctypes.c_size_t
@@ -226,6 +229,26 @@ def kd_select_top_fraction(entropy, hidden, W, num=20, den=100, chunk=1024, work
                                       _ptr(ws), ws.numel(), _stream(dev)),
            "kd_select_top_fraction")
     return mask, idx[: cnt.value], cnt.value
+
+
+def kd_select_samples(entropy, offsets, hidden, W, num=20, den=100, chunk=1024, workspace=None):
+    """Keep floor(num*B/den) of the B samples (positions [offsets[b], offsets[b+1])) by mean
+    entropy. Returns (mask u8 [B], idx i32 [count], count)."""
+    S, H = hidden.shape
+    B = offsets.numel() - 1
+    if offsets.dtype != torch.int64 or not offsets.is_contiguous() or B < 0:
+        raise ValueError("offsets must be a contiguous int64 tensor of B+1 entries")
+    p = make_problem(S, H, W.shape[0], 1, chunk, 1.0, _dtype_code(hidden.dtype), KD_BF16)
+    dev = hidden.device
+    ws = _workspace(p, dev, workspace)
+    mask = torch.empty(max(B, 1), dtype=torch.uint8, device=dev)
+    idx = torch.empty(max(B, 1), dtype=torch.int32, device=dev)
+    cnt = ctypes.c_int64(0)
+    _check(lib.kd_select_samples(ctypes.byref(p), _ptr(hidden), _ptr(W), _ptr(entropy),
+                                 _ptr(offsets), int(B), int(num), int(den), _ptr(mask), _ptr(idx),
+                                 ctypes.byref(cnt), _ptr(ws), ws.numel(), _stream(dev)),
+           "kd_select_samples")
+    return mask[:B], idx[: cnt.value], cnt.value
 
 
 def kd_teacher_topk_workspace_bytes(problem: kd_problem) -> int:

@@ -30,6 +30,8 @@ constexpr int64_t kMaxRows = int64_t(1) << 30;
 constexpr double kSelectEps = 2e-5;    // bound on |fp32-path entropy - fp64 entropy| (nats)
 constexpr int64_t kDwDepth = 8192;     // tokens per dW contraction (a multiple of chunks)
 constexpr int kRefineBatch = 256;      // band rows widened to fp64 per refinement launch
+constexpr int kSampleBandCap = 4096;          // band samples refined (as positions' kBandCap)
+constexpr int kSampleBandPositions = 65536;   // their positions refined in fp64 at most
 // refinement work-groups: one vocabulary row per thread, 256 per group
 inline int64_t refine_blocks(int64_t V) { return ceil_div(V, 256); }
 
@@ -113,6 +115,7 @@ struct Layout {
   size_t G, GT, WT, XcT, Xc, dhp;
   size_t em, es, eu;
   size_t band, refined, scal, dscal, rpart, xb, counters;
+  size_t smean, spos, pent, pstart;
   size_t total;
   int64_t C;          // rows per backward chunk (<= S, >= 1)
   int64_t Vp;         // vocabulary columns of the gradient tile: round_up(V, 8)
@@ -191,6 +194,10 @@ Layout plan(const kd_problem* p) {
   L.rpart = take((size_t)4096 * refine_blocks(V) * 3 * 8);
   L.xb = take((size_t)kRefineBatch * H * 8);
   L.counters = take(4 * 8);
+  L.smean = take(Sx * 8);
+  L.spos = take((size_t)kSampleBandPositions * 4);
+  L.pent = take((size_t)kSampleBandPositions * 8);
+  L.pstart = take((size_t)(kSampleBandCap + 1) * 4);
   L.total = off;
   return L;
 }
@@ -563,6 +570,93 @@ int kd_select_top_fraction(const kd_problem* p, const void* hidden, const void* 
   } else {
     Prof pr("select_final", st);
     KD_HIP(kd::launch_select_final(entropy, S, k, w, n_band, 1, mask_out, idx_out, st));
+  }
+  int32_t cnt = 0;
+  KD_HIP(hipMemcpyAsync(&cnt, w.scal + 2, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  KD_HIP(hipStreamSynchronize(st));
+  *count_out = cnt;
+  return KD_OK;
+}
+
+// ------------------------------------------------------------------ sample selection
+int kd_select_samples(const kd_problem* p, const void* hidden, const void* W, const double* entropy,
+                      const int64_t* offsets, int64_t B, int64_t num, int64_t den,
+                      uint8_t* mask_out, int32_t* idx_out, int64_t* count_out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!count_out || !W || (B > 0 && (!offsets || !entropy || !mask_out || !hidden)))
+    return KD_ERR_NULL;
+  if (den <= 0 || num < 0 || num > den || B < 0 || B > std::max<int64_t>(p->S, 1)) return KD_ERR_ARG;
+  const Layout L = plan(p);
+  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  *count_out = 0;
+  if (B == 0) return KD_OK;
+  kd::SelectWs w;
+  w.keys = nullptr;
+  w.band = at<int32_t>(ws, L.band);
+  w.refined = at<double>(ws, L.refined);
+  w.scal = at<int32_t>(ws, L.scal);
+  w.dscal = at<double>(ws, L.dscal);
+  w.rpart = at<double>(ws, L.rpart);
+  w.hist = nullptr;
+  int32_t* flag = w.scal + 8;
+  KD_HIP(kd::launch_sample_check(offsets, B, p->S, flag, st));
+  int32_t h_flag = 0;
+  KD_HIP(hipMemcpyAsync(&h_flag, flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  KD_HIP(hipStreamSynchronize(st));
+  if (h_flag) return KD_ERR_ARG;
+  double* means = at<double>(ws, L.smean);
+  const int64_t k = (num * B) / den;
+  {
+    Prof pr("sample_means", st);
+    KD_HIP(kd::launch_sample_means(entropy, offsets, B, means, st));
+  }
+  {
+    Prof pr("select_threshold", st);
+    KD_HIP(kd::launch_select_threshold(means, B, k, kSelectEps, w, st));
+  }
+  int32_t h[2] = {0, 0};
+  KD_HIP(hipMemcpyAsync(h, w.scal, sizeof(h), hipMemcpyDeviceToHost, st));
+  KD_HIP(hipStreamSynchronize(st));
+  const int n_band = h[0], n_above = h[1];
+  const int64_t need = k - n_above;
+  int refined = 0;
+  int32_t* pstart = at<int32_t>(ws, L.pstart);
+  int32_t* plist = at<int32_t>(ws, L.spos);
+  double* pent = at<double>(ws, L.pent);
+  // the band straddles the cut: rank it on fp64 means
+  if (need > 0 && need < n_band && n_band <= kSampleBandCap) {
+    KD_HIP(kd::launch_sample_band_positions(offsets, w, n_band, pstart, plist,
+                                            kSampleBandPositions, st));
+    int32_t total = 0;
+    KD_HIP(hipMemcpyAsync(&total, w.scal + 3, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+    KD_HIP(hipStreamSynchronize(st));
+    if (total <= kSampleBandPositions) {
+      refined = 1;
+      const int f32 = p->hw_dtype == KD_F32;
+      const int64_t ld = p->H * L.esz;
+      const int nblk = (int)refine_blocks(p->V);
+      for (int rs = 0; rs < total; rs += kSampleBandCap) {
+        const int n = std::min(kSampleBandCap, total - rs);
+        kd::SelectWs wr = w;
+        wr.band = plist + rs;
+        for (int off = 0; off < n; off += kRefineBatch) {
+          Prof pr("select_refine_fp64", st);
+          KD_HIP(kd::launch_refine(f32, (const char*)hidden, ld, (const char*)W, ld, (int)p->V,
+                                   (int)p->H, wr, at<double>(ws, L.xb), off,
+                                   std::min(kRefineBatch, n - off), nblk, st));
+        }
+        KD_HIP(kd::launch_sample_refined_entropy(wr, n, nblk, pent + rs, st));
+      }
+    }
+  }
+  {
+    Prof pr("sample_final", st);
+    KD_HIP(kd::launch_sample_final(means, offsets, B, k, w, n_band, refined, pstart, pent, mask_out,
+                                   idx_out, st));
   }
   int32_t cnt = 0;
   KD_HIP(hipMemcpyAsync(&cnt, w.scal + 2, sizeof(int32_t), hipMemcpyDeviceToHost, st));

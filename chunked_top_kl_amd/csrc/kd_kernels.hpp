@@ -169,6 +169,18 @@ struct SelectWs {
 };
 hipError_t launch_select_threshold(const double* entropy, int64_t S, int64_t k, double eps,
                                    const SelectWs& w, hipStream_t st);
+hipError_t launch_sample_check(const int64_t* off, int64_t B, int64_t S, int32_t* flag,
+                               hipStream_t st);
+hipError_t launch_sample_means(const double* E, const int64_t* off, int64_t B, double* means,
+                               hipStream_t st);
+hipError_t launch_sample_band_positions(const int64_t* off, const SelectWs& w, int n_band,
+                                        int32_t* pstart, int32_t* plist, int cap, hipStream_t st);
+hipError_t launch_sample_refined_entropy(const SelectWs& w, int n, int nblk, double* pent,
+                                         hipStream_t st);
+hipError_t launch_sample_final(const double* means, const int64_t* off, int64_t B, int64_t k,
+                               const SelectWs& w, int n_band, int refined, const int32_t* pstart,
+                               const double* pent, uint8_t* mask, int32_t* idx_out,
+                               hipStream_t st);
 hipError_t launch_refine(int f32, const char* X, int64_t ldx, const char* W, int64_t ldw, int V,
                          int H, const SelectWs& w, double* xb, int band_off, int band_n, int nblk,
                          hipStream_t st);

@@ -410,3 +410,216 @@ hipError_t launch_select_final(const double* entropy, int64_t S, int64_t k, cons
 }
 
 }  // namespace kd
+
+namespace kd {
+
+// ---------------------------------------------------------------------------
+// Sample selection ("Rethinking Selective Knowledge Distillation", Method
+// section 2, SE-KD3X sample axis: keep the top l% of training samples by the
+// mean student entropy of a frozen student's forward pass). Sample b is the
+// positions [off[b], off[b+1]). Its mean from the sweep's entropies is within
+// eps of the fp64 mean (each term is); the k-th largest mean and the band
+// within 2 eps of it come from select_threshold_kernel over the means, and
+// when the band straddles the cut, the entropies of its samples' positions
+// are recomputed in fp64 (refine_kernel) before the band is ranked by (mean
+// descending, sample ascending).
+// ---------------------------------------------------------------------------
+
+__global__ void sample_zero_flag_kernel(int32_t* flag) {
+  if (threadIdx.x == 0) flag[0] = 0;
+}
+
+// off must be non-decreasing within [0, S]; flag[0] = 1 otherwise
+__global__ __launch_bounds__(256) void sample_offsets_check_kernel(const int64_t* off, int64_t B,
+                                                                   int64_t S, int32_t* flag) {
+  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b <= B;
+       b += (int64_t)gridDim.x * 256) {
+    const int64_t o = off[b];
+    bool bad = o < 0 || o > S;
+    if (b < B) bad = bad || off[b + 1] < o;
+    if (bad) flag[0] = 1;
+  }
+}
+
+// means[b]: fp64 mean of E over the sample (threads' strided partial sums,
+// then a fixed tree); -inf for an empty sample
+__global__ __launch_bounds__(256) void sample_mean_kernel(const double* E, const int64_t* off,
+                                                          int64_t B, double* means) {
+  __shared__ double red[256];
+  const int tid = threadIdx.x;
+  for (int64_t b = blockIdx.x; b < B; b += gridDim.x) {
+    const int64_t a0 = off[b], a1 = off[b + 1];
+    double s = 0.0;
+    for (int64_t t = a0 + tid; t < a1; t += 256) s += E[t];
+    red[tid] = s;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if (tid < o) red[tid] += red[tid + o];
+      __syncthreads();
+    }
+    if (tid == 0) means[b] = a1 > a0 ? red[0] / (double)(a1 - a0) : -INFINITY;
+    __syncthreads();
+  }
+}
+
+// the positions of the band samples, in band order: pstart[i] is where band
+// sample i starts in plist; w.scal[3] = the total (written whatever its size;
+// the list is filled only up to cap)
+__global__ __launch_bounds__(1024) void sample_band_positions_kernel(const int64_t* off, SelectWs w,
+                                                                     int n_band, int32_t* pstart,
+                                                                     int32_t* plist, int cap) {
+  __shared__ int64_t sc[1024];
+  const int tid = threadIdx.x;
+  const int seg = (n_band + 1023) / 1024;
+  const int i0 = tid * seg, i1 = (i0 + seg < n_band) ? i0 + seg : n_band;
+  int64_t c = 0;
+  for (int i = i0; i < i1; ++i) c += off[w.band[i] + 1] - off[w.band[i]];
+  sc[tid] = c;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int64_t v = tid >= o ? sc[tid - o] : 0;
+    __syncthreads();
+    sc[tid] += v;
+    __syncthreads();
+  }
+  int64_t p = sc[tid] - c;
+  for (int i = i0; i < i1; ++i) {
+    const int64_t a0 = off[w.band[i]], n = off[w.band[i] + 1] - a0;
+    pstart[i] = (int32_t)(p < cap ? p : cap);
+    for (int64_t j = 0; j < n; ++j)
+      if (p + j < cap) plist[p + j] = (int32_t)(a0 + j);
+    p += n;
+  }
+  if (tid == 1023) {
+    pstart[n_band] = (int32_t)(sc[1023] < cap ? sc[1023] : cap);
+    w.scal[3] = (int32_t)(sc[1023] < 0x7FFFFFFF ? sc[1023] : 0x7FFFFFFF);
+  }
+}
+
+// fp64 entropies of n refined positions from their partials (rows 0..n-1 of
+// rpart), written to pent[0..n)
+__global__ __launch_bounds__(256) void sample_refined_entropy_kernel(SelectWs w, int n, int nblk,
+                                                                     double* pent) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= n) return;
+  double M = -INFINITY, Ssum = 0.0, U = 0.0;
+  for (int q = 0; q < nblk; ++q) {
+    const double* o = w.rpart + ((int64_t)b * nblk + q) * 3;
+    const double m2 = o[0], s2 = o[1], u2 = o[2];
+    if (m2 == -INFINITY) continue;
+    if (M == -INFINITY) {
+      M = m2;
+      Ssum = s2;
+      U = u2;
+      continue;
+    }
+    const double mn = fmax(M, m2), f1 = exp(M - mn), f2 = exp(m2 - mn);
+    U = (U + Ssum * (M - mn)) * f1 + (u2 + s2 * (m2 - mn)) * f2;
+    Ssum = Ssum * f1 + s2 * f2;
+    M = mn;
+  }
+  pent[b] = log(Ssum) - U / Ssum;
+}
+
+// Final decision (one work-group): the band's means (fp64 from the refined
+// entropies when `refined`), certain keeps, the band ranked by (mean desc,
+// sample asc), the mask and the ascending list of kept samples.
+__global__ __launch_bounds__(1024) void sample_final_kernel(const double* means, const int64_t* off,
+                                                            int64_t B, int64_t k, SelectWs w,
+                                                            int n_band, int refined,
+                                                            const int32_t* pstart,
+                                                            const double* pent, uint8_t* mask,
+                                                            int32_t* idx_out) {
+  __shared__ int32_t sc[1024];
+  const int tid = threadIdx.x;
+  const double hk = w.dscal[0];
+  const int n_above = w.scal[1];
+  const double delta = w.dscal[1];
+  for (int i = tid; i < n_band; i += 1024) {
+    double v = means[w.band[i]];
+    if (refined) {
+      const int a = pstart[i], e = pstart[i + 1];
+      if (e > a) {
+        double s = 0.0;
+        for (int j = a; j < e; ++j) s += pent[j];
+        v = s / (double)(e - a);
+      }
+    }
+    w.refined[i] = v;
+  }
+  for (int64_t b = tid; b < B; b += 1024) mask[b] = (means[b] > hk + delta) ? 1 : 0;
+  __syncthreads();
+  const int64_t need = k - n_above;
+  for (int i = tid; i < n_band; i += 1024) {
+    const double vi = w.refined[i];
+    const int32_t bi = w.band[i];
+    int64_t rank = 0;
+    for (int q = 0; q < n_band; ++q) {
+      const double vq = w.refined[q];
+      rank += (vq > vi || (vq == vi && w.band[q] < bi)) ? 1 : 0;
+    }
+    if (rank < need) mask[bi] = 1;
+  }
+  __syncthreads();
+  const int64_t seg = ceil_div(B, 1024);
+  const int64_t t0 = tid * seg, t1 = (t0 + seg < B) ? t0 + seg : B;
+  int c = 0;
+  for (int64_t b = t0; b < t1; ++b) c += mask[b];
+  sc[tid] = c;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? sc[tid - o] : 0;
+    __syncthreads();
+    sc[tid] += v;
+    __syncthreads();
+  }
+  if (idx_out) {
+    int p = sc[tid] - c;
+    for (int64_t b = t0; b < t1; ++b)
+      if (mask[b]) idx_out[p++] = (int32_t)b;
+  }
+  if (tid == 1023) w.scal[2] = sc[1023];
+}
+
+hipError_t launch_sample_check(const int64_t* off, int64_t B, int64_t S, int32_t* flag,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(sample_zero_flag_kernel, dim3(1), dim3(64), 0, st, flag);
+  const int64_t grid = std::min<int64_t>(ceil_div(B + 1, 256), 4096);
+  hipLaunchKernelGGL(sample_offsets_check_kernel, dim3((unsigned)grid), dim3(256), 0, st, off, B, S,
+                     flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_means(const double* E, const int64_t* off, int64_t B, double* means,
+                               hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sample_mean_kernel, dim3((unsigned)std::min<int64_t>(B, 8192)), dim3(256), 0,
+                     st, E, off, B, means);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_band_positions(const int64_t* off, const SelectWs& w, int n_band,
+                                        int32_t* pstart, int32_t* plist, int cap, hipStream_t st) {
+  hipLaunchKernelGGL(sample_band_positions_kernel, dim3(1), dim3(1024), 0, st, off, w, n_band,
+                     pstart, plist, cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_refined_entropy(const SelectWs& w, int n, int nblk, double* pent,
+                                         hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sample_refined_entropy_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0,
+                     st, w, n, nblk, pent);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_final(const double* means, const int64_t* off, int64_t B, int64_t k,
+                               const SelectWs& w, int n_band, int refined, const int32_t* pstart,
+                               const double* pent, uint8_t* mask, int32_t* idx_out,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(sample_final_kernel, dim3(1), dim3(1024), 0, st, means, off, B, k, w, n_band,
+                     refined, pstart, pent, mask, idx_out);
+  return hipGetLastError();
+}
+
+}  // namespace kd

@@ -182,6 +182,27 @@ int kd_select_top_fraction(const kd_problem* problem, const void* hidden, const 
                            uint8_t* mask_out, int32_t* idx_out, int64_t* count_out,
                            void* ws, size_t ws_bytes, void* stream);
 
+/* Keep floor(num*B/den) of B training samples by the mean entropy of their
+ * positions, highest first, lower sample index on ties ("Rethinking Selective
+ * Knowledge Distillation", Method section 2, SE-KD3X sample axis: the top l% of
+ * samples by mean student entropy from a frozen student's forward pass).
+ * Sample b is positions [offsets[b], offsets[b+1]); an empty sample has mean
+ * -inf. Samples whose mean lies within the entropy error bound of the cut have
+ * their positions' entropies recomputed in fp64 from hidden and W before the
+ * decision, so the kept set is the one fp64 entropies give (when those samples
+ * hold more than 65536 positions, the sweep's entropies decide).
+ *   entropy     [device] [S] float64 from kd_student_entropy (not modified)
+ *   offsets     [device] [B+1] int64, non-decreasing within [0, S]
+ *               (KD_ERR_ARG otherwise); B <= max(S, 1)
+ *   mask_out    [device] [B] uint8: 1 = kept
+ *   idx_out     [device] [B] int32 or NULL: kept samples in ascending order in
+ *               the first count entries
+ *   count_out   [host] number kept. Synchronises the host with the stream.  */
+int kd_select_samples(const kd_problem* problem, const void* hidden, const void* W,
+                      const double* entropy, const int64_t* offsets, int64_t B, int64_t num,
+                      int64_t den, uint8_t* mask_out, int32_t* idx_out, int64_t* count_out,
+                      void* ws, size_t ws_bytes, void* stream);
+
 /* Cache validation ("operations": id range and missing positions).
  *   n_bad_id     [host] ids outside [0, V)
  *   n_empty_row  [host] rows whose K logits are all -inf
