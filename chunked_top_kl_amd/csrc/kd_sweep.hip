@@ -148,6 +148,74 @@ __device__ __forceinline__ void walk_window(int64_t base, int& cur, const int (&
   }
 }
 
+// Column reductions of the forward and entropy epilogues. TAIL excludes the
+// entries at or past the vocabulary (W rows there read as zero, so those
+// logits are 0). The caller branches on its half tile being the last one, so
+// that the per-entry test runs on that tile only: folded into selects it
+// cost every tile about five instructions per entry. The row limit passes
+// through an empty volatile asm so that the tests stay inside the branch
+// (otherwise they are shared between reductions and computed, and spilled,
+// ahead of it on every tile).
+template <bool TAIL>
+__device__ __forceinline__ int col_lim(int vw0, int half, int V) {
+  int lim = V - vw0 - 4 * half;
+  if constexpr (TAIL) asm volatile("" : "+v"(lim));
+  return lim;
+}
+template <bool TAIL>
+__device__ __forceinline__ bool col_in(int e, int lim) {
+  return !TAIL || acc_row(e >> 4, e & 15, 0) < lim;
+}
+
+template <bool TAIL>
+__device__ __forceinline__ float col_max(const float (&z)[64], int vw0, int half, int V) {
+  const int lim = col_lim<TAIL>(vw0, half, V);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 64; ++e)
+    if (col_in<TAIL>(e, lim)) mx = fmaxf(mx, z[e]);
+  return mx;
+}
+
+// sum of 2^(z c - mn) over the column
+template <bool TAIL>
+__device__ __forceinline__ float col_sum_exp2(const float (&z)[64], float c, float mn, int vw0,
+                                              int half, int V) {
+  const int lim = col_lim<TAIL>(vw0, half, V);
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+  for (int e = 0; e < 64; e += 4) {
+    const float t0 = fast_exp2(fmaf(z[e + 0], c, -mn)), t1 = fast_exp2(fmaf(z[e + 1], c, -mn));
+    const float t2 = fast_exp2(fmaf(z[e + 2], c, -mn)), t3 = fast_exp2(fmaf(z[e + 3], c, -mn));
+    s0 += col_in<TAIL>(e + 0, lim) ? t0 : 0.f;
+    s1 += col_in<TAIL>(e + 1, lim) ? t1 : 0.f;
+    s2 += col_in<TAIL>(e + 2, lim) ? t2 : 0.f;
+    s3 += col_in<TAIL>(e + 3, lim) ? t3 : 0.f;
+  }
+  return (s0 + s1) + (s2 + s3);
+}
+
+// sums of 2^y and 2^y y, y = z c - mn, over the column
+template <bool TAIL>
+__device__ __forceinline__ void col_ent(const float (&z)[64], float c, float mn, int vw0, int half,
+                                        int V, float& st, float& ut) {
+  const int lim = col_lim<TAIL>(vw0, half, V);
+  float st0 = 0.f, st1 = 0.f, ut0 = 0.f, ut1 = 0.f;
+#pragma unroll
+  for (int e = 0; e < 64; e += 2) {
+    const float y0 = fmaf(z[e], c, -mn), y1 = fmaf(z[e + 1], c, -mn);
+    float e0 = fast_exp2(y0), e1 = fast_exp2(y1);
+    if (!col_in<TAIL>(e, lim)) e0 = 0.f;
+    if (!col_in<TAIL>(e + 1, lim)) e1 = 0.f;
+    st0 += e0;
+    st1 += e1;
+    ut0 += (e0 > 0.f) ? e0 * y0 : 0.f;
+    ut1 += (e1 > 0.f) ? e1 * y1 : 0.f;
+  }
+  st = st0 + st1;
+  ut = ut0 + ut1;
+}
+
 // z[tgt] (tgt in [0, 64)); 0 for tgt < 0.
 __device__ __forceinline__ float pick64(const float (&z)[64], int tgt) {
   float v = 0.0f;
@@ -188,7 +256,6 @@ __device__ __forceinline__ void grad_tile_staged(floatx16 (&acc)[4][4], const Sw
   const int half = lane >> 5;
   const int vw0 = vt * kTile + wm * 128;
   const bool live = vw0 < a.V;
-  const bool tail = vw0 + 128 > a.V;
   const int Vp = (int)round_up(a.V, 8);
   const int tpad = (int)round_up(rows, 8);
   char* sgt = lds;
@@ -202,15 +269,14 @@ __device__ __forceinline__ void grad_tile_staged(floatx16 (&acc)[4][4], const Sw
       const int j = 2 * jp + jj;
       __builtin_amdgcn_sched_barrier(0);
       if (live) {
+        // vocabulary rows past V have z = 0 (zero W rows): their finite
+        // values land in G's padding columns [V, Vp) and G^T's padding rows,
+        // which the contractions multiply by zeros or never read
         float z[64];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float x = acc[i][j][r];
-            if (tail && vw0 + acc_row(i, r, half) >= a.V) x = -INFINITY;
-            z[i * 16 + r] = x;
-          }
+          for (int r = 0; r < 16; ++r) z[i * 16 + r] = acc[i][j][r];
 #pragma unroll
         for (int e = 0; e < 64; ++e) z[e] = fast_exp2(fmaf(z[e], c, -lse2[j]));
         // token columns past `rows` hold a repeated row: exact zeros
@@ -395,13 +461,18 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       __builtin_amdgcn_sched_barrier(0);
+      // Entries past V hold 0 (zero W rows). The forward and entropy
+      // reductions exclude them on the last tile; the gradient tile writes
+      // their finite values into padding only; the teacher cache writer sets
+      // them to -inf here.
       float z[64];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float x = acc[i][j][r];
-          if (tail && vw0 + acc_row(i, r, half) >= a.V) x = -INFINITY;
+          if constexpr (KIND == kSweepPilot || KIND == kSweepEmit)
+            if (tail && vw0 + acc_row(i, r, half) >= a.V) x = -INFINITY;
           z[i * 16 + r] = x;
         }
 
@@ -456,21 +527,13 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
       }
 
       if constexpr (KIND == kSweepFwd) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 64; ++e) mx = fmaxf(mx, z[e]);
+        const float mx = tail ? col_max<true>(z, vw0, half, a.V) : col_max<false>(z, vw0, half, a.V);
         const float mn = fmaxf(m[j], mx * c);
         if (mn != -INFINITY) {
           const float sc = fast_exp2(m[j] - mn);
-          float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-          for (int e = 0; e < 64; e += 4) {
-            s0 += fast_exp2(fmaf(z[e + 0], c, -mn));
-            s1 += fast_exp2(fmaf(z[e + 1], c, -mn));
-            s2 += fast_exp2(fmaf(z[e + 2], c, -mn));
-            s3 += fast_exp2(fmaf(z[e + 3], c, -mn));
-          }
-          s[j] = s[j] * sc + ((s0 + s1) + (s2 + s3));
+          const float st = tail ? col_sum_exp2<true>(z, c, mn, vw0, half, a.V)
+                                : col_sum_exp2<false>(z, c, mn, vw0, half, a.V);
+          s[j] = s[j] * sc + st;
           m[j] = mn;
         }
         // z at the teacher ids, stored at their sorted positions; the
@@ -483,22 +546,12 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
       }
 
       if constexpr (KIND == kSweepEnt) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 64; ++e) mx = fmaxf(mx, z[e]);
+        const float mx = tail ? col_max<true>(z, vw0, half, a.V) : col_max<false>(z, vw0, half, a.V);
         const float mn = fmaxf(m[j], mx * c);
         if (mn != -INFINITY) {
-          float st0 = 0.f, st1 = 0.f, ut0 = 0.f, ut1 = 0.f;
-#pragma unroll
-          for (int e = 0; e < 64; e += 2) {
-            const float y0 = fmaf(z[e], c, -mn), y1 = fmaf(z[e + 1], c, -mn);
-            const float e0 = fast_exp2(y0), e1 = fast_exp2(y1);
-            st0 += e0;
-            st1 += e1;
-            ut0 += (e0 > 0.f) ? e0 * y0 : 0.f;
-            ut1 += (e1 > 0.f) ? e1 * y1 : 0.f;
-          }
-          const float st = st0 + st1, ut = ut0 + ut1;
+          float st, ut;
+          if (tail) col_ent<true>(z, c, mn, vw0, half, a.V, st, ut);
+          else col_ent<false>(z, c, mn, vw0, half, a.V, st, ut);
           if (m[j] == -INFINITY) {
             S64[j] = st;
             U64[j] = ut;
