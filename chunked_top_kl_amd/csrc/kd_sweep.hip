@@ -360,15 +360,16 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
   const int ns = sweep_splits(ntt, nvt, a.ncu);
   const int total = ntt * ns;
   if ((int)blockIdx.x >= total) return;
-  // Raster. A launch of at most 8 token tiles (one chunk) walks its token
-  // tiles fastest, then vocabulary ranges: the 32 work-groups an XCD runs at
-  // once share each W panel up to 8 ways and each vocabulary range of W is
-  // read by as few XCDs as possible. A launch over many token tiles walks the
-  // vocabulary ranges fastest instead, so that an XCD holds few token panels
-  // at a time (8 of them, 11.8 MB at H = 2880, would not stay in its 4 MB L2
-  // and would be fetched again for every vocabulary tile).
+  // Raster. A launch of at most 8 token tiles (one chunk) takes them in
+  // pairs: the 32 work-groups an XCD runs at once cover 2 token tiles (whose
+  // panels, 2.9 MB at H = 2880, stay in its 4 MB L2) and 16 vocabulary ranges,
+  // each W panel shared 2 ways and each range of W read by 4 XCDs. Measured
+  // on the gradient tile at the 32K-context shapes (ms per launch): all 8
+  // token tiles per XCD 2.27, 4 tiles 2.22, 2 tiles 2.20, 1 tile 2.24. A
+  // launch over many token tiles walks the vocabulary ranges fastest instead,
+  // so that an XCD holds few token panels at a time.
   const int L = xcd_remap(blockIdx.x, total);
-  const int GM = ntt <= 8 ? ntt : 1;
+  const int GM = ntt <= 8 ? (ntt < 2 ? ntt : 2) : 1;
   const int grp = L / (GM * ns), in = L % (GM * ns);
   const int gm = (ntt - grp * GM) < GM ? (ntt - grp * GM) : GM;
   const int jt = grp * GM + in % gm, b = in / gm;
