@@ -18,4 +18,7 @@ from .kd_oracle import (  # noqa: F401
     oracle_validate_topk,
     oracle_teacher_topk,
     oracle_select_samples,
+    oracle_position_signals,
+    oracle_select_by_signal,
+    oracle_select_above,
 )

@@ -49,6 +49,20 @@ Readings where the pages are silent (each is repeated in the design doc):
     renormalised over the row (entries sharing an id add), and the temperature
     then softens the student side only; a row with a negative, NaN or infinite
     value, or with no positive mass, is missing;
+  * position signals ([SKD] Method section 1 lists student cross-entropy,
+    teacher uncertainty 1 - p_t(y_t), teacher-student KL and student entropy):
+    the student side is taken at T = 1 like the entropy, ce_t = log sum_v
+    exp(z_tv) - z_{t,y_t}; p_t is the row's KD target (the renormalised top-K
+    at T, or the given probabilities), so p_t(y_t) = 0 when y_t is not among
+    the row's ids; a label outside [0, V) gives NaN for both, and a missing
+    teacher row NaN for the teacher uncertainty;
+  * per-sequence top-k%: each segment [offsets[b], offsets[b+1]) keeps
+    floor(num*len_b/den) positions by signal, highest first, lower index on
+    ties; NaN signals are never kept (a segment then keeps fewer);
+  * GLS (global-level selection, named in [SKD] Method section 1 without a
+    definition): one threshold for all positions, keep signal >= tau; tau
+    may be the smallest value kept by a top-k% selection over a pooled set of
+    signals (the per-segment thresholds returned below);
   * the teacher cache holds, per position, the K entries of largest teacher
     logit z = h . w_v (before any temperature), ordered by z descending with the
     lower id first among equal logits; the stored logit is z rounded to fp32,
@@ -74,6 +88,9 @@ __all__ = [
     "oracle_validate_topk",
     "oracle_teacher_topk",
     "oracle_select_samples",
+    "oracle_position_signals",
+    "oracle_select_by_signal",
+    "oracle_select_above",
 ]
 
 
@@ -442,3 +459,95 @@ def oracle_select_samples(entropy, offsets, num, den):
     mask = np.zeros(B, dtype=np.uint8)
     mask[keep] = 1
     return mask, keep.astype(np.int32), k, means
+
+
+def oracle_position_signals(hidden, W, ids, tlogits, labels, T=1.0, probs=False, chunk=None):
+    """Per-position importance signals ([SKD] Method section 1: student
+    cross-entropy, teacher uncertainty 1 - p_t(y_t), student entropy; the
+    teacher-student KL per position is oracle_rows' kl_rows).
+
+    entropy_t = H(softmax(z_t)) and ce_t = logsumexp(z_t) - z_{t,y_t}, both at
+    T = 1 with z_t = hidden_t W^T; teacher_unc_t = 1 - p_t(y_t) with p_t the
+    row's KD target (renormalised top-K softmax at T, or the given
+    probabilities), summed over entries sharing the label's id. A label
+    outside [0, V) gives NaN ce and teacher_unc; a missing teacher row gives
+    NaN teacher_unc. Returns dict(entropy, ce, teacher_unc), fp64 [S].
+    """
+    Hd, Wd = _f64(hidden), _f64(W)
+    S, V = Hd.shape[0], Wd.shape[0]
+    y = np.asarray(labels, dtype=np.int64)
+    has = (y >= 0) & (y < V)
+    C = S if chunk is None else int(chunk)
+    ent = np.zeros(S)
+    ce = np.full(S, np.nan)
+    for c0 in range(0, S, max(C, 1)):
+        c1 = min(S, c0 + C)
+        Z = Hd[c0:c1] @ Wd.T
+        ent[c0:c1] = oracle_entropy_rows(Z)
+        lse = _logsumexp_rows(Z)                       # log-normaliser at T = 1
+        yy = np.where(has[c0:c1], y[c0:c1], 0)
+        zy = Z[np.arange(c1 - c0), yy]                 # the student's logit at the label
+        ce[c0:c1] = np.where(has[c0:c1], lse - zy, np.nan)
+    tl = _f64(tlogits)
+    ids = np.asarray(ids)
+    if S and ids.shape[1] and (ids.min() < 0 or ids.max() >= V):
+        raise ValueError("teacher id out of range [0, V)")
+    present = _present_rows(tl, T, probs)
+    tu = np.full(S, np.nan)
+    for t in range(S):
+        if not (has[t] and present[t]):
+            continue
+        if probs:
+            w = np.where(np.isfinite(tl[t]) & (tl[t] > 0.0), tl[t], 0.0)
+        else:
+            sc = tl[t] / float(T)
+            w = np.exp(sc - np.max(sc))                # -inf entries give 0
+        tu[t] = 1.0 - np.sum(w[ids[t] == y[t]]) / np.sum(w)
+    return dict(entropy=ent, ce=ce, teacher_unc=tu)
+
+
+def _check_offsets(off, S):
+    B = off.shape[0] - 1
+    if B < 0 or np.any(np.diff(off) < 0) or (B > 0 and (off[0] < 0 or off[-1] > S)):
+        raise ValueError("offsets must be non-decreasing within [0, S]")
+    return B
+
+
+def oracle_select_by_signal(signal, offsets, num, den):
+    """Top-k% positions by a signal, per segment ([SKD] Method section 1,
+    top-k% selection; per sequence when offsets are given).
+
+    Segment b is positions [offsets[b], offsets[b+1]) (offsets None: one
+    segment [0, S)); it keeps floor(num*len_b/den) positions, highest signal
+    first, lower index first among equal values. NaN signals are never kept.
+    Returns (mask uint8 [S], idx int32 ascending, count, thresholds [B]) with
+    thresholds[b] the smallest kept value of segment b (NaN if none kept).
+    """
+    x = _f64(signal)
+    S = x.shape[0]
+    off = np.array([0, S], dtype=np.int64) if offsets is None else np.asarray(offsets, np.int64)
+    B = _check_offsets(off, S)
+    if den <= 0 or num < 0 or num > den:
+        raise ValueError("need 0 <= num <= den, den > 0")
+    mask = np.zeros(S, dtype=np.uint8)
+    thr = np.full(B, np.nan)
+    for b in range(B):
+        a, e = int(off[b]), int(off[b + 1])
+        cand = np.arange(a, e)[~np.isnan(x[a:e])]
+        k = min((int(num) * (e - a)) // int(den), cand.shape[0])
+        keep = cand[np.argsort(-x[cand], kind="stable")][:k]
+        mask[keep] = 1
+        if k > 0:
+            thr[b] = np.min(x[keep])
+    idx = np.flatnonzero(mask).astype(np.int32)
+    return mask, idx, int(idx.shape[0]), thr
+
+
+def oracle_select_above(signal, tau):
+    """GLS reading: one global threshold, keep the positions whose signal is
+    >= tau; NaN is never kept. Returns (mask uint8 [S], idx int32, count)."""
+    x = _f64(signal)
+    with np.errstate(invalid="ignore"):
+        mask = (x >= float(tau)).astype(np.uint8)
+    idx = np.flatnonzero(mask).astype(np.int32)
+    return mask, idx, int(idx.shape[0])
