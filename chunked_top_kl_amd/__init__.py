@@ -18,6 +18,7 @@ __all__ = [
     "kd_abi_version", "kd_status_str", "kd_topk_kl_workspace_bytes",
     "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_student_entropy",
     "kd_select_top_fraction", "kd_select_samples", "kd_validate_topk",
+    "kd_position_signals", "kd_select_by_signal", "kd_select_above",
     "kd_teacher_topk_workspace_bytes", "kd_teacher_topk",
     "kd_profile_enable", "kd_profile_read", "kd_profile_reset",
     "KDTopKKL", "kd_topk_kl", "LIB_PATH",
@@ -68,6 +69,13 @@ lib.kd_select_top_fraction.argtypes = [_PP, _P, _P, _P, ctypes.c_int64, ctypes.c
 lib.kd_select_samples.restype = ctypes.c_int
 lib.kd_select_samples.argtypes = [_PP, _P, _P, _P, _P, ctypes.c_int64, ctypes.c_int64,
                                   ctypes.c_int64, _P, _P, _I64P, _P, ctypes.c_size_t, _P]
+lib.kd_position_signals.restype = ctypes.c_int
+lib.kd_position_signals.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+lib.kd_select_by_signal.restype = ctypes.c_int
+lib.kd_select_by_signal.argtypes = [_PP, _P, _P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                    _P, _P, _P, _I64P, _P, ctypes.c_size_t, _P]
+lib.kd_select_above.restype = ctypes.c_int
+lib.kd_select_above.argtypes = [_PP, _P, ctypes.c_double, _P, _P, _I64P, _P, ctypes.c_size_t, _P]
 lib.kd_validate_topk.restype = ctypes.c_int
 lib.kd_validate_topk.argtypes = [_PP, _P, _P, _I64P, _I64P, _I64P, _P, ctypes.c_size_t, _P]
 lib.kd_teacher_topk_workspace_bytes.restype = ctypes.c_size_t
@@ -249,6 +257,83 @@ def kd_select_samples(entropy, offsets, hidden, W, num=20, den=100, chunk=1024, 
                                  ctypes.byref(cnt), _ptr(ws), ws.numel(), _stream(dev)),
            "kd_select_samples")
     return mask[:B], idx[: cnt.value], cnt.value
+
+
+def kd_position_signals(hidden, W, topk_ids=None, topk_logits=None, labels=None, T=1.0,
+                        teacher_probs=False, entropy=True, chunk=1024, workspace=None):
+    """Per-position signals, float64 [S] each (None when not computed): entropy at
+    T = 1 (when entropy=True), the student's cross-entropy on the label at T = 1
+    (when labels are given) and the teacher uncertainty 1 - p_t(y_t) (when labels
+    and the teacher rows are given). Returns dict(entropy, ce, teacher_unc)."""
+    if hidden.dim() != 2 or W.dim() != 2 or hidden.shape[1] != W.shape[1]:
+        raise ValueError("hidden [S,H] and W [V,H] expected")
+    S, H = hidden.shape
+    V = W.shape[0]
+    teacher = topk_ids is not None and topk_logits is not None and labels is not None
+    K = topk_ids.shape[1] if teacher else 1
+    tl_dtype = _dtype_code(topk_logits.dtype) if teacher else KD_BF16
+    if labels is not None and (labels.dtype != torch.int32 or labels.numel() != S
+                               or not labels.is_contiguous()):
+        raise ValueError("labels must be a contiguous int32 tensor of S entries")
+    p = make_problem(S, H, V, K, chunk, T, _dtype_code(hidden.dtype), tl_dtype,
+                     KD_TEACHER_PROBS if teacher_probs else KD_TEACHER_LOGITS)
+    dev = hidden.device
+    ws = _workspace(p, dev, workspace)
+    f64 = dict(dtype=torch.float64, device=dev)
+    ent = torch.empty(S, **f64) if entropy else None
+    ce = torch.empty(S, **f64) if labels is not None else None
+    tu = torch.empty(S, **f64) if teacher else None
+    _check(lib.kd_position_signals(ctypes.byref(p), _ptr(hidden), _ptr(W),
+                                   _ptr(topk_ids if teacher else None),
+                                   _ptr(topk_logits if teacher else None), _ptr(labels), _ptr(ent),
+                                   _ptr(ce), _ptr(tu), _ptr(ws), ws.numel(), _stream(dev)),
+           "kd_position_signals")
+    return dict(entropy=ent, ce=ce, teacher_unc=tu)
+
+
+def _signal_problem(signal):
+    if signal.dtype != torch.float64 or signal.dim() != 1 or not signal.is_contiguous():
+        raise ValueError("signal must be a contiguous float64 vector")
+    # only S matters to the selection entry points
+    return make_problem(signal.numel(), 8, 1, 1, 1, 1.0, KD_BF16, KD_BF16)
+
+
+def kd_select_by_signal(signal, offsets=None, num=20, den=100, workspace=None):
+    """Top num/den of each segment [offsets[b], offsets[b+1]) by signal (one segment
+    [0, S) without offsets), highest first, lower index on ties, NaN never kept.
+    Returns (mask u8 [S], idx i32 [count], count, thresholds f64 [B])."""
+    p = _signal_problem(signal)
+    S = signal.numel()
+    if offsets is not None and (offsets.dtype != torch.int64 or not offsets.is_contiguous()
+                                or offsets.numel() < 1):
+        raise ValueError("offsets must be a contiguous int64 tensor of B+1 entries")
+    B = 1 if offsets is None else offsets.numel() - 1
+    dev = signal.device
+    ws = _workspace(p, dev, workspace)
+    mask = torch.empty(max(S, 1), dtype=torch.uint8, device=dev)
+    idx = torch.empty(max(S, 1), dtype=torch.int32, device=dev)
+    thr = torch.empty(max(B, 1), dtype=torch.float64, device=dev)
+    cnt = ctypes.c_int64(0)
+    _check(lib.kd_select_by_signal(ctypes.byref(p), _ptr(signal), _ptr(offsets), int(B), int(num),
+                                   int(den), _ptr(mask), _ptr(idx), _ptr(thr), ctypes.byref(cnt),
+                                   _ptr(ws), ws.numel(), _stream(dev)), "kd_select_by_signal")
+    return mask[:S], idx[: cnt.value], cnt.value, thr[:B]
+
+
+def kd_select_above(signal, tau, workspace=None):
+    """Global threshold: keep signal >= tau (NaN never). Returns (mask u8 [S], idx i32
+    [count], count)."""
+    p = _signal_problem(signal)
+    S = signal.numel()
+    dev = signal.device
+    ws = _workspace(p, dev, workspace)
+    mask = torch.empty(max(S, 1), dtype=torch.uint8, device=dev)
+    idx = torch.empty(max(S, 1), dtype=torch.int32, device=dev)
+    cnt = ctypes.c_int64(0)
+    _check(lib.kd_select_above(ctypes.byref(p), _ptr(signal), float(tau), _ptr(mask), _ptr(idx),
+                               ctypes.byref(cnt), _ptr(ws), ws.numel(), _stream(dev)),
+           "kd_select_above")
+    return mask[:S], idx[: cnt.value], cnt.value
 
 
 def kd_teacher_topk_workspace_bytes(problem: kd_problem) -> int:

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <limits>
 #include <map>
 #include <mutex>
 #include <string>
@@ -116,6 +117,7 @@ struct Layout {
   size_t em, es, eu;
   size_t band, refined, scal, dscal, rpart, xb, counters;
   size_t smean, spos, pent, pstart;
+  size_t lse64;
   size_t total;
   int64_t C;          // rows per backward chunk (<= S, >= 1)
   int64_t Vp;         // vocabulary columns of the gradient tile: round_up(V, 8)
@@ -198,6 +200,7 @@ Layout plan(const kd_problem* p) {
   L.spos = take((size_t)kSampleBandPositions * 4);
   L.pent = take((size_t)kSampleBandPositions * 8);
   L.pstart = take((size_t)(kSampleBandCap + 1) * 4);
+  L.lse64 = take(Sx * 8);
   L.total = off;
   return L;
 }
@@ -517,9 +520,171 @@ int kd_student_entropy(const kd_problem* p, const void* hidden, const void* W, d
   c.es = a.es;
   c.eu = a.eu;
   c.entropy = entropy;
+  c.lse = nullptr;
   Prof pr("entropy_combine", st);
   KD_HIP(kd::launch_ent_combine(c, st));
   return KD_OK;
+}
+
+// ------------------------------------------------------------------ position signals
+int kd_position_signals(const kd_problem* p, const void* hidden, const void* W,
+                        const int32_t* topk_ids, const void* topk_logits, const int32_t* labels,
+                        double* entropy, double* ce, double* teacher_unc, void* ws,
+                        size_t ws_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  const bool sweep = entropy || ce;
+  if (p->S > 0) {
+    if (sweep && (!hidden || !W)) return KD_ERR_NULL;
+    if ((ce || teacher_unc) && !labels) return KD_ERR_NULL;
+    if (teacher_unc && (!topk_ids || !topk_logits)) return KD_ERR_NULL;
+  }
+  const Layout L = plan(p);
+  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const int S = (int)p->S, V = (int)p->V, H = (int)p->H;
+  if (S == 0 || (!sweep && !teacher_unc)) return KD_OK;
+  double* lse = at<double>(ws, L.lse64);
+  if (sweep) {
+    // the student at T = 1 over the full vocabulary: entropy and log-normaliser
+    kd::SweepArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.W = (const char*)W;
+    a.ldw = (int64_t)H * L.esz;
+    a.X = (const char*)hidden;
+    a.ldx = (int64_t)H * L.esz;
+    a.row_begin = 0;
+    a.row_cap = S;
+    a.V = V;
+    a.H = H;
+    a.K = (int)p->K;
+    a.ncu = kCostCUs;
+    a.T = 1.0f;
+    a.em = at<float>(ws, L.em);
+    a.es = at<double>(ws, L.es);
+    a.eu = at<double>(ws, L.eu);
+    {
+      Prof pr("entropy_sweep", st);
+      KD_HIP(kd::launch_sweep(kd::kSweepEnt, p->hw_dtype == KD_F32, 0, a,
+                              kd::sweep_grid(S, V, kCostCUs), st));
+    }
+    kd::EntCombineArgs c;
+    c.S = S;
+    c.V = V;
+    c.ncu = kCostCUs;
+    c.em = a.em;
+    c.es = a.es;
+    c.eu = a.eu;
+    c.entropy = entropy;
+    c.lse = ce ? lse : nullptr;
+    Prof pr("entropy_combine", st);
+    KD_HIP(kd::launch_ent_combine(c, st));
+  }
+  if (ce || teacher_unc) {
+    kd::SignalArgs g;
+    std::memset(&g, 0, sizeof(g));
+    g.S = S;
+    g.V = V;
+    g.H = H;
+    g.K = (int)p->K;
+    g.hw_f32 = p->hw_dtype == KD_F32;
+    g.tl_f32 = p->tl_dtype == KD_F32;
+    g.probs = p->tl_kind == KD_TEACHER_PROBS;
+    g.invT = 1.0 / (double)p->temperature;
+    g.hidden = (const char*)hidden;
+    g.ldh = (int64_t)H * L.esz;
+    g.W = (const char*)W;
+    g.ldw = (int64_t)H * L.esz;
+    g.labels = labels;
+    g.lse = lse;
+    g.ids = topk_ids;
+    g.tl = topk_logits;
+    g.ce = ce;
+    g.tunc = teacher_unc;
+    Prof pr("position_signals", st);
+    KD_HIP(kd::launch_signals(g, st));
+  }
+  return KD_OK;
+}
+
+// ------------------------------------------------------------------ selection by a signal
+// count of the kept positions (mask) into idx (and its host copy)
+static int compact_mask(const Layout& L, void* ws, int64_t S, const uint8_t* mask, int32_t* idx_out,
+                        int64_t* count_out, hipStream_t st) {
+  int32_t* cnt = at<int32_t>(ws, L.count);
+  KD_HIP(kd::launch_compact(mask, nullptr, S, idx_out ? idx_out : at<int32_t>(ws, L.idx),
+                            at<int32_t>(ws, L.pos), cnt, st));
+  int32_t h = 0;
+  KD_HIP(hipMemcpyAsync(&h, cnt, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  KD_HIP(hipStreamSynchronize(st));
+  *count_out = h;
+  return KD_OK;
+}
+
+int kd_select_by_signal(const kd_problem* p, const double* signal, const int64_t* offsets,
+                        int64_t B, int64_t num, int64_t den, uint8_t* mask_out, int32_t* idx_out,
+                        double* thresholds_out, int64_t* count_out, void* ws, size_t ws_bytes,
+                        void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!count_out) return KD_ERR_NULL;
+  if (den <= 0 || den > 0x7FFFFFFF || num < 0 || num > den) return KD_ERR_ARG;
+  if (!offsets) B = 1;
+  if (B < 0 || B > std::max<int64_t>(p->S, 1)) return KD_ERR_ARG;
+  if (p->S > 0 && (!signal || !mask_out)) return KD_ERR_NULL;
+  const Layout L = plan(p);
+  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  *count_out = 0;
+  const int64_t S = p->S;
+  if (offsets && B > 0) {
+    int32_t* flag = at<int32_t>(ws, L.scal) + 8;
+    KD_HIP(kd::launch_sample_check(offsets, B, S, flag, st));
+    int32_t h_flag = 0;
+    KD_HIP(hipMemcpyAsync(&h_flag, flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+    KD_HIP(hipStreamSynchronize(st));
+    if (h_flag) return KD_ERR_ARG;
+  }
+  if (S == 0) {
+    if (thresholds_out && B > 0) {
+      // segments of an empty problem are empty: nothing kept
+      const double nan = std::numeric_limits<double>::quiet_NaN();
+      std::vector<double> h((size_t)B, nan);
+      KD_HIP(hipMemcpyAsync(thresholds_out, h.data(), (size_t)B * 8, hipMemcpyHostToDevice, st));
+      KD_HIP(hipStreamSynchronize(st));
+    }
+    return KD_OK;
+  }
+  {
+    Prof pr("select_segments", st);
+    // positions outside every segment are never kept
+    if (offsets) KD_HIP(kd::launch_fill_u8(mask_out, 0, S, st));
+    KD_HIP(kd::launch_select_segments(signal, offsets, B, S, num, den, mask_out, thresholds_out, st));
+  }
+  return compact_mask(L, ws, S, mask_out, idx_out, count_out, st);
+}
+
+int kd_select_above(const kd_problem* p, const double* signal, double tau, uint8_t* mask_out,
+                    int32_t* idx_out, int64_t* count_out, void* ws, size_t ws_bytes,
+                    void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!count_out) return KD_ERR_NULL;
+  if (p->S > 0 && (!signal || !mask_out)) return KD_ERR_NULL;
+  if (std::isnan(tau)) return KD_ERR_ARG;
+  const Layout L = plan(p);
+  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  *count_out = 0;
+  if (p->S == 0) return KD_OK;
+  {
+    Prof pr("select_above", st);
+    KD_HIP(kd::launch_select_above(signal, p->S, tau, mask_out, st));
+  }
+  return compact_mask(L, ws, p->S, mask_out, idx_out, count_out, st);
 }
 
 int kd_select_top_fraction(const kd_problem* p, const void* hidden, const void* W,

@@ -72,7 +72,22 @@ struct CombineArgs {
 struct EntCombineArgs {
   int S, V, ncu;
   const float* em; const double* es; const double* eu;
-  double* entropy;
+  double* entropy;                    // or NULL
+  double* lse;                        // natural log-normaliser at T = 1, or NULL
+};
+
+// Position signals (one wave per position).
+struct SignalArgs {
+  int64_t S;
+  int V, H, K, hw_f32, tl_f32, probs;
+  double invT;
+  const char* hidden; int64_t ldh;
+  const char* W; int64_t ldw;
+  const int32_t* labels;              // [S]
+  const double* lse;                  // [S] at T = 1 (for ce)
+  const int32_t* ids; const void* tl; // teacher rows (for tunc)
+  double* ce;                         // [S] or NULL
+  double* tunc;                       // [S] or NULL
 };
 
 struct DhArgs {
@@ -156,6 +171,13 @@ hipError_t launch_dw(int f32, const DwArgs& a, hipStream_t st);
 hipError_t launch_validate(const int32_t* ids, const void* tl, int tl_f32, int probs, int64_t S,
                            int K, int V, unsigned long long* counters, hipStream_t st);
 hipError_t launch_fill_u8(uint8_t* p, uint8_t v, int64_t n, hipStream_t st);
+
+hipError_t launch_signals(const SignalArgs& a, hipStream_t st);
+hipError_t launch_select_segments(const double* x, const int64_t* off, int64_t B, int64_t S,
+                                  int64_t num, int64_t den, uint8_t* mask, double* thr,
+                                  hipStream_t st);
+hipError_t launch_select_above(const double* x, int64_t S, double tau, uint8_t* mask,
+                               hipStream_t st);
 
 // selection
 struct SelectWs {

@@ -879,7 +879,8 @@ __global__ __launch_bounds__(256) void ent_combine_kernel(EntCombineArgs a) {
     Ssum = Ssum * f1 + S2 * f2;
     M = mn;
   }
-  a.entropy[t] = log(Ssum) - 0.6931471805599453 * U / Ssum;
+  if (a.entropy) a.entropy[t] = log(Ssum) - 0.6931471805599453 * U / Ssum;
+  if (a.lse) a.lse[t] = 0.6931471805599453 * (M + log2(Ssum));
 }
 
 hipError_t launch_ent_combine(const EntCombineArgs& a, hipStream_t st) {

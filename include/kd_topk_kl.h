@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define KD_ABI_VERSION 2
+#define KD_ABI_VERSION 3
 
 typedef enum kd_status {
   KD_OK = 0,
@@ -202,6 +202,64 @@ int kd_select_samples(const kd_problem* problem, const void* hidden, const void*
                       const double* entropy, const int64_t* offsets, int64_t B, int64_t num,
                       int64_t den, uint8_t* mask_out, int32_t* idx_out, int64_t* count_out,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* Position importance signals ("Rethinking Selective Knowledge Distillation",
+ * Method section 1: student cross-entropy, teacher uncertainty 1 - p_t(y_t),
+ * student entropy; the teacher-student KL per position is kd_topk_kl_fwd's
+ * kl_rows). Each output may be NULL; the others are still computed.
+ *   entropy      [device] [S] float64: H(softmax(z_t)) at T = 1, as
+ *                kd_student_entropy (needs hidden, W)
+ *   ce           [device] [S] float64: log sum_v exp(z_tv) - z_{t,y_t} at T = 1,
+ *                the student's cross-entropy on the label (needs hidden, W,
+ *                labels); NaN where the label is outside [0, V)
+ *   teacher_unc  [device] [S] float64: 1 - p_t(y_t), p_t the row's KD target
+ *                (renormalised top-K softmax at the problem's temperature, or
+ *                the given probabilities for KD_TEACHER_PROBS), entries sharing
+ *                the label's id adding; 1 when the label is not among the ids;
+ *                NaN where the label is outside [0, V) or the teacher row takes
+ *                no part (needs topk_ids, topk_logits, labels)
+ *   labels       [device] [S] int32 next-token ids
+ * Entropy and ce share one projection sweep over the vocabulary; ce adds an
+ * fp64 dot product per position and teacher_unc an fp64 pass over the K
+ * entries. Does not synchronise the host.                                    */
+int kd_position_signals(const kd_problem* problem, const void* hidden, const void* W,
+                        const int32_t* topk_ids, const void* topk_logits, const int32_t* labels,
+                        double* entropy, double* ce, double* teacher_unc, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* Top-k% positions by a signal, per segment ("Rethinking Selective Knowledge
+ * Distillation", Method section 1: top-k% selection; per sequence when a batch
+ * of sequences is given as segments). Segment b is positions
+ * [offsets[b], offsets[b+1]); it keeps floor(num*len_b/den) positions, highest
+ * signal first, lower index first among equal values (-0 equals +0). NaN
+ * signals are never kept, so a segment with fewer non-NaN positions keeps
+ * fewer. Positions outside every segment are not kept. The decision is exact
+ * on the given values.
+ *   signal          [device] [S] float64 (not modified)
+ *   offsets         [device] [B+1] int64, non-decreasing within [0, S]
+ *                   (KD_ERR_ARG otherwise), or NULL: one segment [0, S) (B is
+ *                   then taken as 1)
+ *   num, den        0 <= num <= den, 0 < den < 2^31 (KD_ERR_ARG otherwise)
+ *   mask_out        [device] [S] uint8: 1 = kept
+ *   idx_out         [device] [S] int32 or NULL: kept positions in ascending
+ *                   order in the first count entries
+ *   thresholds_out  [device] [B] float64 or NULL: per segment, the smallest
+ *                   kept value (NaN when none is kept): a global threshold for
+ *                   kd_select_above when computed over a pooled set of signals
+ *   count_out       [host] number kept. Synchronises the host with the stream. */
+int kd_select_by_signal(const kd_problem* problem, const double* signal, const int64_t* offsets,
+                        int64_t B, int64_t num, int64_t den, uint8_t* mask_out,
+                        int32_t* idx_out, double* thresholds_out, int64_t* count_out, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* Global threshold policy (GLS, "Rethinking Selective Knowledge
+ * Distillation", Method section 1, named there without a definition; read
+ * here as one threshold shared by all positions): keep signal >= tau. NaN is
+ * never kept; tau must not be NaN (KD_ERR_ARG).
+ *   mask_out, idx_out, count_out as for kd_select_by_signal.                 */
+int kd_select_above(const kd_problem* problem, const double* signal, double tau,
+                    uint8_t* mask_out, int32_t* idx_out, int64_t* count_out, void* ws,
+                    size_t ws_bytes, void* stream);
 
 /* Cache validation ("operations": id range and missing positions).
  *   n_bad_id     [host] ids outside [0, V)

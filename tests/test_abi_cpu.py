@@ -31,7 +31,7 @@ def test_header_symbols_exported():
 
 
 def test_version_and_status_strings():
-    assert kd.kd_abi_version() == 2
+    assert kd.kd_abi_version() == 3
     for c in range(11):
         assert kd.kd_status_str(c).startswith("KD_")
     assert "unknown" in kd.kd_status_str(99)
@@ -96,3 +96,42 @@ def test_workspace_linear_in_S_and_bounded_in_V():
     a = kd.kd_topk_kl_workspace_bytes(prob(S=32768, H=2880, V=201088, K=100, chunk=1024))
     b = kd.kd_topk_kl_workspace_bytes(prob(S=32768, H=2880, V=201088, K=100, chunk=2048))
     assert b - a >= 1024 * 201088 * 2
+
+
+def test_signal_and_selection_argument_errors():
+    """Host-side rejections of the position-signal and selection entry points."""
+    p = prob()
+    fake = ctypes.c_void_p(0x1000)
+    ws = ctypes.c_void_p(0x10000)
+    need = kd.kd_topk_kl_workspace_bytes(p)
+    cnt = ctypes.c_int64(0)
+    sel = kd.lib.kd_select_by_signal
+    for num, den in [(1, 0), (3, 2), (-1, 4), (1, 1 << 31)]:
+        assert sel(ctypes.byref(p), fake, None, 1, num, den, fake, None, None, ctypes.byref(cnt), ws,
+                   need, None) == KD_ERR_ARG
+    assert sel(ctypes.byref(p), fake, fake, -1, 1, 2, fake, None, None, ctypes.byref(cnt), ws,
+               need, None) == KD_ERR_ARG
+    assert sel(ctypes.byref(p), fake, fake, 129, 1, 2, fake, None, None, ctypes.byref(cnt), ws,
+               need, None) == KD_ERR_ARG                      # B > S
+    assert sel(ctypes.byref(p), fake, None, 1, 1, 2, fake, None, None, None, ws, need,
+               None) == KD_ERR_NULL
+    assert sel(ctypes.byref(p), None, None, 1, 1, 2, fake, None, None, ctypes.byref(cnt), ws, need,
+               None) == KD_ERR_NULL
+    assert sel(ctypes.byref(p), fake, None, 1, 1, 2, fake, None, None, ctypes.byref(cnt), ws,
+               need - 1, None) == KD_ERR_WORKSPACE
+    above = kd.lib.kd_select_above
+    assert above(ctypes.byref(p), fake, float("nan"), fake, None, ctypes.byref(cnt), ws, need,
+                 None) == KD_ERR_ARG
+    assert above(ctypes.byref(p), None, 0.0, fake, None, ctypes.byref(cnt), ws, need,
+                 None) == KD_ERR_NULL
+    sig = kd.lib.kd_position_signals
+    # ce or teacher uncertainty without labels, teacher uncertainty without the cache
+    assert sig(ctypes.byref(p), fake, fake, fake, fake, None, None, fake, None, ws, need,
+               None) == KD_ERR_NULL
+    assert sig(ctypes.byref(p), fake, fake, None, fake, fake, None, None, fake, ws, need,
+               None) == KD_ERR_NULL
+    assert sig(ctypes.byref(p), None, fake, fake, fake, fake, fake, None, None, ws, need,
+               None) == KD_ERR_NULL
+    bad = prob(T=0.0)
+    assert sig(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, None, None, ws, need,
+               None) == KD_ERR_TEMPERATURE
