@@ -19,6 +19,7 @@ __all__ = [
     "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_student_entropy",
     "kd_select_top_fraction", "kd_select_samples", "kd_validate_topk",
     "kd_position_signals", "kd_select_by_signal", "kd_select_above",
+    "kd_select_top_fraction_segments",
     "kd_teacher_topk_workspace_bytes", "kd_teacher_topk",
     "kd_profile_enable", "kd_profile_read", "kd_profile_reset",
     "KDTopKKL", "kd_topk_kl", "LIB_PATH",
@@ -74,6 +75,10 @@ lib.kd_position_signals.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, cty
 lib.kd_select_by_signal.restype = ctypes.c_int
 lib.kd_select_by_signal.argtypes = [_PP, _P, _P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                     _P, _P, _P, _I64P, _P, ctypes.c_size_t, _P]
+lib.kd_select_top_fraction_segments.restype = ctypes.c_int
+lib.kd_select_top_fraction_segments.argtypes = [_PP, _P, _P, _P, _P, ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_int64, _P, _P, _I64P, _P, ctypes.c_size_t,
+                                                _P]
 lib.kd_select_above.restype = ctypes.c_int
 lib.kd_select_above.argtypes = [_PP, _P, ctypes.c_double, _P, _P, _I64P, _P, ctypes.c_size_t, _P]
 lib.kd_validate_topk.restype = ctypes.c_int
@@ -318,6 +323,28 @@ def kd_select_by_signal(signal, offsets=None, num=20, den=100, workspace=None):
                                    int(den), _ptr(mask), _ptr(idx), _ptr(thr), ctypes.byref(cnt),
                                    _ptr(ws), ws.numel(), _stream(dev)), "kd_select_by_signal")
     return mask[:S], idx[: cnt.value], cnt.value, thr[:B]
+
+
+def kd_select_top_fraction_segments(entropy, offsets, hidden, W, num=20, den=100, chunk=1024,
+                                    workspace=None):
+    """Per-sequence top num/den by entropy (segments [offsets[b], offsets[b+1])), decided
+    as fp64 entropies decide. Returns (mask u8 [S], idx i32 [count], count)."""
+    S, H = hidden.shape
+    if offsets.dtype != torch.int64 or not offsets.is_contiguous() or offsets.numel() < 1:
+        raise ValueError("offsets must be a contiguous int64 tensor of B+1 entries")
+    B = offsets.numel() - 1
+    p = make_problem(S, H, W.shape[0], 1, chunk, 1.0, _dtype_code(hidden.dtype), KD_BF16)
+    dev = hidden.device
+    ws = _workspace(p, dev, workspace)
+    mask = torch.empty(max(S, 1), dtype=torch.uint8, device=dev)
+    idx = torch.empty(max(S, 1), dtype=torch.int32, device=dev)
+    cnt = ctypes.c_int64(0)
+    _check(lib.kd_select_top_fraction_segments(ctypes.byref(p), _ptr(hidden), _ptr(W),
+                                               _ptr(entropy), _ptr(offsets), int(B), int(num),
+                                               int(den), _ptr(mask), _ptr(idx), ctypes.byref(cnt),
+                                               _ptr(ws), ws.numel(), _stream(dev)),
+           "kd_select_top_fraction_segments")
+    return mask[:S], idx[: cnt.value], cnt.value
 
 
 def kd_select_above(signal, tau, workspace=None):

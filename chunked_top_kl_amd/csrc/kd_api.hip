@@ -117,7 +117,7 @@ struct Layout {
   size_t em, es, eu;
   size_t band, refined, scal, dscal, rpart, xb, counters;
   size_t smean, spos, pent, pstart;
-  size_t lse64;
+  size_t lse64, segw;
   size_t total;
   int64_t C;          // rows per backward chunk (<= S, >= 1)
   int64_t Vp;         // vocabulary columns of the gradient tile: round_up(V, 8)
@@ -201,6 +201,7 @@ Layout plan(const kd_problem* p) {
   L.pent = take((size_t)kSampleBandPositions * 8);
   L.pstart = take((size_t)(kSampleBandCap + 1) * 4);
   L.lse64 = take(Sx * 8);
+  L.segw = take(Sx * 4 * 4);
   L.total = off;
   return L;
 }
@@ -662,6 +663,92 @@ int kd_select_by_signal(const kd_problem* p, const double* signal, const int64_t
     // positions outside every segment are never kept
     if (offsets) KD_HIP(kd::launch_fill_u8(mask_out, 0, S, st));
     KD_HIP(kd::launch_select_segments(signal, offsets, B, S, num, den, mask_out, thresholds_out, st));
+  }
+  return compact_mask(L, ws, S, mask_out, idx_out, count_out, st);
+}
+
+int kd_select_top_fraction_segments(const kd_problem* p, const void* hidden, const void* W,
+                                    const double* entropy, const int64_t* offsets, int64_t B,
+                                    int64_t num, int64_t den, uint8_t* mask_out, int32_t* idx_out,
+                                    int64_t* count_out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!count_out) return KD_ERR_NULL;
+  if (den <= 0 || den > 0x7FFFFFFF || num < 0 || num > den) return KD_ERR_ARG;
+  if (B < 0 || B > std::max<int64_t>(p->S, 1)) return KD_ERR_ARG;
+  const int64_t S = p->S;
+  if (S > 0 && (!mask_out || !W || !hidden || !entropy || (B > 0 && !offsets))) return KD_ERR_NULL;
+  const Layout L = plan(p);
+  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  *count_out = 0;
+  if (S == 0) return KD_OK;
+  KD_HIP(kd::launch_fill_u8(mask_out, 0, S, st));   // positions outside every segment
+  if (B == 0) return KD_OK;
+  int32_t* flag = at<int32_t>(ws, L.scal) + 8;
+  KD_HIP(kd::launch_sample_check(offsets, B, S, flag, st));
+  int32_t h_flag = 0;
+  KD_HIP(hipMemcpyAsync(&h_flag, flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  KD_HIP(hipStreamSynchronize(st));
+  if (h_flag) return KD_ERR_ARG;
+  double* thr = at<double>(ws, L.smean);
+  int32_t* nband = at<int32_t>(ws, L.segw);
+  int32_t* nabove = nband + S;
+  int32_t* boff = nband + 2 * S;
+  int32_t* need = nband + 3 * S;
+  const double eps2 = 2.0 * kSelectEps;
+  {
+    // the decision on the sweep's entropies, and each segment's k-th largest
+    Prof pr("select_segments", st);
+    KD_HIP(kd::launch_select_segments(entropy, offsets, B, S, num, den, mask_out, thr, st));
+    KD_HIP(kd::launch_seg_band_count(entropy, offsets, B, thr, eps2, nband, nabove, st));
+  }
+  std::vector<int32_t> hb((size_t)B), ha((size_t)B), ho((size_t)B), hn((size_t)B);
+  std::vector<int64_t> hoff((size_t)B + 1);
+  KD_HIP(hipMemcpyAsync(hb.data(), nband, (size_t)B * 4, hipMemcpyDeviceToHost, st));
+  KD_HIP(hipMemcpyAsync(ha.data(), nabove, (size_t)B * 4, hipMemcpyDeviceToHost, st));
+  KD_HIP(hipMemcpyAsync(hoff.data(), offsets, (size_t)(B + 1) * 8, hipMemcpyDeviceToHost, st));
+  KD_HIP(hipStreamSynchronize(st));
+  // segments whose band straddles the cut are refined, up to the list's size;
+  // the others keep the decision on the sweep's entropies
+  int64_t total = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t k = (num * (hoff[b + 1] - hoff[b])) / den;
+    const int64_t nd = k - ha[b];
+    hn[b] = (int32_t)nd;
+    ho[b] = -1;
+    if (nd > 0 && nd < hb[b] && total + hb[b] <= kSampleBandPositions) {
+      ho[b] = (int32_t)total;
+      total += hb[b];
+    }
+  }
+  if (total > 0) {
+    KD_HIP(hipMemcpyAsync(boff, ho.data(), (size_t)B * 4, hipMemcpyHostToDevice, st));
+    KD_HIP(hipMemcpyAsync(need, hn.data(), (size_t)B * 4, hipMemcpyHostToDevice, st));
+    int32_t* plist = at<int32_t>(ws, L.spos);
+    double* pent = at<double>(ws, L.pent);
+    KD_HIP(kd::launch_seg_band_list(entropy, offsets, B, thr, eps2, boff, plist, st));
+    kd::SelectWs w;
+    std::memset(&w, 0, sizeof(w));
+    w.rpart = at<double>(ws, L.rpart);
+    const int f32 = p->hw_dtype == KD_F32;
+    const int64_t ld = p->H * L.esz;
+    const int nblk = (int)refine_blocks(p->V);
+    for (int64_t rs = 0; rs < total; rs += kSampleBandCap) {
+      const int n = (int)std::min<int64_t>(kSampleBandCap, total - rs);
+      kd::SelectWs wr = w;
+      wr.band = plist + rs;
+      for (int o = 0; o < n; o += kRefineBatch) {
+        Prof pr("select_refine_fp64", st);
+        KD_HIP(kd::launch_refine(f32, (const char*)hidden, ld, (const char*)W, ld, (int)p->V,
+                                 (int)p->H, wr, at<double>(ws, L.xb), o,
+                                 std::min(kRefineBatch, n - o), nblk, st));
+      }
+      KD_HIP(kd::launch_sample_refined_entropy(wr, n, nblk, pent + rs, st));
+    }
+    Prof pr("select_segments_final", st);
+    KD_HIP(kd::launch_seg_band_final(B, boff, nband, need, plist, pent, mask_out, st));
   }
   return compact_mask(L, ws, S, mask_out, idx_out, count_out, st);
 }

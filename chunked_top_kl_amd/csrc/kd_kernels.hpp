@@ -178,6 +178,13 @@ hipError_t launch_select_segments(const double* x, const int64_t* off, int64_t B
                                   hipStream_t st);
 hipError_t launch_select_above(const double* x, int64_t S, double tau, uint8_t* mask,
                                hipStream_t st);
+hipError_t launch_seg_band_count(const double* E, const int64_t* off, int64_t B, const double* thr,
+                                 double eps2, int32_t* nband, int32_t* nabove, hipStream_t st);
+hipError_t launch_seg_band_list(const double* E, const int64_t* off, int64_t B, const double* thr,
+                                double eps2, const int32_t* boff, int32_t* list, hipStream_t st);
+hipError_t launch_seg_band_final(int64_t B, const int32_t* boff, const int32_t* nband,
+                                 const int32_t* need, const int32_t* list, const double* pent,
+                                 uint8_t* mask, hipStream_t st);
 
 // selection
 struct SelectWs {

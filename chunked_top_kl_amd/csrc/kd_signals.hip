@@ -208,6 +208,108 @@ hipError_t launch_select_segments(const double* x, const int64_t* off, int64_t B
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Per-sequence top-k% by student entropy, decided as fp64 entropies decide.
+// The sweep's entropies E are within eps of fp64, so with T_b the k_b-th
+// largest E of segment b every entry with E > T_b + 2 eps is in the fp64 top
+// k_b and every entry with E < T_b - 2 eps is out; the band in between is
+// recomputed in fp64 and ranked (entropy desc, index asc) when it straddles
+// the cut.
+
+// per segment: the band's size and the count above it (0 when nothing is kept)
+__global__ __launch_bounds__(256) void seg_band_count_kernel(const double* E, const int64_t* off,
+                                                             const double* thr, double eps2,
+                                                             int32_t* nband, int32_t* nabove) {
+  __shared__ int red[4];
+  const int64_t b = blockIdx.x;
+  const int64_t a0 = off[b], a1 = off[b + 1];
+  const double T = thr[b];
+  int nb = 0, na = 0;
+  if (!isnan(T)) {
+    for (int64_t t = a0 + threadIdx.x; t < a1; t += 256) {
+      const double d = E[t] - T;
+      nb += (fabs(d) <= eps2) ? 1 : 0;
+      na += (d > eps2) ? 1 : 0;
+    }
+  }
+  int tb = 0, ta = 0;
+  block_scan_excl(nb, tb, red);
+  block_scan_excl(na, ta, red);
+  if (threadIdx.x == 0) {
+    nband[b] = tb;
+    nabove[b] = ta;
+  }
+}
+
+// the band positions of each refined segment (boff[b] >= 0), in index order
+__global__ __launch_bounds__(256) void seg_band_list_kernel(const double* E, const int64_t* off,
+                                                            const double* thr, double eps2,
+                                                            const int32_t* boff, int32_t* list) {
+  __shared__ int red[4];
+  const int64_t b = blockIdx.x;
+  const int o = boff[b];
+  if (o < 0) return;
+  const int64_t a0 = off[b], a1 = off[b + 1];
+  const double T = thr[b];
+  int seen = 0;
+  for (int64_t c0 = a0; c0 < a1; c0 += 256) {
+    const int64_t t = c0 + threadIdx.x;
+    const bool in = t < a1 && fabs(E[t] - T) <= eps2;
+    int n = 0;
+    const int r = block_scan_excl(in ? 1 : 0, n, red);
+    if (in) list[o + seen + r] = (int32_t)t;
+    seen += n;
+  }
+}
+
+// a refined segment's band: keep the need[b] entries of largest fp64 entropy,
+// lower index first among equal values
+__global__ __launch_bounds__(256) void seg_band_final_kernel(const int32_t* boff,
+                                                             const int32_t* nband,
+                                                             const int32_t* need,
+                                                             const int32_t* list,
+                                                             const double* pent, uint8_t* mask) {
+  const int64_t b = blockIdx.x;
+  const int o = boff[b];
+  if (o < 0) return;
+  const int m = nband[b], k = need[b];
+  for (int i = threadIdx.x; i < m; i += 256) {
+    const double e = pent[o + i];
+    const int pos = list[o + i];
+    int rank = 0;
+    for (int j = 0; j < m; ++j) {
+      const double f = pent[o + j];
+      rank += (f > e || (f == e && list[o + j] < pos)) ? 1 : 0;
+    }
+    mask[pos] = rank < k ? 1 : 0;
+  }
+}
+
+hipError_t launch_seg_band_count(const double* E, const int64_t* off, int64_t B, const double* thr,
+                                 double eps2, int32_t* nband, int32_t* nabove, hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(seg_band_count_kernel, dim3((unsigned)B), dim3(256), 0, st, E, off, thr, eps2,
+                     nband, nabove);
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_band_list(const double* E, const int64_t* off, int64_t B, const double* thr,
+                                double eps2, const int32_t* boff, int32_t* list, hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(seg_band_list_kernel, dim3((unsigned)B), dim3(256), 0, st, E, off, thr, eps2,
+                     boff, list);
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_band_final(int64_t B, const int32_t* boff, const int32_t* nband,
+                                 const int32_t* need, const int32_t* list, const double* pent,
+                                 uint8_t* mask, hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(seg_band_final_kernel, dim3((unsigned)B), dim3(256), 0, st, boff, nband, need,
+                     list, pent, mask);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void select_above_kernel(const double* x, int64_t S, double tau,
                                                            uint8_t* mask) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;

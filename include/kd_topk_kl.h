@@ -252,6 +252,25 @@ int kd_select_by_signal(const kd_problem* problem, const double* signal, const i
                         int32_t* idx_out, double* thresholds_out, int64_t* count_out, void* ws,
                         size_t ws_bytes, void* stream);
 
+/* Per-sequence top-k% by student entropy (SE-KD, "Rethinking Selective
+ * Knowledge Distillation", Method section 2, applied within each sequence of a
+ * batch): segment b = positions [offsets[b], offsets[b+1]) keeps
+ * floor(num*len_b/den) positions of highest entropy, lower index first on ties.
+ * As in kd_select_top_fraction, the entries within the entropy error bound of
+ * a segment's cut are recomputed in fp64 from hidden and W before the
+ * decision, so the kept set is the one fp64 entropies give (beyond 65536 such
+ * entries in all, the remaining segments are decided on the sweep's values).
+ *   entropy     [device] [S] float64 from kd_student_entropy (not modified)
+ *   offsets     [device] [B+1] int64, non-decreasing within [0, S] (KD_ERR_ARG
+ *               otherwise); positions outside every segment are not kept
+ *   num, den    0 <= num <= den, 0 < den < 2^31
+ *   mask_out, idx_out, count_out as for kd_select_top_fraction.            */
+int kd_select_top_fraction_segments(const kd_problem* problem, const void* hidden,
+                                    const void* W, const double* entropy,
+                                    const int64_t* offsets, int64_t B, int64_t num, int64_t den,
+                                    uint8_t* mask_out, int32_t* idx_out, int64_t* count_out,
+                                    void* ws, size_t ws_bytes, void* stream);
+
 /* Global threshold policy (GLS, "Rethinking Selective Knowledge
  * Distillation", Method section 1, named there without a definition; read
  * here as one threshold shared by all positions): keep signal >= tau. NaN is

@@ -135,3 +135,22 @@ def test_signal_and_selection_argument_errors():
     bad = prob(T=0.0)
     assert sig(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, None, None, ws, need,
                None) == KD_ERR_TEMPERATURE
+
+
+def test_per_sequence_selection_argument_errors():
+    p = prob()
+    fake = ctypes.c_void_p(0x1000)
+    ws = ctypes.c_void_p(0x10000)
+    need = kd.kd_topk_kl_workspace_bytes(p)
+    cnt = ctypes.c_int64(0)
+    f = kd.lib.kd_select_top_fraction_segments
+    assert f(ctypes.byref(p), fake, fake, fake, fake, 4, 3, 2, fake, None, ctypes.byref(cnt), ws,
+             need, None) == KD_ERR_ARG
+    assert f(ctypes.byref(p), fake, fake, fake, fake, 129, 1, 2, fake, None, ctypes.byref(cnt), ws,
+             need, None) == KD_ERR_ARG
+    assert f(ctypes.byref(p), fake, fake, fake, None, 4, 1, 2, fake, None, ctypes.byref(cnt), ws,
+             need, None) == KD_ERR_NULL
+    assert f(ctypes.byref(p), None, fake, fake, fake, 4, 1, 2, fake, None, ctypes.byref(cnt), ws,
+             need, None) == KD_ERR_NULL
+    assert f(ctypes.byref(p), fake, fake, fake, fake, 4, 1, 2, fake, None, ctypes.byref(cnt), ws,
+             need - 1, None) == KD_ERR_WORKSPACE

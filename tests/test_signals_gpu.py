@@ -183,3 +183,62 @@ def test_select_rejects_bad_offsets(kd):
     for off in ([0, 5, 3], [0, 11], [-1, 4]):
         with pytest.raises(kd.KdError):
             kd.kd_select_by_signal(x, torch.tensor(off, dtype=torch.int64, device="cuda"), 1, 2)
+
+
+def test_signals_and_selection_full_size(kd):
+    """The entropy-selective workload's shapes (S=32768 H=2048 V=151936 K=100,
+    T=1): signals of every position on the GPU, the oracle at sampled rows;
+    per-sequence selection over 32 sequences of random lengths covering all
+    positions, bit for bit on a seeded signal."""
+    S, H, V, K = 32768, 2048, 151936, 100
+    p = make_problem(S, H, V, K, T=1.0, chunk=1024, seed=1005)
+    hidden, W, ids, tl = to_device(p)
+    labels = _labels(p, 440)
+    got = kd.kd_position_signals(hidden, W, ids, tl, torch.from_numpy(labels).cuda(), T=p.T)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(441)
+    rows = np.unique(np.concatenate([[0, S - 1], rng.choice(S, 94, replace=False)]))
+    ref = oracle_position_signals(p.hidden[rows], p.W, p.ids[rows], p.tlogits[rows], labels[rows],
+                                  T=p.T, chunk=32)
+    assert np.max(np.abs(got["entropy"].cpu().numpy()[rows] - ref["entropy"])) <= ENT_TOL
+    for name, tol in (("ce", CE_TOL), ("teacher_unc", TU_TOL)):
+        g, r = got[name].cpu().numpy()[rows], ref[name]
+        assert np.array_equal(np.isnan(g), np.isnan(r)), name
+        ok = ~np.isnan(r)
+        assert float(np.max(np.abs(g[ok] - r[ok]))) <= tol, name
+    x = np.round(rng.standard_normal(S), 3)              # ties at 1e-3 resolution
+    cuts = np.sort(rng.choice(np.arange(1, S), 31, replace=False))
+    off = np.concatenate([[0], cuts, [S]])
+    _select(kd, x, off, 20, 100)
+
+
+@pytest.mark.parametrize("case", ["spread", "crowded"])
+def test_per_sequence_entropy_selection(kd, case):
+    """SE-KD within each sequence (kd_select_top_fraction_segments): the kept set
+    equals the one fp64 entropies give, bit for bit. Crowded entropies (closer
+    than the sweep's error bound) make the fp64 band refinement decide; the
+    test asserts that it ran."""
+    from oracle import oracle_entropy
+    rng = np.random.default_rng(450)
+    lens = rng.integers(1, 200, size=24)
+    lens[5] = 0
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    S = int(off[-1]) + 13                               # positions past the last segment
+    p = make_problem(S, 128, 4001, 4, seed=451, hidden_std=(0.05 if case == "crowded" else 1.5))
+    hidden, W, _, _ = to_device(p)
+    ent = kd.kd_student_entropy(hidden, W)
+    toff = torch.from_numpy(off).cuda()
+    kd.kd_profile_reset()
+    kd.kd_profile_enable(True)
+    mask, idx, cnt = kd.kd_select_top_fraction_segments(ent, toff, hidden, W, 30, 100)
+    torch.cuda.synchronize()
+    kd.kd_profile_enable(False)
+    steps = kd.kd_profile_read()
+    kd.kd_profile_reset()
+    ref_e = oracle_entropy(p.hidden, p.W, chunk=500)
+    rmask, ridx, rc, _ = oracle_select_by_signal(ref_e, off, 30, 100)
+    assert cnt == rc
+    assert np.array_equal(mask.cpu().numpy(), rmask)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    if case == "crowded":
+        assert "select_refine_fp64" in steps
