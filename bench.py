@@ -213,6 +213,66 @@ def teacher_leg(kd, torch, wl, t, p, steps=3, warmup=1, cpu_rows=64, cpu=True):
     return out
 
 
+def selection_leg(kd, torch, wl, t, steps=3, warmup=1, n_seq=32, seed=77):
+    """Position signals and selection policies at the workload's shapes: all S
+    positions as n_seq sequences of equal length, labels drawn uniformly. Times
+    kd_position_signals (one entropy sweep at T = 1, counted as 2*S*H*V FLOP,
+    plus the label dot products and teacher rows), per-sequence SE-KD
+    selection (20%), per-sequence top 20% by cross-entropy, sample selection
+    by mean entropy (20%) and a global threshold."""
+    S, H, V = wl["S"], wl["H"], wl["V"]
+    hidden, W, ids, tl = t
+    rng = np.random.default_rng(seed)
+    labels = torch.from_numpy(rng.integers(0, V, size=S).astype(np.int32)).cuda()
+    off = torch.from_numpy((np.arange(n_seq + 1, dtype=np.int64) * S) // n_seq).cuda()
+    prob = kd.make_problem(S, H, V, wl["K"], wl["chunk"], wl["T"], kd.KD_BF16, kd.KD_BF16)
+    ws = torch.empty(kd.kd_topk_kl_workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+
+    def timed(fn):
+        for _ in range(warmup):
+            r = fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            r = fn()
+        torch.cuda.synchronize()
+        return r, (time.perf_counter() - t0) * 1000.0 / steps
+
+    kd.kd_profile_reset()
+    kd.kd_profile_enable(True)
+    sig, t_sig = timed(lambda: kd.kd_position_signals(hidden, W, ids, tl, labels, T=wl["T"],
+                                                      workspace=ws))
+    ent, ce = sig["entropy"], sig["ce"]
+    (_, _, k_seq), t_seq = timed(lambda: kd.kd_select_top_fraction_segments(
+        ent, off, hidden, W, 20, 100, workspace=ws))
+    (_, _, k_ce, thr), t_ce = timed(lambda: kd.kd_select_by_signal(ce, off, 20, 100, workspace=ws))
+    (_, _, k_smp), t_smp = timed(lambda: kd.kd_select_samples(ent, off, hidden, W, 20, 100,
+                                                              workspace=ws))
+    tau = float(torch.quantile(ce[: min(S, 1 << 20)].float(), 0.8))
+    (_, _, k_thr), t_thr = timed(lambda: kd.kd_select_above(ce, tau, workspace=ws))
+    kd.kd_profile_enable(False)
+    prof = kd.kd_profile_read()
+    kd.kd_profile_reset()
+    calls = steps + warmup
+    kernels = {name: dict(launches_per_call=round(n / calls, 2), avg_ms=round(tot / max(n, 1), 5))
+               for name, (n, tot) in prof.items()}
+    es = kernels.get("entropy_sweep")
+    sweep_tf = None
+    if es:
+        sweep_tf = round(2.0 * S * H * V / (es["avg_ms"] / 1000.0) / 1e12, 1)
+    out = dict(workload=f"{wl['name']}; {n_seq} sequences of {S // n_seq} positions",
+               signals_ms=round(t_sig, 3), entropy_sweep_tflops=sweep_tf,
+               entropy_sweep_roofline_frac=(round(sweep_tf / PEAK_BF16_TFLOPS, 4) if sweep_tf else None),
+               per_sequence_sekd_ms=round(t_seq, 3), per_sequence_sekd_kept=int(k_seq),
+               per_sequence_ce_ms=round(t_ce, 3), per_sequence_ce_kept=int(k_ce),
+               sample_select_ms=round(t_smp, 3), samples_kept=int(k_smp),
+               threshold_ms=round(t_thr, 3), threshold_kept=int(k_thr), kernels=kernels)
+    log(f"[bench] selection leg: signals {t_sig:.2f} ms, per-sequence SE-KD {t_seq:.2f} ms")
+    del ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def mem_sweep(kd, torch, sizes, seed=1004):
     """Peak device memory of one fwd+bwd at the 256K-context shapes for several S."""
     from kd_synth import make_problem
@@ -265,6 +325,8 @@ def main():
                     help="skip the fwd+bwd timing and peak memory at chunks 512/1024/2048")
     ap.add_argument("--no-teacher", action="store_true",
                     help="skip the teacher top-K cache writer leg")
+    ap.add_argument("--no-selection", action="store_true",
+                    help="skip the position-signal and selection-policy leg")
     ap.add_argument("--teacher-only", action="store_true",
                     help="time only the teacher top-K cache writer (steps / warmup calls) and "
                          "print its line")
@@ -401,6 +463,8 @@ def main():
         result["chunk_sweep"] = chunk_sweep(kd, torch, wl, t, [512, 1024, 2048])
     if not args.no_teacher and args.workload == "c3":
         result["teacher_topk"] = teacher_leg(kd, torch, wl, t, p, cpu=not args.no_cpu_baseline)
+    if not args.no_selection:
+        result["selection"] = selection_leg(kd, torch, wl, t)
     if not args.no_mem_sweep:
         sizes = [int(x) for x in args.mem_sizes.split(",") if x]
         del t
