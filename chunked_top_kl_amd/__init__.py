@@ -19,7 +19,7 @@ __all__ = [
     "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_student_entropy",
     "kd_select_top_fraction", "kd_select_samples", "kd_validate_topk",
     "kd_position_signals", "kd_select_by_signal", "kd_select_above",
-    "kd_select_top_fraction_segments",
+    "kd_select_top_fraction_segments", "kd_validate_topk_order",
     "kd_teacher_topk_workspace_bytes", "kd_teacher_topk",
     "kd_profile_enable", "kd_profile_read", "kd_profile_reset",
     "KDTopKKL", "kd_topk_kl", "LIB_PATH",
@@ -81,6 +81,8 @@ lib.kd_select_top_fraction_segments.argtypes = [_PP, _P, _P, _P, _P, ctypes.c_in
                                                 _P]
 lib.kd_select_above.restype = ctypes.c_int
 lib.kd_select_above.argtypes = [_PP, _P, ctypes.c_double, _P, _P, _I64P, _P, ctypes.c_size_t, _P]
+lib.kd_validate_topk_order.restype = ctypes.c_int
+lib.kd_validate_topk_order.argtypes = [_PP, _P, _P, _I64P, _I64P, _P, ctypes.c_size_t, _P]
 lib.kd_validate_topk.restype = ctypes.c_int
 lib.kd_validate_topk.argtypes = [_PP, _P, _P, _I64P, _I64P, _I64P, _P, ctypes.c_size_t, _P]
 lib.kd_teacher_topk_workspace_bytes.restype = ctypes.c_size_t
@@ -390,6 +392,19 @@ def kd_teacher_topk(hidden, W, K, chunk=2048, out_dtype=torch.bfloat16, workspac
                                _ptr(workspace), workspace.numel(), _stream(dev)),
            "kd_teacher_topk")
     return ids, logits
+
+
+def kd_validate_topk_order(topk_ids, topk_logits, V, workspace=None):
+    """(rows whose K values are not non-increasing, rows holding an id twice)."""
+    S, K = topk_ids.shape
+    p = make_problem(S, 8, V, K, 1, 1.0, KD_BF16, _dtype_code(topk_logits.dtype))
+    dev = topk_ids.device
+    ws = _workspace(p, dev, workspace)
+    a, b = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(lib.kd_validate_topk_order(ctypes.byref(p), _ptr(topk_ids), _ptr(topk_logits),
+                                      ctypes.byref(a), ctypes.byref(b), _ptr(ws), ws.numel(),
+                                      _stream(dev)), "kd_validate_topk_order")
+    return a.value, b.value
 
 
 def kd_validate_topk(topk_ids, topk_logits, V, workspace=None, teacher_probs=False):

@@ -1080,6 +1080,29 @@ int kd_validate_topk(const kd_problem* p, const int32_t* ids, const void* tl, in
   return KD_OK;
 }
 
+int kd_validate_topk_order(const kd_problem* p, const int32_t* ids, const void* tl,
+                           int64_t* n_unsorted_row, int64_t* n_duplicate_row, void* ws,
+                           size_t ws_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!n_unsorted_row || !n_duplicate_row || (p->S > 0 && (!ids || !tl))) return KD_ERR_NULL;
+  const Layout L = plan(p);
+  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  unsigned long long* cnt = at<unsigned long long>(ws, L.counters);
+  {
+    Prof pr("validate_order", st);
+    KD_HIP(kd::launch_validate_order(ids, tl, p->tl_dtype == KD_F32, p->S, (int)p->K, cnt, st));
+  }
+  unsigned long long h[2] = {0, 0};
+  KD_HIP(hipMemcpyAsync(h, cnt, sizeof(h), hipMemcpyDeviceToHost, st));
+  KD_HIP(hipStreamSynchronize(st));
+  *n_unsorted_row = (int64_t)h[0];
+  *n_duplicate_row = (int64_t)h[1];
+  return KD_OK;
+}
+
 int kd_profile_enable(int on) {
   std::lock_guard<std::mutex> g(g_prof_mu);
   g_prof_on = on != 0;

@@ -171,6 +171,8 @@ hipError_t launch_dw(int f32, const DwArgs& a, hipStream_t st);
 hipError_t launch_validate(const int32_t* ids, const void* tl, int tl_f32, int probs, int64_t S,
                            int K, int V, unsigned long long* counters, hipStream_t st);
 hipError_t launch_fill_u8(uint8_t* p, uint8_t v, int64_t n, hipStream_t st);
+hipError_t launch_validate_order(const int32_t* ids, const void* tl, int tl_f32, int64_t S, int K,
+                                 unsigned long long* counters, hipStream_t st);
 
 hipError_t launch_signals(const SignalArgs& a, hipStream_t st);
 hipError_t launch_select_segments(const double* x, const int64_t* off, int64_t B, int64_t S,

@@ -238,6 +238,43 @@ hipError_t launch_validate(const int32_t* ids, const void* tl, int tl_f32, int p
   return hipGetLastError();
 }
 
+// The cache's top-K order ("operations" lists the top-K sorting among the
+// cache checks), one wave per row: [0] rows with some value smaller than the
+// next (NaN compares with nothing), [1] rows holding an id more than once.
+__global__ __launch_bounds__(64) void validate_order_kernel(const int32_t* ids, const void* tl,
+                                                           int tl_f32, int64_t S, int K,
+                                                           unsigned long long* counters) {
+  extern __shared__ int32_t rid[];
+  const int lane = threadIdx.x;
+  const int64_t t = blockIdx.x;
+  if (t >= S) return;
+  int uns = 0, dup = 0;
+  for (int k = lane; k < K; k += 64) {
+    rid[k] = ids[t * K + k];
+    if (k + 1 < K) uns |= load_logit(tl, tl_f32, t * K + k) < load_logit(tl, tl_f32, t * K + k + 1);
+  }
+  __syncthreads();
+  for (int k = lane; k < K; k += 64) {
+    const int id = rid[k];
+    for (int j = k + 1; j < K; ++j) dup |= (rid[j] == id) ? 1 : 0;
+  }
+  uns = __any(uns);
+  dup = __any(dup);
+  if (lane == 0) {
+    if (uns) atomicAdd(&counters[0], 1ull);
+    if (dup) atomicAdd(&counters[1], 1ull);
+  }
+}
+
+hipError_t launch_validate_order(const int32_t* ids, const void* tl, int tl_f32, int64_t S, int K,
+                                 unsigned long long* counters, hipStream_t st) {
+  hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(64), 0, st, counters, 2);
+  if (S > 0)
+    hipLaunchKernelGGL(validate_order_kernel, dim3((unsigned)S), dim3(64), (size_t)K * 4, st, ids,
+                       tl, tl_f32, S, K, counters);
+  return hipGetLastError();
+}
+
 __global__ void fill_u8_kernel(uint8_t* p, uint8_t v, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
     p[i] = v;

@@ -289,6 +289,17 @@ int kd_validate_topk(const kd_problem* problem, const int32_t* topk_ids, const v
                      int64_t* n_bad_id, int64_t* n_empty_row, int64_t* n_bad_logit,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* Cache validation, the top-K order ("operations": the cache checks include
+ * the top-K sorting):
+ *   n_unsorted_row   [host] rows whose K values (logits, or probabilities) are
+ *                    not non-increasing: some value smaller than the next (NaN
+ *                    compares with nothing and is counted by kd_validate_topk)
+ *   n_duplicate_row  [host] rows holding an id more than once
+ * One wave per row, O(K^2) id comparisons per row. Synchronises the host.    */
+int kd_validate_topk_order(const kd_problem* problem, const int32_t* topk_ids,
+                           const void* topk_logits, int64_t* n_unsorted_row,
+                           int64_t* n_duplicate_row, void* ws, size_t ws_bytes, void* stream);
+
 /* Teacher top-K cache writer ("offline top-K logits": the teacher's output
  * is computed once and only each position's K most likely tokens are kept;
  * "operations": the cache stores token ids and logits per position, in top-K

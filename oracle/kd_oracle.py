@@ -91,6 +91,7 @@ __all__ = [
     "oracle_position_signals",
     "oracle_select_by_signal",
     "oracle_select_above",
+    "oracle_validate_topk_order",
 ]
 
 
@@ -392,6 +393,20 @@ def oracle_validate_topk(ids, tlogits, V):
     n_empty = int(np.count_nonzero(np.all(np.isneginf(tl), axis=1))) if tl.size else 0
     n_bad_logit = int(np.count_nonzero(np.isnan(tl) | np.isposinf(tl)))
     return n_bad_id, n_empty, n_bad_logit
+
+
+def oracle_validate_topk_order(ids, tlogits):
+    """The cache's top-K order ([HF "operations"] lists the top-K sorting among
+    the cache checks): rows whose K values are not non-increasing (some value
+    smaller than the next; a NaN compares with nothing), and rows holding an id
+    more than once. Returns (n_unsorted_rows, n_duplicate_rows)."""
+    ids = np.asarray(ids)
+    tl = _f64(tlogits)
+    with np.errstate(invalid="ignore"):
+        unsorted = np.any(tl[:, :-1] < tl[:, 1:], axis=1) if tl.shape[1] > 1 else np.zeros(tl.shape[0], bool)
+    srt = np.sort(ids, axis=1)
+    dup = np.any(srt[:, :-1] == srt[:, 1:], axis=1) if ids.shape[1] > 1 else np.zeros(ids.shape[0], bool)
+    return int(np.count_nonzero(unsorted)), int(np.count_nonzero(dup))
 
 
 def _round_bf16_values(x32: np.ndarray) -> np.ndarray:

@@ -158,3 +158,24 @@ def test_select_above():
     _, i1, _, thr = oracle_select_by_signal(y, None, 15, 100)
     _, i2, _ = oracle_select_above(y, thr[0])
     assert np.array_equal(i1, i2)
+
+
+def test_validate_order_against_scalar_loops():
+    """Top-K order checks of the cache ("operations": the top-K sorting)."""
+    from oracle import oracle_validate_topk_order
+    rng = np.random.default_rng(8)
+    S, K = 60, 7
+    tl = -np.sort(-rng.standard_normal((S, K)), axis=1)
+    ids = np.stack([rng.choice(50, K, replace=False) for _ in range(S)])
+    tl[3, 4], tl[3, 5] = tl[3, 5], tl[3, 4] + 0.5          # an increase
+    tl[9, 2] = np.nan                                       # compares with nothing
+    tl[11, :] = 1.0                                         # equal values are in order
+    tl[12, 6] = -np.inf                                     # -inf last is in order
+    tl[13, 0] = -np.inf                                     # -inf first is not
+    ids[20, 5] = ids[20, 1]
+    ids[21, 6] = ids[21, 0]
+    got = oracle_validate_topk_order(ids, tl)
+    uns = sum(any(tl[t, k] < tl[t, k + 1] for k in range(K - 1)) for t in range(S))
+    dup = sum(len(set(ids[t])) < K for t in range(S))
+    assert got == (uns, dup) == (2, 2)
+    assert oracle_validate_topk_order(ids[:, :1], tl[:, :1]) == (0, 0)

@@ -242,3 +242,34 @@ def test_per_sequence_entropy_selection(kd, case):
     assert np.array_equal(idx.cpu().numpy(), ridx)
     if case == "crowded":
         assert "select_refine_fp64" in steps
+
+
+@pytest.mark.parametrize("K", [1, 100, 700])
+def test_validate_order(kd, K):
+    """Cache top-K order checks (kd_validate_topk_order) against the oracle:
+    planted increases, NaN, -inf first, and duplicate ids; bf16 and fp32."""
+    from oracle import oracle_validate_topk_order
+    p = make_problem(500, 8, 50000, K, seed=460)
+    rng = np.random.default_rng(461)
+    ids = p.ids.copy()
+    tl = p.tlogits.copy()
+    if K > 1:
+        for t in rng.choice(500, 40, replace=False):
+            k = int(rng.integers(0, K - 1))
+            tl[t, k], tl[t, k + 1] = tl[t, k + 1], tl[t, k] + np.float32(1.0)
+        tl[7, K // 2] = np.nan
+        tl[8, 0] = -np.inf
+        for t in rng.choice(500, 25, replace=False):
+            a, b = rng.choice(K, 2, replace=False)
+            ids[t, a] = ids[t, b]
+    for f32 in (False, True):
+        if f32:
+            tlt = torch.from_numpy(np.ascontiguousarray(tl, dtype=np.float32)).cuda()
+            ref_tl = tl
+        else:
+            from kd_synth import bf16_bits_from_f32, f32_from_bf16_bits
+            bits = bf16_bits_from_f32(tl.astype(np.float32))
+            ref_tl = f32_from_bf16_bits(bits)
+            tlt = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+        got = kd.kd_validate_topk_order(torch.from_numpy(ids).cuda(), tlt, p.V)
+        assert got == oracle_validate_topk_order(ids, ref_tl)
