@@ -41,11 +41,14 @@ __device__ inline int xcd_remap(int hid, int total) {
 // Vocabulary-sweep split: a work-group owns one 256-row token tile and a
 // contiguous range of 256-row vocabulary tiles. Choose the number of ranges so
 // that (rounds of work-groups over the CUs) x (tiles per work-group) is least,
-// with at least 8 ranges when the vocabulary allows (so that concurrent
-// work-groups on one XCD share W panels 8 ways and token panels 4 ways).
+// the fewest ranges (at least 6) among equal costs. Fewer, longer ranges put
+// more token tiles and fewer W ranges on an XCD at once: at the 32K-context
+// shapes the forward took 33.3 ms with 10 ranges, 32.3 with 8 and 30.9 with 6
+// or 4 (A/B on one MI355X), and the entropy sweep at the entropy-selective
+// shapes 18.3 ms with 18 ranges and 17.7 with 6.
 __host__ __device__ inline int sweep_splits(int ntok_tiles, int nvt, int ncu) {
   if (ntok_tiles <= 0) return 1;
-  int lo = nvt < 8 ? nvt : 8;
+  int lo = nvt < 6 ? nvt : 6;
   int hi = nvt < 64 ? nvt : 64;
   int best = lo;
   int64_t best_cost = -1;
