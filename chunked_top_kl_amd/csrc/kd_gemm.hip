@@ -228,6 +228,44 @@ __global__ __launch_bounds__(256) void transpose_w_kernel(const T* W, int V, int
   }
 }
 
+// The bf16 transpose with 16-byte accesses on both sides: a 64 (v) x 64 (h)
+// tile is read as 8 granules of 8 h per row and written as 8 granules of 8 v
+// per h row (H and Vp are multiples of 8, so no granule straddles an edge).
+// The LDS tile's row pitch of 66 elements puts the 8 rows read for one output
+// granule in distinct banks.
+__global__ __launch_bounds__(256) void transpose_w_b16_kernel(const uint16_t* W, int V, int H,
+                                                              uint16_t* WT, int Vp, int ldwt) {
+  __shared__ uint16_t tile[64][66];
+  const int v0 = blockIdx.x * 64, h0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int row = pass * 32 + (tid >> 3), g = tid & 7;
+    const int v = v0 + row, h = h0 + 8 * g;
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    if (v < V && h < H) x = *(const uint4*)(W + (int64_t)v * H + h);
+    const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[row][8 * g + 2 * e] = (uint16_t)(w4[e] & 0xFFFFu);
+      tile[row][8 * g + 2 * e + 1] = (uint16_t)(w4[e] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int hh = pass * 32 + (tid >> 3), j = tid & 7;
+    const int h = h0 + hh, v = v0 + 8 * j;
+    if (h < H && v < Vp) {
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[e] = (uint32_t)tile[8 * j + 2 * e][hh] | ((uint32_t)tile[8 * j + 2 * e + 1][hh] << 16);
+      *(uint4*)(WT + (int64_t)h * ldwt + v) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
 hipError_t launch_transpose_w(int f32, const char* W, int V, int H, char* WT, int Vp, int ldwt,
                               hipStream_t st) {
   dim3 grid((unsigned)ceil_div(Vp, 64), (unsigned)ceil_div(H, 64));
@@ -235,8 +273,8 @@ hipError_t launch_transpose_w(int f32, const char* W, int V, int H, char* WT, in
     hipLaunchKernelGGL(transpose_w_kernel<float>, grid, dim3(256), 0, st, (const float*)W, V, H,
                        (float*)WT, Vp, ldwt);
   else
-    hipLaunchKernelGGL(transpose_w_kernel<__bf16>, grid, dim3(256), 0, st, (const __bf16*)W, V,
-                       H, (__bf16*)WT, Vp, ldwt);
+    hipLaunchKernelGGL(transpose_w_b16_kernel, grid, dim3(256), 0, st, (const uint16_t*)W, V, H,
+                       (uint16_t*)WT, Vp, ldwt);
   return hipGetLastError();
 }
 
