@@ -195,6 +195,53 @@ __global__ __launch_bounds__(256) void gather_rows_t_kernel(const char* X, int64
   }
 }
 
+// The same for bf16 with 16-byte accesses: each row of a 64 (r) x 64 (h) tile
+// is read (and copied to xc) as 8 granules of 8 h, and each h row of the
+// output is written as granules of 8 r (H, Cp, ldo and ldx are multiples of
+// 8 elements, so no granule straddles an edge).
+__global__ __launch_bounds__(256) void gather_rows_t_b16_kernel(const char* X, int64_t ldx,
+                                                                const int32_t* idx,
+                                                                const int32_t* nrows_dev,
+                                                                int row_begin, int row_cap, int H,
+                                                                char* out, int64_t ldo, int Cp,
+                                                                char* xc) {
+  __shared__ uint16_t tile[64][66];
+  const int rows = chunk_rows(nrows_dev, row_begin, row_cap);
+  if (rows <= 0) return;
+  const int r0 = blockIdx.x * 64, h0 = blockIdx.y * 64;
+  if (r0 >= Cp) return;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int rr = pass * 32 + (tid >> 3), g = tid & 7;
+    const int r = r0 + rr, h = h0 + 8 * g;
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    if (r < rows && h < H) {
+      x = *(const uint4*)(X + (int64_t)idx[row_begin + r] * ldx + (int64_t)h * 2);
+      *(uint4*)(xc + (int64_t)r * ldx + (int64_t)h * 2) = x;
+    }
+    const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[rr][8 * g + 2 * e] = (uint16_t)(w4[e] & 0xFFFFu);
+      tile[rr][8 * g + 2 * e + 1] = (uint16_t)(w4[e] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int hh = pass * 32 + (tid >> 3), j = tid & 7;
+    const int h = h0 + hh, r = r0 + 8 * j;
+    if (h < H && r < Cp) {
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[e] = (uint32_t)tile[8 * j + 2 * e][hh] | ((uint32_t)tile[8 * j + 2 * e + 1][hh] << 16);
+      *(uint4*)(out + (int64_t)h * ldo + (int64_t)r * 2) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
 hipError_t launch_gather_rows_t(int f32, const char* X, int64_t ldx, const int32_t* idx,
                                 const int32_t* nrows_dev, int row_begin, int row_cap, int H,
                                 char* out, int64_t ldo, int Cp, char* xc, hipStream_t st) {
@@ -203,8 +250,8 @@ hipError_t launch_gather_rows_t(int f32, const char* X, int64_t ldx, const int32
     hipLaunchKernelGGL(gather_rows_t_kernel<float>, grid, dim3(256), 0, st, X, ldx, idx, nrows_dev,
                        row_begin, row_cap, H, out, ldo, Cp, xc);
   else
-    hipLaunchKernelGGL(gather_rows_t_kernel<__bf16>, grid, dim3(256), 0, st, X, ldx, idx,
-                       nrows_dev, row_begin, row_cap, H, out, ldo, Cp, xc);
+    hipLaunchKernelGGL(gather_rows_t_b16_kernel, grid, dim3(256), 0, st, X, ldx, idx, nrows_dev,
+                       row_begin, row_cap, H, out, ldo, Cp, xc);
   return hipGetLastError();
 }
 
