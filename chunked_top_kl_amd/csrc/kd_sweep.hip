@@ -167,26 +167,28 @@ __device__ __forceinline__ bool col_in(int e, int lim) {
   return !TAIL || acc_row(e >> 4, e & 15, 0) < lim;
 }
 
-template <bool TAIL>
-__device__ __forceinline__ float col_max(const float (&z)[64], int vw0, int half, int V) {
+// z(e) gives entry e of the lane's column (an accumulator register, so that
+// the forward keeps no copy of the column in VGPRs)
+template <bool TAIL, class Z>
+__device__ __forceinline__ float col_max(const Z& z, int vw0, int half, int V) {
   const int lim = col_lim<TAIL>(vw0, half, V);
   float mx = -INFINITY;
 #pragma unroll
   for (int e = 0; e < 64; ++e)
-    if (col_in<TAIL>(e, lim)) mx = fmaxf(mx, z[e]);
+    if (col_in<TAIL>(e, lim)) mx = fmaxf(mx, z(e));
   return mx;
 }
 
 // sum of 2^(z c - mn) over the column
-template <bool TAIL>
-__device__ __forceinline__ float col_sum_exp2(const float (&z)[64], float c, float mn, int vw0,
-                                              int half, int V) {
+template <bool TAIL, class Z>
+__device__ __forceinline__ float col_sum_exp2(const Z& z, float c, float mn, int vw0, int half,
+                                              int V) {
   const int lim = col_lim<TAIL>(vw0, half, V);
   float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
   for (int e = 0; e < 64; e += 4) {
-    const float t0 = fast_exp2(fmaf(z[e + 0], c, -mn)), t1 = fast_exp2(fmaf(z[e + 1], c, -mn));
-    const float t2 = fast_exp2(fmaf(z[e + 2], c, -mn)), t3 = fast_exp2(fmaf(z[e + 3], c, -mn));
+    const float t0 = fast_exp2(fmaf(z(e + 0), c, -mn)), t1 = fast_exp2(fmaf(z(e + 1), c, -mn));
+    const float t2 = fast_exp2(fmaf(z(e + 2), c, -mn)), t3 = fast_exp2(fmaf(z(e + 3), c, -mn));
     s0 += col_in<TAIL>(e + 0, lim) ? t0 : 0.f;
     s1 += col_in<TAIL>(e + 1, lim) ? t1 : 0.f;
     s2 += col_in<TAIL>(e + 2, lim) ? t2 : 0.f;
@@ -196,14 +198,14 @@ __device__ __forceinline__ float col_sum_exp2(const float (&z)[64], float c, flo
 }
 
 // sums of 2^y and 2^y y, y = z c - mn, over the column
-template <bool TAIL>
-__device__ __forceinline__ void col_ent(const float (&z)[64], float c, float mn, int vw0, int half,
-                                        int V, float& st, float& ut) {
+template <bool TAIL, class Z>
+__device__ __forceinline__ void col_ent(const Z& z, float c, float mn, int vw0, int half, int V,
+                                        float& st, float& ut) {
   const int lim = col_lim<TAIL>(vw0, half, V);
   float st0 = 0.f, st1 = 0.f, ut0 = 0.f, ut1 = 0.f;
 #pragma unroll
   for (int e = 0; e < 64; e += 2) {
-    const float y0 = fmaf(z[e], c, -mn), y1 = fmaf(z[e + 1], c, -mn);
+    const float y0 = fmaf(z(e), c, -mn), y1 = fmaf(z(e + 1), c, -mn);
     float e0 = fast_exp2(y0), e1 = fast_exp2(y1);
     if (!col_in<TAIL>(e, lim)) e0 = 0.f;
     if (!col_in<TAIL>(e + 1, lim)) e1 = 0.f;
@@ -216,11 +218,12 @@ __device__ __forceinline__ void col_ent(const float (&z)[64], float c, float mn,
   ut = ut0 + ut1;
 }
 
-// z[tgt] (tgt in [0, 64)); 0 for tgt < 0.
-__device__ __forceinline__ float pick64(const float (&z)[64], int tgt) {
+// z(tgt) (tgt in [0, 64)); 0 for tgt < 0.
+template <class Z>
+__device__ __forceinline__ float pick64(const Z& z, int tgt) {
   float v = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 64; ++e) v = (e == tgt) ? z[e] : v;
+  for (int e = 0; e < 64; ++e) v = (e == tgt) ? z(e) : v;
   return v;
 }
 
@@ -449,18 +452,27 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
     const int Vp = (int)round_up(a.V, 8);
     const int tpad = (int)round_up(rows, 8);
 
-    // the next teacher ids of every token column, for the walks below
+    // the next teacher ids of every token column, for the walks below. The
+    // row offsets pass through an opaque copy each tile, so that the
+    // addresses derived from them are formed here rather than hoisted out of
+    // the tile loop (eight live 64-bit pointers, spilled and reloaded with a
+    // wait for memory on every tile).
     int win[4][kWin];
+    int64_t cb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cb[j] = opaque(cbase[j]);
     if constexpr (KIND == kSweepFwd) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) window_load(cbase[j], ccur[j], a.ids_s, a.K, win[j]);
+      for (int j = 0; j < 4; ++j) window_load(cb[j], ccur[j], a.ids_s, a.K, win[j]);
     }
 
-    // One token column at a time: its 64 accumulators are copied to registers
-    // (z), processed, and the next column starts only after this one is done
-    // (sched_barrier), which bounds the live registers of the epilogue.
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    // One token column at a time; the next column starts only after this one
+    // is done (sched_barrier), which bounds the live registers of the
+    // epilogue. The body is instantiated per column, so that every
+    // accumulator index is a constant: the forward and entropy reductions read
+    // the accumulators directly, the other kinds through a copy (z).
+    auto column = [&](auto jc) {
+      constexpr int j = decltype(jc)::value;
       __builtin_amdgcn_sched_barrier(0);
       // Entries past V hold 0 (zero W rows). The forward and entropy
       // reductions exclude them on the last tile; the gradient tile writes
@@ -528,31 +540,33 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
       }
 
       if constexpr (KIND == kSweepFwd) {
-        const float mx = tail ? col_max<true>(z, vw0, half, a.V) : col_max<false>(z, vw0, half, a.V);
+        const auto za = [&](int e) { return acc[e >> 4][j][e & 15]; };
+        const float mx = tail ? col_max<true>(za, vw0, half, a.V) : col_max<false>(za, vw0, half, a.V);
         const float mn = fmaxf(m[j], mx * c);
         if (mn != -INFINITY) {
           const float sc = fast_exp2(m[j] - mn);
-          const float st = tail ? col_sum_exp2<true>(z, c, mn, vw0, half, a.V)
-                                : col_sum_exp2<false>(z, c, mn, vw0, half, a.V);
+          const float st = tail ? col_sum_exp2<true>(za, c, mn, vw0, half, a.V)
+                                : col_sum_exp2<false>(za, c, mn, vw0, half, a.V);
           s[j] = s[j] * sc + st;
           m[j] = mn;
         }
         // z at the teacher ids, stored at their sorted positions; the
         // combine forms sum_k p_k z_k from them
-        walk_window(cbase[j], ccur[j], win[j], a.ids_s, a.K, vw0, half,
+        walk_window(cb[j], ccur[j], win[j], a.ids_s, a.K, vw0, half,
                     [&](int tgt, int64_t e) {
-                      const float val = pick64(z, tgt);
+                      const float val = pick64(za, tgt);
                       if (tgt >= 0) a.zs[e] = val;
                     });
       }
 
       if constexpr (KIND == kSweepEnt) {
-        const float mx = tail ? col_max<true>(z, vw0, half, a.V) : col_max<false>(z, vw0, half, a.V);
+        const auto za = [&](int e) { return acc[e >> 4][j][e & 15]; };
+        const float mx = tail ? col_max<true>(za, vw0, half, a.V) : col_max<false>(za, vw0, half, a.V);
         const float mn = fmaxf(m[j], mx * c);
         if (mn != -INFINITY) {
           float st, ut;
-          if (tail) col_ent<true>(z, c, mn, vw0, half, a.V, st, ut);
-          else col_ent<false>(z, c, mn, vw0, half, a.V, st, ut);
+          if (tail) col_ent<true>(za, c, mn, vw0, half, a.V, st, ut);
+          else col_ent<false>(za, c, mn, vw0, half, a.V, st, ut);
           if (m[j] == -INFINITY) {
             S64[j] = st;
             U64[j] = ut;
@@ -610,7 +624,11 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    column(std::integral_constant<int, 0>());
+    column(std::integral_constant<int, 1>());
+    column(std::integral_constant<int, 2>());
+    column(std::integral_constant<int, 3>());
   }
 
   if constexpr (KIND == kSweepBwdG || KIND == kSweepPilot || KIND == kSweepEmit) return;
