@@ -22,4 +22,5 @@ from .kd_oracle import (  # noqa: F401
     oracle_select_by_signal,
     oracle_select_above,
     oracle_validate_topk_order,
+    oracle_teacher_sample,
 )

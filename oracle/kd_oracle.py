@@ -63,6 +63,12 @@ Readings where the pages are silent (each is repeated in the design doc):
     definition): one threshold for all positions, keep signal >= tau; tau
     may be the smallest value kept by a top-k% selection over a pooled set of
     signals (the per-segment thresholds returned below);
+  * sampled sparse targets ([SKD] SE-KD3X class axis, RS-KD: the teacher's
+    logits randomly sampled into sparse targets; no procedure is given): N
+    token ids drawn per position from the teacher's full softmax p_t =
+    softmax(z_t / T) by inverse transform of given uniforms, the cumulative
+    mass taken in ascending vocabulary order; the target gives each draw
+    probability 1/N (draws of one id add);
   * the teacher cache holds, per position, the K entries of largest teacher
     logit z = h . w_v (before any temperature), ordered by z descending with the
     lower id first among equal logits; the stored logit is z rounded to fp32,
@@ -92,6 +98,7 @@ __all__ = [
     "oracle_select_by_signal",
     "oracle_select_above",
     "oracle_validate_topk_order",
+    "oracle_teacher_sample",
 ]
 
 
@@ -566,3 +573,27 @@ def oracle_select_above(signal, tau):
         mask = (x >= float(tau)).astype(np.uint8)
     idx = np.flatnonzero(mask).astype(np.int32)
     return mask, idx, int(idx.shape[0])
+
+
+def oracle_teacher_sample(hidden, W, T, uniforms, chunk=None):
+    """Sampled sparse teacher targets ([SKD] SE-KD3X class axis, RS-KD): for
+    each position t and uniform u in [0, 1), the smallest vocabulary id v with
+    F_t(v) > u, where F_t(v) is the cumulative teacher probability
+    softmax(z_t / T) over ids 0..v (z_t = hidden_t W^T, fp64). A u at or above
+    the last cumulative value (rounding) gives the largest id of positive
+    probability. Returns ids int32 [S, N]; a target is (ids, 1/N each)."""
+    Hd, Wd = _f64(hidden), _f64(W)
+    U = _f64(uniforms)
+    S, N = U.shape
+    C = S if chunk is None else int(chunk)
+    ids = np.zeros((S, N), dtype=np.int32)
+    for c0 in range(0, S, max(C, 1)):
+        c1 = min(S, c0 + C)
+        Z = (Hd[c0:c1] @ Wd.T) / float(T)
+        P = np.exp(Z - _logsumexp_rows(Z)[:, None])
+        F = np.cumsum(P, axis=1)
+        for r in range(c1 - c0):
+            last = int(np.flatnonzero(P[r] > 0.0)[-1])
+            v = np.searchsorted(F[r], U[c0 + r], side="right")     # first F > u
+            ids[c0 + r] = np.minimum(v, last)
+    return ids
