@@ -219,7 +219,9 @@ def selection_leg(kd, torch, wl, t, steps=3, warmup=1, n_seq=32, seed=77):
     kd_position_signals (one entropy sweep at T = 1, counted as 2*S*H*V FLOP,
     plus the label dot products and teacher rows), per-sequence SE-KD
     selection (20%), per-sequence top 20% by cross-entropy, sample selection
-    by mean entropy (20%) and a global threshold."""
+    by mean entropy (20%), a global threshold, and sampled teacher targets
+    (K ids per position drawn from softmax(z/T) of the same projection: three
+    vocabulary sweeps, counted as 3*2*S*H*V FLOP)."""
     S, H, V = wl["S"], wl["H"], wl["V"]
     hidden, W, ids, tl = t
     rng = np.random.default_rng(seed)
@@ -250,6 +252,14 @@ def selection_leg(kd, torch, wl, t, steps=3, warmup=1, n_seq=32, seed=77):
                                                               workspace=ws))
     tau = float(torch.quantile(ce[: min(S, 1 << 20)].float(), 0.8))
     (_, _, k_thr), t_thr = timed(lambda: kd.kd_select_above(ce, tau, workspace=ws))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    u = torch.sort(torch.rand(S, wl["K"], dtype=torch.float64, device="cuda", generator=gen),
+                   dim=1).values.contiguous()
+    sprob = kd.make_problem(S, H, V, wl["K"], wl["chunk"], wl["T"], kd.KD_BF16, kd.KD_F32)
+    sws = torch.empty(kd.kd_teacher_sample_workspace_bytes(sprob), dtype=torch.uint8, device="cuda")
+    sids, t_tsm = timed(lambda: kd.kd_teacher_sample(hidden, W, u, T=wl["T"], chunk=wl["chunk"],
+                                                     workspace=sws))
     kd.kd_profile_enable(False)
     prof = kd.kd_profile_read()
     kd.kd_profile_reset()
@@ -266,9 +276,14 @@ def selection_leg(kd, torch, wl, t, steps=3, warmup=1, n_seq=32, seed=77):
                per_sequence_sekd_ms=round(t_seq, 3), per_sequence_sekd_kept=int(k_seq),
                per_sequence_ce_ms=round(t_ce, 3), per_sequence_ce_kept=int(k_ce),
                sample_select_ms=round(t_smp, 3), samples_kept=int(k_smp),
-               threshold_ms=round(t_thr, 3), threshold_kept=int(k_thr), kernels=kernels)
-    log(f"[bench] selection leg: signals {t_sig:.2f} ms, per-sequence SE-KD {t_seq:.2f} ms")
-    del ws
+               threshold_ms=round(t_thr, 3), threshold_kept=int(k_thr),
+               teacher_sample_ms=round(t_tsm, 3),
+               teacher_sample_tflops=round(3 * 2.0 * S * H * V / (t_tsm / 1000.0) / 1e12, 1),
+               teacher_sample_ids_in_range=bool(int(sids.min()) >= 0 and int(sids.max()) < V),
+               kernels=kernels)
+    log(f"[bench] selection leg: signals {t_sig:.2f} ms, per-sequence SE-KD {t_seq:.2f} ms, "
+        f"sampled targets {t_tsm:.2f} ms")
+    del ws, sws, u, sids
     torch.cuda.empty_cache()
     return out
 

@@ -21,6 +21,7 @@ __all__ = [
     "kd_position_signals", "kd_select_by_signal", "kd_select_above",
     "kd_select_top_fraction_segments", "kd_validate_topk_order",
     "kd_teacher_topk_workspace_bytes", "kd_teacher_topk",
+    "kd_teacher_sample_workspace_bytes", "kd_teacher_sample",
     "kd_profile_enable", "kd_profile_read", "kd_profile_reset",
     "KDTopKKL", "kd_topk_kl", "LIB_PATH",
 ]
@@ -89,6 +90,10 @@ lib.kd_teacher_topk_workspace_bytes.restype = ctypes.c_size_t
 lib.kd_teacher_topk_workspace_bytes.argtypes = [_PP]
 lib.kd_teacher_topk.restype = ctypes.c_int
 lib.kd_teacher_topk.argtypes = [_PP, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+lib.kd_teacher_sample_workspace_bytes.restype = ctypes.c_size_t
+lib.kd_teacher_sample_workspace_bytes.argtypes = [_PP]
+lib.kd_teacher_sample.restype = ctypes.c_int
+lib.kd_teacher_sample.argtypes = [_PP, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.kd_profile_enable.restype = ctypes.c_int
 lib.kd_profile_enable.argtypes = [ctypes.c_int]
 lib.kd_profile_read.restype = ctypes.c_int
@@ -392,6 +397,37 @@ def kd_teacher_topk(hidden, W, K, chunk=2048, out_dtype=torch.bfloat16, workspac
                                _ptr(workspace), workspace.numel(), _stream(dev)),
            "kd_teacher_topk")
     return ids, logits
+
+
+def kd_teacher_sample_workspace_bytes(problem: kd_problem) -> int:
+    return int(lib.kd_teacher_sample_workspace_bytes(ctypes.byref(problem)))
+
+
+def kd_teacher_sample(hidden, W, uniforms, T=1.0, chunk=1024, workspace=None):
+    """Sampled teacher targets: ids int32 [S,N], entry (t, n) the smallest id v whose
+    cumulative probability under softmax(hidden_t W^T / T) exceeds uniforms[t, n]
+    (uniforms: float64 [S,N] in [0, 1), each row non-decreasing)."""
+    if hidden.dim() != 2 or W.dim() != 2 or hidden.shape[1] != W.shape[1]:
+        raise ValueError("hidden [S,H] and W [V,H] expected")
+    if hidden.dtype != W.dtype or not hidden.is_contiguous() or not W.is_contiguous():
+        raise ValueError("hidden and W must be contiguous and of one dtype")
+    if (uniforms.dtype != torch.float64 or uniforms.dim() != 2 or not uniforms.is_contiguous()
+            or uniforms.shape[0] != hidden.shape[0]):
+        raise ValueError("uniforms: contiguous float64 [S,N] expected")
+    S, H = hidden.shape
+    N = uniforms.shape[1]
+    p = make_problem(S, H, W.shape[0], N, chunk, T, _dtype_code(hidden.dtype), KD_F32)
+    dev = hidden.device
+    need = kd_teacher_sample_workspace_bytes(p)
+    if need == 0:
+        raise KdError(2, "kd_teacher_sample")
+    if workspace is None or workspace.numel() < need or workspace.data_ptr() % 256 != 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ids = torch.empty(S, N, dtype=torch.int32, device=dev)
+    _check(lib.kd_teacher_sample(ctypes.byref(p), _ptr(hidden), _ptr(W), _ptr(uniforms),
+                                 _ptr(ids), _ptr(workspace), workspace.numel(), _stream(dev)),
+           "kd_teacher_sample")
+    return ids
 
 
 def kd_validate_topk_order(topk_ids, topk_logits, V, workspace=None):

@@ -1054,6 +1054,128 @@ int kd_teacher_topk(const kd_problem* p, const void* hidden, const void* W, int3
   return KD_OK;
 }
 
+// ------------------------------------------------------------------ sampled teacher targets
+struct SampleLayout {
+  int64_t C, ldm, nu, pe;   // rows per chunk, unit-mass pitch, 128-entry units, partial slots
+  size_t flag, em, es, eu, lse, mass, dunit, dres, total;
+};
+
+SampleLayout plan_sample(const kd_problem* p) {
+  SampleLayout L{};
+  const int64_t S = std::max<int64_t>(p->S, 1), N = p->K;
+  L.C = std::min<int64_t>(p->chunk, S);
+  L.ldm = kd::round_up(L.C, 64);
+  L.nu = kd::ceil_div(p->V, 128);
+  L.pe = (int64_t)kd::sweep_grid(S, (int)p->V, kCostCUs) * kd::kTile;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (size_t)kd::round_up((int64_t)bytes, 256);
+    return o;
+  };
+  L.flag = take(8);
+  L.em = take((size_t)L.pe * 4);
+  L.es = take((size_t)L.pe * 8);
+  L.eu = take((size_t)L.pe * 8);
+  L.lse = take((size_t)S * 8);
+  L.mass = take((size_t)L.nu * L.ldm * 8);
+  L.dunit = take((size_t)L.C * N * 4);
+  L.dres = take((size_t)L.C * N * 8);
+  L.total = off;
+  return L;
+}
+
+size_t kd_teacher_sample_workspace_bytes(const kd_problem* p) {
+  if (check_problem(p)) return 0;
+  return plan_sample(p).total;
+}
+
+int kd_teacher_sample(const kd_problem* p, const void* hidden, const void* W,
+                      const double* uniforms, int32_t* ids_out, void* ws, size_t ws_bytes,
+                      void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!W || (p->S > 0 && (!hidden || !uniforms || !ids_out))) return KD_ERR_NULL;
+  const SampleLayout L = plan_sample(p);
+  if (!ws || ((uintptr_t)ws & 255u) != 0 || ws_bytes < L.total) return KD_ERR_WORKSPACE;
+  if ((rc = check_device())) return rc;
+  if (p->S == 0) return KD_OK;
+  hipStream_t st = (hipStream_t)stream;
+  const int f32 = p->hw_dtype == KD_F32;
+  const int64_t esz = f32 ? 4 : 2;
+  const int S = (int)p->S, H = (int)p->H, V = (int)p->V, N = (int)p->K;
+  const int64_t ld = (int64_t)H * esz;
+  int32_t* flag = at<int32_t>(ws, L.flag);
+  KD_HIP(kd::launch_draw_check(uniforms, S, N, flag, st));
+  int32_t h_flag = 0;
+  KD_HIP(hipMemcpyAsync(&h_flag, flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  KD_HIP(hipStreamSynchronize(st));
+  if (h_flag) return KD_ERR_ARG;
+  kd::SweepArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.W = (const char*)W;
+  a.ldw = ld;
+  a.X = (const char*)hidden;
+  a.ldx = ld;
+  a.row_cap = S;
+  a.V = V;
+  a.H = H;
+  a.K = N;
+  a.ncu = kCostCUs;
+  a.T = p->temperature;
+  a.em = at<float>(ws, L.em);
+  a.es = at<double>(ws, L.es);
+  a.eu = at<double>(ws, L.eu);
+  double* lse = at<double>(ws, L.lse);
+  {
+    // log-normaliser of z/T over the full vocabulary
+    Prof pr("sample_lse", st);
+    KD_HIP(kd::launch_sweep(kd::kSweepEnt, f32, 0, a, kd::sweep_grid(S, V, kCostCUs), st));
+    kd::EntCombineArgs c;
+    c.S = S;
+    c.V = V;
+    c.ncu = kCostCUs;
+    c.em = a.em;
+    c.es = a.es;
+    c.eu = a.eu;
+    c.entropy = nullptr;
+    c.lse = lse;
+    KD_HIP(kd::launch_ent_combine(c, st));
+  }
+  double* mass = at<double>(ws, L.mass);
+  int32_t* dunit = at<int32_t>(ws, L.dunit);
+  double* dres = at<double>(ws, L.dres);
+  for (int64_t c0 = 0; c0 < S; c0 += L.C) {
+    const int rows = (int)std::min<int64_t>(L.C, S - c0);
+    kd::SweepArgs b = a;
+    b.X = (const char*)hidden + c0 * ld;
+    b.row_cap = rows;
+    b.slse = lse + c0;
+    b.tmass = mass;
+    b.ldm = L.ldm;
+    b.N = N;
+    const int grid = kd::sweep_grid(rows, V, kCostCUs);
+    {
+      Prof pr("sample_mass", st);
+      KD_HIP(kd::launch_sweep(kd::kSweepSMass, f32, 0, b, grid, st));
+    }
+    {
+      Prof pr("sample_assign", st);
+      KD_HIP(kd::launch_draw_cumsum(mass, L.ldm, (int)L.nu, rows, st));
+      KD_HIP(kd::launch_draw_assign(mass, L.ldm, (int)L.nu, rows, uniforms + c0 * N, N, dunit,
+                                    dres, ids_out + c0 * N, st));
+    }
+    b.dunit = dunit;
+    b.dres = dres;
+    b.sids = ids_out + c0 * N;
+    {
+      Prof pr("sample_draw", st);
+      KD_HIP(kd::launch_sweep(kd::kSweepSDraw, f32, 0, b, grid, st));
+    }
+  }
+  return KD_OK;
+}
+
 int kd_validate_topk(const kd_problem* p, const int32_t* ids, const void* tl, int64_t* n_bad_id,
                      int64_t* n_empty_row, int64_t* n_bad_logit, void* ws, size_t ws_bytes,
                      void* stream) {

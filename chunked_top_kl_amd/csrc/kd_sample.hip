@@ -1,0 +1,125 @@
+// Sampled sparse teacher targets ("Rethinking Selective Knowledge
+// Distillation", Method section 2: RS-KD, the class axis of SE-KD3X): N ids
+// per position drawn from the teacher's softmax at temperature T by inverse
+// transform in vocabulary order, each draw given by a caller's uniform u: the
+// smallest id v with F(v) > u, F the cumulative probability over ids 0..v.
+//
+// The vocabulary sweeps (kd_sweep.hip) store the mass of every 128-entry
+// unit of each row and later resolve a draw inside its unit. Between them,
+// these kernels turn the unit masses into a cumulative sum and give every
+// draw its unit and the residual mass inside it.
+#include "kd_common.hpp"
+#include "kd_kernels.hpp"
+
+#include <algorithm>
+
+namespace kd {
+
+__global__ void draw_zero_flag_kernel(int32_t* flag) {
+  if (threadIdx.x == 0) flag[0] = 0;
+}
+
+// flag <- 1 when a uniform is outside [0, 1) (NaN included) or a row of them
+// decreases
+__global__ __launch_bounds__(256) void draw_check_kernel(const double* u, int64_t S, int N,
+                                                         int32_t* flag) {
+  const int64_t n_all = S * N;
+  bool bad = false;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_all;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const double x = u[i];
+    bad |= !(x >= 0.0 && x < 1.0);
+    if (i % N != 0) bad |= u[i - 1] > x;
+  }
+  if (bad) flag[0] = 1;
+}
+
+hipError_t launch_draw_check(const double* u, int64_t S, int N, int32_t* flag, hipStream_t st) {
+  hipLaunchKernelGGL(draw_zero_flag_kernel, dim3(1), dim3(64), 0, st, flag);
+  const int64_t n = S * N;
+  const int grid = (int)std::min<int64_t>(ceil_div(n, 256), 2048);
+  if (grid > 0) hipLaunchKernelGGL(draw_check_kernel, dim3(grid), dim3(256), 0, st, u, S, N, flag);
+  return hipGetLastError();
+}
+
+// One thread per row: the unit masses become their running sum in vocabulary
+// order, in fp64 and in place ([unit][row], pitch ldm), so that neighbouring
+// threads touch neighbouring addresses. Sequential addition of non-negative
+// terms keeps the sum non-decreasing, which the search below relies on.
+__global__ __launch_bounds__(256) void draw_cumsum_kernel(double* m, int64_t ldm, int nu, int rows) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows) return;
+  double run = 0.0;
+  double* p = m + t;
+  // 32 units at a time: their loads are issued together, then added in order
+  constexpr int kB = 32;
+  for (int k0 = 0; k0 < nu; k0 += kB) {
+    double v[kB];
+#pragma unroll
+    for (int i = 0; i < kB; ++i) v[i] = (k0 + i < nu) ? p[(int64_t)(k0 + i) * ldm] : 0.0;
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      run += v[i];
+      v[i] = run;
+    }
+#pragma unroll
+    for (int i = 0; i < kB; ++i)
+      if (k0 + i < nu) p[(int64_t)(k0 + i) * ldm] = v[i];
+  }
+}
+
+hipError_t launch_draw_cumsum(double* tmass, int64_t ldm, int nu, int rows, hipStream_t st) {
+  if (rows > 0)
+    hipLaunchKernelGGL(draw_cumsum_kernel, dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, st,
+                       tmass, ldm, nu, rows);
+  return hipGetLastError();
+}
+
+// One thread per draw (row t, draw n). With Z the row's total mass, the draw
+// aims at mass u Z: its unit is the first whose cumulative mass exceeds that,
+// and its residual the aim less the mass of the units before. An aim at or
+// above Z (u within rounding of 1) takes the unit where the cumulative mass
+// first reaches Z (the last unit of positive mass) with an unbounded residual:
+// the draw pass then takes that unit's last entry of positive weight. A row
+// whose total is not a positive finite number (non-finite logits) gets unit
+// -1, which no unit matches, and keeps the id -1 written here.
+__global__ __launch_bounds__(256) void draw_assign_kernel(const double* cum, int64_t ldm, int nu,
+                                                          int rows, const double* u, int N,
+                                                          int32_t* dunit, double* dres,
+                                                          int32_t* sids) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= (int64_t)rows * N) return;
+  const int t = (int)(i / N);
+  const double* c = cum + t;
+  const double Z = c[(int64_t)(nu - 1) * ldm];
+  sids[i] = -1;
+  if (!(Z > 0.0) || !(Z < INFINITY)) {
+    dunit[i] = -1;
+    dres[i] = 0.0;
+    return;
+  }
+  const double aim = u[i] * Z;
+  const bool top = aim >= Z;
+  // first unit k with cum[k] > aim (or, at the top, cum[k] >= Z)
+  int lo = 0, hi = nu - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const double v = c[(int64_t)mid * ldm];
+    const bool past = top ? v >= Z : v > aim;
+    if (past) hi = mid;
+    else lo = mid + 1;
+  }
+  dunit[i] = lo;
+  dres[i] = top ? INFINITY : aim - (lo > 0 ? c[(int64_t)(lo - 1) * ldm] : 0.0);
+}
+
+hipError_t launch_draw_assign(const double* cum, int64_t ldm, int nu, int rows, const double* u,
+                              int N, int32_t* dunit, double* dres, int32_t* sids, hipStream_t st) {
+  const int64_t n = (int64_t)rows * N;
+  if (n > 0)
+    hipLaunchKernelGGL(draw_assign_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, cum,
+                       ldm, nu, rows, u, N, dunit, dres, sids);
+  return hipGetLastError();
+}
+
+}  // namespace kd

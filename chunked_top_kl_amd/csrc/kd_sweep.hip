@@ -10,7 +10,12 @@
 //    computed once and only each position's K largest kept): a pilot pass
 //    that stores the maxima of groups of 16 logits of the first vocabulary
 //    rows, and an emit pass that appends every logit at or above a per-row
-//    threshold to the row's candidate list (kd_teacher.hip picks the K).
+//    threshold to the row's candidate list (kd_teacher.hip picks the K);
+//  - sampled targets (RS-KD: ids drawn from the teacher's softmax at T by
+//    inverse transform in vocabulary order): a mass pass that stores the
+//    probability mass of every 128-entry vocabulary unit of each row, and a
+//    draw pass that, for the draws assigned to a unit (kd_sample.hip),
+//    finds the entry where the running mass passes the draw's residual.
 //
 // Orientation: MFMA rows (M) are vocabulary entries (A = W tile), MFMA columns
 // (N) are tokens (B = hidden rows). Each lane therefore owns whole token
@@ -400,6 +405,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
   int ccur[4];
   float lse2[4];
   float tej[4];   // emission threshold of each token column (teacher cache writer)
+  int dcur[4], dnext[4];   // sampled targets: next draw of the column and its unit
   float coef = 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -420,6 +426,19 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
     tej[j] = INFINITY;
     if constexpr (KIND == kSweepEmit)
       if (tl0 + 32 * j < rows) tej[j] = a.te[tl0 + 32 * j];
+    if constexpr (KIND == kSweepSMass || KIND == kSweepSDraw)
+      lse2[j] = (tl0 + 32 * j < rows) ? (float)(a.slse[orow[j]] * 1.4426950408889634) : 0.0f;
+    dcur[j] = a.N;
+    dnext[j] = 0x7FFFFFFF;
+    if constexpr (KIND == kSweepSDraw) {
+      // a row's draws are ordered by unit; start at the first one in this
+      // work-group's vocabulary range
+      if (tl0 + 32 * j < rows) {
+        const int32_t* du = a.dunit + (int64_t)(tl0 + 32 * j) * a.N;
+        dcur[j] = lower_bound_ids(du, a.N, 2 * vt_begin);
+        dnext[j] = dcur[j] < a.N ? du[dcur[j]] : 0x7FFFFFFF;
+      }
+    }
   }
   if constexpr (KIND == kSweepBwdG) {
     const int n = *a.nrows_dev;
@@ -580,6 +599,99 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
         }
       }
 
+      if constexpr (KIND == kSweepSMass || KIND == kSweepSDraw) {
+        // weights 2^(z c - lse2) (the teacher softmax at T; entries past V
+        // weigh 0), summed per quad: four consecutive vocabulary entries. The
+        // lane's quad k = 4i + q sits at position 2k + half of the wave's
+        // 128-entry unit; the partner lane (other half) holds the others.
+        // Both passes compute the same values in the same order, so the draw
+        // pass sees the masses the mass pass stored.
+#pragma unroll
+        for (int e = 0; e < 64; ++e) {
+          const bool in = !tail || vw0 + acc_row(e >> 4, e & 15, half) < a.V;
+          z[e] = in ? fast_exp2(fmaf(z[e], c, -lse2[j])) : 0.0f;
+        }
+        float g[16], gp[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) g[k] = (z[4 * k] + z[4 * k + 1]) + (z[4 * k + 2] + z[4 * k + 3]);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) gp[k] = __shfl_xor(g[k], 32, 64);
+        // quad at position 2k is half 0's, at 2k + 1 half 1's
+        const auto quad = [&](int k, int s) { return (s == half) ? g[k] : gp[k]; };
+        const int t = tl0 + 32 * j;
+        const int unit = vw0 >> 7;
+        if constexpr (KIND == kSweepSMass) {
+          float run = 0.0f;
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            run += quad(k, 0);
+            run += quad(k, 1);
+          }
+          if (t < rows && half == 0) a.tmass[(int64_t)unit * a.ldm + t] = (double)run;
+        } else {
+          // the column's draws up to this unit: those of lower units belong
+          // to the other wave and are passed over
+          const int64_t rb = (int64_t)t * a.N;
+          while (true) {
+            const bool act = dnext[j] <= unit;
+            if (ballot(act) == 0) break;
+            if (act && dnext[j] == unit) {
+              double r = a.dres[rb + dcur[j]];
+              // the first quad whose running mass passes r; past the unit's
+              // mass (rounding, or a draw at the top of the distribution),
+              // the last quad of positive mass with r unbounded
+              float run = 0.0f, pb = 0.0f, pbl = 0.0f;
+              int qs = -1, ql = -1;
+#pragma unroll
+              for (int k = 0; k < 16; ++k)
+#pragma unroll
+                for (int sh = 0; sh < 2; ++sh) {
+                  const float gq = quad(k, sh);
+                  const float pa = run + gq;
+                  if (qs < 0 && (double)pa > r) {
+                    qs = 2 * k + sh;
+                    pb = run;
+                  }
+                  if (gq > 0.0f) {
+                    ql = 2 * k + sh;
+                    pbl = run;
+                  }
+                  run = pa;
+                }
+              if (qs < 0) {
+                qs = ql;
+                pb = pbl;
+                r = INFINITY;
+              }
+              if (qs >= 0 && (qs & 1) == half) {
+                // inside the quad: the first entry whose running mass passes
+                // the rest of r, else its last entry of positive weight
+                const int kq = qs >> 1;
+                float e0 = 0.0f, e1 = 0.0f, e2 = 0.0f, e3 = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 16; ++k)
+                  if (k == kq) {
+                    e0 = z[4 * k];
+                    e1 = z[4 * k + 1];
+                    e2 = z[4 * k + 2];
+                    e3 = z[4 * k + 3];
+                  }
+                const double rq = r - (double)pb;
+                const float c0 = e0, c1 = c0 + e1, c2 = c1 + e2, c3 = c2 + e3;
+                int pick = (double)c0 > rq ? 0 : (double)c1 > rq ? 1 : (double)c2 > rq ? 2
+                         : (double)c3 > rq ? 3 : -1;
+                if (pick < 0) pick = e3 > 0.0f ? 3 : e2 > 0.0f ? 2 : e1 > 0.0f ? 1 : 0;
+                a.sids[rb + dcur[j]] = vw0 + 4 * qs + pick;
+              }
+            }
+            if (act) {
+              ++dcur[j];
+              dnext[j] = dcur[j] < a.N ? a.dunit[rb + dcur[j]] : 0x7FFFFFFF;
+            }
+          }
+        }
+      }
+
       if constexpr (KIND == kSweepBwdG) {
         // coef * q; the teacher term is applied by grad_teacher_kernel
 #pragma unroll
@@ -631,7 +743,9 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
     column(std::integral_constant<int, 3>());
   }
 
-  if constexpr (KIND == kSweepBwdG || KIND == kSweepPilot || KIND == kSweepEmit) return;
+  if constexpr (KIND == kSweepBwdG || KIND == kSweepPilot || KIND == kSweepEmit ||
+                KIND == kSweepSMass || KIND == kSweepSDraw)
+    return;
 
   // ---- end of sweep: merge lane halves, then the two waves sharing tokens
 #pragma unroll
@@ -721,6 +835,10 @@ KD_SWEEP_KERNEL(kd_teacher_pilot_bf16, __bf16, kSweepPilot, false)
 KD_SWEEP_KERNEL(kd_teacher_emit_bf16, __bf16, kSweepEmit, false)
 KD_SWEEP_KERNEL(kd_teacher_pilot_f32, float, kSweepPilot, false)
 KD_SWEEP_KERNEL(kd_teacher_emit_f32, float, kSweepEmit, false)
+KD_SWEEP_KERNEL(kd_sample_mass_bf16, __bf16, kSweepSMass, false)
+KD_SWEEP_KERNEL(kd_sample_draw_bf16, __bf16, kSweepSDraw, false)
+KD_SWEEP_KERNEL(kd_sample_mass_f32, float, kSweepSMass, false)
+KD_SWEEP_KERNEL(kd_sample_draw_f32, float, kSweepSDraw, false)
 #undef KD_SWEEP_KERNEL
 
 hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid, hipStream_t st) {
@@ -733,6 +851,8 @@ hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid
     else if (kind == kSweepBwdG) KD_SWEEP(kd_bwd_grad_tile_bf16);
     else if (kind == kSweepPilot) KD_SWEEP(kd_teacher_pilot_bf16);
     else if (kind == kSweepEmit) KD_SWEEP(kd_teacher_emit_bf16);
+    else if (kind == kSweepSMass) KD_SWEEP(kd_sample_mass_bf16);
+    else if (kind == kSweepSDraw) KD_SWEEP(kd_sample_draw_bf16);
     else KD_SWEEP(kd_entropy_sweep_bf16);
   } else {
     if (kind == kSweepFwd && map) KD_SWEEP(kd_fwd_lse_gather_rows_f32);
@@ -740,6 +860,8 @@ hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid
     else if (kind == kSweepBwdG) KD_SWEEP(kd_bwd_grad_tile_f32);
     else if (kind == kSweepPilot) KD_SWEEP(kd_teacher_pilot_f32);
     else if (kind == kSweepEmit) KD_SWEEP(kd_teacher_emit_f32);
+    else if (kind == kSweepSMass) KD_SWEEP(kd_sample_mass_f32);
+    else if (kind == kSweepSDraw) KD_SWEEP(kd_sample_draw_f32);
     else KD_SWEEP(kd_entropy_sweep_f32);
   }
 #undef KD_SWEEP

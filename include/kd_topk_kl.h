@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define KD_ABI_VERSION 3
+#define KD_ABI_VERSION 4
 
 typedef enum kd_status {
   KD_OK = 0,
@@ -323,6 +323,40 @@ size_t kd_teacher_topk_workspace_bytes(const kd_problem* problem);
 int kd_teacher_topk(const kd_problem* problem, const void* hidden, const void* W,
                     int32_t* topk_ids, void* topk_logits, void* ws, size_t ws_bytes,
                     void* stream);
+
+/* Sampled sparse teacher targets ("Rethinking Selective Knowledge
+ * Distillation", Method section 2: RS-KD, the class axis of SE-KD3X, where a
+ * position's target is a few ids sampled from the teacher's distribution).
+ * For every position t and draw n (N = problem->K draws, 1 <= N <= min(V,
+ * 4096)), with u = uniforms[t,n]: the smallest vocabulary id v such that the
+ * cumulative teacher probability F_t(v) = sum over ids w <= v of
+ * softmax(z_t / T)_w exceeds u (inverse transform in vocabulary order),
+ * z_tv = h_t . w_v and T = problem->temperature. The target of position t is
+ * then the N ids with weight 1/N each (give it to kd_topk_kl_* as a
+ * probability cache: tl_kind KD_TEACHER_PROBS, equal values; repeated ids
+ * add up). The [S,V] grid is never stored: a full-vocabulary sweep gives each
+ * row's log-normaliser, then per chunk of problem->chunk positions one sweep
+ * stores the mass of every 128 consecutive ids and another resolves each
+ * draw inside its 128 ids.
+ *   hidden    [device] [S,H] hw_dtype: the teacher's final hidden states
+ *   W         [device] [V,H] hw_dtype: the teacher's output projection
+ *   uniforms  [device] [S,N] double in [0, 1), each row non-decreasing (sort
+ *             the caller's draws per row; the ids come out in that order).
+ *             Checked first: KD_ERR_ARG, with nothing written, otherwise
+ *             (this check synchronises the host).
+ *   ids_out   [device] [S,N] int32 output
+ *   ws        at least kd_teacher_sample_workspace_bytes(problem) bytes (this
+ *             entry point does not use kd_topk_kl_workspace_bytes).
+ * Precision: the probabilities are formed in fp32 from the fp32-accumulated
+ * logits, their masses summed in fp32 per 4 and 128 ids and in fp64 above,
+ * so F_t is met to about 1e-5 absolute; a u that close to a step of F_t may
+ * get the neighbouring id. A u within rounding of 1 gives the largest id of
+ * positive computed probability. A position with non-finite logits gets -1
+ * for every draw. problem->K is N here; problem->tl_* are not used.          */
+size_t kd_teacher_sample_workspace_bytes(const kd_problem* problem);
+int kd_teacher_sample(const kd_problem* problem, const void* hidden, const void* W,
+                      const double* uniforms, int32_t* ids_out, void* ws, size_t ws_bytes,
+                      void* stream);
 
 /* Kernel timing (off by default). When on, every kernel the library enqueues
  * is bracketed by HIP events on the same stream. kd_profile_read synchronises

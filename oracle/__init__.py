@@ -22,5 +22,6 @@ from .kd_oracle import (  # noqa: F401
     oracle_select_by_signal,
     oracle_select_above,
     oracle_validate_topk_order,
+    oracle_teacher_cdf,
     oracle_teacher_sample,
 )

@@ -575,6 +575,15 @@ def oracle_select_above(signal, tau):
     return mask, idx, int(idx.shape[0])
 
 
+def oracle_teacher_cdf(hidden, W, T):
+    """Teacher distribution of the sampled targets: P = softmax(z / T) per row
+    (z = hidden W^T, fp64) and F, its cumulative sum over ids 0..v in
+    vocabulary order. Returns (P, F), each [S, V] fp64."""
+    Z = (_f64(hidden) @ _f64(W).T) / float(T)
+    P = np.exp(Z - _logsumexp_rows(Z)[:, None])
+    return P, np.cumsum(P, axis=1)
+
+
 def oracle_teacher_sample(hidden, W, T, uniforms, chunk=None):
     """Sampled sparse teacher targets ([SKD] SE-KD3X class axis, RS-KD): for
     each position t and uniform u in [0, 1), the smallest vocabulary id v with
@@ -589,9 +598,7 @@ def oracle_teacher_sample(hidden, W, T, uniforms, chunk=None):
     ids = np.zeros((S, N), dtype=np.int32)
     for c0 in range(0, S, max(C, 1)):
         c1 = min(S, c0 + C)
-        Z = (Hd[c0:c1] @ Wd.T) / float(T)
-        P = np.exp(Z - _logsumexp_rows(Z)[:, None])
-        F = np.cumsum(P, axis=1)
+        P, F = oracle_teacher_cdf(Hd[c0:c1], Wd, T)
         for r in range(c1 - c0):
             last = int(np.flatnonzero(P[r] > 0.0)[-1])
             v = np.searchsorted(F[r], U[c0 + r], side="right")     # first F > u

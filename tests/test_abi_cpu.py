@@ -31,7 +31,7 @@ def test_header_symbols_exported():
 
 
 def test_version_and_status_strings():
-    assert kd.kd_abi_version() == 3
+    assert kd.kd_abi_version() == 4
     for c in range(11):
         assert kd.kd_status_str(c).startswith("KD_")
     assert "unknown" in kd.kd_status_str(99)
@@ -154,3 +154,24 @@ def test_per_sequence_selection_argument_errors():
              need, None) == KD_ERR_NULL
     assert f(ctypes.byref(p), fake, fake, fake, fake, 4, 1, 2, fake, None, ctypes.byref(cnt), ws,
              need - 1, None) == KD_ERR_WORKSPACE
+
+
+def test_teacher_sample_argument_errors():
+    fake = ctypes.c_void_p(0x1000)
+    ws = ctypes.c_void_p(0x10000)
+    f = kd.lib.kd_teacher_sample
+    p = prob(K=100)
+    need = kd.kd_teacher_sample_workspace_bytes(p)
+    assert need > 0
+    assert kd.kd_teacher_sample_workspace_bytes(prob(K=1001)) == 0       # N > V
+    assert f(ctypes.byref(prob(K=1001)), fake, fake, fake, fake, ws, need, None) == KD_ERR_SHAPE
+    assert f(ctypes.byref(prob(T=0.0)), fake, fake, fake, fake, ws, need, None) == KD_ERR_TEMPERATURE
+    assert f(ctypes.byref(p), fake, fake, None, fake, ws, need, None) == KD_ERR_NULL
+    assert f(ctypes.byref(p), fake, fake, fake, None, ws, need, None) == KD_ERR_NULL
+    assert f(ctypes.byref(p), fake, None, fake, fake, ws, need, None) == KD_ERR_NULL
+    assert f(ctypes.byref(p), fake, fake, fake, fake, ws, need - 1, None) == KD_ERR_WORKSPACE
+    assert f(ctypes.byref(p), fake, fake, fake, fake, ctypes.c_void_p(0x10010), need,
+             None) == KD_ERR_WORKSPACE
+    # the workspace holds per-chunk unit masses and draws, not [S, V]
+    big = kd.kd_teacher_sample_workspace_bytes(prob(S=32768, H=2880, V=201088, K=100, chunk=1024))
+    assert big < 64 << 20

@@ -69,3 +69,21 @@ def test_frequencies_follow_probabilities():
     freq = np.bincount(ids[0], minlength=V) / N
     # binomial standard error; 5 sigma
     assert np.all(np.abs(freq - p) <= 5 * np.sqrt(p * (1 - p) / N) + 1e-12)
+
+
+def test_cdf_matches_scalar_softmax():
+    from oracle import oracle_teacher_cdf
+    rng = np.random.default_rng(12)
+    h = rng.standard_normal((3, 4))
+    W = rng.standard_normal((11, 4))
+    T = 0.6
+    P, F = oracle_teacher_cdf(h, W, T)
+    for t in range(3):
+        z = [sum(h[t, k] * W[v, k] for k in range(4)) / T for v in range(11)]
+        e = [math.exp(x - max(z)) for x in z]
+        tot = math.fsum(e)
+        run = 0.0
+        for v in range(11):
+            run += e[v] / tot
+            assert abs(P[t, v] - e[v] / tot) <= 1e-15
+            assert abs(F[t, v] - run) <= 1e-14
