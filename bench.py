@@ -428,8 +428,7 @@ def main():
     kernels = {}
     for name, (n, tot) in prof.items():
         per = tot / max(n, 1)
-        rows = N_rows if name in ("fwd_lse_gather",) else S
-        f = kernel_flops(name, wl, C, rows if name != "entropy_sweep" else S)
+        f = kernel_flops(name, wl, C, N_rows if name == "fwd_lse_gather" else S)
         if name in ("bwd_grad_tile", "bwd_dhidden", "bwd_dw"):
             f = 8.0 * N_rows * H * V / 4.0 / max(n / args.steps, 1)   # per launch, averaged over chunks
         kernels[name] = dict(launches_per_step=round(n / args.steps, 2), ms_per_step=round(tot / args.steps, 4),
@@ -437,7 +436,8 @@ def main():
                              tflops=(round(f / (per / 1000.0) / 1e12, 1) if f else None))
     dom = max(kernels.items(), key=lambda kv: kv[1]["ms_per_step"])
     dom_name, dom_v = dom
-    dom_flops = kernel_flops(dom_name, wl, C, N_rows)
+    # the forward runs over the rows in the loss, the entropy sweep over all S
+    dom_flops = kernel_flops(dom_name, wl, C, S if dom_name == "entropy_sweep" else N_rows)
     if dom_name in ("bwd_grad_tile", "bwd_dhidden", "bwd_dw"):
         dom_flops = 8.0 * N_rows * H * V / 4.0 / max(dom_v["launches_per_step"], 1)
     achieved = dom_flops / (dom_v["avg_ms"] / 1000.0) / 1e12 if dom_flops else None
