@@ -220,8 +220,8 @@ def selection_leg(kd, torch, wl, t, steps=3, warmup=1, n_seq=32, seed=77):
     plus the label dot products and teacher rows), per-sequence SE-KD
     selection (20%), per-sequence top 20% by cross-entropy, sample selection
     by mean entropy (20%), a global threshold, and sampled teacher targets
-    (K ids per position drawn from softmax(z/T) of the same projection: three
-    vocabulary sweeps, counted as 3*2*S*H*V FLOP)."""
+    (K ids per position drawn from softmax(z/T) of the same projection: two
+    vocabulary sweeps, counted as 2*2*S*H*V FLOP)."""
     S, H, V = wl["S"], wl["H"], wl["V"]
     hidden, W, ids, tl = t
     rng = np.random.default_rng(seed)
@@ -278,7 +278,7 @@ def selection_leg(kd, torch, wl, t, steps=3, warmup=1, n_seq=32, seed=77):
                sample_select_ms=round(t_smp, 3), samples_kept=int(k_smp),
                threshold_ms=round(t_thr, 3), threshold_kept=int(k_thr),
                teacher_sample_ms=round(t_tsm, 3),
-               teacher_sample_tflops=round(3 * 2.0 * S * H * V / (t_tsm / 1000.0) / 1e12, 1),
+               teacher_sample_tflops=round(2 * 2.0 * S * H * V / (t_tsm / 1000.0) / 1e12, 1),
                teacher_sample_ids_in_range=bool(int(sids.min()) >= 0 and int(sids.max()) < V),
                kernels=kernels)
     log(f"[bench] selection leg: signals {t_sig:.2f} ms, per-sequence SE-KD {t_seq:.2f} ms, "

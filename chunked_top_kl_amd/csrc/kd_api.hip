@@ -1056,8 +1056,8 @@ int kd_teacher_topk(const kd_problem* p, const void* hidden, const void* W, int3
 
 // ------------------------------------------------------------------ sampled teacher targets
 struct SampleLayout {
-  int64_t C, ldm, nu, pe;   // rows per chunk, unit-mass pitch, 128-entry units, partial slots
-  size_t flag, em, es, eu, lse, mass, dunit, dres, total;
+  int64_t C, ldm, nu;   // rows per chunk, unit-mass pitch, 128-entry units
+  size_t flag, mass, scale, rowmax, dunit, dres, total;
 };
 
 SampleLayout plan_sample(const kd_problem* p) {
@@ -1066,7 +1066,6 @@ SampleLayout plan_sample(const kd_problem* p) {
   L.C = std::min<int64_t>(p->chunk, S);
   L.ldm = kd::round_up(L.C, 64);
   L.nu = kd::ceil_div(p->V, 128);
-  L.pe = (int64_t)kd::sweep_grid(S, (int)p->V, kCostCUs) * kd::kTile;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -1074,11 +1073,9 @@ SampleLayout plan_sample(const kd_problem* p) {
     return o;
   };
   L.flag = take(8);
-  L.em = take((size_t)L.pe * 4);
-  L.es = take((size_t)L.pe * 8);
-  L.eu = take((size_t)L.pe * 8);
-  L.lse = take((size_t)S * 8);
   L.mass = take((size_t)L.nu * L.ldm * 8);
+  L.scale = take((size_t)L.nu * L.ldm * 4);
+  L.rowmax = take((size_t)L.C * 4);
   L.dunit = take((size_t)L.C * N * 4);
   L.dres = take((size_t)L.C * N * 8);
   L.total = off;
@@ -1111,47 +1108,27 @@ int kd_teacher_sample(const kd_problem* p, const void* hidden, const void* W,
   KD_HIP(hipMemcpyAsync(&h_flag, flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));
   KD_HIP(hipStreamSynchronize(st));
   if (h_flag) return KD_ERR_ARG;
-  kd::SweepArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.W = (const char*)W;
-  a.ldw = ld;
-  a.X = (const char*)hidden;
-  a.ldx = ld;
-  a.row_cap = S;
-  a.V = V;
-  a.H = H;
-  a.K = N;
-  a.ncu = kCostCUs;
-  a.T = p->temperature;
-  a.em = at<float>(ws, L.em);
-  a.es = at<double>(ws, L.es);
-  a.eu = at<double>(ws, L.eu);
-  double* lse = at<double>(ws, L.lse);
-  {
-    // log-normaliser of z/T over the full vocabulary
-    Prof pr("sample_lse", st);
-    KD_HIP(kd::launch_sweep(kd::kSweepEnt, f32, 0, a, kd::sweep_grid(S, V, kCostCUs), st));
-    kd::EntCombineArgs c;
-    c.S = S;
-    c.V = V;
-    c.ncu = kCostCUs;
-    c.em = a.em;
-    c.es = a.es;
-    c.eu = a.eu;
-    c.entropy = nullptr;
-    c.lse = lse;
-    KD_HIP(kd::launch_ent_combine(c, st));
-  }
   double* mass = at<double>(ws, L.mass);
+  float* scale = at<float>(ws, L.scale);
+  float* rowmax = at<float>(ws, L.rowmax);
   int32_t* dunit = at<int32_t>(ws, L.dunit);
   double* dres = at<double>(ws, L.dres);
   for (int64_t c0 = 0; c0 < S; c0 += L.C) {
     const int rows = (int)std::min<int64_t>(L.C, S - c0);
-    kd::SweepArgs b = a;
+    kd::SweepArgs b;
+    std::memset(&b, 0, sizeof(b));
+    b.W = (const char*)W;
+    b.ldw = ld;
     b.X = (const char*)hidden + c0 * ld;
+    b.ldx = ld;
     b.row_cap = rows;
-    b.slse = lse + c0;
+    b.V = V;
+    b.H = H;
+    b.K = N;
+    b.ncu = kCostCUs;
+    b.T = p->temperature;
     b.tmass = mass;
+    b.tscale = scale;
     b.ldm = L.ldm;
     b.N = N;
     const int grid = kd::sweep_grid(rows, V, kCostCUs);
@@ -1161,9 +1138,9 @@ int kd_teacher_sample(const kd_problem* p, const void* hidden, const void* W,
     }
     {
       Prof pr("sample_assign", st);
-      KD_HIP(kd::launch_draw_cumsum(mass, L.ldm, (int)L.nu, rows, st));
-      KD_HIP(kd::launch_draw_assign(mass, L.ldm, (int)L.nu, rows, uniforms + c0 * N, N, dunit,
-                                    dres, ids_out + c0 * N, st));
+      KD_HIP(kd::launch_draw_cumsum(mass, scale, L.ldm, (int)L.nu, rows, rowmax, st));
+      KD_HIP(kd::launch_draw_assign(mass, scale, rowmax, L.ldm, (int)L.nu, rows, uniforms + c0 * N,
+                                    N, dunit, dres, ids_out + c0 * N, st));
     }
     b.dunit = dunit;
     b.dres = dres;

@@ -38,11 +38,12 @@ struct SweepArgs {
   // (row r at r * cap); ids are stored + id_offset
   float* zp; int64_t ldp;
   const float* te; int32_t* cnt; int32_t* cid; float* cz; int64_t cap; int id_offset;
-  // sampled targets (launch row r): log-normaliser of z/T slse[r]; the mass
-  // of each 128-entry vocabulary unit u (one wave's half tile), tmass[u * ldm
-  // + r]; per draw n of row r its unit dunit[r * N + n] and the residual mass
-  // dres[r * N + n] inside that unit; the sampled id sids[r * N + n]
-  const double* slse; double* tmass; int64_t ldm;
+  // sampled targets (launch row r): the mass of each 128-entry vocabulary
+  // unit u (one wave's half tile), tmass[u * ldm + r], in the unit's own scale
+  // 2^-tscale[u * ldm + r] (tscale = its largest z * log2(e) / T); per draw n
+  // of row r its unit dunit[r * N + n] and the residual mass dres[r * N + n]
+  // inside that unit, in the unit's scale; the sampled id sids[r * N + n]
+  double* tmass; float* tscale; int64_t ldm;
   const int32_t* dunit; const double* dres; int32_t* sids; int N;
 };
 
@@ -162,11 +163,14 @@ hipError_t launch_teacher_final(int f32, const TeacherArgs& a, int32_t* big, int
 hipError_t launch_grad_teacher(int f32, const GradTeacherArgs& a, hipStream_t st);
 // sampled targets: the uniforms check (flag set when a value is outside [0, 1)
 // or a row decreases); the in-place cumulative sum of the unit masses of
-// `rows` rows; the unit and residual of each draw of those rows
+// `rows` rows, brought to the row's largest scale (rowmax); the unit and
+// residual of each draw of those rows
 hipError_t launch_draw_check(const double* u, int64_t S, int N, int32_t* flag, hipStream_t st);
-hipError_t launch_draw_cumsum(double* tmass, int64_t ldm, int nu, int rows, hipStream_t st);
-hipError_t launch_draw_assign(const double* cum, int64_t ldm, int nu, int rows, const double* u,
-                              int N, int32_t* dunit, double* dres, int32_t* sids, hipStream_t st);
+hipError_t launch_draw_cumsum(double* tmass, const float* tscale, int64_t ldm, int nu, int rows,
+                              float* rowmax, hipStream_t st);
+hipError_t launch_draw_assign(const double* cum, const float* tscale, const float* rowmax,
+                              int64_t ldm, int nu, int rows, const double* u, int N,
+                              int32_t* dunit, double* dres, int32_t* sids, hipStream_t st);
 int sweep_grid(int64_t rows_max, int V, int ncu);
 hipError_t launch_fwd_combine(const CombineArgs& a, hipStream_t st);
 hipError_t launch_ent_combine(const EntCombineArgs& a, hipStream_t st);

@@ -5,9 +5,10 @@
 // smallest id v with F(v) > u, F the cumulative probability over ids 0..v.
 //
 // The vocabulary sweeps (kd_sweep.hip) store the mass of every 128-entry
-// unit of each row and later resolve a draw inside its unit. Between them,
-// these kernels turn the unit masses into a cumulative sum and give every
-// draw its unit and the residual mass inside it.
+// unit of each row, each in its own scale, and later resolve a draw inside
+// its unit. Between them, these kernels turn the unit masses into a
+// cumulative sum in one scale per row and give every draw its unit and the
+// residual mass inside it.
 #include "kd_common.hpp"
 #include "kd_kernels.hpp"
 
@@ -42,24 +43,46 @@ hipError_t launch_draw_check(const double* u, int64_t S, int N, int32_t* flag, h
   return hipGetLastError();
 }
 
-// One thread per row: the unit masses become their running sum in vocabulary
-// order, in fp64 and in place ([unit][row], pitch ldm), so that neighbouring
-// threads touch neighbouring addresses. Sequential addition of non-negative
-// terms keeps the sum non-decreasing, which the search below relies on.
-__global__ __launch_bounds__(256) void draw_cumsum_kernel(double* m, int64_t ldm, int nu, int rows) {
+// One thread per row. Each unit's mass is stored in its own scale 2^-sc
+// (sc = c times the unit's largest logit); with M the row's largest sc, the
+// masses are brought to the scale 2^-M and become their running sum in
+// vocabulary order, in fp64 and in place ([unit][row], pitch ldm), so that
+// neighbouring threads touch neighbouring addresses. Sequential addition of
+// non-negative terms keeps the sum non-decreasing, which the search below
+// relies on. A row with non-finite logits gets a NaN sum.
+__global__ __launch_bounds__(256) void draw_cumsum_kernel(double* m, const float* sc, int64_t ldm,
+                                                          int nu, int rows, float* rowmax) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= rows) return;
+  // 32 units at a time: their loads are issued together, then used in order
+  constexpr int kB = 32;
+  float M = -INFINITY;
+  for (int k0 = 0; k0 < nu; k0 += kB) {
+    float v[kB];
+#pragma unroll
+    for (int i = 0; i < kB; ++i) v[i] = (k0 + i < nu) ? sc[(int64_t)(k0 + i) * ldm + t] : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kB; ++i) M = fmaxf(M, v[i]);
+  }
+  rowmax[t] = M;
   double run = 0.0;
   double* p = m + t;
-  // 32 units at a time: their loads are issued together, then added in order
-  constexpr int kB = 32;
   for (int k0 = 0; k0 < nu; k0 += kB) {
     double v[kB];
-#pragma unroll
-    for (int i = 0; i < kB; ++i) v[i] = (k0 + i < nu) ? p[(int64_t)(k0 + i) * ldm] : 0.0;
+    float f[kB];
 #pragma unroll
     for (int i = 0; i < kB; ++i) {
-      run += v[i];
+      const bool in = k0 + i < nu;
+      v[i] = in ? p[(int64_t)(k0 + i) * ldm] : 0.0;
+      f[i] = in ? sc[(int64_t)(k0 + i) * ldm + t] : M;
+    }
+    // the scale factor in fp32 (the exponent difference is exact in fp64 and
+    // small where it matters): its 1e-7 relative error is far below that of
+    // the weights themselves
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      const float d = (float)((double)f[i] - (double)M);
+      run += v[i] * (double)__builtin_amdgcn_exp2f(d);
       v[i] = run;
     }
 #pragma unroll
@@ -68,22 +91,25 @@ __global__ __launch_bounds__(256) void draw_cumsum_kernel(double* m, int64_t ldm
   }
 }
 
-hipError_t launch_draw_cumsum(double* tmass, int64_t ldm, int nu, int rows, hipStream_t st) {
+hipError_t launch_draw_cumsum(double* tmass, const float* tscale, int64_t ldm, int nu, int rows,
+                              float* rowmax, hipStream_t st) {
   if (rows > 0)
     hipLaunchKernelGGL(draw_cumsum_kernel, dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, st,
-                       tmass, ldm, nu, rows);
+                       tmass, tscale, ldm, nu, rows, rowmax);
   return hipGetLastError();
 }
 
 // One thread per draw (row t, draw n). With Z the row's total mass, the draw
 // aims at mass u Z: its unit is the first whose cumulative mass exceeds that,
-// and its residual the aim less the mass of the units before. An aim at or
-// above Z (u within rounding of 1) takes the unit where the cumulative mass
-// first reaches Z (the last unit of positive mass) with an unbounded residual:
-// the draw pass then takes that unit's last entry of positive weight. A row
-// whose total is not a positive finite number (non-finite logits) gets unit
-// -1, which no unit matches, and keeps the id -1 written here.
-__global__ __launch_bounds__(256) void draw_assign_kernel(const double* cum, int64_t ldm, int nu,
+// and its residual the aim less the mass of the units before, given in the
+// unit's own scale. An aim at or above Z (u within rounding of 1) takes the
+// unit where the cumulative mass first reaches Z (the last unit of positive
+// mass) with an unbounded residual: the draw pass then takes that unit's last
+// entry of positive weight. A row whose total is not a positive finite number
+// (non-finite logits) gets unit -1, which no unit matches, and keeps the id -1
+// written here.
+__global__ __launch_bounds__(256) void draw_assign_kernel(const double* cum, const float* sc,
+                                                          const float* rowmax, int64_t ldm, int nu,
                                                           int rows, const double* u, int N,
                                                           int32_t* dunit, double* dres,
                                                           int32_t* sids) {
@@ -110,15 +136,21 @@ __global__ __launch_bounds__(256) void draw_assign_kernel(const double* cum, int
     else lo = mid + 1;
   }
   dunit[i] = lo;
-  dres[i] = top ? INFINITY : aim - (lo > 0 ? c[(int64_t)(lo - 1) * ldm] : 0.0);
+  if (top) {
+    dres[i] = INFINITY;
+  } else {
+    const double r = aim - (lo > 0 ? c[(int64_t)(lo - 1) * ldm] : 0.0);
+    dres[i] = r * exp2((double)rowmax[t] - (double)sc[(int64_t)lo * ldm + t]);
+  }
 }
 
-hipError_t launch_draw_assign(const double* cum, int64_t ldm, int nu, int rows, const double* u,
-                              int N, int32_t* dunit, double* dres, int32_t* sids, hipStream_t st) {
+hipError_t launch_draw_assign(const double* cum, const float* tscale, const float* rowmax,
+                              int64_t ldm, int nu, int rows, const double* u, int N,
+                              int32_t* dunit, double* dres, int32_t* sids, hipStream_t st) {
   const int64_t n = (int64_t)rows * N;
   if (n > 0)
     hipLaunchKernelGGL(draw_assign_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, cum,
-                       ldm, nu, rows, u, N, dunit, dres, sids);
+                       tscale, rowmax, ldm, nu, rows, u, N, dunit, dres, sids);
   return hipGetLastError();
 }
 

@@ -13,9 +13,10 @@
 //    threshold to the row's candidate list (kd_teacher.hip picks the K);
 //  - sampled targets (RS-KD: ids drawn from the teacher's softmax at T by
 //    inverse transform in vocabulary order): a mass pass that stores the
-//    probability mass of every 128-entry vocabulary unit of each row, and a
-//    draw pass that, for the draws assigned to a unit (kd_sample.hip),
-//    finds the entry where the running mass passes the draw's residual.
+//    probability mass of every 128-entry vocabulary unit of each row (in the
+//    unit's own scale, with that scale), and a draw pass that, for the draws
+//    assigned to a unit (kd_sample.hip), finds the entry where the running
+//    mass passes the draw's residual.
 //
 // Orientation: MFMA rows (M) are vocabulary entries (A = W tile), MFMA columns
 // (N) are tokens (B = hidden rows). Each lane therefore owns whole token
@@ -426,8 +427,6 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
     tej[j] = INFINITY;
     if constexpr (KIND == kSweepEmit)
       if (tl0 + 32 * j < rows) tej[j] = a.te[tl0 + 32 * j];
-    if constexpr (KIND == kSweepSMass || KIND == kSweepSDraw)
-      lse2[j] = (tl0 + 32 * j < rows) ? (float)(a.slse[orow[j]] * 1.4426950408889634) : 0.0f;
     dcur[j] = a.N;
     dnext[j] = 0x7FFFFFFF;
     if constexpr (KIND == kSweepSDraw) {
@@ -600,16 +599,25 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
       }
 
       if constexpr (KIND == kSweepSMass || KIND == kSweepSDraw) {
-        // weights 2^(z c - lse2) (the teacher softmax at T; entries past V
-        // weigh 0), summed per quad: four consecutive vocabulary entries. The
-        // lane's quad k = 4i + q sits at position 2k + half of the wave's
-        // 128-entry unit; the partner lane (other half) holds the others.
-        // Both passes compute the same values in the same order, so the draw
-        // pass sees the masses the mass pass stored.
+        // weights 2^(z c - mc) of the teacher softmax at T in the unit's own
+        // scale, mc = c times the largest z of the unit's 128 entries (entries
+        // past V weigh 0), summed per quad: four consecutive vocabulary
+        // entries. The lane's quad k = 4i + q sits at position 2k + half of
+        // the unit; the partner lane (other half) holds the others. Both
+        // passes compute the same values in the same order, so the draw pass
+        // sees the masses the mass pass stored.
+        float mx = -INFINITY;
 #pragma unroll
         for (int e = 0; e < 64; ++e) {
           const bool in = !tail || vw0 + acc_row(e >> 4, e & 15, half) < a.V;
-          z[e] = in ? fast_exp2(fmaf(z[e], c, -lse2[j])) : 0.0f;
+          mx = in ? fmaxf(mx, z[e]) : mx;
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mc = mx * c;
+#pragma unroll
+        for (int e = 0; e < 64; ++e) {
+          const bool in = !tail || vw0 + acc_row(e >> 4, e & 15, half) < a.V;
+          z[e] = in ? fast_exp2(fmaf(z[e], c, -mc)) : 0.0f;
         }
         float g[16], gp[16];
 #pragma unroll
@@ -627,7 +635,10 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
             run += quad(k, 0);
             run += quad(k, 1);
           }
-          if (t < rows && half == 0) a.tmass[(int64_t)unit * a.ldm + t] = (double)run;
+          if (t < rows && half == 0) {
+            a.tmass[(int64_t)unit * a.ldm + t] = (double)run;
+            a.tscale[(int64_t)unit * a.ldm + t] = mc;
+          }
         } else {
           // the column's draws up to this unit: those of lower units belong
           // to the other wave and are passed over

@@ -334,10 +334,10 @@ int kd_teacher_topk(const kd_problem* problem, const void* hidden, const void* W
  * z_tv = h_t . w_v and T = problem->temperature. The target of position t is
  * then the N ids with weight 1/N each (give it to kd_topk_kl_* as a
  * probability cache: tl_kind KD_TEACHER_PROBS, equal values; repeated ids
- * add up). The [S,V] grid is never stored: a full-vocabulary sweep gives each
- * row's log-normaliser, then per chunk of problem->chunk positions one sweep
- * stores the mass of every 128 consecutive ids and another resolves each
- * draw inside its 128 ids.
+ * add up). The [S,V] grid is never stored: per chunk of problem->chunk
+ * positions one sweep stores the mass of every 128 consecutive ids (each in
+ * the scale of its own largest logit) and another resolves each draw inside
+ * its 128 ids.
  *   hidden    [device] [S,H] hw_dtype: the teacher's final hidden states
  *   W         [device] [V,H] hw_dtype: the teacher's output projection
  *   uniforms  [device] [S,N] double in [0, 1), each row non-decreasing (sort
@@ -347,9 +347,9 @@ int kd_teacher_topk(const kd_problem* problem, const void* hidden, const void* W
  *   ids_out   [device] [S,N] int32 output
  *   ws        at least kd_teacher_sample_workspace_bytes(problem) bytes (this
  *             entry point does not use kd_topk_kl_workspace_bytes).
- * Precision: the probabilities are formed in fp32 from the fp32-accumulated
- * logits, their masses summed in fp32 per 4 and 128 ids and in fp64 above,
- * so F_t is met to about 1e-5 absolute; a u that close to a step of F_t may
+ * Precision: the weights are formed in fp32 from the fp32-accumulated
+ * logits, relative to the largest logit of their 128 ids, summed in fp32 per
+ * 4 and 128 ids and in fp64 above, so F_t is met to about 1e-5 absolute; a u that close to a step of F_t may
  * get the neighbouring id. A u within rounding of 1 gives the largest id of
  * positive computed probability. A position with non-finite logits gets -1
  * for every draw. problem->K is N here; problem->tl_* are not used.          */
