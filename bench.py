@@ -434,6 +434,13 @@ def main():
         kernels[name] = dict(launches_per_step=round(n / args.steps, 2), ms_per_step=round(tot / args.steps, 4),
                              avg_ms=round(per, 5),
                              tflops=(round(f / (per / 1000.0) / 1e12, 1) if f else None))
+    if "prepass" in kernels:
+        # teacher prepass: ids (4 B) and logits read, (id, p, k) (12 B) per entry and
+        # 5 B per row written; an HBM-bound step, reported against 8 TB/s
+        tl_b = 2 if wl.get("tl_dtype", "bf16") == "bf16" else 4
+        pb = S * wl["K"] * (4 + tl_b) + S * wl["K"] * 12 + 5 * S
+        gbs = pb / (kernels["prepass"]["avg_ms"] / 1000.0) / 1e9
+        kernels["prepass"].update(bytes=pb, gb_per_s=round(gbs, 1), hbm_frac=round(gbs / 8000.0, 4))
     dom = max(kernels.items(), key=lambda kv: kv[1]["ms_per_step"])
     dom_name, dom_v = dom
     # the forward runs over the rows in the loss, the entropy sweep over all S
