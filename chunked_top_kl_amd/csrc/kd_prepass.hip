@@ -132,10 +132,174 @@ __global__ void prepass_kernel(const int32_t* ids, const void* tl, int tl_f32, i
   }
 }
 
+// The same steps for rows of at most 128 entries, held in registers: entries
+// lane and lane + 64 of the row in each lane, sorted by a bitonic network whose
+// exchanges are cross-lane shuffles (and, at distance 64, a swap inside the
+// lane), so that the four rows of a work-group never wait for each other and
+// nothing goes through LDS. The probability of a run of equal ids is a
+// segmented running sum over the sorted entries, read at the run's last entry.
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__global__ __launch_bounds__(256) void prepass_reg_kernel(const int32_t* ids, const void* tl,
+                                                          int tl_f32, int probs, int64_t S, int K,
+                                                          int V, float invT, int32_t* ids_s,
+                                                          float* p_s, int32_t* korig_s,
+                                                          float* negH_out, uint8_t* present,
+                                                          float* z_topk) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= S) return;   // wave-uniform; the kernel has no work-group barrier
+  const int64_t base = t * K;
+  int id[2];
+  float l[2];
+  bool has[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int k = lane + 64 * s;
+    has[s] = k < K;
+    id[s] = has[s] ? ids[base + k] : 0;
+    l[s] = has[s] ? load_logit(tl, tl_f32, base + k) : -INFINITY;
+  }
+  // 1. row max over usable entries (logits), flags
+  float mx = -INFINITY;
+  int bad = 0;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    if (!has[s]) continue;
+    if (probs) {
+      if (!(isfinite(l[s]) && l[s] >= 0.0f)) bad = 1;
+    } else {
+      if (isnan(l[s]) || l[s] == INFINITY) bad = 1;
+      if (id[s] >= 0 && id[s] < V && isfinite(l[s])) mx = fmaxf(mx, l[s] * invT);
+    }
+  }
+  mx = wave_max(mx);
+  bad = (int)wave_sum((float)bad) > 0;
+  // 2. normaliser
+  float z = 0.0f;
+  if (probs || mx != -INFINITY) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (has[s] && id[s] >= 0 && id[s] < V && isfinite(l[s])) {
+        if (probs) z += l[s] > 0.0f ? l[s] : 0.0f;
+        else z += __expf(l[s] * invT - mx);
+      }
+    }
+  }
+  z = wave_sum(z);
+  const float logz = __logf(z);
+  const bool has_mass = probs ? (z > 0.0f) : (mx != -INFINITY);
+  // 3. probabilities and sort keys (id, k); entries past K sort last
+  uint64_t key[2];
+  float p[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int k = lane + 64 * s;
+    key[s] = ~0ull;
+    p[s] = 0.0f;
+    if (has[s]) {
+      const bool inr = id[s] >= 0 && id[s] < V;
+      if (inr && isfinite(l[s]) && has_mass) {
+        if (probs) p[s] = l[s] > 0.0f ? l[s] / z : 0.0f;
+        else p[s] = __expf((l[s] * invT - mx) - logz);
+      }
+      const uint32_t kid = inr ? (uint32_t)id[s] : 0x7FFFFFFFu;
+      key[s] = ((uint64_t)kid << 32) | (uint32_t)k;
+      if (z_topk) z_topk[base + k] = __int_as_float(0x7FC00000);  // NaN until gathered
+    }
+  }
+  // 4. bitonic sort of entry i = lane + 64 s, ascending by key
+  for (int kk = 2; kk <= 128; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      if (j == 64) {   // only for kk = 128: ascending across the two slots
+        if (key[1] < key[0]) {
+          const uint64_t tk = key[0];
+          key[0] = key[1];
+          key[1] = tk;
+          const float tp = p[0];
+          p[0] = p[1];
+          p[1] = tp;
+        }
+        continue;
+      }
+      const bool lower = (lane & j) == 0;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int i = lane + 64 * s;
+        const bool up = (i & kk) == 0;
+        const uint64_t ok = shfl_xor_u64(key[s], j);
+        const float op = __shfl_xor(p[s], j, 64);
+        const bool take = (lower == up) ? (ok < key[s]) : (ok > key[s]);
+        if (take) {
+          key[s] = ok;
+          p[s] = op;
+        }
+      }
+    }
+  }
+  // 5. runs of equal ids: segmented inclusive sum of p within each slot, the
+  // second slot continuing the first slot's last run
+  uint32_t idv[2];
+  idv[0] = (uint32_t)(key[0] >> 32);
+  idv[1] = (uint32_t)(key[1] >> 32);
+  const uint32_t last0 = (uint32_t)__shfl((int)idv[0], 63, 64);
+  const uint32_t first1 = (uint32_t)__shfl((int)idv[1], 0, 64);
+  float v[2];
+  int f[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const uint32_t up1 = (uint32_t)__shfl_up((int)idv[s], 1, 64);
+    const uint32_t prev = lane > 0 ? up1 : (s == 0 ? ~idv[s] : last0);
+    f[s] = prev != idv[s] ? 1 : 0;
+    v[s] = p[s];
+    for (int d = 1; d < 64; d <<= 1) {
+      const float vu = __shfl_up(v[s], d, 64);
+      const int fu = __shfl_up(f[s], d, 64);
+      if (lane >= d) {
+        if (!f[s]) v[s] = vu + v[s];
+        f[s] |= fu;
+      }
+    }
+  }
+  const float carry = __shfl(v[0], 63, 64);
+  if (!f[1]) v[1] = carry + v[1];
+  float nh = 0.0f;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const uint32_t dn = (uint32_t)__shfl_down((int)idv[s], 1, 64);
+    const bool tail = lane < 63 ? dn != idv[s] : (s == 0 ? first1 != idv[0] : true);
+    const bool valid = idv[s] < 0x7FFFFFFFu;
+    if (tail && valid && v[s] > 0.0f) nh += v[s] * __logf(v[s]);
+  }
+  nh = wave_sum(nh);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int k = lane + 64 * s;
+    if (k < K) {
+      ids_s[base + k] = (int32_t)idv[s];
+      p_s[base + k] = p[s];
+      korig_s[base + k] = (int32_t)(key[s] & 0xFFFFFFFFu);
+    }
+  }
+  if (lane == 0) {
+    negH_out[t] = nh;
+    present[t] = (!bad && has_mass) ? 1 : 0;
+  }
+}
+
 hipError_t launch_prepass(const int32_t* ids, const void* tl, int tl_f32, int probs, int64_t S,
                           int K, int V, float T, int32_t* ids_s, float* p_s, int32_t* korig_s,
                           float* negH, uint8_t* present, float* z_topk, hipStream_t st) {
   if (S <= 0) return hipSuccess;
+  if (K <= 128) {
+    hipLaunchKernelGGL(prepass_reg_kernel, dim3((unsigned)ceil_div(S, 4)), dim3(256), 0, st, ids, tl,
+                       tl_f32, probs, S, K, V, 1.0f / T, ids_s, p_s, korig_s, negH, present, z_topk);
+    return hipGetLastError();
+  }
   int n2 = 1;
   while (n2 < K) n2 <<= 1;
   const int rpb = n2 <= 1024 ? 4 : 1;
