@@ -101,6 +101,28 @@ def test_mask_missing_rows_duplicates_neg_inf(kd):
     check_against_oracle(p, got2)
 
 
+@pytest.mark.parametrize("K", [65, 128, 129, 300])
+def test_prepass_sort_paths_long_duplicate_runs(kd, K):
+    """Both teacher-prepass sorts (rows of up to 128 entries in registers, longer
+    rows in LDS) with runs of equal ids long enough to cross lanes and the two
+    entries a lane holds, and -inf entries; the probabilities of equal ids
+    add."""
+    # V < 4K: the input recipe then draws each row as a random K-subset (its
+    # redraw of colliding rows would take very long at K = 300 of 3001)
+    S, H, V = 300, 64, 4 * K - 1
+    p = make_problem(S, H, V, K, T=1.3, chunk=128, seed=500 + K)
+    rng = np.random.Generator(np.random.PCG64(K))
+    rows = np.arange(0, S, 2)
+    p.ids[rows] = rng.integers(0, 20, size=(len(rows), K)).astype(np.int32)
+    p.ids[7, : K // 2] = 3                      # one run over half the row
+    tl = p.tlogits.copy()
+    tl[11, 1:K:3] = -np.inf
+    p.tl_bits = bf16_bits_from_f32(tl)
+    p.tlogits = f32_from_bf16_bits(p.tl_bits)
+    got = run_fwd_bwd(kd, p, grad=0.7)
+    check_against_oracle(p, got, grad=0.7)
+
+
 def test_z_topk_gathers_the_cached_ids_exactly(kd):
     # W[v,0] = floor(v/256), W[v,1] = v mod 256 (exact in bf16); even rows e0, odd rows e1,
     # each pair shares its teacher ids: z at the gathered ids decodes back to the id.
