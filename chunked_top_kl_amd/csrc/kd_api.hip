@@ -924,7 +924,8 @@ constexpr int kTeacherBigGroups = 16;      // work-groups (and scratch areas) fo
 
 struct TeacherLayout {
   int64_t C, P, NG, ldp, cap;   // P pilot vocabulary rows, NG groups of 16 of them
-  size_t zp, cid, cz, cnt, te, bnd, tau2, big, nbig, wpart, wmax, scratch, total;
+  int64_t scnt_ld;              // per row: 4 emit writers for each vocabulary range
+  size_t zp, cid, cz, cnt, scnt, te, bnd, tau2, big, nbig, wpart, wmax, scratch, total;
 };
 
 TeacherLayout plan_teacher(const kd_problem* p) {
@@ -934,7 +935,16 @@ TeacherLayout plan_teacher(const kd_problem* p) {
   L.P = std::min<int64_t>(V, kPilotRows);
   L.NG = kd::ceil_div(L.P, kd::kTile) * 16;
   L.ldp = kd::round_up(L.C, 64);
-  L.cap = V;   // a row's candidates are distinct vocabulary entries
+  // a row's candidates are distinct vocabulary entries; the emit pass lays
+  // them out in per-writer sub-lists that together span whole 256-entry tiles
+  L.cap = kd::round_up(V, kd::kTile);
+  {
+    const int nvt = (int)kd::ceil_div(V, kd::kTile);
+    int nsmax = 1;
+    for (int n = 1; n <= (int)kd::ceil_div(L.C, kd::kTile); ++n)
+      nsmax = std::max(nsmax, kd::sweep_splits(n, nvt, kCostCUs));
+    L.scnt_ld = (int64_t)nsmax * 4;
+  }
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -945,6 +955,7 @@ TeacherLayout plan_teacher(const kd_problem* p) {
   L.cid = take((size_t)L.C * L.cap * 4);
   L.cz = take((size_t)L.C * L.cap * 4);
   L.cnt = take((size_t)L.C * 4);
+  L.scnt = take((size_t)L.C * L.scnt_ld * 4);
   L.te = take((size_t)L.C * 4);
   L.bnd = take((size_t)L.C * 8);
   L.tau2 = take((size_t)L.C * 4);
@@ -1042,8 +1053,17 @@ int kd_teacher_topk(const kd_problem* p, const void* hidden, const void* W, int3
       e.cz = t.cz;
       e.cap = t.cap;
       e.id_offset = 0;
-      Prof pr("teacher_emit", st);
-      KD_HIP(kd::launch_sweep(kd::kSweepEmit, f32, 0, e, kd::sweep_grid(rows, V, kCostCUs), st));
+      e.scnt = at<int32_t>(ws, L.scnt);
+      e.scnt_ld = L.scnt_ld;
+      {
+        Prof pr("teacher_emit", st);
+        KD_HIP(kd::launch_sweep(kd::kSweepEmit, f32, 0, e, kd::sweep_grid(rows, V, kCostCUs), st));
+      }
+      Prof pr("teacher_gather", st);
+      const int nvt = (int)kd::ceil_div(V, kd::kTile);
+      const int ns = kd::sweep_splits((int)kd::ceil_div(rows, kd::kTile), nvt, kCostCUs);
+      KD_HIP(kd::launch_teacher_gather(t.cid, t.cz, t.cap, e.scnt, e.scnt_ld, ns, nvt, rows, t.cnt,
+                                       st));
     }
     {
       Prof pr("teacher_final", st);

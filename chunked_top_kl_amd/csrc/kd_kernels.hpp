@@ -45,6 +45,9 @@ struct SweepArgs {
   // inside that unit, in the unit's scale; the sampled id sids[r * N + n]
   double* tmass; float* tscale; int64_t ldm;
   const int32_t* dunit; const double* dres; int32_t* sids; int N;
+  // teacher cache writer: length of each writer's candidate sub-list,
+  // scnt[r * scnt_ld + range * 4 + writer]
+  int32_t* scnt; int64_t scnt_ld;
 };
 
 constexpr int kTeacherWnormGroups = 1024;   // work-groups of the max ||w_v|| pass
@@ -161,6 +164,11 @@ hipError_t launch_teacher_threshold(int f32, const TeacherArgs& a, int32_t* nbig
 hipError_t launch_teacher_final(int f32, const TeacherArgs& a, int32_t* big, int32_t* nbig,
                                 float* tau2, int grid, int grid_big, hipStream_t st);
 hipError_t launch_grad_teacher(int f32, const GradTeacherArgs& a, hipStream_t st);
+// teacher cache writer: closes the gaps between the emit pass's sub-lists of
+// each of `rows` rows (ns vocabulary ranges x 4 writers) and sets cnt
+hipError_t launch_teacher_gather(int32_t* cid, float* cz, int64_t cap, const int32_t* scnt,
+                                 int64_t scnt_ld, int ns, int nvt, int rows, int32_t* cnt,
+                                 hipStream_t st);
 // sampled targets: the uniforms check (flag set when a value is outside [0, 1)
 // or a row decreases); the in-place cumulative sum of the unit masses of
 // `rows` rows, brought to the row's largest scale (rowmax); the unit and

@@ -10,7 +10,8 @@
 //    computed once and only each position's K largest kept): a pilot pass
 //    that stores the maxima of groups of 16 logits of the first vocabulary
 //    rows, and an emit pass that appends every logit at or above a per-row
-//    threshold to the row's candidate list (kd_teacher.hip picks the K);
+//    threshold to the row's candidate list, in one sub-list per writer
+//    (kd_teacher.hip gathers them and picks the K);
 //  - sampled targets (RS-KD: ids drawn from the teacher's softmax at T by
 //    inverse transform in vocabulary order): a mass pass that stores the
 //    probability mass of every 128-entry vocabulary unit of each row (in the
@@ -407,6 +408,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
   float lse2[4];
   float tej[4];   // emission threshold of each token column (teacher cache writer)
   int dcur[4], dnext[4];   // sampled targets: next draw of the column and its unit
+  int ecnt[4];             // teacher cache writer: candidates this lane appended per column
   float coef = 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -425,6 +427,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
     if constexpr (KIND == kSweepBwdG)
       lse2[j] = (tl0 + 32 * j < rows) ? a.lse[orow[j]] * kLog2e : 0.0f;
     tej[j] = INFINITY;
+    ecnt[j] = 0;
     if constexpr (KIND == kSweepEmit)
       if (tl0 + 32 * j < rows) tej[j] = a.te[tl0 + 32 * j];
     dcur[j] = a.N;
@@ -527,32 +530,25 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
 
       if constexpr (KIND == kSweepEmit) {
         // every logit at or above the row's threshold joins the row's
-        // candidate list (columns past the rows have an infinite threshold).
-        // Entries past V are tested explicitly: they hold -inf, which a
-        // threshold of -inf (a row with fewer pilot groups than K) admits.
-        // The lane's hits are counted first and their slots reserved with one
-        // atomic, so the hits of a column do not each wait for a round trip.
+        // candidates (columns past the rows have an infinite threshold and
+        // are excluded besides). Entries past V are tested explicitly: they
+        // hold -inf, which a threshold of -inf (a row with fewer pilot groups
+        // than K) admits. Each writer - this work-group's vocabulary range,
+        // and within it this wave and lane half - appends to a sub-list of
+        // its own in the row's list, with room for every entry it can see
+        // (64 per tile of the range), so no atomic is needed; the gather
+        // kernel then closes the gaps.
         const int t = tl0 + 32 * j;
-        int nh = 0;
+        const int nr = vt_end - vt_begin;
+        const int64_t sb = (int64_t)t * a.cap + (int64_t)vt_begin * kTile +
+                           (int64_t)(wm * 2 + half) * nr * 64;
 #pragma unroll
         for (int e = 0; e < 64; ++e) {
           const int v = vw0 + acc_row(e >> 4, e & 15, half);
-          nh += (z[e] >= tej[j] && (!tail || v < a.V)) ? 1 : 0;
-        }
-        if (nh > 0) {
-          int pos = atomicAdd(a.cnt + t, nh);
-          int32_t* cid = a.cid + (int64_t)t * a.cap;
-          float* cz = a.cz + (int64_t)t * a.cap;
-#pragma unroll
-          for (int e = 0; e < 64; ++e) {
-            const int v = vw0 + acc_row(e >> 4, e & 15, half);
-            if (z[e] >= tej[j] && (!tail || v < a.V)) {
-              if (pos < a.cap) {   // always: a row emits each vocabulary entry once
-                cid[pos] = v + a.id_offset;
-                cz[pos] = z[e];
-              }
-              ++pos;
-            }
+          if (z[e] >= tej[j] && t < rows && (!tail || v < a.V)) {
+            a.cid[sb + ecnt[j]] = v + a.id_offset;
+            a.cz[sb + ecnt[j]] = z[e];
+            ++ecnt[j];
           }
         }
       }
@@ -754,6 +750,14 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
     column(std::integral_constant<int, 3>());
   }
 
+  if constexpr (KIND == kSweepEmit) {
+    // the length of each of this lane's sub-lists: [row][range][writer]
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = tl0 + 32 * j;
+      if (t < rows) a.scnt[(int64_t)t * a.scnt_ld + b * 4 + wm * 2 + half] = ecnt[j];
+    }
+  }
   if constexpr (KIND == kSweepBwdG || KIND == kSweepPilot || KIND == kSweepEmit ||
                 KIND == kSweepSMass || KIND == kSweepSDraw)
     return;

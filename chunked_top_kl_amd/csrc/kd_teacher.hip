@@ -443,6 +443,86 @@ __global__ __launch_bounds__(256) void teacher_final_big_kernel(TeacherArgs a, c
   }
 }
 
+// Gather of the emit pass's candidates. The pass wrote each row's candidates
+// into one sub-list per writer: vocabulary range b (tiles [b nvt / ns,
+// (b + 1) nvt / ns)) and writer w (wave and lane half) start at tile_begin *
+// 256 + w * (tiles in the range) * 64 of the row's list. One work-group per
+// row forms the running total of the sub-list lengths, then moves the
+// candidates to the front of the list, 256 at a time: candidate i (in
+// sub-list order) goes to position i from a position at or after i, and each
+// round's reads have all returned before any of its writes (a wait for the
+// loads, then a barrier), so no candidate is overwritten before it is read.
+constexpr int kGatherMaxSub = 4096;
+
+__global__ __launch_bounds__(256) void teacher_gather_kernel(int32_t* cid, float* cz, int64_t cap,
+                                                             const int32_t* scnt, int64_t scnt_ld,
+                                                             int ns, int nvt, int rows,
+                                                             int32_t* cnt) {
+  __shared__ int pre[kGatherMaxSub + 1];
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x;
+  const int nsub = ns * 4;
+  const int32_t* sc = scnt + (int64_t)t * scnt_ld;
+  if (tid < 64) {
+    // exclusive running total of the lengths, 64 sub-lists at a time
+    int run = 0;
+    for (int c0 = 0; c0 < nsub; c0 += 64) {
+      const int v = (c0 + tid < nsub) ? sc[c0 + tid] : 0;
+      int x = v;
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (tid >= d) x += y;
+      }
+      if (c0 + tid < nsub) pre[c0 + tid] = run + x - v;
+      run += __shfl(x, 63, 64);
+    }
+    if (tid == 0) pre[nsub] = run;
+  }
+  __syncthreads();
+  const int total = pre[nsub];
+  int32_t* ci = cid + (int64_t)t * cap;
+  float* cv = cz + (int64_t)t * cap;
+  for (int r0 = 0; r0 < total; r0 += 256) {
+    const int i = r0 + tid;
+    const bool has = i < total;
+    int32_t id = 0;
+    float z = 0.0f;
+    if (has) {
+      // the sub-list holding candidate i: the last s with pre[s] <= i
+      int lo = 0, hi = nsub - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= i) lo = mid;
+        else hi = mid - 1;
+      }
+      const int b = lo >> 2, w = lo & 3;
+      const int vb = (int)((int64_t)b * nvt / ns), ve = (int)((int64_t)(b + 1) * nvt / ns);
+      const int64_t src = (int64_t)vb * 256 + (int64_t)w * (ve - vb) * 64 + (i - pre[lo]);
+      id = ci[src];
+      z = cv[src];
+    }
+    // the loads must have returned before any thread stores: a work-group
+    // barrier alone does not wait for them
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (has) {
+      ci[i] = id;
+      cv[i] = z;
+    }
+  }
+  if (tid == 0) cnt[t] = total;
+}
+
+hipError_t launch_teacher_gather(int32_t* cid, float* cz, int64_t cap, const int32_t* scnt,
+                                 int64_t scnt_ld, int ns, int nvt, int rows, int32_t* cnt,
+                                 hipStream_t st) {
+  if (ns * 4 > kGatherMaxSub) return hipErrorInvalidValue;
+  if (rows > 0)
+    hipLaunchKernelGGL(teacher_gather_kernel, dim3((unsigned)rows), dim3(256), 0, st, cid, cz, cap,
+                       scnt, scnt_ld, ns, nvt, rows, cnt);
+  return hipGetLastError();
+}
+
 hipError_t launch_teacher_threshold(int f32, const TeacherArgs& a, int32_t* nbig, hipStream_t st) {
   const int grid = (int)ceil_div(a.rows, kThrRows);
   if (grid <= 0) return hipSuccess;
