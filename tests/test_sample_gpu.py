@@ -88,6 +88,7 @@ def check_brackets(ids, u, F):
     ("bf16", 300, 256, 5000, 0.75, 128, 16),     # 3 chunks, ragged rows and vocabulary
     ("f32", 130, 72, 1000, 1.0, 64, 8),
     ("bf16", 77, 64, 257, 1.5, 1024, 5),          # one chunk, a one-entry last unit
+    ("bf16", 50, 64, 100, 1.0, 16, 4),            # V below one 128-entry unit
 ])
 def test_midpoints_exact(kd, dtype, S, H, V, T, chunk, N):
     h, W, th, tW = teacher(S, H, V, seed=S + V, dtype=dtype)
