@@ -388,15 +388,27 @@ def oracle_entropy_select_kl(hidden, W, ids, tlogits, num=20, den=100, T=1.0, gr
     return r
 
 
-def oracle_validate_topk(ids, tlogits, V):
+def oracle_validate_topk(ids, tlogits, V, probs=False):
     """Cache checks named in [HF "operations"]: token id range and missing positions.
 
-    Returns (n_bad_id, n_empty_row, n_bad_logit): ids outside [0, V); rows whose
-    K logits are all -inf; logits that are NaN or +inf.
+    Returns (n_bad_id, n_empty_row, n_bad_value).
+      logits (probs=False): ids outside [0, V); rows whose K logits are all
+        -inf; logits that are NaN or +inf.
+      probabilities (probs=True, sampled sparse targets, [SKD] SE-KD3X class
+        axis): ids outside [0, V); rows with no value that is finite and
+        positive (no mass); values that are not finite and >= 0.
+    A row counted as empty or holding a bad value takes no part in the loss.
     """
     ids = np.asarray(ids)
     tl = _f64(tlogits)
     n_bad_id = int(np.count_nonzero((ids < 0) | (ids >= V)))
+    if probs:
+        fin = np.isfinite(tl)
+        with np.errstate(invalid="ignore"):
+            mass = fin & (tl > 0.0)
+            bad = ~(fin & (tl >= 0.0))
+        n_empty = int(np.count_nonzero(~np.any(mass, axis=1))) if tl.shape[1] else tl.shape[0]
+        return n_bad_id, n_empty, int(np.count_nonzero(bad))
     n_empty = int(np.count_nonzero(np.all(np.isneginf(tl), axis=1))) if tl.size else 0
     n_bad_logit = int(np.count_nonzero(np.isnan(tl) | np.isposinf(tl)))
     return n_bad_id, n_empty, n_bad_logit

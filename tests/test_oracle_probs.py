@@ -9,7 +9,7 @@ import math
 
 import numpy as np
 
-from oracle import oracle_from_logits, oracle_loss_grads
+from oracle import oracle_from_logits, oracle_loss_grads, oracle_validate_topk
 
 
 def _case(seed, S=7, H=6, V=31, K=5):
@@ -81,3 +81,40 @@ def test_malformed_rows_are_missing():
     ok[[1, 3, 4]] = False
     sub = oracle_loss_grads(hidden[ok], W, ids[ok], p[ok], probs=True)
     assert abs(r["loss"] - sub["loss"]) <= 1e-12 * abs(sub["loss"])
+
+
+def test_validation_counts_for_probabilities_by_hand():
+    # counted by hand: ids 12 and -3 are out of range for V = 10; values -0.5,
+    # NaN, +inf and -inf are not finite and >= 0; rows 1 (zeros only) and 3
+    # (only bad values) hold no finite positive value
+    ids = np.array([[0, 5, 12], [1, 2, 3], [4, -3, 6], [7, 8, 9]])
+    pv = np.array([[0.5, 0.0, 0.25],
+                   [0.0, 0.0, 0.0],
+                   [-0.5, 0.3, np.nan],
+                   [np.inf, -np.inf, np.nan]])
+    assert oracle_validate_topk(ids, pv, 10, probs=True) == (2, 2, 5)
+    # the same values read as logits: only NaN and +inf are bad, no row is all -inf
+    assert oracle_validate_topk(ids, pv, 10) == (2, 0, 3)
+
+
+def test_validation_flags_exactly_the_rows_the_loss_leaves_out():
+    hidden, W, ids, _ = _case(66, S=40)
+    rng = np.random.default_rng(67)
+    p = rng.random(ids.shape)
+    p[rng.random(ids.shape) < 0.3] = 0.0
+    p[rng.random(ids.shape) < 0.05] = -1.0
+    p[rng.random(ids.shape) < 0.05] = np.nan
+    p[7, :] = 0.0
+    r = oracle_loss_grads(hidden, W, ids, p, probs=True)
+    # a row is left out of the loss exactly when validating it alone reports it
+    # empty or holding a bad value
+    for t in range(ids.shape[0]):
+        _, n_empty, n_bad = oracle_validate_topk(ids[t:t + 1], p[t:t + 1], W.shape[0], probs=True)
+        assert (n_empty + n_bad > 0) == (not r["valid"][t])
+    assert not r["valid"][7]
+
+
+def test_softmax_targets_validate_clean():
+    _, _, ids, tl = _case(68)
+    e = np.exp(tl - tl.max(axis=1, keepdims=True))
+    assert oracle_validate_topk(ids, e / e.sum(axis=1, keepdims=True), 31, probs=True) == (0, 0, 0)
