@@ -43,24 +43,45 @@ STEP_PATTERNS = [
     ("kd_bwd_dhidden", "bwd_dhidden"),
     ("kd_bwd_dw", "bwd_dw"),
     ("dh_reduce_kernel", "bwd_dhidden_reduce"),
+    ("grad_teacher_kernel", "bwd_grad_teacher"),
     ("fwd_combine_kernel", "fwd_combine"),
     ("loss_final_kernel", "fwd_combine"),
     ("ent_combine_kernel", "entropy_combine"),
-    ("prepass_kernel", "prepass"),
+    ("prepass", "prepass"),                      # prepass_kernel, prepass_reg_kernel
     ("compact_kernel", "compact"),
     ("zero_rows_kernel", "zero_rows"),
     ("gather_rows_t", "gather_rows_t"),
     ("transpose_w", "transpose_w"),
+    ("signals_kernel", "position_signals"),
+    ("seg_band_final", "select_segments_final"),
+    ("select_segments", "select_segments"),
+    ("seg_band_", "select_segments"),
+    ("fill_u8_kernel", "select_segments"),
+    ("select_above", "select_above"),
     ("select_threshold", "select_threshold"),
     ("refine_kernel", "select_refine_fp64"),
     ("band_rows_f64", "select_refine_fp64"),
+    ("sample_refined_entropy", "select_refine_fp64"),
     ("select_final", "select_final"),
+    ("sample_mean_kernel", "sample_means"),
+    ("sample_mark_kernel", "select_refine_fp64"),
+    ("sample_band_mean", "sample_final"),
+    ("sample_final", "sample_final"),
+    ("sample_zero_flag", "offsets_check"),
+    ("sample_offsets_check", "offsets_check"),
     ("kd_teacher_pilot", "teacher_pilot"),
     ("kd_teacher_emit", "teacher_emit"),
     ("teacher_threshold_kernel", "teacher_threshold"),
-    ("teacher_final_kernel", "teacher_final"),
-    ("teacher_final_big_kernel", "teacher_final"),
+    ("teacher_gather_kernel", "teacher_gather"),
+    ("teacher_final", "teacher_final"),          # teacher_final_kernel, teacher_final_big_kernel
     ("teacher_wnorm", "teacher_wnorm"),
+    ("kd_sample_mass", "sample_mass"),
+    ("kd_sample_draw", "sample_draw"),
+    ("draw_cumsum", "sample_assign"),
+    ("draw_assign", "sample_assign"),
+    ("draw_zero_flag", "uniforms_check"),
+    ("draw_check", "uniforms_check"),
+    ("validate_order", "validate_order"),
     ("validate_kernel", "validate"),
     ("zero_u64_kernel", "validate"),
     ("copyBuffer", "device_copy"),

@@ -64,3 +64,36 @@ def test_trace_summary(tmp_path):
     assert js["steps"]["bwd_dw"]["avg_ms"] == 1.0
     assert js["steps"]["fwd_lse_gather"]["launches"] == 2
     assert js["steps"]["fwd_lse_gather"]["avg_ms"] == 2.0
+
+
+def _kernel_names():
+    """Names of every __global__ kernel defined in the library's sources."""
+    import os
+    import re
+    from chunked_top_kl_amd.prof_summary import CSRC
+    names = set()
+    for fn in sorted(os.listdir(CSRC)):
+        if not fn.endswith(".hip"):
+            continue
+        text = open(os.path.join(CSRC, fn)).read()
+        for m in re.finditer(r"__global__\s+(?:__launch_bounds__\([^)]*\)\s*)?void\s+"
+                             r"([A-Za-z_][A-Za-z_0-9]*)\s*\(", text):
+            names.add(m.group(1))
+        # kernels stamped out by a macro: KD_SWEEP_KERNEL(name, ...)
+        for m in re.finditer(r"^KD_SWEEP_KERNEL\(([A-Za-z_0-9]+),", text, re.M):
+            names.add(m.group(1))
+    names.discard("NAME")
+    return names
+
+
+def test_every_kernel_maps_to_a_step():
+    names = _kernel_names()
+    assert "prepass_reg_kernel" in names and "kd_bwd_dw_bf16" in names and len(names) > 50
+    unmapped = sorted(n for n in names if step_of(n) == "other")
+    assert not unmapped, unmapped
+    assert step_of("void kd::prepass_reg_kernel<64>(kd::PrepassArgs)") == "prepass"
+    assert step_of("kd::grad_teacher_kernel<__bf16>(kd::GradTeacherArgs)") == "bwd_grad_teacher"
+    assert step_of("teacher_gather_kernel") == "teacher_gather"
+    assert step_of("kd_sample_draw_bf16") == "sample_draw"
+    assert step_of("kd::sample_refined_entropy_kernel(kd::SelectWs, int, int, double*)") == \
+        "select_refine_fp64"
