@@ -110,15 +110,91 @@ def blas_threads():
 
 
 def cpu_baseline(p, wl, rows):
-    """fp64 oracle forward+backward on the first `rows` positions of the same workload."""
+    """fp64 oracle forward+backward on the first `rows` positions of the same workload.
+    `cores` is the number of BLAS threads the oracle's products ran on; the
+    host's logical CPU count is given beside it."""
     from oracle import oracle_loss_grads
     threads = blas_threads()
     t0 = time.perf_counter()
     oracle_loss_grads(p.hidden[:rows], p.W, p.ids[:rows], p.tlogits[:rows], T=wl["T"], chunk=128)
     dt = time.perf_counter() - t0
     return dict(value=rows / dt, unit="tokens/s", cores=int(threads), kind="oracle",
+                host_cpu_count=os.cpu_count(), blas_threads=int(threads),
                 sample=f"first {rows} positions of the workload (full H and V): fp64 loss, "
                        f"dHidden and the dW contribution of those rows, row blocks of 128; {dt:.1f} s")
+
+
+def kernel_table(prof, wl, C, N_rows, steps):
+    """Per-step launches, time and achieved TFLOP/s of each profiled step."""
+    S, H, V = wl["S"], wl["H"], wl["V"]
+    kernels = {}
+    for name, (n, tot) in prof.items():
+        per = tot / max(n, 1)
+        f = kernel_flops(name, wl, C, N_rows if name == "fwd_lse_gather" else S)
+        if name in ("bwd_grad_tile", "bwd_dhidden", "bwd_dw"):
+            f = 8.0 * N_rows * H * V / 4.0 / max(n / steps, 1)   # per launch, averaged over chunks
+        kernels[name] = dict(launches_per_step=round(n / steps, 2), ms_per_step=round(tot / steps, 4),
+                             avg_ms=round(per, 5),
+                             tflops=(round(f / (per / 1000.0) / 1e12, 1) if f else None))
+    if "prepass" in kernels:
+        # teacher prepass: ids (4 B) and logits read, (id, p, k) (12 B) per entry and
+        # 5 B per row written; an HBM-bound step, reported against 8 TB/s
+        tl_b = 2 if wl.get("tl_dtype", "bf16") == "bf16" else 4
+        pb = S * wl["K"] * (4 + tl_b) + S * wl["K"] * 12 + 5 * S
+        gbs = pb / (kernels["prepass"]["avg_ms"] / 1000.0) / 1e9
+        kernels["prepass"].update(bytes=pb, gb_per_s=round(gbs, 1), hbm_frac=round(gbs / 8000.0, 4))
+    return kernels
+
+
+def time_workload(kd, torch, key, p=None, steps=3, warmup=1):
+    """fwd+bwd of another configuration at its full size (the entropy-selective
+    one with its entropy sweep and selection): ms per step, tokens/s, the MFMA
+    fraction of the counted work, peak device memory and the per-step kernels."""
+    from kd_synth import make_problem
+    wl = dict(WORKLOADS[key])
+    S, H, V, K, C = wl["S"], wl["H"], wl["V"], wl["K"], wl["chunk"]
+    if p is None:
+        log(f"[bench] generating inputs: {wl['name']}")
+        p = make_problem(S, H, V, K, T=wl["T"], chunk=C, seed=wl["seed"])
+    t = to_dev(p, torch)
+    prob = kd.make_problem(S, H, V, K, C, wl["T"], kd.KD_BF16, kd.KD_BF16)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    base = torch.cuda.memory_allocated() - sum(x.numel() * x.element_size() for x in t)
+    ws = torch.empty(kd.kd_topk_kl_workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+    step = (lambda: run_c5_step(kd, torch, wl, t, ws)) if key == "c5" else \
+        (lambda: run_step(kd, torch, wl, t, ws))
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    kd.kd_profile_reset()
+    kd.kd_profile_enable(True)
+    t0 = time.perf_counter()
+    res = None
+    for _ in range(steps):
+        res = None          # the previous step's outputs are freed before the next step
+        res = step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / steps
+    kd.kd_profile_enable(False)
+    prof = kd.kd_profile_read()
+    kd.kd_profile_reset()
+    peak = (torch.cuda.max_memory_allocated() - base) / 2**30
+    N_rows = int(res[1]) if key == "c5" else S
+    flops = 2.0 * S * H * V + 8.0 * N_rows * H * V if key == "c5" else 8.0 * S * H * V
+    loss = float(res[0][0]["loss"][0]) if key == "c5" else float(res[0]["loss"][0])
+    out = dict(workload=wl["name"], steps=steps, warmup=warmup, ms_per_step=round(ms, 3),
+               tokens_per_s=round(S / (ms / 1000.0), 1),
+               mfma_frac=round(flops / (ms / 1000.0) / (PEAK_BF16_TFLOPS * 1e12), 4),
+               counted_tflop_per_step=round(flops / 1e12, 3), rows_in_loss=N_rows,
+               peak_gib=round(peak, 3), loss=loss,
+               kernels=kernel_table(prof, wl, C, N_rows, steps))
+    log(f"[bench] {key}: {ms:.2f} ms/step, {out['tokens_per_s']:.0f} tokens/s, "
+        f"MFMA {100 * out['mfma_frac']:.1f}%, peak {out['peak_gib']} GiB")
+    del ws, t, res
+    torch.cuda.empty_cache()
+    return out
 
 
 def chunk_sweep(kd, torch, wl, t, chunks, steps=3, warmup=1):
@@ -136,6 +212,7 @@ def chunk_sweep(kd, torch, wl, t, chunks, steps=3, warmup=1):
         for _ in range(warmup):
             run_step(kd, torch, wlc, t, ws)
         torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
         t0 = time.perf_counter()
         for _ in range(steps):
             run_step(kd, torch, wlc, t, ws)
@@ -207,7 +284,7 @@ def teacher_leg(kd, torch, wl, t, p, steps=3, warmup=1, cpu_rows=64, cpu=True):
         oracle_teacher_topk(p.hidden[:cpu_rows], p.W, K, out_dtype="bf16")
         d = time.perf_counter() - t0
         out["cpu_baseline"] = dict(value=cpu_rows / d, unit="tokens/s", cores=blas_threads(),
-                                   kind="oracle",
+                                   kind="oracle", host_cpu_count=os.cpu_count(),
                                    sample=f"first {cpu_rows} positions (full H and V): fp64 logits and "
                                           f"the sorted top-{K}; {d:.1f} s")
     return out
@@ -288,13 +365,11 @@ def selection_leg(kd, torch, wl, t, steps=3, warmup=1, n_seq=32, seed=77):
     return out
 
 
-def mem_sweep(kd, torch, sizes, seed=1004):
-    """Peak device memory of one fwd+bwd at the 256K-context shapes for several S."""
-    from kd_synth import make_problem
+def mem_sweep(kd, torch, sizes, p):
+    """Peak device memory of one fwd+bwd at the 256K-context shapes for several S
+    (the first S rows of the 256K-context inputs `p`)."""
     H, V, K, T, C = 3072, 128256, 100, 2.0, 2048
-    Smax = max(sizes)
-    log(f"[bench] generating memory-sweep inputs S<={Smax}")
-    p = make_problem(Smax, H, V, K, T=T, chunk=C, seed=seed)
+    assert (p.H, p.V, p.K) == (H, V, K) and p.S >= max(sizes)
     out = {}
     for S in sorted(sizes):
         torch.cuda.synchronize()
@@ -345,6 +420,9 @@ def main():
     ap.add_argument("--teacher-only", action="store_true",
                     help="time only the teacher top-K cache writer (steps / warmup calls) and "
                          "print its line")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the timed fwd+bwd of the other configurations (8K, 256K, "
+                         "entropy-selective) at full size")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -404,7 +482,9 @@ def main():
     kd.kd_profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    res = None
     for _ in range(args.steps):
+        res = None          # the previous step's outputs are freed before the next step
         res = step()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
@@ -425,22 +505,7 @@ def main():
         flops = 8.0 * S * H * V
     mfma_frac = flops / (ms / 1000.0) / (PEAK_BF16_TFLOPS * 1e12)
 
-    kernels = {}
-    for name, (n, tot) in prof.items():
-        per = tot / max(n, 1)
-        f = kernel_flops(name, wl, C, N_rows if name == "fwd_lse_gather" else S)
-        if name in ("bwd_grad_tile", "bwd_dhidden", "bwd_dw"):
-            f = 8.0 * N_rows * H * V / 4.0 / max(n / args.steps, 1)   # per launch, averaged over chunks
-        kernels[name] = dict(launches_per_step=round(n / args.steps, 2), ms_per_step=round(tot / args.steps, 4),
-                             avg_ms=round(per, 5),
-                             tflops=(round(f / (per / 1000.0) / 1e12, 1) if f else None))
-    if "prepass" in kernels:
-        # teacher prepass: ids (4 B) and logits read, (id, p, k) (12 B) per entry and
-        # 5 B per row written; an HBM-bound step, reported against 8 TB/s
-        tl_b = 2 if wl.get("tl_dtype", "bf16") == "bf16" else 4
-        pb = S * wl["K"] * (4 + tl_b) + S * wl["K"] * 12 + 5 * S
-        gbs = pb / (kernels["prepass"]["avg_ms"] / 1000.0) / 1e9
-        kernels["prepass"].update(bytes=pb, gb_per_s=round(gbs, 1), hbm_frac=round(gbs / 8000.0, 4))
+    kernels = kernel_table(prof, wl, C, N_rows, args.steps)
     dom = max(kernels.items(), key=lambda kv: kv[1]["ms_per_step"])
     dom_name, dom_v = dom
     # the forward runs over the rows in the loss, the entropy sweep over all S
@@ -453,7 +518,8 @@ def main():
                     peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / PEAK_BF16_TFLOPS, 4) if achieved else None,
                     traffic=tr["bytes"] if tr else None,
-                    traffic_unit="HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
+                    traffic_unit="bytes per launch past L2 (calibrated FETCH_SIZE + WRITE_SIZE: "
+                                 "L2 misses, served by the MALL or by HBM)",
                     traffic_detail=tr,
                     flops_per_launch=dom_flops, avg_ms=dom_v["avg_ms"])
 
@@ -487,11 +553,26 @@ def main():
         result["teacher_topk"] = teacher_leg(kd, torch, wl, t, p, cpu=not args.no_cpu_baseline)
     if not args.no_selection:
         result["selection"] = selection_leg(kd, torch, wl, t)
+    del t
+    torch.cuda.empty_cache()
+    if not args.no_workloads:
+        # the other configurations at full size, beside the headline one
+        result["workloads"] = {}
+        for key in ("c2", "c5"):
+            if key != args.workload:
+                result["workloads"][key] = time_workload(kd, torch, key)
+    p4 = None
+    if not args.no_mem_sweep or (not args.no_workloads and args.workload != "c4"):
+        c4 = WORKLOADS["c4"]
+        log("[bench] generating the 256K-context inputs")
+        p4 = make_problem(c4["S"], c4["H"], c4["V"], c4["K"], T=c4["T"], chunk=c4["chunk"],
+                          seed=c4["seed"])
     if not args.no_mem_sweep:
         sizes = [int(x) for x in args.mem_sizes.split(",") if x]
-        del t
-        torch.cuda.empty_cache()
-        result["peak_gib_vs_S"] = mem_sweep(kd, torch, sizes)
+        result["peak_gib_vs_S"] = mem_sweep(kd, torch, sizes, p4)
+    if not args.no_workloads and args.workload != "c4":
+        result["workloads"]["c4"] = time_workload(kd, torch, "c4", p=p4)
+    del p4
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows")
         result["cpu_baseline"] = cpu_baseline(p, wl, args.cpu_rows)

@@ -31,8 +31,7 @@ constexpr int64_t kMaxRows = int64_t(1) << 30;
 constexpr double kSelectEps = 2e-5;    // bound on |fp32-path entropy - fp64 entropy| (nats)
 constexpr int64_t kDwDepth = 8192;     // tokens per dW contraction (a multiple of chunks)
 constexpr int kRefineBatch = 256;      // band rows widened to fp64 per refinement launch
-constexpr int kSampleBandCap = 4096;          // band samples refined (as positions' kBandCap)
-constexpr int kSampleBandPositions = 65536;   // their positions refined in fp64 at most
+constexpr int kRefinePiece = 4096;     // band rows whose fp64 refinement partials are held at once
 // refinement work-groups: one vocabulary row per thread, 256 per group
 inline int64_t refine_blocks(int64_t V) { return ceil_div(V, 256); }
 
@@ -77,36 +76,21 @@ struct Prof {
 };
 
 // ------------------------------------------------------------------ device check
+constexpr int kMaxDevices = 64;
+
 int check_device() {
   static std::mutex mu;
-  static std::map<int, bool> ok_by_dev;
+  static signed char ok_by_dev[kMaxDevices];   // 0 not checked yet, 1 gfx950, -1 other
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return KD_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return KD_ERR_HIP;
   std::lock_guard<std::mutex> g(mu);
-  auto it = ok_by_dev.find(dev);
-  if (it == ok_by_dev.end()) {
+  if (ok_by_dev[dev] == 0) {
     hipDeviceProp_t p;
     if (hipGetDeviceProperties(&p, dev) != hipSuccess) return KD_ERR_HIP;
-    bool ok = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
-    it = ok_by_dev.emplace(dev, ok).first;
+    ok_by_dev[dev] = std::strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
   }
-  return it->second ? KD_OK : KD_ERR_ARCH;
-}
-
-// ------------------------------------------------------------------ problem checks
-int check_problem(const kd_problem* p) {
-  if (!p) return KD_ERR_NULL;
-  if (p->hw_dtype != KD_BF16 && p->hw_dtype != KD_F32) return KD_ERR_DTYPE;
-  if (p->tl_dtype != KD_BF16 && p->tl_dtype != KD_F32) return KD_ERR_DTYPE;
-  if (p->tl_kind != KD_TEACHER_LOGITS && p->tl_kind != KD_TEACHER_PROBS) return KD_ERR_ARG;
-  if (p->S < 0 || p->S > kMaxRows) return KD_ERR_SHAPE;
-  if (p->H <= 0 || p->V <= 0 || p->K <= 0) return KD_ERR_SHAPE;
-  if (p->K > p->V || p->K > kMaxK) return KD_ERR_SHAPE;
-  if (p->H % 8 != 0 || p->H > (int64_t(1) << 20)) return KD_ERR_SHAPE;
-  if (p->V > (int64_t(1) << 30)) return KD_ERR_SHAPE;
-  if (!(p->temperature > 0.0f) || !std::isfinite(p->temperature)) return KD_ERR_TEMPERATURE;
-  if (p->chunk <= 0) return KD_ERR_CHUNK;
-  return KD_OK;
+  return ok_by_dev[dev] > 0 ? KD_OK : KD_ERR_ARCH;
 }
 
 // ------------------------------------------------------------------ workspace plan
@@ -116,7 +100,7 @@ struct Layout {
   size_t G, GT, WT, XcT, Xc, dhp;
   size_t em, es, eu;
   size_t band, refined, scal, dscal, rpart, xb, counters;
-  size_t smean, spos, pent, pstart;
+  size_t smean, spos, pent;
   size_t lse64, segw;
   size_t total;
   int64_t C;          // rows per backward chunk (<= S, >= 1)
@@ -193,17 +177,38 @@ Layout plan(const kd_problem* p) {
   L.refined = take(Sx * 8);
   L.scal = take(16 * 4);
   L.dscal = take(16 * 8);
-  L.rpart = take((size_t)4096 * refine_blocks(V) * 3 * 8);
+  L.rpart = take((size_t)kRefinePiece * refine_blocks(V) * 3 * 8);
   L.xb = take((size_t)kRefineBatch * H * 8);
   L.counters = take(4 * 8);
   L.smean = take(Sx * 8);
-  L.spos = take((size_t)kSampleBandPositions * 4);
-  L.pent = take((size_t)kSampleBandPositions * 8);
-  L.pstart = take((size_t)(kSampleBandCap + 1) * 4);
+  L.spos = take(Sx * 4);
+  L.pent = take(Sx * 8);
   L.lse64 = take(Sx * 8);
   L.segw = take(Sx * 4 * 4);
   L.total = off;
   return L;
+}
+
+// ------------------------------------------------------------------ problem checks
+int check_problem(const kd_problem* p) {
+  if (!p) return KD_ERR_NULL;
+  if (p->hw_dtype != KD_BF16 && p->hw_dtype != KD_F32) return KD_ERR_DTYPE;
+  if (p->tl_dtype != KD_BF16 && p->tl_dtype != KD_F32) return KD_ERR_DTYPE;
+  if (p->tl_kind != KD_TEACHER_LOGITS && p->tl_kind != KD_TEACHER_PROBS) return KD_ERR_ARG;
+  if (p->S < 0 || p->S > kMaxRows) return KD_ERR_SHAPE;
+  if (p->H <= 0 || p->V <= 0 || p->K <= 0) return KD_ERR_SHAPE;
+  if (p->K > p->V || p->K > kMaxK) return KD_ERR_SHAPE;
+  if (p->H % 8 != 0 || p->H > (int64_t(1) << 20)) return KD_ERR_SHAPE;
+  if (p->V > (int64_t(1) << 30)) return KD_ERR_SHAPE;
+  if (!(p->temperature > 0.0f) || !std::isfinite(p->temperature)) return KD_ERR_TEMPERATURE;
+  if (p->chunk <= 0) return KD_ERR_CHUNK;
+  // every operand tile of the contractions (256 rows of the widest pitch, the
+  // gradient tile and W^T rows or the transposed chunk rows) must lie in one
+  // buffer range, whose size is below 2^31 bytes
+  const Layout L = plan(p);
+  if (256 * L.Vld * L.esz >= (int64_t(1) << 31) || 256 * L.Cld * L.esz >= (int64_t(1) << 31))
+    return KD_ERR_SHAPE;
+  return KD_OK;
 }
 
 template <typename T>
@@ -268,16 +273,16 @@ size_t kd_topk_kl_workspace_bytes(const kd_problem* p) {
   return plan(p).total;
 }
 
-int kd_topk_kl_fwd(const kd_problem* p, const void* hidden, const void* W, const int32_t* ids,
-                   const void* tl, const uint8_t* mask, float* loss, float* lse, float* kl_rows,
-                   float* z_topk, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_problem(p);
-  if (rc) return rc;
-  if (!W || !loss || (p->S > 0 && (!hidden || !ids || !tl || !lse))) return KD_ERR_NULL;
-  const Layout L = plan(p);
-  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
-  if ((rc = check_device())) return rc;
-  hipStream_t st = (hipStream_t)stream;
+}  // extern "C"
+
+namespace {
+
+// The forward's launches, with its buffers at the plan's offsets in ws.
+// Arguments are checked by the caller.
+int fwd_run(const kd_problem* p, const Layout& L, const void* hidden, const void* W,
+            const int32_t* ids, const void* tl, const uint8_t* mask, float* loss, float* lse,
+            float* kl_rows, float* z_topk, void* ws, hipStream_t st) {
+  int rc;
   if ((rc = teacher_tables(p, L, ids, tl, mask, z_topk, ws, st))) return rc;
   const int S = (int)p->S, V = (int)p->V, H = (int)p->H, K = (int)p->K;
   const int f32 = p->hw_dtype == KD_F32;
@@ -335,6 +340,30 @@ int kd_topk_kl_fwd(const kd_problem* p, const void* hidden, const void* W, const
     KD_HIP(kd::launch_fwd_combine(c, st));
   }
   return KD_OK;
+}
+
+int fwd_check(const kd_problem* p, const void* hidden, const void* W, const int32_t* ids,
+              const void* tl, const float* loss, const float* lse) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!W || !loss || (p->S > 0 && (!hidden || !ids || !tl || !lse))) return KD_ERR_NULL;
+  return KD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kd_topk_kl_fwd(const kd_problem* p, const void* hidden, const void* W, const int32_t* ids,
+                   const void* tl, const uint8_t* mask, float* loss, float* lse, float* kl_rows,
+                   float* z_topk, void* ws, size_t ws_bytes, void* stream) {
+  int rc = fwd_check(p, hidden, W, ids, tl, loss, lse);
+  if (rc) return rc;
+  const Layout L = plan(p);
+  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  return fwd_run(p, L, hidden, W, ids, tl, mask, loss, lse, kl_rows, z_topk, ws,
+                 (hipStream_t)stream);
 }
 
 int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const int32_t* ids,
@@ -609,6 +638,31 @@ int kd_position_signals(const kd_problem* p, const void* hidden, const void* W,
   return KD_OK;
 }
 
+// fp64 entropies of the n positions list[0..n) into out[0..n): refinement
+// partials for at most kRefinePiece positions at a time, kRefineBatch rows
+// widened per launch
+static int refine_positions(const kd_problem* p, const Layout& L, void* ws, const void* hidden,
+                            const void* W, kd::SelectWs w, const int32_t* list, int64_t n,
+                            double* out, hipStream_t st) {
+  const int f32 = p->hw_dtype == KD_F32;
+  const int64_t ld = p->H * L.esz;
+  const int nblk = (int)refine_blocks(p->V);
+  for (int64_t rs = 0; rs < n; rs += kRefinePiece) {
+    const int np = (int)std::min<int64_t>(kRefinePiece, n - rs);
+    kd::SelectWs wr = w;
+    wr.band = const_cast<int32_t*>(list) + rs;
+    for (int o = 0; o < np; o += kRefineBatch) {
+      Prof pr("select_refine_fp64", st);
+      KD_HIP(kd::launch_refine(f32, (const char*)hidden, ld, (const char*)W, ld, (int)p->V,
+                               (int)p->H, wr, at<double>(ws, L.xb), o,
+                               std::min(kRefineBatch, np - o), nblk, st));
+    }
+    Prof pr("select_refine_fp64", st);
+    KD_HIP(kd::launch_sample_refined_entropy(wr, np, nblk, out + rs, st));
+  }
+  return KD_OK;
+}
+
 // ------------------------------------------------------------------ selection by a signal
 // count of the kept positions (mask) into idx (and its host copy)
 static int compact_mask(const Layout& L, void* ws, int64_t S, const uint8_t* mask, int32_t* idx_out,
@@ -710,15 +764,16 @@ int kd_select_top_fraction_segments(const kd_problem* p, const void* hidden, con
   KD_HIP(hipMemcpyAsync(ha.data(), nabove, (size_t)B * 4, hipMemcpyDeviceToHost, st));
   KD_HIP(hipMemcpyAsync(hoff.data(), offsets, (size_t)(B + 1) * 8, hipMemcpyDeviceToHost, st));
   KD_HIP(hipStreamSynchronize(st));
-  // segments whose band straddles the cut are refined, up to the list's size;
-  // the others keep the decision on the sweep's entropies
+  // segments whose band straddles the cut are refined (segments are disjoint,
+  // so their bands list at most S positions); the others keep the decision on
+  // the sweep's entropies, which no band position can change
   int64_t total = 0;
   for (int64_t b = 0; b < B; ++b) {
     const int64_t k = (num * (hoff[b + 1] - hoff[b])) / den;
     const int64_t nd = k - ha[b];
     hn[b] = (int32_t)nd;
     ho[b] = -1;
-    if (nd > 0 && nd < hb[b] && total + hb[b] <= kSampleBandPositions) {
+    if (nd > 0 && nd < hb[b]) {
       ho[b] = (int32_t)total;
       total += hb[b];
     }
@@ -732,21 +787,7 @@ int kd_select_top_fraction_segments(const kd_problem* p, const void* hidden, con
     kd::SelectWs w;
     std::memset(&w, 0, sizeof(w));
     w.rpart = at<double>(ws, L.rpart);
-    const int f32 = p->hw_dtype == KD_F32;
-    const int64_t ld = p->H * L.esz;
-    const int nblk = (int)refine_blocks(p->V);
-    for (int64_t rs = 0; rs < total; rs += kSampleBandCap) {
-      const int n = (int)std::min<int64_t>(kSampleBandCap, total - rs);
-      kd::SelectWs wr = w;
-      wr.band = plist + rs;
-      for (int o = 0; o < n; o += kRefineBatch) {
-        Prof pr("select_refine_fp64", st);
-        KD_HIP(kd::launch_refine(f32, (const char*)hidden, ld, (const char*)W, ld, (int)p->V,
-                                 (int)p->H, wr, at<double>(ws, L.xb), o,
-                                 std::min(kRefineBatch, n - o), nblk, st));
-      }
-      KD_HIP(kd::launch_sample_refined_entropy(wr, n, nblk, pent + rs, st));
-    }
+    if ((rc = refine_positions(p, L, ws, hidden, W, w, plist, total, pent, st))) return rc;
     Prof pr("select_segments_final", st);
     KD_HIP(kd::launch_seg_band_final(B, boff, nband, need, plist, pent, mask_out, st));
   }
@@ -805,23 +846,11 @@ int kd_select_top_fraction(const kd_problem* p, const void* hidden, const void* 
   int32_t n_band = 0;
   KD_HIP(hipMemcpyAsync(&n_band, w.scal, sizeof(int32_t), hipMemcpyDeviceToHost, st));
   KD_HIP(hipStreamSynchronize(st));
-  const int f32 = p->hw_dtype == KD_F32;
-  const int64_t ld = p->H * L.esz;
-  if (n_band > 0 && n_band <= 4096) {
-    const int nblk = refine_blocks(p->V);
-    for (int off = 0; off < n_band; off += kRefineBatch) {
-      const int n = std::min(kRefineBatch, n_band - off);
-      Prof pr("select_refine_fp64", st);
-      KD_HIP(kd::launch_refine(f32, (const char*)hidden, ld, (const char*)W, ld, (int)p->V,
-                               (int)p->H, w, at<double>(ws, L.xb), off, n, nblk, st));
-    }
-    {
-      Prof pr("select_final", st);
-      KD_HIP(kd::launch_select_final(entropy, S, k, w, n_band, nblk, mask_out, idx_out, st));
-    }
-  } else {
+  // every band row is recomputed in fp64, in pieces, whatever the band's size
+  if ((rc = refine_positions(p, L, ws, hidden, W, w, w.band, n_band, w.refined, st))) return rc;
+  {
     Prof pr("select_final", st);
-    KD_HIP(kd::launch_select_final(entropy, S, k, w, n_band, 1, mask_out, idx_out, st));
+    KD_HIP(kd::launch_select_final(entropy, S, k, w, n_band, mask_out, idx_out, st));
   }
   int32_t cnt = 0;
   KD_HIP(hipMemcpyAsync(&cnt, w.scal + 2, sizeof(int32_t), hipMemcpyDeviceToHost, st));
@@ -876,39 +905,29 @@ int kd_select_samples(const kd_problem* p, const void* hidden, const void* W, co
   const int n_band = h[0], n_above = h[1];
   const int64_t need = k - n_above;
   int refined = 0;
-  int32_t* pstart = at<int32_t>(ws, L.pstart);
-  int32_t* plist = at<int32_t>(ws, L.spos);
-  double* pent = at<double>(ws, L.pent);
-  // the band straddles the cut: rank it on fp64 means
-  if (need > 0 && need < n_band && n_band <= kSampleBandCap) {
-    KD_HIP(kd::launch_sample_band_positions(offsets, w, n_band, pstart, plist,
-                                            kSampleBandPositions, st));
+  // the band straddles the cut: the entropies of every position of its
+  // samples are recomputed in fp64 (each position once, whatever the band's
+  // size or the samples' overlap) and the band is ranked on fp64 means
+  if (need > 0 && need < n_band) {
+    const int64_t S = p->S;
+    uint8_t* flag = at<uint8_t>(ws, L.segw);
+    int32_t* plist = at<int32_t>(ws, L.spos);
+    int32_t* ppos = at<int32_t>(ws, L.pos);
+    double* pent = at<double>(ws, L.pent);
+    int32_t* cnt_dev = at<int32_t>(ws, L.count);
+    KD_HIP(kd::launch_fill_u8(flag, 0, S, st));
+    KD_HIP(kd::launch_sample_mark(offsets, w, n_band, flag, st));
+    KD_HIP(kd::launch_compact(flag, nullptr, S, plist, ppos, cnt_dev, st));
     int32_t total = 0;
-    KD_HIP(hipMemcpyAsync(&total, w.scal + 3, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+    KD_HIP(hipMemcpyAsync(&total, cnt_dev, sizeof(int32_t), hipMemcpyDeviceToHost, st));
     KD_HIP(hipStreamSynchronize(st));
-    if (total <= kSampleBandPositions) {
-      refined = 1;
-      const int f32 = p->hw_dtype == KD_F32;
-      const int64_t ld = p->H * L.esz;
-      const int nblk = (int)refine_blocks(p->V);
-      for (int rs = 0; rs < total; rs += kSampleBandCap) {
-        const int n = std::min(kSampleBandCap, total - rs);
-        kd::SelectWs wr = w;
-        wr.band = plist + rs;
-        for (int off = 0; off < n; off += kRefineBatch) {
-          Prof pr("select_refine_fp64", st);
-          KD_HIP(kd::launch_refine(f32, (const char*)hidden, ld, (const char*)W, ld, (int)p->V,
-                                   (int)p->H, wr, at<double>(ws, L.xb), off,
-                                   std::min(kRefineBatch, n - off), nblk, st));
-        }
-        KD_HIP(kd::launch_sample_refined_entropy(wr, n, nblk, pent + rs, st));
-      }
-    }
+    if ((rc = refine_positions(p, L, ws, hidden, W, w, plist, total, pent, st))) return rc;
+    KD_HIP(kd::launch_sample_band_means(offsets, w, n_band, ppos, pent, st));
+    refined = 1;
   }
   {
     Prof pr("sample_final", st);
-    KD_HIP(kd::launch_sample_final(means, offsets, B, k, w, n_band, refined, pstart, pent, mask_out,
-                                   idx_out, st));
+    KD_HIP(kd::launch_sample_final(means, B, k, w, n_band, refined, mask_out, idx_out, st));
   }
   int32_t cnt = 0;
   KD_HIP(hipMemcpyAsync(&cnt, w.scal + 2, sizeof(int32_t), hipMemcpyDeviceToHost, st));

@@ -218,7 +218,7 @@ hipError_t launch_seg_band_final(int64_t B, const int32_t* boff, const int32_t* 
 struct SelectWs {
   unsigned long long* keys;   // [S]
   int32_t* band;              // [S] band rows
-  double* refined;            // [S] fp64 entropies of band rows (band order)
+  double* refined;            // [S] fp64 entropies (or sample means) of band rows, band order
   int32_t* scal;              // small scalars: [0]=n_band [1]=n_above [2]=k
   double* dscal;              // [0]=threshold value
   double* rpart;              // refine partials [cap][nblk][3]
@@ -230,19 +230,21 @@ hipError_t launch_sample_check(const int64_t* off, int64_t B, int64_t S, int32_t
                                hipStream_t st);
 hipError_t launch_sample_means(const double* E, const int64_t* off, int64_t B, double* means,
                                hipStream_t st);
-hipError_t launch_sample_band_positions(const int64_t* off, const SelectWs& w, int n_band,
-                                        int32_t* pstart, int32_t* plist, int cap, hipStream_t st);
+// sample selection: flag the positions of the band samples; the fp64 mean of
+// each band sample's refined entropies (pent[pos[t]]) into w.refined
+hipError_t launch_sample_mark(const int64_t* off, const SelectWs& w, int n_band, uint8_t* flag,
+                              hipStream_t st);
+hipError_t launch_sample_band_means(const int64_t* off, const SelectWs& w, int n_band,
+                                    const int32_t* pos, const double* pent, hipStream_t st);
 hipError_t launch_sample_refined_entropy(const SelectWs& w, int n, int nblk, double* pent,
                                          hipStream_t st);
-hipError_t launch_sample_final(const double* means, const int64_t* off, int64_t B, int64_t k,
-                               const SelectWs& w, int n_band, int refined, const int32_t* pstart,
-                               const double* pent, uint8_t* mask, int32_t* idx_out,
+hipError_t launch_sample_final(const double* means, int64_t B, int64_t k, const SelectWs& w,
+                               int n_band, int refined, uint8_t* mask, int32_t* idx_out,
                                hipStream_t st);
 hipError_t launch_refine(int f32, const char* X, int64_t ldx, const char* W, int64_t ldw, int V,
                          int H, const SelectWs& w, double* xb, int band_off, int band_n, int nblk,
                          hipStream_t st);
 hipError_t launch_select_final(const double* entropy, int64_t S, int64_t k, const SelectWs& w,
-                               int n_band, int nblk, uint8_t* mask, int32_t* idx_out,
-                               hipStream_t st);
+                               int n_band, uint8_t* mask, int32_t* idx_out, hipStream_t st);
 
 }  // namespace kd

@@ -5,17 +5,16 @@
 // The entropies from the projection sweep carry fp32 rounding (|error| <
 // eps). The k-th largest value H_k is found by a radix select; positions with
 // E > H_k + 2 eps are certainly kept, E < H_k - 2 eps certainly dropped, and
-// the band in between is recomputed in fp64 from hidden and W and ranked by
-// (entropy descending, position ascending). The kept set is then the one an
-// fp64 evaluation of the entropies decides.
+// the band in between is recomputed in fp64 from hidden and W (in pieces of
+// at most kRefinePiece rows, whatever its size) and ranked by (entropy
+// descending, position ascending). The kept set is then the one an fp64
+// evaluation of the entropies decides.
 #include <algorithm>
 
 #include "kd_common.hpp"
 #include "kd_kernels.hpp"
 
 namespace kd {
-
-constexpr int kBandCap = 4096;   // band rows refined in fp64; above this the fp32 values decide
 
 __device__ inline unsigned long long ord_key(double e) {
   unsigned long long b = (unsigned long long)__double_as_longlong(e);
@@ -326,63 +325,87 @@ hipError_t launch_refine(int f32, const char* X, int64_t ldx, const char* W, int
 }
 
 // ---------------------------------------------------------------------------
-// Final decision (single work-group): refined band entropies, rank within the
-// band by (entropy desc, position asc), mask and ascending index list.
-// n_band <= kBandCap uses the fp64 values; a larger band is ranked on the
-// fp32-path values.
+// Keep `need` of the n values vals[0..n), largest first, lower index first
+// among equal values, by setting mask[tgt[b]] = 1 for each kept b. One
+// work-group of 1024 threads: a radix select of the need-th largest value on
+// order-preserving 64-bit keys (8 passes of 8 bits), then the entries above
+// it and the first ties in index order. Every thread must call it.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void select_final_kernel(const double* E, int64_t S, int64_t k,
-                                                            SelectWs w, int n_band, int nblk,
-                                                            uint8_t* mask, int32_t* idx_out) {
-  __shared__ int32_t sc[1024];
+struct BandKeepSmem {
+  unsigned int hist[256];
+  unsigned long long prefix;
+  int64_t krem;
+  int32_t sc[1024];
+};
+
+__device__ void band_keep(BandKeepSmem& sm, const double* vals, int n, int64_t need,
+                          const int32_t* tgt, uint8_t* mask) {
   const int tid = threadIdx.x;
-  const double hk = w.dscal[0];
-  const int n_above = w.scal[1];
-  const double delta = w.dscal[1];
-  const bool refined = n_band <= kBandCap;
-  // 1. refined entropies of band rows
-  for (int b = tid; b < n_band; b += 1024) {
-    double val;
-    if (refined) {
-      double M = -INFINITY, Ssum = 0.0, U = 0.0;
-      for (int q = 0; q < nblk; ++q) {
-        const double* o = w.rpart + ((int64_t)b * nblk + q) * 3;
-        const double m2 = o[0], s2 = o[1], u2 = o[2];
-        if (m2 == -INFINITY) continue;
-        if (M == -INFINITY) {
-          M = m2; Ssum = s2; U = u2;
-          continue;
-        }
-        const double mn = fmax(M, m2), f1 = exp(M - mn), f2 = exp(m2 - mn);
-        U = (U + Ssum * (M - mn)) * f1 + (u2 + s2 * (m2 - mn)) * f2;
-        Ssum = Ssum * f1 + s2 * f2;
-        M = mn;
+  if (need > n) need = n;
+  if (need <= 0) return;
+  if (tid == 0) {
+    sm.prefix = 0ull;
+    sm.krem = need;
+  }
+  __syncthreads();
+  unsigned long long msk = 0ull;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    if (tid < 256) sm.hist[tid] = 0u;
+    __syncthreads();
+    const unsigned long long prefix = sm.prefix;
+    for (int b = tid; b < n; b += 1024) {
+      const unsigned long long key = ord_key(vals[b]);
+      if ((key & msk) == prefix) atomicAdd(&sm.hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int64_t krem = sm.krem, cum = 0;
+      int d = 255;
+      for (; d > 0; --d) {
+        if (cum + (int64_t)sm.hist[d] >= krem) break;
+        cum += sm.hist[d];
       }
-      val = log(Ssum) - U / Ssum;
-    } else {
-      val = E[w.band[b]];
+      sm.krem = krem - cum;
+      sm.prefix = prefix | ((unsigned long long)d << shift);
     }
-    w.refined[b] = val;
+    msk |= 255ull << shift;
+    __syncthreads();
   }
-  // 2. mask of certain keeps
-  for (int64_t t = tid; t < S; t += 1024) mask[t] = (E[t] > hk + delta) ? 1 : 0;
+  // kstar: the need-th largest key; ties_kept of the entries equal to it are kept
+  const unsigned long long kstar = sm.prefix;
+  const int64_t ties_kept = sm.krem;
+  const int seg = (n + 1023) / 1024;
+  const int b0 = tid * seg, b1 = (b0 + seg < n) ? b0 + seg : n;
+  int c = 0;
+  for (int b = b0; b < b1; ++b) c += (ord_key(vals[b]) == kstar) ? 1 : 0;
+  sm.sc[tid] = c;
   __syncthreads();
-  // 3. band rows ranked by (refined desc, position asc); keep the first k - n_above
-  const int64_t need = k - n_above;
-  for (int b = tid; b < n_band; b += 1024) {
-    const double vb = w.refined[b];
-    const int32_t tb = w.band[b];
-    int64_t rank = 0;
-    for (int q = 0; q < n_band; ++q) {
-      const double vq = w.refined[q];
-      rank += (vq > vb || (vq == vb && w.band[q] < tb)) ? 1 : 0;
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? sm.sc[tid - o] : 0;
+    __syncthreads();
+    sm.sc[tid] += v;
+    __syncthreads();
+  }
+  int64_t r = sm.sc[tid] - c;   // ties before this thread's entries
+  for (int b = b0; b < b1; ++b) {
+    const unsigned long long key = ord_key(vals[b]);
+    if (key > kstar) {
+      mask[tgt[b]] = 1;
+    } else if (key == kstar) {
+      if (r < ties_kept) mask[tgt[b]] = 1;
+      ++r;
     }
-    if (rank < need) mask[tb] = 1;
   }
   __syncthreads();
-  // 4. ascending index list of kept positions
-  const int64_t seg = ceil_div(S, 1024);
-  const int64_t t0 = tid * seg, t1 = (t0 + seg < S) ? t0 + seg : S;
+}
+
+// Ascending list of the positions t < n with mask[t] set, and its length in
+// *count (one work-group of 1024 threads; every thread must call it).
+__device__ void mask_list(int32_t* sc, const uint8_t* mask, int64_t n, int32_t* idx_out,
+                          int32_t* count) {
+  const int tid = threadIdx.x;
+  const int64_t seg = ceil_div(n, 1024);
+  const int64_t t0 = tid * seg, t1 = (t0 + seg < n) ? t0 + seg : n;
   int c = 0;
   for (int64_t t = t0; t < t1; ++t) c += mask[t];
   sc[tid] = c;
@@ -398,14 +421,33 @@ __global__ __launch_bounds__(1024) void select_final_kernel(const double* E, int
     for (int64_t t = t0; t < t1; ++t)
       if (mask[t]) idx_out[off++] = (int32_t)t;
   }
-  if (tid == 1023) w.scal[2] = sc[1023];
+  if (tid == 1023) count[0] = sc[1023];
+}
+
+// ---------------------------------------------------------------------------
+// Final decision (one work-group): positions above the band are kept; the
+// band rows, whose fp64 entropies are in w.refined (band order = ascending
+// position), are ranked by (entropy desc, position asc) and the first
+// k - n_above kept; then the mask and the ascending index list.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void select_final_kernel(const double* E, int64_t S, int64_t k,
+                                                            SelectWs w, int n_band, uint8_t* mask,
+                                                            int32_t* idx_out) {
+  __shared__ BandKeepSmem sm;
+  const int tid = threadIdx.x;
+  const double hk = w.dscal[0];
+  const int n_above = w.scal[1];
+  const double delta = w.dscal[1];
+  for (int64_t t = tid; t < S; t += 1024) mask[t] = (E[t] > hk + delta) ? 1 : 0;
+  __syncthreads();
+  band_keep(sm, w.refined, n_band, k - n_above, w.band, mask);
+  mask_list(sm.sc, mask, S, idx_out, w.scal + 2);
 }
 
 hipError_t launch_select_final(const double* entropy, int64_t S, int64_t k, const SelectWs& w,
-                               int n_band, int nblk, uint8_t* mask, int32_t* idx_out,
-                               hipStream_t st) {
+                               int n_band, uint8_t* mask, int32_t* idx_out, hipStream_t st) {
   hipLaunchKernelGGL(select_final_kernel, dim3(1), dim3(1024), 0, st, entropy, S, k, w, n_band,
-                     nblk, mask, idx_out);
+                     mask, idx_out);
   return hipGetLastError();
 }
 
@@ -462,37 +504,36 @@ __global__ __launch_bounds__(256) void sample_mean_kernel(const double* E, const
   }
 }
 
-// the positions of the band samples, in band order: pstart[i] is where band
-// sample i starts in plist; w.scal[3] = the total (written whatever its size;
-// the list is filled only up to cap)
-__global__ __launch_bounds__(1024) void sample_band_positions_kernel(const int64_t* off, SelectWs w,
-                                                                     int n_band, int32_t* pstart,
-                                                                     int32_t* plist, int cap) {
-  __shared__ int64_t sc[1024];
+// flag[t] = 1 for every position t of a band sample (one work-group per band
+// sample; samples may overlap)
+__global__ __launch_bounds__(256) void sample_mark_kernel(const int64_t* off, SelectWs w,
+                                                          int n_band, uint8_t* flag) {
+  for (int i = blockIdx.x; i < n_band; i += gridDim.x) {
+    const int64_t a0 = off[w.band[i]], a1 = off[w.band[i] + 1];
+    for (int64_t t = a0 + threadIdx.x; t < a1; t += 256) flag[t] = 1;
+  }
+}
+
+// w.refined[i]: fp64 mean over band sample i's positions of their refined
+// entropies pent[pos[t]] (threads' strided partial sums, then a fixed tree);
+// -inf for an empty sample
+__global__ __launch_bounds__(256) void sample_band_mean_kernel(const int64_t* off, SelectWs w,
+                                                               int n_band, const int32_t* pos,
+                                                               const double* pent) {
+  __shared__ double red[256];
   const int tid = threadIdx.x;
-  const int seg = (n_band + 1023) / 1024;
-  const int i0 = tid * seg, i1 = (i0 + seg < n_band) ? i0 + seg : n_band;
-  int64_t c = 0;
-  for (int i = i0; i < i1; ++i) c += off[w.band[i] + 1] - off[w.band[i]];
-  sc[tid] = c;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int64_t v = tid >= o ? sc[tid - o] : 0;
+  for (int i = blockIdx.x; i < n_band; i += gridDim.x) {
+    const int64_t a0 = off[w.band[i]], a1 = off[w.band[i] + 1];
+    double s = 0.0;
+    for (int64_t t = a0 + tid; t < a1; t += 256) s += pent[pos[t]];
+    red[tid] = s;
     __syncthreads();
-    sc[tid] += v;
+    for (int o = 128; o > 0; o >>= 1) {
+      if (tid < o) red[tid] += red[tid + o];
+      __syncthreads();
+    }
+    if (tid == 0) w.refined[i] = a1 > a0 ? red[0] / (double)(a1 - a0) : -INFINITY;
     __syncthreads();
-  }
-  int64_t p = sc[tid] - c;
-  for (int i = i0; i < i1; ++i) {
-    const int64_t a0 = off[w.band[i]], n = off[w.band[i] + 1] - a0;
-    pstart[i] = (int32_t)(p < cap ? p : cap);
-    for (int64_t j = 0; j < n; ++j)
-      if (p + j < cap) plist[p + j] = (int32_t)(a0 + j);
-    p += n;
-  }
-  if (tid == 1023) {
-    pstart[n_band] = (int32_t)(sc[1023] < cap ? sc[1023] : cap);
-    w.scal[3] = (int32_t)(sc[1023] < 0x7FFFFFFF ? sc[1023] : 0x7FFFFFFF);
   }
 }
 
@@ -521,64 +562,25 @@ __global__ __launch_bounds__(256) void sample_refined_entropy_kernel(SelectWs w,
   pent[b] = log(Ssum) - U / Ssum;
 }
 
-// Final decision (one work-group): the band's means (fp64 from the refined
-// entropies when `refined`), certain keeps, the band ranked by (mean desc,
-// sample asc), the mask and the ascending list of kept samples.
-__global__ __launch_bounds__(1024) void sample_final_kernel(const double* means, const int64_t* off,
-                                                            int64_t B, int64_t k, SelectWs w,
-                                                            int n_band, int refined,
-                                                            const int32_t* pstart,
-                                                            const double* pent, uint8_t* mask,
+// Final decision (one work-group): samples above the band are kept; the band
+// (ascending sample order) is ranked by (mean desc, sample asc) on its fp64
+// means in w.refined when `refined`, else on the sweep's means, and the first
+// k - n_above kept; then the mask and the ascending list of kept samples.
+__global__ __launch_bounds__(1024) void sample_final_kernel(const double* means, int64_t B,
+                                                            int64_t k, SelectWs w, int n_band,
+                                                            int refined, uint8_t* mask,
                                                             int32_t* idx_out) {
-  __shared__ int32_t sc[1024];
+  __shared__ BandKeepSmem sm;
   const int tid = threadIdx.x;
   const double hk = w.dscal[0];
   const int n_above = w.scal[1];
   const double delta = w.dscal[1];
-  for (int i = tid; i < n_band; i += 1024) {
-    double v = means[w.band[i]];
-    if (refined) {
-      const int a = pstart[i], e = pstart[i + 1];
-      if (e > a) {
-        double s = 0.0;
-        for (int j = a; j < e; ++j) s += pent[j];
-        v = s / (double)(e - a);
-      }
-    }
-    w.refined[i] = v;
-  }
+  if (!refined)
+    for (int i = tid; i < n_band; i += 1024) w.refined[i] = means[w.band[i]];
   for (int64_t b = tid; b < B; b += 1024) mask[b] = (means[b] > hk + delta) ? 1 : 0;
   __syncthreads();
-  const int64_t need = k - n_above;
-  for (int i = tid; i < n_band; i += 1024) {
-    const double vi = w.refined[i];
-    const int32_t bi = w.band[i];
-    int64_t rank = 0;
-    for (int q = 0; q < n_band; ++q) {
-      const double vq = w.refined[q];
-      rank += (vq > vi || (vq == vi && w.band[q] < bi)) ? 1 : 0;
-    }
-    if (rank < need) mask[bi] = 1;
-  }
-  __syncthreads();
-  const int64_t seg = ceil_div(B, 1024);
-  const int64_t t0 = tid * seg, t1 = (t0 + seg < B) ? t0 + seg : B;
-  int c = 0;
-  for (int64_t b = t0; b < t1; ++b) c += mask[b];
-  sc[tid] = c;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int v = tid >= o ? sc[tid - o] : 0;
-    __syncthreads();
-    sc[tid] += v;
-    __syncthreads();
-  }
-  if (idx_out) {
-    int p = sc[tid] - c;
-    for (int64_t b = t0; b < t1; ++b)
-      if (mask[b]) idx_out[p++] = (int32_t)b;
-  }
-  if (tid == 1023) w.scal[2] = sc[1023];
+  band_keep(sm, w.refined, n_band, k - n_above, w.band, mask);
+  mask_list(sm.sc, mask, B, idx_out, w.scal + 2);
 }
 
 hipError_t launch_sample_check(const int64_t* off, int64_t B, int64_t S, int32_t* flag,
@@ -598,10 +600,19 @@ hipError_t launch_sample_means(const double* E, const int64_t* off, int64_t B, d
   return hipGetLastError();
 }
 
-hipError_t launch_sample_band_positions(const int64_t* off, const SelectWs& w, int n_band,
-                                        int32_t* pstart, int32_t* plist, int cap, hipStream_t st) {
-  hipLaunchKernelGGL(sample_band_positions_kernel, dim3(1), dim3(1024), 0, st, off, w, n_band,
-                     pstart, plist, cap);
+hipError_t launch_sample_mark(const int64_t* off, const SelectWs& w, int n_band, uint8_t* flag,
+                              hipStream_t st) {
+  if (n_band <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sample_mark_kernel, dim3((unsigned)std::min(n_band, 8192)), dim3(256), 0, st,
+                     off, w, n_band, flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_band_means(const int64_t* off, const SelectWs& w, int n_band,
+                                    const int32_t* pos, const double* pent, hipStream_t st) {
+  if (n_band <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sample_band_mean_kernel, dim3((unsigned)std::min(n_band, 8192)), dim3(256), 0,
+                     st, off, w, n_band, pos, pent);
   return hipGetLastError();
 }
 
@@ -613,12 +624,11 @@ hipError_t launch_sample_refined_entropy(const SelectWs& w, int n, int nblk, dou
   return hipGetLastError();
 }
 
-hipError_t launch_sample_final(const double* means, const int64_t* off, int64_t B, int64_t k,
-                               const SelectWs& w, int n_band, int refined, const int32_t* pstart,
-                               const double* pent, uint8_t* mask, int32_t* idx_out,
+hipError_t launch_sample_final(const double* means, int64_t B, int64_t k, const SelectWs& w,
+                               int n_band, int refined, uint8_t* mask, int32_t* idx_out,
                                hipStream_t st) {
-  hipLaunchKernelGGL(sample_final_kernel, dim3(1), dim3(1024), 0, st, means, off, B, k, w, n_band,
-                     refined, pstart, pent, mask, idx_out);
+  hipLaunchKernelGGL(sample_final_kernel, dim3(1), dim3(1024), 0, st, means, B, k, w, n_band,
+                     refined, mask, idx_out);
   return hipGetLastError();
 }
 

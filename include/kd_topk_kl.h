@@ -97,6 +97,10 @@ typedef enum kd_teacher_kind { KD_TEACHER_LOGITS = 0, KD_TEACHER_PROBS = 1 } kd_
  *   K      teacher entries per position, 1 <= K <= min(V, 4096)
  *   chunk  rows per backward chunk: bounds the [chunk, V] bf16 gradient tile
  *          held in the workspace (the only workspace term that grows with V)
+ * Size limits (KD_ERR_SHAPE otherwise): S < 2^30, H <= 2^20, V <= 2^30, and
+ * 256 rows of the padded gradient-tile pitch (about V elements of hw_dtype)
+ * and of the transposed chunk pitch (about 8192 or chunk elements) each below
+ * 2^31 bytes: V up to about 4.19M for bf16 (2.09M for fp32). 
  *   temperature  T > 0, applied to teacher and student logits alike (to the
  *                student only when tl_kind is KD_TEACHER_PROBS)
  *   hw_dtype     storage type of hidden and W (both the same)
@@ -170,8 +174,13 @@ int kd_student_entropy(const kd_problem* problem, const void* hidden, const void
 
 /* Keep the floor(num*S/den) positions of highest entropy, lower index first
  * on ties (SE-KD top-k% selection, Method section 2). Entropies within a band
- * around the cut are recomputed in fp64 from hidden and W before the decision,
- * so the kept set is the one an fp64 evaluation gives.
+ * around the cut are recomputed in fp64 from hidden and W before the decision
+ * (the whole band, in pieces, whatever its size), so the kept set is the one
+ * an fp64 evaluation gives. The band is +-2e-5 nats around the k-th largest
+ * entropy: it assumes that kd_student_entropy's fp32-path values are within
+ * 2e-5 nats of the fp64 entropies, which holds for logits |z| of order 10 or
+ * less at H of a few thousand (the tests check it for unit-variance logits
+ * and for logits of standard deviation 4).
  *   entropy     [device] [S] float64 from kd_student_entropy (not modified)
  *   mask_out    [device] [S] uint8: 1 = kept
  *   idx_out     [device] [S] int32 or NULL: kept positions in ascending order
@@ -189,8 +198,8 @@ int kd_select_top_fraction(const kd_problem* problem, const void* hidden, const 
  * Sample b is positions [offsets[b], offsets[b+1]); an empty sample has mean
  * -inf. Samples whose mean lies within the entropy error bound of the cut have
  * their positions' entropies recomputed in fp64 from hidden and W before the
- * decision, so the kept set is the one fp64 entropies give (when those samples
- * hold more than 65536 positions, the sweep's entropies decide).
+ * decision (each such position once, in pieces, whatever their number), so
+ * the kept set is the one fp64 entropies give.
  *   entropy     [device] [S] float64 from kd_student_entropy (not modified)
  *   offsets     [device] [B+1] int64, non-decreasing within [0, S]
  *               (KD_ERR_ARG otherwise); B <= max(S, 1)
@@ -258,8 +267,8 @@ int kd_select_by_signal(const kd_problem* problem, const double* signal, const i
  * floor(num*len_b/den) positions of highest entropy, lower index first on ties.
  * As in kd_select_top_fraction, the entries within the entropy error bound of
  * a segment's cut are recomputed in fp64 from hidden and W before the
- * decision, so the kept set is the one fp64 entropies give (beyond 65536 such
- * entries in all, the remaining segments are decided on the sweep's values).
+ * decision (every such entry, in pieces, whatever their number), so the kept
+ * set is the one fp64 entropies give.
  *   entropy     [device] [S] float64 from kd_student_entropy (not modified)
  *   offsets     [device] [B+1] int64, non-decreasing within [0, S] (KD_ERR_ARG
  *               otherwise); positions outside every segment are not kept

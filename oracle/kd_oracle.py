@@ -310,24 +310,31 @@ def oracle_dW_rows(hidden, W, ids, tlogits, T, lse, valid, vocab_rows, grad_loss
     lse = _f64(lse)
     with np.errstate(invalid="ignore", over="ignore"):
         Q = np.exp(Zc / float(T) - np.where(valid, lse, 0.0)[:, None])
-    Pc = np.zeros_like(Q)
+    # teacher probability of each cached entry, Pk[t, k]
     if probs:
         pv = _f64(tlogits)
         use = np.isfinite(pv) & (pv > 0.0)
         mass = np.sum(np.where(use, pv, 0.0), axis=1)
         ok = _present_rows(pv, T, probs=True)
-        for k in range(ids.shape[1]):
-            pk = np.where(ok & use[:, k], pv[:, k] / np.where(mass > 0.0, mass, 1.0), 0.0)
-            hit = ids[:, k][:, None] == vocab_rows[None, :]
-            Pc += np.where(hit, pk[:, None], 0.0)
+        Pk = np.where(ok[:, None] & use, pv / np.where(mass > 0.0, mass, 1.0)[:, None], 0.0)
     else:
         scaled = _f64(tlogits) / float(T)
         lt = _logsumexp_rows(scaled)                             # teacher log-normaliser per row
-        for k in range(ids.shape[1]):
-            with np.errstate(invalid="ignore"):
-                pk = np.where(np.isfinite(lt), np.exp(scaled[:, k] - np.where(np.isfinite(lt), lt, 0.0)), 0.0)
-            hit = ids[:, k][:, None] == vocab_rows[None, :]
-            Pc += np.where(hit, pk[:, None], 0.0)
+        fin = np.isfinite(lt)
+        with np.errstate(invalid="ignore"):
+            Pk = np.where(fin[:, None], np.exp(scaled - np.where(fin, lt, 0.0)[:, None]), 0.0)
+    # Pc[t, j] = sum of Pk[t, k] over the entries whose id is vocab_rows[j]
+    # (entries sharing an id add, in the order of k)
+    if ids.size and (ids.min() < 0 or ids.max() >= W.shape[0]):
+        raise ValueError("teacher id out of range [0, V)")
+    uniq, inv = np.unique(vocab_rows, return_inverse=True)
+    col = np.full(int(W.shape[0]), -1, dtype=np.int64)
+    col[uniq] = np.arange(uniq.shape[0])
+    c = col[ids]
+    hit = c >= 0
+    Pu = np.zeros((ids.shape[0], uniq.shape[0]))
+    np.add.at(Pu, (np.nonzero(hit)[0], c[hit]), Pk[hit])
+    Pc = Pu[:, inv]
     coef = float(grad_loss) / (float(T) * N)
     G = np.where(valid[:, None], Q - Pc, 0.0) * coef
     return G.T @ Hd

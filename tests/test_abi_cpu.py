@@ -175,3 +175,22 @@ def test_teacher_sample_argument_errors():
     # the workspace holds per-chunk unit masses and draws, not [S, V]
     big = kd.kd_teacher_sample_workspace_bytes(prob(S=32768, H=2880, V=201088, K=100, chunk=1024))
     assert big < 64 << 20
+
+
+@pytest.mark.parametrize("kw", [dict(V=4_300_000, K=10), dict(V=2_200_000, K=10, hw=1),
+                                dict(chunk=5_000_000, S=10_000_000)])
+def test_operand_ranges_beyond_2gib_rejected(kw):
+    # a 256-row operand tile of the gradient tile / W^T (about V elements per
+    # row) or of the transposed chunk (about chunk elements per row) must fit
+    # one buffer range of less than 2^31 bytes
+    p = prob(**kw)
+    assert kd.kd_topk_kl_workspace_bytes(p) == 0
+    fake = ctypes.c_void_p(0x1000)
+    rc = kd.lib.kd_topk_kl_fwd(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, None,
+                               None, fake, 1 << 40, None)
+    assert rc == KD_ERR_SHAPE
+
+
+def test_largest_accepted_vocabulary():
+    assert kd.kd_topk_kl_workspace_bytes(prob(V=4_000_000, K=10)) > 0
+    assert kd.kd_topk_kl_workspace_bytes(prob(V=2_000_000, K=10, hw=1)) > 0

@@ -292,6 +292,24 @@ def test_entropy_matches_oracle(kd):
     assert err <= 2e-5
 
 
+def test_entropy_and_selection_with_large_logits(kd):
+    # logits of standard deviation 4 (hidden ~ N(0, 16), W ~ N(0, 1/H)) at a
+    # hidden size of 2048: the fp32-path entropies stay within the 2e-5 nats
+    # that the selection's band assumes, and the kept set is the fp64 one
+    S, H, V = 2000, 2048, 6007
+    p = make_problem(S, H, V, 4, seed=16, hidden_std=4.0)
+    hidden, W, _, _ = to_device(p)
+    ent = kd.kd_student_entropy(hidden, W)
+    mask, idx, cnt = kd.kd_select_top_fraction(ent, hidden, W, 20, 100)
+    ref = oracle_entropy(p.hidden, p.W, chunk=500)
+    err = float(np.max(np.abs(ent.cpu().numpy() - ref)))
+    print(f"entropy max abs err at logit std 4: {err:.3e}")
+    assert err <= 2e-5
+    rmask, ridx, rk = oracle_select_top_fraction(ref, 20, 100)
+    assert cnt == rk
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+
+
 @pytest.mark.parametrize("case", ["spread", "crowded", "ties"])
 def test_selection_index_set_bit_exact(kd, case):
     S, H, V = 3000, 128, 4001
@@ -320,6 +338,30 @@ def test_selection_ragged_hidden(kd, H, hw):
     ent = kd.kd_student_entropy(hidden, W)
     mask, idx, cnt = kd.kd_select_top_fraction(ent, hidden, W, 20, 100)
     ref_e = oracle_entropy(p.hidden, p.W, chunk=400)
+    rmask, ridx, rk = oracle_select_top_fraction(ref_e, 20, 100)
+    assert cnt == rk
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.array_equal(mask.cpu().numpy(), rmask)
+
+
+def test_selection_band_larger_than_a_refinement_piece(kd):
+    # entropies crowded well inside the fp32-path error bound: the whole band
+    # (about S positions, several pieces of 4096) is recomputed in fp64 and
+    # ranked there; the kept set equals the fp64 oracle's bit for bit
+    S, H, V = 20000, 128, 4001
+    p = make_problem(S, H, V, 4, seed=18, hidden_std=0.01)
+    hidden, W, _, _ = to_device(p)
+    ent = kd.kd_student_entropy(hidden, W)
+    kd.kd_profile_reset()
+    kd.kd_profile_enable(True)
+    mask, idx, cnt = kd.kd_select_top_fraction(ent, hidden, W, 20, 100)
+    torch.cuda.synchronize()
+    kd.kd_profile_enable(False)
+    steps = kd.kd_profile_read()
+    kd.kd_profile_reset()
+    # one launch per 256 band rows plus one per piece: more than one piece ran
+    assert steps["select_refine_fp64"][0] > 4096 // 256 + 1
+    ref_e = oracle_entropy(p.hidden, p.W, chunk=2000)
     rmask, ridx, rk = oracle_select_top_fraction(ref_e, 20, 100)
     assert cnt == rk
     assert np.array_equal(idx.cpu().numpy(), ridx)

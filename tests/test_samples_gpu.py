@@ -60,6 +60,25 @@ def test_samples_match_oracle(kd, case):
         assert "select_refine_fp64" in steps
 
 
+def test_band_of_many_samples_and_positions(kd):
+    # more than 4096 band samples holding more than 65536 positions, means
+    # crowded inside the fp32-path error: every position of the band samples is
+    # recomputed in fp64 (in pieces) and the band ranked on fp64 means
+    rng = np.random.default_rng(78)
+    lengths = rng.integers(1, 32, size=6000)
+    S = int(lengths.sum())
+    assert S > 65536
+    p = make_problem(S, 64, 2000, 4, seed=79, hidden_std=0.01)
+    hidden, W, _, _ = to_device(p)
+    kd.kd_profile_reset()
+    kd.kd_profile_enable(True)
+    run(kd, p.hidden, p.W, hidden, W, offsets_of(lengths), 20, 100)
+    kd.kd_profile_enable(False)
+    steps = kd.kd_profile_read()
+    kd.kd_profile_reset()
+    assert steps["select_refine_fp64"][0] > 65536 // 256
+
+
 def test_duplicate_samples_tie_to_lower_index(kd):
     rng = np.random.default_rng(74)
     lengths = np.array([20, 35, 20, 20, 35, 10])

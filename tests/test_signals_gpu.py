@@ -244,6 +244,32 @@ def test_per_sequence_entropy_selection(kd, case):
         assert "select_refine_fp64" in steps
 
 
+def test_per_sequence_selection_band_above_65536_positions(kd):
+    """Per-sequence SE-KD where the straddling bands of all segments hold more
+    than 65536 positions in all: every one is refined in fp64 (in pieces) and
+    the kept set equals the fp64 oracle's bit for bit."""
+    from oracle import oracle_entropy
+    S = 80000
+    off = (np.arange(41, dtype=np.int64) * S) // 40
+    p = make_problem(S, 64, 2000, 4, seed=452, hidden_std=0.01)
+    hidden, W, _, _ = to_device(p)
+    ent = kd.kd_student_entropy(hidden, W)
+    kd.kd_profile_reset()
+    kd.kd_profile_enable(True)
+    mask, idx, cnt = kd.kd_select_top_fraction_segments(ent, torch.from_numpy(off).cuda(), hidden, W,
+                                                        20, 100)
+    torch.cuda.synchronize()
+    kd.kd_profile_enable(False)
+    steps = kd.kd_profile_read()
+    kd.kd_profile_reset()
+    assert steps["select_refine_fp64"][0] > 65536 // 256
+    ref_e = oracle_entropy(p.hidden, p.W, chunk=4000)
+    rmask, ridx, rc, _ = oracle_select_by_signal(ref_e, off, 20, 100)
+    assert cnt == rc
+    assert np.array_equal(mask.cpu().numpy(), rmask)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+
+
 @pytest.mark.parametrize("K", [1, 100, 700])
 def test_validate_order(kd, K):
     """Cache top-K order checks (kd_validate_topk_order) against the oracle:
