@@ -1,18 +1,25 @@
 """GPU parity at the full sizes of the workload configurations, in the launch
 configuration the benchmark times (the configuration's chunk, bf16, default
-workspace), through the C ABI.
+workspace), through the C ABI, against the fp64 oracle.
 
-The fp64 oracle cannot compute every output at these sizes on the host, so
-each test states what it compares:
+What is compared with the oracle at each size:
   * 8K context: loss, lse and KL of every row (the oracle's forward over all
-    rows), dHidden at 256 sampled rows and dW at 256 sampled vocabulary rows
-    (from the oracle's own lse of every row).
-  * 32K context, large vocabulary, and 256K context: lse, KL and dHidden at
-    sampled rows; the loss equals the mean of the per-row KL; the rows of dW
-    sum to zero over the vocabulary (the gradient of each row's softmax sums
-    to zero, at any size).
-  * entropy-selective: the entropy of every position (oracle, fp64), the kept
-    index set bit for bit, and the selective KL at sampled kept rows.
+    rows, computed here), dHidden at 1024 sampled rows and dW at 512 sampled
+    vocabulary rows.
+  * 32K context (large vocabulary) and 256K context: the loss, and the lse
+    and KL of every row, against the oracle's values stored in tests/golden
+    (written by tests/golden/make_full_size.py, which calls only the oracle;
+    the test first checks that the seeded generator reproduced the inputs
+    those values were computed on); dHidden at 1024 sampled rows (the first
+    and last row of every chunk, the ragged end, random rows) and dW at 512
+    sampled vocabulary rows (teacher ids, the last vocabulary tile, random
+    rows; every row of dW sums over all dW groups of chunks), both from the
+    oracle computed here.
+  * entropy-selective: the entropy of every position against the stored
+    oracle values, the kept index set bit for bit, and the selective KL's
+    loss, the lse and KL of every kept row, dHidden at 1024 kept rows and dW
+    at 512 vocabulary rows against the oracle over the kept rows.
+The rows of dW also sum to zero over the vocabulary (an extra check).
 Tolerances are those of the other parity tests.
 """
 import math
@@ -25,9 +32,12 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 from kd_synth import make_problem  # noqa: E402
-from oracle import (oracle_dW_rows, oracle_entropy, oracle_rows,  # noqa: E402
-                    oracle_select_top_fraction)
+from oracle import (oracle_dW_rows, oracle_rows, oracle_select_top_fraction)  # noqa: E402
+from tests.golden.make_full_size import input_digest, load, load_problem  # noqa: E402
 from tests.kd_gpu_helpers import BF16_GRAD_FRAC, BF16_LOSS_RTOL, rel, to_device  # noqa: E402
+
+N_DH_ROWS = 1024
+N_DW_ROWS = 512
 
 
 @pytest.fixture(scope="module")
@@ -43,25 +53,67 @@ def gpu_fwd_bwd(kd, p, mask=None):
     g = torch.ones(1, dtype=torch.float32, device="cuda")
     dh, dW = kd.kd_topk_kl_bwd(hidden, W, ids, tl, out["lse"], g, p.T, p.chunk, mk)
     torch.cuda.synchronize()
-    return out, dh, dW
+    res = dict(loss=float(out["loss"][0]), lse=out["lse"].cpu().numpy(),
+               kl=out["kl_rows"].cpu().numpy(), dh=dh.cpu().numpy(), dW=dW)
+    del hidden, W, ids, tl, out, dh
+    return res
 
 
-def check_rows(p, out, dh, rows, N):
-    """lse, KL and dHidden of sampled rows against the oracle's definition."""
-    ref = oracle_rows(p.hidden[rows], p.W, p.ids[rows], p.tlogits[rows], p.T, N)
-    lse = out["lse"].cpu().numpy()[rows]
-    kl = out["kl_rows"].cpu().numpy()[rows]
-    assert np.max(np.abs(lse - ref["lse"])) <= 1e-4 * max(1.0, float(np.max(np.abs(ref["lse"]))))
-    assert np.max(np.abs(kl - ref["kl_rows"])) <= 1e-3 * max(1.0, float(np.max(ref["kl_rows"])))
-    got_dh = dh.cpu().numpy()[rows]
-    err = float(np.max(np.abs(got_dh - ref["dH"])))
-    assert err <= BF16_GRAD_FRAC * float(np.max(np.abs(ref["dH"])))
-    return ref
+def stored(name):
+    """The oracle's stored per-row values for a workload, after checking that
+    the generator reproduced the inputs they were computed on."""
+    meta, ref = load(name)
+    p = load_problem(name)
+    assert input_digest(p) == meta["inputs_sha256"], \
+        "the seeded inputs differ from those of the stored oracle values"
+    return p, meta, ref
 
 
-def check_loss_is_mean_kl(out, N):
-    kl = out["kl_rows"].cpu().numpy().astype(np.float64)
-    assert rel(float(out["loss"][0]), math.fsum(kl) / N) <= 1e-5
+def check_row_values(lse, kl, ref_lse, ref_kl):
+    assert np.max(np.abs(lse - ref_lse)) <= 1e-4 * max(1.0, float(np.max(np.abs(ref_lse))))
+    assert np.max(np.abs(kl - ref_kl)) <= 1e-3 * max(1.0, float(np.max(ref_kl)))
+
+
+def sampled_rows(rows_in_loss, chunk, n, rng):
+    """n of the loss's rows (given in compacted order): the first and last of
+    every chunk, the last row, and random rows."""
+    N = len(rows_in_loss)
+    pick = set()
+    for c0 in range(0, N, chunk):
+        pick.add(c0)
+        pick.add(min(N, c0 + chunk) - 1)
+    rest = np.setdiff1d(np.arange(N), np.fromiter(pick, dtype=np.int64))
+    extra = rng.choice(rest, max(0, n - len(pick)), replace=False)
+    sel = np.sort(np.concatenate([np.fromiter(pick, dtype=np.int64), extra]))
+    return rows_in_loss[sel]
+
+
+def sampled_vocab(p, rows, n, rng):
+    """n vocabulary rows: teacher ids of a few loss rows, the last vocabulary
+    tile (256 rows) and the very last row, row 0, random rows."""
+    v = {0, p.V - 1}
+    v.update(int(x) for x in p.ids[rows[0], :16])
+    v.update(int(x) for x in p.ids[rows[-1], :16])
+    v.update(range(max(0, p.V - 256), p.V, 17))
+    rest = np.setdiff1d(np.arange(p.V), np.fromiter(v, dtype=np.int64))
+    extra = rng.choice(rest, max(0, n - len(v)), replace=False)
+    return np.sort(np.concatenate([np.fromiter(v, dtype=np.int64), extra]))
+
+
+def check_dh_rows(p, W64, dh, rows, N):
+    ref = np.empty((len(rows), p.H))
+    for b0 in range(0, len(rows), 256):
+        r = rows[b0:b0 + 256]
+        ref[b0:b0 + 256] = oracle_rows(p.hidden[r], W64, p.ids[r], p.tlogits[r], p.T, N)["dH"]
+    err = float(np.max(np.abs(dh[rows] - ref)))
+    assert err <= BF16_GRAD_FRAC * float(np.max(np.abs(ref))), err
+
+
+def check_dw_rows(p, W64, dW, lse, valid, vrows):
+    ref = oracle_dW_rows(p.hidden, W64, p.ids, p.tlogits, p.T, lse, valid, vrows)
+    got = dW[torch.from_numpy(vrows).cuda()].cpu().numpy()
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= BF16_GRAD_FRAC * float(np.max(np.abs(ref))), err
 
 
 def check_dW_rows_sum_to_zero(dW):
@@ -74,76 +126,70 @@ def check_dW_rows_sum_to_zero(dW):
 def test_full_8k_context(kd):
     # S=8192 H=3072 V=128256 K=100 T=1 chunk=1024
     p = make_problem(8192, 3072, 128256, 100, T=1.0, chunk=1024, seed=1002)
-    out, dh, dW = gpu_fwd_bwd(kd, p)
+    r = gpu_fwd_bwd(kd, p)
     S = p.S
+    W64 = p.W.astype(np.float64)
     # oracle forward over every row, in row blocks
     kl = np.empty(S)
     lse = np.empty(S)
     for r0 in range(0, S, 512):
-        rr = oracle_rows(p.hidden[r0:r0 + 512], p.W, p.ids[r0:r0 + 512], p.tlogits[r0:r0 + 512],
+        rr = oracle_rows(p.hidden[r0:r0 + 512], W64, p.ids[r0:r0 + 512], p.tlogits[r0:r0 + 512],
                          p.T, S, grads=False)
         kl[r0:r0 + 512] = rr["kl_rows"]
         lse[r0:r0 + 512] = rr["lse"]
-    loss = math.fsum(kl) / S
-    assert rel(float(out["loss"][0]), loss) <= BF16_LOSS_RTOL
-    got_lse = out["lse"].cpu().numpy()
-    assert np.max(np.abs(got_lse - lse)) <= 1e-4 * max(1.0, float(np.max(np.abs(lse))))
-    got_kl = out["kl_rows"].cpu().numpy()
-    assert np.max(np.abs(got_kl - kl)) <= 1e-3 * max(1.0, float(np.max(kl)))
+    assert rel(r["loss"], math.fsum(kl) / S) <= BF16_LOSS_RTOL
+    check_row_values(r["lse"], r["kl"], lse, kl)
     rng = np.random.default_rng(81)
-    rows = np.sort(rng.choice(S, 256, replace=False))
-    check_rows(p, out, dh, rows, S)
-    vrows = np.sort(rng.choice(p.V, 256, replace=False))
-    vrows[0] = int(p.ids[0, 0])                          # at least one teacher id
-    vrows = np.unique(vrows)
-    ref_dw = oracle_dW_rows(p.hidden, p.W, p.ids, p.tlogits, p.T, lse, np.ones(S, bool), vrows)
-    got_dw = dW.cpu().numpy()[vrows]
-    err = float(np.max(np.abs(got_dw - ref_dw)))
-    assert err <= BF16_GRAD_FRAC * float(np.max(np.abs(ref_dw)))
+    rows = sampled_rows(np.arange(S), p.chunk, N_DH_ROWS, rng)
+    check_dh_rows(p, W64, r["dh"], rows, S)
+    check_dw_rows(p, W64, r["dW"], lse, np.ones(S, bool), sampled_vocab(p, rows, N_DW_ROWS, rng))
+    check_dW_rows_sum_to_zero(r["dW"])
 
 
 @pytest.mark.parametrize("cfg", ["32k_context", "256k_context"])
-def test_full_size_sampled_rows(kd, cfg):
-    if cfg == "32k_context":
-        p = make_problem(32768, 2880, 201088, 100, T=1.0, chunk=2048, seed=1003)
-        nrows = 128
-    else:
-        p = make_problem(262144, 3072, 128256, 100, T=2.0, chunk=2048, seed=1004)
-        nrows = 64
-    out, dh, dW = gpu_fwd_bwd(kd, p)
+def test_full_size_against_oracle(kd, cfg):
+    p, meta, ref = stored(cfg)
+    r = gpu_fwd_bwd(kd, p)
     S = p.S
+    assert rel(r["loss"], meta["loss"]) <= BF16_LOSS_RTOL
+    check_row_values(r["lse"], r["kl"], ref["lse"], ref["kl"])
+    W64 = p.W.astype(np.float64)
     rng = np.random.default_rng(82)
-    rows = np.sort(rng.choice(S, nrows, replace=False))
-    rows[-1] = S - 1                                     # the ragged end of the last chunk
-    rows = np.unique(rows)
-    check_rows(p, out, dh, rows, S)
-    check_loss_is_mean_kl(out, S)
-    check_dW_rows_sum_to_zero(dW)
+    rows = sampled_rows(np.arange(S), p.chunk, N_DH_ROWS, rng)
+    check_dh_rows(p, W64, r["dh"], rows, S)
+    check_dw_rows(p, W64, r["dW"], ref["lse"], np.ones(S, bool),
+                  sampled_vocab(p, rows, N_DW_ROWS, rng))
+    check_dW_rows_sum_to_zero(r["dW"])
 
 
 def test_full_entropy_selective(kd):
     # S=32768 H=2048 V=151936 K=100, top 20% by entropy, chunk 1024, T=1
-    S, H, V, K = 32768, 2048, 151936, 100
-    p = make_problem(S, H, V, K, T=1.0, chunk=1024, seed=1005)
+    p, meta, ref = stored("entropy_selective")
+    S = p.S
     hidden, W, ids, tl = to_device(p)
     ent = kd.kd_student_entropy(hidden, W)
     mask, idx, cnt = kd.kd_select_top_fraction(ent, hidden, W, 20, 100)
     torch.cuda.synchronize()
-    ref_e = oracle_entropy(p.hidden, p.W, chunk=512)
     got_e = ent.cpu().numpy()
-    assert np.max(np.abs(got_e - ref_e)) <= 2e-5
-    rmask, ridx, rk = oracle_select_top_fraction(ref_e, 20, 100)
+    assert np.max(np.abs(got_e - ref["entropy"])) <= 2e-5
+    rmask, ridx, rk = oracle_select_top_fraction(ref["entropy"], 20, 100)
+    assert np.array_equal(ridx, ref["idx"])
     assert cnt == rk == (20 * S) // 100
     assert np.array_equal(idx.cpu().numpy(), ridx)
+    del hidden, W, ids, tl, ent, idx
     m = mask.cpu().numpy().astype(bool)
-    out, dh, dW = gpu_fwd_bwd(kd, p, mask=m)
-    rng = np.random.default_rng(83)
-    rows = np.sort(rng.choice(ridx, 128, replace=False))
-    check_rows(p, out, dh, rows, int(rk))
+    r = gpu_fwd_bwd(kd, p, mask=m)
+    assert rel(r["loss"], meta["loss"]) <= BF16_LOSS_RTOL
+    check_row_values(r["lse"][ridx], r["kl"][ridx], ref["lse"], ref["kl"])
     # unselected rows take no part: zero dHidden, zero lse
-    off = np.flatnonzero(~m)[:512]
-    assert np.all(dh.cpu().numpy()[off] == 0.0)
-    assert np.all(out["lse"].cpu().numpy()[off] == 0.0)
-    kl = out["kl_rows"].cpu().numpy().astype(np.float64)
-    assert rel(float(out["loss"][0]), math.fsum(kl[m]) / int(rk)) <= 1e-5
-    check_dW_rows_sum_to_zero(dW)
+    off = np.flatnonzero(~m)
+    assert np.all(r["dh"][off] == 0.0)
+    assert np.all(r["lse"][off] == 0.0)
+    W64 = p.W.astype(np.float64)
+    rng = np.random.default_rng(83)
+    rows = sampled_rows(ridx, p.chunk, N_DH_ROWS, rng)
+    check_dh_rows(p, W64, r["dh"], rows, int(rk))
+    lse_all = np.zeros(S)
+    lse_all[ridx] = ref["lse"]
+    check_dw_rows(p, W64, r["dW"], lse_all, m, sampled_vocab(p, rows, N_DW_ROWS, rng))
+    check_dW_rows_sum_to_zero(r["dW"])
