@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "KD_BF16", "KD_F32", "KD_TEACHER_LOGITS", "KD_TEACHER_PROBS", "KdError", "kd_problem", "lib",
     "kd_abi_version", "kd_status_str", "kd_topk_kl_workspace_bytes",
-    "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_student_entropy",
+    "kd_topk_kl_fwd", "kd_topk_kl_fwd_noalloc", "kd_topk_kl_bwd", "kd_student_entropy",
     "kd_select_top_fraction", "kd_select_samples", "kd_validate_topk",
     "kd_position_signals", "kd_select_by_signal", "kd_select_above",
     "kd_select_top_fraction_segments", "kd_validate_topk_order",
@@ -60,6 +60,9 @@ lib.kd_topk_kl_workspace_bytes.restype = ctypes.c_size_t
 lib.kd_topk_kl_workspace_bytes.argtypes = [_PP]
 lib.kd_topk_kl_fwd.restype = ctypes.c_int
 lib.kd_topk_kl_fwd.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+lib.kd_topk_kl_fwd_noalloc.restype = ctypes.c_int
+lib.kd_topk_kl_fwd_noalloc.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+KD_NOALLOC_SCRATCH_BYTES = 64 << 20
 lib.kd_topk_kl_bwd.restype = ctypes.c_int
 lib.kd_topk_kl_bwd.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P,
                                ctypes.c_size_t, _P]
@@ -197,6 +200,25 @@ def kd_topk_kl_fwd(hidden, W, topk_ids, topk_logits, T=1.0, chunk=1024, mask=Non
     _check(lib.kd_topk_kl_fwd(ctypes.byref(p), _ptr(hidden), _ptr(W), _ptr(topk_ids),
                               _ptr(topk_logits), _ptr(mask), _ptr(loss), _ptr(lse), _ptr(kl),
                               _ptr(zt), _ptr(ws), ws.numel(), _stream(dev)), "kd_topk_kl_fwd")
+    return dict(loss=loss, lse=lse, kl_rows=kl, z_topk=zt)
+
+
+def kd_topk_kl_fwd_noalloc(hidden, W, topk_ids, topk_logits, T=1.0, chunk=1024, mask=None,
+                           want_kl_rows=False, want_z_topk=False, teacher_probs=False):
+    """kd_topk_kl_fwd through the entry point that allocates nothing on the
+    device: the library's fixed per-GPU scratch stands in for the workspace.
+    The outputs are allocated here, by the caller. Calls that overlap in time
+    on one GPU race."""
+    p = _problem_of(hidden, W, topk_ids, topk_logits, T, chunk, teacher_probs)
+    mask = _mask_arg(mask, p.S)
+    dev = hidden.device
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(p.S, dtype=torch.float32, device=dev)
+    kl = torch.empty(p.S, dtype=torch.float32, device=dev) if want_kl_rows else None
+    zt = torch.empty(p.S, p.K, dtype=torch.float32, device=dev) if want_z_topk else None
+    _check(lib.kd_topk_kl_fwd_noalloc(ctypes.byref(p), _ptr(hidden), _ptr(W), _ptr(topk_ids),
+                                      _ptr(topk_logits), _ptr(mask), _ptr(loss), _ptr(lse),
+                                      _ptr(kl), _ptr(zt), _stream(dev)), "kd_topk_kl_fwd_noalloc")
     return dict(loss=loss, lse=lse, kl_rows=kl, z_topk=zt)
 
 

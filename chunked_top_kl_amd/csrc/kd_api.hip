@@ -42,6 +42,7 @@ struct ProfRec {
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+thread_local bool t_prof_off = false;   // set while a call that must not create events runs
 std::vector<ProfRec> g_prof_recs;
 std::vector<hipEvent_t> g_event_pool;
 
@@ -62,7 +63,7 @@ struct Prof {
   hipEvent_t a = nullptr, b = nullptr;
   Prof(const char* n, hipStream_t s) : st(s), name(n) {
     std::lock_guard<std::mutex> g(g_prof_mu);
-    if (!g_prof_on) return;
+    if (!g_prof_on || t_prof_off) return;
     a = pool_event();
     b = pool_event();
     if (a && b) hipEventRecord(a, st);
@@ -97,6 +98,7 @@ int check_device() {
 struct Layout {
   size_t count, present, pos, idx, ids_s, p_s, korig_s, negH;
   size_t pm, ps, zs, bsum;
+  size_t fwd_total;   // the forward uses only the buffers laid out before this offset
   size_t G, GT, WT, XcT, Xc, dhp;
   size_t em, es, eu;
   size_t band, refined, scal, dscal, rpart, xb, counters;
@@ -162,6 +164,7 @@ Layout plan(const kd_problem* p) {
   L.ps = take(pe * 4);
   L.zs = take(Sx * K * 4);
   L.bsum = take((ceil_div(Sx, 256) + 1) * 8);
+  L.fwd_total = off;
   L.G = take(L.C * L.Vld * L.esz);
   L.GT = take(L.Vp * L.Cld * L.esz);
   L.WT = take(H * L.Vld * L.esz);
@@ -277,8 +280,8 @@ size_t kd_topk_kl_workspace_bytes(const kd_problem* p) {
 
 namespace {
 
-// The forward's launches, with its buffers at the plan's offsets in ws.
-// Arguments are checked by the caller.
+// The forward's launches, with its buffers at the plan's offsets in ws (only
+// those before L.fwd_total are touched). Arguments are checked by the caller.
 int fwd_run(const kd_problem* p, const Layout& L, const void* hidden, const void* W,
             const int32_t* ids, const void* tl, const uint8_t* mask, float* loss, float* lse,
             float* kl_rows, float* z_topk, void* ws, hipStream_t st) {
@@ -352,6 +355,38 @@ int fwd_check(const kd_problem* p, const void* hidden, const void* W, const int3
 
 }  // namespace
 
+// Scratch of kd_topk_kl_fwd_noalloc: a fixed device array, one copy on each
+// GPU the library runs on, held until the process ends. In host code its name
+// stands for no device address: kernels and copies get the address that
+// hipGetSymbolAddress returns for the current device, taken once per device.
+static __device__ __attribute__((aligned(256))) char scratch[KD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];
+
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KD_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return KD_ERR_HIP;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return KD_ERR_HIP;
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return KD_OK;
+}
+
+struct NoProfile {
+  NoProfile() { t_prof_off = true; }
+  ~NoProfile() { t_prof_off = false; }
+};
+
+}  // namespace
+
 extern "C" {
 
 int kd_topk_kl_fwd(const kd_problem* p, const void* hidden, const void* W, const int32_t* ids,
@@ -362,6 +397,21 @@ int kd_topk_kl_fwd(const kd_problem* p, const void* hidden, const void* W, const
   const Layout L = plan(p);
   if ((rc = check_ws(L, ws, ws_bytes))) return rc;
   if ((rc = check_device())) return rc;
+  return fwd_run(p, L, hidden, W, ids, tl, mask, loss, lse, kl_rows, z_topk, ws,
+                 (hipStream_t)stream);
+}
+
+int kd_topk_kl_fwd_noalloc(const kd_problem* p, const void* hidden, const void* W,
+                           const int32_t* ids, const void* tl, const uint8_t* mask, float* loss,
+                           float* lse, float* kl_rows, float* z_topk, void* stream) {
+  int rc = fwd_check(p, hidden, W, ids, tl, loss, lse);
+  if (rc) return rc;
+  const Layout L = plan(p);
+  if (L.fwd_total > (size_t)KD_NOALLOC_SCRATCH_BYTES) return KD_ERR_WORKSPACE;
+  if ((rc = check_device())) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_of_current_device(&ws))) return rc;
+  NoProfile np;
   return fwd_run(p, L, hidden, W, ids, tl, mask, loss, lse, kl_rows, z_topk, ws,
                  (hipStream_t)stream);
 }

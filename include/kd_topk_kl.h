@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define KD_ABI_VERSION 4
+#define KD_ABI_VERSION 5
 
 typedef enum kd_status {
   KD_OK = 0,
@@ -144,6 +144,25 @@ int kd_topk_kl_fwd(const kd_problem* problem, const void* hidden, const void* W,
                    const int32_t* topk_ids, const void* topk_logits, const uint8_t* mask,
                    float* loss, float* lse, float* kl_rows, float* z_topk,
                    void* ws, size_t ws_bytes, void* stream);
+
+/* The forward pass for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation, outputs and argument rules as
+ * kd_topk_kl_fwd, without the workspace argument. Its scratch is a fixed
+ * device array of KD_NOALLOC_SCRATCH_BYTES inside the library, one copy per
+ * GPU, held until the process ends. A problem whose forward scratch is larger
+ * returns KD_ERR_WORKSPACE before any launch: the scratch is about
+ * S*(16*K + 13) bytes plus 8 bytes per row and vocabulary range of the sweep,
+ * so S up to about 40000 at K = 100. It calls no hipMalloc or hipFree and
+ * records no profiling events. Every call on one GPU uses that GPU's array:
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * and give wrong results, so such callers must serialise them. Nothing in the
+ * array needs clearing between calls: every value a call reads, it wrote.   */
+#define KD_NOALLOC_SCRATCH_BYTES 67108864
+int kd_topk_kl_fwd_noalloc(const kd_problem* problem, const void* hidden, const void* W,
+                           const int32_t* topk_ids, const void* topk_logits,
+                           const uint8_t* mask, float* loss, float* lse, float* kl_rows,
+                           float* z_topk, void* stream);
 
 /* Backward pass: rows are projected again chunk by chunk ("backward
  * recomputes the chunk"); the logit gradient
