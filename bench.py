@@ -18,6 +18,7 @@ fp64 CPU oracle timed on a bounded sample of rows.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -146,7 +147,7 @@ def kernel_table(prof, wl, C, N_rows, steps):
     return kernels
 
 
-def time_workload(kd, torch, key, p=None, steps=3, warmup=1):
+def time_workload(kd, torch, key, p=None, steps=3, warmup=1, comparators=False):
     """fwd+bwd of another configuration at its full size (the entropy-selective
     one with its entropy sweep and selection): ms per step, tokens/s, the MFMA
     fraction of the counted work, peak device memory and the per-step kernels."""
@@ -192,7 +193,63 @@ def time_workload(kd, torch, key, p=None, steps=3, warmup=1):
                kernels=kernel_table(prof, wl, C, N_rows, steps))
     log(f"[bench] {key}: {ms:.2f} ms/step, {out['tokens_per_s']:.0f} tokens/s, "
         f"MFMA {100 * out['mfma_frac']:.1f}%, peak {out['peak_gib']} GiB")
-    del ws, t, res
+    del ws, res
+    if comparators:
+        out["comparators"] = comparator_leg(kd, torch, wl, t)
+    del t
+    torch.cuda.empty_cache()
+    return out
+
+
+def comparator_leg(kd, torch, wl, t, steps=3, warmup=1):
+    """The dense and forward-chunked loss forms ("what chunked KL loss does")
+    at the workload's shapes: fwd+bwd ms per step, tokens/s and peak device
+    memory (inputs, outputs, the workspace with its stored grids), beside the
+    fused form's numbers from the main timing. Same counted FLOP: the
+    comparators project once (no recompute), so their MFMA work is
+    6*S*H*V, while 8*S*H*V is what the fused form runs."""
+    S, H, V, K, C = wl["S"], wl["H"], wl["V"], wl["K"], wl["chunk"]
+    hidden, W, ids, tl = t
+    in_bytes = sum(x.numel() * x.element_size() for x in t)
+    out = {}
+    for name, form in (("forward_chunked", kd.KD_FORM_FORWARD_CHUNKED), ("dense", kd.KD_FORM_DENSE)):
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        prob = kd.make_problem(S, H, V, K, C, wl["T"], kd.KD_BF16, kd.KD_BF16)
+        need = kd.lib.kd_kl_comparator_workspace_bytes(ctypes.byref(prob), form)
+        free, _ = torch.cuda.mem_get_info()
+        if need + (4 << 30) > free:
+            out[name] = dict(skipped=f"workspace {need / 2**30:.1f} GiB does not fit")
+            continue
+        base = torch.cuda.memory_allocated() - in_bytes
+        torch.cuda.reset_peak_memory_stats()
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        g = torch.ones(1, dtype=torch.float32, device="cuda")
+
+        def step():
+            o = kd.kd_kl_comparator_fwd(hidden, W, ids, tl, form, wl["T"], C, workspace=ws)
+            dh, dW = kd.kd_kl_comparator_bwd(hidden, W, ids, tl, o["lse"], g, form, ws, wl["T"], C)
+            return o, dh, dW
+
+        for _ in range(warmup):
+            res = step()
+            del res
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        res = None
+        for _ in range(steps):
+            res = None
+            res = step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1000.0 / steps
+        peak = (torch.cuda.max_memory_allocated() - base) / 2**30
+        out[name] = dict(ms_per_step=round(ms, 3), tokens_per_s=round(S / (ms / 1000.0), 1),
+                         peak_gib=round(peak, 3), workspace_gib=round(need / 2**30, 3),
+                         loss=float(res[0]["loss"][0]),
+                         mfma_frac_of_its_6SHV=round(6.0 * S * H * V / (ms / 1000.0)
+                                                     / (PEAK_BF16_TFLOPS * 1e12), 4))
+        log(f"[bench] {name} form: {ms:.2f} ms/step, peak {peak:.2f} GiB")
+        del ws, res
     torch.cuda.empty_cache()
     return out
 
@@ -420,6 +477,8 @@ def main():
     ap.add_argument("--teacher-only", action="store_true",
                     help="time only the teacher top-K cache writer (steps / warmup calls) and "
                          "print its line")
+    ap.add_argument("--no-comparators", action="store_true",
+                    help="skip the dense and forward-chunked loss forms (8K and 32K contexts)")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the timed fwd+bwd of the other configurations (8K, 256K, "
                          "entropy-selective) at full size")
@@ -549,6 +608,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_chunk_sweep and args.workload == "c3":
         result["chunk_sweep"] = chunk_sweep(kd, torch, wl, t, [512, 1024, 2048])
+    if not args.no_comparators and args.workload in ("c2", "c3"):
+        result["comparators"] = comparator_leg(kd, torch, wl, t)
     if not args.no_teacher and args.workload == "c3":
         result["teacher_topk"] = teacher_leg(kd, torch, wl, t, p, cpu=not args.no_cpu_baseline)
     if not args.no_selection:
@@ -560,7 +621,8 @@ def main():
         result["workloads"] = {}
         for key in ("c2", "c5"):
             if key != args.workload:
-                result["workloads"][key] = time_workload(kd, torch, key)
+                result["workloads"][key] = time_workload(
+                    kd, torch, key, comparators=(key == "c2" and not args.no_comparators))
     p4 = None
     if not args.no_mem_sweep or (not args.no_workloads and args.workload != "c4"):
         c4 = WORKLOADS["c4"]

@@ -17,6 +17,8 @@ __all__ = [
     "KD_BF16", "KD_F32", "KD_TEACHER_LOGITS", "KD_TEACHER_PROBS", "KdError", "kd_problem", "lib",
     "kd_abi_version", "kd_status_str", "kd_topk_kl_workspace_bytes",
     "kd_topk_kl_fwd", "kd_topk_kl_fwd_noalloc", "kd_topk_kl_bwd", "kd_student_entropy",
+    "KD_FORM_FUSED", "KD_FORM_DENSE", "KD_FORM_FORWARD_CHUNKED", "kd_kl_comparator_fwd",
+    "kd_kl_comparator_bwd",
     "kd_select_top_fraction", "kd_select_samples", "kd_validate_topk",
     "kd_position_signals", "kd_select_by_signal", "kd_select_above",
     "kd_select_top_fraction_segments", "kd_validate_topk_order",
@@ -63,6 +65,15 @@ lib.kd_topk_kl_fwd.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctyp
 lib.kd_topk_kl_fwd_noalloc.restype = ctypes.c_int
 lib.kd_topk_kl_fwd_noalloc.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 KD_NOALLOC_SCRATCH_BYTES = 64 << 20
+KD_FORM_FUSED, KD_FORM_DENSE, KD_FORM_FORWARD_CHUNKED = 0, 1, 2
+lib.kd_kl_comparator_workspace_bytes.restype = ctypes.c_size_t
+lib.kd_kl_comparator_workspace_bytes.argtypes = [_PP, ctypes.c_int]
+lib.kd_kl_comparator_fwd.restype = ctypes.c_int
+lib.kd_kl_comparator_fwd.argtypes = [_PP, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     ctypes.c_size_t, _P]
+lib.kd_kl_comparator_bwd.restype = ctypes.c_int
+lib.kd_kl_comparator_bwd.argtypes = [_PP, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     ctypes.c_int, _P, ctypes.c_size_t, _P]
 lib.kd_topk_kl_bwd.restype = ctypes.c_int
 lib.kd_topk_kl_bwd.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P,
                                ctypes.c_size_t, _P]
@@ -242,6 +253,56 @@ def kd_topk_kl_bwd(hidden, W, topk_ids, topk_logits, lse, grad_loss, T=1.0, chun
                               _ptr(topk_logits), _ptr(mask), _ptr(lse), _ptr(grad_loss),
                               _ptr(dh), _ptr(dW), 1 if accumulate_dW else 0, _ptr(ws),
                               ws.numel(), _stream(dev)), "kd_topk_kl_bwd")
+    return dh, dW
+
+
+def kd_kl_comparator_fwd(hidden, W, topk_ids, topk_logits, form, T=1.0, chunk=1024, mask=None,
+                         want_kl_rows=False, workspace=None, teacher_probs=False):
+    """Forward of a comparator loss form (KD_FORM_DENSE or KD_FORM_FORWARD_CHUNKED).
+    Returns dict(loss, lse, kl_rows, workspace): pass the same workspace to
+    kd_kl_comparator_bwd, which reads the grids the forward stored there."""
+    p = _problem_of(hidden, W, topk_ids, topk_logits, T, chunk, teacher_probs)
+    mask = _mask_arg(mask, p.S)
+    dev = hidden.device
+    need = lib.kd_kl_comparator_workspace_bytes(ctypes.byref(p), int(form))
+    if need == 0:
+        raise KdError(10, "kd_kl_comparator_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace.numel() < need:
+        raise ValueError(f"workspace too small: {workspace.numel()} < {need} bytes")
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(p.S, dtype=torch.float32, device=dev)
+    kl = torch.empty(p.S, dtype=torch.float32, device=dev) if want_kl_rows else None
+    _check(lib.kd_kl_comparator_fwd(ctypes.byref(p), int(form), _ptr(hidden), _ptr(W),
+                                    _ptr(topk_ids), _ptr(topk_logits), _ptr(mask), _ptr(loss),
+                                    _ptr(lse), _ptr(kl), _ptr(workspace), workspace.numel(),
+                                    _stream(dev)), "kd_kl_comparator_fwd")
+    return dict(loss=loss, lse=lse, kl_rows=kl, workspace=workspace)
+
+
+def kd_kl_comparator_bwd(hidden, W, topk_ids, topk_logits, lse, grad_loss, form, workspace,
+                         T=1.0, chunk=1024, mask=None, dW=None, accumulate_dW=False,
+                         teacher_probs=False):
+    """Backward of a comparator loss form, from the grids its forward left in
+    `workspace`. Returns (dhidden [S,H] f32, dW [V,H] f32)."""
+    p = _problem_of(hidden, W, topk_ids, topk_logits, T, chunk, teacher_probs)
+    mask = _mask_arg(mask, p.S)
+    dev = hidden.device
+    if grad_loss.dtype != torch.float32 or grad_loss.numel() != 1:
+        raise ValueError("grad_loss must be a float32 tensor of one element")
+    grad_loss = grad_loss.contiguous()
+    dh = torch.empty(p.S, p.H, dtype=torch.float32, device=dev)
+    if dW is None:
+        dW = torch.empty(p.V, p.H, dtype=torch.float32, device=dev)
+        accumulate_dW = False
+    elif dW.dtype != torch.float32 or tuple(dW.shape) != (p.V, p.H) or not dW.is_contiguous():
+        raise ValueError("dW must be a contiguous float32 [V,H] tensor")
+    _check(lib.kd_kl_comparator_bwd(ctypes.byref(p), int(form), _ptr(hidden), _ptr(W),
+                                    _ptr(topk_ids), _ptr(topk_logits), _ptr(mask), _ptr(lse),
+                                    _ptr(grad_loss), _ptr(dh), _ptr(dW),
+                                    1 if accumulate_dW else 0, _ptr(workspace), workspace.numel(),
+                                    _stream(dev)), "kd_kl_comparator_bwd")
     return dh, dW
 
 

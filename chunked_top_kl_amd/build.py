@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkdtopk.so")
 
 SOURCES = ["kd_api.hip", "kd_sweep.hip", "kd_gemm.hip", "kd_prepass.hip", "kd_select.hip",
-           "kd_teacher.hip", "kd_signals.hip", "kd_sample.hip"]
+           "kd_teacher.hip", "kd_signals.hip", "kd_sample.hip", "kd_compare.hip"]
 
 ARCH = "gfx950"
 HIP_FLAGS = [

@@ -416,19 +416,35 @@ int kd_topk_kl_fwd_noalloc(const kd_problem* p, const void* hidden, const void* 
                  (hipStream_t)stream);
 }
 
-int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const int32_t* ids,
-                   const void* tl, const uint8_t* mask, const float* lse, const float* grad_loss,
-                   float* dhidden, float* dW, int accumulate_dW, void* ws, size_t ws_bytes,
-                   void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Where the backward's logit gradient of a chunk comes from: the fused path
+// projects the chunk again (gradient tile sweep and teacher scatter); the
+// comparator forms read it from the grids their forward stored.
+struct CmpGrids {
+  int form;                  // KD_FORM_FUSED, KD_FORM_DENSE or KD_FORM_FORWARD_CHUNKED
+  const uint16_t* Z; int64_t ldz;
+  float* P; float* logQ; int64_t ldd;
+};
+
+int bwd_check(const kd_problem* p, const void* hidden, const void* W, const int32_t* ids,
+              const void* tl, const float* lse, const float* grad_loss, const float* dhidden,
+              const float* dW, int accumulate_dW) {
   int rc = check_problem(p);
   if (rc) return rc;
   if (!W || !dW || !grad_loss || (p->S > 0 && (!hidden || !ids || !tl || !lse || !dhidden)))
     return KD_ERR_NULL;
   if (accumulate_dW != 0 && accumulate_dW != 1) return KD_ERR_ARG;
-  const Layout L = plan(p);
-  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
-  if ((rc = check_device())) return rc;
-  hipStream_t st = (hipStream_t)stream;
+  return KD_OK;
+}
+
+int bwd_run(const kd_problem* p, const Layout& L, const CmpGrids& cg, const void* hidden,
+            const void* W, const int32_t* ids, const void* tl, const uint8_t* mask,
+            const float* lse, const float* grad_loss, float* dhidden, float* dW,
+            int accumulate_dW, void* ws, hipStream_t st) {
+  int rc;
   if ((rc = teacher_tables(p, L, ids, tl, mask, nullptr, ws, st))) return rc;
   const int S = (int)p->S, V = (int)p->V, H = (int)p->H, K = (int)p->K;
   const int f32 = p->hw_dtype == KD_F32;
@@ -457,7 +473,38 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
                                       at<char>(ws, L.XcT) + slot * L.slot * L.esz, L.Cld * L.esz,
                                       (int)L.slot, at<char>(ws, L.Xc), st));
     }
-    if (S > 0) {
+    if (S > 0 && cg.form != KD_FORM_FUSED) {
+      // the chunk's logit gradient from the stored grids, then its transpose
+      kd::CmpRowArgs ra;
+      std::memset(&ra, 0, sizeof(ra));
+      ra.Z = cg.Z;
+      ra.ldz = cg.ldz;
+      ra.idx = at<int32_t>(ws, L.idx);
+      ra.nrows_dev = at<int32_t>(ws, L.count);
+      ra.row_begin = row_begin;
+      ra.row_cap = C;
+      ra.V = V;
+      ra.Vp = Vp;
+      ra.K = K;
+      ra.T = p->temperature;
+      ra.ids_s = at<int32_t>(ws, L.ids_s);
+      ra.p_s = at<float>(ws, L.p_s);
+      ra.lse = const_cast<float*>(lse);
+      ra.P = cg.P;
+      ra.logQ = cg.logQ;
+      ra.ldd = cg.ldd;
+      ra.grad_loss = grad_loss;
+      ra.G = at<uint16_t>(ws, L.G);
+      ra.ldg = L.Vld;
+      {
+        Prof pr("cmp_grad", st);
+        KD_HIP(kd::launch_cmp_rows(cg.form == KD_FORM_DENSE ? kd::kCmpGradDense
+                                                            : kd::kCmpGradSparse, ra, st));
+      }
+      Prof pr("cmp_transpose", st);
+      KD_HIP(kd::launch_cmp_transpose(ra.G, L.Vld, ra.nrows_dev, row_begin, C, Vp,
+                                      at<uint16_t>(ws, L.GT) + slot * L.slot, L.Cld, st));
+    } else if (S > 0) {
       kd::SweepArgs a;
       std::memset(&a, 0, sizeof(a));
       a.W = (const char*)W;
@@ -558,6 +605,185 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
     }
   }
   return KD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const int32_t* ids,
+                   const void* tl, const uint8_t* mask, const float* lse, const float* grad_loss,
+                   float* dhidden, float* dW, int accumulate_dW, void* ws, size_t ws_bytes,
+                   void* stream) {
+  int rc = bwd_check(p, hidden, W, ids, tl, lse, grad_loss, dhidden, dW, accumulate_dW);
+  if (rc) return rc;
+  const Layout L = plan(p);
+  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+  if ((rc = check_device())) return rc;
+  CmpGrids cg;
+  std::memset(&cg, 0, sizeof(cg));
+  cg.form = KD_FORM_FUSED;
+  return bwd_run(p, L, cg, hidden, W, ids, tl, mask, lse, grad_loss, dhidden, dW, accumulate_dW,
+                 ws, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of the comparator forms: the fused layout (teacher tables, the
+// chunk's gradient tile and its transpose, W^T, dHidden partials), then the
+// stored grids: the bf16 logits of every row (both forms) and, for the dense
+// form, the fp32 teacher grid P and log-probabilities logQ of every row.
+struct CmpLayout {
+  size_t Z, kl, P, logQ, total;
+  int64_t ldz, ldd;   // row pitches in elements
+};
+
+CmpLayout plan_cmp(const kd_problem* p, int form, const Layout& L) {
+  CmpLayout c;
+  std::memset(&c, 0, sizeof(c));
+  const int64_t Sx = p->S > 0 ? p->S : 1;
+  size_t off = L.total;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (size_t)round_up((int64_t)bytes, 256);
+    return o;
+  };
+  c.ldz = L.Vld;
+  c.Z = take((size_t)Sx * c.ldz * 2);
+  c.kl = take((size_t)Sx * 4);
+  if (form == KD_FORM_DENSE) {
+    c.ldd = L.Vld;
+    c.P = take((size_t)Sx * c.ldd * 4);
+    c.logQ = take((size_t)Sx * c.ldd * 4);
+  }
+  c.total = off;
+  return c;
+}
+
+int cmp_check(const kd_problem* p, int form) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (form != KD_FORM_DENSE && form != KD_FORM_FORWARD_CHUNKED) return KD_ERR_ARG;
+  if (p->hw_dtype != KD_BF16) return KD_ERR_DTYPE;
+  return KD_OK;
+}
+
+CmpGrids cmp_grids(const kd_problem* p, int form, const CmpLayout& c, void* ws) {
+  (void)p;
+  CmpGrids g;
+  std::memset(&g, 0, sizeof(g));
+  g.form = form;
+  g.Z = at<uint16_t>(ws, c.Z);
+  g.ldz = c.ldz;
+  if (form == KD_FORM_DENSE) {
+    g.P = at<float>(ws, c.P);
+    g.logQ = at<float>(ws, c.logQ);
+    g.ldd = c.ldd;
+  }
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kd_kl_comparator_workspace_bytes(const kd_problem* p, int form) {
+  if (cmp_check(p, form) != KD_OK) return 0;
+  const Layout L = plan(p);
+  return plan_cmp(p, form, L).total;
+}
+
+int kd_kl_comparator_fwd(const kd_problem* p, int form, const void* hidden, const void* W,
+                         const int32_t* ids, const void* tl, const uint8_t* mask, float* loss,
+                         float* lse, float* kl_rows, void* ws, size_t ws_bytes, void* stream) {
+  int rc = cmp_check(p, form);
+  if (rc) return rc;
+  if ((rc = fwd_check(p, hidden, W, ids, tl, loss, lse))) return rc;
+  const Layout L = plan(p);
+  const CmpLayout CL = plan_cmp(p, form, L);
+  if (!ws || ((uintptr_t)ws & 255u) != 0 || ws_bytes < CL.total) return KD_ERR_WORKSPACE;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = teacher_tables(p, L, ids, tl, mask, nullptr, ws, st))) return rc;
+  const CmpGrids g = cmp_grids(p, form, CL, ws);
+  const int S = (int)p->S, V = (int)p->V, H = (int)p->H;
+  float* kl = at<float>(ws, CL.kl);
+  // the dense form projects every row in one pass, the forward-chunked form
+  // a chunk of rows at a time; both keep the logits of every row
+  const int RL = form == KD_FORM_DENSE ? std::max(S, 1) : (int)L.C;
+  for (int c0 = 0; c0 < S; c0 += RL) {
+    const int rcap = std::min(RL, S - c0);
+    kd::SweepArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.W = (const char*)W;
+    a.ldw = (int64_t)H * 2;
+    a.X = (const char*)hidden;
+    a.ldx = (int64_t)H * 2;
+    a.idx = at<int32_t>(ws, L.idx);
+    a.nrows_dev = at<int32_t>(ws, L.count);
+    a.row_begin = c0;
+    a.row_cap = rcap;
+    a.V = V;
+    a.H = H;
+    a.K = (int)p->K;
+    a.ncu = kCostCUs;
+    a.T = p->temperature;
+    a.G = (char*)(g.Z + (int64_t)c0 * g.ldz);
+    a.ldg = g.ldz * 2;
+    {
+      Prof pr("cmp_logits", st);
+      KD_HIP(kd::launch_sweep(kd::kSweepLogits, 0, 1, a, kd::sweep_grid(rcap, V, kCostCUs), st));
+    }
+    kd::CmpRowArgs ra;
+    std::memset(&ra, 0, sizeof(ra));
+    ra.Z = g.Z;
+    ra.ldz = g.ldz;
+    ra.idx = a.idx;
+    ra.nrows_dev = a.nrows_dev;
+    ra.row_begin = c0;
+    ra.row_cap = rcap;
+    ra.V = V;
+    ra.Vp = (int)L.Vp;
+    ra.K = (int)p->K;
+    ra.T = p->temperature;
+    ra.ids_s = at<int32_t>(ws, L.ids_s);
+    ra.p_s = at<float>(ws, L.p_s);
+    ra.negH = at<float>(ws, L.negH);
+    ra.lse = lse;
+    ra.kl = kl;
+    ra.P = g.P;
+    ra.logQ = g.logQ;
+    ra.ldd = g.ldd;
+    Prof pr("cmp_rows", st);
+    if (form == KD_FORM_DENSE) {
+      KD_HIP(kd::launch_cmp_rows(kd::kCmpDenseGrid, ra, st));
+      KD_HIP(kd::launch_cmp_rows(kd::kCmpKlDense, ra, st));
+    } else {
+      KD_HIP(kd::launch_cmp_rows(kd::kCmpKlSparse, ra, st));
+    }
+  }
+  Prof pr("cmp_loss", st);
+  KD_HIP(kd::launch_cmp_loss(at<int32_t>(ws, L.pos), p->S, lse, kl, kl_rows,
+                             at<double>(ws, L.bsum), at<int32_t>(ws, L.count), loss, st));
+  return KD_OK;
+}
+
+int kd_kl_comparator_bwd(const kd_problem* p, int form, const void* hidden, const void* W,
+                         const int32_t* ids, const void* tl, const uint8_t* mask,
+                         const float* lse, const float* grad_loss, float* dhidden, float* dW,
+                         int accumulate_dW, void* ws, size_t ws_bytes, void* stream) {
+  int rc = cmp_check(p, form);
+  if (rc) return rc;
+  if ((rc = bwd_check(p, hidden, W, ids, tl, lse, grad_loss, dhidden, dW, accumulate_dW)))
+    return rc;
+  const Layout L = plan(p);
+  const CmpLayout CL = plan_cmp(p, form, L);
+  if (!ws || ((uintptr_t)ws & 255u) != 0 || ws_bytes < CL.total) return KD_ERR_WORKSPACE;
+  if ((rc = check_device())) return rc;
+  return bwd_run(p, L, cmp_grids(p, form, CL, ws), hidden, W, ids, tl, mask, lse, grad_loss,
+                 dhidden, dW, accumulate_dW, ws, (hipStream_t)stream);
 }
 
 int kd_student_entropy(const kd_problem* p, const void* hidden, const void* W, double* entropy,

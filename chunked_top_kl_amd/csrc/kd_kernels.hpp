@@ -7,7 +7,7 @@
 namespace kd {
 
 enum SweepKind { kSweepFwd = 0, kSweepBwdG = 1, kSweepEnt = 2, kSweepPilot = 3, kSweepEmit = 4,
-                 kSweepSMass = 5, kSweepSDraw = 6 };
+                 kSweepSMass = 5, kSweepSDraw = 6, kSweepLogits = 7 };
 
 // Vocabulary-sweep projection (forward LSE + gather, backward gradient tile,
 // entropy). Rows are "launch rows" r in [0, rows): compacted row
@@ -29,7 +29,8 @@ struct SweepArgs {
   float* zs;                          // [S,K], indexed like ids_s
   // backward
   const float* lse; const float* grad_loss;
-  char* G; int64_t ldg;               // gradient tile [row_cap, Vp], bytes per row
+  char* G; int64_t ldg;               // gradient tile [row_cap, Vp], bytes per row (the
+                                      // logits kind stores z there, bf16)
   char* GT; int64_t ldgt;             // the same tile transposed [Vp, Cp]
   // entropy partials
   float* em; double* es; double* eu;
@@ -150,6 +151,24 @@ struct GradTeacherArgs {
   float T;
 };
 
+// Comparator loss forms (dense, forward-chunked): per-row passes over the
+// stored bf16 logits Z (compacted row cr at Z + cr * ldz) and, for the dense
+// form, the fp32 grids P and logQ (row cr at + cr * ldd). Teacher tables, lse
+// and kl are indexed by original row; G by launch row r (row_begin + r).
+struct CmpRowArgs {
+  const uint16_t* Z; int64_t ldz;
+  const int32_t* idx; const int32_t* nrows_dev;
+  int row_begin, row_cap, V, Vp, K;
+  float T;
+  const int32_t* ids_s; const float* p_s; const float* negH;
+  float* lse; float* kl;
+  float* P; float* logQ; int64_t ldd;
+  const float* grad_loss;
+  uint16_t* G; int64_t ldg;
+};
+enum CmpRowKind { kCmpKlSparse = 0, kCmpDenseGrid = 1, kCmpKlDense = 2, kCmpGradSparse = 3,
+                  kCmpGradDense = 4 };
+
 // ------------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error.
 hipError_t launch_prepass(const int32_t* ids, const void* tl, int tl_f32, int probs, int64_t S,
@@ -181,6 +200,15 @@ hipError_t launch_draw_assign(const double* cum, const float* tscale, const floa
                               int32_t* dunit, double* dres, int32_t* sids, hipStream_t st);
 int sweep_grid(int64_t rows_max, int V, int ncu);
 hipError_t launch_fwd_combine(const CombineArgs& a, hipStream_t st);
+hipError_t launch_loss_final(const double* block_sums, int nblk, const int32_t* nrows_dev,
+                             float* loss, hipStream_t st);
+hipError_t launch_cmp_rows(int what, const CmpRowArgs& a, hipStream_t st);
+hipError_t launch_cmp_transpose(const uint16_t* G, int64_t ldg, const int32_t* nrows_dev,
+                                int row_begin, int row_cap, int Vp, uint16_t* GT, int64_t ldgt,
+                                hipStream_t st);
+hipError_t launch_cmp_loss(const int32_t* pos, int64_t S, float* lse, float* kl, float* kl_out,
+                           double* block_sums, const int32_t* nrows_dev, float* loss,
+                           hipStream_t st);
 hipError_t launch_ent_combine(const EntCombineArgs& a, hipStream_t st);
 hipError_t launch_gather_rows_t(int f32, const char* X, int64_t ldx, const int32_t* idx,
                                 const int32_t* nrows_dev, int row_begin, int row_cap, int H,

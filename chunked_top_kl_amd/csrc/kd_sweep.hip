@@ -12,6 +12,9 @@
 //    rows, and an emit pass that appends every logit at or above a per-row
 //    threshold to the row's candidate list, in one sub-list per writer
 //    (kd_teacher.hip gathers them and picks the K);
+//  - logits (the dense and forward-chunked comparator forms of "what
+//    chunked KL loss does", which keep the student logits): z itself stored
+//    as a bf16 tile [rows][Vp] through the gradient tile's staged store;
 //  - sampled targets (RS-KD: ids drawn from the teacher's softmax at T by
 //    inverse transform in vocabulary order): a mass pass that stores the
 //    probability mass of every 128-entry vocabulary unit of each row (in the
@@ -259,6 +262,9 @@ __device__ __forceinline__ int staged_token(int tp, int jp) {
   return (tp >> 6) * 128 + 64 * jp + (tp & 63);
 }
 
+// LOGITS: the same store of z itself (no exponential, no scale) into the G
+// rows only; nothing of G^T is staged or stored.
+template <bool LOGITS>
 __device__ __forceinline__ void grad_tile_staged(floatx16 (&acc)[4][4], const SweepArgs& a, int vt,
                                                  int jt, int rows, int tl0, float c, float coef,
                                                  const float (&lse2)[4], char* lds) {
@@ -287,10 +293,12 @@ __device__ __forceinline__ void grad_tile_staged(floatx16 (&acc)[4][4], const Sw
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) z[i * 16 + r] = acc[i][j][r];
+        if constexpr (!LOGITS) {
 #pragma unroll
-        for (int e = 0; e < 64; ++e) z[e] = fast_exp2(fmaf(z[e], c, -lse2[j]));
+          for (int e = 0; e < 64; ++e) z[e] = fast_exp2(fmaf(z[e], c, -lse2[j]));
+        }
         // token columns past `rows` hold a repeated row: exact zeros
-        const float cf = (tl0 + 32 * j < rows) ? coef : 0.0f;
+        const float cf = LOGITS ? 1.0f : ((tl0 + 32 * j < rows) ? coef : 0.0f);
         const int tp = wn * 64 + jj * 32 + (lane & 31);
         // staging bases of this lane's first row (wm*128 + 4*half); row
         // dv further on is at + dv*256 (G^T part) and + dv*2 (G part). The
@@ -312,10 +320,12 @@ __device__ __forceinline__ void grad_tile_staged(floatx16 (&acc)[4][4], const Sw
                                 (__bf16)(z[i * 16 + 4 * q + 3] * cf)};
             const uint32_t u01 = __builtin_bit_cast(uint32_t, p01);
             const uint32_t u23 = __builtin_bit_cast(uint32_t, p23);
-            *(uint16_t*)(gtb + (dv + 0) * 256) = (uint16_t)u01;
-            *(uint16_t*)(gtb + (dv + 1) * 256) = (uint16_t)(u01 >> 16);
-            *(uint16_t*)(gtb + (dv + 2) * 256) = (uint16_t)u23;
-            *(uint16_t*)(gtb + (dv + 3) * 256) = (uint16_t)(u23 >> 16);
+            if constexpr (!LOGITS) {
+              *(uint16_t*)(gtb + (dv + 0) * 256) = (uint16_t)u01;
+              *(uint16_t*)(gtb + (dv + 1) * 256) = (uint16_t)(u01 >> 16);
+              *(uint16_t*)(gtb + (dv + 2) * 256) = (uint16_t)u23;
+              *(uint16_t*)(gtb + (dv + 3) * 256) = (uint16_t)(u23 >> 16);
+            }
             *(uint2*)(gb + dv * 2) = make_uint2(u01, u23);
           }
       }
@@ -324,7 +334,7 @@ __device__ __forceinline__ void grad_tile_staged(floatx16 (&acc)[4][4], const Sw
     __syncthreads();
     // G^T rows: 256 rows x 16 granules of 8 tokens
 #pragma unroll 4
-    for (int it = 0; it < 16; ++it) {
+    for (int it = 0; it < (LOGITS ? 0 : 16); ++it) {
       const int g = it * 256 + tid;
       const int vl = g >> 4, gr = g & 15;
       const int v = vt * kTile + vl;
@@ -464,7 +474,12 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
 
     const int vw0 = vt * kTile + wm * 128;
     if constexpr (KIND == kSweepBwdG && sizeof(T) == 2) {
-      grad_tile_staged(acc, a, vt, jt, rows, tl0, c, coef, lse2, lds);
+      grad_tile_staged<false>(acc, a, vt, jt, rows, tl0, c, coef, lse2, lds);
+      continue;
+    }
+    if constexpr (KIND == kSweepLogits) {
+      static_assert(sizeof(T) == 2, "the logits tile is stored as bf16");
+      grad_tile_staged<true>(acc, a, vt, jt, rows, tl0, c, coef, lse2, lds);
       continue;
     }
     if (vw0 >= a.V) continue;  // wave-uniform: this half tile is past the vocabulary
@@ -758,7 +773,8 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
       if (t < rows) a.scnt[(int64_t)t * a.scnt_ld + b * 4 + wm * 2 + half] = ecnt[j];
     }
   }
-  if constexpr (KIND == kSweepBwdG || KIND == kSweepPilot || KIND == kSweepEmit ||
+  if constexpr (KIND == kSweepBwdG || KIND == kSweepLogits || KIND == kSweepPilot ||
+                KIND == kSweepEmit ||
                 KIND == kSweepSMass || KIND == kSweepSDraw)
     return;
 
@@ -854,6 +870,8 @@ KD_SWEEP_KERNEL(kd_sample_mass_bf16, __bf16, kSweepSMass, false)
 KD_SWEEP_KERNEL(kd_sample_draw_bf16, __bf16, kSweepSDraw, false)
 KD_SWEEP_KERNEL(kd_sample_mass_f32, float, kSweepSMass, false)
 KD_SWEEP_KERNEL(kd_sample_draw_f32, float, kSweepSDraw, false)
+KD_SWEEP_KERNEL(kd_cmp_logits_bf16, __bf16, kSweepLogits, false)
+KD_SWEEP_KERNEL(kd_cmp_logits_rows_bf16, __bf16, kSweepLogits, true)
 #undef KD_SWEEP_KERNEL
 
 hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid, hipStream_t st) {
@@ -868,6 +886,8 @@ hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid
     else if (kind == kSweepEmit) KD_SWEEP(kd_teacher_emit_bf16);
     else if (kind == kSweepSMass) KD_SWEEP(kd_sample_mass_bf16);
     else if (kind == kSweepSDraw) KD_SWEEP(kd_sample_draw_bf16);
+    else if (kind == kSweepLogits && map) KD_SWEEP(kd_cmp_logits_rows_bf16);
+    else if (kind == kSweepLogits) KD_SWEEP(kd_cmp_logits_bf16);
     else KD_SWEEP(kd_entropy_sweep_bf16);
   } else {
     if (kind == kSweepFwd && map) KD_SWEEP(kd_fwd_lse_gather_rows_f32);
@@ -877,6 +897,7 @@ hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid
     else if (kind == kSweepEmit) KD_SWEEP(kd_teacher_emit_f32);
     else if (kind == kSweepSMass) KD_SWEEP(kd_sample_mass_f32);
     else if (kind == kSweepSDraw) KD_SWEEP(kd_sample_draw_f32);
+    else if (kind == kSweepLogits) return hipErrorInvalidValue;   // bf16 only
     else KD_SWEEP(kd_entropy_sweep_f32);
   }
 #undef KD_SWEEP
@@ -1003,6 +1024,13 @@ __global__ __launch_bounds__(256) void loss_final_kernel(const double* block_sum
     const int n = *nrows_dev;
     loss[0] = n > 0 ? (float)(red[0] / (double)n) : 0.0f;
   }
+}
+
+hipError_t launch_loss_final(const double* block_sums, int nblk, const int32_t* nrows_dev,
+                             float* loss, hipStream_t st) {
+  hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(256), 0, st, block_sums, nblk, nrows_dev,
+                     loss);
+  return hipGetLastError();
 }
 
 hipError_t launch_fwd_combine(const CombineArgs& a, hipStream_t st) {

@@ -84,6 +84,12 @@ STEP_PATTERNS = [
     ("validate_order", "validate_order"),
     ("validate_kernel", "validate"),
     ("zero_u64_kernel", "validate"),
+    ("kd_cmp_logits", "cmp_logits"),
+    ("cmp_kl_", "cmp_rows"),
+    ("cmp_dense_grid", "cmp_rows"),
+    ("cmp_loss_blocks", "cmp_loss"),
+    ("cmp_grad_kernel", "cmp_grad"),
+    ("cmp_transpose", "cmp_transpose"),
     ("copyBuffer", "device_copy"),
 ]
 

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define KD_ABI_VERSION 5
+#define KD_ABI_VERSION 6
 
 typedef enum kd_status {
   KD_OK = 0,
@@ -181,6 +181,52 @@ int kd_topk_kl_bwd(const kd_problem* problem, const void* hidden, const void* W,
                    const float* lse, const float* grad_loss,
                    float* dhidden, float* dW, int accumulate_dW,
                    void* ws, size_t ws_bytes, void* stream);
+
+/* Comparator forms of the loss ("what chunked KL loss does" sets the fused
+ * chunked loss beside two others, and the "operations" section says the
+ * fused one is slower than the forward-chunked one at short context, since
+ * its backward projects again). Same loss, same gradients, different memory:
+ *   KD_FORM_DENSE            the cached top-K expanded into a dense teacher
+ *                            probability grid P [S,V] (fp32), the student's
+ *                            log-probabilities logQ [S,V] (fp32) from the
+ *                            logits Z [S,V] (bf16) of one projection over all
+ *                            rows; KL per row from the grids; the backward
+ *                            takes the logit gradient from P and logQ.
+ *   KD_FORM_FORWARD_CHUNKED  the teacher stays sparse and rows are projected
+ *                            chunk by chunk, but the logits Z [S,V] (bf16) of
+ *                            every row are kept; the backward takes the logit
+ *                            gradient from Z instead of projecting again.
+ * KD_FORM_FUSED names kd_topk_kl_fwd / kd_topk_kl_bwd, which keep no grid.  */
+typedef enum kd_loss_form {
+  KD_FORM_FUSED = 0,
+  KD_FORM_DENSE = 1,
+  KD_FORM_FORWARD_CHUNKED = 2
+} kd_loss_form;
+
+/* Workspace bytes of a comparator form (0 for an invalid problem or form).
+ * It holds the stored grids: about S*Vp*2 bytes (forward-chunked) or
+ * S*Vp*10 bytes (dense), Vp = V rounded up to 8, on top of
+ * kd_topk_kl_workspace_bytes. */
+size_t kd_kl_comparator_workspace_bytes(const kd_problem* problem, int form);
+
+/* Forward of a comparator form: the same arguments and outputs as
+ * kd_topk_kl_fwd (z_topk is not offered), with form = KD_FORM_DENSE or
+ * KD_FORM_FORWARD_CHUNKED (KD_ERR_ARG otherwise). hw_dtype must be KD_BF16
+ * (KD_ERR_DTYPE otherwise). The grids it stores stay in ws for
+ * kd_kl_comparator_bwd. Does not synchronise the host.                      */
+int kd_kl_comparator_fwd(const kd_problem* problem, int form, const void* hidden, const void* W,
+                         const int32_t* topk_ids, const void* topk_logits, const uint8_t* mask,
+                         float* loss, float* lse, float* kl_rows, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Backward of a comparator form: the same arguments and outputs as
+ * kd_topk_kl_bwd. It reads the grids that kd_kl_comparator_fwd of the same
+ * form left in ws: call it with the same problem, inputs, mask and ws, with no
+ * other call on that ws in between.                                         */
+int kd_kl_comparator_bwd(const kd_problem* problem, int form, const void* hidden, const void* W,
+                         const int32_t* topk_ids, const void* topk_logits, const uint8_t* mask,
+                         const float* lse, const float* grad_loss, float* dhidden, float* dW,
+                         int accumulate_dW, void* ws, size_t ws_bytes, void* stream);
 
 /* Per-position student entropy H(q_t) = -sum_v q_tv ln q_tv in nats, with
  * q_t = softmax(z_t) over the full vocabulary at temperature 1 ("Rethinking
