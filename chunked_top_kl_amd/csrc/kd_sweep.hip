@@ -262,12 +262,15 @@ __device__ __forceinline__ int staged_token(int tp, int jp) {
   return (tp >> 6) * 128 + 64 * jp + (tp & 63);
 }
 
+// The scale coef is folded into the exponent, coef * 2^x = 2^(x + log2|coef|),
+// and its sign applied to the bf16 bits (lc2 = log2|coef|, -inf for 0;
+// sgn = the sign bit of coef in both halves of a bf16 pair).
 // LOGITS: the same store of z itself (no exponential, no scale) into the G
 // rows only; nothing of G^T is staged or stored.
 template <bool LOGITS>
 __device__ __forceinline__ void grad_tile_staged(floatx16 (&acc)[4][4], const SweepArgs& a, int vt,
-                                                 int jt, int rows, int tl0, float c, float coef,
-                                                 const float (&lse2)[4], char* lds) {
+                                                 int jt, int rows, int tl0, float c, float lc2,
+                                                 uint32_t sgn, const float (&lse2)[4], char* lds) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int half = lane >> 5;
   const int vw0 = vt * kTile + wm * 128;
@@ -294,11 +297,11 @@ __device__ __forceinline__ void grad_tile_staged(floatx16 (&acc)[4][4], const Sw
 #pragma unroll
           for (int r = 0; r < 16; ++r) z[i * 16 + r] = acc[i][j][r];
         if constexpr (!LOGITS) {
+          // token columns past `rows` hold a repeated row: exact zeros
+          const float off = (tl0 + 32 * j < rows) ? lc2 - lse2[j] : -INFINITY;
 #pragma unroll
-          for (int e = 0; e < 64; ++e) z[e] = fast_exp2(fmaf(z[e], c, -lse2[j]));
+          for (int e = 0; e < 64; ++e) z[e] = fast_exp2(fmaf(z[e], c, off));
         }
-        // token columns past `rows` hold a repeated row: exact zeros
-        const float cf = LOGITS ? 1.0f : ((tl0 + 32 * j < rows) ? coef : 0.0f);
         const int tp = wn * 64 + jj * 32 + (lane & 31);
         // staging bases of this lane's first row (wm*128 + 4*half); row
         // dv further on is at + dv*256 (G^T part) and + dv*2 (G part). The
@@ -314,12 +317,10 @@ __device__ __forceinline__ void grad_tile_staged(floatx16 (&acc)[4][4], const Sw
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int dv = i * 32 + 8 * q;
-            const bf16x2 p01 = {(__bf16)(z[i * 16 + 4 * q + 0] * cf),
-                                (__bf16)(z[i * 16 + 4 * q + 1] * cf)};
-            const bf16x2 p23 = {(__bf16)(z[i * 16 + 4 * q + 2] * cf),
-                                (__bf16)(z[i * 16 + 4 * q + 3] * cf)};
-            const uint32_t u01 = __builtin_bit_cast(uint32_t, p01);
-            const uint32_t u23 = __builtin_bit_cast(uint32_t, p23);
+            const bf16x2 p01 = {(__bf16)z[i * 16 + 4 * q + 0], (__bf16)z[i * 16 + 4 * q + 1]};
+            const bf16x2 p23 = {(__bf16)z[i * 16 + 4 * q + 2], (__bf16)z[i * 16 + 4 * q + 3]};
+            const uint32_t u01 = __builtin_bit_cast(uint32_t, p01) ^ sgn;
+            const uint32_t u23 = __builtin_bit_cast(uint32_t, p23) ^ sgn;
             if constexpr (!LOGITS) {
               *(uint16_t*)(gtb + (dv + 0) * 256) = (uint16_t)u01;
               *(uint16_t*)(gtb + (dv + 1) * 256) = (uint16_t)(u01 >> 16);
@@ -419,7 +420,8 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
   float tej[4];   // emission threshold of each token column (teacher cache writer)
   int dcur[4], dnext[4];   // sampled targets: next draw of the column and its unit
   int ecnt[4];             // teacher cache writer: candidates this lane appended per column
-  float coef = 0.0f;
+  float coef = 0.0f, lc2 = -INFINITY;
+  uint32_t sgn = 0u;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     m[j] = -INFINITY;
@@ -455,6 +457,8 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
   if constexpr (KIND == kSweepBwdG) {
     const int n = *a.nrows_dev;
     coef = (n > 0) ? a.grad_loss[0] / ((float)n * a.T) : 0.0f;
+    lc2 = coef != 0.0f ? log2f(fabsf(coef)) : -INFINITY;
+    sgn = coef < 0.0f ? 0x80008000u : 0u;
   }
 
   for (int vt = vt_begin; vt < vt_end; ++vt) {
@@ -474,12 +478,12 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
 
     const int vw0 = vt * kTile + wm * 128;
     if constexpr (KIND == kSweepBwdG && sizeof(T) == 2) {
-      grad_tile_staged<false>(acc, a, vt, jt, rows, tl0, c, coef, lse2, lds);
+      grad_tile_staged<false>(acc, a, vt, jt, rows, tl0, c, lc2, sgn, lse2, lds);
       continue;
     }
     if constexpr (KIND == kSweepLogits) {
       static_assert(sizeof(T) == 2, "the logits tile is stored as bf16");
-      grad_tile_staged<true>(acc, a, vt, jt, rows, tl0, c, coef, lse2, lds);
+      grad_tile_staged<true>(acc, a, vt, jt, rows, tl0, c, 0.0f, 0u, lse2, lds);
       continue;
     }
     if (vw0 >= a.V) continue;  // wave-uniform: this half tile is past the vocabulary

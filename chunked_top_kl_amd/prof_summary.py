@@ -221,23 +221,134 @@ def summarize_traffic(fetch_csv: str, write_csv: str, calib_mib: int, commands,
     return "\n".join(out)
 
 
+# ---------------------------------------------------------------------------
+# hardware counters (MFMA utilisation, instruction mix, L2, texture path)
+# ---------------------------------------------------------------------------
+def _pmc_means(paths):
+    """{step: {counter: mean per dispatch}} over one or more --pmc CSV dumps
+    (each pass a run of its own); also {step: dispatches}."""
+    sums = collections.defaultdict(lambda: collections.defaultdict(float))
+    cnts = collections.defaultdict(lambda: collections.defaultdict(int))
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            step = step_of(r["Kernel_Name"])
+            sums[step][r["Counter_Name"]] += float(r["Counter_Value"])
+            cnts[step][r["Counter_Name"]] += 1
+    means = {st: {c: sums[st][c] / cnts[st][c] for c in sums[st]} for st in sums}
+    disp = {st: max(cnts[st].values()) for st in cnts}
+    return means, disp
+
+
+def _derived(m, avg_ns=None, xcc=8, cus=256):
+    """Ratios of the mean counters of one step. With the step's mean duration
+    from a kernel trace: the shader clock (GRBM_GUI_ACTIVE is summed over the
+    XCCs) and the TD / TA busy fraction per CU-cycle (summed over the CUs)."""
+    d = {}
+    g = m.get("GRBM_GUI_ACTIVE")
+    if g:
+        cyc = g / xcc
+        if avg_ns:
+            d["clock_ghz"] = cyc / avg_ns
+        for c, k in (("TD_TD_BUSY_sum", "td_busy_per_cu_cycle"), ("TA_TA_BUSY_sum", "ta_busy_per_cu_cycle")):
+            if c in m:
+                d[k] = m[c] / (cyc * cus)
+    if "MfmaUtil" in m:
+        d["mfma_util_pct"] = m["MfmaUtil"]
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in m:
+        d["bf16_mfma_flop"] = m["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0
+    h, mi = m.get("TCC_HIT_sum"), m.get("TCC_MISS_sum")
+    if h is not None and mi is not None and h + mi > 0:
+        d["l2_hit_rate"] = h / (h + mi)
+    if m.get("SQ_INSTS_LDS"):
+        if "SQ_LDS_BANK_CONFLICT" in m:
+            d["lds_bank_conflict_cycles_per_lds_inst"] = m["SQ_LDS_BANK_CONFLICT"] / m["SQ_INSTS_LDS"]
+    if m.get("SQ_INSTS_MFMA"):
+        for c, k in (("SQ_INSTS_VALU", "valu_inst_per_mfma_inst"), ("SQ_INSTS_LDS", "lds_inst_per_mfma_inst")):
+            if c in m:
+                d[k] = m[c] / m["SQ_INSTS_MFMA"]
+    if m.get("TCP_TCC_READ_REQ_sum") and "TCP_TCC_READ_REQ_LATENCY_sum" in m:
+        d["l2_read_latency_cycles"] = m["TCP_TCC_READ_REQ_LATENCY_sum"] / m["TCP_TCC_READ_REQ_sum"]
+    return d
+
+
+def summarize_counters(paths, commands, workload: str, steps_of_interest=None,
+                       trace_stats=None) -> str:
+    means, disp = _pmc_means(paths)
+    avg_ns = {}
+    if trace_stats:
+        tot = collections.defaultdict(float)
+        cnt = collections.defaultdict(int)
+        for r in csv.DictReader(open(trace_stats)):
+            st = step_of(r["Name"])
+            tot[st] += float(r["TotalDurationNs"])
+            cnt[st] += int(r["Calls"])
+        avg_ns = {st: tot[st] / cnt[st] for st in tot if cnt[st]}
+    names = sorted(means, key=lambda st: -means[st].get("GRBM_GUI_ACTIVE", 0.0) * disp[st])
+    if steps_of_interest:
+        names = [n for n in names if n in steps_of_interest]
+    out = [f"# Hardware counters per launch: {workload}\n",
+           "rocprofv3 `--pmc`, one pass per counter set (each a run of its own), mean per",
+           "dispatch of each path step. `MfmaUtil` is rocprofv3's derived metric:",
+           "SQ_VALU_MFMA_BUSY_CYCLES summed over SIMDs / (GRBM_GUI_ACTIVE x SIMDs), in percent.",
+           "bf16 MFMA flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512. L2 hit rate = TCC_HIT /",
+           "(TCC_HIT + TCC_MISS). L2 read latency = TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ",
+           "(cycles per request, as seen from the vector L1). Clock = GRBM_GUI_ACTIVE / 8 XCCs",
+           "over the step's mean duration in the kernel trace of the same sources; TD and TA",
+           "busy = TD_TD_BUSY / TA_TA_BUSY summed over the CUs, per CU-cycle (256 CUs).\n",
+           "Commands (from the repository root):\n"]
+    out += [f"    {c}" for c in commands]
+    out += ["", "| step | launches | MfmaUtil % | clock GHz | bf16 MFMA TFLOP per launch | "
+            "VALU / MFMA inst | LDS / MFMA inst | LDS bank-conflict cycles / LDS inst | L2 hit | "
+            "L2 read latency | TD busy | TA busy |",
+            "|:--|--:|--:|--:|--:|--:|--:|--:|--:|--:|--:|--:|"]
+
+    def f(x, fmt):
+        return "" if x is None else format(x, fmt)
+
+    data = {}
+    for st in names:
+        d = _derived(means[st], avg_ns.get(st))
+        out.append(f"| {st} | {disp[st]} | {f(d.get('mfma_util_pct'), '.1f')} | "
+                   f"{f(d.get('clock_ghz'), '.2f')} | "
+                   f"{f(d.get('bf16_mfma_flop', 0) / 1e12 if 'bf16_mfma_flop' in d else None, '.3f')} | "
+                   f"{f(d.get('valu_inst_per_mfma_inst'), '.3f')} | "
+                   f"{f(d.get('lds_inst_per_mfma_inst'), '.3f')} | "
+                   f"{f(d.get('lds_bank_conflict_cycles_per_lds_inst'), '.3f')} | "
+                   f"{f(d.get('l2_hit_rate'), '.3f')} | {f(d.get('l2_read_latency_cycles'), '.0f')} | "
+                   f"{f(d.get('td_busy_per_cu_cycle'), '.2f')} | {f(d.get('ta_busy_per_cu_cycle'), '.2f')} |")
+        data[st] = dict(launches=disp[st], derived={k: round(v, 6) for k, v in d.items()},
+                        counters={k: round(v, 3) for k, v in sorted(means[st].items())})
+    out += ["", "Machine-readable copy (mean counter values per dispatch):", "",
+            _json_block(dict(kind="hw_counters", workload=workload,
+                             kernel_sources_sha256=kernel_sources_hash(), steps=data))]
+    return "\n".join(out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description="summaries of rocprofv3 output")
     sub = ap.add_subparsers(dest="what", required=True)
     t = sub.add_parser("trace")
     t.add_argument("--stats", required=True)
     t.add_argument("--steps", type=int, default=0)
+    c = sub.add_parser("counters")
+    c.add_argument("--pmc", action="append", required=True, help="a --pmc CSV dump (repeatable)")
+    c.add_argument("--steps-of-interest", default="")
+    c.add_argument("--trace-stats", default=None,
+                   help="kernel-trace stats CSV of the same sources (for the clock)")
     m = sub.add_parser("traffic")
     m.add_argument("--fetch", required=True)
     m.add_argument("--write", required=True)
     m.add_argument("--calib-mib", type=int, required=True)
-    for p in (t, m):
+    for p in (t, m, c):
         p.add_argument("--out", required=True)
         p.add_argument("--workload", required=True)
         p.add_argument("--command", action="append", default=[])
     a = ap.parse_args(argv)
     if a.what == "trace":
         text = summarize_trace(a.stats, a.command, a.workload, a.steps)
+    elif a.what == "counters":
+        soi = [x for x in a.steps_of_interest.split(",") if x]
+        text = summarize_counters(a.pmc, a.command, a.workload, soi or None, a.trace_stats)
     else:
         text = summarize_traffic(a.fetch, a.write, a.calib_mib, a.command, a.workload)
     with open(a.out, "w") as f:

@@ -97,3 +97,24 @@ def test_every_kernel_maps_to_a_step():
     assert step_of("kd_sample_draw_bf16") == "sample_draw"
     assert step_of("kd::sample_refined_entropy_kernel(kd::SelectWs, int, int, double*)") == \
         "select_refine_fp64"
+
+
+def test_counter_summary(tmp_path):
+    from chunked_top_kl_amd.prof_summary import summarize_counters
+    a = tmp_path / "a.csv"
+    b = tmp_path / "b.csv"
+    _pmc_csv(a, "MfmaUtil", [("kd_bwd_dw_bf16", 60.0), ("kd_bwd_dw_bf16", 50.0)])
+    with open(b, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=PMC_FIELDS)
+        w.writeheader()
+        for i, (c, v) in enumerate((("TCC_HIT_sum", 90.0), ("TCC_MISS_sum", 10.0),
+                                    ("SQ_INSTS_VALU_MFMA_MOPS_BF16", 2.0))):
+            w.writerow(dict(Dispatch_Id=0, Kernel_Name="kd_bwd_dw_bf16", Counter_Name=c,
+                            Counter_Value=v))
+    out = tmp_path / "c.md"
+    out.write_text(summarize_counters([str(a), str(b)], ["cmd"], "wl"))
+    js = read_summary_json(str(out))
+    d = js["steps"]["bwd_dw"]["derived"]
+    assert d["mfma_util_pct"] == 55.0
+    assert abs(d["l2_hit_rate"] - 0.9) < 1e-12
+    assert d["bf16_mfma_flop"] == 1024.0
