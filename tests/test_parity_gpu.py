@@ -71,6 +71,7 @@ def test_c1_tiny_fp32(kd):
     (1000, 136, 1537, 17, 96, 2.0),     # ragged S/V/H/chunk, V % 8 != 0, H % 64 != 0
     (300, 64, 4099, 100, 300, 1.0),     # one chunk, V % 256 tail
     (513, 256, 777, 33, 512, 0.7),      # S just past two tiles
+    (640, 224, 2003, 9, 320, 1.0),      # H tail of 224 columns: 4 and 3 column blocks
 ])
 def test_bf16_ragged(kd, S, H, V, K, chunk, T):
     p = make_problem(S, H, V, K, T=T, chunk=chunk, seed=S + V)
@@ -225,6 +226,14 @@ def test_empty_problems(kd):
     got = run_fwd_bwd(kd, p, mask=np.zeros(260, dtype=np.uint8))
     assert got["loss"][0] == 0.0 and np.all(got["dH"] == 0) and np.all(got["dW"] == 0)
     assert np.all(got["lse"] == 0) and np.all(np.isnan(got["z_topk"]))
+
+
+def test_fp32_h_tail(kd):
+    # fp32 contractions with H = 200: the waves of the h tile compute 4 and
+    # 3 of their column blocks
+    p = make_problem(300, 200, 1500, 8, T=1.0, chunk=128, hw_dtype="f32", tl_dtype="f32",
+                     seed=12)
+    check_against_oracle(p, run_fwd_bwd(kd, p), loss_rtol=1e-5, grad_frac=1e-4)
 
 
 def test_k1_and_k_equals_v(kd):
