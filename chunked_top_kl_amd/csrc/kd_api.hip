@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -40,8 +41,10 @@ struct ProfRec {
   const char* name;
   hipEvent_t a, b;
 };
+// Profiling (kd_profile_*): an opt-in measurement facility, off by default.
+// While it is off a launch scope reads one atomic flag and records nothing.
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+std::atomic<bool> g_prof_on{false};
 thread_local bool t_prof_off = false;   // set while a call that must not create events runs
 std::vector<ProfRec> g_prof_recs;
 std::vector<hipEvent_t> g_event_pool;
@@ -62,8 +65,9 @@ struct Prof {
   const char* name;
   hipEvent_t a = nullptr, b = nullptr;
   Prof(const char* n, hipStream_t s) : st(s), name(n) {
+    if (!g_prof_on.load(std::memory_order_relaxed) || t_prof_off) return;
     std::lock_guard<std::mutex> g(g_prof_mu);
-    if (!g_prof_on || t_prof_off) return;
+    if (!g_prof_on.load(std::memory_order_relaxed)) return;
     a = pool_event();
     b = pool_event();
     if (a && b) hipEventRecord(a, st);

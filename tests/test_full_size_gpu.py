@@ -193,3 +193,26 @@ def test_full_entropy_selective(kd):
     lse_all[ridx] = ref["lse"]
     check_dw_rows(p, W64, r["dW"], lse_all, m, sampled_vocab(p, rows, N_DW_ROWS, rng))
     check_dW_rows_sum_to_zero(r["dW"])
+
+
+@pytest.mark.parametrize("form", ["forward_chunked", "dense"])
+def test_full_32k_context_comparator_forms(kd, form):
+    # the comparator forms at the 32K-context size (the dense form's grids take
+    # about 66 GB of workspace): loss, every row's lse and KL against the stored
+    # oracle values; dHidden at 256 rows and dW at 128 vocabulary rows
+    p, meta, ref = stored("32k_context")
+    code = kd.KD_FORM_DENSE if form == "dense" else kd.KD_FORM_FORWARD_CHUNKED
+    hidden, W, ids, tl = to_device(p)
+    out = kd.kd_kl_comparator_fwd(hidden, W, ids, tl, code, p.T, p.chunk, want_kl_rows=True)
+    g = torch.ones(1, dtype=torch.float32, device="cuda")
+    dh, dW = kd.kd_kl_comparator_bwd(hidden, W, ids, tl, out["lse"], g, code, out["workspace"],
+                                     p.T, p.chunk)
+    torch.cuda.synchronize()
+    del out["workspace"]
+    assert rel(float(out["loss"][0]), meta["loss"]) <= BF16_LOSS_RTOL
+    check_row_values(out["lse"].cpu().numpy(), out["kl_rows"].cpu().numpy(), ref["lse"], ref["kl"])
+    W64 = p.W.astype(np.float64)
+    rng = np.random.default_rng(84)
+    rows = sampled_rows(np.arange(p.S), p.chunk, 256, rng)
+    check_dh_rows(p, W64, dh.cpu().numpy(), rows, p.S)
+    check_dw_rows(p, W64, dW, ref["lse"], np.ones(p.S, bool), sampled_vocab(p, rows, 128, rng))
