@@ -19,6 +19,9 @@ What is compared with the oracle at each size:
     oracle values, the kept index set bit for bit, and the selective KL's
     loss, the lse and KL of every kept row, dHidden at 1024 kept rows and dW
     at 512 vocabulary rows against the oracle over the kept rows.
+  * the comparator forms (dense, forward-chunked) at the 32K-context size:
+    the loss and every row's lse and KL against the stored oracle values,
+    dHidden at 256 rows and dW at 128 vocabulary rows.
 The rows of dW also sum to zero over the vocabulary (an extra check).
 Tolerances are those of the other parity tests.
 """
