@@ -103,7 +103,7 @@ struct Layout {
   size_t count, present, pos, idx, ids_s, p_s, korig_s, negH;
   size_t pm, ps, zs, bsum;
   size_t fwd_total;   // the forward uses only the buffers laid out before this offset
-  size_t G, GT, WT, XcT, Xc, dhp;
+  size_t G, GT, WT, XcT, Xc, dhp;   // GT: fp32 only
   size_t em, es, eu;
   size_t band, refined, scal, dscal, rpart, xb, counters;
   size_t smean, spos, pent;
@@ -121,6 +121,7 @@ struct Layout {
                       // 256 rows of a dW operand tile do not share one offset
                       // modulo a large power of two (L2 channel conflicts)
   int64_t esz;
+  int64_t Gbs;        // bf16: bytes between the column blocks of the gradient tiles
   int ks;             // dHidden vocabulary splits
 };
 
@@ -169,8 +170,18 @@ Layout plan(const kd_problem* p) {
   L.zs = take(Sx * K * 4);
   L.bsum = take((ceil_div(Sx, 256) + 1) * 8);
   L.fwd_total = off;
-  L.G = take(L.C * L.Vld * L.esz);
-  L.GT = take(L.Vp * L.Cld * L.esz);
+  if (L.esz == 2) {
+    // bf16: the gradient tiles of a whole dW group (slot s at rows
+    // [s * slot, s * slot + slot)) in blocks of 256 vocabulary columns, rows
+    // 512 bytes apart inside a block; dW reads them as they are
+    L.Gbs = L.nd * L.slot * 512;
+    L.G = take(ceil_div(L.Vp, 256) * L.Gbs);
+    L.GT = off;   // no transposed copy
+  } else {
+    // fp32: one chunk's tile, and the group's tiles transposed for dW
+    L.G = take(L.C * L.Vld * L.esz);
+    L.GT = take(L.Vp * L.Cld * L.esz);
+  }
   L.WT = take(H * L.Vld * L.esz);
   L.XcT = take(H * L.Cld * L.esz);
   L.Xc = take(L.C * H * L.esz);
@@ -470,6 +481,10 @@ int bwd_run(const kd_problem* p, const Layout& L, const CmpGrids& cg, const void
   for (int ci = 0; ci < nchunks; ++ci) {
     const int row_begin = ci * C;
     const int slot = (int)(ci % L.nd);   // this chunk's columns in the dW group
+    // this chunk's gradient tile: its slot of the group, blocked (bf16: ldg is
+    // the block stride), or the one row-major tile (fp32: ldg is the row pitch)
+    char* Gc = at<char>(ws, L.G) + (f32 ? 0 : (int64_t)slot * L.slot * 512);
+    const int64_t ldg = f32 ? L.Vld * L.esz : L.Gbs;
     if (S > 0) {
       Prof pr("gather_rows_t", st);
       KD_HIP(kd::launch_gather_rows_t(f32, (const char*)hidden, row_bytes, at<int32_t>(ws, L.idx),
@@ -498,16 +513,11 @@ int bwd_run(const kd_problem* p, const Layout& L, const CmpGrids& cg, const void
       ra.logQ = cg.logQ;
       ra.ldd = cg.ldd;
       ra.grad_loss = grad_loss;
-      ra.G = at<uint16_t>(ws, L.G);
-      ra.ldg = L.Vld;
-      {
-        Prof pr("cmp_grad", st);
-        KD_HIP(kd::launch_cmp_rows(cg.form == KD_FORM_DENSE ? kd::kCmpGradDense
-                                                            : kd::kCmpGradSparse, ra, st));
-      }
-      Prof pr("cmp_transpose", st);
-      KD_HIP(kd::launch_cmp_transpose(ra.G, L.Vld, ra.nrows_dev, row_begin, C, Vp,
-                                      at<uint16_t>(ws, L.GT) + slot * L.slot, L.Cld, st));
+      ra.G = (uint16_t*)Gc;
+      ra.ldg = ldg / 2;
+      Prof pr("cmp_grad", st);
+      KD_HIP(kd::launch_cmp_rows(cg.form == KD_FORM_DENSE ? kd::kCmpGradDense
+                                                          : kd::kCmpGradSparse, ra, st));
     } else if (S > 0) {
       kd::SweepArgs a;
       std::memset(&a, 0, sizeof(a));
@@ -531,9 +541,9 @@ int bwd_run(const kd_problem* p, const Layout& L, const CmpGrids& cg, const void
       a.korig_s = at<int32_t>(ws, L.korig_s);
       a.lse = lse;
       a.grad_loss = grad_loss;
-      a.G = at<char>(ws, L.G);
-      a.ldg = L.Vld * L.esz;
-      a.GT = at<char>(ws, L.GT) + slot * L.slot * L.esz;
+      a.G = Gc;
+      a.ldg = ldg;
+      a.GT = f32 ? at<char>(ws, L.GT) + slot * L.slot * L.esz : nullptr;
       a.ldgt = L.Cld * L.esz;
       {
         Prof pr("bwd_grad_tile", st);
@@ -558,8 +568,8 @@ int bwd_run(const kd_problem* p, const Layout& L, const CmpGrids& cg, const void
     }
     if (S > 0) {
       kd::DhArgs d;
-      d.G = at<char>(ws, L.G);
-      d.ldg = L.Vld * L.esz;
+      d.G = Gc;
+      d.ldg = ldg;
       d.WT = at<char>(ws, L.WT);
       d.ldwt = L.Vld * L.esz;
       d.nrows_dev = at<int32_t>(ws, L.count);
@@ -590,7 +600,9 @@ int bwd_run(const kd_problem* p, const Layout& L, const CmpGrids& cg, const void
     }
     if (slot == L.nd - 1 || ci == nchunks - 1) {
       kd::DwArgs w;
-      w.GT = at<char>(ws, L.GT);
+      w.G = at<char>(ws, L.G);
+      w.ldg = L.Gbs;
+      w.GT = f32 ? at<char>(ws, L.GT) : nullptr;
       w.ldgt = L.Cld * L.esz;
       w.Vp = Vp;
       w.XcT = at<char>(ws, L.XcT);

@@ -172,23 +172,32 @@ __global__ __launch_bounds__(256) void cmp_kl_dense_kernel(CmpRowArgs a) {
   }
 }
 
-// Logit gradient of a chunk's rows into G [r][Vp] (bf16, zeros in [V, Vp)):
+// Logit gradient of a chunk's rows into G (bf16, zeros in [V, Vp)), stored in
+// blocks of 256 columns as the fused path stores it (rows 256 elements apart
+// inside a block, blocks ldg elements apart):
 //   forward-chunked: coef (exp(z/T - lse) - p) with p at the teacher ids
 //     (summed over a run of equal ids), from the stored logits;
 //   dense: coef (exp(logQ) - P) from the stored grids;
-// coef = grad_loss / (T N).
+// coef = grad_loss / (T N). Rows in [rows, round_up(rows, 8)) are written as
+// zeros: the dW contraction reads whole groups of 8 rows.
 template <bool DENSE>
 __global__ __launch_bounds__(256) void cmp_grad_kernel(CmpRowArgs a) {
   const int rows = cmp_rows(a.nrows_dev, a.row_begin, a.row_cap);
   const int r = blockIdx.x;
-  if (r >= rows) return;
+  if (r >= ((rows + 7) & ~7)) return;
+  // granule g (8 columns) of row r
+  uint16_t* G = a.G + (int64_t)r * 256;
+  auto gran = [&](int g) { return G + (int64_t)(g >> 5) * a.ldg + 8 * (g & 31); };
+  if (r >= rows) {
+    for (int g = threadIdx.x; g < a.Vp / 8; g += 256) *(uint4*)gran(g) = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
   const int cr = a.row_begin + r;
   const int t = a.idx[cr];
   const int n = *a.nrows_dev;
   const float coef = n > 0 ? a.grad_loss[0] / ((float)n * a.T) : 0.0f;
   const float invT = 1.0f / a.T;
   const float lse = a.lse[t];
-  uint16_t* G = a.G + (int64_t)r * a.ldg;
   const uint16_t* z = a.Z + (int64_t)cr * a.ldz;
   const int ng = a.Vp / 8;
   for (int g = threadIdx.x; g < ng; g += 256) {
@@ -204,7 +213,7 @@ __global__ __launch_bounds__(256) void cmp_grad_kernel(CmpRowArgs a) {
       for (int e = 0; e < 8; ++e)
         x[e] = (8 * g + e < a.V) ? coef * __expf(fmaf(x[e], invT, -lse)) : 0.0f;
     }
-    *(uint4*)(G + 8 * g) = pack8(x);
+    *(uint4*)gran(g) = pack8(x);
   }
   if constexpr (!DENSE) {
     __syncthreads();
@@ -215,49 +224,7 @@ __global__ __launch_bounds__(256) void cmp_grad_kernel(CmpRowArgs a) {
       float p = 0.0f;
       for (int q = k; q < a.K && a.ids_s[base + q] == id; ++q) p += a.p_s[base + q];
       const float qv = __expf(fmaf(__uint_as_float((uint32_t)z[id] << 16), invT, -lse));
-      G[id] = (uint16_t)f32_to_bf16_bits(coef * (qv - p));
-    }
-  }
-}
-
-// GT[v][r] = G[r][v] for the chunk's rows r < rows, 0 for rows <= r < tpad
-// (v < Vp): the transposed gradient tile that dW reads, 64 x 64 tiles through
-// LDS with 16-byte accesses on both sides.
-__global__ __launch_bounds__(256) void cmp_transpose_kernel(const uint16_t* G, int64_t ldg,
-                                                            const int32_t* nrows_dev,
-                                                            int row_begin, int row_cap, int Vp,
-                                                            uint16_t* GT, int64_t ldgt) {
-  __shared__ uint16_t tile[64][66];
-  const int rows = cmp_rows(nrows_dev, row_begin, row_cap);
-  if (rows <= 0) return;
-  const int tpad = (rows + 7) & ~7;
-  const int r0 = blockIdx.x * 64, v0 = blockIdx.y * 64;
-  if (r0 >= tpad) return;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int rr = pass * 32 + (tid >> 3), g = tid & 7;
-    const int r = r0 + rr, v = v0 + 8 * g;
-    uint4 x = make_uint4(0u, 0u, 0u, 0u);
-    if (r < rows && v < Vp) x = *(const uint4*)(G + (int64_t)r * ldg + v);
-    const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      tile[rr][8 * g + 2 * e] = (uint16_t)(w4[e] & 0xFFFFu);
-      tile[rr][8 * g + 2 * e + 1] = (uint16_t)(w4[e] >> 16);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int vv = pass * 32 + (tid >> 3), j = tid & 7;
-    const int v = v0 + vv, r = r0 + 8 * j;
-    if (v < Vp && r < tpad) {
-      uint32_t o[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        o[e] = (uint32_t)tile[8 * j + 2 * e][vv] | ((uint32_t)tile[8 * j + 2 * e + 1][vv] << 16);
-      *(uint4*)(GT + (int64_t)v * ldgt + r) = make_uint4(o[0], o[1], o[2], o[3]);
+      gran(id >> 3)[id & 7] = (uint16_t)f32_to_bf16_bits(coef * (qv - p));
     }
   }
 }
@@ -290,7 +257,9 @@ __global__ __launch_bounds__(256) void cmp_loss_blocks_kernel(const int32_t* pos
 
 hipError_t launch_cmp_rows(int what, const CmpRowArgs& a, hipStream_t st) {
   if (a.row_cap <= 0) return hipSuccess;
-  const dim3 g((unsigned)a.row_cap), b(256);
+  // the gradient kinds also cover the zero rows up to round_up(rows, 8)
+  const bool grad = what == kCmpGradSparse || what == kCmpGradDense;
+  const dim3 g((unsigned)(grad ? round_up(a.row_cap, 8) : a.row_cap)), b(256);
   switch (what) {
     case kCmpKlSparse: hipLaunchKernelGGL(cmp_kl_sparse_kernel, g, b, 0, st, a); break;
     case kCmpDenseGrid: hipLaunchKernelGGL(cmp_dense_grid_kernel, g, b, 0, st, a); break;
@@ -299,16 +268,6 @@ hipError_t launch_cmp_rows(int what, const CmpRowArgs& a, hipStream_t st) {
     case kCmpGradDense: hipLaunchKernelGGL(cmp_grad_kernel<true>, g, b, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_cmp_transpose(const uint16_t* G, int64_t ldg, const int32_t* nrows_dev,
-                                int row_begin, int row_cap, int Vp, uint16_t* GT, int64_t ldgt,
-                                hipStream_t st) {
-  if (row_cap <= 0) return hipSuccess;
-  const dim3 grid((unsigned)ceil_div(round_up(row_cap, 8), 64), (unsigned)ceil_div(Vp, 64));
-  hipLaunchKernelGGL(cmp_transpose_kernel, grid, dim3(256), 0, st, G, ldg, nrows_dev, row_begin,
-                     row_cap, Vp, GT, ldgt);
   return hipGetLastError();
 }
 

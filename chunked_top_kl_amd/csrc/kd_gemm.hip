@@ -27,8 +27,10 @@ __device__ inline int chunk_rows(const int32_t* nrows_dev, int row_begin, int ro
 
 // ---------------------------------------------------------------------------
 // dHidden partials: part[split][r][h] = sum_{v in split} G[r][v] W[v][h]
-//   M = chunk rows (A = G [rows][Vp]), N = h (B = W^T [H][Vp]); both operands
-//   K (= vocabulary) contiguous. The vocabulary is split into `ks` ranges.
+//   M = chunk rows, N = h (B = W^T [H][Vp]); K = vocabulary. A = G: bf16 in
+//   blocks of 256 vocabulary columns (rows 512 bytes apart, blocks ldg bytes
+//   apart), fp32 as rows [rows][Vp] (row pitch ldg). The vocabulary is split
+//   into `ks` ranges.
 // ---------------------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ void dh_body(DhArgs a) {
@@ -49,13 +51,21 @@ __device__ __forceinline__ void dh_body(DhArgs a) {
   const int kend = (kbeg + per < nks_total) ? kbeg + per : nks_total;
   const int nk = kend > kbeg ? kend - kbeg : 0;
 
-  DmaOperand la, lb;
-  la.init(a.G + (int64_t)m * kTile * a.ldg, a.ldg, rows - m * kTile, (int64_t)kbeg * kKB,
-          (int64_t)a.V * esz);
+  DmaOperand lb;
   lb.init(a.WT + (int64_t)n * kTile * a.ldwt, a.ldwt, a.H - n * kTile, (int64_t)kbeg * kKB,
           (int64_t)a.V * esz);
   floatx16 acc[4][4];
-  gemm_mainloop<T, kDhAEarly>(acc, la, lb, nk, lds);
+  if constexpr (sizeof(T) == 2) {
+    DmaOperandBlk la;
+    la.init(a.G + (int64_t)m * kTile * 512, a.ldg, rows - m * kTile, (int64_t)kbeg * kKB,
+            (int64_t)a.V * esz);
+    gemm_mainloop<T, kDhAEarly>(acc, la, lb, nk, lds);
+  } else {
+    DmaOperand la;
+    la.init(a.G + (int64_t)m * kTile * a.ldg, a.ldg, rows - m * kTile, (int64_t)kbeg * kKB,
+            (int64_t)a.V * esz);
+    gemm_mainloop<T, kDhAEarly>(acc, la, lb, nk, lds);
+  }
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
   float* part = a.part + (int64_t)split * dh_split_stride(a.row_cap, a.H);
@@ -327,8 +337,10 @@ hipError_t launch_transpose_w(int f32, const char* W, int V, int H, char* WT, in
 
 // ---------------------------------------------------------------------------
 // dW[v][h] (+)= sum_r G[r][v] X_c[r][h]
-//   M = v (A = G^T [Vp][slots]), N = h (B = X_c^T [H][slots]); K = the token
-//   columns of a group of chunks, contiguous in both. Group 0 with
+//   M = v, N = h (B = X_c^T [H][slots]); K = the token rows of a group of
+//   chunks. bf16: A is the group's G itself, in blocks of 256 vocabulary
+//   columns ([slots][256] per block, blocks ldg bytes apart), read MN-major
+//   (transposed fragment reads); fp32: A = G^T [Vp][slots]. Group 0 with
 //   beta_first = 0 overwrites dW (and writes zeros when it is empty); later
 //   groups add, and return at once when they hold no rows.
 // ---------------------------------------------------------------------------
@@ -356,11 +368,20 @@ __device__ __forceinline__ void dw_body(DwArgs a) {
   const int in = L % (GM * nt);
   const int m = first_m + in % gsz, n = in / gsz;
 
-  DmaOperand la, lb;
-  la.init(a.GT + (int64_t)m * kTile * a.ldgt, a.ldgt, a.Vp - m * kTile, 0, (int64_t)rows * esz);
+  DmaOperand lb;
   lb.init(a.XcT + (int64_t)n * kTile * a.ldxt, a.ldxt, a.H - n * kTile, 0, (int64_t)rows * esz);
   floatx16 acc[4][4];
-  gemm_mainloop<T, kDwAEarly>(acc, la, lb, (int)ceil_div((int64_t)rows * esz, kKB), lds);
+  const int nk = (int)ceil_div((int64_t)rows * esz, kKB);
+  if constexpr (sizeof(T) == 2) {
+    // block m; its columns past Vp only feed rows of dW that are never stored
+    DmaOperandMN la;
+    la.init(a.G + (int64_t)m * a.ldg, 512, rows);
+    gemm_mainloop<T, kDwAEarly, true>(acc, la, lb, nk, lds);
+  } else {
+    DmaOperand la;
+    la.init(a.GT + (int64_t)m * kTile * a.ldgt, a.ldgt, a.Vp - m * kTile, 0, (int64_t)rows * esz);
+    gemm_mainloop<T, kDwAEarly>(acc, la, lb, nk, lds);
+  }
 
   const bool beta = (a.group_begin > 0) || a.beta_first;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;

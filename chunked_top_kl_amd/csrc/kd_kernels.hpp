@@ -29,9 +29,12 @@ struct SweepArgs {
   float* zs;                          // [S,K], indexed like ids_s
   // backward
   const float* lse; const float* grad_loss;
-  char* G; int64_t ldg;               // gradient tile [row_cap, Vp], bytes per row (the
-                                      // logits kind stores z there, bf16)
-  char* GT; int64_t ldgt;             // the same tile transposed [Vp, Cp]
+  char* G; int64_t ldg;               // gradient tile: bf16 in blocks of 256 vocabulary
+                                      // columns, [rows][256] each, blocks ldg bytes
+                                      // apart; fp32 [row_cap, Vp], ldg bytes per row.
+                                      // The logits kind stores z as rows [rows][Vld]
+                                      // (ldg bytes per row).
+  char* GT; int64_t ldgt;             // fp32: the same tile transposed [Vp, Cp] (bf16: unused)
   // entropy partials
   float* em; double* es; double* eu;
   // teacher cache writer: pilot group maxima zp[g][r] (pitch ldp floats); per-row
@@ -103,7 +106,8 @@ struct SignalArgs {
 };
 
 struct DhArgs {
-  const char* G; int64_t ldg;         // [rows, Vp]
+  const char* G; int64_t ldg;         // bf16: the chunk's rows of the blocked gradient
+                                      // tiles (ldg = block stride); fp32: [rows, Vp]
   const char* WT; int64_t ldwt;       // W transposed [H, Vp]
   const int32_t* nrows_dev;
   int row_begin, row_cap, V, H, ncu;
@@ -129,7 +133,9 @@ struct DhReduceArgs {
 // occupies token columns [k*slot, k*slot + round_up(rows_k, 8)) of G^T and
 // X_c^T (zeros past rows_k), slot = round_up(C, 8).
 struct DwArgs {
-  const char* GT; int64_t ldgt; int Vp;             // gradient tiles transposed [Vp, slots]
+  const char* G; int64_t ldg;                       // bf16: the group's blocked gradient tiles
+                                                    // (ldg = block stride)
+  const char* GT; int64_t ldgt; int Vp;             // fp32: the same transposed [Vp, slots]
   const char* XcT; int64_t ldxt;                    // gathered hidden rows transposed [H, slots]
   const int32_t* nrows_dev;
   int group_begin;                                  // first compacted row of the group
@@ -140,8 +146,8 @@ struct DwArgs {
 
 // Teacher term of the gradient tile of one chunk (see kd_sweep.hip).
 struct GradTeacherArgs {
-  char* G; int64_t ldg;            // [rows][Vld]
-  char* GT; int64_t ldgt;          // [Vp][slots], this chunk's slot
+  char* G; int64_t ldg;            // bf16: blocked (ldg = block stride); fp32: [rows][Vld]
+  char* GT; int64_t ldgt;          // fp32: [Vp][slots], this chunk's slot; bf16: null
   const int32_t* idx;              // compacted row -> original row
   const int32_t* nrows_dev;
   int row_begin, row_cap, K;
@@ -164,7 +170,8 @@ struct CmpRowArgs {
   float* lse; float* kl;
   float* P; float* logQ; int64_t ldd;
   const float* grad_loss;
-  uint16_t* G; int64_t ldg;
+  uint16_t* G; int64_t ldg;   // the chunk's rows of the blocked gradient tiles (ldg = block
+                              // stride, elements)
 };
 enum CmpRowKind { kCmpKlSparse = 0, kCmpDenseGrid = 1, kCmpKlDense = 2, kCmpGradSparse = 3,
                   kCmpGradDense = 4 };
@@ -203,9 +210,6 @@ hipError_t launch_fwd_combine(const CombineArgs& a, hipStream_t st);
 hipError_t launch_loss_final(const double* block_sums, int nblk, const int32_t* nrows_dev,
                              float* loss, hipStream_t st);
 hipError_t launch_cmp_rows(int what, const CmpRowArgs& a, hipStream_t st);
-hipError_t launch_cmp_transpose(const uint16_t* G, int64_t ldg, const int32_t* nrows_dev,
-                                int row_begin, int row_cap, int Vp, uint16_t* GT, int64_t ldgt,
-                                hipStream_t st);
 hipError_t launch_cmp_loss(const int32_t* pos, int64_t S, float* lse, float* kl, float* kl_out,
                            double* block_sums, const int32_t* nrows_dev, float* loss,
                            hipStream_t st);

@@ -239,34 +239,29 @@ __device__ __forceinline__ float pick64(const Z& z, int tgt) {
 
 // ---------------------------------------------------------------------------
 // Gradient tile epilogue (bf16): G = coef * 2^(z*c - lse2) (the teacher term
-// is applied afterwards by grad_teacher_kernel) for the
-// 256 x 256 tile, written to G [rows][Vp] and G^T [Vp][Cp] through LDS so
-// that both are stored as whole 16-byte granules along their rows.
+// is applied afterwards by grad_teacher_kernel) for the 256 x 256 tile,
+// written through LDS as whole 16-byte granules. G is stored in blocks of 256
+// vocabulary columns: block b holds columns [256 b, 256 b + 256) of every row,
+// rows 512 bytes apart, blocks a.ldg bytes apart, so a tile's 256 rows are one
+// contiguous 128 KB store. The dW contraction reads a block's rows as they are
+// (transposed fragment reads), so no transposed copy is written.
 //
-// Half of the token columns at a time (columns j = 2jp, 2jp+1 of every lane)
-// are staged in the idle main-loop stage area as
-//   G^T part: [256 v][128 t'] bf16, 256 B per row, 16-byte granule index
-//             xor 4 on rows with bit 2 set (the two lane halves write rows
-//             four apart);
-//   G part:   [128 t'][256 v] bf16, rows kGPitch = 528 B apart (padding
-//             puts the rows that consecutive lanes write in distinct banks),
-// with staging column t' = wn*64 + (j&1)*32 + lane%32, i.e. tile token
-// (t' / 64) * 128 + 64 jp + t' % 64. Then all 256 threads store rows.
-// Every wave takes part in the barriers; a wave whose half tile lies past the
-// vocabulary computes nothing (its rows are at or past Vp and never stored).
+// The tile is staged in the idle main-loop stage area as [256 t][256 v] bf16,
+// rows kGPitch = 528 B apart (padding puts the rows that consecutive lanes
+// write in distinct banks), then all 256 threads store rows. Every wave takes
+// part in the barriers; a wave whose half tile lies past the vocabulary
+// computes nothing (its rows are at or past Vp and never stored).
 // ---------------------------------------------------------------------------
 constexpr int kGPitch = 528;
-constexpr int kStagingLds = 64 * 1024 + 128 * kGPitch;   // inside the main-loop stage area
-
-__device__ __forceinline__ int staged_token(int tp, int jp) {
-  return (tp >> 6) * 128 + 64 * jp + (tp & 63);
-}
+constexpr int kStagingLds = 256 * kGPitch;   // inside the main-loop stage area
 
 // The scale coef is folded into the exponent, coef * 2^x = 2^(x + log2|coef|),
 // and its sign applied to the bf16 bits (lc2 = log2|coef|, -inf for 0;
-// sgn = the sign bit of coef in both halves of a bf16 pair).
-// LOGITS: the same store of z itself (no exponential, no scale) into the G
-// rows only; nothing of G^T is staged or stored.
+// sgn = the sign bit of coef in both halves of a bf16 pair). Token rows in
+// [rows, round_up(rows, 8)) are written as zeros (the dW contraction reads
+// whole groups of 8 token rows).
+// LOGITS: the same store of z itself (no exponential, no scale), rows < rows
+// only, as rows [rows][Vld] (a.ldg bytes per row).
 template <bool LOGITS>
 __device__ __forceinline__ void grad_tile_staged(floatx16 (&acc)[4][4], const SweepArgs& a, int vt,
                                                  int jt, int rows, int tl0, float c, float lc2,
@@ -276,90 +271,62 @@ __device__ __forceinline__ void grad_tile_staged(floatx16 (&acc)[4][4], const Sw
   const int vw0 = vt * kTile + wm * 128;
   const bool live = vw0 < a.V;
   const int Vp = (int)round_up(a.V, 8);
-  const int tpad = (int)round_up(rows, 8);
-  char* sgt = lds;
-  char* sg = lds + 64 * 1024;
+  const int tlim = LOGITS ? rows : (int)round_up(rows, 8);
+  char* sg = lds;
   // every wave has read its last main-loop fragments before the area is reused
   __syncthreads();
 #pragma unroll
-  for (int jp = 0; jp < 2; ++jp) {
+  for (int j = 0; j < 4; ++j) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (live) {
+      // vocabulary rows past V have z = 0 (zero W rows): their finite values
+      // land in G's padding columns [V, Vp), which the contractions multiply
+      // by zeros or never read
+      float z[64];
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int j = 2 * jp + jj;
-      __builtin_amdgcn_sched_barrier(0);
-      if (live) {
-        // vocabulary rows past V have z = 0 (zero W rows): their finite
-        // values land in G's padding columns [V, Vp) and G^T's padding rows,
-        // which the contractions multiply by zeros or never read
-        float z[64];
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int r = 0; r < 16; ++r) z[i * 16 + r] = acc[i][j][r];
+      if constexpr (!LOGITS) {
+        // token columns past `rows` hold a repeated row: exact zeros
+        const float off = (tl0 + 32 * j < rows) ? lc2 - lse2[j] : -INFINITY;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) z[i * 16 + r] = acc[i][j][r];
-        if constexpr (!LOGITS) {
-          // token columns past `rows` hold a repeated row: exact zeros
-          const float off = (tl0 + 32 * j < rows) ? lc2 - lse2[j] : -INFINITY;
+        for (int e = 0; e < 64; ++e) z[e] = fast_exp2(fmaf(z[e], c, off));
+      }
+      // this lane's token row of the tile and its first vocabulary column
+      // (wm*128 + 4*half); entry (i, r) is at column + i*32 + 8*(r/4) + r%4
+      char* gb = sg + (wn * 128 + 32 * j + (lane & 31)) * kGPitch + (wm * 128 + 4 * half) * 2;
 #pragma unroll
-          for (int e = 0; e < 64; ++e) z[e] = fast_exp2(fmaf(z[e], c, off));
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int dv = i * 32 + 8 * q;
+          const bf16x2 p01 = {(__bf16)z[i * 16 + 4 * q + 0], (__bf16)z[i * 16 + 4 * q + 1]};
+          const bf16x2 p23 = {(__bf16)z[i * 16 + 4 * q + 2], (__bf16)z[i * 16 + 4 * q + 3]};
+          const uint32_t u01 = __builtin_bit_cast(uint32_t, p01) ^ sgn;
+          const uint32_t u23 = __builtin_bit_cast(uint32_t, p23) ^ sgn;
+          *(uint2*)(gb + dv * 2) = make_uint2(u01, u23);
         }
-        const int tp = wn * 64 + jj * 32 + (lane & 31);
-        // staging bases of this lane's first row (wm*128 + 4*half); row
-        // dv further on is at + dv*256 (G^T part) and + dv*2 (G part). The
-        // G^T granule swizzle bit ((row >> 2) & 1) is the lane half for all
-        // of this lane's rows.
-        char* gtb = sgt + (wm * 128 + 4 * half) * 256 +
-                    ((((tp >> 3) ^ (half << 2)) << 4) + (tp & 7) * 2);
-        char* gb = sg + tp * kGPitch + (wm * 128 + 4 * half) * 2;
-        // coef * q; the teacher term at the teacher ids is applied afterwards
-        // (grad_teacher_kernel)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int dv = i * 32 + 8 * q;
-            const bf16x2 p01 = {(__bf16)z[i * 16 + 4 * q + 0], (__bf16)z[i * 16 + 4 * q + 1]};
-            const bf16x2 p23 = {(__bf16)z[i * 16 + 4 * q + 2], (__bf16)z[i * 16 + 4 * q + 3]};
-            const uint32_t u01 = __builtin_bit_cast(uint32_t, p01) ^ sgn;
-            const uint32_t u23 = __builtin_bit_cast(uint32_t, p23) ^ sgn;
-            if constexpr (!LOGITS) {
-              *(uint16_t*)(gtb + (dv + 0) * 256) = (uint16_t)u01;
-              *(uint16_t*)(gtb + (dv + 1) * 256) = (uint16_t)(u01 >> 16);
-              *(uint16_t*)(gtb + (dv + 2) * 256) = (uint16_t)u23;
-              *(uint16_t*)(gtb + (dv + 3) * 256) = (uint16_t)(u23 >> 16);
-            }
-            *(uint2*)(gb + dv * 2) = make_uint2(u01, u23);
-          }
-      }
-      __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
-    // G^T rows: 256 rows x 16 granules of 8 tokens
-#pragma unroll 4
-    for (int it = 0; it < (LOGITS ? 0 : 16); ++it) {
-      const int g = it * 256 + tid;
-      const int vl = g >> 4, gr = g & 15;
-      const int v = vt * kTile + vl;
-      const int t = jt * kTile + staged_token(gr * 8, jp);
-      if (v < Vp && t < tpad) {
-        const u32x4 val = *(const u32x4*)(sgt + vl * 256 + ((gr ^ (((vl >> 2) & 1) << 2)) << 4));
-        __builtin_nontemporal_store(val, (u32x4*)(a.GT + (int64_t)v * a.ldgt + (int64_t)t * 2));
-      }
-    }
-    // G rows: 128 rows x 32 granules of 8 vocabulary entries
-#pragma unroll 4
-    for (int it = 0; it < 16; ++it) {
-      const int g = it * 256 + tid;
-      const int tp = g >> 5, gr = g & 31;
-      const int t = jt * kTile + staged_token(tp, jp);
-      const int v = vt * kTile + gr * 8;
-      if (t < rows && v < Vp) {
-        const u32x4 val = *(const u32x4*)(sg + tp * kGPitch + gr * 16);
-        __builtin_nontemporal_store(val, (u32x4*)(a.G + (int64_t)t * a.ldg + (int64_t)v * 2));
-      }
-    }
-    // the next half (or the next tile's loads) reuses the area
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
   }
+  __syncthreads();
+  // 256 rows x 32 granules of 8 vocabulary entries
+  char* gt = LOGITS ? a.G + (int64_t)vt * kTile * 2 : a.G + (int64_t)vt * a.ldg;
+  const int64_t rpitch = LOGITS ? a.ldg : 512;
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int g = it * 256 + tid;
+    const int tp = g >> 5, gr = g & 31;
+    const int t = jt * kTile + tp;
+    const int v = vt * kTile + gr * 8;
+    if (t < tlim && v < Vp) {
+      const u32x4 val = *(const u32x4*)(sg + tp * kGPitch + gr * 16);
+      __builtin_nontemporal_store(val, (u32x4*)(gt + (int64_t)t * rpitch + gr * 16));
+    }
+  }
+  // the next tile's loads reuse the area
+  __syncthreads();
 }
 
 template <typename T, int KIND, bool MAP>
@@ -718,7 +685,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
         }
       }
 
-      if constexpr (KIND == kSweepBwdG) {
+      if constexpr (KIND == kSweepBwdG && sizeof(T) == 4) {
         // coef * q; the teacher term is applied by grad_teacher_kernel
 #pragma unroll
         for (int e = 0; e < 64; ++e) z[e] = fast_exp2(fmaf(z[e], c, -lse2[j]));
@@ -741,23 +708,12 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
               const float g1 = gv ? z[i * 16 + 4 * q + 1] * coef : 0.0f;
               const float g2 = gv ? z[i * 16 + 4 * q + 2] * coef : 0.0f;
               const float g3 = gv ? z[i * 16 + 4 * q + 3] * coef : 0.0f;
-              char* gt = a.GT + (int64_t)v * a.ldgt + (int64_t)t * sizeof(T);
-              if constexpr (sizeof(T) == 2) {
-                const uint32_t b0 = f32_to_bf16_bits(g0), b1 = f32_to_bf16_bits(g1);
-                const uint32_t b2 = f32_to_bf16_bits(g2), b3 = f32_to_bf16_bits(g3);
-                if (gv)
-                  *(uint2*)(grow + (int64_t)v * 2) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-                *(uint16_t*)(gt) = (uint16_t)b0;
-                *(uint16_t*)(gt + a.ldgt) = (uint16_t)b1;
-                *(uint16_t*)(gt + 2 * a.ldgt) = (uint16_t)b2;
-                *(uint16_t*)(gt + 3 * a.ldgt) = (uint16_t)b3;
-              } else {
-                if (gv) *(float4*)(grow + (int64_t)v * 4) = make_float4(g0, g1, g2, g3);
-                *(float*)(gt) = g0;
-                *(float*)(gt + a.ldgt) = g1;
-                *(float*)(gt + 2 * a.ldgt) = g2;
-                *(float*)(gt + 3 * a.ldgt) = g3;
-              }
+              char* gt = a.GT + (int64_t)v * a.ldgt + (int64_t)t * 4;
+              if (gv) *(float4*)(grow + (int64_t)v * 4) = make_float4(g0, g1, g2, g3);
+              *(float*)(gt) = g0;
+              *(float*)(gt + a.ldgt) = g1;
+              *(float*)(gt + 2 * a.ldgt) = g2;
+              *(float*)(gt + 3 * a.ldgt) = g3;
             }
         }
       }
@@ -936,15 +892,15 @@ __global__ __launch_bounds__(256) void grad_teacher_kernel(GradTeacherArgs a) {
   const int n = *a.nrows_dev;
   const float coef = (n > 0) ? a.grad_loss[0] / ((float)n * a.T) : 0.0f;
   const float d = coef * P;
-  T* g = (T*)(a.G + (int64_t)r * a.ldg) + id;
-  T* gt = (T*)(a.GT + (int64_t)id * a.ldgt) + r;
   if constexpr (sizeof(T) == 2) {
-    const float x = bf16_to_f32(*(const uint16_t*)g);
+    // bf16: G only, in blocks of 256 columns (the dW contraction reads G itself)
+    uint16_t* g = (uint16_t*)(a.G + (int64_t)(id >> 8) * a.ldg + (int64_t)r * 512) + (id & 255);
+    const float x = bf16_to_f32(*g);
     const bf16x2 y = {(__bf16)(x - d), (__bf16)0.0f};
-    const uint16_t b = (uint16_t)__builtin_bit_cast(uint32_t, y);
-    *(uint16_t*)g = b;
-    *(uint16_t*)gt = b;
+    *g = (uint16_t)__builtin_bit_cast(uint32_t, y);
   } else {
+    T* g = (T*)(a.G + (int64_t)r * a.ldg) + id;
+    T* gt = (T*)(a.GT + (int64_t)id * a.ldgt) + r;
     const float y = *g - d;
     *g = y;
     *gt = y;

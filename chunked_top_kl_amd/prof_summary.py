@@ -89,7 +89,6 @@ STEP_PATTERNS = [
     ("cmp_dense_grid", "cmp_rows"),
     ("cmp_loss_blocks", "cmp_loss"),
     ("cmp_grad_kernel", "cmp_grad"),
-    ("cmp_transpose", "cmp_transpose"),
     ("copyBuffer", "device_copy"),
 ]
 

@@ -436,7 +436,10 @@ int kd_teacher_sample(const kd_problem* problem, const void* hidden, const void*
  * is bracketed by HIP events on the same stream. kd_profile_read synchronises
  * those events and reports, per kernel name, the number of launches and the
  * summed duration in milliseconds; it returns the number of names written (at
- * most max_entries). kd_profile_reset discards the records.                 */
+ * most max_entries). kd_profile_reset discards the records. The records and
+ * the on/off flag are process-wide (shared by every thread and device, guarded
+ * by a lock that is taken only while profiling is on); they never change a
+ * result. The no-alloc forward records no events.                          */
 typedef struct kd_kernel_stat {
   char name[48];
   int64_t launches;
