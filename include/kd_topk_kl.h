@@ -95,8 +95,10 @@ typedef enum kd_teacher_kind { KD_TEACHER_LOGITS = 0, KD_TEACHER_PROBS = 1 } kd_
  *   H      hidden size; multiple of 8
  *   V      vocabulary size (rows of W)
  *   K      teacher entries per position, 1 <= K <= min(V, 4096)
- *   chunk  rows per backward chunk: bounds the [chunk, V] bf16 gradient tile
- *          held in the workspace (the only workspace term that grows with V)
+ *   chunk  rows per backward chunk. The backward holds the gradient tiles
+ *          of a group of consecutive chunks (about max(chunk, 8192) rows x V
+ *          in hw_dtype; fp32 also keeps a transposed copy): with W^T, the
+ *          only workspace terms that grow with V
  * Size limits (KD_ERR_SHAPE otherwise): S < 2^30, H <= 2^20, V <= 2^30, and
  * 256 rows of the padded gradient-tile pitch (about V elements of hw_dtype)
  * and of the transposed chunk pitch (about 8192 or chunk elements) each below
@@ -122,8 +124,9 @@ const char* kd_status_str(int status);
 
 /* Workspace bytes needed by every entry point below for this problem (the
  * maximum over them). Returns 0 if the problem itself is invalid. The size is
- * linear in S (per-row teacher tables and partials) plus a constant part
- * (the [chunk, V] bf16 gradient tile and split-K partials of dHidden). */
+ * linear in S (per-row teacher tables and partials) plus a part that does
+ * not grow with S (the gradient tiles of a group of chunks, W^T and the
+ * split-K partials of dHidden). */
 size_t kd_topk_kl_workspace_bytes(const kd_problem* problem);
 
 /* Forward pass ("what chunked KL loss does": project, fold into the loss,
@@ -168,7 +171,7 @@ int kd_topk_kl_fwd_noalloc(const kd_problem* problem, const void* hidden, const 
  * recomputes the chunk"); the logit gradient
  *   G_tv = g/N * (softmax(z_t/T)_v - p_t(v)) / T,   g = *grad_loss,
  * with p_t(v) the teacher probability scattered to its id, is formed in the
- * projection's epilogue as a bf16 [chunk,V] tile and contracted twice:
+ * projection's epilogue as a [chunk,V] tile in hw_dtype and contracted twice:
  *   dhidden[t] = G_t W  (rows not taking part are set to 0),
  *   dW        (+)= G^T hidden_chunk, accumulated over chunks in fp32.
  *   lse         [device] [S] float32 from kd_topk_kl_fwd with the same inputs
