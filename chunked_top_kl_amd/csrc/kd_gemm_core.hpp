@@ -442,9 +442,29 @@ __device__ __forceinline__ void mfma_sub_loads_reads(floatx16 (&acc)[4][4], cons
     }
 }
 
+// Issue stages 0 and 1 of the next main loop ahead of time, into the buffers
+// its own prologue would use, so that they load while the caller works on the
+// previous tile's accumulators; that main loop is then called with
+// prefetched = true. Nothing may use the LDS in between. (Memory waits the
+// compiler places in between, such as spill reloads, wait for these loads as
+// well: the vector memory counter retires in order.)
+template <bool A_EARLY, class OA, class OB>
+__device__ inline void gemm_prefetch(const OA& la, const OB& lb, int nk, char* lds) {
+  if (nk <= 0) return;
+  const uint32_t base = lds_addr(lds);
+  // every wave has read its last fragments of the previous call
+  __syncthreads();
+  if constexpr (A_EARLY) { la.issue(0, base); lb.issue(0, base + kLBase); }
+  else { lb.issue(0, base); la.issue(0, base + kLBase); }
+  if (nk > 1) {
+    if constexpr (A_EARLY) { la.issue(1, base + kOpBuf); lb.issue(1, base + kLBase + kOpBuf); }
+    else { lb.issue(1, base + kOpBuf); la.issue(1, base + kLBase + kOpBuf); }
+  }
+}
+
 template <typename T, bool A_EARLY, bool A_MN = false, class OA, class OB>
 __device__ inline void gemm_mainloop(floatx16 (&acc)[4][4], const OA& la, const OB& lb, int nk,
-                                     char* lds) {
+                                     char* lds, bool prefetched = false) {
   using V = typename Frag<T>::type;
   static_assert(!A_MN || sizeof(T) == 2, "the transposed fragment read is for bf16");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
@@ -470,16 +490,20 @@ __device__ inline void gemm_mainloop(floatx16 (&acc)[4][4], const OA& la, const 
     if constexpr (A_EARLY) lb.issue(kt, base + kLBase + i * kOpBuf);
     else la.issue(kt, base + kLBase + i * kOpBuf);
   };
-  // every wave has finished reading the stages of a previous call
-  __syncthreads();
-  issue_e(0, 0);
-  issue_l(0, 0);
-  if (nk > 1) {
-    issue_e(1, 1);
-    issue_l(1, 1);
-    wait_vmcnt<16>();
-  } else {
+  if (prefetched) {
     wait_vmcnt<0>();
+  } else {
+    // every wave has finished reading the stages of a previous call
+    __syncthreads();
+    issue_e(0, 0);
+    issue_l(0, 0);
+    if (nk > 1) {
+      issue_e(1, 1);
+      issue_l(1, 1);
+      wait_vmcnt<16>();
+    } else {
+      wait_vmcnt<0>();
+    }
   }
   __syncthreads();
   SubFrags<V> f0, f1;

@@ -428,6 +428,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
     sgn = coef < 0.0f ? 0x80008000u : 0u;
   }
 
+  bool pf = false;
   for (int vt = vt_begin; vt < vt_end; ++vt) {
     // operand state is rebuilt per tile so that nothing of the main loop stays
     // live (and spillable) across the register-heavy epilogues
@@ -441,7 +442,19 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
               kbytes);
     }
     floatx16 acc[4][4];
-    gemm_mainloop<T, kSweepAEarly>(acc, la, lb, nk, lds);
+    gemm_mainloop<T, kSweepAEarly>(acc, la, lb, nk, lds, pf);
+    pf = false;
+    if constexpr (KIND != kSweepBwdG && KIND != kSweepLogits) {
+      // the next tile's first two stages load while this tile's epilogue runs
+      // (these epilogues use no LDS; the gradient and logits tiles stage
+      // their stores there)
+      if (vt + 1 < vt_end) {
+        DmaOperand ln;
+        ln.init(a.W + (int64_t)(vt + 1) * kTile * a.ldw, a.ldw, a.V - (vt + 1) * kTile, 0, kbytes);
+        gemm_prefetch<kSweepAEarly>(ln, lb, nk, lds);
+        pf = true;
+      }
+    }
 
     const int vw0 = vt * kTile + wm * 128;
     if constexpr (KIND == kSweepBwdG && sizeof(T) == 2) {
