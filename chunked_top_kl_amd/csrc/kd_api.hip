@@ -111,12 +111,12 @@ struct Layout {
   size_t total;
   int64_t C;          // rows per backward chunk (<= S, >= 1)
   int64_t Vp;         // vocabulary columns of the gradient tile: round_up(V, 8)
-  int64_t Vld;        // row pitch (elements) of G and W^T: an odd multiple of 128 bytes,
+  int64_t Vld;        // row pitch (elements) of W^T (and of fp32's G): an odd multiple of 128 bytes,
                       // so that the 256 rows of an operand tile spread over all
                       // 128-byte offsets modulo 4 KB (L2 channels)
-  int64_t slot;       // token columns of one chunk in the transposed tiles: round_up(C, 8)
+  int64_t slot;       // token rows (columns, transposed) of one chunk in a dW group: round_up(C, 8)
   int64_t nd;         // chunks per dW contraction (group)
-  int64_t Cp;         // token columns of the transposed tiles: nd slots rounded to 32
+  int64_t Cp;         // token columns of X_c^T (and fp32's G^T): nd slots rounded to 32
   int64_t Cld;        // their row pitch in elements: Cp plus 128 bytes, so that the
                       // 256 rows of a dW operand tile do not share one offset
                       // modulo a large power of two (L2 channel conflicts)

@@ -130,8 +130,9 @@ struct DhReduceArgs {
 };
 
 // dW contracts a group of consecutive chunks at once: chunk k of the group
-// occupies token columns [k*slot, k*slot + round_up(rows_k, 8)) of G^T and
-// X_c^T (zeros past rows_k), slot = round_up(C, 8).
+// occupies token rows [k*slot, k*slot + round_up(rows_k, 8)) of the gradient
+// tiles (bf16; token columns of G^T for fp32) and token columns of X_c^T
+// (zeros past rows_k), slot = round_up(C, 8).
 struct DwArgs {
   const char* G; int64_t ldg;                       // bf16: the group's blocked gradient tiles
                                                     // (ldg = block stride)

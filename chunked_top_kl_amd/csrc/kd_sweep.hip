@@ -881,7 +881,8 @@ hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid
 // Teacher term of the gradient tile. The tile kernel stores coef * q for
 // every vocabulary entry; this kernel rewrites the entries at the teacher ids
 // of each chunk row as coef * q - coef * P, P the summed probability of a run
-// of equal ids in the sorted table (duplicates add), in both G and G^T. One
+// of equal ids in the sorted table (duplicates add), in G (and, for fp32, in
+// G^T). One
 // thread per (row, k); the first entry of a run does the update, so no two
 // threads touch one element. The stored value is read back, so the entry is
 // rounded to the storage type twice (once as coef * q); the second rounding
