@@ -302,6 +302,117 @@ __global__ __launch_bounds__(256) void refine_kernel(const double* __restrict__ 
   }
 }
 
+// The same partials on the fp64 matrix cores (bf16 W): a work-group takes 16
+// band rows and a tile of 256 vocabulary rows, each wave 64 of them as four
+// 16 x 16 blocks of v_mfma_f64_16x16x4f64 (D[i][j] += sum over k < 4 of
+// A[i][k] B[k][j]; lane l holds A[l%16][l/16] and B[l/16][l%16], and D[4r +
+// l/16][l%16] in register r). The K order is permuted so that each lane loads
+// whole 16-byte pieces: in a step of 32 h, lane l takes h = hs + 8 (l/16) + e
+// for the MFMA of index e < 8, as both operands' k = l/16. Band rows past the
+// end repeat the last one and vocabulary rows past V the last row; neither
+// result is used. Every product is exact in fp64 (bf16 by widened bf16 or
+// fp64-widened inputs) and the sums are fp64.
+constexpr int kRefMR = 16;   // band rows per work-group
+typedef double doublex4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void refine_mfma_kernel(const double* __restrict__ xb,
+                                                          const char* Wm, int64_t ldw, int V,
+                                                          int H, SelectWs w, int band_off, int n,
+                                                          int nblk) {
+  __shared__ double red[3][4][kRefMR];
+  // work-group order: the band groups of one vocabulary tile are consecutive
+  // on one XCD, so the tile's W rows are fetched from HBM about once
+  const int ng = (n + kRefMR - 1) / kRefMR;
+  const int total = ng * nblk;
+  const int per_xcd = (total + 7) / 8;
+  const int logical = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (logical >= total) return;
+  const int grp = logical % ng, vt = logical / ng;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, q = lane >> 4;
+  const int r0 = grp * kRefMR;
+  const int nr = (n - r0) < kRefMR ? (n - r0) : kRefMR;
+  const double* xr = xb + (int64_t)(r0 + (col < nr ? col : nr - 1)) * H + 8 * q;
+  const int vb = vt * kRefTile + wave * 64 + col;
+  const char* wr[4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+    const int v = vb + 16 * jb;
+    wr[jb] = Wm + (int64_t)(v < V ? v : V - 1) * ldw + 16 * q;
+  }
+  doublex4 acc[4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) acc[jb] = doublex4{0.0, 0.0, 0.0, 0.0};
+  // one step of 32 h; H is a multiple of 8, so a lane's 8 h are all inside
+  // or all past the row (then zeros)
+  uint4 wv[4];
+  double2 xv[4];
+  auto load = [&](int hs) {
+    const bool in = hs + 8 * q < H;
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+      wv[jb] = in ? *(const uint4*)(wr[jb] + (int64_t)hs * 2) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2)
+      xv[e2] = in ? *(const double2*)(xr + hs + 2 * e2) : make_double2(0.0, 0.0);
+  };
+  load(0);
+  for (int hs = 0; hs < H; hs += 32) {
+    const uint4 cw[4] = {wv[0], wv[1], wv[2], wv[3]};
+    const double2 cx[4] = {xv[0], xv[1], xv[2], xv[3]};
+    if (hs + 32 < H) load(hs + 32);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double a = (e & 1) ? cx[e >> 1].y : cx[e >> 1].x;
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        const uint32_t word = (e >> 1) == 0 ? cw[jb].x : (e >> 1) == 1 ? cw[jb].y
+                            : (e >> 1) == 2 ? cw[jb].z : cw[jb].w;
+        const double b = (double)__uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16));
+        acc[jb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[jb], 0, 0, 0);
+      }
+    }
+  }
+  // (m, s, u) of band row 4r + q over this lane's 4 vocabulary rows, then over
+  // the 16 lanes of the row (one per vocabulary column), then the 4 waves
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    double m = -INFINITY, sum = 0.0, uu = 0.0;
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+      if (vb + 16 * jb < V) m = fmax(m, acc[jb][r]);
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        if (vb + 16 * jb < V) {
+          const double d = acc[jb][r] - m, ex = exp(d);
+          sum += ex;
+          uu += ex * d;
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const double m2 = __shfl_xor(m, o), s2 = __shfl_xor(sum, o), v2 = __shfl_xor(uu, o);
+      msu_merge(m, sum, uu, m2, s2, v2);
+    }
+    if (col == 0) {
+      red[0][wave][4 * r + q] = m;
+      red[1][wave][4 * r + q] = sum;
+      red[2][wave][4 * r + q] = uu;
+    }
+  }
+  __syncthreads();
+  if (tid < kRefMR && tid < nr) {
+    double M = red[0][0][tid], Ssum = red[1][0][tid], U = red[2][0][tid];
+    for (int qq = 1; qq < 4; ++qq) msu_merge(M, Ssum, U, red[0][qq][tid], red[1][qq][tid], red[2][qq][tid]);
+    double* o = w.rpart + ((int64_t)(band_off + r0 + tid) * nblk + vt) * 3;
+    o[0] = M;
+    o[1] = Ssum;
+    o[2] = U;
+  }
+}
+
 hipError_t launch_refine(int f32, const char* X, int64_t ldx, const char* W, int64_t ldw, int V,
                          int H, const SelectWs& w, double* xb, int band_off, int band_n, int nblk,
                          hipStream_t st) {
@@ -318,8 +429,10 @@ hipError_t launch_refine(int f32, const char* X, int64_t ldx, const char* W, int
   } else {
     hipLaunchKernelGGL(band_rows_f64_kernel<__bf16>, dim3((unsigned)std::min<int64_t>(widen, 4096)),
                        dim3(256), 0, st, X, ldx, H, w.band, band_off, band_n, xb);
-    hipLaunchKernelGGL(refine_kernel<__bf16>, grid, dim3(256), 0, st, xb, W, ldw, V, H, w,
-                       band_off, band_n, nblk);
+    const int64_t nwm = ceil_div((int64_t)ceil_div(band_n, kRefMR) * nblk, 8) * 8;
+    if (nwm > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(refine_mfma_kernel, dim3((unsigned)nwm), dim3(256), 0, st, xb, W, ldw, V,
+                       H, w, band_off, band_n, nblk);
   }
   return hipGetLastError();
 }

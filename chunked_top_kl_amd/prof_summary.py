@@ -60,6 +60,7 @@ STEP_PATTERNS = [
     ("select_above", "select_above"),
     ("select_threshold", "select_threshold"),
     ("refine_kernel", "select_refine_fp64"),
+    ("refine_mfma_kernel", "select_refine_fp64"),
     ("band_rows_f64", "select_refine_fp64"),
     ("sample_refined_entropy", "select_refine_fp64"),
     ("select_final", "select_final"),
