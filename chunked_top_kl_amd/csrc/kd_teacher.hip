@@ -122,12 +122,23 @@ __global__ __launch_bounds__(256) void teacher_wnorm_kernel(const char* W, int64
   __shared__ double best[4];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   double m = 0.0;
+  // one wave per row, 16 bytes per lane per load (H is a multiple of 8, so
+  // a row is whole 16-byte granules)
+  constexpr int per = 16 / (int)sizeof(T);
+  const int ng = H / per;
   for (int v = blockIdx.x * 4 + wv; v < V; v += gridDim.x * 4) {
     const char* row = W + (int64_t)v * ldw;
     double ss = 0.0;
-    for (int h = lane; h < H; h += 64) {
-      const double x = elem_f64<T>(row, h);
-      ss = fma(x, x, ss);
+    for (int g = lane; g < ng; g += 64) {
+      const uint4 raw = *(const uint4*)(row + (int64_t)g * 16);
+      const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int e = 0; e < per; ++e) {
+        double x;
+        if constexpr (sizeof(T) == 2) x = (double)bf16_to_f32((uint16_t)(wd[e >> 1] >> ((e & 1) * 16)));
+        else x = (double)__uint_as_float(wd[e]);
+        ss = fma(x, x, ss);
+      }
     }
     for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
     m = fmax(m, ss);
