@@ -34,6 +34,11 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
+# The fp64 band refinement keeps its MFMA accumulators in VGPRs: with the
+# default form the compiler copies them between AGPRs and VGPRs on every step
+# of its loop. The selection kernels are the file's only MFMA users.
+FILE_FLAGS = {"kd_select.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -59,7 +64,7 @@ def build_library(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        jobs.append([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
+        jobs.append([hipcc, *HIP_FLAGS, *FILE_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
                      os.path.join(CSRC, src), "-o", obj])
     workers = min(len(jobs), max(1, (os.cpu_count() or 2)))
     with cf.ThreadPoolExecutor(max_workers=workers) as ex:

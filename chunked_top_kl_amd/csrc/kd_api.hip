@@ -931,8 +931,8 @@ int kd_position_signals(const kd_problem* p, const void* hidden, const void* W,
 }
 
 // fp64 entropies of the n positions list[0..n) into out[0..n): refinement
-// partials for at most kRefinePiece positions at a time, kRefineBatch rows
-// widened per launch
+// partials for at most kRefinePiece positions at a time; bf16 rows are read in
+// place, one launch per piece, fp32 rows widened kRefineBatch per launch
 static int refine_positions(const kd_problem* p, const Layout& L, void* ws, const void* hidden,
                             const void* W, kd::SelectWs w, const int32_t* list, int64_t n,
                             double* out, hipStream_t st) {
@@ -943,11 +943,12 @@ static int refine_positions(const kd_problem* p, const Layout& L, void* ws, cons
     const int np = (int)std::min<int64_t>(kRefinePiece, n - rs);
     kd::SelectWs wr = w;
     wr.band = const_cast<int32_t*>(list) + rs;
-    for (int o = 0; o < np; o += kRefineBatch) {
+    const int batch = f32 ? kRefineBatch : np;
+    for (int o = 0; o < np; o += batch) {
       Prof pr("select_refine_fp64", st);
       KD_HIP(kd::launch_refine(f32, (const char*)hidden, ld, (const char*)W, ld, (int)p->V,
-                               (int)p->H, wr, at<double>(ws, L.xb), o,
-                               std::min(kRefineBatch, np - o), nblk, st));
+                               (int)p->H, wr, at<double>(ws, L.xb), o, std::min(batch, np - o),
+                               nblk, st));
     }
     Prof pr("select_refine_fp64", st);
     KD_HIP(kd::launch_sample_refined_entropy(wr, np, nblk, out + rs, st));

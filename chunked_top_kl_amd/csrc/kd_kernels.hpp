@@ -274,6 +274,9 @@ hipError_t launch_sample_refined_entropy(const SelectWs& w, int n, int nblk, dou
 hipError_t launch_sample_final(const double* means, int64_t B, int64_t k, const SelectWs& w,
                                int n_band, int refined, uint8_t* mask, int32_t* idx_out,
                                hipStream_t st);
+// fp64 refinement partials of band rows [band_off, band_off + band_n) of w.band
+// (xb: fp32 rows widened there, at most kRefineBatch of them; bf16 rows are
+// read in place and xb is not used)
 hipError_t launch_refine(int f32, const char* X, int64_t ldx, const char* W, int64_t ldw, int V,
                          int H, const SelectWs& w, double* xb, int band_off, int band_n, int nblk,
                          hipStream_t st);

@@ -315,7 +315,7 @@ __global__ __launch_bounds__(256) void refine_kernel(const double* __restrict__ 
 constexpr int kRefMR = 16;   // band rows per work-group
 typedef double doublex4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void refine_mfma_kernel(const double* __restrict__ xb,
+__global__ __launch_bounds__(256) void refine_mfma_kernel(const char* X, int64_t ldx,
                                                           const char* Wm, int64_t ldw, int V,
                                                           int H, SelectWs w, int band_off, int n,
                                                           int nblk) {
@@ -332,7 +332,9 @@ __global__ __launch_bounds__(256) void refine_mfma_kernel(const double* __restri
   const int col = lane & 15, q = lane >> 4;
   const int r0 = grp * kRefMR;
   const int nr = (n - r0) < kRefMR ? (n - r0) : kRefMR;
-  const double* xr = xb + (int64_t)(r0 + (col < nr ? col : nr - 1)) * H + 8 * q;
+  // band rows past the end repeat the last one (their results are not kept)
+  const int brow = w.band[band_off + r0 + (col < nr ? col : nr - 1)];
+  const char* xr = X + (int64_t)brow * ldx + 16 * q;
   const int vb = vt * kRefTile + wave * 64 + col;
   const char* wr[4];
 #pragma unroll
@@ -343,35 +345,63 @@ __global__ __launch_bounds__(256) void refine_mfma_kernel(const double* __restri
   doublex4 acc[4];
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) acc[jb] = doublex4{0.0, 0.0, 0.0, 0.0};
-  // one step of 32 h; H is a multiple of 8, so a lane's 8 h are all inside
-  // or all past the row (then zeros)
-  uint4 wv[4];
-  double2 xv[4];
-  auto load = [&](int hs) {
-    const bool in = hs + 8 * q < H;
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
-      wv[jb] = in ? *(const uint4*)(wr[jb] + (int64_t)hs * 2) : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2)
-      xv[e2] = in ? *(const double2*)(xr + hs + 2 * e2) : make_double2(0.0, 0.0);
+  // steps of 32 h: lane quarter q takes h = hs + 8q .. hs + 8q + 7, and MFMA e
+  // of a step its element e (the same permutation of h on both operands)
+  auto widen = [](const uint4& c, int e) {
+    const uint32_t word = (e >> 1) == 0 ? c.x : (e >> 1) == 1 ? c.y : (e >> 1) == 2 ? c.z : c.w;
+    return (double)__uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16));
   };
-  load(0);
-  for (int hs = 0; hs < H; hs += 32) {
-    const uint4 cw[4] = {wv[0], wv[1], wv[2], wv[3]};
-    const double2 cx[4] = {xv[0], xv[1], xv[2], xv[3]};
-    if (hs + 32 < H) load(hs + 32);
+  auto step = [&](const uint4 (&cw)[4], const uint4& cx) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const double a = (e & 1) ? cx[e >> 1].y : cx[e >> 1].x;
+      const double a = widen(cx, e);
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb) {
-        const uint32_t word = (e >> 1) == 0 ? cw[jb].x : (e >> 1) == 1 ? cw[jb].y
-                            : (e >> 1) == 2 ? cw[jb].z : cw[jb].w;
-        const double b = (double)__uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16));
-        acc[jb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[jb], 0, 0, 0);
+        acc[jb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, widen(cw[jb], e), acc[jb], 0, 0, 0);
       }
     }
+  };
+  // full steps: every lane's 8 h lie inside the row, so the loads need no
+  // test. Two operand sets alternate: the next step's operands are loaded
+  // before this step's MFMAs (the last load of the loop reloads a step in
+  // bounds when there is no next one; it is not used)
+  const int hfull = H & ~31;
+  uint4 wa[4], wb[4], xa, xn;
+  auto load = [&](uint4 (&wv)[4], uint4& xv, int hs) {
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) wv[jb] = *(const uint4*)(wr[jb] + (int64_t)hs * 2);
+    xv = *(const uint4*)(xr + (int64_t)hs * 2);
+  };
+  {
+    // the first step's operands through a select, so that the loop-carried
+    // operands are not all plain loads (a PHI of loads would be folded into
+    // one load at the top of the loop, which then waits for it at once)
+    const bool in = hfull > 0;
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) wa[jb] = in ? *(const uint4*)wr[jb] : make_uint4(0u, 0u, 0u, 0u);
+    xa = in ? *(const uint4*)xr : make_uint4(0u, 0u, 0u, 0u);
+  }
+  int hs = 0;
+  // (the scheduling barriers keep each load ahead of the MFMAs it overlaps)
+  for (; hs + 64 <= hfull; hs += 64) {
+    load(wb, xn, hs + 32);
+    __builtin_amdgcn_sched_barrier(0);
+    step(wa, xa);
+    load(wa, xa, hs + 64 < hfull ? hs + 64 : hs);
+    __builtin_amdgcn_sched_barrier(0);
+    step(wb, xn);
+  }
+  if (hs < hfull) step(wa, xa);   // an odd number of full steps: the last one
+  if (hfull < H) {
+    // the last, partial step: H is a multiple of 8, so a lane's 8 h are all
+    // inside the row or all past it (then zeros)
+    const bool in = hfull + 8 * q < H;
+    uint4 tw[4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+      tw[jb] = in ? *(const uint4*)(wr[jb] + (int64_t)hfull * 2) : make_uint4(0u, 0u, 0u, 0u);
+    const uint4 tx = in ? *(const uint4*)(xr + (int64_t)hfull * 2) : make_uint4(0u, 0u, 0u, 0u);
+    step(tw, tx);
   }
   // (m, s, u) of band row 4r + q over this lane's 4 vocabulary rows, then over
   // the 16 lanes of the row (one per vocabulary column), then the 4 waves
@@ -427,12 +457,11 @@ hipError_t launch_refine(int f32, const char* X, int64_t ldx, const char* W, int
     hipLaunchKernelGGL(refine_kernel<float>, grid, dim3(256), 0, st, xb, W, ldw, V, H, w,
                        band_off, band_n, nblk);
   } else {
-    hipLaunchKernelGGL(band_rows_f64_kernel<__bf16>, dim3((unsigned)std::min<int64_t>(widen, 4096)),
-                       dim3(256), 0, st, X, ldx, H, w.band, band_off, band_n, xb);
+    // bf16 band rows are read in place (the fp64 widening is exact)
     const int64_t nwm = ceil_div((int64_t)ceil_div(band_n, kRefMR) * nblk, 8) * 8;
     if (nwm > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(refine_mfma_kernel, dim3((unsigned)nwm), dim3(256), 0, st, xb, W, ldw, V,
-                       H, w, band_off, band_n, nblk);
+    hipLaunchKernelGGL(refine_mfma_kernel, dim3((unsigned)nwm), dim3(256), 0, st, X, ldx, W, ldw,
+                       V, H, w, band_off, band_n, nblk);
   }
   return hipGetLastError();
 }
