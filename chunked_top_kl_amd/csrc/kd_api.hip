@@ -29,7 +29,8 @@ using kd::round_up;
 constexpr int kCostCUs = 256;
 constexpr int64_t kMaxK = 4096;
 constexpr int64_t kMaxRows = int64_t(1) << 30;
-constexpr double kSelectEps = 2e-5;    // bound on |fp32-path entropy - fp64 entropy| (nats)
+constexpr double kSelectEps = 2e-5;    // least bound on |fp32-path entropy - fp64 entropy| (nats)
+constexpr int kEpsProbe = 16;           // positions whose entropy error is measured per selection
 constexpr int64_t kDwDepth = 8192;     // tokens per dW contraction (a multiple of chunks)
 constexpr int kRefineBatch = 256;      // band rows widened to fp64 per refinement launch
 constexpr int kRefinePiece = 4096;     // band rows whose fp64 refinement partials are held at once
@@ -935,7 +936,8 @@ int kd_position_signals(const kd_problem* p, const void* hidden, const void* W,
 // place, one launch per piece, fp32 rows widened kRefineBatch per launch
 static int refine_positions(const kd_problem* p, const Layout& L, void* ws, const void* hidden,
                             const void* W, kd::SelectWs w, const int32_t* list, int64_t n,
-                            double* out, hipStream_t st) {
+                            double* out, hipStream_t st,
+                            const char* scope = "select_refine_fp64") {
   const int f32 = p->hw_dtype == KD_F32;
   const int64_t ld = p->H * L.esz;
   const int nblk = (int)refine_blocks(p->V);
@@ -945,14 +947,41 @@ static int refine_positions(const kd_problem* p, const Layout& L, void* ws, cons
     wr.band = const_cast<int32_t*>(list) + rs;
     const int batch = f32 ? kRefineBatch : np;
     for (int o = 0; o < np; o += batch) {
-      Prof pr("select_refine_fp64", st);
+      Prof pr(scope, st);
       KD_HIP(kd::launch_refine(f32, (const char*)hidden, ld, (const char*)W, ld, (int)p->V,
                                (int)p->H, wr, at<double>(ws, L.xb), o, std::min(batch, np - o),
                                nblk, st));
     }
-    Prof pr("select_refine_fp64", st);
+    Prof pr(scope, st);
     KD_HIP(kd::launch_sample_refined_entropy(wr, np, nblk, out + rs, st));
   }
+  return KD_OK;
+}
+
+// The bound eps on |entropy - fp64 entropy| that the selections' bands use:
+// kSelectEps, or four times the largest error measured on kEpsProbe positions
+// spread over [0, S) (their entropies recomputed in fp64) if that is larger,
+// so that entropies less accurate than kSelectEps assumes widen the band
+// instead of deciding the cut. Synchronises the host.
+static int select_eps(const kd_problem* p, const Layout& L, void* ws, const void* hidden,
+                      const void* W, const double* entropy, double* eps, hipStream_t st) {
+  *eps = kSelectEps;
+  const int n = (int)std::min<int64_t>(p->S, kEpsProbe);
+  if (n <= 0) return KD_OK;
+  int32_t* list = at<int32_t>(ws, L.spos);
+  double* ref = at<double>(ws, L.pent);
+  double* err = at<double>(ws, L.dscal) + 4;
+  KD_HIP(kd::launch_probe_list(list, n, p->S, st));
+  kd::SelectWs w;
+  std::memset(&w, 0, sizeof(w));
+  w.rpart = at<double>(ws, L.rpart);
+  int rc = refine_positions(p, L, ws, hidden, W, w, list, n, ref, st, "select_error_probe");
+  if (rc) return rc;
+  KD_HIP(kd::launch_max_abs_diff(entropy, list, n, ref, err, st));
+  double h = 0.0;
+  KD_HIP(hipMemcpyAsync(&h, err, sizeof(double), hipMemcpyDeviceToHost, st));
+  KD_HIP(hipStreamSynchronize(st));
+  if (4.0 * h > *eps) *eps = 4.0 * h;   // false for NaN
   return KD_OK;
 }
 
@@ -1044,7 +1073,9 @@ int kd_select_top_fraction_segments(const kd_problem* p, const void* hidden, con
   int32_t* nabove = nband + S;
   int32_t* boff = nband + 2 * S;
   int32_t* need = nband + 3 * S;
-  const double eps2 = 2.0 * kSelectEps;
+  double eps = kSelectEps;
+  if ((rc = select_eps(p, L, ws, hidden, W, entropy, &eps, st))) return rc;
+  const double eps2 = 2.0 * eps;
   {
     // the decision on the sweep's entropies, and each segment's k-th largest
     Prof pr("select_segments", st);
@@ -1132,9 +1163,11 @@ int kd_select_top_fraction(const kd_problem* p, const void* hidden, const void* 
   w.dscal = at<double>(ws, L.dscal);
   w.rpart = at<double>(ws, L.rpart);
   w.hist = nullptr;
+  double eps = kSelectEps;
+  if ((rc = select_eps(p, L, ws, hidden, W, entropy, &eps, st))) return rc;
   {
     Prof pr("select_threshold", st);
-    KD_HIP(kd::launch_select_threshold(entropy, S, k, kSelectEps, w, st));
+    KD_HIP(kd::launch_select_threshold(entropy, S, k, eps, w, st));
   }
   int32_t n_band = 0;
   KD_HIP(hipMemcpyAsync(&n_band, w.scal, sizeof(int32_t), hipMemcpyDeviceToHost, st));
@@ -1188,9 +1221,11 @@ int kd_select_samples(const kd_problem* p, const void* hidden, const void* W, co
     Prof pr("sample_means", st);
     KD_HIP(kd::launch_sample_means(entropy, offsets, B, means, st));
   }
+  double eps = kSelectEps;
+  if ((rc = select_eps(p, L, ws, hidden, W, entropy, &eps, st))) return rc;
   {
     Prof pr("select_threshold", st);
-    KD_HIP(kd::launch_select_threshold(means, B, k, kSelectEps, w, st));
+    KD_HIP(kd::launch_select_threshold(means, B, k, eps, w, st));
   }
   int32_t h[2] = {0, 0};
   KD_HIP(hipMemcpyAsync(h, w.scal, sizeof(h), hipMemcpyDeviceToHost, st));

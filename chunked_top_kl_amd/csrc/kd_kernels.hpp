@@ -280,6 +280,10 @@ hipError_t launch_sample_final(const double* means, int64_t B, int64_t k, const 
 hipError_t launch_refine(int f32, const char* X, int64_t ldx, const char* W, int64_t ldw, int V,
                          int H, const SelectWs& w, double* xb, int band_off, int band_n, int nblk,
                          hipStream_t st);
+// list[i] = floor(i*S/n), i < n; *out = max_i |E[list[i]] - ref[i]| (NaN terms skipped)
+hipError_t launch_probe_list(int32_t* list, int n, int64_t S, hipStream_t st);
+hipError_t launch_max_abs_diff(const double* E, const int32_t* list, int n, const double* ref,
+                               double* out, hipStream_t st);
 hipError_t launch_select_final(const double* entropy, int64_t S, int64_t k, const SelectWs& w,
                                int n_band, uint8_t* mask, int32_t* idx_out, hipStream_t st);
 

@@ -774,4 +774,41 @@ hipError_t launch_sample_final(const double* means, int64_t B, int64_t k, const 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Error probe: n positions spread evenly over [0, S) (list[i] = floor(i*S/n)),
+// and the largest |E[list[i]] - ref[i]| over them (NaN terms are skipped).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void probe_list_kernel(int32_t* list, int n, int64_t S) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) list[i] = (int32_t)(((int64_t)i * S) / n);
+}
+
+__global__ __launch_bounds__(256) void max_abs_diff_kernel(const double* E, const int32_t* list,
+                                                           int n, const double* ref, double* out) {
+  __shared__ double red[256];
+  const int tid = threadIdx.x;
+  double m = 0.0;
+  for (int i = tid; i < n; i += 256) m = fmax(m, fabs(E[list[i]] - ref[i]));
+  red[tid] = m;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] = fmax(red[tid], red[tid + o]);
+    __syncthreads();
+  }
+  if (tid == 0) *out = red[0];
+}
+
+hipError_t launch_probe_list(int32_t* list, int n, int64_t S, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(probe_list_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, list,
+                     n, S);
+  return hipGetLastError();
+}
+
+hipError_t launch_max_abs_diff(const double* E, const int32_t* list, int n, const double* ref,
+                               double* out, hipStream_t st) {
+  hipLaunchKernelGGL(max_abs_diff_kernel, dim3(1), dim3(256), 0, st, E, list, n, ref, out);
+  return hipGetLastError();
+}
+
 }  // namespace kd

@@ -63,6 +63,8 @@ STEP_PATTERNS = [
     ("refine_mfma_kernel", "select_refine_fp64"),
     ("band_rows_f64", "select_refine_fp64"),
     ("sample_refined_entropy", "select_refine_fp64"),
+    ("probe_list_kernel", "select_error_probe"),
+    ("max_abs_diff_kernel", "select_error_probe"),
     ("select_final", "select_final"),
     ("sample_mean_kernel", "sample_means"),
     ("sample_mark_kernel", "select_refine_fp64"),

@@ -244,11 +244,15 @@ int kd_student_entropy(const kd_problem* problem, const void* hidden, const void
  * on ties (SE-KD top-k% selection, Method section 2). Entropies within a band
  * around the cut are recomputed in fp64 from hidden and W before the decision
  * (the whole band, in pieces, whatever its size), so the kept set is the one
- * an fp64 evaluation gives. The band is +-2e-5 nats around the k-th largest
- * entropy: it assumes that kd_student_entropy's fp32-path values are within
- * 2e-5 nats of the fp64 entropies, which holds for logits |z| of order 10 or
- * less at H of a few thousand (the tests check it for unit-variance logits
- * and for logits of standard deviation 4).
+ * an fp64 evaluation gives. The band is +-2 eps around the k-th largest
+ * entropy, where eps bounds |entropy - fp64 entropy|: 2e-5 nats (which
+ * kd_student_entropy's fp32-path values meet for logits |z| of order 10 or
+ * less at H of a few thousand), or four times the largest such error measured
+ * on 16 positions spread evenly over [0, S) if that is larger (every call
+ * recomputes those 16 in fp64 first). Entropies less accurate than 2e-5 nats
+ * thus widen the band instead of deciding the cut. The tests check the kept
+ * set against the fp64 one for unit-variance logits, logits of standard
+ * deviation 4, and entropies given with errors of up to 1e-4 nats.
  *   entropy     [device] [S] float64 from kd_student_entropy (not modified)
  *   mask_out    [device] [S] uint8: 1 = kept
  *   idx_out     [device] [S] int32 or NULL: kept positions in ascending order
@@ -264,7 +268,8 @@ int kd_select_top_fraction(const kd_problem* problem, const void* hidden, const 
  * Knowledge Distillation", Method section 2, SE-KD3X sample axis: the top l% of
  * samples by mean student entropy from a frozen student's forward pass).
  * Sample b is positions [offsets[b], offsets[b+1]); an empty sample has mean
- * -inf. Samples whose mean lies within the entropy error bound of the cut have
+ * -inf. Samples whose mean lies within 2 eps of the cut (eps the entropy error
+ * bound of kd_select_top_fraction, measured the same way) have
  * their positions' entropies recomputed in fp64 from hidden and W before the
  * decision (each such position once, in pieces, whatever their number), so
  * the kept set is the one fp64 entropies give.
@@ -333,8 +338,8 @@ int kd_select_by_signal(const kd_problem* problem, const double* signal, const i
  * Knowledge Distillation", Method section 2, applied within each sequence of a
  * batch): segment b = positions [offsets[b], offsets[b+1]) keeps
  * floor(num*len_b/den) positions of highest entropy, lower index first on ties.
- * As in kd_select_top_fraction, the entries within the entropy error bound of
- * a segment's cut are recomputed in fp64 from hidden and W before the
+ * As in kd_select_top_fraction, the entries within 2 eps of a segment's cut
+ * (eps the same measured entropy error bound) are recomputed in fp64 from hidden and W before the
  * decision (every such entry, in pieces, whatever their number), so the kept
  * set is the one fp64 entropies give.
  *   entropy     [device] [S] float64 from kd_student_entropy (not modified)

@@ -319,6 +319,28 @@ def test_entropy_and_selection_with_large_logits(kd):
     assert np.array_equal(idx.cpu().numpy(), ridx)
 
 
+def test_selection_widens_the_band_for_less_accurate_entropies(kd):
+    # entropies given with errors of up to 1e-4 nats, five times the band's
+    # least bound: a band of +-4e-5 would leave positions on the wrong side
+    # of the cut, but the error measured on the probe positions widens it, so
+    # the kept set is still the fp64 oracle's
+    S, H, V = 3000, 128, 4001
+    p = make_problem(S, H, V, 4, seed=19, hidden_std=0.2)
+    hidden, W, _, _ = to_device(p)
+    ent = kd.kd_student_entropy(hidden, W)
+    noise = np.random.default_rng(20).uniform(-1e-4, 1e-4, size=S)
+    noisy = ent + torch.from_numpy(noise).cuda()
+    mask, idx, cnt = kd.kd_select_top_fraction(noisy, hidden, W, 20, 100)
+    ref_e = oracle_entropy(p.hidden, p.W, chunk=500)
+    rmask, ridx, rk = oracle_select_top_fraction(ref_e, 20, 100)
+    assert cnt == rk
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.array_equal(mask.cpu().numpy(), rmask)
+    # the noisy values alone decide differently
+    _, nidx, _ = oracle_select_top_fraction(ref_e + noise, 20, 100)
+    assert not np.array_equal(nidx, ridx)
+
+
 @pytest.mark.parametrize("case", ["spread", "crowded", "ties"])
 def test_selection_index_set_bit_exact(kd, case):
     S, H, V = 3000, 128, 4001

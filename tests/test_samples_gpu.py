@@ -3,7 +3,9 @@ the sample axis of SE-KD3X in "Rethinking Selective Knowledge Distillation",
 Method section 2) against the fp64 oracle: the kept samples bit for bit.
 
 Cases: samples of random lengths; crowded entropies (sample means closer than
-the fp32-path error, so the fp64 refinement of the band decides); duplicate
+the fp32-path error, so the fp64 refinement of the band decides); entropies
+given with errors beyond the band's least bound (the measured error widens
+it); duplicate
 samples (exact ties, lower index first); empty samples and the kept-count
 edges; malformed offsets rejected.
 """
@@ -79,6 +81,28 @@ def test_band_of_many_samples_and_positions(kd):
     # a refinement launch and an entropy launch per piece of 4096 positions
     # (bf16 rows): more than 65536 positions were refined
     assert steps["select_refine_fp64"][0] > 2 * (65536 // 4096)
+
+
+def test_samples_with_less_accurate_entropies(kd):
+    # entropies given with errors of up to 1e-4 nats (beyond the band's least
+    # bound of 2e-5), samples of 5 positions: the measured error widens the
+    # band over the means and the kept samples are still the fp64 ones
+    S = 600 * 5
+    off = (np.arange(601, dtype=np.int64) * S) // 600
+    p = make_problem(S, 128, 4001, 4, seed=23, hidden_std=0.2)
+    hidden, W, _, _ = to_device(p)
+    ent = kd.kd_student_entropy(hidden, W)
+    noise = np.random.default_rng(24).uniform(-1e-4, 1e-4, size=S)
+    noisy = ent + torch.from_numpy(noise).cuda()
+    mask, idx, cnt = kd.kd_select_samples(noisy, torch.from_numpy(off).cuda(), hidden, W, 20, 100)
+    torch.cuda.synchronize()
+    ref_e = oracle_entropy(p.hidden, p.W, chunk=500)
+    rmask, ridx, rk, _ = oracle_select_samples(ref_e, off, 20, 100)
+    assert cnt == rk
+    assert np.array_equal(mask.cpu().numpy(), rmask)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    _, nidx, _, _ = oracle_select_samples(ref_e + noise, off, 20, 100)
+    assert not np.array_equal(nidx, ridx)
 
 
 def test_duplicate_samples_tie_to_lower_index(kd):

@@ -244,6 +244,31 @@ def test_per_sequence_entropy_selection(kd, case):
         assert "select_refine_fp64" in steps
 
 
+def test_per_sequence_selection_with_less_accurate_entropies(kd):
+    """Per-sequence SE-KD on entropies given with errors of up to 1e-4 nats,
+    five times the band's least bound: the error measured on the probe
+    positions widens every segment's band, so the kept set is still the fp64
+    oracle's (a band of +-4e-5 would leave positions on the wrong side)."""
+    from oracle import oracle_entropy
+    S = 3000
+    off = (np.arange(7, dtype=np.int64) * S) // 6
+    p = make_problem(S, 128, 4001, 4, seed=21, hidden_std=0.2)
+    hidden, W, _, _ = to_device(p)
+    ent = kd.kd_student_entropy(hidden, W)
+    noise = np.random.default_rng(22).uniform(-1e-4, 1e-4, size=S)
+    noisy = ent + torch.from_numpy(noise).cuda()
+    mask, idx, cnt = kd.kd_select_top_fraction_segments(noisy, torch.from_numpy(off).cuda(), hidden,
+                                                        W, 20, 100)
+    torch.cuda.synchronize()
+    ref_e = oracle_entropy(p.hidden, p.W, chunk=500)
+    rmask, ridx, rc, _ = oracle_select_by_signal(ref_e, off, 20, 100)
+    assert cnt == rc
+    assert np.array_equal(mask.cpu().numpy(), rmask)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    _, nidx, _, _ = oracle_select_by_signal(ref_e + noise, off, 20, 100)
+    assert not np.array_equal(nidx, ridx)
+
+
 def test_per_sequence_selection_band_above_65536_positions(kd):
     """Per-sequence SE-KD where the straddling bands of all segments hold more
     than 65536 positions in all: every one is refined in fp64 (in pieces) and
