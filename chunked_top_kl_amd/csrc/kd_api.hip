@@ -192,16 +192,16 @@ Layout plan(const kd_problem* p) {
   L.em = take(pe * 4);
   L.es = take(pe * 8);
   L.eu = take(pe * 8);
-  L.band = take(Sx * 4);
-  L.refined = take(Sx * 8);
+  L.band = take((Sx + kEpsProbe) * 4);     // band list, then the error probe's positions
+  L.refined = take((Sx + kEpsProbe) * 8);
   L.scal = take(16 * 4);
   L.dscal = take(16 * 8);
   L.rpart = take((size_t)kRefinePiece * refine_blocks(V) * 3 * 8);
   L.xb = take((size_t)kRefineBatch * H * 8);
   L.counters = take(4 * 8);
   L.smean = take(Sx * 8);
-  L.spos = take(Sx * 4);
-  L.pent = take(Sx * 8);
+  L.spos = take((Sx + kEpsProbe) * 4);
+  L.pent = take((Sx + kEpsProbe) * 8);
   L.lse64 = take(Sx * 8);
   L.segw = take(Sx * 4 * 4);
   L.total = off;
@@ -958,31 +958,42 @@ static int refine_positions(const kd_problem* p, const Layout& L, void* ws, cons
   return KD_OK;
 }
 
-// The bound eps on |entropy - fp64 entropy| that the selections' bands use:
-// kSelectEps, or four times the largest error measured on kEpsProbe positions
-// spread over [0, S) (their entropies recomputed in fp64) if that is larger,
-// so that entropies less accurate than kSelectEps assumes widen the band
-// instead of deciding the cut. Synchronises the host.
-static int select_eps(const kd_problem* p, const Layout& L, void* ws, const void* hidden,
-                      const void* W, const double* entropy, double* eps, hipStream_t st) {
-  *eps = kSelectEps;
-  const int n = (int)std::min<int64_t>(p->S, kEpsProbe);
-  if (n <= 0) return KD_OK;
-  int32_t* list = at<int32_t>(ws, L.spos);
-  double* ref = at<double>(ws, L.pent);
+// The bound eps on |entropy - fp64 entropy| that the selections' bands use is
+// kSelectEps, or four times the largest error measured on the positions that
+// a selection refines in fp64 if that is larger: its band (computed first
+// with kSelectEps) and kEpsProbe positions spread evenly over [0, S), which
+// ride along in the same refinement. A selection whose measured bound exceeds
+// kSelectEps is redone once with the wider band, so that entropies less
+// accurate than kSelectEps assumes widen the band instead of deciding the cut.
+//
+// refine_and_measure: the fp64 entropies of list[0..n) into out[0..n); with
+// probe set, the probe positions are appended (list[n..], out[n..]: the arrays
+// hold S + kEpsProbe entries) and *h is the largest |entropy - fp64 entropy|
+// over all of them (NaN terms skipped). Synchronises the host when probing.
+static int refine_and_measure(const kd_problem* p, const Layout& L, void* ws, const void* hidden,
+                              const void* W, const kd::SelectWs& w, int32_t* list, int64_t n,
+                              double* out, const double* entropy, bool probe, double* h,
+                              hipStream_t st) {
+  *h = 0.0;
+  const int64_t np = probe ? std::min<int64_t>(p->S, kEpsProbe) : 0;
+  if (np > 0) KD_HIP(kd::launch_probe_list(list + n, (int)np, p->S, st));
+  if (n + np == 0) return KD_OK;
+  // a refinement of the probe positions alone is profiled on its own
+  int rc = refine_positions(p, L, ws, hidden, W, w, list, n + np, out, st,
+                            n > 0 ? "select_refine_fp64" : "select_error_probe");
+  if (rc || !probe) return rc;
   double* err = at<double>(ws, L.dscal) + 4;
-  KD_HIP(kd::launch_probe_list(list, n, p->S, st));
-  kd::SelectWs w;
-  std::memset(&w, 0, sizeof(w));
-  w.rpart = at<double>(ws, L.rpart);
-  int rc = refine_positions(p, L, ws, hidden, W, w, list, n, ref, st, "select_error_probe");
-  if (rc) return rc;
-  KD_HIP(kd::launch_max_abs_diff(entropy, list, n, ref, err, st));
-  double h = 0.0;
-  KD_HIP(hipMemcpyAsync(&h, err, sizeof(double), hipMemcpyDeviceToHost, st));
+  KD_HIP(kd::launch_max_abs_diff(entropy, list, (int)(n + np), out, err, st));
+  KD_HIP(hipMemcpyAsync(h, err, sizeof(double), hipMemcpyDeviceToHost, st));
   KD_HIP(hipStreamSynchronize(st));
-  if (4.0 * h > *eps) *eps = 4.0 * h;   // false for NaN
   return KD_OK;
+}
+
+// the wider bound when the measured error h calls for it (false for NaN)
+static bool widen_eps(double h, double* eps) {
+  if (!(4.0 * h > *eps)) return false;
+  *eps = 4.0 * h;
+  return true;
 }
 
 // ------------------------------------------------------------------ selection by a signal
@@ -1073,47 +1084,56 @@ int kd_select_top_fraction_segments(const kd_problem* p, const void* hidden, con
   int32_t* nabove = nband + S;
   int32_t* boff = nband + 2 * S;
   int32_t* need = nband + 3 * S;
-  double eps = kSelectEps;
-  if ((rc = select_eps(p, L, ws, hidden, W, entropy, &eps, st))) return rc;
-  const double eps2 = 2.0 * eps;
-  {
-    // the decision on the sweep's entropies, and each segment's k-th largest
-    Prof pr("select_segments", st);
-    KD_HIP(kd::launch_select_segments(entropy, offsets, B, S, num, den, mask_out, thr, st));
-    KD_HIP(kd::launch_seg_band_count(entropy, offsets, B, thr, eps2, nband, nabove, st));
-  }
+  int32_t* plist = at<int32_t>(ws, L.spos);
+  double* pent = at<double>(ws, L.pent);
+  kd::SelectWs w;
+  std::memset(&w, 0, sizeof(w));
+  w.rpart = at<double>(ws, L.rpart);
   std::vector<int32_t> hb((size_t)B), ha((size_t)B), ho((size_t)B), hn((size_t)B);
   std::vector<int64_t> hoff((size_t)B + 1);
-  KD_HIP(hipMemcpyAsync(hb.data(), nband, (size_t)B * 4, hipMemcpyDeviceToHost, st));
-  KD_HIP(hipMemcpyAsync(ha.data(), nabove, (size_t)B * 4, hipMemcpyDeviceToHost, st));
-  KD_HIP(hipMemcpyAsync(hoff.data(), offsets, (size_t)(B + 1) * 8, hipMemcpyDeviceToHost, st));
-  KD_HIP(hipStreamSynchronize(st));
-  // segments whose band straddles the cut are refined (segments are disjoint,
-  // so their bands list at most S positions); the others keep the decision on
-  // the sweep's entropies, which no band position can change
-  int64_t total = 0;
-  for (int64_t b = 0; b < B; ++b) {
-    const int64_t k = (num * (hoff[b + 1] - hoff[b])) / den;
-    const int64_t nd = k - ha[b];
-    hn[b] = (int32_t)nd;
-    ho[b] = -1;
-    if (nd > 0 && nd < hb[b]) {
-      ho[b] = (int32_t)total;
-      total += hb[b];
+  double eps = kSelectEps;
+  for (int pass = 0; pass < 2; ++pass) {
+    const double eps2 = 2.0 * eps;
+    {
+      // the decision on the sweep's entropies, and each segment's k-th largest
+      Prof pr("select_segments", st);
+      KD_HIP(kd::launch_select_segments(entropy, offsets, B, S, num, den, mask_out, thr, st));
+      KD_HIP(kd::launch_seg_band_count(entropy, offsets, B, thr, eps2, nband, nabove, st));
     }
-  }
-  if (total > 0) {
-    KD_HIP(hipMemcpyAsync(boff, ho.data(), (size_t)B * 4, hipMemcpyHostToDevice, st));
-    KD_HIP(hipMemcpyAsync(need, hn.data(), (size_t)B * 4, hipMemcpyHostToDevice, st));
-    int32_t* plist = at<int32_t>(ws, L.spos);
-    double* pent = at<double>(ws, L.pent);
-    KD_HIP(kd::launch_seg_band_list(entropy, offsets, B, thr, eps2, boff, plist, st));
-    kd::SelectWs w;
-    std::memset(&w, 0, sizeof(w));
-    w.rpart = at<double>(ws, L.rpart);
-    if ((rc = refine_positions(p, L, ws, hidden, W, w, plist, total, pent, st))) return rc;
-    Prof pr("select_segments_final", st);
-    KD_HIP(kd::launch_seg_band_final(B, boff, nband, need, plist, pent, mask_out, st));
+    KD_HIP(hipMemcpyAsync(hb.data(), nband, (size_t)B * 4, hipMemcpyDeviceToHost, st));
+    KD_HIP(hipMemcpyAsync(ha.data(), nabove, (size_t)B * 4, hipMemcpyDeviceToHost, st));
+    KD_HIP(hipMemcpyAsync(hoff.data(), offsets, (size_t)(B + 1) * 8, hipMemcpyDeviceToHost, st));
+    KD_HIP(hipStreamSynchronize(st));
+    // segments whose band straddles the cut are refined (segments are
+    // disjoint, so their bands list at most S positions); the others keep the
+    // decision on the sweep's entropies, which no band position can change
+    int64_t total = 0;
+    for (int64_t b = 0; b < B; ++b) {
+      const int64_t k = (num * (hoff[b + 1] - hoff[b])) / den;
+      const int64_t nd = k - ha[b];
+      hn[b] = (int32_t)nd;
+      ho[b] = -1;
+      if (nd > 0 && nd < hb[b]) {
+        ho[b] = (int32_t)total;
+        total += hb[b];
+      }
+    }
+    if (total > 0) {
+      KD_HIP(hipMemcpyAsync(boff, ho.data(), (size_t)B * 4, hipMemcpyHostToDevice, st));
+      KD_HIP(hipMemcpyAsync(need, hn.data(), (size_t)B * 4, hipMemcpyHostToDevice, st));
+      KD_HIP(kd::launch_seg_band_list(entropy, offsets, B, thr, eps2, boff, plist, st));
+    }
+    // the first pass measures the error on the band and the probe positions
+    double h = 0.0;
+    if ((rc = refine_and_measure(p, L, ws, hidden, W, w, plist, total, pent, entropy, pass == 0,
+                                 &h, st)))
+      return rc;
+    if (pass == 0 && widen_eps(h, &eps)) continue;
+    if (total > 0) {
+      Prof pr("select_segments_final", st);
+      KD_HIP(kd::launch_seg_band_final(B, boff, nband, need, plist, pent, mask_out, st));
+    }
+    break;
   }
   return compact_mask(L, ws, S, mask_out, idx_out, count_out, st);
 }
@@ -1164,16 +1184,23 @@ int kd_select_top_fraction(const kd_problem* p, const void* hidden, const void* 
   w.rpart = at<double>(ws, L.rpart);
   w.hist = nullptr;
   double eps = kSelectEps;
-  if ((rc = select_eps(p, L, ws, hidden, W, entropy, &eps, st))) return rc;
-  {
-    Prof pr("select_threshold", st);
-    KD_HIP(kd::launch_select_threshold(entropy, S, k, eps, w, st));
-  }
   int32_t n_band = 0;
-  KD_HIP(hipMemcpyAsync(&n_band, w.scal, sizeof(int32_t), hipMemcpyDeviceToHost, st));
-  KD_HIP(hipStreamSynchronize(st));
-  // every band row is recomputed in fp64, in pieces, whatever the band's size
-  if ((rc = refine_positions(p, L, ws, hidden, W, w, w.band, n_band, w.refined, st))) return rc;
+  for (int pass = 0; pass < 2; ++pass) {
+    {
+      Prof pr("select_threshold", st);
+      KD_HIP(kd::launch_select_threshold(entropy, S, k, eps, w, st));
+    }
+    KD_HIP(hipMemcpyAsync(&n_band, w.scal, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+    KD_HIP(hipStreamSynchronize(st));
+    // every band row is recomputed in fp64, in pieces, whatever the band's
+    // size; the first pass also measures the error (band and probe positions)
+    double h = 0.0;
+    if ((rc = refine_and_measure(p, L, ws, hidden, W, w, w.band, n_band, w.refined, entropy,
+                                 pass == 0, &h, st)))
+      return rc;
+    if (pass == 0 && widen_eps(h, &eps)) continue;
+    break;
+  }
   {
     Prof pr("select_final", st);
     KD_HIP(kd::launch_select_final(entropy, S, k, w, n_band, mask_out, idx_out, st));
@@ -1221,37 +1248,44 @@ int kd_select_samples(const kd_problem* p, const void* hidden, const void* W, co
     Prof pr("sample_means", st);
     KD_HIP(kd::launch_sample_means(entropy, offsets, B, means, st));
   }
+  const int64_t S = p->S;
+  uint8_t* pflag = at<uint8_t>(ws, L.segw);
+  int32_t* plist = at<int32_t>(ws, L.spos);
+  int32_t* ppos = at<int32_t>(ws, L.pos);
+  double* pent = at<double>(ws, L.pent);
+  int32_t* cnt_dev = at<int32_t>(ws, L.count);
   double eps = kSelectEps;
-  if ((rc = select_eps(p, L, ws, hidden, W, entropy, &eps, st))) return rc;
-  {
-    Prof pr("select_threshold", st);
-    KD_HIP(kd::launch_select_threshold(means, B, k, eps, w, st));
-  }
-  int32_t h[2] = {0, 0};
-  KD_HIP(hipMemcpyAsync(h, w.scal, sizeof(h), hipMemcpyDeviceToHost, st));
-  KD_HIP(hipStreamSynchronize(st));
-  const int n_band = h[0], n_above = h[1];
-  const int64_t need = k - n_above;
-  int refined = 0;
-  // the band straddles the cut: the entropies of every position of its
-  // samples are recomputed in fp64 (each position once, whatever the band's
-  // size or the samples' overlap) and the band is ranked on fp64 means
-  if (need > 0 && need < n_band) {
-    const int64_t S = p->S;
-    uint8_t* flag = at<uint8_t>(ws, L.segw);
-    int32_t* plist = at<int32_t>(ws, L.spos);
-    int32_t* ppos = at<int32_t>(ws, L.pos);
-    double* pent = at<double>(ws, L.pent);
-    int32_t* cnt_dev = at<int32_t>(ws, L.count);
-    KD_HIP(kd::launch_fill_u8(flag, 0, S, st));
-    KD_HIP(kd::launch_sample_mark(offsets, w, n_band, flag, st));
-    KD_HIP(kd::launch_compact(flag, nullptr, S, plist, ppos, cnt_dev, st));
-    int32_t total = 0;
-    KD_HIP(hipMemcpyAsync(&total, cnt_dev, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  int n_band = 0, refined = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    {
+      Prof pr("select_threshold", st);
+      KD_HIP(kd::launch_select_threshold(means, B, k, eps, w, st));
+    }
+    int32_t hs[2] = {0, 0};
+    KD_HIP(hipMemcpyAsync(hs, w.scal, sizeof(hs), hipMemcpyDeviceToHost, st));
     KD_HIP(hipStreamSynchronize(st));
-    if ((rc = refine_positions(p, L, ws, hidden, W, w, plist, total, pent, st))) return rc;
-    KD_HIP(kd::launch_sample_band_means(offsets, w, n_band, ppos, pent, st));
-    refined = 1;
+    n_band = hs[0];
+    const int64_t need = k - hs[1];
+    // the band straddles the cut: the entropies of every position of its
+    // samples are recomputed in fp64 (each position once, whatever the band's
+    // size or the samples' overlap) and the band is ranked on fp64 means
+    refined = need > 0 && need < n_band;
+    int32_t total = 0;
+    if (refined) {
+      KD_HIP(kd::launch_fill_u8(pflag, 0, S, st));
+      KD_HIP(kd::launch_sample_mark(offsets, w, n_band, pflag, st));
+      KD_HIP(kd::launch_compact(pflag, nullptr, S, plist, ppos, cnt_dev, st));
+      KD_HIP(hipMemcpyAsync(&total, cnt_dev, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+      KD_HIP(hipStreamSynchronize(st));
+    }
+    // the first pass also measures the error (those positions and the probe)
+    double herr = 0.0;
+    if ((rc = refine_and_measure(p, L, ws, hidden, W, w, plist, total, pent, entropy, pass == 0,
+                                 &herr, st)))
+      return rc;
+    if (pass == 0 && widen_eps(herr, &eps)) continue;
+    if (refined) KD_HIP(kd::launch_sample_band_means(offsets, w, n_band, ppos, pent, st));
+    break;
   }
   {
     Prof pr("sample_final", st);

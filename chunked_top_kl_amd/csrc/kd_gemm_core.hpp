@@ -67,7 +67,12 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc_uniform(const void* p, int64_
                                            n, 0x00020000);
 }
 
-// 16 bytes per lane from rs at voff into LDS at m0 + 16 * lane.
+// 16 bytes per lane from rs at voff into LDS at m0 + 16 * lane. M0 is written
+// and consumed inside the one asm statement. The compiler warns that it does
+// not preserve a reserved register named as a clobber; no code it generates
+// for these kernels reads M0 (no indirect register indexing, no LDS-DMA
+// builtins, no messages), which the generated assembly shows: its only M0
+// references are the writes of this statement.
 __device__ __forceinline__ void dma16(uint32_t m0, uint32_t voff, __amdgpu_buffer_rsrc_t rs) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(m0), "v"(voff), "s"(rs) : "memory", "m0");

@@ -248,9 +248,11 @@ int kd_student_entropy(const kd_problem* problem, const void* hidden, const void
  * entropy, where eps bounds |entropy - fp64 entropy|: 2e-5 nats (which
  * kd_student_entropy's fp32-path values meet for logits |z| of order 10 or
  * less at H of a few thousand), or four times the largest such error measured
- * on 16 positions spread evenly over [0, S) if that is larger (every call
- * recomputes those 16 in fp64 first). Entropies less accurate than 2e-5 nats
- * thus widen the band instead of deciding the cut. The tests check the kept
+ * on the positions the call recomputes in fp64 if that is larger: its band
+ * (taken first with 2e-5 nats) and 16 positions spread evenly over [0, S),
+ * refined together; a call whose measured bound exceeds 2e-5 nats is redone
+ * once with the wider band. Entropies less accurate than 2e-5 nats thus widen
+ * the band instead of deciding the cut. The tests check the kept
  * set against the fp64 one for unit-variance logits, logits of standard
  * deviation 4, and entropies given with errors of up to 1e-4 nats.
  *   entropy     [device] [S] float64 from kd_student_entropy (not modified)
