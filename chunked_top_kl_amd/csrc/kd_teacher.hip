@@ -189,10 +189,15 @@ __device__ inline double logit_bound(int H, double hn, double wmax) {
 // from per-row LDS histograms.
 // ---------------------------------------------------------------------------
 constexpr int kThrRows = 16;
+// a row's histogram is 257 words apart from the next, so the same bin of the
+// 16 rows (the rows of a row block hold similar values, and pass 0 puts most
+// of them in one or two bins) falls in 16 different LDS banks
+constexpr int kThrHist = 257;
+constexpr int kThrVals = 64;   // group maxima per thread: the pilot has at most 16 * 64 groups
 
 template <typename T>
 __global__ __launch_bounds__(256) void teacher_threshold_kernel(TeacherArgs a, int32_t* nbig) {
-  __shared__ uint32_t hist[kThrRows][256];
+  __shared__ uint32_t hist[kThrRows][kThrHist];
   __shared__ uint32_t prefix[kThrRows];
   __shared__ int krem[kThrRows];
   __shared__ double nrm[16][kThrRows];
@@ -215,30 +220,64 @@ __global__ __launch_bounds__(256) void teacher_threshold_kernel(TeacherArgs a, i
     prefix[tid] = 0u;
     krem[tid] = a.K;
   }
+  // the thread's group maxima as order-preserving keys, read once
+  uint32_t key[kThrVals];
+#pragma unroll
+  for (int u = 0; u < kThrVals; ++u) {
+    const int g = sub + 16 * u;
+    key[u] = (live && g < a.P) ? fkey(a.zp[(int64_t)g * a.ldp + r]) : 0u;
+  }
+  const int lane = tid & 63, wv = tid >> 6;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     const uint32_t hmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
     __syncthreads();
-    for (int q = tid; q < kThrRows * 256; q += 256) (&hist[0][0])[q] = 0u;
+    for (int q = tid; q < kThrRows * kThrHist; q += 256) (&hist[0][0])[q] = 0u;
     __syncthreads();
     if (live) {
       const uint32_t pre = prefix[row];
-      for (int g = sub; g < a.P; g += 16) {
-        const uint32_t key = fkey(a.zp[(int64_t)g * a.ldp + r]);
-        if ((key & hmask) == pre) atomicAdd(&hist[row][(key >> shift) & 255u], 1u);
-      }
+#pragma unroll
+      for (int u = 0; u < kThrVals; ++u)
+        if (sub + 16 * u < a.P && (key[u] & hmask) == pre)
+          atomicAdd(&hist[row][(key[u] >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid < kThrRows && r0 + tid < a.rows) {
-      int k = krem[tid];
-      int d = 255;
-      for (; d > 0; --d) {
-        const int c = (int)hist[tid][d];
-        if (c >= k) break;
-        k -= c;
+    // each row's digit: the largest d whose bins d..255 hold at least krem
+    // keys (0 if none do), and krem less the keys above d. Wave wv takes rows
+    // 4wv .. 4wv + 3; lane l holds bins 255 - 4l .. 252 - 4l, and a scan over
+    // the lanes gives the keys above them, so the one lane whose bins hold
+    // the crossing sets the row's digit.
+    for (int rr = 0; rr < 4; ++rr) {
+      const int q = wv * 4 + rr;
+      if (r0 + q >= a.rows) break;   // the same on every lane of the wave
+      const int k = krem[q];
+      int c[4], sum = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = (int)hist[q][255 - 4 * lane - j];
+        sum += c[j];
       }
-      prefix[tid] |= (uint32_t)d << shift;
-      krem[tid] = k;
+      int incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      int above = incl - sum;
+      if (above < k) {
+        int d = -1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int dd = 255 - 4 * lane - j;
+          if (d >= 0) continue;
+          if (above + c[j] >= k || dd == 0) d = dd;
+          else above += c[j];
+        }
+        if (d >= 0) {
+          prefix[q] |= (uint32_t)d << shift;
+          krem[q] = k - above;
+        }
+      }
     }
   }
   __syncthreads();
@@ -272,17 +311,29 @@ __device__ inline void write_entry(const TeacherArgs& a, int r, int rank, int id
 // ---------------------------------------------------------------------------
 constexpr int kRegCand = 16;
 
-__device__ inline void radix_step(uint32_t* hist, uint32_t* s_prefix, int* s_krem, int shift) {
-  if (threadIdx.x == 0) {
-    int k = *s_krem;
-    int d = 255;
-    for (; d > 0; --d) {
-      const int c = (int)hist[d];
-      if (c >= k) break;
-      k -= c;
-    }
+__device__ inline void radix_step(const uint32_t* hist, uint32_t* s_prefix, int* s_krem, int shift,
+                                  int* s_wsum) {
+  // the largest d whose bins d..255 hold at least krem keys (0 if none do),
+  // and krem less the keys above d: thread t holds bin 255 - t, and a scan
+  // over the threads gives the keys above it, so the one thread whose bin
+  // holds the crossing sets the digit. All threads call it.
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int d = 255 - t;
+  const int c = (int)hist[d];
+  const int k = *s_krem;
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) s_wsum[wv] = incl;
+  __syncthreads();
+  for (int q = 0; q < wv; ++q) incl += s_wsum[q];
+  const int above = incl - c;
+  if (above < k && (incl >= k || d == 0)) {
     *s_prefix |= (uint32_t)d << shift;
-    *s_krem = k;
+    *s_krem = k - above;
   }
 }
 
@@ -291,7 +342,7 @@ __global__ __launch_bounds__(256) void teacher_final_kernel(TeacherArgs a, int32
                                                             int32_t* nbig, float* tau2_out) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t s_prefix;
-  __shared__ int s_krem, s_m;
+  __shared__ int s_krem, s_m, s_wsum[4];
   __shared__ int lid[kBandLds];
   __shared__ double lz[kBandLds];
   const int tid = threadIdx.x;
@@ -331,7 +382,7 @@ __global__ __launch_bounds__(256) void teacher_final_kernel(TeacherArgs a, int32
         }
       }
       __syncthreads();
-      radix_step(hist, &s_prefix, &s_krem, shift);
+      radix_step(hist, &s_prefix, &s_krem, shift, s_wsum);
     }
     __syncthreads();
     const float tau2 = funkey(s_prefix);
