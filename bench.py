@@ -412,7 +412,9 @@ def selection_leg(kd, torch, wl, t, steps=3, warmup=1, n_seq=32, seed=77):
                sample_select_ms=round(t_smp, 3), samples_kept=int(k_smp),
                threshold_ms=round(t_thr, 3), threshold_kept=int(k_thr),
                teacher_sample_ms=round(t_tsm, 3),
-               teacher_sample_tflops=round(2 * 2.0 * S * H * V / (t_tsm / 1000.0) / 1e12, 1),
+               # one projection sweep counted (the mass sweep); the draw pass
+               # recomputes only the drawn-in tiles and is not counted
+               teacher_sample_tflops=round(2.0 * S * H * V / (t_tsm / 1000.0) / 1e12, 1),
                teacher_sample_ids_in_range=bool(int(sids.min()) >= 0 and int(sids.max()) < V),
                kernels=kernels)
     log(f"[bench] selection leg: signals {t_sig:.2f} ms, per-sequence SE-KD {t_seq:.2f} ms, "

@@ -71,11 +71,12 @@ struct Prof {
     if (!g_prof_on.load(std::memory_order_relaxed)) return;
     a = pool_event();
     b = pool_event();
-    if (a && b) hipEventRecord(a, st);
+    // a scope whose events cannot be recorded is not kept
+    if (a && b && hipEventRecord(a, st) != hipSuccess) a = nullptr;
   }
   ~Prof() {
     if (!a || !b) return;
-    hipEventRecord(b, st);
+    if (hipEventRecord(b, st) != hipSuccess) return;
     std::lock_guard<std::mutex> g(g_prof_mu);
     g_prof_recs.push_back({name, a, b});
   }
@@ -1457,8 +1458,8 @@ int kd_teacher_topk(const kd_problem* p, const void* hidden, const void* W, int3
 
 // ------------------------------------------------------------------ sampled teacher targets
 struct SampleLayout {
-  int64_t C, ldm, nu;   // rows per chunk, unit-mass pitch, 128-entry units
-  size_t flag, mass, scale, rowmax, dunit, dres, total;
+  int64_t C, ldm, nu, nvt;   // rows per chunk, unit-mass pitch, 128-entry units, 256-entry tiles
+  size_t flag, mass, scale, rowmax, dunit, dres, tcnt, toff, tfill, tlist, total;
 };
 
 SampleLayout plan_sample(const kd_problem* p) {
@@ -1467,6 +1468,7 @@ SampleLayout plan_sample(const kd_problem* p) {
   L.C = std::min<int64_t>(p->chunk, S);
   L.ldm = kd::round_up(L.C, 64);
   L.nu = kd::ceil_div(p->V, 128);
+  L.nvt = kd::ceil_div(p->V, 256);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -1479,6 +1481,12 @@ SampleLayout plan_sample(const kd_problem* p) {
   L.rowmax = take((size_t)L.C * 4);
   L.dunit = take((size_t)L.C * N * 4);
   L.dres = take((size_t)L.C * N * 8);
+  // the draw pass's rows per drawn-in tile: a row is listed once per tile,
+  // at most min(N, tiles) times
+  L.tcnt = take((size_t)L.nvt * 4);
+  L.toff = take((size_t)L.nvt * 4);
+  L.tfill = take((size_t)L.nvt * 4);
+  L.tlist = take((size_t)L.C * std::min<int64_t>(N, L.nvt) * 4);
   L.total = off;
   return L;
 }
@@ -1514,6 +1522,10 @@ int kd_teacher_sample(const kd_problem* p, const void* hidden, const void* W,
   float* rowmax = at<float>(ws, L.rowmax);
   int32_t* dunit = at<int32_t>(ws, L.dunit);
   double* dres = at<double>(ws, L.dres);
+  int32_t* tcnt = at<int32_t>(ws, L.tcnt);
+  int32_t* toff = at<int32_t>(ws, L.toff);
+  int32_t* tfill = at<int32_t>(ws, L.tfill);
+  int32_t* tlist = at<int32_t>(ws, L.tlist);
   for (int64_t c0 = 0; c0 < S; c0 += L.C) {
     const int rows = (int)std::min<int64_t>(L.C, S - c0);
     kd::SweepArgs b;
@@ -1547,8 +1559,19 @@ int kd_teacher_sample(const kd_problem* p, const void* hidden, const void* W,
     b.dres = dres;
     b.sids = ids_out + c0 * N;
     {
+      // each draw resolved inside its unit: only the vocabulary tiles some
+      // row draws in are recomputed, for the rows that draw there
+      {
+        Prof pt("sample_draw_tiles", st);
+        KD_HIP(kd::launch_draw_tiles(dunit, rows, N, (int)L.nvt, tcnt, toff, tfill, tlist, st));
+      }
       Prof pr("sample_draw", st);
-      KD_HIP(kd::launch_sweep(kd::kSweepSDraw, f32, 0, b, grid, st));
+      b.idx = tlist;
+      b.tcnt = tcnt;
+      b.toff = toff;
+      const int64_t tgrid = L.nvt * kd::ceil_div(rows, kd::kTile);
+      if (tgrid > INT32_MAX) return KD_ERR_SHAPE;
+      KD_HIP(kd::launch_sweep(kd::kSweepSDrawTiles, f32, 1, b, (int)tgrid, st));
     }
   }
   return KD_OK;

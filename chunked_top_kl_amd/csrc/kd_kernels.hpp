@@ -7,7 +7,7 @@
 namespace kd {
 
 enum SweepKind { kSweepFwd = 0, kSweepBwdG = 1, kSweepEnt = 2, kSweepPilot = 3, kSweepEmit = 4,
-                 kSweepSMass = 5, kSweepSDraw = 6, kSweepLogits = 7 };
+                 kSweepSMass = 5, kSweepLogits = 7, kSweepSDrawTiles = 8 };
 
 // Vocabulary-sweep projection (forward LSE + gather, backward gradient tile,
 // entropy). Rows are "launch rows" r in [0, rows): compacted row
@@ -49,6 +49,10 @@ struct SweepArgs {
   // inside that unit, in the unit's scale; the sampled id sids[r * N + n]
   double* tmass; float* tscale; int64_t ldm;
   const int32_t* dunit; const double* dres; int32_t* sids; int N;
+  // the draw pass over the drawn-in tiles only: vocabulary tile vt's rows
+  // (launch rows that draw in units 2vt or 2vt + 1) are idx[toff[vt] ..],
+  // tcnt[vt] of them; one work-group per tile and 256 of its rows
+  const int32_t* tcnt; const int32_t* toff;
   // teacher cache writer: length of each writer's candidate sub-list,
   // scnt[r * scnt_ld + range * 4 + writer]
   int32_t* scnt; int64_t scnt_ld;
@@ -206,6 +210,11 @@ hipError_t launch_draw_cumsum(double* tmass, const float* tscale, int64_t ldm, i
 hipError_t launch_draw_assign(const double* cum, const float* tscale, const float* rowmax,
                               int64_t ldm, int nu, int rows, const double* u, int N,
                               int32_t* dunit, double* dres, int32_t* sids, hipStream_t st);
+// the rows of a chunk that draw in each vocabulary tile of 256 entries (units
+// 2vt and 2vt + 1): tcnt[vt] rows, listed in tlist[toff[vt] ..] (a row once per
+// tile it draws in, in no particular order); tfill is scratch, nvt entries
+hipError_t launch_draw_tiles(const int32_t* dunit, int rows, int N, int nvt, int32_t* tcnt,
+                             int32_t* toff, int32_t* tfill, int32_t* tlist, hipStream_t st);
 int sweep_grid(int64_t rows_max, int V, int ncu);
 hipError_t launch_fwd_combine(const CombineArgs& a, hipStream_t st);
 hipError_t launch_loss_final(const double* block_sums, int nblk, const int32_t* nrows_dev,

@@ -154,4 +154,86 @@ hipError_t launch_draw_assign(const double* cum, const float* tscale, const floa
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Rows per drawn-in vocabulary tile. A row's draws are ordered by unit (its
+// uniforms do not decrease), so the tiles it draws in are runs of its unit
+// list; a row of non-finite logits has unit -1 on every draw and none.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void draw_tiles_zero_kernel(int32_t* a, int32_t* b, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+    a[i] = 0;
+    b[i] = 0;
+  }
+}
+
+// one thread per draw; the first draw of each run of a row's draws in one
+// tile stands for the row there
+__device__ inline int draw_tile_start(const int32_t* du, int64_t i, int N) {
+  const int u = du[i];
+  if (u < 0) return -1;
+  const int tile = u >> 1;
+  if (i % N != 0 && (du[i - 1] >> 1) == tile) return -1;
+  return tile;
+}
+
+__global__ __launch_bounds__(256) void draw_tile_count_kernel(const int32_t* du, int rows, int N,
+                                                              int32_t* tcnt) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)rows * N) return;
+  const int tile = draw_tile_start(du, i, N);
+  if (tile >= 0) atomicAdd(&tcnt[tile], 1);
+}
+
+// exclusive running sum of cnt[0..n) into off, one work-group of 1024 threads
+__global__ __launch_bounds__(1024) void draw_tile_scan_kernel(const int32_t* cnt, int n,
+                                                              int32_t* off) {
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < n; base += 1024) {
+    const int i = base + tid;
+    const int v = i < n ? cnt[i] : 0;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wv] = x;
+    __syncthreads();
+    int pre = carry;
+    for (int q = 0; q < wv; ++q) pre += wsum[q];
+    if (i < n) off[i] = pre + x - v;
+    __syncthreads();
+    if (tid == 1023) carry = pre + x;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void draw_tile_fill_kernel(const int32_t* du, int rows, int N,
+                                                             const int32_t* toff, int32_t* tfill,
+                                                             int32_t* tlist) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)rows * N) return;
+  const int tile = draw_tile_start(du, i, N);
+  if (tile >= 0) tlist[toff[tile] + atomicAdd(&tfill[tile], 1)] = (int32_t)(i / N);
+}
+
+hipError_t launch_draw_tiles(const int32_t* dunit, int rows, int N, int nvt, int32_t* tcnt,
+                             int32_t* toff, int32_t* tfill, int32_t* tlist, hipStream_t st) {
+  if (rows <= 0 || nvt <= 0) return hipSuccess;
+  const int zg = (int)std::min<int64_t>(ceil_div(nvt, 256), 1024);
+  hipLaunchKernelGGL(draw_tiles_zero_kernel, dim3(zg), dim3(256), 0, st, tcnt, tfill, nvt);
+  const int64_t dg = ceil_div((int64_t)rows * N, 256);
+  if (dg > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(draw_tile_count_kernel, dim3((unsigned)dg), dim3(256), 0, st, dunit, rows, N,
+                     tcnt);
+  hipLaunchKernelGGL(draw_tile_scan_kernel, dim3(1), dim3(1024), 0, st, tcnt, nvt, toff);
+  hipLaunchKernelGGL(draw_tile_fill_kernel, dim3((unsigned)dg), dim3(256), 0, st, dunit, rows, N,
+                     toff, tfill, tlist);
+  return hipGetLastError();
+}
+
 }  // namespace kd

@@ -338,31 +338,55 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
   const int half = lane >> 5;
 
   int rows = a.row_cap;
-  if (a.nrows_dev) {
-    int n = *a.nrows_dev - a.row_begin;
-    rows = n < rows ? n : rows;
+  int ntt, jt, b, vt_begin, vt_end;
+  if constexpr (KIND == kSweepSDrawTiles) {
+    // one vocabulary tile and up to kTile of the launch rows that draw in it
+    // (listed at idx + toff[vt]). Work-groups go slice by slice over all
+    // tiles: the first slices, nearly all of the work, are dispatched first
+    // and spread over every XCD; the later slices of most tiles are empty and
+    // end at once.
+    const int nvt = (int)ceil_div(a.V, kTile);
+    const int nsl = (int)ceil_div(a.row_cap, kTile);
+    if ((int)blockIdx.x >= nvt * nsl) return;
+    const int vt = (int)blockIdx.x % nvt, sl = (int)blockIdx.x / nvt;
+    const int n = a.tcnt[vt] - sl * kTile;
+    if (n <= 0) return;
+    a.idx += a.toff[vt];
+    a.row_begin = sl * kTile;
+    rows = n < kTile ? n : kTile;
+    ntt = 1;
+    jt = 0;
+    b = 0;
+    vt_begin = vt;
+    vt_end = vt + 1;
+  } else {
+    if (a.nrows_dev) {
+      int n = *a.nrows_dev - a.row_begin;
+      rows = n < rows ? n : rows;
+    }
+    if (rows <= 0) return;
+    ntt = (int)ceil_div(rows, kTile);
+    const int nvt = (int)ceil_div(a.V, kTile);
+    const int ns = sweep_splits(ntt, nvt, a.ncu);
+    const int total = ntt * ns;
+    if ((int)blockIdx.x >= total) return;
+    // Raster. A launch of at most 8 token tiles (one chunk) takes them in
+    // pairs: the 32 work-groups an XCD runs at once cover 2 token tiles (whose
+    // panels, 2.9 MB at H = 2880, stay in its 4 MB L2) and 16 vocabulary
+    // ranges, each W panel shared 2 ways and each range of W read by 4 XCDs.
+    // Measured on the gradient tile at the 32K-context shapes (ms per launch):
+    // all 8 token tiles per XCD 2.27, 4 tiles 2.22, 2 tiles 2.20, 1 tile 2.24.
+    // A launch over many token tiles walks the vocabulary ranges fastest
+    // instead, so that an XCD holds few token panels at a time.
+    const int L = xcd_remap(blockIdx.x, total);
+    const int GM = ntt <= 8 ? (ntt < 2 ? ntt : 2) : 1;
+    const int grp = L / (GM * ns), in = L % (GM * ns);
+    const int gm = (ntt - grp * GM) < GM ? (ntt - grp * GM) : GM;
+    jt = grp * GM + in % gm;
+    b = in / gm;
+    vt_begin = (int)((int64_t)b * nvt / ns);
+    vt_end = (int)((int64_t)(b + 1) * nvt / ns);
   }
-  if (rows <= 0) return;
-  const int ntt = (int)ceil_div(rows, kTile);
-  const int nvt = (int)ceil_div(a.V, kTile);
-  const int ns = sweep_splits(ntt, nvt, a.ncu);
-  const int total = ntt * ns;
-  if ((int)blockIdx.x >= total) return;
-  // Raster. A launch of at most 8 token tiles (one chunk) takes them in
-  // pairs: the 32 work-groups an XCD runs at once cover 2 token tiles (whose
-  // panels, 2.9 MB at H = 2880, stay in its 4 MB L2) and 16 vocabulary ranges,
-  // each W panel shared 2 ways and each range of W read by 4 XCDs. Measured
-  // on the gradient tile at the 32K-context shapes (ms per launch): all 8
-  // token tiles per XCD 2.27, 4 tiles 2.22, 2 tiles 2.20, 1 tile 2.24. A
-  // launch over many token tiles walks the vocabulary ranges fastest instead,
-  // so that an XCD holds few token panels at a time.
-  const int L = xcd_remap(blockIdx.x, total);
-  const int GM = ntt <= 8 ? (ntt < 2 ? ntt : 2) : 1;
-  const int grp = L / (GM * ns), in = L % (GM * ns);
-  const int gm = (ntt - grp * GM) < GM ? (ntt - grp * GM) : GM;
-  const int jt = grp * GM + in % gm, b = in / gm;
-  const int vt_begin = (int)((int64_t)b * nvt / ns);
-  const int vt_end = (int)((int64_t)(b + 1) * nvt / ns);
 
   constexpr int esz = Elem<T>::size;
   const int64_t kbytes = (int64_t)a.H * esz;
@@ -411,11 +435,11 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
       if (tl0 + 32 * j < rows) tej[j] = a.te[tl0 + 32 * j];
     dcur[j] = a.N;
     dnext[j] = 0x7FFFFFFF;
-    if constexpr (KIND == kSweepSDraw) {
+    if constexpr (KIND == kSweepSDrawTiles) {
       // a row's draws are ordered by unit; start at the first one in this
-      // work-group's vocabulary range
+      // work-group's vocabulary tile
       if (tl0 + 32 * j < rows) {
-        const int32_t* du = a.dunit + (int64_t)(tl0 + 32 * j) * a.N;
+        const int32_t* du = a.dunit + (int64_t)orow[j] * a.N;
         dcur[j] = lower_bound_ids(du, a.N, 2 * vt_begin);
         dnext[j] = dcur[j] < a.N ? du[dcur[j]] : 0x7FFFFFFF;
       }
@@ -593,7 +617,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
         }
       }
 
-      if constexpr (KIND == kSweepSMass || KIND == kSweepSDraw) {
+      if constexpr (KIND == kSweepSMass || KIND == kSweepSDrawTiles) {
         // weights 2^(z c - mc) of the teacher softmax at T in the unit's own
         // scale, mc = c times the largest z of the unit's 128 entries (entries
         // past V weigh 0), summed per quad: four consecutive vocabulary
@@ -637,7 +661,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
         } else {
           // the column's draws up to this unit: those of lower units belong
           // to the other wave and are passed over
-          const int64_t rb = (int64_t)t * a.N;
+          const int64_t rb = (int64_t)orow[j] * a.N;
           while (true) {
             const bool act = dnext[j] <= unit;
             if (ballot(act) == 0) break;
@@ -748,7 +772,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
   }
   if constexpr (KIND == kSweepBwdG || KIND == kSweepLogits || KIND == kSweepPilot ||
                 KIND == kSweepEmit ||
-                KIND == kSweepSMass || KIND == kSweepSDraw)
+                KIND == kSweepSMass || KIND == kSweepSDrawTiles)
     return;
 
   // ---- end of sweep: merge lane halves, then the two waves sharing tokens
@@ -840,9 +864,9 @@ KD_SWEEP_KERNEL(kd_teacher_emit_bf16, __bf16, kSweepEmit, false)
 KD_SWEEP_KERNEL(kd_teacher_pilot_f32, float, kSweepPilot, false)
 KD_SWEEP_KERNEL(kd_teacher_emit_f32, float, kSweepEmit, false)
 KD_SWEEP_KERNEL(kd_sample_mass_bf16, __bf16, kSweepSMass, false)
-KD_SWEEP_KERNEL(kd_sample_draw_bf16, __bf16, kSweepSDraw, false)
 KD_SWEEP_KERNEL(kd_sample_mass_f32, float, kSweepSMass, false)
-KD_SWEEP_KERNEL(kd_sample_draw_f32, float, kSweepSDraw, false)
+KD_SWEEP_KERNEL(kd_sample_draw_tiles_bf16, __bf16, kSweepSDrawTiles, true)
+KD_SWEEP_KERNEL(kd_sample_draw_tiles_f32, float, kSweepSDrawTiles, true)
 KD_SWEEP_KERNEL(kd_cmp_logits_bf16, __bf16, kSweepLogits, false)
 KD_SWEEP_KERNEL(kd_cmp_logits_rows_bf16, __bf16, kSweepLogits, true)
 #undef KD_SWEEP_KERNEL
@@ -858,7 +882,7 @@ hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid
     else if (kind == kSweepPilot) KD_SWEEP(kd_teacher_pilot_bf16);
     else if (kind == kSweepEmit) KD_SWEEP(kd_teacher_emit_bf16);
     else if (kind == kSweepSMass) KD_SWEEP(kd_sample_mass_bf16);
-    else if (kind == kSweepSDraw) KD_SWEEP(kd_sample_draw_bf16);
+    else if (kind == kSweepSDrawTiles) KD_SWEEP(kd_sample_draw_tiles_bf16);
     else if (kind == kSweepLogits && map) KD_SWEEP(kd_cmp_logits_rows_bf16);
     else if (kind == kSweepLogits) KD_SWEEP(kd_cmp_logits_bf16);
     else KD_SWEEP(kd_entropy_sweep_bf16);
@@ -869,7 +893,7 @@ hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid
     else if (kind == kSweepPilot) KD_SWEEP(kd_teacher_pilot_f32);
     else if (kind == kSweepEmit) KD_SWEEP(kd_teacher_emit_f32);
     else if (kind == kSweepSMass) KD_SWEEP(kd_sample_mass_f32);
-    else if (kind == kSweepSDraw) KD_SWEEP(kd_sample_draw_f32);
+    else if (kind == kSweepSDrawTiles) KD_SWEEP(kd_sample_draw_tiles_f32);
     else if (kind == kSweepLogits) return hipErrorInvalidValue;   // bf16 only
     else KD_SWEEP(kd_entropy_sweep_f32);
   }

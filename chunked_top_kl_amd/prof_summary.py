@@ -80,6 +80,7 @@ STEP_PATTERNS = [
     ("teacher_wnorm", "teacher_wnorm"),
     ("kd_sample_mass", "sample_mass"),
     ("kd_sample_draw", "sample_draw"),
+    ("draw_tile", "sample_draw"),
     ("draw_cumsum", "sample_assign"),
     ("draw_assign", "sample_assign"),
     ("draw_zero_flag", "uniforms_check"),

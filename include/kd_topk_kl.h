@@ -420,8 +420,9 @@ int kd_teacher_topk(const kd_problem* problem, const void* hidden, const void* W
  * probability cache: tl_kind KD_TEACHER_PROBS, equal values; repeated ids
  * add up). The [S,V] grid is never stored: per chunk of problem->chunk
  * positions one sweep stores the mass of every 128 consecutive ids (each in
- * the scale of its own largest logit) and another resolves each draw inside
- * its 128 ids.
+ * the scale of its own largest logit), and a second pass resolves each draw
+ * inside its 128 ids, recomputing only the tiles of 256 ids that positions
+ * of the chunk draw in, for those positions.
  *   hidden    [device] [S,H] hw_dtype: the teacher's final hidden states
  *   W         [device] [V,H] hw_dtype: the teacher's output projection
  *   uniforms  [device] [S,N] double in [0, 1), each row non-decreasing (sort
