@@ -1465,10 +1465,14 @@ struct SampleLayout {
 SampleLayout plan_sample(const kd_problem* p) {
   SampleLayout L{};
   const int64_t S = std::max<int64_t>(p->S, 1), N = p->K;
-  L.C = std::min<int64_t>(p->chunk, S);
-  L.ldm = kd::round_up(L.C, 64);
   L.nu = kd::ceil_div(p->V, 128);
   L.nvt = kd::ceil_div(p->V, 256);
+  // rows per chunk; the draw pass's row lists (at most min(N, tiles) entries
+  // per row) keep int32 offsets, so a chunk holds fewer than 2^31 of them
+  // (each row is sampled on its own: the chunking does not change the ids)
+  L.C = std::min<int64_t>(std::min<int64_t>(p->chunk, S),
+                          INT32_MAX / std::max<int64_t>(std::min<int64_t>(N, L.nvt), 1));
+  L.ldm = kd::round_up(L.C, 64);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
