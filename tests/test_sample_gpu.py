@@ -14,7 +14,9 @@ land on the neighbouring id, so the checks are:
     F(v-1) - DELTA <= u < F(v) + DELTA, and the ids of a row never decrease;
   - edges: u = 0 and u just below 1, one draw per row, rows spread over
     several chunks with a ragged last one, a vocabulary that is not a
-    multiple of the 128-entry units, fp32 inputs, invalid uniforms rejected.
+    multiple of the 128-entry units, fp32 inputs, invalid uniforms rejected;
+  - many rows drawing in one vocabulary tile (several slices of the draw
+    pass), and the same ids whatever the chunking.
 Inputs are synthetic teachers with hidden states of standard deviation 4 and
 weights of 1/sqrt(H), which gives peaked distributions (top probability of a
 few percent to tens of percent).
@@ -109,6 +111,32 @@ def test_random_uniforms(kd):
     check_brackets(got, u, F)
     ref = oracle_teacher_sample(h, W, T, u)
     assert np.mean(got == ref) >= 0.9
+
+
+def test_many_rows_drawing_in_one_tile(kd):
+    # every position's distribution peaks on the same few ids, so one
+    # vocabulary tile holds far more than 256 drawing rows (several slices of
+    # the draw pass); the ids must not depend on the chunking (each row is
+    # sampled on its own), and must match the oracle at step middles
+    S, H, V, N, T = 1500, 128, 3000, 32, 1.0
+    h, W, th, tW = teacher(S, H, V, seed=77)
+    # a shared direction in every hidden state, and ids 1300..1303 aligned with it
+    rng = np.random.Generator(np.random.PCG64(78))
+    d = rng.standard_normal(H).astype(np.float32)
+    d /= np.linalg.norm(d)
+    h = h + np.float32(8.0) * d[None, :]
+    W[1300:1304] += np.float32(1.5) * d[None, :]
+    hb, wb = bf16_bits_from_f32(h), bf16_bits_from_f32(W)
+    h, W = f32_from_bf16_bits(hb), f32_from_bf16_bits(wb)
+    th, tW = np_bf16_to_torch(hb), np_bf16_to_torch(wb)
+    P, F = oracle_teacher_cdf(h, W, T)
+    assert np.median(P[:, 1300:1304].sum(axis=1)) > 0.5
+    u, want = midpoint_uniforms(P, F, N, np.random.default_rng(79))
+    whole = run(kd, th, tW, u, T, chunk=S)
+    small = run(kd, th, tW, u, T, chunk=100)
+    assert np.array_equal(whole, small)
+    assert np.array_equal(whole, want)
+    assert np.sum((want >= 1280) & (want < 1536)) > 4 * 256
 
 
 def test_edges(kd):
