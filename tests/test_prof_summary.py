@@ -94,7 +94,8 @@ def test_every_kernel_maps_to_a_step():
     assert step_of("void kd::prepass_reg_kernel<64>(kd::PrepassArgs)") == "prepass"
     assert step_of("kd::grad_teacher_kernel<__bf16>(kd::GradTeacherArgs)") == "bwd_grad_teacher"
     assert step_of("teacher_gather_kernel") == "teacher_gather"
-    assert step_of("kd_sample_draw_bf16") == "sample_draw"
+    assert step_of("kd_sample_draw_tiles_bf16") == "sample_draw"
+    assert step_of("kd::draw_tile_fill_kernel(int const*, int, int, int const*, int*, int*)") == "sample_draw"
     assert step_of("kd::sample_refined_entropy_kernel(kd::SelectWs, int, int, double*)") == \
         "select_refine_fp64"
 
