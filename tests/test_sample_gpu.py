@@ -16,7 +16,9 @@ land on the neighbouring id, so the checks are:
     several chunks with a ragged last one, a vocabulary that is not a
     multiple of the 128-entry units, fp32 inputs, invalid uniforms rejected;
   - many rows drawing in one vocabulary tile (several slices of the draw
-    pass), and the same ids whatever the chunking.
+    pass), and the same ids whatever the chunking;
+  - positions whose hidden state holds inf or NaN get -1 on every draw, the
+    others are unaffected.
 Inputs are synthetic teachers with hidden states of standard deviation 4 and
 weights of 1/sqrt(H), which gives peaked distributions (top probability of a
 few percent to tens of percent).
@@ -160,6 +162,27 @@ def test_edges(kd):
     u1 = np.random.default_rng(6).random((S, 1))
     got1 = run(kd, th, tW, u1, T, chunk=1024)
     check_brackets(got1, u1, F)
+
+
+def test_rows_with_non_finite_logits(kd):
+    # a position whose hidden state holds inf or NaN has no distribution: every
+    # draw gives -1, and the other positions are sampled as usual
+    S, H, V, N, T = 200, 64, 900, 12, 1.0
+    h, W, th, tW = teacher(S, H, V, seed=31)
+    bad = [3, 77, 199]
+    hb = bf16_bits_from_f32(h)
+    hb[3, 5] = 0x7F80          # +inf
+    hb[77, 0] = 0x7FC0         # NaN
+    hb[199, 63] = 0xFF80       # -inf
+    th = np_bf16_to_torch(hb)
+    good = np.setdiff1d(np.arange(S), bad)
+    P, F = oracle_teacher_cdf(h[good], W, T)
+    u = np.sort(np.random.default_rng(32).random((S, N)), axis=1)
+    um, want = midpoint_uniforms(P, F, N, np.random.default_rng(33))
+    u[good] = um
+    got = run(kd, th, tW, u, T, chunk=64)
+    assert np.all(got[bad] == -1)
+    assert np.array_equal(got[good], want)
 
 
 @pytest.mark.parametrize("bad", ["one", "negative", "nan", "decreasing"])
