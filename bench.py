@@ -63,7 +63,7 @@ def kernel_flops(name, wl, C_rows, S_rows):
     H, V = wl["H"], wl["V"]
     if name in ("fwd_lse_gather", "entropy_sweep"):
         return 2.0 * S_rows * H * V
-    if name in ("bwd_grad_tile", "bwd_dhidden", "bwd_dw"):
+    if name in ("bwd_grad_tile", "bwd_dhidden", "bwd_dw", "fwd_lse_gather_keep"):
         return 2.0 * C_rows * H * V
     return None
 
@@ -194,6 +194,9 @@ def time_workload(kd, torch, key, p=None, steps=3, warmup=1, comparators=False):
     log(f"[bench] {key}: {ms:.2f} ms/step, {out['tokens_per_s']:.0f} tokens/s, "
         f"MFMA {100 * out['mfma_frac']:.1f}%, peak {out['peak_gib']} GiB")
     del ws, res
+    if key != "c5":
+        out["one_call"] = one_call_leg(kd, torch, wl, t, steps=steps, warmup=warmup,
+                                       two_call_ms=ms)
     if comparators:
         out["comparators"] = comparator_leg(kd, torch, wl, t)
     del t
@@ -250,6 +253,61 @@ def comparator_leg(kd, torch, wl, t, steps=3, warmup=1):
                                                      / (PEAK_BF16_TFLOPS * 1e12), 4))
         log(f"[bench] {name} form: {ms:.2f} ms/step, peak {peak:.2f} GiB")
         del ws, res
+    torch.cuda.empty_cache()
+    return out
+
+
+def one_call_leg(kd, torch, wl, t, steps=5, warmup=2, two_call_ms=None):
+    """The forward and backward in one call (kd_topk_kl_fwd_bwd: each chunk's
+    logits kept, its gradient tile formed from them, no second projection) at
+    the workload's shapes: ms per step, tokens/s, peak device memory (inputs,
+    outputs, workspace), the per-step kernels, and the MFMA fraction of the
+    6*S*H*V it projects (the counted 8*S*H*V over its time as well, for
+    comparison with the two calls)."""
+    S, H, V, K, C = wl["S"], wl["H"], wl["V"], wl["K"], wl["chunk"]
+    hidden, W, ids, tl = t
+    in_bytes = sum(x.numel() * x.element_size() for x in t)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    base = torch.cuda.memory_allocated() - in_bytes
+    torch.cuda.reset_peak_memory_stats()
+    need = kd.kd_topk_kl_fwd_bwd_workspace_bytes(hidden, W, ids, tl, wl["T"], C)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    g = torch.ones(1, dtype=torch.float32, device="cuda")
+
+    def step():
+        return kd.kd_topk_kl_fwd_bwd(hidden, W, ids, tl, g, wl["T"], C, workspace=ws)
+
+    for _ in range(warmup):
+        res = step()
+        del res
+    torch.cuda.synchronize()
+    kd.kd_profile_reset()
+    kd.kd_profile_enable(True)
+    t0 = time.perf_counter()
+    res = None
+    for _ in range(steps):
+        res = None
+        res = step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / steps
+    kd.kd_profile_enable(False)
+    prof = kd.kd_profile_read()
+    kd.kd_profile_reset()
+    peak = (torch.cuda.max_memory_allocated() - base) / 2**30
+    out = dict(ms_per_step=round(ms, 3), tokens_per_s=round(S / (ms / 1000.0), 1),
+               peak_gib=round(peak, 3), workspace_gib=round(need / 2**30, 3),
+               loss=float(res["loss"][0]),
+               mfma_frac_of_its_6SHV=round(6.0 * S * H * V / (ms / 1000.0)
+                                           / (PEAK_BF16_TFLOPS * 1e12), 4),
+               counted_8SHV_frac=round(8.0 * S * H * V / (ms / 1000.0)
+                                       / (PEAK_BF16_TFLOPS * 1e12), 4),
+               kernels=kernel_table(prof, wl, C, S, steps))
+    if two_call_ms:
+        out["speedup_vs_two_calls"] = round(two_call_ms / ms, 3)
+    log(f"[bench] one call: {ms:.2f} ms/step, {out['tokens_per_s']:.0f} tokens/s, "
+        f"peak {peak:.2f} GiB")
+    del ws, res
     torch.cuda.empty_cache()
     return out
 
@@ -479,6 +537,8 @@ def main():
     ap.add_argument("--teacher-only", action="store_true",
                     help="time only the teacher top-K cache writer (steps / warmup calls) and "
                          "print its line")
+    ap.add_argument("--no-one-call", action="store_true",
+                    help="skip the forward and backward in one call (kd_topk_kl_fwd_bwd)")
     ap.add_argument("--no-comparators", action="store_true",
                     help="skip the dense and forward-chunked loss forms (8K and 32K contexts)")
     ap.add_argument("--no-workloads", action="store_true",
@@ -608,6 +668,8 @@ def main():
     }
     del ws
     torch.cuda.empty_cache()
+    if not args.no_one_call and args.workload != "c5":
+        result["one_call"] = one_call_leg(kd, torch, wl, t, two_call_ms=ms)
     if not args.no_chunk_sweep and args.workload == "c3":
         result["chunk_sweep"] = chunk_sweep(kd, torch, wl, t, [512, 1024, 2048])
     if not args.no_comparators and args.workload in ("c2", "c3"):

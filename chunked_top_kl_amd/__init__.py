@@ -17,6 +17,7 @@ __all__ = [
     "KD_BF16", "KD_F32", "KD_TEACHER_LOGITS", "KD_TEACHER_PROBS", "KdError", "kd_problem", "lib",
     "kd_abi_version", "kd_status_str", "kd_topk_kl_workspace_bytes",
     "kd_topk_kl_fwd", "kd_topk_kl_fwd_noalloc", "kd_topk_kl_bwd", "kd_student_entropy",
+    "kd_topk_kl_fwd_bwd_workspace_bytes", "kd_topk_kl_fwd_bwd",
     "KD_FORM_FUSED", "KD_FORM_DENSE", "KD_FORM_FORWARD_CHUNKED", "kd_kl_comparator_fwd",
     "kd_kl_comparator_bwd",
     "kd_select_top_fraction", "kd_select_samples", "kd_validate_topk",
@@ -77,6 +78,11 @@ lib.kd_kl_comparator_bwd.argtypes = [_PP, ctypes.c_int, _P, _P, _P, _P, _P, _P, 
 lib.kd_topk_kl_bwd.restype = ctypes.c_int
 lib.kd_topk_kl_bwd.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P,
                                ctypes.c_size_t, _P]
+lib.kd_topk_kl_fwd_bwd_workspace_bytes.restype = ctypes.c_size_t
+lib.kd_topk_kl_fwd_bwd_workspace_bytes.argtypes = [_PP]
+lib.kd_topk_kl_fwd_bwd.restype = ctypes.c_int
+lib.kd_topk_kl_fwd_bwd.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                   ctypes.c_int, _P, ctypes.c_size_t, _P]
 lib.kd_student_entropy.restype = ctypes.c_int
 lib.kd_student_entropy.argtypes = [_PP, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.kd_select_top_fraction.restype = ctypes.c_int
@@ -254,6 +260,50 @@ def kd_topk_kl_bwd(hidden, W, topk_ids, topk_logits, lse, grad_loss, T=1.0, chun
                               _ptr(dh), _ptr(dW), 1 if accumulate_dW else 0, _ptr(ws),
                               ws.numel(), _stream(dev)), "kd_topk_kl_bwd")
     return dh, dW
+
+
+def kd_topk_kl_fwd_bwd_workspace_bytes(hidden, W, topk_ids, topk_logits, T=1.0, chunk=1024,
+                                       teacher_probs=False) -> int:
+    p = _problem_of(hidden, W, topk_ids, topk_logits, T, chunk, teacher_probs)
+    return int(lib.kd_topk_kl_fwd_bwd_workspace_bytes(ctypes.byref(p)))
+
+
+def kd_topk_kl_fwd_bwd(hidden, W, topk_ids, topk_logits, grad_loss, T=1.0, chunk=1024,
+                       mask=None, want_kl_rows=False, want_z_topk=False, dW=None,
+                       accumulate_dW=False, workspace=None, teacher_probs=False):
+    """Forward and backward in one call (bf16 hidden and W), with the upstream
+    gradient grad_loss ([1] float32) known up front. Returns dict(loss, lse,
+    kl_rows, z_topk, dhidden, dW): those of kd_topk_kl_fwd followed by
+    kd_topk_kl_bwd."""
+    p = _problem_of(hidden, W, topk_ids, topk_logits, T, chunk, teacher_probs)
+    mask = _mask_arg(mask, p.S)
+    dev = hidden.device
+    need = lib.kd_topk_kl_fwd_bwd_workspace_bytes(ctypes.byref(p))
+    if need == 0:
+        raise KdError(3 if p.hw_dtype != KD_BF16 else 2, "kd_topk_kl_fwd_bwd_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace.numel() < need:
+        raise ValueError(f"workspace too small: {workspace.numel()} < {need} bytes")
+    if grad_loss.dtype != torch.float32 or grad_loss.numel() != 1:
+        raise ValueError("grad_loss must be a float32 tensor of one element")
+    grad_loss = grad_loss.contiguous()
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(p.S, dtype=torch.float32, device=dev)
+    kl = torch.empty(p.S, dtype=torch.float32, device=dev) if want_kl_rows else None
+    zt = torch.empty(p.S, p.K, dtype=torch.float32, device=dev) if want_z_topk else None
+    dh = torch.empty(p.S, p.H, dtype=torch.float32, device=dev)
+    if dW is None:
+        dW = torch.empty(p.V, p.H, dtype=torch.float32, device=dev)
+        accumulate_dW = False
+    elif dW.dtype != torch.float32 or tuple(dW.shape) != (p.V, p.H) or not dW.is_contiguous():
+        raise ValueError("dW must be a contiguous float32 [V,H] tensor")
+    _check(lib.kd_topk_kl_fwd_bwd(ctypes.byref(p), _ptr(hidden), _ptr(W), _ptr(topk_ids),
+                                  _ptr(topk_logits), _ptr(mask), _ptr(grad_loss), _ptr(loss),
+                                  _ptr(lse), _ptr(kl), _ptr(zt), _ptr(dh), _ptr(dW),
+                                  1 if accumulate_dW else 0, _ptr(workspace), workspace.numel(),
+                                  _stream(dev)), "kd_topk_kl_fwd_bwd")
+    return dict(loss=loss, lse=lse, kl_rows=kl, z_topk=zt, dhidden=dh, dW=dW)
 
 
 def kd_kl_comparator_fwd(hidden, W, topk_ids, topk_logits, form, T=1.0, chunk=1024, mask=None,

@@ -457,6 +457,147 @@ int bwd_check(const kd_problem* p, const void* hidden, const void* W, const int3
   return KD_OK;
 }
 
+// Chunk ci's rows, gathered in order into Xc (for its sweep) and transposed
+// into its slot of X_c^T (for the dW contraction).
+int gather_chunk_rows(const kd_problem* p, const Layout& L, const void* hidden, int ci, void* ws,
+                      hipStream_t st) {
+  const int H = (int)p->H, C = (int)L.C;
+  const int slot = (int)(ci % L.nd);
+  Prof pr("gather_rows_t", st);
+  KD_HIP(kd::launch_gather_rows_t(p->hw_dtype == KD_F32, (const char*)hidden, (int64_t)H * L.esz,
+                                  at<int32_t>(ws, L.idx), at<int32_t>(ws, L.count), ci * C, C, H,
+                                  at<char>(ws, L.XcT) + slot * L.slot * L.esz, L.Cld * L.esz,
+                                  (int)L.slot, at<char>(ws, L.Xc), st));
+  return KD_OK;
+}
+
+// Sweep arguments over chunk ci's gathered rows, with its gradient tile: its
+// slot of the dW group, blocked (bf16: ldg is the block stride), or the one
+// row-major tile (fp32: ldg is the row pitch) and its slot of G^T.
+kd::SweepArgs chunk_sweep_args(const kd_problem* p, const Layout& L, const void* W, int ci,
+                               const float* lse, const float* grad_loss, void* ws) {
+  const int f32 = p->hw_dtype == KD_F32;
+  const int slot = (int)(ci % L.nd);
+  const int64_t row_bytes = p->H * L.esz;
+  kd::SweepArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.W = (const char*)W;
+  a.ldw = row_bytes;
+  a.X = at<char>(ws, L.Xc);
+  a.ldx = row_bytes;
+  a.x_row0 = 0;
+  a.idx = at<int32_t>(ws, L.idx);
+  a.nrows_dev = at<int32_t>(ws, L.count);
+  a.row_begin = ci * (int)L.C;
+  a.row_cap = (int)L.C;
+  a.V = (int)p->V;
+  a.H = (int)p->H;
+  a.K = (int)p->K;
+  a.ncu = kCostCUs;
+  a.T = p->temperature;
+  a.ids_s = at<int32_t>(ws, L.ids_s);
+  a.p_s = at<float>(ws, L.p_s);
+  a.korig_s = at<int32_t>(ws, L.korig_s);
+  a.lse = lse;
+  a.grad_loss = grad_loss;
+  a.G = at<char>(ws, L.G) + (f32 ? 0 : (int64_t)slot * L.slot * 512);
+  a.ldg = f32 ? L.Vld * L.esz : L.Gbs;
+  a.GT = f32 ? at<char>(ws, L.GT) + slot * L.slot * L.esz : nullptr;
+  a.ldgt = L.Cld * L.esz;
+  return a;
+}
+
+// Teacher term of a chunk's gradient tile, after the tile itself (a: the
+// tile's sweep arguments).
+int grad_teacher(const kd_problem* p, const Layout& L, const kd::SweepArgs& a, int row_begin,
+                 const float* grad_loss, void* ws, hipStream_t st) {
+  (void)ws;
+  kd::GradTeacherArgs gt;
+  gt.G = a.G;
+  gt.ldg = a.ldg;
+  gt.GT = a.GT;
+  gt.ldgt = a.ldgt;
+  gt.idx = a.idx;
+  gt.nrows_dev = a.nrows_dev;
+  gt.row_begin = row_begin;
+  gt.row_cap = (int)L.C;
+  gt.K = (int)p->K;
+  gt.ids_s = a.ids_s;
+  gt.p_s = a.p_s;
+  gt.grad_loss = grad_loss;
+  gt.T = p->temperature;
+  Prof pr("bwd_grad_teacher", st);
+  KD_HIP(kd::launch_grad_teacher(p->hw_dtype == KD_F32, gt, st));
+  return KD_OK;
+}
+
+// dHidden of chunk ci from its gradient tile Gc, and dW once the chunk closes
+// a dW group (or is the last chunk; with no rows that launch still writes dW,
+// zeros unless accumulating).
+int chunk_contractions(const kd_problem* p, const Layout& L, char* Gc, int64_t ldg, int ci,
+                       int nchunks, float* dhidden, float* dW, int accumulate_dW, void* ws,
+                       hipStream_t st) {
+  const int S = (int)p->S, V = (int)p->V, H = (int)p->H;
+  const int f32 = p->hw_dtype == KD_F32;
+  const int C = (int)L.C;
+  const int row_begin = ci * C;
+  const int slot = (int)(ci % L.nd);
+  if (S > 0) {
+    kd::DhArgs d;
+    d.G = Gc;
+    d.ldg = ldg;
+    d.WT = at<char>(ws, L.WT);
+    d.ldwt = L.Vld * L.esz;
+    d.nrows_dev = at<int32_t>(ws, L.count);
+    d.row_begin = row_begin;
+    d.row_cap = C;
+    d.V = V;
+    d.H = H;
+    d.ncu = kCostCUs;
+    d.ks = L.ks;
+    d.part = at<float>(ws, L.dhp);
+    {
+      Prof pr("bwd_dhidden", st);
+      KD_HIP(kd::launch_dh(f32, d, kd::dh_grid(C, V, H, kCostCUs, f32), st));
+    }
+    kd::DhReduceArgs r;
+    r.ks = L.ks;
+    r.part = at<float>(ws, L.dhp);
+    r.idx = at<int32_t>(ws, L.idx);
+    r.nrows_dev = at<int32_t>(ws, L.count);
+    r.row_begin = row_begin;
+    r.row_cap = C;
+    r.V = V;
+    r.H = H;
+    r.ncu = kCostCUs;
+    r.dH = dhidden;
+    Prof pr("bwd_dhidden_reduce", st);
+    KD_HIP(kd::launch_dh_reduce(r, st));
+  }
+  if (slot == L.nd - 1 || ci == nchunks - 1) {
+    kd::DwArgs w;
+    w.G = at<char>(ws, L.G);
+    w.ldg = L.Gbs;
+    w.GT = f32 ? at<char>(ws, L.GT) : nullptr;
+    w.ldgt = L.Cld * L.esz;
+    w.Vp = (int)L.Vp;
+    w.XcT = at<char>(ws, L.XcT);
+    w.ldxt = L.Cld * L.esz;
+    w.nrows_dev = at<int32_t>(ws, L.count);
+    w.group_begin = (ci - slot) * C;
+    w.group_chunks = slot + 1;
+    w.chunk = C;
+    w.slot = (int)L.slot;
+    w.V = V;
+    w.H = H;
+    w.beta_first = accumulate_dW;
+    w.dW = dW;
+    Prof pr("bwd_dw", st);
+    KD_HIP(kd::launch_dw(f32, w, st));
+  }
+  return KD_OK;
+}
+
 int bwd_run(const kd_problem* p, const Layout& L, const CmpGrids& cg, const void* hidden,
             const void* W, const int32_t* ids, const void* tl, const uint8_t* mask,
             const float* lse, const float* grad_loss, float* dhidden, float* dW,
@@ -470,9 +611,7 @@ int bwd_run(const kd_problem* p, const Layout& L, const CmpGrids& cg, const void
     Prof pr("zero_rows", st);
     KD_HIP(kd::launch_zero_invalid_rows(at<int32_t>(ws, L.pos), S, H, dhidden, st));
   }
-  const int64_t row_bytes = (int64_t)H * L.esz;
   const int nchunks = S > 0 ? (int)ceil_div(S, C) : 1;
-  const int dgrid = kd::dh_grid(C, V, H, kCostCUs, f32);
   const int sgrid = kd::sweep_grid(C, V, kCostCUs);
   const int Vp = (int)L.Vp;
   if (S > 0) {
@@ -487,13 +626,7 @@ int bwd_run(const kd_problem* p, const Layout& L, const CmpGrids& cg, const void
     // the block stride), or the one row-major tile (fp32: ldg is the row pitch)
     char* Gc = at<char>(ws, L.G) + (f32 ? 0 : (int64_t)slot * L.slot * 512);
     const int64_t ldg = f32 ? L.Vld * L.esz : L.Gbs;
-    if (S > 0) {
-      Prof pr("gather_rows_t", st);
-      KD_HIP(kd::launch_gather_rows_t(f32, (const char*)hidden, row_bytes, at<int32_t>(ws, L.idx),
-                                      at<int32_t>(ws, L.count), row_begin, C, H,
-                                      at<char>(ws, L.XcT) + slot * L.slot * L.esz, L.Cld * L.esz,
-                                      (int)L.slot, at<char>(ws, L.Xc), st));
-    }
+    if (S > 0 && (rc = gather_chunk_rows(p, L, hidden, ci, ws, st))) return rc;
     if (S > 0 && cg.form != KD_FORM_FUSED) {
       // the chunk's logit gradient from the stored grids, then its transpose
       kd::CmpRowArgs ra;
@@ -521,107 +654,119 @@ int bwd_run(const kd_problem* p, const Layout& L, const CmpGrids& cg, const void
       KD_HIP(kd::launch_cmp_rows(cg.form == KD_FORM_DENSE ? kd::kCmpGradDense
                                                           : kd::kCmpGradSparse, ra, st));
     } else if (S > 0) {
-      kd::SweepArgs a;
-      std::memset(&a, 0, sizeof(a));
-      a.W = (const char*)W;
-      a.ldw = row_bytes;
-      // the chunk's rows, gathered in order by the pass above
-      a.X = at<char>(ws, L.Xc);
-      a.ldx = row_bytes;
-      a.x_row0 = 0;
-      a.idx = at<int32_t>(ws, L.idx);
-      a.nrows_dev = at<int32_t>(ws, L.count);
-      a.row_begin = row_begin;
-      a.row_cap = C;
-      a.V = V;
-      a.H = H;
-      a.K = K;
-      a.ncu = kCostCUs;
-      a.T = p->temperature;
-      a.ids_s = at<int32_t>(ws, L.ids_s);
-      a.p_s = at<float>(ws, L.p_s);
-      a.korig_s = at<int32_t>(ws, L.korig_s);
-      a.lse = lse;
-      a.grad_loss = grad_loss;
-      a.G = Gc;
-      a.ldg = ldg;
-      a.GT = f32 ? at<char>(ws, L.GT) + slot * L.slot * L.esz : nullptr;
-      a.ldgt = L.Cld * L.esz;
+      const kd::SweepArgs a = chunk_sweep_args(p, L, W, ci, lse, grad_loss, ws);
       {
         Prof pr("bwd_grad_tile", st);
         KD_HIP(kd::launch_sweep(kd::kSweepBwdG, f32, 0, a, sgrid, st));
       }
-      kd::GradTeacherArgs gt;
-      gt.G = a.G;
-      gt.ldg = a.ldg;
-      gt.GT = a.GT;
-      gt.ldgt = a.ldgt;
-      gt.idx = a.idx;
-      gt.nrows_dev = a.nrows_dev;
-      gt.row_begin = row_begin;
-      gt.row_cap = C;
-      gt.K = K;
-      gt.ids_s = a.ids_s;
-      gt.p_s = a.p_s;
-      gt.grad_loss = grad_loss;
-      gt.T = p->temperature;
-      Prof pr("bwd_grad_teacher", st);
-      KD_HIP(kd::launch_grad_teacher(f32, gt, st));
+      if ((rc = grad_teacher(p, L, a, row_begin, grad_loss, ws, st))) return rc;
     }
-    if (S > 0) {
-      kd::DhArgs d;
-      d.G = Gc;
-      d.ldg = ldg;
-      d.WT = at<char>(ws, L.WT);
-      d.ldwt = L.Vld * L.esz;
-      d.nrows_dev = at<int32_t>(ws, L.count);
-      d.row_begin = row_begin;
-      d.row_cap = C;
-      d.V = V;
-      d.H = H;
-      d.ncu = kCostCUs;
-      d.ks = L.ks;
-      d.part = at<float>(ws, L.dhp);
-      {
-        Prof pr("bwd_dhidden", st);
-        KD_HIP(kd::launch_dh(f32, d, dgrid, st));
-      }
-      kd::DhReduceArgs r;
-      r.ks = L.ks;
-      r.part = at<float>(ws, L.dhp);
-      r.idx = at<int32_t>(ws, L.idx);
-      r.nrows_dev = at<int32_t>(ws, L.count);
-      r.row_begin = row_begin;
-      r.row_cap = C;
-      r.V = V;
-      r.H = H;
-      r.ncu = kCostCUs;
-      r.dH = dhidden;
-      Prof pr("bwd_dhidden_reduce", st);
-      KD_HIP(kd::launch_dh_reduce(r, st));
-    }
-    if (slot == L.nd - 1 || ci == nchunks - 1) {
-      kd::DwArgs w;
-      w.G = at<char>(ws, L.G);
-      w.ldg = L.Gbs;
-      w.GT = f32 ? at<char>(ws, L.GT) : nullptr;
-      w.ldgt = L.Cld * L.esz;
-      w.Vp = Vp;
-      w.XcT = at<char>(ws, L.XcT);
-      w.ldxt = L.Cld * L.esz;
-      w.nrows_dev = at<int32_t>(ws, L.count);
-      w.group_begin = (ci - slot) * C;
-      w.group_chunks = slot + 1;
-      w.chunk = C;
-      w.slot = (int)L.slot;
-      w.V = V;
-      w.H = H;
-      w.beta_first = accumulate_dW;
-      w.dW = dW;
-      Prof pr("bwd_dw", st);
-      KD_HIP(kd::launch_dw(f32, w, st));
-    }
+    if ((rc = chunk_contractions(p, L, Gc, ldg, ci, nchunks, dhidden, dW, accumulate_dW, ws,
+                                 st)))
+      return rc;
   }
+  return KD_OK;
+}
+
+// ------------------------------------------------------------------ forward and backward in one call
+// The workspace of the one-call path: the two-call plan, then one chunk's
+// logits (fp32, as the sweep's lanes hold them) and KL_t of every row.
+struct FbLayout {
+  size_t Z, kl, total;
+};
+
+FbLayout plan_fb(const kd_problem* p, const Layout& L) {
+  FbLayout F;
+  size_t off = L.total;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (size_t)round_up((int64_t)bytes, 256);
+    return o;
+  };
+  F.Z = take((size_t)ceil_div(L.C, kd::kTile) * ceil_div(p->V, kd::kTile) * kd::kZTile * 4);
+  F.kl = take((size_t)(p->S > 0 ? p->S : 1) * 4);
+  F.total = off;
+  return F;
+}
+
+// Per chunk: its rows gathered; one sweep gives the partials of its rows'
+// log-normalisers and the logits at their teacher ids, and stores every
+// logit; the chunk's combine gives lse and KL_t; the gradient tile is formed
+// from the stored logits (no second projection); then the teacher term,
+// dHidden and, at the end of a dW group, dW. The loss is formed once every
+// row's KL_t is known.
+int fwd_bwd_run(const kd_problem* p, const Layout& L, const FbLayout& F, const void* hidden,
+                const void* W, const int32_t* ids, const void* tl, const uint8_t* mask,
+                const float* grad_loss, float* loss, float* lse, float* kl_rows, float* z_topk,
+                float* dhidden, float* dW, int accumulate_dW, void* ws, hipStream_t st) {
+  int rc;
+  if ((rc = teacher_tables(p, L, ids, tl, mask, z_topk, ws, st))) return rc;
+  const int S = (int)p->S, V = (int)p->V, H = (int)p->H, K = (int)p->K;
+  const int C = (int)L.C;
+  if (S > 0) {
+    {
+      Prof pr("zero_rows", st);
+      KD_HIP(kd::launch_zero_invalid_rows(at<int32_t>(ws, L.pos), S, H, dhidden, st));
+    }
+    Prof pr("transpose_w", st);
+    KD_HIP(kd::launch_transpose_w(0, (const char*)W, V, H, at<char>(ws, L.WT), (int)L.Vp,
+                                  (int)L.Vld, st));
+  }
+  float* klbuf = kl_rows ? kl_rows : at<float>(ws, F.kl);
+  kd::CombineArgs c;
+  std::memset(&c, 0, sizeof(c));
+  c.S = S;
+  c.V = V;
+  c.ncu = kCostCUs;
+  c.K = K;
+  c.idx = at<int32_t>(ws, L.idx);
+  c.T = p->temperature;
+  c.pos = at<int32_t>(ws, L.pos);
+  c.nrows_dev = at<int32_t>(ws, L.count);
+  c.pm = at<float>(ws, L.pm);
+  c.ps = at<float>(ws, L.ps);
+  c.ids_s = at<int32_t>(ws, L.ids_s);
+  c.p_s = at<float>(ws, L.p_s);
+  c.korig_s = at<int32_t>(ws, L.korig_s);
+  c.zs = at<float>(ws, L.zs);
+  c.negH = at<float>(ws, L.negH);
+  c.lse = lse;
+  c.kl_rows = kl_rows;
+  c.z_topk = z_topk;
+  c.block_sums = at<double>(ws, L.bsum);
+  c.loss = loss;
+  const int nchunks = S > 0 ? (int)ceil_div(S, C) : 1;
+  const int sgrid = kd::sweep_grid(C, V, kCostCUs);
+  const int zgrid = (int)(ceil_div(C, kd::kTile) * ceil_div(V, kd::kTile));
+  for (int ci = 0; ci < nchunks; ++ci) {
+    const int row_begin = ci * C;
+    kd::SweepArgs a = chunk_sweep_args(p, L, W, ci, lse, grad_loss, ws);
+    if (S > 0) {
+      if ((rc = gather_chunk_rows(p, L, hidden, ci, ws, st))) return rc;
+      a.pm = at<float>(ws, L.pm);
+      a.ps = at<float>(ws, L.ps);
+      a.zs = at<float>(ws, L.zs);
+      a.Zt = at<float>(ws, F.Z);
+      {
+        Prof pr("fwd_lse_gather_keep", st);
+        KD_HIP(kd::launch_sweep(kd::kSweepFwdZ, 0, 0, a, sgrid, st));
+      }
+      {
+        Prof pr("fwd_combine", st);
+        KD_HIP(kd::launch_fwd_combine_chunk(c, row_begin, C, klbuf, st));
+      }
+      {
+        Prof pr("grad_tile_from_logits", st);
+        KD_HIP(kd::launch_zgrad(a, zgrid, st));
+      }
+      if ((rc = grad_teacher(p, L, a, row_begin, grad_loss, ws, st))) return rc;
+    }
+    if ((rc = chunk_contractions(p, L, a.G, a.ldg, ci, nchunks, dhidden, dW, accumulate_dW, ws,
+                                 st)))
+      return rc;
+  }
+  Prof pr("fwd_finish", st);
+  KD_HIP(kd::launch_fwd_finish(c, klbuf, st));
   return KD_OK;
 }
 
@@ -643,6 +788,28 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
   cg.form = KD_FORM_FUSED;
   return bwd_run(p, L, cg, hidden, W, ids, tl, mask, lse, grad_loss, dhidden, dW, accumulate_dW,
                  ws, (hipStream_t)stream);
+}
+
+size_t kd_topk_kl_fwd_bwd_workspace_bytes(const kd_problem* p) {
+  if (check_problem(p) != KD_OK || p->hw_dtype != KD_BF16) return 0;
+  return plan_fb(p, plan(p)).total;
+}
+
+int kd_topk_kl_fwd_bwd(const kd_problem* p, const void* hidden, const void* W, const int32_t* ids,
+                       const void* tl, const uint8_t* mask, const float* grad_loss, float* loss,
+                       float* lse, float* kl_rows, float* z_topk, float* dhidden, float* dW,
+                       int accumulate_dW, void* ws, size_t ws_bytes, void* stream) {
+  int rc = fwd_check(p, hidden, W, ids, tl, loss, lse);
+  if (rc) return rc;
+  if ((rc = bwd_check(p, hidden, W, ids, tl, lse, grad_loss, dhidden, dW, accumulate_dW)))
+    return rc;
+  if (p->hw_dtype != KD_BF16) return KD_ERR_DTYPE;
+  const Layout L = plan(p);
+  const FbLayout F = plan_fb(p, L);
+  if (!ws || ((uintptr_t)ws & 255u) != 0 || ws_bytes < F.total) return KD_ERR_WORKSPACE;
+  if ((rc = check_device())) return rc;
+  return fwd_bwd_run(p, L, F, hidden, W, ids, tl, mask, grad_loss, loss, lse, kl_rows, z_topk,
+                     dhidden, dW, accumulate_dW, ws, (hipStream_t)stream);
 }
 
 }  // extern "C"

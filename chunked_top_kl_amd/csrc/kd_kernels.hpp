@@ -7,7 +7,9 @@
 namespace kd {
 
 enum SweepKind { kSweepFwd = 0, kSweepBwdG = 1, kSweepEnt = 2, kSweepPilot = 3, kSweepEmit = 4,
-                 kSweepSMass = 5, kSweepLogits = 7, kSweepSDrawTiles = 8 };
+                 kSweepSMass = 5, kSweepLogits = 7, kSweepSDrawTiles = 8, kSweepFwdZ = 9 };
+
+constexpr int64_t kZTile = 65536;     // floats of one stored 256 x 256 logit tile
 
 // Vocabulary-sweep projection (forward LSE + gather, backward gradient tile,
 // entropy). Rows are "launch rows" r in [0, rows): compacted row
@@ -27,6 +29,12 @@ struct SweepArgs {
   // and z at every teacher id, at its position in the sorted table
   float* pm; float* ps;
   float* zs;                          // [S,K], indexed like ids_s
+  // the forward that keeps its logits (bf16 inputs, no row map): the fp32
+  // accumulators of tile (token tile jt, vocabulary tile vt) as the lanes hold
+  // them, at Zt + (jt * ceil(V/256) + vt) * kZTile floats; within a tile, wave
+  // w's lane l holds the 16 bytes of (block i, column j, quad q) at float
+  // ((w * 64 + (i * 4 + j) * 4 + q) * 64 + l) * 4
+  float* Zt;
   // backward
   const float* lse; const float* grad_loss;
   char* G; int64_t ldg;               // gradient tile: bf16 in blocks of 256 vocabulary
@@ -77,6 +85,7 @@ struct TeacherArgs {
 
 struct CombineArgs {
   int S, V, ncu, K;
+  const int32_t* idx;                 // compacted -> original row (the per-chunk combine)
   int identity;                       // forward ran over all S rows in order (no row map)
   float T;
   const int32_t* pos; const int32_t* nrows_dev;
@@ -217,6 +226,15 @@ hipError_t launch_draw_tiles(const int32_t* dunit, int rows, int N, int nvt, int
                              int32_t* toff, int32_t* tfill, int32_t* tlist, hipStream_t st);
 int sweep_grid(int64_t rows_max, int V, int ncu);
 hipError_t launch_fwd_combine(const CombineArgs& a, hipStream_t st);
+// The forward and backward in one call: the forward combine of one chunk's
+// launch rows (lse, KL_t into kl_out[t] and z_topk of original row t), the
+// loss over every row once all chunks are combined, and the chunk's gradient
+// tile from the logits its forward sweep stored (grid: token tiles x
+// vocabulary tiles of a full chunk).
+hipError_t launch_fwd_combine_chunk(const CombineArgs& a, int row_begin, int row_cap,
+                                    float* kl_out, hipStream_t st);
+hipError_t launch_fwd_finish(const CombineArgs& a, const float* kl_in, hipStream_t st);
+hipError_t launch_zgrad(const SweepArgs& a, int grid, hipStream_t st);
 hipError_t launch_loss_final(const double* block_sums, int nblk, const int32_t* nrows_dev,
                              float* loss, hipStream_t st);
 hipError_t launch_cmp_rows(int what, const CmpRowArgs& a, hipStream_t st);

@@ -336,6 +336,9 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
   static_assert(kStagingLds <= kMainLds, "staging area");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int half = lane >> 5;
+  // the forward, and the forward that also stores its logits
+  constexpr bool kFwd = KIND == kSweepFwd || KIND == kSweepFwdZ;
+  static_assert(KIND != kSweepFwdZ || (sizeof(T) == 2 && !MAP), "stored logits: bf16, no row map");
 
   int rows = a.row_cap;
   int ntt, jt, b, vt_begin, vt_end;
@@ -422,7 +425,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
     lse2[j] = 0.0f;
     cbase[j] = 0;
     ccur[j] = 0;
-    if constexpr (KIND == kSweepFwd) {
+    if constexpr (kFwd) {
       cbase[j] = (int64_t)orow[j] * a.K;
       ccur[j] = (tl0 + 32 * j < rows) ? lower_bound_ids(a.ids_s + cbase[j], a.K, vt_begin * kTile)
                                       : a.K;
@@ -505,7 +508,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
     int64_t cb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) cb[j] = opaque(cbase[j]);
-    if constexpr (KIND == kSweepFwd) {
+    if constexpr (kFwd) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) window_load(cb[j], ccur[j], a.ids_s, a.K, win[j]);
     }
@@ -576,7 +579,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
         }
       }
 
-      if constexpr (KIND == kSweepFwd) {
+      if constexpr (kFwd) {
         const auto za = [&](int e) { return acc[e >> 4][j][e & 15]; };
         const float mx = tail ? col_max<true>(za, vw0, half, a.V) : col_max<false>(za, vw0, half, a.V);
         const float mn = fmaxf(m[j], mx * c);
@@ -754,6 +757,25 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
             }
         }
       }
+      if constexpr (KIND == kSweepFwdZ) {
+        // the column's logits as the lanes hold them, each store instruction
+        // 1 KB of consecutive lanes, after the column's reductions (so that
+        // the column's accumulators are free again afterwards). A buffer
+        // resource over the tile keeps the addresses in scalar registers.
+        const __amdgpu_buffer_rsrc_t zr = make_rsrc_uniform(
+            a.Zt + ((int64_t)jt * ceil_div(a.V, kTile) + vt) * kZTile, kZTile * 4);
+        const int wofs = __builtin_amdgcn_readfirstlane(w) * 64 * 1024;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const u32x4 v = {__float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1]),
+                             __float_as_uint(acc[i][j][4 * q + 2]),
+                             __float_as_uint(acc[i][j][4 * q + 3])};
+            __builtin_amdgcn_raw_buffer_store_b128(v, zr, lane * 16,
+                                                   wofs + ((i * 4 + j) * 4 + q) * 1024, 0);
+          }
+      }
       __builtin_amdgcn_sched_barrier(0);
     };
     column(std::integral_constant<int, 0>());
@@ -778,7 +800,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
   // ---- end of sweep: merge lane halves, then the two waves sharing tokens
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    if constexpr (KIND == kSweepFwd) {
+    if constexpr (kFwd) {
       const float m2 = __shfl_xor(m[j], 32, 64), s2 = __shfl_xor(s[j], 32, 64);
       lse2_merge(m[j], s[j], m2, s2);
     } else {
@@ -797,7 +819,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
     for (int j = 0; j < 4; ++j) {
       const int t = wn * 128 + j * 32 + lane;
       xm[t] = m[j];
-      if constexpr (KIND == kSweepFwd) {
+      if constexpr (kFwd) {
         xa[t] = s[j];
       } else {
         xa[t] = S64[j];
@@ -812,7 +834,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
       const int t = wn * 128 + j * 32 + lane;
       if (tl0 + 32 * j >= rows) continue;
       const int64_t o = (int64_t)b * ntt * kTile + tl0 + 32 * j;
-      if constexpr (KIND == kSweepFwd) {
+      if constexpr (kFwd) {
         lse2_merge(m[j], s[j], xm[t], (float)xa[t]);
         a.pm[o] = m[j];
         a.ps[o] = s[j];
@@ -869,6 +891,7 @@ KD_SWEEP_KERNEL(kd_sample_draw_tiles_bf16, __bf16, kSweepSDrawTiles, true)
 KD_SWEEP_KERNEL(kd_sample_draw_tiles_f32, float, kSweepSDrawTiles, true)
 KD_SWEEP_KERNEL(kd_cmp_logits_bf16, __bf16, kSweepLogits, false)
 KD_SWEEP_KERNEL(kd_cmp_logits_rows_bf16, __bf16, kSweepLogits, true)
+KD_SWEEP_KERNEL(kd_fwd_lse_gather_keep_bf16, __bf16, kSweepFwdZ, false)
 #undef KD_SWEEP_KERNEL
 
 hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid, hipStream_t st) {
@@ -878,6 +901,8 @@ hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid
   if (!f32) {
     if (kind == kSweepFwd && map) KD_SWEEP(kd_fwd_lse_gather_rows_bf16);
     else if (kind == kSweepFwd) KD_SWEEP(kd_fwd_lse_gather_bf16);
+    else if (kind == kSweepFwdZ && map) return hipErrorInvalidValue;   // no row map
+    else if (kind == kSweepFwdZ) KD_SWEEP(kd_fwd_lse_gather_keep_bf16);
     else if (kind == kSweepBwdG) KD_SWEEP(kd_bwd_grad_tile_bf16);
     else if (kind == kSweepPilot) KD_SWEEP(kd_teacher_pilot_bf16);
     else if (kind == kSweepEmit) KD_SWEEP(kd_teacher_emit_bf16);
@@ -894,10 +919,71 @@ hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid
     else if (kind == kSweepEmit) KD_SWEEP(kd_teacher_emit_f32);
     else if (kind == kSweepSMass) KD_SWEEP(kd_sample_mass_f32);
     else if (kind == kSweepSDrawTiles) KD_SWEEP(kd_sample_draw_tiles_f32);
-    else if (kind == kSweepLogits) return hipErrorInvalidValue;   // bf16 only
+    else if (kind == kSweepLogits || kind == kSweepFwdZ) return hipErrorInvalidValue;   // bf16 only
     else KD_SWEEP(kd_entropy_sweep_f32);
   }
 #undef KD_SWEEP
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Gradient tile of one chunk from the logits its forward sweep stored (the
+// forward and backward in one call): work-group (jt, vt) reads tile (jt, vt)
+// back into the accumulator layout and runs the gradient tile's own epilogue,
+// so G is the one the recomputing sweep would write from the same logits.
+// Launch rows, lse, coef and the store are those of kd_bwd_grad_tile_bf16.
+// ---------------------------------------------------------------------------
+extern "C" __global__ __launch_bounds__(256, 1) void kd_grad_tile_from_logits_bf16(SweepArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kStagingLds];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  int rows = *a.nrows_dev - a.row_begin;
+  rows = rows < a.row_cap ? rows : a.row_cap;
+  if (rows <= 0) return;
+  const int ntt = (int)ceil_div(rows, kTile), nvt = (int)ceil_div(a.V, kTile);
+  if ((int)blockIdx.x >= ntt * nvt) return;
+  const int jt = (int)blockIdx.x / nvt, vt = (int)blockIdx.x % nvt;
+  const float c = kLog2e / a.T;
+  const int tl0 = jt * kTile + wn * 128 + (lane & 31);
+  float lse2[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = tl0 + 32 * j;
+    lse2[j] = r < rows ? a.lse[a.idx[a.row_begin + r]] * kLog2e : 0.0f;
+  }
+  const int n = *a.nrows_dev;
+  const float coef = (n > 0) ? a.grad_loss[0] / ((float)n * a.T) : 0.0f;
+  const float lc2 = coef != 0.0f ? log2f(fabsf(coef)) : -INFINITY;
+  const uint32_t sgn = coef < 0.0f ? 0x80008000u : 0u;
+  floatx16 acc[4][4];
+  if (vt * kTile + wm * 128 < a.V) {
+    // half tiles past the vocabulary were not stored (and are not read below)
+    const float* zt = a.Zt + ((int64_t)jt * nvt + vt) * kZTile + (w * 64 * 64 + lane) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = *(const float4*)(zt + ((i * 4 + j) * 4 + q) * 256);
+          acc[i][j][4 * q] = v.x;
+          acc[i][j][4 * q + 1] = v.y;
+          acc[i][j][4 * q + 2] = v.z;
+          acc[i][j][4 * q + 3] = v.w;
+        }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  }
+  grad_tile_staged<false>(acc, a, vt, jt, rows, tl0, c, lc2, sgn, lse2, lds);
+}
+
+hipError_t launch_zgrad(const SweepArgs& a, int grid, hipStream_t st) {
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kd_grad_tile_from_logits_bf16, dim3(grid), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -958,46 +1044,42 @@ hipError_t launch_grad_teacher(int f32, const GradTeacherArgs& a, hipStream_t st
 // then fp64 block sums of KL over valid rows (fixed order, no atomics).
 //   KL_t = sum_k p log p - (sum_k p z_k)/T + log sum_v exp(z_v/T)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void fwd_combine_kernel(CombineArgs a) {
-  __shared__ double red[256];
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  double contrib = 0.0;
-  if (t < a.S) {
-    const int pr = a.pos[t];
-    if (pr < 0) {
-      a.lse[t] = 0.0f;
-      if (a.kl_rows) a.kl_rows[t] = 0.0f;
-      if (a.z_topk)
-        for (int k = 0; k < a.K; ++k) a.z_topk[(int64_t)t * a.K + k] = __int_as_float(0x7FC00000);
-    } else {
-      // partial row: the original row when the forward ran over all rows
-      const int r = a.identity ? t : pr;
-      const int n = a.identity ? a.S : *a.nrows_dev;
-      const int ns = sweep_splits((int)ceil_div(n, kTile), (int)ceil_div(a.V, kTile), a.ncu);
-      float M = -INFINITY, sum = 0.0f;
-      const int64_t stride = ceil_div(n, kTile) * kTile;
-      for (int b = 0; b < ns; ++b) {
-        const int64_t o = (int64_t)b * stride + r;
-        lse2_merge(M, sum, a.pm[o], a.ps[o]);
-      }
-      // sum_k p_k z_k over the row's usable ids, in sorted order; z_topk in
-      // the caller's order
-      const int64_t base = (int64_t)t * a.K;
-      const float invT = 1.0f / a.T;
-      double dot = 0.0;
-      for (int k = 0; k < a.K; ++k) {
-        if (a.ids_s[base + k] == 0x7FFFFFFF) break;   // out-of-range ids sort last
-        const float zv = a.zs[base + k];
-        dot += (double)a.p_s[base + k] * (double)zv;
-        if (a.z_topk) a.z_topk[base + a.korig_s[base + k]] = zv * invT;
-      }
-      const float lse = (M + __log2f(sum)) * kLn2;
-      const float kl = (float)((double)a.negH[t] - dot / (double)a.T + (double)lse);
-      a.lse[t] = lse;
-      if (a.kl_rows) a.kl_rows[t] = kl;
-      contrib = kl;
-    }
+// One row: merge its ns split partials (at pm/ps[b * stride + r]) into lse,
+// write lse and z_topk of original row t, and return KL_t.
+__device__ inline float combine_row(const CombineArgs& a, int t, int64_t r, int ns, int64_t stride) {
+  float M = -INFINITY, sum = 0.0f;
+  for (int b = 0; b < ns; ++b) {
+    const int64_t o = (int64_t)b * stride + r;
+    lse2_merge(M, sum, a.pm[o], a.ps[o]);
   }
+  // sum_k p_k z_k over the row's usable ids, in sorted order; z_topk in
+  // the caller's order
+  const int64_t base = (int64_t)t * a.K;
+  const float invT = 1.0f / a.T;
+  double dot = 0.0;
+  for (int k = 0; k < a.K; ++k) {
+    if (a.ids_s[base + k] == 0x7FFFFFFF) break;   // out-of-range ids sort last
+    const float zv = a.zs[base + k];
+    dot += (double)a.p_s[base + k] * (double)zv;
+    if (a.z_topk) a.z_topk[base + a.korig_s[base + k]] = zv * invT;
+  }
+  const float lse = (M + __log2f(sum)) * kLn2;
+  a.lse[t] = lse;
+  return (float)((double)a.negH[t] - dot / (double)a.T + (double)lse);
+}
+
+// A row outside the loss: lse and KL 0, z_topk NaN.
+__device__ inline void combine_row_out(const CombineArgs& a, int t) {
+  a.lse[t] = 0.0f;
+  if (a.kl_rows) a.kl_rows[t] = 0.0f;
+  if (a.z_topk)
+    for (int k = 0; k < a.K; ++k) a.z_topk[(int64_t)t * a.K + k] = __int_as_float(0x7FC00000);
+}
+
+// Fixed-order fp64 sum of the 256 contributions of a work-group into
+// block_sums[blockIdx.x].
+__device__ inline void block_sum_kl(const CombineArgs& a, double contrib) {
+  __shared__ double red[256];
   red[threadIdx.x] = contrib;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
@@ -1005,6 +1087,58 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(CombineArgs a) {
     __syncthreads();
   }
   if (threadIdx.x == 0) a.block_sums[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(256) void fwd_combine_kernel(CombineArgs a) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  double contrib = 0.0;
+  if (t < a.S) {
+    const int pr = a.pos[t];
+    if (pr < 0) {
+      combine_row_out(a, t);
+    } else {
+      // partial row: the original row when the forward ran over all rows
+      const int r = a.identity ? t : pr;
+      const int n = a.identity ? a.S : *a.nrows_dev;
+      const int ns = sweep_splits((int)ceil_div(n, kTile), (int)ceil_div(a.V, kTile), a.ncu);
+      const float kl = combine_row(a, t, r, ns, ceil_div(n, kTile) * kTile);
+      if (a.kl_rows) a.kl_rows[t] = kl;
+      contrib = kl;
+    }
+  }
+  block_sum_kl(a, contrib);
+}
+
+// The rows of one chunk launch (launch row r, compacted row row_begin + r):
+// the chunk's sweep wrote their partials with the split count of its own
+// token tiles.
+__global__ __launch_bounds__(256) void fwd_combine_chunk_kernel(CombineArgs a, int row_begin,
+                                                                int row_cap, float* kl_out) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  int n = *a.nrows_dev - row_begin;
+  n = n < row_cap ? n : row_cap;
+  if (r >= n) return;
+  const int t = a.idx[row_begin + r];
+  const int ns = sweep_splits((int)ceil_div(n, kTile), (int)ceil_div(a.V, kTile), a.ncu);
+  kl_out[t] = combine_row(a, t, r, ns, ceil_div(n, kTile) * kTile);
+}
+
+// After every chunk's combine: the rows outside the loss, kl_rows, and the
+// block sums of KL over the rows in the loss (the same fixed order as the
+// one-pass combine).
+__global__ __launch_bounds__(256) void fwd_finish_kernel(CombineArgs a, const float* kl_in) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  double contrib = 0.0;
+  if (t < a.S) {
+    if (a.pos[t] < 0) {
+      combine_row_out(a, t);
+    } else {
+      const float kl = kl_in[t];
+      if (a.kl_rows && a.kl_rows != kl_in) a.kl_rows[t] = kl;
+      contrib = kl;
+    }
+  }
+  block_sum_kl(a, contrib);
 }
 
 __global__ __launch_bounds__(256) void loss_final_kernel(const double* block_sums, int nblk,
@@ -1034,6 +1168,23 @@ hipError_t launch_loss_final(const double* block_sums, int nblk, const int32_t* 
 hipError_t launch_fwd_combine(const CombineArgs& a, hipStream_t st) {
   const int nblk = (int)ceil_div(a.S, 256);
   if (nblk > 0) hipLaunchKernelGGL(fwd_combine_kernel, dim3(nblk), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(256), 0, st, (const double*)a.block_sums,
+                     nblk, a.nrows_dev, a.loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_combine_chunk(const CombineArgs& a, int row_begin, int row_cap,
+                                    float* kl_out, hipStream_t st) {
+  const int nblk = (int)ceil_div(row_cap, 256);
+  if (nblk > 0)
+    hipLaunchKernelGGL(fwd_combine_chunk_kernel, dim3(nblk), dim3(256), 0, st, a, row_begin,
+                       row_cap, kl_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_finish(const CombineArgs& a, const float* kl_in, hipStream_t st) {
+  const int nblk = (int)ceil_div(a.S, 256);
+  if (nblk > 0) hipLaunchKernelGGL(fwd_finish_kernel, dim3(nblk), dim3(256), 0, st, a, kl_in);
   hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(256), 0, st, (const double*)a.block_sums,
                      nblk, a.nrows_dev, a.loss);
   return hipGetLastError();

@@ -37,7 +37,9 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 # kernel symbol (mangled or demangled) -> path step, as named by the library's
 # profiling scopes; the first matching pattern wins
 STEP_PATTERNS = [
+    ("kd_fwd_lse_gather_keep", "fwd_lse_gather_keep"),
     ("kd_fwd_lse_gather", "fwd_lse_gather"),
+    ("kd_grad_tile_from_logits", "grad_tile_from_logits"),
     ("kd_bwd_grad_tile", "bwd_grad_tile"),
     ("kd_entropy_sweep", "entropy_sweep"),
     ("kd_bwd_dhidden", "bwd_dhidden"),
@@ -45,6 +47,8 @@ STEP_PATTERNS = [
     ("dh_reduce_kernel", "bwd_dhidden_reduce"),
     ("grad_teacher_kernel", "bwd_grad_teacher"),
     ("fwd_combine_kernel", "fwd_combine"),
+    ("fwd_combine_chunk_kernel", "fwd_combine"),
+    ("fwd_finish_kernel", "fwd_finish"),
     ("loss_final_kernel", "fwd_combine"),
     ("ent_combine_kernel", "entropy_combine"),
     ("prepass", "prepass"),                      # prepass_kernel, prepass_reg_kernel

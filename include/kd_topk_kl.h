@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define KD_ABI_VERSION 6
+#define KD_ABI_VERSION 7
 
 typedef enum kd_status {
   KD_OK = 0,
@@ -184,6 +184,33 @@ int kd_topk_kl_bwd(const kd_problem* problem, const void* hidden, const void* W,
                    const float* lse, const float* grad_loss,
                    float* dhidden, float* dW, int accumulate_dW,
                    void* ws, size_t ws_bytes, void* stream);
+
+/* Forward and backward in one call, for callers that know the upstream
+ * gradient before the forward (training steps: g = 1, or a loss scale). The
+ * fused chunked loss of "what chunked KL loss does", with the chunk's
+ * gradient taken without projecting the chunk a second time: per chunk, one
+ * projection sweep forms the partial log-normalisers and the logits at the
+ * teacher ids (as kd_topk_kl_fwd) and keeps the chunk's fp32 logits
+ * [chunk,V] in the workspace; once the chunk's lse is known, the logit
+ * gradient G (as kd_topk_kl_bwd) is formed from them, then dhidden and dW.
+ * This trades the recompute that the "operations" section charges to the
+ * fused loss at short context for one chunk of fp32 logits (4*chunk*V bytes,
+ * not growing with S). Outputs are those of kd_topk_kl_fwd followed by
+ * kd_topk_kl_bwd with the same arguments, within fp32 rounding: lse is
+ * merged over the vocabulary ranges of a chunk's sweep rather than of one
+ * sweep over all rows, so it may differ in the last bits, and G with it.
+ *   grad_loss   [device] [1] float32 upstream gradient g of loss
+ *   loss, lse, kl_rows, z_topk   as kd_topk_kl_fwd
+ *   dhidden, dW, accumulate_dW   as kd_topk_kl_bwd
+ *   ws          kd_topk_kl_fwd_bwd_workspace_bytes(problem) bytes, 256-aligned
+ * hw_dtype must be KD_BF16 (KD_ERR_DTYPE otherwise; fp32 inputs use the two
+ * calls). Errors as kd_topk_kl_fwd and kd_topk_kl_bwd. Does not sync.       */
+size_t kd_topk_kl_fwd_bwd_workspace_bytes(const kd_problem* problem);
+int kd_topk_kl_fwd_bwd(const kd_problem* problem, const void* hidden, const void* W,
+                       const int32_t* topk_ids, const void* topk_logits, const uint8_t* mask,
+                       const float* grad_loss, float* loss, float* lse, float* kl_rows,
+                       float* z_topk, float* dhidden, float* dW, int accumulate_dW,
+                       void* ws, size_t ws_bytes, void* stream);
 
 /* Comparator forms of the loss ("what chunked KL loss does" sets the fused
  * chunked loss beside two others, and the "operations" section says the

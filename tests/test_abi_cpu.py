@@ -31,7 +31,7 @@ def test_header_symbols_exported():
 
 
 def test_version_and_status_strings():
-    assert kd.kd_abi_version() == 6
+    assert kd.kd_abi_version() == 7
     for c in range(11):
         assert kd.kd_status_str(c).startswith("KD_")
     assert "unknown" in kd.kd_status_str(99)
