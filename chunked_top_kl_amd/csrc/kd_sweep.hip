@@ -956,7 +956,10 @@ extern "C" __global__ __launch_bounds__(256, 1) void kd_grad_tile_from_logits_bf
   const uint32_t sgn = coef < 0.0f ? 0x80008000u : 0u;
   floatx16 acc[4][4];
   if (vt * kTile + wm * 128 < a.V) {
-    // half tiles past the vocabulary were not stored (and are not read below)
+    // half tiles past the vocabulary were not stored (and are not read below);
+    // the logits are read once: non-temporal loads (0.47 -> 0.44 ms per chunk
+    // of 2048 rows at V = 201088; non-temporal stores in the sweep made it
+    // slower by as much)
     const float* zt = a.Zt + ((int64_t)jt * nvt + vt) * kZTile + (w * 64 * 64 + lane) * 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -964,11 +967,12 @@ extern "C" __global__ __launch_bounds__(256, 1) void kd_grad_tile_from_logits_bf
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float4 v = *(const float4*)(zt + ((i * 4 + j) * 4 + q) * 256);
-          acc[i][j][4 * q] = v.x;
-          acc[i][j][4 * q + 1] = v.y;
-          acc[i][j][4 * q + 2] = v.z;
-          acc[i][j][4 * q + 3] = v.w;
+          const floatx4 v =
+              __builtin_nontemporal_load((const floatx4*)(zt + ((i * 4 + j) * 4 + q) * 256));
+          acc[i][j][4 * q] = v[0];
+          acc[i][j][4 * q + 1] = v[1];
+          acc[i][j][4 * q + 2] = v[2];
+          acc[i][j][4 * q + 3] = v[3];
         }
   } else {
 #pragma unroll
@@ -1111,16 +1115,44 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(CombineArgs a) {
 
 // The rows of one chunk launch (launch row r, compacted row row_begin + r):
 // the chunk's sweep wrote their partials with the split count of its own
-// token tiles.
+// token tiles. One wave per row: lane b merges splits b, b + 64, ..., lane k
+// takes teacher entries k, k + 64, ...; both are then folded over the wave in
+// a fixed order (the row's result does not depend on timing).
 __global__ __launch_bounds__(256) void fwd_combine_chunk_kernel(CombineArgs a, int row_begin,
                                                                 int row_cap, float* kl_out) {
-  const int r = blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   int n = *a.nrows_dev - row_begin;
   n = n < row_cap ? n : row_cap;
   if (r >= n) return;
   const int t = a.idx[row_begin + r];
   const int ns = sweep_splits((int)ceil_div(n, kTile), (int)ceil_div(a.V, kTile), a.ncu);
-  kl_out[t] = combine_row(a, t, r, ns, ceil_div(n, kTile) * kTile);
+  const int64_t stride = ceil_div(n, kTile) * kTile;
+  float M = -INFINITY, sum = 0.0f;
+  for (int b = lane; b < ns; b += 64) lse2_merge(M, sum, a.pm[(int64_t)b * stride + r],
+                                                 a.ps[(int64_t)b * stride + r]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(M, o, 64), s2 = __shfl_xor(sum, o, 64);
+    lse2_merge(M, sum, m2, s2);
+  }
+  // sum_k p_k z_k over the row's usable ids (out-of-range ids sort last and
+  // are left out); z_topk in the caller's order
+  const int64_t base = (int64_t)t * a.K;
+  const float invT = 1.0f / a.T;
+  double dot = 0.0;
+  for (int k = lane; k < a.K; k += 64) {
+    if (a.ids_s[base + k] == 0x7FFFFFFF) break;
+    const float zv = a.zs[base + k];
+    dot += (double)a.p_s[base + k] * (double)zv;
+    if (a.z_topk) a.z_topk[base + a.korig_s[base + k]] = zv * invT;
+  }
+  dot = wave_sum_d(dot);
+  if (lane == 0) {
+    const float lse = (M + __log2f(sum)) * kLn2;
+    a.lse[t] = lse;
+    kl_out[t] = (float)((double)a.negH[t] - dot / (double)a.T + (double)lse);
+  }
 }
 
 // After every chunk's combine: the rows outside the loss, kl_rows, and the
@@ -1175,7 +1207,7 @@ hipError_t launch_fwd_combine(const CombineArgs& a, hipStream_t st) {
 
 hipError_t launch_fwd_combine_chunk(const CombineArgs& a, int row_begin, int row_cap,
                                     float* kl_out, hipStream_t st) {
-  const int nblk = (int)ceil_div(row_cap, 256);
+  const int nblk = (int)ceil_div(row_cap, 4);
   if (nblk > 0)
     hipLaunchKernelGGL(fwd_combine_chunk_kernel, dim3(nblk), dim3(256), 0, st, a, row_begin,
                        row_cap, kl_out);

@@ -19,6 +19,10 @@ What is compared with the oracle at each size:
     oracle values, the kept index set bit for bit, and the selective KL's
     loss, the lse and KL of every kept row, dHidden at 1024 kept rows and dW
     at 512 vocabulary rows against the oracle over the kept rows.
+  * the forward and backward in one call (kd_topk_kl_fwd_bwd) at the
+    32K-context and 256K-context sizes: the loss and every row's lse and KL
+    against the stored oracle values, dHidden at 1024 rows and dW at 512
+    vocabulary rows.
   * the comparator forms (dense, forward-chunked) at the 32K-context size:
     the loss and every row's lse and KL against the stored oracle values,
     dHidden at 256 rows and dW at 128 vocabulary rows.
@@ -219,3 +223,23 @@ def test_full_32k_context_comparator_forms(kd, form):
     rows = sampled_rows(np.arange(p.S), p.chunk, 256, rng)
     check_dh_rows(p, W64, dh.cpu().numpy(), rows, p.S)
     check_dw_rows(p, W64, dW, ref["lse"], np.ones(p.S, bool), sampled_vocab(p, rows, 128, rng))
+
+
+@pytest.mark.parametrize("cfg", ["32k_context", "256k_context"])
+def test_full_size_one_call(kd, cfg):
+    # the forward and backward in one call, with the configuration's chunk
+    p, meta, ref = stored(cfg)
+    hidden, W, ids, tl = to_device(p)
+    g = torch.ones(1, dtype=torch.float32, device="cuda")
+    out = kd.kd_topk_kl_fwd_bwd(hidden, W, ids, tl, g, p.T, p.chunk, want_kl_rows=True)
+    torch.cuda.synchronize()
+    del hidden, W, ids, tl
+    assert rel(float(out["loss"][0]), meta["loss"]) <= BF16_LOSS_RTOL
+    check_row_values(out["lse"].cpu().numpy(), out["kl_rows"].cpu().numpy(), ref["lse"], ref["kl"])
+    W64 = p.W.astype(np.float64)
+    rng = np.random.default_rng(85)
+    rows = sampled_rows(np.arange(p.S), p.chunk, N_DH_ROWS, rng)
+    check_dh_rows(p, W64, out["dhidden"].cpu().numpy(), rows, p.S)
+    check_dw_rows(p, W64, out["dW"], ref["lse"], np.ones(p.S, bool),
+                  sampled_vocab(p, rows, N_DW_ROWS, rng))
+    check_dW_rows_sum_to_zero(out["dW"])
