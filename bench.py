@@ -13,7 +13,10 @@ Prints ONE JSON line. Besides tokens/s it reports the achieved MFMA fraction
 (counting 4 contractions of 2*S*H*V FLOP per step), per-kernel HIP-event
 timings over the timed region, the roofline of the dominant kernel, peak
 device memory against S for the 256K-context configuration shapes, and the
-fp64 CPU oracle timed on a bounded sample of rows.
+fp64 CPU oracle timed on a bounded sample of rows. Beside the step it times
+the forward and backward in one call (kd_topk_kl_fwd_bwd: each chunk's logits
+kept, no second projection; the `one_call` objects), the loss's comparator
+forms, the chunk sizes, the teacher cache writer and the selection policies.
 """
 from __future__ import annotations
 
