@@ -197,9 +197,8 @@ def time_workload(kd, torch, key, p=None, steps=3, warmup=1, comparators=False):
     log(f"[bench] {key}: {ms:.2f} ms/step, {out['tokens_per_s']:.0f} tokens/s, "
         f"MFMA {100 * out['mfma_frac']:.1f}%, peak {out['peak_gib']} GiB")
     del ws, res
-    if key != "c5":
-        out["one_call"] = one_call_leg(kd, torch, wl, t, steps=steps, warmup=warmup,
-                                       two_call_ms=ms)
+    out["one_call"] = one_call_leg(kd, torch, wl, t, steps=steps, warmup=warmup,
+                                   two_call_ms=ms, select=(key == "c5"))
     if comparators:
         out["comparators"] = comparator_leg(kd, torch, wl, t)
     del t
@@ -260,13 +259,15 @@ def comparator_leg(kd, torch, wl, t, steps=3, warmup=1):
     return out
 
 
-def one_call_leg(kd, torch, wl, t, steps=5, warmup=2, two_call_ms=None):
+def one_call_leg(kd, torch, wl, t, steps=5, warmup=2, two_call_ms=None, select=False):
     """The forward and backward in one call (kd_topk_kl_fwd_bwd: each chunk's
     logits kept, its gradient tile formed from them, no second projection) at
     the workload's shapes: ms per step, tokens/s, peak device memory (inputs,
     outputs, workspace), the per-step kernels, and the MFMA fraction of the
     6*S*H*V it projects (the counted 8*S*H*V over its time as well, for
-    comparison with the two calls)."""
+    comparison with the two calls). select: the entropy-selective step (entropy
+    sweep, top-20% selection, then the one call on the kept rows; the MFMA
+    fractions then count the rows in the loss)."""
     S, H, V, K, C = wl["S"], wl["H"], wl["V"], wl["K"], wl["chunk"]
     hidden, W, ids, tl = t
     in_bytes = sum(x.numel() * x.element_size() for x in t)
@@ -279,7 +280,13 @@ def one_call_leg(kd, torch, wl, t, steps=5, warmup=2, two_call_ms=None):
     g = torch.ones(1, dtype=torch.float32, device="cuda")
 
     def step():
-        return kd.kd_topk_kl_fwd_bwd(hidden, W, ids, tl, g, wl["T"], C, workspace=ws)
+        if not select:
+            return kd.kd_topk_kl_fwd_bwd(hidden, W, ids, tl, g, wl["T"], C, workspace=ws)
+        # entropy-selective: the entropy sweep and the selection first (the
+        # one-call workspace holds theirs), then the one call on the kept rows
+        ent = kd.kd_student_entropy(hidden, W, workspace=ws)
+        mask, _, _ = kd.kd_select_top_fraction(ent, hidden, W, 20, 100, workspace=ws)
+        return kd.kd_topk_kl_fwd_bwd(hidden, W, ids, tl, g, wl["T"], C, mask, workspace=ws)
 
     for _ in range(warmup):
         res = step()
@@ -298,14 +305,16 @@ def one_call_leg(kd, torch, wl, t, steps=5, warmup=2, two_call_ms=None):
     prof = kd.kd_profile_read()
     kd.kd_profile_reset()
     peak = (torch.cuda.max_memory_allocated() - base) / 2**30
+    N = (20 * S) // 100 if select else S
+    pre = 2.0 * S * H * V if select else 0.0     # the entropy sweep
     out = dict(ms_per_step=round(ms, 3), tokens_per_s=round(S / (ms / 1000.0), 1),
                peak_gib=round(peak, 3), workspace_gib=round(need / 2**30, 3),
                loss=float(res["loss"][0]),
-               mfma_frac_of_its_6SHV=round(6.0 * S * H * V / (ms / 1000.0)
+               mfma_frac_of_its_6SHV=round((pre + 6.0 * N * H * V) / (ms / 1000.0)
                                            / (PEAK_BF16_TFLOPS * 1e12), 4),
-               counted_8SHV_frac=round(8.0 * S * H * V / (ms / 1000.0)
+               counted_8SHV_frac=round((pre + 8.0 * N * H * V) / (ms / 1000.0)
                                        / (PEAK_BF16_TFLOPS * 1e12), 4),
-               kernels=kernel_table(prof, wl, C, S, steps))
+               kernels=kernel_table(prof, wl, C, N, steps))
     if two_call_ms:
         out["speedup_vs_two_calls"] = round(two_call_ms / ms, 3)
     log(f"[bench] one call: {ms:.2f} ms/step, {out['tokens_per_s']:.0f} tokens/s, "
@@ -671,8 +680,9 @@ def main():
     }
     del ws
     torch.cuda.empty_cache()
-    if not args.no_one_call and args.workload != "c5":
-        result["one_call"] = one_call_leg(kd, torch, wl, t, two_call_ms=ms)
+    if not args.no_one_call:
+        result["one_call"] = one_call_leg(kd, torch, wl, t, two_call_ms=ms,
+                                          select=(args.workload == "c5"))
     if not args.no_chunk_sweep and args.workload == "c3":
         result["chunk_sweep"] = chunk_sweep(kd, torch, wl, t, [512, 1024, 2048])
     if not args.no_comparators and args.workload in ("c2", "c3"):

@@ -11,7 +11,8 @@ tile from them instead of projecting the chunk again. What it must agree on:
     over other vocabulary ranges), dHidden and dW within 1e-3 of their
     largest magnitude (the gradient tile differs only through lse).
 Shapes span several 256-row tiles, ragged tails in S, V, H and the chunk,
-masks, missing rows, duplicate ids, several dW groups and empty problems.
+masks, missing rows, duplicate ids, several dW groups, probability targets
+and empty problems.
 """
 import numpy as np
 import pytest
@@ -22,8 +23,8 @@ pytestmark = [pytest.mark.gpu,
 
 from kd_synth import bf16_bits_from_f32, f32_from_bf16_bits, make_problem  # noqa: E402
 from oracle import oracle_loss_grads  # noqa: E402
-from tests.kd_gpu_helpers import (BF16_GRAD_FRAC, BF16_LOSS_RTOL, max_abs_frac, rel,  # noqa: E402
-                                  to_device)
+from tests.kd_gpu_helpers import (BF16_GRAD_FRAC, BF16_LOSS_RTOL, max_abs_frac,  # noqa: E402
+                                  np_bf16_to_torch, rel, to_device)
 
 TWO_CALL_GRAD_FRAC = 1e-3   # one call against two calls: dHidden, dW
 
@@ -189,3 +190,40 @@ def test_one_call_rejects_fp32(kd):
     with pytest.raises(kd.KdError) as e:
         kd.kd_topk_kl_fwd_bwd(hidden, W, ids, tl, g, p.T, p.chunk)
     assert e.value.code == 3
+
+
+def test_one_call_probability_targets(kd):
+    # teacher probabilities at the ids (KD_TEACHER_PROBS), with zeros, a
+    # negative value, a NaN and an all-zero row (the last three rows excluded)
+    p = make_problem(700, 192, 5000, 50, T=1.5, chunk=256, seed=68)
+    rng = np.random.default_rng(69)
+    pr = rng.random(p.ids.shape).astype(np.float32)
+    pr[rng.random(p.ids.shape) < 0.2] = 0.0
+    pr[3, :] = 0.0
+    pr[5, 2] = -0.25
+    pr[8, 1] = np.nan
+    bits = bf16_bits_from_f32(pr)
+    pr = f32_from_bf16_bits(bits)
+    tpr = np_bf16_to_torch(bits)
+    mask = np.ones(p.S, dtype=bool)
+    mask[100:140] = False
+    hidden, W, ids, _ = to_device(p)
+    mk = torch.from_numpy(mask.astype(np.uint8)).cuda()
+    g = torch.tensor([0.8], dtype=torch.float32, device="cuda")
+    out = _np(kd.kd_topk_kl_fwd_bwd(hidden, W, ids, tpr, g, p.T, p.chunk, mk, want_kl_rows=True,
+                                    want_z_topk=True, teacher_probs=True))
+    torch.cuda.synchronize()
+    ref = oracle_loss_grads(p.hidden, p.W, p.ids, pr, T=p.T, mask=mask, grad_loss=0.8, probs=True)
+    assert rel(float(out["loss"][0]), ref["loss"]) <= BF16_LOSS_RTOL
+    assert max_abs_frac(out["dhidden"], ref["dH"]) <= BF16_GRAD_FRAC
+    assert max_abs_frac(out["dW"], ref["dW"]) <= BF16_GRAD_FRAC
+    assert np.all(out["dhidden"][~ref["valid"]] == 0.0)
+    two = kd.kd_topk_kl_fwd(hidden, W, ids, tpr, p.T, p.chunk, mk, want_kl_rows=True,
+                            want_z_topk=True, teacher_probs=True)
+    dh, dW = kd.kd_topk_kl_bwd(hidden, W, ids, tpr, two["lse"], g, p.T, p.chunk, mk,
+                               teacher_probs=True)
+    torch.cuda.synchronize()
+    res = _np(two)
+    res["dhidden"] = dh.cpu().numpy()
+    res["dW"] = dW.cpu().numpy()
+    check_two_calls(out, res)
