@@ -71,13 +71,20 @@ def kernel_flops(name, wl, C_rows, S_rows):
     return None
 
 
-def measured_traffic(wl, step, slug=None):
+def teacher_profile_name(wl):
+    """The workload name the teacher cache writer's counter summaries carry."""
+    return (f"teacher top-K cache writer at the 32K context shapes: S={wl['S']} H={wl['H']} "
+            f"V={wl['V']} K={wl['K']} chunk={wl['chunk']} bf16")
+
+
+def measured_traffic(wl, step, slug=None, name=None):
     """HBM bytes per launch of `step` from the committed counter summary of this
-    workload, or None when there is none or the kernel sources changed since."""
+    workload (named `name`, else the workload's own name), or None when there
+    is none or the kernel sources changed since."""
     from chunked_top_kl_amd.prof_summary import kernel_sources_hash, read_summary_json
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{slug or wl['slug']}.md")
     js = read_summary_json(path)
-    if not js or js.get("workload") != wl["name"]:
+    if not js or js.get("workload") != (name or wl["name"]):
         return None
     if js.get("kernel_sources_sha256") != kernel_sources_hash():
         log(f"[bench] {os.path.relpath(path, ROOT)} was measured on other kernel sources: traffic null")
@@ -393,7 +400,8 @@ def teacher_leg(kd, torch, wl, t, p, steps=3, warmup=1, cpu_rows=64, cpu=True):
     if em:
         f = 2.0 * S * H * V / em["launches_per_step"]
         a = f / (em["avg_ms"] / 1000.0) / 1e12
-        tr = measured_traffic(wl, "teacher_emit", slug="teacher_topk_" + wl["slug"])
+        tr = measured_traffic(wl, "teacher_emit", slug="teacher_topk_" + wl["slug"],
+                              name=teacher_profile_name(wl))
         roofline = dict(kernel="teacher_emit", bound="mfma", achieved=round(a, 1),
                         peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=round(a / PEAK_BF16_TFLOPS, 4),
                         traffic=tr["bytes"] if tr else None, traffic_detail=tr,
