@@ -17,7 +17,7 @@ __all__ = [
     "KD_BF16", "KD_F32", "KD_TEACHER_LOGITS", "KD_TEACHER_PROBS", "KdError", "kd_problem", "lib",
     "kd_abi_version", "kd_status_str", "kd_topk_kl_workspace_bytes",
     "kd_topk_kl_fwd", "kd_topk_kl_fwd_noalloc", "kd_topk_kl_bwd", "kd_student_entropy",
-    "kd_topk_kl_fwd_bwd_workspace_bytes", "kd_topk_kl_fwd_bwd",
+    "kd_topk_kl_fwd_bwd_workspace_bytes", "kd_topk_kl_fwd_bwd", "kd_scale_f32",
     "KD_FORM_FUSED", "KD_FORM_DENSE", "KD_FORM_FORWARD_CHUNKED", "kd_kl_comparator_fwd",
     "kd_kl_comparator_bwd",
     "kd_select_top_fraction", "kd_select_samples", "kd_validate_topk",
@@ -26,7 +26,7 @@ __all__ = [
     "kd_teacher_topk_workspace_bytes", "kd_teacher_topk",
     "kd_teacher_sample_workspace_bytes", "kd_teacher_sample",
     "kd_profile_enable", "kd_profile_read", "kd_profile_reset",
-    "KDTopKKL", "kd_topk_kl", "LIB_PATH",
+    "KDTopKKL", "KDTopKKLOneCall", "kd_topk_kl", "LIB_PATH",
 ]
 
 KD_BF16, KD_F32 = 0, 1
@@ -83,6 +83,8 @@ lib.kd_topk_kl_fwd_bwd_workspace_bytes.argtypes = [_PP]
 lib.kd_topk_kl_fwd_bwd.restype = ctypes.c_int
 lib.kd_topk_kl_fwd_bwd.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    ctypes.c_int, _P, ctypes.c_size_t, _P]
+lib.kd_scale_f32.restype = ctypes.c_int
+lib.kd_scale_f32.argtypes = [_P, ctypes.c_int64, _P, _P]
 lib.kd_student_entropy.restype = ctypes.c_int
 lib.kd_student_entropy.argtypes = [_PP, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.kd_select_top_fraction.restype = ctypes.c_int
@@ -304,6 +306,17 @@ def kd_topk_kl_fwd_bwd(hidden, W, topk_ids, topk_logits, grad_loss, T=1.0, chunk
                                   1 if accumulate_dW else 0, _ptr(workspace), workspace.numel(),
                                   _stream(dev)), "kd_topk_kl_fwd_bwd")
     return dict(loss=loss, lse=lse, kl_rows=kl, z_topk=zt, dhidden=dh, dW=dW)
+
+
+def kd_scale_f32(x, g):
+    """x *= g[0] in place (x: contiguous float32 device tensor, g: [1] float32)."""
+    if x.dtype != torch.float32 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 tensor")
+    if g.dtype != torch.float32 or g.numel() != 1:
+        raise ValueError("g must be a float32 tensor of one element")
+    g = g.contiguous()
+    _check(lib.kd_scale_f32(_ptr(x), x.numel(), _ptr(g), _stream(x.device)), "kd_scale_f32")
+    return x
 
 
 def kd_kl_comparator_fwd(hidden, W, topk_ids, topk_logits, form, T=1.0, chunk=1024, mask=None,
@@ -631,9 +644,39 @@ class KDTopKKL(torch.autograd.Function):
         return dh, dW, None, None, None, None, None, None
 
 
+class KDTopKKLOneCall(torch.autograd.Function):
+    """The same loss, with its gradients formed during the forward by
+    kd_topk_kl_fwd_bwd at an upstream gradient of 1 (each chunk projected once);
+    the backward scales them by the upstream gradient it receives."""
+
+    @staticmethod
+    def forward(ctx, hidden, W, topk_ids, topk_logits, T, chunk, mask, teacher_probs=False):
+        one = torch.ones(1, dtype=torch.float32, device=hidden.device)
+        out = kd_topk_kl_fwd_bwd(hidden, W, topk_ids, topk_logits, one, T, chunk, mask,
+                                 teacher_probs=teacher_probs)
+        ctx.save_for_backward(out["dhidden"], out["dW"])
+        ctx.dtypes = (hidden.dtype, W.dtype)
+        return out["loss"][0]
+
+    @staticmethod
+    def backward(ctx, grad):
+        dh, dW = ctx.saved_tensors
+        g = grad.detach().reshape(1).to(torch.float32).contiguous()
+        dh_out = dW_out = None
+        if ctx.needs_input_grad[0]:
+            dh_out = kd_scale_f32(dh, g).to(ctx.dtypes[0])
+        if ctx.needs_input_grad[1]:
+            dW_out = kd_scale_f32(dW, g).to(ctx.dtypes[1])
+        return dh_out, dW_out, None, None, None, None, None, None
+
+
 def kd_topk_kl(hidden, W, topk_ids, topk_logits, T=1.0, chunk=1024, mask=None,
-               teacher_probs=False):
+               teacher_probs=False, one_call=False):
     """Differentiable fused chunked top-K KL loss (scalar). teacher_probs: topk_logits
-    hold teacher probabilities (sampled sparse targets) instead of logits."""
-    return KDTopKKL.apply(hidden, W, topk_ids, topk_logits, float(T), int(chunk), mask,
-                          bool(teacher_probs))
+    hold teacher probabilities (sampled sparse targets) instead of logits.
+    one_call: form the gradients in the forward (kd_topk_kl_fwd_bwd, bf16 hidden
+    and W; one chunk of fp32 logits more memory, no second projection), for
+    training steps that always run the backward."""
+    fn = KDTopKKLOneCall if one_call else KDTopKKL
+    return fn.apply(hidden, W, topk_ids, topk_logits, float(T), int(chunk), mask,
+                    bool(teacher_probs))

@@ -812,6 +812,17 @@ int kd_topk_kl_fwd_bwd(const kd_problem* p, const void* hidden, const void* W, c
                      dhidden, dW, accumulate_dW, ws, (hipStream_t)stream);
 }
 
+int kd_scale_f32(float* x, int64_t n, const float* g, void* stream) {
+  if (n < 0) return KD_ERR_SHAPE;
+  if (n > 0 && (!x || !g)) return KD_ERR_NULL;
+  if (n == 0) return KD_OK;
+  int rc;
+  if ((rc = check_device())) return rc;
+  Prof pr("scale_grads", (hipStream_t)stream);
+  KD_HIP(kd::launch_scale(x, n, g, (hipStream_t)stream));
+  return KD_OK;
+}
+
 }  // extern "C"
 
 namespace {

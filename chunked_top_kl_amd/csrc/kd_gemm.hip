@@ -171,6 +171,30 @@ hipError_t launch_zero_invalid_rows(const int32_t* pos, int64_t S, int H, float*
   return hipGetLastError();
 }
 
+// x[i] *= g[0] over n floats (16-byte accesses where x is 16-byte aligned)
+__global__ __launch_bounds__(256) void scale_kernel(float* x, int64_t n, const float* g) {
+  const float f = g[0];
+  const int64_t n4 = ((uintptr_t)x & 15u) == 0 ? n / 4 : 0;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n4; q += stride) {
+    float4 v = ((float4*)x)[q];
+    v.x *= f;
+    v.y *= f;
+    v.z *= f;
+    v.w *= f;
+    ((float4*)x)[q] = v;
+  }
+  for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) x[i] *= f;
+}
+
+hipError_t launch_scale(float* x, int64_t n, const float* g, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int64_t grid = ceil_div(ceil_div(n, 4), 256);
+  if (grid > 8192) grid = 8192;
+  hipLaunchKernelGGL(scale_kernel, dim3((int)grid), dim3(256), 0, st, x, n, g);
+  return hipGetLastError();
+}
+
 // out[h][r] = X[idx[row_begin + r]][h] for the chunk's rows r < rows and
 // out[h][r] = 0 for rows <= r < Cp (the gathered rows, transposed: the dW
 // product reads them with K = chunk rows contiguous). 64 x 64 tiles via LDS.

@@ -247,6 +247,7 @@ hipError_t launch_gather_rows_t(int f32, const char* X, int64_t ldx, const int32
                                 char* out, int64_t ldo, int Cp, char* xc, hipStream_t st);
 hipError_t launch_transpose_w(int f32, const char* W, int V, int H, char* WT, int Vp, int ldwt,
                               hipStream_t st);
+hipError_t launch_scale(float* x, int64_t n, const float* g, hipStream_t st);
 hipError_t launch_zero_invalid_rows(const int32_t* pos, int64_t S, int H, float* dH,
                                     hipStream_t st);
 hipError_t launch_dh(int f32, const DhArgs& a, int grid, hipStream_t st);

@@ -97,6 +97,7 @@ STEP_PATTERNS = [
     ("cmp_dense_grid", "cmp_rows"),
     ("cmp_loss_blocks", "cmp_loss"),
     ("cmp_grad_kernel", "cmp_grad"),
+    ("scale_kernel", "scale_grads"),
     ("copyBuffer", "device_copy"),
 ]
 

@@ -212,6 +212,13 @@ int kd_topk_kl_fwd_bwd(const kd_problem* problem, const void* hidden, const void
                        float* z_topk, float* dhidden, float* dW, int accumulate_dW,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* x[i] *= *g for i < n (x, g: device float32). With kd_topk_kl_fwd_bwd run
+ * at g = 1 in a forward pass, this applies the upstream gradient that an
+ * autograd backward receives later to dhidden and dW: the chunked loss's
+ * gradient is linear in g. Errors: KD_ERR_SHAPE for n < 0, KD_ERR_NULL for a
+ * NULL pointer with n > 0. Does not sync.                                   */
+int kd_scale_f32(float* x, int64_t n, const float* g, void* stream);
+
 /* Comparator forms of the loss ("what chunked KL loss does" sets the fused
  * chunked loss beside two others, and the "operations" section says the
  * fused one is slower than the forward-chunked one at short context, since

@@ -227,3 +227,39 @@ def test_one_call_probability_targets(kd):
     res["dhidden"] = dh.cpu().numpy()
     res["dW"] = dW.cpu().numpy()
     check_two_calls(out, res)
+
+
+def test_one_call_autograd(kd):
+    # the autograd wrapper with the gradients formed in the forward: the same
+    # loss and gradients as the two-call wrapper, for an upstream gradient of 2
+    p = make_problem(500, 128, 2100, 12, T=1.3, chunk=192, seed=17)
+    hidden, W, ids, tl = to_device(p)
+    grads = []
+    for one_call in (True, False):
+        h = hidden.clone().requires_grad_(True)
+        w = W.clone().requires_grad_(True)
+        loss = kd.kd_topk_kl(h, w, ids, tl, p.T, p.chunk, one_call=one_call) * 2.0
+        loss.backward()
+        grads.append((float(loss.detach()), h.grad.float().cpu().numpy(),
+                      w.grad.float().cpu().numpy()))
+    ref = oracle_loss_grads(p.hidden, p.W, p.ids, p.tlogits, T=p.T, grad_loss=2.0)
+    (l1, dh1, dw1), (l2, dh2, dw2) = grads
+    assert rel(l1 / 2.0, ref["loss"]) <= BF16_LOSS_RTOL and rel(l1, l2) <= 1e-5
+    assert max_abs_frac(dh1, ref["dH"]) <= BF16_GRAD_FRAC
+    assert max_abs_frac(dw1, ref["dW"]) <= BF16_GRAD_FRAC
+    # the bf16 gradients of the two wrappers round the same fp32 values up to
+    # the gradient tile's lse difference
+    assert max_abs_frac(dh1, dh2) <= 1e-2 and max_abs_frac(dw1, dw2) <= 1e-2
+
+
+def test_scale_f32(kd):
+    # x *= g over aligned and unaligned ranges with a ragged tail
+    base = torch.arange(1, 1 + 4099, dtype=torch.float32, device="cuda")
+    g = torch.tensor([-0.75], dtype=torch.float32, device="cuda")
+    for lo in (0, 1):
+        x = base.clone()
+        kd.kd_scale_f32(x[lo:], g)
+        torch.cuda.synchronize()
+        want = base.clone()
+        want[lo:] *= -0.75
+        assert torch.equal(x, want)
