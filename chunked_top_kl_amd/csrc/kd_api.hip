@@ -703,13 +703,14 @@ int fwd_bwd_run(const kd_problem* p, const Layout& L, const FbLayout& F, const v
   if ((rc = teacher_tables(p, L, ids, tl, mask, z_topk, ws, st))) return rc;
   const int S = (int)p->S, V = (int)p->V, H = (int)p->H, K = (int)p->K;
   const int C = (int)L.C;
+  const int f32 = p->hw_dtype == KD_F32;
   if (S > 0) {
     {
       Prof pr("zero_rows", st);
       KD_HIP(kd::launch_zero_invalid_rows(at<int32_t>(ws, L.pos), S, H, dhidden, st));
     }
     Prof pr("transpose_w", st);
-    KD_HIP(kd::launch_transpose_w(0, (const char*)W, V, H, at<char>(ws, L.WT), (int)L.Vp,
+    KD_HIP(kd::launch_transpose_w(f32, (const char*)W, V, H, at<char>(ws, L.WT), (int)L.Vp,
                                   (int)L.Vld, st));
   }
   float* klbuf = kl_rows ? kl_rows : at<float>(ws, F.kl);
@@ -749,7 +750,7 @@ int fwd_bwd_run(const kd_problem* p, const Layout& L, const FbLayout& F, const v
       a.Zt = at<float>(ws, F.Z);
       {
         Prof pr("fwd_lse_gather_keep", st);
-        KD_HIP(kd::launch_sweep(kd::kSweepFwdZ, 0, 0, a, sgrid, st));
+        KD_HIP(kd::launch_sweep(kd::kSweepFwdZ, f32, 0, a, sgrid, st));
       }
       {
         Prof pr("fwd_combine", st);
@@ -757,7 +758,7 @@ int fwd_bwd_run(const kd_problem* p, const Layout& L, const FbLayout& F, const v
       }
       {
         Prof pr("grad_tile_from_logits", st);
-        KD_HIP(kd::launch_zgrad(a, zgrid, st));
+        KD_HIP(kd::launch_zgrad(f32, a, zgrid, st));
       }
       if ((rc = grad_teacher(p, L, a, row_begin, grad_loss, ws, st))) return rc;
     }
@@ -791,7 +792,7 @@ int kd_topk_kl_bwd(const kd_problem* p, const void* hidden, const void* W, const
 }
 
 size_t kd_topk_kl_fwd_bwd_workspace_bytes(const kd_problem* p) {
-  if (check_problem(p) != KD_OK || p->hw_dtype != KD_BF16) return 0;
+  if (check_problem(p) != KD_OK) return 0;
   return plan_fb(p, plan(p)).total;
 }
 
@@ -803,7 +804,6 @@ int kd_topk_kl_fwd_bwd(const kd_problem* p, const void* hidden, const void* W, c
   if (rc) return rc;
   if ((rc = bwd_check(p, hidden, W, ids, tl, lse, grad_loss, dhidden, dW, accumulate_dW)))
     return rc;
-  if (p->hw_dtype != KD_BF16) return KD_ERR_DTYPE;
   const Layout L = plan(p);
   const FbLayout F = plan_fb(p, L);
   if (!ws || ((uintptr_t)ws & 255u) != 0 || ws_bytes < F.total) return KD_ERR_WORKSPACE;

@@ -29,7 +29,7 @@ struct SweepArgs {
   // and z at every teacher id, at its position in the sorted table
   float* pm; float* ps;
   float* zs;                          // [S,K], indexed like ids_s
-  // the forward that keeps its logits (bf16 inputs, no row map): the fp32
+  // the forward that keeps its logits (no row map): the fp32
   // accumulators of tile (token tile jt, vocabulary tile vt) as the lanes hold
   // them, at Zt + (jt * ceil(V/256) + vt) * kZTile floats; within a tile, wave
   // w's lane l holds the 16 bytes of (block i, column j, quad q) at float
@@ -234,7 +234,7 @@ hipError_t launch_fwd_combine(const CombineArgs& a, hipStream_t st);
 hipError_t launch_fwd_combine_chunk(const CombineArgs& a, int row_begin, int row_cap,
                                     float* kl_out, hipStream_t st);
 hipError_t launch_fwd_finish(const CombineArgs& a, const float* kl_in, hipStream_t st);
-hipError_t launch_zgrad(const SweepArgs& a, int grid, hipStream_t st);
+hipError_t launch_zgrad(int f32, const SweepArgs& a, int grid, hipStream_t st);
 hipError_t launch_loss_final(const double* block_sums, int nblk, const int32_t* nrows_dev,
                              float* loss, hipStream_t st);
 hipError_t launch_cmp_rows(int what, const CmpRowArgs& a, hipStream_t st);

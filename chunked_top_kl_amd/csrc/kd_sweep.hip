@@ -252,6 +252,43 @@ __device__ __forceinline__ float pick64(const Z& z, int tgt) {
 // part in the barriers; a wave whose half tile lies past the vocabulary
 // computes nothing (its rows are at or past Vp and never stored).
 // ---------------------------------------------------------------------------
+// fp32 gradient tile, one token column t of a lane (its 64 logits z of the
+// half tile from vocabulary row vw0): coef * q (the teacher term is applied by
+// grad_teacher_kernel) into G [rows][Vp], which feeds dHidden, and G^T
+// [Vp][Cp], which feeds dW. Token columns in [rows, round_up(rows, 8)) are
+// written as zeros into G^T, so that the 16-byte granules the contractions
+// read never hold stale data; vocabulary rows in [V, Vp) hold finite values
+// that meet zero rows of W^T.
+__device__ __forceinline__ void grad_column_f32(float (&z)[64], const SweepArgs& a, int t, int vw0,
+                                                int half, int rows, float c, float coef,
+                                                float lse2) {
+  const int Vp = (int)round_up(a.V, 8);
+  const int tpad = (int)round_up(rows, 8);
+#pragma unroll
+  for (int e = 0; e < 64; ++e) z[e] = fast_exp2(fmaf(z[e], c, -lse2));
+  if (t >= tpad) return;
+  const bool gv = t < rows;
+  char* grow = a.G + (int64_t)t * a.ldg;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int v = vw0 + i * 32 + 8 * q + 4 * half;
+      if (v >= Vp) continue;
+      // token columns past `rows` hold a repeated row: exact zeros
+      const float g0 = gv ? z[i * 16 + 4 * q + 0] * coef : 0.0f;
+      const float g1 = gv ? z[i * 16 + 4 * q + 1] * coef : 0.0f;
+      const float g2 = gv ? z[i * 16 + 4 * q + 2] * coef : 0.0f;
+      const float g3 = gv ? z[i * 16 + 4 * q + 3] * coef : 0.0f;
+      char* gt = a.GT + (int64_t)v * a.ldgt + (int64_t)t * 4;
+      if (gv) *(float4*)(grow + (int64_t)v * 4) = make_float4(g0, g1, g2, g3);
+      *(float*)(gt) = g0;
+      *(float*)(gt + a.ldgt) = g1;
+      *(float*)(gt + 2 * a.ldgt) = g2;
+      *(float*)(gt + 3 * a.ldgt) = g3;
+    }
+}
+
 constexpr int kGPitch = 528;
 constexpr int kStagingLds = 256 * kGPitch;   // inside the main-loop stage area
 
@@ -338,7 +375,7 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
   const int half = lane >> 5;
   // the forward, and the forward that also stores its logits
   constexpr bool kFwd = KIND == kSweepFwd || KIND == kSweepFwdZ;
-  static_assert(KIND != kSweepFwdZ || (sizeof(T) == 2 && !MAP), "stored logits: bf16, no row map");
+  static_assert(KIND != kSweepFwdZ || !MAP, "stored logits: no row map");
 
   int rows = a.row_cap;
   int ntt, jt, b, vt_begin, vt_end;
@@ -495,9 +532,6 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
     }
     if (vw0 >= a.V) continue;  // wave-uniform: this half tile is past the vocabulary
     const bool tail = vw0 + 128 > a.V;
-    // columns in [V, round_up(V, 8)) of G are written as zeros (see the store)
-    const int Vp = (int)round_up(a.V, 8);
-    const int tpad = (int)round_up(rows, 8);
 
     // the next teacher ids of every token column, for the walks below. The
     // row offsets pass through an opaque copy each tile, so that the
@@ -725,38 +759,8 @@ __device__ __forceinline__ void sweep_body(SweepArgs a) {
         }
       }
 
-      if constexpr (KIND == kSweepBwdG && sizeof(T) == 4) {
-        // coef * q; the teacher term is applied by grad_teacher_kernel
-#pragma unroll
-        for (int e = 0; e < 64; ++e) z[e] = fast_exp2(fmaf(z[e], c, -lse2[j]));
-        // G [rows][Vp] feeds dHidden, G^T [Vp][Cp] feeds dW. Vocabulary
-        // columns in [V, Vp) and token columns in [rows, round_up(rows, 8))
-        // are written as zeros so that 16-byte granules read by the
-        // contractions never hold stale data.
-        const int t = tl0 + 32 * j;
-        if (t < tpad) {
-          const bool gv = t < rows;
-          char* grow = a.G + (int64_t)t * a.ldg;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int v = vw0 + i * 32 + 8 * q + 4 * half;
-              if (v >= Vp) continue;
-              // token columns past `rows` hold a repeated row: exact zeros
-              const float g0 = gv ? z[i * 16 + 4 * q + 0] * coef : 0.0f;
-              const float g1 = gv ? z[i * 16 + 4 * q + 1] * coef : 0.0f;
-              const float g2 = gv ? z[i * 16 + 4 * q + 2] * coef : 0.0f;
-              const float g3 = gv ? z[i * 16 + 4 * q + 3] * coef : 0.0f;
-              char* gt = a.GT + (int64_t)v * a.ldgt + (int64_t)t * 4;
-              if (gv) *(float4*)(grow + (int64_t)v * 4) = make_float4(g0, g1, g2, g3);
-              *(float*)(gt) = g0;
-              *(float*)(gt + a.ldgt) = g1;
-              *(float*)(gt + 2 * a.ldgt) = g2;
-              *(float*)(gt + 3 * a.ldgt) = g3;
-            }
-        }
-      }
+      if constexpr (KIND == kSweepBwdG && sizeof(T) == 4)
+        grad_column_f32(z, a, tl0 + 32 * j, vw0, half, rows, c, coef, lse2[j]);
       if constexpr (KIND == kSweepFwdZ) {
         // the column's logits as the lanes hold them, each store instruction
         // 1 KB of consecutive lanes, after the column's reductions (so that
@@ -892,6 +896,7 @@ KD_SWEEP_KERNEL(kd_sample_draw_tiles_f32, float, kSweepSDrawTiles, true)
 KD_SWEEP_KERNEL(kd_cmp_logits_bf16, __bf16, kSweepLogits, false)
 KD_SWEEP_KERNEL(kd_cmp_logits_rows_bf16, __bf16, kSweepLogits, true)
 KD_SWEEP_KERNEL(kd_fwd_lse_gather_keep_bf16, __bf16, kSweepFwdZ, false)
+KD_SWEEP_KERNEL(kd_fwd_lse_gather_keep_f32, float, kSweepFwdZ, false)
 #undef KD_SWEEP_KERNEL
 
 hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid, hipStream_t st) {
@@ -919,7 +924,9 @@ hipError_t launch_sweep(int kind, int f32, int map, const SweepArgs& a, int grid
     else if (kind == kSweepEmit) KD_SWEEP(kd_teacher_emit_f32);
     else if (kind == kSweepSMass) KD_SWEEP(kd_sample_mass_f32);
     else if (kind == kSweepSDrawTiles) KD_SWEEP(kd_sample_draw_tiles_f32);
-    else if (kind == kSweepLogits || kind == kSweepFwdZ) return hipErrorInvalidValue;   // bf16 only
+    else if (kind == kSweepFwdZ && map) return hipErrorInvalidValue;   // no row map
+    else if (kind == kSweepFwdZ) KD_SWEEP(kd_fwd_lse_gather_keep_f32);
+    else if (kind == kSweepLogits) return hipErrorInvalidValue;   // bf16 only
     else KD_SWEEP(kd_entropy_sweep_f32);
   }
 #undef KD_SWEEP
@@ -985,9 +992,50 @@ extern "C" __global__ __launch_bounds__(256, 1) void kd_grad_tile_from_logits_bf
   grad_tile_staged<false>(acc, a, vt, jt, rows, tl0, c, lc2, sgn, lse2, lds);
 }
 
-hipError_t launch_zgrad(const SweepArgs& a, int grid, hipStream_t st) {
+// The same for fp32 inputs: the fp32 tile's epilogue (G and G^T, no staging),
+// one token column at a time.
+extern "C" __global__ __launch_bounds__(256) void kd_grad_tile_from_logits_f32(SweepArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int half = lane >> 5;
+  int rows = *a.nrows_dev - a.row_begin;
+  rows = rows < a.row_cap ? rows : a.row_cap;
+  if (rows <= 0) return;
+  const int ntt = (int)ceil_div(rows, kTile), nvt = (int)ceil_div(a.V, kTile);
+  if ((int)blockIdx.x >= ntt * nvt) return;
+  const int jt = (int)blockIdx.x / nvt, vt = (int)blockIdx.x % nvt;
+  const int vw0 = vt * kTile + wm * 128;
+  if (vw0 >= a.V) return;   // wave-uniform: this half tile is past the vocabulary
+  const float c = kLog2e / a.T;
+  const int tl0 = jt * kTile + wn * 128 + (lane & 31);
+  const int n = *a.nrows_dev;
+  const float coef = (n > 0) ? a.grad_loss[0] / ((float)n * a.T) : 0.0f;
+  const float* zt = a.Zt + ((int64_t)jt * nvt + vt) * kZTile + (w * 64 * 64 + lane) * 4;
+#pragma unroll 1
+  for (int j = 0; j < 4; ++j) {
+    const int r = tl0 + 32 * j;
+    const float lse2 = r < rows ? a.lse[a.idx[a.row_begin + r]] * kLog2e : 0.0f;
+    float z[64];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const floatx4 v =
+            __builtin_nontemporal_load((const floatx4*)(zt + ((i * 4 + j) * 4 + q) * 256));
+        z[i * 16 + 4 * q] = v[0];
+        z[i * 16 + 4 * q + 1] = v[1];
+        z[i * 16 + 4 * q + 2] = v[2];
+        z[i * 16 + 4 * q + 3] = v[3];
+      }
+    grad_column_f32(z, a, r, vw0, half, rows, c, coef, lse2);
+  }
+}
+
+hipError_t launch_zgrad(int f32, const SweepArgs& a, int grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kd_grad_tile_from_logits_bf16, dim3(grid), dim3(kThreads), 0, st, a);
+  if (f32)
+    hipLaunchKernelGGL(kd_grad_tile_from_logits_f32, dim3(grid), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(kd_grad_tile_from_logits_bf16, dim3(grid), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -203,8 +203,7 @@ int kd_topk_kl_bwd(const kd_problem* problem, const void* hidden, const void* W,
  *   loss, lse, kl_rows, z_topk   as kd_topk_kl_fwd
  *   dhidden, dW, accumulate_dW   as kd_topk_kl_bwd
  *   ws          kd_topk_kl_fwd_bwd_workspace_bytes(problem) bytes, 256-aligned
- * hw_dtype must be KD_BF16 (KD_ERR_DTYPE otherwise; fp32 inputs use the two
- * calls). Errors as kd_topk_kl_fwd and kd_topk_kl_bwd. Does not sync.       */
+ * Errors as kd_topk_kl_fwd and kd_topk_kl_bwd. Does not sync.                */
 size_t kd_topk_kl_fwd_bwd_workspace_bytes(const kd_problem* problem);
 int kd_topk_kl_fwd_bwd(const kd_problem* problem, const void* hidden, const void* W,
                        const int32_t* topk_ids, const void* topk_logits, const uint8_t* mask,

@@ -183,13 +183,18 @@ def test_one_call_zero_gradient_and_empty(kd):
     assert torch.all(out["dW"] == 0)
 
 
-def test_one_call_rejects_fp32(kd):
-    p = make_problem(128, 64, 1000, 10, T=1.0, chunk=32, hw_dtype="f32", tl_dtype="f32", seed=9)
-    hidden, W, ids, tl = to_device(p)
-    g = torch.ones(1, dtype=torch.float32, device="cuda")
-    with pytest.raises(kd.KdError) as e:
-        kd.kd_topk_kl_fwd_bwd(hidden, W, ids, tl, g, p.T, p.chunk)
-    assert e.value.code == 3
+@pytest.mark.parametrize("S,H,V,K,chunk,T", [
+    (128, 64, 1000, 10, 32, 1.0),       # the tiny fp32 configuration
+    (700, 200, 1537, 13, 256, 2.0),     # ragged fp32: H tail of 200, V % 8 != 0
+])
+def test_one_call_fp32(kd, S, H, V, K, chunk, T):
+    p = make_problem(S, H, V, K, T=T, chunk=chunk, hw_dtype="f32", tl_dtype="f32", seed=S + H)
+    got = one_call(kd, p, grad=0.9)
+    ref = oracle_loss_grads(p.hidden, p.W, p.ids, p.tlogits, T=p.T, grad_loss=0.9)
+    assert rel(float(got["loss"][0]), ref["loss"]) <= 1e-5
+    assert max_abs_frac(got["dhidden"], ref["dH"]) <= 1e-4
+    assert max_abs_frac(got["dW"], ref["dW"]) <= 1e-4
+    check_two_calls(got, two_calls(kd, p, grad=0.9))
 
 
 def test_one_call_probability_targets(kd):
