@@ -324,6 +324,18 @@ def one_call_leg(kd, torch, wl, t, steps=5, warmup=2, two_call_ms=None, select=F
                kernels=kernel_table(prof, wl, C, N, steps))
     if two_call_ms:
         out["speedup_vs_two_calls"] = round(two_call_ms / ms, 3)
+    gp = out["kernels"].get("grad_tile_from_logits")
+    if gp and not select:
+        # the gradient tile from the kept logits: HBM-bound, 4 bytes of logit
+        # read and 2 bytes of gradient written per (row, vocabulary entry) of a
+        # chunk (the padding to whole tiles and 8 columns left out)
+        b = (4.0 + 2.0) * min(C, S) * V
+        gbs = b / (gp["avg_ms"] / 1000.0) / 1e9
+        tr = measured_traffic(wl, "grad_tile_from_logits")
+        out["roofline_grad_tile_from_logits"] = dict(
+            bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+            frac=round(gbs / PEAK_HBM_GBS, 4), bytes_per_launch=b,
+            traffic=tr["bytes"] if tr else None, avg_ms=gp["avg_ms"])
     log(f"[bench] one call: {ms:.2f} ms/step, {out['tokens_per_s']:.0f} tokens/s, "
         f"peak {peak:.2f} GiB")
     del ws, res
