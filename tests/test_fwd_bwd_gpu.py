@@ -95,7 +95,8 @@ def check_two_calls(got, two):
     (300, 64, 4099, 100, 300, 1.0, 1.0),     # one chunk, V % 256 tail
     (513, 256, 777, 33, 512, 0.7, -0.6),     # S just past two tiles, negative upstream gradient
     (640, 224, 2003, 9, 320, 1.0, 0.25),     # H tail of 224 columns
-    (700, 64, 300, 5, 700, 1.0, 1.0),        # V below one vocabulary tile
+    (700, 64, 300, 5, 700, 1.0, 1.0),        # V below two vocabulary tiles
+    (260, 8, 100, 3, 64, 1.0, 1.0),          # H of one 16-byte granule, V below half a tile
 ])
 def test_one_call_ragged(kd, S, H, V, K, chunk, T, grad):
     p = make_problem(S, H, V, K, T=T, chunk=chunk, seed=3 * S + V)
