@@ -273,16 +273,15 @@ def kd_topk_kl_fwd_bwd_workspace_bytes(hidden, W, topk_ids, topk_logits, T=1.0, 
 def kd_topk_kl_fwd_bwd(hidden, W, topk_ids, topk_logits, grad_loss, T=1.0, chunk=1024,
                        mask=None, want_kl_rows=False, want_z_topk=False, dW=None,
                        accumulate_dW=False, workspace=None, teacher_probs=False):
-    """Forward and backward in one call (bf16 hidden and W), with the upstream
-    gradient grad_loss ([1] float32) known up front. Returns dict(loss, lse,
-    kl_rows, z_topk, dhidden, dW): those of kd_topk_kl_fwd followed by
-    kd_topk_kl_bwd."""
+    """Forward and backward in one call, with the upstream gradient grad_loss
+    ([1] float32) known up front. Returns dict(loss, lse, kl_rows, z_topk,
+    dhidden, dW): those of kd_topk_kl_fwd followed by kd_topk_kl_bwd."""
     p = _problem_of(hidden, W, topk_ids, topk_logits, T, chunk, teacher_probs)
     mask = _mask_arg(mask, p.S)
     dev = hidden.device
     need = lib.kd_topk_kl_fwd_bwd_workspace_bytes(ctypes.byref(p))
     if need == 0:
-        raise KdError(3 if p.hw_dtype != KD_BF16 else 2, "kd_topk_kl_fwd_bwd_workspace_bytes")
+        raise KdError(2, "kd_topk_kl_fwd_bwd_workspace_bytes")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     elif workspace.numel() < need:
@@ -674,9 +673,9 @@ def kd_topk_kl(hidden, W, topk_ids, topk_logits, T=1.0, chunk=1024, mask=None,
                teacher_probs=False, one_call=False):
     """Differentiable fused chunked top-K KL loss (scalar). teacher_probs: topk_logits
     hold teacher probabilities (sampled sparse targets) instead of logits.
-    one_call: form the gradients in the forward (kd_topk_kl_fwd_bwd, bf16 hidden
-    and W; one chunk of fp32 logits more memory, no second projection), for
-    training steps that always run the backward."""
+    one_call: form the gradients in the forward (kd_topk_kl_fwd_bwd: one chunk
+    of fp32 logits more memory, no second projection), for training steps that
+    always run the backward."""
     fn = KDTopKKLOneCall if one_call else KDTopKKL
     return fn.apply(hidden, W, topk_ids, topk_logits, float(T), int(chunk), mask,
                     bool(teacher_probs))
