@@ -198,3 +198,39 @@ def test_operand_ranges_beyond_2gib_rejected(kw):
 def test_largest_accepted_vocabulary():
     assert kd.kd_topk_kl_workspace_bytes(prob(V=4_000_000, K=10)) > 0
     assert kd.kd_topk_kl_workspace_bytes(prob(V=2_000_000, K=10, hw=1)) > 0
+
+
+def test_one_call_workspace_and_argument_errors():
+    # the one call needs the two-call workspace plus one chunk of fp32 logits
+    # (4 * chunk * V, in whole 256 x 256 tiles) and one float per row
+    p = prob(S=32768, H=2880, V=201088, K=100, chunk=2048)
+    lib = kd.lib
+    two = kd.kd_topk_kl_workspace_bytes(p)
+    one = lib.kd_topk_kl_fwd_bwd_workspace_bytes(ctypes.byref(p))
+    tiles = ((2048 + 255) // 256) * ((201088 + 255) // 256)
+    assert one - two >= tiles * 65536 * 4 + 32768 * 4
+    assert one - two < tiles * 65536 * 4 + 32768 * 4 + 2 * 256
+    # the extra part does not grow with S
+    p2 = prob(S=262144, H=2880, V=201088, K=100, chunk=2048)
+    extra2 = lib.kd_topk_kl_fwd_bwd_workspace_bytes(ctypes.byref(p2)) - kd.kd_topk_kl_workspace_bytes(p2)
+    assert extra2 - (one - two) < (262144 - 32768) * 4 + 256
+    fake = ctypes.c_void_p(0x1000)
+    ws = ctypes.c_void_p(0x10000)
+    f = lib.kd_topk_kl_fwd_bwd
+    # argument order: problem, hidden, W, ids, logits, mask, grad_loss, loss,
+    # lse, kl_rows, z_topk, dhidden, dW, accumulate_dW, ws, ws_bytes, stream
+    assert f(ctypes.byref(p), fake, fake, fake, fake, None, None, fake, fake, None, None, fake, fake,
+             0, ws, one, None) == KD_ERR_NULL
+    assert f(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, fake, None, None, None, fake,
+             0, ws, one, None) == KD_ERR_NULL
+    assert f(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, fake, None, None, fake, fake,
+             2, ws, one, None) == 10
+    assert f(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, fake, None, None, fake, fake,
+             0, ws, one - 1, None) == 6
+    assert f(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, fake, None, None, fake, fake,
+             0, ctypes.c_void_p(0x10010), one, None) == 6
+    bad = prob(S=32768, H=2880, V=201088, K=100, chunk=0)
+    assert lib.kd_topk_kl_fwd_bwd_workspace_bytes(ctypes.byref(bad)) == 0
+    assert lib.kd_scale_f32(None, 4, fake, None) == KD_ERR_NULL
+    assert lib.kd_scale_f32(fake, -1, fake, None) == KD_ERR_SHAPE
+    assert lib.kd_scale_f32(None, 0, None, None) == KD_OK
